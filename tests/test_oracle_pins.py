@@ -1,0 +1,294 @@
+"""Pins for the fp64 oracle: checks against things other than itself.
+
+Each test names what fixes the expected value: an invariant the page
+"Tensor Parallelism > Combining Column and Row Parallelism" states, a closed
+form, or brute force on tiny shapes with independent scalar code.
+"""
+import math
+from decimal import Decimal, getcontext
+
+import numpy as np
+import pytest
+
+import oracle
+from attention_shards_amd import synthetic as syn
+
+
+def rms(a):
+    return float(np.sqrt(np.mean(np.square(a))))
+
+
+def rel_err(a, b):
+    return float(np.max(np.abs(a - b))) / rms(b)
+
+
+# ---------------------------------------------------------------------------
+# GeLU: closed forms of z * Phi(z)
+# ---------------------------------------------------------------------------
+
+def _decimal_pi():
+    # Machin's formula with the arctan series, in Decimal arithmetic.
+    def arctan_inv(x):
+        x = Decimal(x)
+        term = 1 / x
+        total = term
+        n = 1
+        x2 = x * x
+        while True:
+            term /= -x2
+            add = term / (2 * n + 1)
+            if abs(add) < Decimal(10) ** (-(getcontext().prec + 2)):
+                break
+            total += add
+            n += 1
+        return total
+    return 16 * arctan_inv(5) - 4 * arctan_inv(239)
+
+
+def _phi_taylor(x: float) -> float:
+    """Standard normal CDF from the Maclaurin series of erf, 60 digits."""
+    getcontext().prec = 60
+    u = Decimal(x) / Decimal(2).sqrt()
+    term = u
+    s = u
+    n = 0
+    while True:
+        n += 1
+        term = -term * u * u / n
+        add = term / (2 * n + 1)
+        s += add
+        if abs(add) < Decimal(10) ** -55:
+            break
+    erf = 2 / _decimal_pi().sqrt() * s
+    return float((1 + erf) / 2)
+
+
+# Standard normal CDF, Abramowitz & Stegun, Handbook, Table 26.1 (10 places).
+AS_TABLE_26_1 = {0.5: 0.6914624613, 1.0: 0.8413447461, 1.5: 0.9331927987,
+                 2.0: 0.9772498681, 2.5: 0.9937903347, 3.0: 0.9986501020}
+
+
+def test_phi_series_matches_printed_table():
+    for x, p in AS_TABLE_26_1.items():
+        assert abs(_phi_taylor(x) - p) < 1e-10, x
+
+
+@pytest.mark.parametrize("z", [-3.0, -2.7, -1.0, -0.5, -1e-3, 0.25, 1.0, 2.7, 3.0])
+def test_gelu_equals_z_phi(z):
+    want = z * _phi_taylor(z)
+    got = float(oracle.gelu(np.array([z]))[0])
+    assert abs(got - want) <= 4e-16 * max(1.0, abs(z)), (z, got, want)
+
+
+def test_gelu_special_values():
+    g = oracle.gelu(np.array([0.0, 40.0, -40.0]))
+    assert g[0] == 0.0
+    assert g[1] == 40.0
+    assert abs(g[2]) < 1e-300
+    z = np.linspace(-6, 6, 1001)
+    # Phi(z) + Phi(-z) = 1  =>  GeLU(z) - GeLU(-z) = z
+    assert np.max(np.abs(oracle.gelu(z) - oracle.gelu(-z) - z)) < 1e-15
+
+
+def test_gelu_is_not_the_tanh_form():
+    # the tanh approximation differs by ~4.7e-4 near z = 2.7; the exact form
+    # must be far closer to z*Phi(z) than that
+    z = 2.7
+    tanh_form = 0.5 * z * (1 + math.tanh(math.sqrt(2 / math.pi)
+                                         * (z + 0.044715 * z ** 3)))
+    exact = z * _phi_taylor(z)
+    assert abs(tanh_form - exact) > 1e-4
+    assert abs(float(oracle.gelu(np.array([z]))[0]) - exact) < 1e-14
+
+
+# ---------------------------------------------------------------------------
+# FFN: invariants stated on the page, closed forms, brute force
+# ---------------------------------------------------------------------------
+
+def _ffn(seed, M, h, f, dtype=syn.BF16):
+    d = syn.make_ffn_inputs(seed, M, h, f, dtype)
+    return (syn.to_f64(d["X"], dtype), syn.to_f64(d["W1"], dtype),
+            syn.to_f64(d["W2"], dtype))
+
+
+@pytest.mark.parametrize("t", [1, 2, 4, 8])
+def test_shard_sum_identity(t):
+    """FFN step 3: sum over GPUs of the partials equals the unsharded FFN."""
+    X, W1, W2 = _ffn(11, 37, 64, 256)
+    f = W1.shape[1]
+    total = sum(oracle.ffn_shard(X, W1[:, syn.column_slice(f, i, t)],
+                                 W2[syn.column_slice(f, i, t), :])
+                for i in range(t))
+    assert rel_err(total, oracle.ffn_full(X, W1, W2)) < 1e-12
+
+
+@pytest.mark.parametrize("t,i", [(2, 1), (4, 2), (8, 7)])
+def test_local_gelu_is_slice_of_global(t, i):
+    """GeLU is element-wise, so the local GeLU is a slice of the global one."""
+    X, W1, _ = _ffn(12, 19, 48, 192)
+    cols = syn.column_slice(W1.shape[1], i, t)
+    local = oracle.column_parallel(X, W1[:, cols])
+    glob = oracle.column_parallel(X, W1)[:, cols]
+    assert np.max(np.abs(local - glob)) <= 1e-14 * np.max(np.abs(glob))
+    # and not a slice of some other shard
+    other = oracle.column_parallel(X, W1)[:, syn.column_slice(W1.shape[1], (i + 1) % t, t)]
+    assert np.max(np.abs(local - other)) > 1e-3
+
+
+def test_permutation_invariance():
+    """Column layout of layer 1 = row layout of layer 2: permuting W1's
+    columns and W2's rows by the same permutation leaves Y unchanged."""
+    X, W1, W2 = _ffn(13, 23, 32, 128)
+    perm = np.random.default_rng(0).permutation(W1.shape[1])
+    a = oracle.ffn_full(X, W1, W2)
+    b = oracle.ffn_full(X, W1[:, perm], W2[perm, :])
+    assert rel_err(b, a) < 1e-13
+    bad = oracle.ffn_full(X, W1[:, perm], W2)
+    assert rel_err(bad, a) > 0.1
+
+
+def test_identity_weights_give_gelu_of_x():
+    X = syn.to_f64(syn.normal_tensor(14, 0, (9, 16), 1.0), syn.BF16)
+    eye = np.eye(16)
+    Y = oracle.ffn_shard(X, eye, eye)
+    want = np.vectorize(lambda z: z * _phi_taylor(z))(X)
+    assert np.max(np.abs(Y - want)) < 1e-15
+
+
+def test_power_of_two_scaling_is_exact():
+    X, W1, W2 = _ffn(15, 7, 16, 64)
+    assert np.array_equal(oracle.ffn_shard(X, W1, 2.0 * W2),
+                          2.0 * oracle.ffn_shard(X, W1, W2))
+
+
+@pytest.mark.parametrize("t", [1, 2, 4])
+def test_ffn_brute_force_tiny(t):
+    """Scalar loops with math.erf (independent of numpy/scipy) on M=2, h=4, f=8."""
+    X, W1, W2 = _ffn(16, 2, 4, 8)
+    M, h = X.shape
+    f = W1.shape[1]
+    fs = f // t
+    for i in range(t):
+        want = [[0.0] * h for _ in range(M)]
+        for r in range(M):
+            for jj in range(fs):
+                j = i * fs + jj
+                z = 0.0
+                for k in range(h):
+                    z += X[r, k] * W1[k, j]
+                g = 0.5 * z * (1.0 + math.erf(z / math.sqrt(2.0)))
+                for c in range(h):
+                    want[r][c] += g * W2[j, c]
+        got = oracle.ffn_shard(X, W1[:, i * fs:(i + 1) * fs],
+                               W2[i * fs:(i + 1) * fs, :])
+        assert np.max(np.abs(got - np.array(want))) < 1e-14
+
+
+# ---------------------------------------------------------------------------
+# Attention
+# ---------------------------------------------------------------------------
+
+def _attn(seed, batch, seq, h, nh, d):
+    a = syn.make_attn_inputs(seed, batch, seq, h, nh, d)
+    return tuple(syn.to_f64(a[k], syn.BF16) for k in ("X", "WQ", "WK", "WV", "WO"))
+
+
+@pytest.mark.parametrize("causal", [True, False])
+@pytest.mark.parametrize("t", [2, 4])
+def test_attention_shard_sum_is_unsharded_mha(t, causal):
+    """Heads are independent and W_o is row-parallel: the sum of the t
+    partials equals the unsharded multi-head attention output."""
+    X, WQ, WK, WV, WO = _attn(21, 2, 24, 32, 4, 8)
+    total = sum(oracle.attn_shard(X, WQ, WK, WV, WO, 2, 24, 4, 8, i, t, causal)
+                for i in range(t))
+    full = oracle.attn_full(X, WQ, WK, WV, WO, 2, 24, 4, 8, causal)
+    assert rel_err(total, full) < 1e-12
+
+
+def test_head_independence():
+    """Changing head j's Q/K/V weights changes only head j's output columns."""
+    X, WQ, WK, WV, _ = _attn(22, 1, 20, 32, 4, 8)
+    Q, K, V = X @ WQ, X @ WK, X @ WV
+    O = oracle.attention_heads(Q, K, V, 1, 20, 4, 8)
+    WQ2 = WQ.copy()
+    WQ2[:, 16:24] = 0.0                      # head 2
+    WV2 = WV.copy()
+    WV2[:, 16:24] *= -3.0
+    O2 = oracle.attention_heads(X @ WQ2, K, X @ WV2, 1, 20, 4, 8)
+    keep = np.r_[0:16, 24:32]
+    assert np.array_equal(O[:, keep], O2[:, keep])
+    assert np.max(np.abs(O[:, 16:24] - O2[:, 16:24])) > 1e-3
+
+
+def test_causal_row0_and_single_token():
+    X, WQ, WK, WV, _ = _attn(23, 1, 16, 32, 2, 16)
+    Q, K, V = X @ WQ, X @ WK, X @ WV
+    O = oracle.attention_heads(Q, K, V, 1, 16, 2, 16, causal=True)
+    assert np.max(np.abs(O[0] - V[0])) < 1e-15          # row 0 sees only key 0
+    O1 = oracle.attention_heads(Q[:1], K[:1], V[:1], 1, 1, 2, 16, causal=False)
+    assert np.max(np.abs(O1 - V[:1])) < 1e-15           # one token: O = V
+
+
+def test_zero_queries_give_prefix_mean():
+    """W_Q = 0 makes all kept scores equal: causal output is the prefix mean
+    of V and non-causal output is the full mean."""
+    X, _, WK, WV, _ = _attn(24, 2, 33, 32, 2, 16)
+    Q = np.zeros((66, 32))
+    K, V = X @ WK, X @ WV
+    O = oracle.attention_heads(Q, K, V, 2, 33, 2, 16, causal=True)
+    for b in range(2):
+        Vb = V[b * 33:(b + 1) * 33]
+        want = np.cumsum(Vb, axis=0) / np.arange(1, 34)[:, None]
+        assert np.max(np.abs(O[b * 33:(b + 1) * 33] - want)) < 1e-14
+    On = oracle.attention_heads(Q, K, V, 2, 33, 2, 16, causal=False)
+    assert np.max(np.abs(On[:33] - V[:33].mean(axis=0))) < 1e-14
+
+
+@pytest.mark.parametrize("causal", [True, False])
+def test_attention_brute_force_tiny(causal):
+    """Scalar loops with math.exp on S=3, h=4, n_h=2, d=2, t=2."""
+    X, WQ, WK, WV, WO = _attn(25, 1, 3, 4, 2, 2)
+    S, h, nh, d, t = 3, 4, 2, 2, 2
+    for i in range(t):
+        y = [[0.0] * h for _ in range(S)]
+        for hh in range(i * nh // t, (i + 1) * nh // t):
+            cols = range(hh * d, (hh + 1) * d)
+            q = [[sum(X[r, k] * WQ[k, c] for k in range(h)) for c in cols] for r in range(S)]
+            kk = [[sum(X[r, k] * WK[k, c] for k in range(h)) for c in cols] for r in range(S)]
+            v = [[sum(X[r, k] * WV[k, c] for k in range(h)) for c in cols] for r in range(S)]
+            for r in range(S):
+                keys = range(r + 1) if causal else range(S)
+                sc = [sum(q[r][e] * kk[j][e] for e in range(d)) / math.sqrt(d) for j in keys]
+                mx = max(sc)
+                w = [math.exp(s - mx) for s in sc]
+                z = sum(w)
+                o = [sum(w[n] * v[j][e] for n, j in enumerate(keys)) / z for e in range(d)]
+                for c in range(h):
+                    y[r][c] += sum(o[e] * WO[hh * d + e, c] for e in range(d))
+        got = oracle.attn_shard(X, WQ, WK, WV, WO, 1, S, nh, d, i, t, causal)
+        assert np.max(np.abs(got - np.array(y))) < 1e-14
+
+
+# ---------------------------------------------------------------------------
+# Reduce
+# ---------------------------------------------------------------------------
+
+def test_reduce_small_integers_exact():
+    rng = np.random.default_rng(3)
+    parts = [rng.integers(-64, 64, size=(5, 7)).astype(np.float64) for _ in range(8)]
+    R = rng.integers(-64, 64, size=(5, 7)).astype(np.float64)
+    out = oracle.partial_reduce(parts, R)
+    want = np.zeros((5, 7))
+    for r in range(5):
+        for c in range(7):
+            want[r, c] = sum(int(p[r, c]) for p in parts) + int(R[r, c])
+    assert np.array_equal(out, want)
+
+
+def test_reduce_copy_and_residual_once():
+    p = np.arange(12.0).reshape(3, 4)
+    assert np.array_equal(oracle.partial_reduce([p]), p)
+    ones = np.ones((3, 4))
+    # t partials each equal to c, residual r: out = t*c + r (r added once)
+    assert np.array_equal(oracle.partial_reduce([ones * 3] * 4, ones * 5),
+                          ones * 17)
