@@ -1,0 +1,493 @@
+// Dense GEMMs of the shard path on gfx950 matrix cores.
+//
+//   bf16:  C[M,N] = A[M,K] * B[K,N], v_mfma_f32_32x32x16_bf16, fp32 accumulators.
+//   fp32:  the same product with v_mfma_f32_16x16x4_f32.
+//
+// They serve the column-parallel W1 product with its element-wise GeLU
+// epilogue, the row-parallel W2 product, the head-sharded QKV projection and
+// the row-parallel output projection (page "Tensor Parallelism > Combining
+// Column and Row Parallelism", FFN steps 1-2 and the attention paragraphs).
+//
+// bf16 kernel layout
+//   * A (activations) is K-contiguous; B (weights, "X W" orientation) is
+//     N-contiguous.  Both MFMA operands want 8 consecutive K values per lane,
+//     so B is transposed on its way into LDS: each thread loads an 8(k) x 8(n)
+//     block with eight 16-byte loads and repacks it with v_perm_b32 into eight
+//     16-byte k-runs.
+//   * LDS holds A as [BM][64] and B^T as [BN][64] bf16 (128-byte rows of eight
+//     16-byte chunks).  Chunk c of row r lives at chunk c ^ ((r ^ r>>3) & 7),
+//     which keeps the 16-byte operand reads of 8 (or 16) consecutive rows on
+//     distinct banks.
+//   * Two LDS stages: while the MFMAs consume stage k, the global loads for
+//     stage k+1 are in flight into registers; one barrier per K step.
+//   * Workgroup ids are remapped so each XCD (dispatch is round-robin over
+//     the 8 XCDs) receives a contiguous run of tiles, ordered in groups of 8
+//     tile-rows so neighbouring tiles share A and B panels in that XCD's L2.
+#include "internal.h"
+
+namespace tp {
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int BK = 64;
+constexpr int ROW_BYTES = BK * 2;
+
+__device__ __forceinline__ int swz(int r) { return (r ^ (r >> 3)) & 7; }
+
+// fp32 -> bf16, round to nearest even (finite values).
+__device__ __forceinline__ uint32_t f2bf(float f) {
+  uint32_t u = __float_as_uint(f);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return u >> 16;
+}
+__device__ __forceinline__ float bf2f(uint32_t b) {
+  return __uint_as_float(b << 16);
+}
+
+__device__ __forceinline__ float gelu_erf(float z) {
+  return 0.5f * z * (1.0f + erff(z * 0.70710678118654752f));
+}
+
+// ---------------------------------------------------------------------------
+// Epilogues: store4 receives four accumulators of columns col0..col0+3 of one
+// row (col0 % 4 == 0; the caller has checked row < M and col0 < N, and N % 4
+// == 0 so the run is entirely inside the matrix).
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ void store_run4(void* C, int64_t ldc, int out, int row,
+                                           int col0, const float* v) {
+  if (out == OUT_F32) {
+    float* c = static_cast<float*>(C) + (int64_t)row * ldc + col0;
+    *reinterpret_cast<f32x4*>(c) = f32x4{v[0], v[1], v[2], v[3]};
+  } else {
+    uint16_t* c = static_cast<uint16_t*>(C) + (int64_t)row * ldc + col0;
+    uint2 w;
+    w.x = f2bf(v[0]) | (f2bf(v[1]) << 16);
+    w.y = f2bf(v[2]) | (f2bf(v[3]) << 16);
+    *reinterpret_cast<uint2*>(c) = w;
+  }
+}
+
+struct EpiStore {
+  void* C;
+  int64_t ldc;
+  int out;  // OutType
+  __device__ void store4(int row, int col0, const float* v) const {
+    store_run4(C, ldc, out, row, col0, v);
+  }
+};
+
+struct EpiGelu {
+  void* C;
+  int64_t ldc;
+  int out;
+  __device__ void store4(int row, int col0, const float* v) const {
+    float g[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) g[r] = gelu_erf(v[r]);
+    store_run4(C, ldc, out, row, col0, g);
+  }
+};
+
+// Scatter of the QKV projection into the attention workspace (d == 128).
+struct EpiQkv {
+  QkvOut q;
+  __device__ void store4(int row, int col0, const float* v) const {
+    const int hall = col0 >> 7;          // head index over [Q | K | V]
+    const int dd = col0 & 127;
+    const int sec = hall / q.nl;         // 0 = Q, 1 = K, 2 = V
+    const int head = hall - sec * q.nl;
+    const int b = row / q.seq;
+    const int s = row - b * q.seq;
+    const int64_t bh = (int64_t)b * q.nl + head;
+    uint32_t hi[4], lo[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      hi[r] = f2bf(v[r]);
+      lo[r] = f2bf(v[r] - bf2f(hi[r]));
+    }
+    if (sec < 2) {
+      const int64_t off = (bh * q.seq_pad + s) * 128 + dd;
+      uint16_t* ph = sec == 0 ? q.q_hi : q.k_hi;
+      uint16_t* pl = sec == 0 ? q.q_lo : q.k_lo;
+      *reinterpret_cast<uint2*>(ph + off) = uint2{hi[0] | (hi[1] << 16), hi[2] | (hi[3] << 16)};
+      *reinterpret_cast<uint2*>(pl + off) = uint2{lo[0] | (lo[1] << 16), lo[2] | (lo[3] << 16)};
+    } else {
+      // V: fp16 hi/lo pair (the probabilities multiplying it are fp16)
+      const int64_t off = (bh * 128 + dd) * q.seq_pad + s;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const _Float16 vh = (_Float16)v[r];
+        const _Float16 vl = (_Float16)(v[r] - (float)vh);
+        q.vt_hi[off + (int64_t)r * q.seq_pad] = __builtin_bit_cast(uint16_t, vh);
+        q.vt_lo[off + (int64_t)r * q.seq_pad] = __builtin_bit_cast(uint16_t, vl);
+      }
+    }
+  }
+};
+
+// Tile index with the XCD-contiguous remap and grouped (8 tile-rows) order.
+__device__ __forceinline__ void tile_coords(int tiles_m, int tiles_n, int& tm,
+                                            int& tn) {
+  const int bid = blockIdx.x;
+  const int nb = gridDim.x;
+  const int xcd = bid & 7, j = bid >> 3, q = nb >> 3, r = nb & 7;
+  const int lin = xcd * q + (xcd < r ? xcd : r) + j;
+  constexpr int GROUP = 8;
+  const int per_group = GROUP * tiles_n;
+  const int g = lin / per_group;
+  const int first_m = g * GROUP;
+  const int gsize = min(tiles_m - first_m, GROUP);
+  const int w = lin - g * per_group;
+  tm = first_m + w % gsize;
+  tn = w / gsize;
+}
+
+// ---------------------------------------------------------------------------
+// bf16 kernel
+// ---------------------------------------------------------------------------
+template <int BM, int BN, int WM, int WN, class Epi>
+__global__ void __launch_bounds__(WM * WN * 64)
+gemm_bf16_kernel(const uint16_t* __restrict__ A, int64_t lda,
+                 const uint16_t* __restrict__ B, int64_t ldb, int M, int N,
+                 int K, int kwrap, int tiles_m, int tiles_n, Epi epi) {
+  // Row gk of the K range reads B row (gk < kwrap ? gk : gk - kwrap); with
+  // kwrap < K (K <= 2 kwrap) the same B is used twice, which multiplies an
+  // A laid out as [A_hi | A_lo] by B in two passes.
+  constexpr int NT = WM * WN * 64;
+  constexpr int A_PASS = BM * 8 / NT;             // 16-byte chunks per thread
+  constexpr int B_BLOCKS = (BK / 8) * (BN / 8);      // 8x8 blocks per tile
+  constexpr int B_PASS = (B_BLOCKS + NT - 1) / NT;
+  constexpr int FM = BM / WM / 32;
+  constexpr int FN = BN / WN / 32;
+  constexpr int STAGE = (BM + BN) * ROW_BYTES;
+  static_assert(A_PASS * NT == BM * 8, "A tile split");
+  static_assert(FM >= 1 && FN >= 1, "wave tile");
+
+  __shared__ __attribute__((aligned(16))) uint8_t smem[2 * STAGE];
+
+  int tm, tn;
+  tile_coords(tiles_m, tiles_n, tm, tn);
+  const int m0 = tm * BM, n0 = tn * BN;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wr0 = (wave / WN) * (BM / WM);
+  const int wc0 = (wave % WN) * (BN / WN);
+
+  u32x4 ra[A_PASS];
+  u32x4 rb[B_PASS][8];
+  f32x16 acc[FM][FN];
+#pragma unroll
+  for (int mi = 0; mi < FM; ++mi)
+#pragma unroll
+    for (int ni = 0; ni < FN; ++ni)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[mi][ni][e] = 0.0f;
+
+  auto gload = [&](int k0) {
+#pragma unroll
+    for (int p = 0; p < A_PASS; ++p) {
+      const int idx = p * NT + tid;
+      const int r = idx >> 3, c = idx & 7;
+      const int gr = m0 + r, gk = k0 + c * 8;
+      if (gr < M && gk < K)
+        ra[p] = *reinterpret_cast<const u32x4*>(A + (int64_t)gr * lda + gk);
+      else
+        ra[p] = u32x4{0, 0, 0, 0};
+    }
+#pragma unroll
+    for (int p = 0; p < B_PASS; ++p) {
+      const int idx = p * NT + tid;
+      const bool own = (B_BLOCKS % NT == 0) || idx < B_BLOCKS;
+      const int kg = idx / (BN / 8), ng = idx % (BN / 8);
+      const int gn = n0 + ng * 8;
+#pragma unroll
+      for (int jj = 0; jj < 8; ++jj) {
+        const int gk = k0 + kg * 8 + jj;
+        const int bk = gk < kwrap ? gk : gk - kwrap;
+        if (own && gk < K && gn < N)
+          rb[p][jj] = *reinterpret_cast<const u32x4*>(B + (int64_t)bk * ldb + gn);
+        else
+          rb[p][jj] = u32x4{0, 0, 0, 0};
+      }
+    }
+  };
+
+  auto lstore = [&](int stage) {
+    uint8_t* la = smem + stage * STAGE;
+    uint8_t* lb = la + BM * ROW_BYTES;
+#pragma unroll
+    for (int p = 0; p < A_PASS; ++p) {
+      const int idx = p * NT + tid;
+      const int r = idx >> 3, c = idx & 7;
+      *reinterpret_cast<u32x4*>(la + r * ROW_BYTES + ((c ^ swz(r)) << 4)) = ra[p];
+    }
+#pragma unroll
+    for (int p = 0; p < B_PASS; ++p) {
+      const int idx = p * NT + tid;
+      if (B_BLOCKS % NT != 0 && idx >= B_BLOCKS) continue;
+      const int kg = idx / (BN / 8), ng = idx % (BN / 8);
+#pragma unroll
+      for (int n = 0; n < 8; ++n) {
+        const uint32_t sel = (n & 1) ? 0x07060302u : 0x05040100u;
+        u32x4 v;
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+          v[q] = __builtin_amdgcn_perm(rb[p][2 * q + 1][n >> 1], rb[p][2 * q][n >> 1], sel);
+        const int row = ng * 8 + n;
+        *reinterpret_cast<u32x4*>(lb + row * ROW_BYTES + ((kg ^ swz(row)) << 4)) = v;
+      }
+    }
+  };
+
+  auto compute = [&](int stage) {
+    const uint8_t* la = smem + stage * STAGE;
+    const uint8_t* lb = la + BM * ROW_BYTES;
+#pragma unroll
+    for (int ks = 0; ks < BK / 16; ++ks) {
+      const int ch = 2 * ks + (lane >> 5);
+      bf16x8 a[FM], b[FN];
+#pragma unroll
+      for (int mi = 0; mi < FM; ++mi) {
+        const int row = wr0 + mi * 32 + (lane & 31);
+        a[mi] = *reinterpret_cast<const bf16x8*>(la + row * ROW_BYTES + ((ch ^ swz(row)) << 4));
+      }
+#pragma unroll
+      for (int ni = 0; ni < FN; ++ni) {
+        const int row = wc0 + ni * 32 + (lane & 31);
+        b[ni] = *reinterpret_cast<const bf16x8*>(lb + row * ROW_BYTES + ((ch ^ swz(row)) << 4));
+      }
+#pragma unroll
+      for (int mi = 0; mi < FM; ++mi)
+#pragma unroll
+        for (int ni = 0; ni < FN; ++ni)
+          acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[mi], b[ni], acc[mi][ni], 0, 0, 0);
+    }
+  };
+
+  const int nk = (K + BK - 1) / BK;
+  gload(0);
+  lstore(0);
+  __syncthreads();
+  for (int kt = 0; kt < nk; ++kt) {
+    const int cur = kt & 1;
+    if (kt + 1 < nk) gload((kt + 1) * BK);
+    compute(cur);
+    if (kt + 1 < nk) lstore(cur ^ 1);
+    __syncthreads();
+  }
+
+  // Epilogue through LDS: per 32-row slab, each wave parks its fp32
+  // accumulators in its own LDS region (32 x WCOLS, padded), then reads them
+  // back as runs of 4 consecutive columns for vector stores.
+  // 32x32 accumulator layout: lane l, register e holds row
+  // 8*(e/4) + 4*(l/32) + e%4 and column l%32 of the block.
+  constexpr int WCOLS = BN / WN;
+  constexpr int PITCH = WCOLS + 4;
+  static_assert(WM * WN * 32 * PITCH * 4 <= 2 * STAGE, "epilogue staging fits");
+  float* stage_f = reinterpret_cast<float*>(smem) + wave * 32 * PITCH;
+#pragma unroll
+  for (int mi = 0; mi < FM; ++mi) {
+#pragma unroll
+    for (int ni = 0; ni < FN; ++ni)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int i = 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
+        stage_f[i * PITCH + ni * 32 + (lane & 31)] = acc[mi][ni][e];
+      }
+    __syncthreads();
+    constexpr int RUNS = WCOLS / 4;           // 4-column runs per row
+    constexpr int ROWS_PER_PASS = 64 / RUNS;  // rows covered by one wave pass
+    for (int rr = lane / RUNS; rr < 32; rr += ROWS_PER_PASS) {
+      const int c4 = (lane % RUNS) * 4;
+      const int row = m0 + wr0 + mi * 32 + rr;
+      const int col0 = n0 + wc0 + c4;
+      if (row < M && col0 < N) {
+        const f32x4 v4 = *reinterpret_cast<const f32x4*>(stage_f + rr * PITCH + c4);
+        float v[4] = {v4[0], v4[1], v4[2], v4[3]};
+        epi.store4(row, col0, v);
+      }
+    }
+    __syncthreads();
+  }
+}
+
+// Tile configurations.  The choice minimises the estimated time: full
+// 256-CU waves of tiles times the tile's cost, the larger tiles being
+// cheaper per element (less LDS and L2 traffic per MFMA).
+struct TileChoice {
+  int bm, bn;
+};
+
+TileChoice choose_bf16_tile(int M, int N) {
+  const TileChoice cand[3] = {{256, 256}, {256, 128}, {128, 128}};
+  const double eff[3] = {1.0, 0.88, 0.72};
+  int best = 0;
+  double best_cost = 1e300;
+  for (int c = 0; c < 3; ++c) {
+    const int64_t tiles = (int64_t)((M + cand[c].bm - 1) / cand[c].bm) *
+                          ((N + cand[c].bn - 1) / cand[c].bn);
+    const double waves = (double)((tiles + 255) / 256);
+    const double cost = waves * cand[c].bm * cand[c].bn / eff[c];
+    if (cost < best_cost * 0.999) {
+      best_cost = cost;
+      best = c;
+    }
+  }
+  return cand[best];
+}
+
+template <int BM, int BN, int WM, int WN, class Epi>
+hipError_t launch_bf16(const uint16_t* A, int64_t lda, const uint16_t* B,
+                       int64_t ldb, int M, int N, int K, int kwrap,
+                       const Epi& epi, hipStream_t s) {
+  const int tm = (M + BM - 1) / BM, tn = (N + BN - 1) / BN;
+  hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, WM, WN, Epi>), dim3(tm * tn),
+                     dim3(WM * WN * 64), 0, s, A, lda, B, ldb, M, N, K, kwrap,
+                     tm, tn, epi);
+  return hipGetLastError();
+}
+
+template <class Epi>
+hipError_t dispatch_bf16(const uint16_t* A, int64_t lda, const uint16_t* B,
+                         int64_t ldb, int M, int N, int K, int kwrap,
+                         const Epi& epi, hipStream_t s) {
+  if (M == 0 || N == 0) return hipSuccess;
+  const TileChoice t = choose_bf16_tile(M, N);
+  if (t.bm == 256 && t.bn == 256)
+    return launch_bf16<256, 256, 2, 2>(A, lda, B, ldb, M, N, K, kwrap, epi, s);
+  if (t.bm == 256 && t.bn == 128)
+    return launch_bf16<256, 128, 2, 2>(A, lda, B, ldb, M, N, K, kwrap, epi, s);
+  return launch_bf16<128, 128, 2, 2>(A, lda, B, ldb, M, N, K, kwrap, epi, s);
+}
+
+// ---------------------------------------------------------------------------
+// fp32 kernel: 64x64 tiles, 4 waves of 32x32, v_mfma_f32_16x16x4_f32.
+// ---------------------------------------------------------------------------
+constexpr int F_BM = 64, F_BN = 64, F_BK = 32;
+
+template <class Epi>
+__global__ void __launch_bounds__(256)
+gemm_f32_kernel(const float* __restrict__ A, int64_t lda,
+                const float* __restrict__ B, int64_t ldb, int M, int N, int K,
+                int tiles_m, int tiles_n, Epi epi) {
+  __shared__ float As[F_BM][F_BK + 1];
+  __shared__ float Bs[F_BK][F_BN + 4];
+  int tm, tn;
+  tile_coords(tiles_m, tiles_n, tm, tn);
+  const int m0 = tm * F_BM, n0 = tn * F_BN;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wr0 = (wave >> 1) * 32, wc0 = (wave & 1) * 32;
+  f32x4 acc[2][2];
+#pragma unroll
+  for (int a = 0; a < 2; ++a)
+#pragma unroll
+    for (int b = 0; b < 2; ++b) acc[a][b] = f32x4{0, 0, 0, 0};
+
+  for (int k0 = 0; k0 < K; k0 += F_BK) {
+#pragma unroll
+    for (int p = 0; p < 2; ++p) {
+      const int idx = p * 256 + tid;  // 512 float4 in the 64x32 A tile
+      const int r = idx >> 3, c = (idx & 7) * 4;
+      f32x4 v = f32x4{0, 0, 0, 0};
+      if (m0 + r < M && k0 + c < K)
+        v = *reinterpret_cast<const f32x4*>(A + (int64_t)(m0 + r) * lda + k0 + c);
+      As[r][c] = v[0];
+      As[r][c + 1] = v[1];
+      As[r][c + 2] = v[2];
+      As[r][c + 3] = v[3];
+    }
+#pragma unroll
+    for (int p = 0; p < 2; ++p) {
+      const int idx = p * 256 + tid;  // 512 float4 in the 32x64 B tile
+      const int r = idx >> 4, c = (idx & 15) * 4;
+      f32x4 v = f32x4{0, 0, 0, 0};
+      if (k0 + r < K && n0 + c < N)
+        v = *reinterpret_cast<const f32x4*>(B + (int64_t)(k0 + r) * ldb + n0 + c);
+      *reinterpret_cast<f32x4*>(&Bs[r][c]) = v;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int kk = 0; kk < F_BK; kk += 4) {
+      float a[2], b[2];
+#pragma unroll
+      for (int mi = 0; mi < 2; ++mi) a[mi] = As[wr0 + mi * 16 + (lane & 15)][kk + (lane >> 4)];
+#pragma unroll
+      for (int ni = 0; ni < 2; ++ni) b[ni] = Bs[kk + (lane >> 4)][wc0 + ni * 16 + (lane & 15)];
+#pragma unroll
+      for (int mi = 0; mi < 2; ++mi)
+#pragma unroll
+        for (int ni = 0; ni < 2; ++ni)
+          acc[mi][ni] = __builtin_amdgcn_mfma_f32_16x16x4f32(a[mi], b[ni], acc[mi][ni], 0, 0, 0);
+    }
+    __syncthreads();
+  }
+  // 16x16 accumulator layout: lane l, register e holds row 4*(l/16)+e and
+  // column l%16 of the block.  Transpose through LDS into runs of 4 columns.
+  __shared__ __attribute__((aligned(16))) float stg[4][32][36];
+#pragma unroll
+  for (int mi = 0; mi < 2; ++mi)
+#pragma unroll
+    for (int ni = 0; ni < 2; ++ni)
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        stg[wave][mi * 16 + 4 * (lane >> 4) + e][ni * 16 + (lane & 15)] = acc[mi][ni][e];
+  __syncthreads();
+  for (int rr = lane >> 3; rr < 32; rr += 8) {
+    const int c4 = (lane & 7) * 4;
+    const int row = m0 + wr0 + rr, col0 = n0 + wc0 + c4;
+    if (row < M && col0 < N) {
+      const f32x4 v4 = *reinterpret_cast<const f32x4*>(&stg[wave][rr][c4]);
+      float v[4] = {v4[0], v4[1], v4[2], v4[3]};
+      epi.store4(row, col0, v);
+    }
+  }
+}
+
+template <class Epi>
+hipError_t launch_f32(const float* A, int64_t lda, const float* B, int64_t ldb,
+                      int M, int N, int K, const Epi& epi, hipStream_t s) {
+  if (M == 0 || N == 0) return hipSuccess;
+  const int tm = (M + F_BM - 1) / F_BM, tn = (N + F_BN - 1) / F_BN;
+  hipLaunchKernelGGL((gemm_f32_kernel<Epi>), dim3(tm * tn), dim3(256), 0, s, A,
+                     lda, B, ldb, M, N, K, tm, tn, epi);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t gemm_bf16_store(const uint16_t* A, int64_t lda, const uint16_t* B,
+                           int64_t ldb, void* C, int64_t ldc, OutType out,
+                           int M, int N, int K, hipStream_t s) {
+  return dispatch_bf16(A, lda, B, ldb, M, N, K, K, EpiStore{C, ldc, (int)out}, s);
+}
+
+hipError_t gemm_bf16_store_split_a(const uint16_t* A2, int64_t lda,
+                                   const uint16_t* B, int64_t ldb, void* C,
+                                   int64_t ldc, OutType out, int M, int N, int K,
+                                   hipStream_t s) {
+  return dispatch_bf16(A2, lda, B, ldb, M, N, 2 * K, K, EpiStore{C, ldc, (int)out}, s);
+}
+
+hipError_t gemm_bf16_gelu(const uint16_t* A, int64_t lda, const uint16_t* B,
+                          int64_t ldb, uint16_t* C, int64_t ldc, int M, int N,
+                          int K, hipStream_t s) {
+  return dispatch_bf16(A, lda, B, ldb, M, N, K, K, EpiGelu{C, ldc, (int)OUT_BF16}, s);
+}
+
+hipError_t gemm_bf16_qkv(const uint16_t* A, int64_t lda, const uint16_t* B,
+                         int64_t ldb, const QkvOut& q, int M, int N, int K,
+                         hipStream_t s) {
+  return dispatch_bf16(A, lda, B, ldb, M, N, K, K, EpiQkv{q}, s);
+}
+
+hipError_t gemm_f32(const float* A, int64_t lda, const float* B, int64_t ldb,
+                    void* C, int64_t ldc, OutType out, bool gelu, int M, int N,
+                    int K, hipStream_t s) {
+  if (gelu) return launch_f32(A, lda, B, ldb, M, N, K, EpiGelu{C, ldc, (int)out}, s);
+  return launch_f32(A, lda, B, ldb, M, N, K, EpiStore{C, ldc, (int)out}, s);
+}
+
+}  // namespace tp

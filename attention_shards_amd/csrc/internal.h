@@ -1,0 +1,73 @@
+// Internal declarations shared by the host dispatch (tp_shard.cpp) and the
+// HIP kernel files.  Not part of the public ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace tp {
+
+// Output element type of a GEMM epilogue.
+enum OutType { OUT_F32 = 0, OUT_BF16 = 1 };
+
+// Where the QKV projection's epilogue scatters its columns.  All buffers are
+// 16-bit words.  Q and K are [batch][nl][seq_pad][d] (d contiguous), each a
+// bf16 hi/lo pair: hi = bf16(v), lo = bf16(v - hi).  V is stored transposed,
+// [batch][nl][d][seq_pad] (sequence contiguous), because it is the row
+// operand of the probability-times-value product, as an fp16 hi/lo pair
+// (the probabilities are fp16).
+struct QkvOut {
+  uint16_t* q_hi;
+  uint16_t* q_lo;
+  uint16_t* k_hi;
+  uint16_t* k_lo;
+  uint16_t* vt_hi;
+  uint16_t* vt_lo;
+  int32_t seq;      // tokens per sequence
+  int32_t seq_pad;  // seq rounded up to the attention key tile (64)
+  int32_t nl;       // local heads
+  int32_t d;        // head dim
+};
+
+// C[M,N] = A[M,K] * B[K,N] with bf16 inputs and fp32 accumulation.
+// A is K-contiguous (row stride lda), B is N-contiguous (row stride ldb).
+// Requirements checked by the caller: K % 8 == 0, N % 8 == 0, lda/ldb % 8 == 0,
+// 16-byte aligned A and B.
+hipError_t gemm_bf16_store(const uint16_t* A, int64_t lda, const uint16_t* B,
+                           int64_t ldb, void* C, int64_t ldc, OutType out,
+                           int M, int N, int K, hipStream_t s);
+// Same product, C = bf16(GeLU_erf(acc)).
+hipError_t gemm_bf16_gelu(const uint16_t* A, int64_t lda, const uint16_t* B,
+                          int64_t ldb, uint16_t* C, int64_t ldc, int M, int N,
+                          int K, hipStream_t s);
+// C = [A_hi | A_lo] * B: A2 is [M, 2K] (row stride lda), the same B[K,N]
+// multiplies both halves (two MFMA passes over K).
+hipError_t gemm_bf16_store_split_a(const uint16_t* A2, int64_t lda,
+                                   const uint16_t* B, int64_t ldb, void* C,
+                                   int64_t ldc, OutType out, int M, int N, int K,
+                                   hipStream_t s);
+// Same product scattered into the attention workspace (N == 3*nl*d).
+hipError_t gemm_bf16_qkv(const uint16_t* A, int64_t lda, const uint16_t* B,
+                         int64_t ldb, const QkvOut& q, int M, int N, int K,
+                         hipStream_t s);
+
+// fp32 inputs, fp32 MFMA.  Requirements: K % 4 == 0, N % 4 == 0.
+hipError_t gemm_f32(const float* A, int64_t lda, const float* B, int64_t ldb,
+                    void* C, int64_t ldc, OutType out, bool gelu, int M, int N,
+                    int K, hipStream_t s);
+
+// Causal / full attention over the QKV workspace; writes O as a bf16 hi/lo
+// pair [batch*seq, 2*nl*d]: O_hi in columns [0, nl*d), O_lo in
+// [nl*d, 2*nl*d).  d must be 128.
+hipError_t attention_fwd(const QkvOut& q, int batch, bool causal, uint16_t* O,
+                         hipStream_t s);
+
+// out = sum_i P_i + R, fp32 accumulate.  n % 8 == 0.
+struct ReducePtrs {
+  const void* p[64];
+};
+hipError_t partial_reduce(const ReducePtrs& ptrs, int t, int pdt,
+                          const void* R, int rdt, void* out, int odt,
+                          int64_t n, hipStream_t s);
+
+}  // namespace tp

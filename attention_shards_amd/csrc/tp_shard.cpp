@@ -1,0 +1,344 @@
+// C ABI of libtpshard.so: argument validation, workspace layout and launch
+// sequencing for one GPU's share of a tensor-parallel transformer sub-layer
+// (page "Tensor Parallelism > Combining Column and Row Parallelism").
+//
+// Every check runs before the first HIP call, so a rejected call enqueues
+// nothing and touches no device state; this file's only HIP calls are the
+// kernel launches (through the tp:: launchers) and error queries.
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdint>
+#include <cstdio>
+#include <string>
+
+#include "../../include/tp_shard.h"
+#include "internal.h"
+
+namespace {
+
+thread_local std::string g_err;
+
+tp_status_t fail(tp_status_t st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return st;
+}
+
+tp_status_t ok() {
+  g_err.clear();
+  return TP_SUCCESS;
+}
+
+bool valid_dtype(int32_t d) { return d == TP_F32 || d == TP_BF16; }
+int64_t esize(int32_t d) { return d == TP_F32 ? 4 : 2; }
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+struct Range {
+  uintptr_t lo, hi;  // [lo, hi)
+};
+Range range_of(const void* p, int64_t bytes) {
+  const uintptr_t a = reinterpret_cast<uintptr_t>(p);
+  return Range{a, a + (uintptr_t)(bytes > 0 ? bytes : 0)};
+}
+bool overlap(Range a, Range b) { return a.lo < b.hi && b.lo < a.hi && a.hi > a.lo && b.hi > b.lo; }
+
+// Bytes spanned by a [rows, cols] view with row stride ld.
+int64_t span_bytes(int64_t rows, int64_t cols, int64_t ld, int64_t es) {
+  if (rows <= 0 || cols <= 0) return 0;
+  return ((rows - 1) * ld + cols) * es;
+}
+
+tp_status_t hip_status(hipError_t e, const char* what) {
+  if (e == hipSuccess) return ok();
+  return fail(TP_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+constexpr int64_t kInt32Max = 2147483647;
+constexpr int64_t kAttnHeadDim = 128;
+constexpr int64_t kAttnKeyTile = 64;
+
+int64_t align256(int64_t b) { return (b + 255) / 256 * 256; }
+
+// Attention workspace: six [batch*nl, seq_pad, d] 16-bit arrays (Q, K, V^T as
+// hi/lo pairs) followed by O [batch*seq, 2*nl*d] bf16 (hi half, lo half).
+struct AttnLayout {
+  int64_t seq_pad, part_bytes, o_bytes, total;
+};
+AttnLayout attn_layout(int64_t batch, int64_t seq, int64_t nl, int64_t d) {
+  AttnLayout L;
+  L.seq_pad = (seq + kAttnKeyTile - 1) / kAttnKeyTile * kAttnKeyTile;
+  L.part_bytes = align256(batch * nl * L.seq_pad * d * 2);
+  L.o_bytes = align256(batch * seq * 2 * nl * d * 2);
+  L.total = 6 * L.part_bytes + L.o_bytes;
+  return L;
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t tp_abi_version(void) { return TP_ABI_VERSION; }
+
+const char* tp_status_string(int32_t s) {
+  switch (s) {
+    case TP_SUCCESS: return "TP_SUCCESS";
+    case TP_ERR_NULL: return "TP_ERR_NULL";
+    case TP_ERR_SHAPE: return "TP_ERR_SHAPE";
+    case TP_ERR_SHARD: return "TP_ERR_SHARD";
+    case TP_ERR_DIVISIBILITY: return "TP_ERR_DIVISIBILITY";
+    case TP_ERR_DTYPE: return "TP_ERR_DTYPE";
+    case TP_ERR_WORKSPACE: return "TP_ERR_WORKSPACE";
+    case TP_ERR_ALIAS: return "TP_ERR_ALIAS";
+    case TP_ERR_HIP: return "TP_ERR_HIP";
+    case TP_ERR_UNSUPPORTED: return "TP_ERR_UNSUPPORTED";
+    case TP_ERR_ALIGNMENT: return "TP_ERR_ALIGNMENT";
+    default: return "TP_ERR_UNKNOWN_STATUS";
+  }
+}
+
+const char* tp_last_error_message(void) { return g_err.c_str(); }
+
+// ---------------------------------------------------------------------------
+// FFN shard
+// ---------------------------------------------------------------------------
+size_t tp_ffn_shard_workspace_bytes(int64_t tokens, int64_t hidden, int64_t ffn,
+                                    int32_t t, int32_t in_dtype) {
+  (void)hidden;
+  if (tokens < 0 || ffn <= 0 || t < 1 || ffn % t != 0 || !valid_dtype(in_dtype)) return 0;
+  return (size_t)align256(tokens * (ffn / t) * esize(in_dtype));
+}
+
+tp_status_t tp_ffn_shard(const void* X, const void* W1_i, const void* W2_i,
+                         void* Y_i, int64_t tokens, int64_t hidden, int64_t ffn,
+                         int32_t i, int32_t t, int64_t ld_w1, int32_t in_dtype,
+                         int32_t out_dtype, void* workspace,
+                         size_t workspace_bytes, void* stream) {
+  try {
+    if (!valid_dtype(in_dtype) || !valid_dtype(out_dtype))
+      return fail(TP_ERR_DTYPE, "tp_ffn_shard: dtype codes in=%d out=%d", in_dtype, out_dtype);
+    if (t < 1 || i < 0 || i >= t)
+      return fail(TP_ERR_SHARD, "tp_ffn_shard: shard i=%d of t=%d", i, t);
+    if (tokens < 0 || hidden <= 0 || ffn <= 0)
+      return fail(TP_ERR_SHAPE, "tp_ffn_shard(i=%d): tokens=%lld hidden=%lld ffn=%lld", i,
+                  (long long)tokens, (long long)hidden, (long long)ffn);
+    if (ffn % t != 0)
+      return fail(TP_ERR_DIVISIBILITY, "tp_ffn_shard(i=%d): ffn=%lld not divisible by t=%d", i,
+                  (long long)ffn, t);
+    const int64_t fs = ffn / t;
+    const int64_t es = esize(in_dtype);
+    const int64_t vec = 16 / es;
+    if (ld_w1 == 0) ld_w1 = fs;
+    if (hidden % vec || fs % vec || ld_w1 % vec || ld_w1 < fs)
+      return fail(TP_ERR_SHAPE,
+                  "tp_ffn_shard(i=%d): hidden=%lld, ffn/t=%lld and ld_w1=%lld must be multiples "
+                  "of %lld with ld_w1 >= ffn/t",
+                  i, (long long)hidden, (long long)fs, (long long)ld_w1, (long long)vec);
+    if (tokens > kInt32Max || hidden > kInt32Max || fs > kInt32Max)
+      return fail(TP_ERR_SHAPE, "tp_ffn_shard(i=%d): a dimension exceeds 2^31-1", i);
+    if (tokens == 0) return ok();
+    if (!X || !W1_i || !W2_i || !Y_i)
+      return fail(TP_ERR_NULL, "tp_ffn_shard(i=%d): NULL tensor pointer", i);
+    if (!workspace)
+      return fail(TP_ERR_WORKSPACE, "tp_ffn_shard(i=%d): NULL workspace", i);
+    if (!aligned16(X) || !aligned16(W1_i) || !aligned16(W2_i) || !aligned16(Y_i) ||
+        !aligned16(workspace))
+      return fail(TP_ERR_ALIGNMENT, "tp_ffn_shard(i=%d): pointers must be 16-byte aligned", i);
+    const size_t need = tp_ffn_shard_workspace_bytes(tokens, hidden, ffn, t, in_dtype);
+    if (workspace_bytes < need)
+      return fail(TP_ERR_WORKSPACE, "tp_ffn_shard(i=%d): workspace %zu bytes < %zu needed", i,
+                  workspace_bytes, need);
+    const Range rx = range_of(X, tokens * hidden * es);
+    const Range rw1 = range_of(W1_i, span_bytes(hidden, fs, ld_w1, es));
+    const Range rw2 = range_of(W2_i, fs * hidden * es);
+    const Range ry = range_of(Y_i, tokens * hidden * esize(out_dtype));
+    const Range rws = range_of(workspace, tokens * fs * es);
+    if (overlap(ry, rx) || overlap(ry, rw1) || overlap(ry, rw2) || overlap(ry, rws))
+      return fail(TP_ERR_ALIAS, "tp_ffn_shard(i=%d): Y_i overlaps an input or the workspace", i);
+    if (overlap(rws, rx) || overlap(rws, rw1) || overlap(rws, rw2))
+      return fail(TP_ERR_ALIAS, "tp_ffn_shard(i=%d): workspace overlaps an input", i);
+
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    (void)hipGetLastError();
+    const int M = (int)tokens, H = (int)hidden, F = (int)fs;
+    hipError_t e;
+    if (in_dtype == TP_BF16) {
+      uint16_t* zh = static_cast<uint16_t*>(workspace);
+      e = tp::gemm_bf16_gelu(static_cast<const uint16_t*>(X), H,
+                             static_cast<const uint16_t*>(W1_i), ld_w1, zh, F, M, F, H, s);
+      if (e != hipSuccess) return hip_status(e, "tp_ffn_shard: GEMM1 launch");
+      e = tp::gemm_bf16_store(zh, F, static_cast<const uint16_t*>(W2_i), H, Y_i, H,
+                              out_dtype == TP_F32 ? tp::OUT_F32 : tp::OUT_BF16, M, H, F, s);
+      if (e != hipSuccess) return hip_status(e, "tp_ffn_shard: GEMM2 launch");
+    } else {
+      float* zh = static_cast<float*>(workspace);
+      e = tp::gemm_f32(static_cast<const float*>(X), H, static_cast<const float*>(W1_i), ld_w1,
+                       zh, F, tp::OUT_F32, true, M, F, H, s);
+      if (e != hipSuccess) return hip_status(e, "tp_ffn_shard: GEMM1 launch");
+      e = tp::gemm_f32(zh, F, static_cast<const float*>(W2_i), H, Y_i, H,
+                       out_dtype == TP_F32 ? tp::OUT_F32 : tp::OUT_BF16, false, M, H, F, s);
+      if (e != hipSuccess) return hip_status(e, "tp_ffn_shard: GEMM2 launch");
+    }
+    return ok();
+  } catch (...) {
+    return fail(TP_ERR_HIP, "tp_ffn_shard: internal exception");
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Attention shard
+// ---------------------------------------------------------------------------
+size_t tp_attn_shard_workspace_bytes(int64_t batch, int64_t seq, int32_t n_heads,
+                                     int32_t head_dim, int32_t t) {
+  if (batch < 0 || seq < 0 || n_heads < 1 || head_dim < 1 || t < 1 || n_heads % t) return 0;
+  return (size_t)attn_layout(batch, seq, n_heads / t, head_dim).total;
+}
+
+tp_status_t tp_attn_shard(const void* X, const void* Wqkv_i, const void* Wo_i,
+                          void* Y_i, int64_t batch, int64_t seq, int64_t hidden,
+                          int32_t n_heads, int32_t head_dim, int32_t i,
+                          int32_t t, int32_t causal, int32_t in_dtype,
+                          int32_t out_dtype, void* workspace,
+                          size_t workspace_bytes, void* stream) {
+  try {
+    if (!valid_dtype(in_dtype) || !valid_dtype(out_dtype))
+      return fail(TP_ERR_DTYPE, "tp_attn_shard: dtype codes in=%d out=%d", in_dtype, out_dtype);
+    if (in_dtype != TP_BF16)
+      return fail(TP_ERR_UNSUPPORTED, "tp_attn_shard: only bf16 inputs are implemented");
+    if (t < 1 || i < 0 || i >= t)
+      return fail(TP_ERR_SHARD, "tp_attn_shard: shard i=%d of t=%d", i, t);
+    if (batch < 0 || seq < 0 || hidden <= 0 || n_heads < 1 || head_dim < 1 ||
+        (causal != 0 && causal != 1))
+      return fail(TP_ERR_SHAPE,
+                  "tp_attn_shard(i=%d): batch=%lld seq=%lld hidden=%lld n_heads=%d head_dim=%d "
+                  "causal=%d",
+                  i, (long long)batch, (long long)seq, (long long)hidden, n_heads, head_dim,
+                  causal);
+    if (n_heads % t != 0)
+      return fail(TP_ERR_DIVISIBILITY, "tp_attn_shard(i=%d): n_heads=%d not divisible by t=%d",
+                  i, n_heads, t);
+    if (head_dim != kAttnHeadDim)
+      return fail(TP_ERR_UNSUPPORTED, "tp_attn_shard(i=%d): head_dim=%d (only 128)", i, head_dim);
+    if (hidden % 8 != 0)
+      return fail(TP_ERR_SHAPE, "tp_attn_shard(i=%d): hidden=%lld must be a multiple of 8", i,
+                  (long long)hidden);
+    const int64_t nl = n_heads / t;
+    const int64_t tokens = batch * seq;
+    if (tokens > kInt32Max || hidden > kInt32Max || 3 * nl * head_dim > kInt32Max ||
+        batch * nl * ((seq + 63) / 64) > kInt32Max)
+      return fail(TP_ERR_SHAPE, "tp_attn_shard(i=%d): a dimension exceeds 2^31-1", i);
+    if (tokens == 0) return ok();
+    if (!X || !Wqkv_i || !Wo_i || !Y_i)
+      return fail(TP_ERR_NULL, "tp_attn_shard(i=%d): NULL tensor pointer", i);
+    if (!workspace) return fail(TP_ERR_WORKSPACE, "tp_attn_shard(i=%d): NULL workspace", i);
+    if (!aligned16(X) || !aligned16(Wqkv_i) || !aligned16(Wo_i) || !aligned16(Y_i) ||
+        !aligned16(workspace))
+      return fail(TP_ERR_ALIGNMENT, "tp_attn_shard(i=%d): pointers must be 16-byte aligned", i);
+    const AttnLayout L = attn_layout(batch, seq, nl, head_dim);
+    if (workspace_bytes < (size_t)L.total)
+      return fail(TP_ERR_WORKSPACE, "tp_attn_shard(i=%d): workspace %zu bytes < %lld needed", i,
+                  workspace_bytes, (long long)L.total);
+    const int64_t nqkv = 3 * nl * head_dim;
+    const Range rx = range_of(X, tokens * hidden * 2);
+    const Range rq = range_of(Wqkv_i, hidden * nqkv * 2);
+    const Range ro = range_of(Wo_i, nl * head_dim * hidden * 2);
+    const Range ry = range_of(Y_i, tokens * hidden * esize(out_dtype));
+    const Range rws = range_of(workspace, L.total);
+    if (overlap(ry, rx) || overlap(ry, rq) || overlap(ry, ro) || overlap(ry, rws))
+      return fail(TP_ERR_ALIAS, "tp_attn_shard(i=%d): Y_i overlaps an input or the workspace", i);
+    if (overlap(rws, rx) || overlap(rws, rq) || overlap(rws, ro))
+      return fail(TP_ERR_ALIAS, "tp_attn_shard(i=%d): workspace overlaps an input", i);
+
+    uint8_t* ws = static_cast<uint8_t*>(workspace);
+    tp::QkvOut q;
+    q.q_hi = reinterpret_cast<uint16_t*>(ws + 0 * L.part_bytes);
+    q.q_lo = reinterpret_cast<uint16_t*>(ws + 1 * L.part_bytes);
+    q.k_hi = reinterpret_cast<uint16_t*>(ws + 2 * L.part_bytes);
+    q.k_lo = reinterpret_cast<uint16_t*>(ws + 3 * L.part_bytes);
+    q.vt_hi = reinterpret_cast<uint16_t*>(ws + 4 * L.part_bytes);
+    q.vt_lo = reinterpret_cast<uint16_t*>(ws + 5 * L.part_bytes);
+    q.seq = (int32_t)seq;
+    q.seq_pad = (int32_t)L.seq_pad;
+    q.nl = (int32_t)nl;
+    q.d = head_dim;
+    uint16_t* O = reinterpret_cast<uint16_t*>(ws + 6 * L.part_bytes);
+
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    (void)hipGetLastError();
+    hipError_t e = tp::gemm_bf16_qkv(static_cast<const uint16_t*>(X), hidden,
+                                     static_cast<const uint16_t*>(Wqkv_i), nqkv, q,
+                                     (int)tokens, (int)nqkv, (int)hidden, s);
+    if (e != hipSuccess) return hip_status(e, "tp_attn_shard: QKV launch");
+    e = tp::attention_fwd(q, (int)batch, causal != 0, O, s);
+    if (e != hipSuccess) return hip_status(e, "tp_attn_shard: attention launch");
+    e = tp::gemm_bf16_store_split_a(O, 2 * nl * head_dim, static_cast<const uint16_t*>(Wo_i),
+                                    hidden, Y_i, hidden,
+                                    out_dtype == TP_F32 ? tp::OUT_F32 : tp::OUT_BF16,
+                                    (int)tokens, (int)hidden, (int)(nl * head_dim), s);
+    if (e != hipSuccess) return hip_status(e, "tp_attn_shard: output projection launch");
+    return ok();
+  } catch (...) {
+    return fail(TP_ERR_HIP, "tp_attn_shard: internal exception");
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Partial reduce
+// ---------------------------------------------------------------------------
+tp_status_t tp_partial_reduce(const void* const* partials, int32_t t,
+                              const void* residual, void* out, int64_t rows,
+                              int64_t cols, int32_t partial_dtype,
+                              int32_t residual_dtype, int32_t out_dtype,
+                              void* stream) {
+  try {
+    if (!valid_dtype(partial_dtype) || !valid_dtype(out_dtype) ||
+        (residual && !valid_dtype(residual_dtype)))
+      return fail(TP_ERR_DTYPE, "tp_partial_reduce: dtype codes p=%d r=%d o=%d", partial_dtype,
+                  residual_dtype, out_dtype);
+    if (t < 1 || t > TP_MAX_PARTIALS)
+      return fail(TP_ERR_SHARD, "tp_partial_reduce: t=%d outside [1, %d]", t, TP_MAX_PARTIALS);
+    if (rows < 0 || cols < 0 || cols % 8 != 0)
+      return fail(TP_ERR_SHAPE, "tp_partial_reduce: rows=%lld cols=%lld (cols multiple of 8)",
+                  (long long)rows, (long long)cols);
+    const int64_t n = rows * cols;
+    if (n == 0) return ok();
+    if (!partials || !out) return fail(TP_ERR_NULL, "tp_partial_reduce: NULL pointer");
+    tp::ReducePtrs ptrs;
+    for (int k = 0; k < t; ++k) {
+      if (!partials[k]) return fail(TP_ERR_NULL, "tp_partial_reduce: partials[%d] is NULL", k);
+      if (!aligned16(partials[k]))
+        return fail(TP_ERR_ALIGNMENT, "tp_partial_reduce: partials[%d] not 16-byte aligned", k);
+      ptrs.p[k] = partials[k];
+    }
+    for (int k = t; k < TP_MAX_PARTIALS; ++k) ptrs.p[k] = nullptr;
+    if (!aligned16(out) || (residual && !aligned16(residual)))
+      return fail(TP_ERR_ALIGNMENT, "tp_partial_reduce: pointers must be 16-byte aligned");
+    // out may be exactly one of the inputs (same address, same element size):
+    // every element group is read in full by the thread that writes it.
+    const int64_t ob = esize(out_dtype);
+    const Range ro = range_of(out, n * ob);
+    for (int k = 0; k < t; ++k) {
+      const int64_t pb = esize(partial_dtype);
+      if (overlap(ro, range_of(partials[k], n * pb)) && !(partials[k] == out && pb == ob))
+        return fail(TP_ERR_ALIAS, "tp_partial_reduce: out overlaps partials[%d]", k);
+    }
+    if (residual) {
+      const int64_t rb = esize(residual_dtype);
+      if (overlap(ro, range_of(residual, n * rb)) && !(residual == out && rb == ob))
+        return fail(TP_ERR_ALIAS, "tp_partial_reduce: out overlaps the residual");
+    }
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    (void)hipGetLastError();
+    const hipError_t e = tp::partial_reduce(ptrs, t, partial_dtype, residual, residual_dtype,
+                                            out, out_dtype, n, s);
+    return hip_status(e, "tp_partial_reduce: launch");
+  } catch (...) {
+    return fail(TP_ERR_HIP, "tp_partial_reduce: internal exception");
+  }
+}
+
+}  // extern "C"

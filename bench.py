@@ -1,0 +1,297 @@
+#!/usr/bin/env python3
+"""Throughput of one GPU's share of a tensor-parallel FFN sub-layer on MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+                    [--sweep OUT.jsonl]
+
+Workload (one "step"): FFN shard i=3 of t=8 at hidden 4096, ffn 16384,
+4096 tokens (2 sequences of 2048), bf16 inputs with fp32 accumulation:
+  1. tp_ffn_shard: Z_3 = X W1_3 (W1_3 a zero-copy column view of the full W1),
+     GeLU in the epilogue, Y_3 = GeLU(Z_3) W2_3 -> bf16 partial;
+  2. tp_partial_reduce: out = sum of the 8 partials + residual (fp32 out).
+     The other seven partials are the other shards' results, computed once
+     before timing: they stand for what the peers would contribute.
+value = algorithmic FFN FLOPs of the shard (4*M*h*f/t) / wall time per step.
+
+The same run also times the attention shard (t=8, 8 of 64 heads of 128,
+hidden 8192, 2048 tokens, causal) and reports it under "rows", and, on rank 0
+at N=1, times the fp64 CPU oracle on a bounded sample of the FFN workload
+("cpu_baseline").  Prints ONE JSON line.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2516.6     # MI355X dense bf16 MFMA (256 CU x 2.4 GHz x 4096 FLOP/clk)
+PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
+METRIC = "TP-shard FFN TFLOP/s vs hidden size (bf16, 1 GPU); % of MFMA peak"
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_ffn_shard_h4096_t8.json")
+
+FFN = dict(tokens=4096, hidden=4096, ffn=16384, t=8, i=3, seed=2)
+ATTN = dict(batch=1, seq=2048, hidden=8192, n_heads=64, head_dim=128, t=8, i=0, seed=4)
+
+
+def ffn_flops(M, h, f, t):
+    return 4.0 * M * h * f / t
+
+
+def attn_flops(batch, seq, hidden, n_heads, head_dim, t):
+    nl = n_heads // t
+    S = seq
+    qkv = 2.0 * batch * S * hidden * 3 * nl * head_dim
+    core = 4.0 * head_dim * (S * (S + 1) / 2) * nl * batch      # causal pairs only
+    out = 2.0 * batch * S * nl * head_dim * hidden
+    return qkv + core + out
+
+
+def src_hash(*names):
+    h = hashlib.sha256()
+    for n in names:
+        with open(os.path.join(ROOT, "attention_shards_amd", "csrc", n), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def load_traffic():
+    """HBM bytes per FFN-shard call from the committed rocprofv3 counter runs,
+    or None when the kernels changed since those counters were taken."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if rec.get("kernel_source_sha") != src_hash("gemm.hip"):
+        return None
+    return rec.get("traffic_bytes")
+
+
+def dev_tensor(np_arr, dtype):
+    import numpy as np
+    import torch
+    from attention_shards_amd import synthetic as syn
+    if dtype == syn.BF16:
+        return torch.from_numpy(np.ascontiguousarray(np_arr).view(np.int16)).view(torch.bfloat16).cuda()
+    return torch.from_numpy(np.ascontiguousarray(np_arr)).cuda()
+
+
+def time_events(fn, steps, warmup):
+    import torch
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(steps)]
+    for a, b in ev:
+        a.record()
+        fn()
+        b.record()
+    torch.cuda.synchronize()
+    return sum(a.elapsed_time(b) for a, b in ev) / steps
+
+
+def cpu_baseline(d, budget_s=12.0):
+    """fp64 oracle on a bounded row sample of the FFN shard workload."""
+    import numpy as np
+    import oracle
+    from attention_shards_amd import synthetic as syn
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max((i.get("num_threads", 1) for i in threadpool_info()), default=1)
+    except Exception:
+        cores = 1
+    p = FFN
+    cols = syn.column_slice(p["ffn"], p["i"], p["t"])
+    W1_i = syn.to_f64(d["W1"][:, cols], syn.BF16)
+    W2_i = syn.to_f64(d["W2"][cols, :], syn.BF16)
+    rows_done, block = 0, 256
+    t0 = time.perf_counter()
+    while rows_done < p["tokens"] and time.perf_counter() - t0 < budget_s:
+        Xb = syn.to_f64(d["X"][rows_done:rows_done + block], syn.BF16)
+        oracle.ffn_shard(Xb, W1_i, W2_i)
+        rows_done += Xb.shape[0]
+    dt = time.perf_counter() - t0
+    fl = ffn_flops(rows_done, p["hidden"], p["ffn"], p["t"])
+    return {"value": round(fl / dt / 1e12, 5), "unit": "TFLOP/s", "cores": int(cores),
+            "kind": "oracle",
+            "sample": f"{rows_done} of {p['tokens']} token rows of the FFN shard "
+                      f"(fp64 numpy, {dt:.1f} s)"}
+
+
+def sweep(path, steps, warmup):
+    """Hidden-size sweep h = 2048..22528 step 2048, t in {1,2,4,8}, 2048 tokens.
+    Timing only (device-seeded inputs); parity of sweep points is in tests."""
+    import torch
+    from attention_shards_amd import binding as B
+    g = torch.Generator(device="cuda")
+    with open(path, "w") as out:
+        for h in range(2048, 22528 + 1, 2048):
+            g.manual_seed(300 + h // 2048)
+            f = 4 * h
+            X = torch.randn(2048, h, device="cuda", generator=g).to(torch.bfloat16)
+            for t in (1, 2, 4, 8):
+                fs = f // t
+                W1 = (torch.randn(h, fs, device="cuda", generator=g) * 0.02).to(torch.bfloat16)
+                W2 = (torch.randn(fs, h, device="cuda", generator=g) * 0.02).to(torch.bfloat16)
+                Y = torch.empty(2048, h, device="cuda")
+                ws = torch.empty(B.tp_ffn_shard_workspace_bytes(2048, h, f, t, B.TP_BF16),
+                                 dtype=torch.uint8, device="cuda")
+                ms = time_events(lambda: B.tp_ffn_shard(X, W1, W2, Y, 0, t, workspace=ws),
+                                 steps, warmup)
+                tf = ffn_flops(2048, h, f, t) / (ms * 1e-3) / 1e12
+                rec = {"hidden": h, "t": t, "ms": round(ms, 5), "tflops": round(tf, 2),
+                       "frac_peak": round(tf / PEAK_BF16_TFLOPS, 4)}
+                out.write(json.dumps(rec) + "\n")
+                print(json.dumps(rec), file=sys.stderr, flush=True)
+                del W1, W2, Y, ws
+            del X
+            torch.cuda.empty_cache()
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--sweep", metavar="OUT_JSONL", default=None)
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU's shard only: this library runs on a single "
+              "GPU and has no multi-GPU path; run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+    from attention_shards_amd import binding as B
+    from attention_shards_amd import synthetic as syn
+    B.load()
+    if not torch.cuda.is_available():
+        print("no GPU visible", file=sys.stderr)
+        sys.exit(1)
+
+    if args.sweep:
+        sweep(args.sweep, max(5, args.steps // 5), 3)
+
+    # ---------------- FFN sub-layer step ----------------
+    p = FFN
+    M, h, f, t, i = p["tokens"], p["hidden"], p["ffn"], p["t"], p["i"]
+    fs = f // t
+    d = syn.make_ffn_inputs(p["seed"], M, h, f, syn.BF16, residual=True)
+    X = dev_tensor(d["X"], syn.BF16)
+    W1 = dev_tensor(d["W1"], syn.BF16)
+    W2 = dev_tensor(d["W2"], syn.BF16)
+    R = dev_tensor(d["R"], syn.BF16)
+    parts = [torch.empty(M, h, dtype=torch.bfloat16, device="cuda") for _ in range(t)]
+    ws = torch.empty(B.tp_ffn_shard_workspace_bytes(M, h, f, t, B.TP_BF16),
+                     dtype=torch.uint8, device="cuda")
+    out = torch.empty(M, h, dtype=torch.float32, device="cuda")
+    W1v = [W1[:, j * fs:(j + 1) * fs] for j in range(t)]
+    W2v = [W2[j * fs:(j + 1) * fs] for j in range(t)]
+    for j in range(t):                      # the peers' partials, once
+        B.tp_ffn_shard(X, W1v[j], W2v[j], parts[j], j, t, workspace=ws)
+    torch.cuda.synchronize()
+
+    def ffn():
+        B.tp_ffn_shard(X, W1v[i], W2v[i], parts[i], i, t, workspace=ws)
+
+    def red():
+        B.tp_partial_reduce(parts, R, out)
+
+    for _ in range(args.warmup):
+        ffn()
+        red()
+    torch.cuda.synchronize()
+    ev = [tuple(torch.cuda.Event(enable_timing=True) for _ in range(3))
+          for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for e0, e1, e2 in ev:
+        e0.record()
+        ffn()
+        e1.record()
+        red()
+        e2.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_step = wall / args.steps * 1e3
+    ffn_ms = sum(a.elapsed_time(b) for a, b, _ in ev) / args.steps
+    red_ms = sum(b.elapsed_time(c) for _, b, c in ev) / args.steps
+    fl = ffn_flops(M, h, f, t)
+    value = fl / (ms_step * 1e-3) / 1e12
+    ffn_tf = fl / (ffn_ms * 1e-3) / 1e12
+    red_bytes = (t * 2 + 2 + 4) * M * h
+    red_gbs = red_bytes / (red_ms * 1e-3) / 1e9
+    del parts, W1v, W2v, W1, W2, ws, out
+    torch.cuda.empty_cache()
+
+    # ---------------- attention shard ----------------
+    a = ATTN
+    ad = syn.make_attn_inputs(a["seed"], a["batch"], a["seq"], a["hidden"], a["n_heads"],
+                              a["head_dim"])
+    nl = a["n_heads"] // a["t"]
+    Xa = dev_tensor(ad["X"], syn.BF16)
+    Wqkv = dev_tensor(syn.qkv_held_shard(ad["WQ"], ad["WK"], ad["WV"], a["n_heads"],
+                                         a["head_dim"], a["i"], a["t"]), syn.BF16)
+    Wo = dev_tensor(np.ascontiguousarray(
+        ad["WO"][syn.head_slice(a["n_heads"], a["head_dim"], a["i"], a["t"]), :]), syn.BF16)
+    Ya = torch.empty(a["batch"] * a["seq"], a["hidden"], dtype=torch.float32, device="cuda")
+    wsa = torch.empty(B.tp_attn_shard_workspace_bytes(a["batch"], a["seq"], a["n_heads"],
+                                                      a["head_dim"], a["t"]),
+                      dtype=torch.uint8, device="cuda")
+    attn_ms = time_events(lambda: B.tp_attn_shard(Xa, Wqkv, Wo, Ya, a["batch"], a["seq"],
+                                                  a["n_heads"], a["head_dim"], a["i"], a["t"],
+                                                  True, workspace=wsa),
+                          args.steps, args.warmup)
+    afl = attn_flops(a["batch"], a["seq"], a["hidden"], a["n_heads"], a["head_dim"], a["t"])
+    attn_tf = afl / (attn_ms * 1e-3) / 1e12
+    del ad
+
+    traffic = load_traffic()
+    res = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded PCG64 normals: activations N(0,1), weights N(0,0.02^2))",
+        "config": {"workload": "ffn_shard_t8_i3_h4096_f16384_tokens4096_plus_reduce8",
+                   "tokens": M, "hidden": h, "ffn": f, "t": t, "i": i,
+                   "partial_dtype": "bf16", "reduce_out_dtype": "f32"},
+        "roofline": {"bound": "mfma", "kernel": "tp_ffn_shard (GEMM1+GeLU, GEMM2)",
+                     "achieved": round(ffn_tf, 2), "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(ffn_tf / PEAK_BF16_TFLOPS, 4),
+                     "traffic": traffic, "per_launch_flop": fl,
+                     "avg_launch_ms": round(ffn_ms, 5)},
+        "rows": {
+            "ffn_shard": {"ms": round(ffn_ms, 5), "tflops": round(ffn_tf, 2),
+                          "frac_peak": round(ffn_tf / PEAK_BF16_TFLOPS, 4)},
+            "partial_reduce": {"ms": round(red_ms, 5), "bytes": red_bytes,
+                               "gbs": round(red_gbs, 1),
+                               "frac_hbm_peak": round(red_gbs / PEAK_HBM_GBS, 4),
+                               "bound": "hbm"},
+            "attn_shard": {"workload": "t8_i0_h8192_64x128heads_seq2048_causal",
+                           "ms": round(attn_ms, 5), "flop": afl,
+                           "tflops": round(attn_tf, 2),
+                           "frac_peak": round(attn_tf / PEAK_BF16_TFLOPS, 4)},
+        },
+    }
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline(d)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

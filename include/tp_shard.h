@@ -1,0 +1,185 @@
+/*
+ * tp_shard.h -- C ABI of libtpshard.so: one GPU's share of a Megatron-style
+ * tensor-parallel transformer sub-layer, on AMD Instinct MI355X (gfx950).
+ *
+ * The operations follow the page "Tensor Parallelism > Combining Column and
+ * Row Parallelism" (mbrenndoerfer.com):
+ *   - FFN, steps 1-2: GPU i receives the full input X, computes
+ *     Z_i = X W_{1,i} with its column shard of W1, applies GeLU locally, and
+ *     multiplies by its row shard W_{2,i}, which gives a partial sum Y_i over
+ *     the full output space                                 -> tp_ffn_shard
+ *   - attention: QKV projections split by heads (each GPU holds the Q, K, V
+ *     weights of its heads), per-head attention, and the row-parallel output
+ *     projection, again a partial sum                       -> tp_attn_shard
+ *   - FFN step 3 and the closing paragraph: the partials are summed and the
+ *     residual is added to the sum                          -> tp_partial_reduce
+ *     (here an in-HBM sum of t buffers on one GPU, not a collective).
+ *
+ * Conventions shared by every entry point
+ *   - Pointers to tensors are DEVICE pointers owned by the caller; the library
+ *     never allocates, frees or copies them, and keeps no reference after the
+ *     call returns.  They must be 16-byte aligned (TP_ERR_ALIGNMENT).
+ *   - Matrices are dense row-major ("X W" orientation: X[M,h], W1[h,f],
+ *     W2[f,h]); only W1_i may be a strided view (ld_w1).
+ *   - bf16 is bfloat16 (1-8-7), fp32 is IEEE binary32.
+ *   - `stream` is a hipStream_t passed as void*; NULL means the null stream.
+ *     TP_SUCCESS means "work enqueued on stream": results are stream-ordered
+ *     and the caller synchronizes.
+ *   - All arguments are validated BEFORE any HIP call; on failure nothing is
+ *     enqueued, the status code is returned and tp_last_error_message()
+ *     gives a thread-local description.  No C++ exception crosses the ABI.
+ *   - Results are bitwise reproducible for the same inputs, shapes and
+ *     device: no atomics, fixed summation orders.
+ *   - Functions are re-entrant; calls on different streams may run
+ *     concurrently as long as their output buffers and workspaces differ.
+ */
+#ifndef TP_SHARD_H
+#define TP_SHARD_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define TP_ABI_VERSION 1
+#define TP_MAX_PARTIALS 64
+
+/* Element types of tensors crossing the ABI. */
+typedef enum {
+  TP_F32 = 0,  /* IEEE binary32 */
+  TP_BF16 = 1  /* bfloat16, stored as 16-bit words */
+} tp_dtype_t;
+
+typedef enum {
+  TP_SUCCESS = 0,
+  TP_ERR_NULL = 1,          /* a required pointer is NULL */
+  TP_ERR_SHAPE = 2,         /* negative size, or size not a multiple of the
+                               16-byte vector width along a contiguous dim */
+  TP_ERR_SHARD = 3,         /* t < 1, or i outside [0, t) */
+  TP_ERR_DIVISIBILITY = 4,  /* ffn % t != 0, or n_heads % t != 0 */
+  TP_ERR_DTYPE = 5,         /* unknown dtype code or unsupported combination */
+  TP_ERR_WORKSPACE = 6,     /* workspace NULL or smaller than the query says */
+  TP_ERR_ALIAS = 7,         /* an output overlaps an input it must not */
+  TP_ERR_HIP = 8,           /* a HIP call failed (text in the message) */
+  TP_ERR_UNSUPPORTED = 9,   /* valid but not implemented (e.g. head_dim) */
+  TP_ERR_ALIGNMENT = 10     /* pointer not 16-byte aligned */
+} tp_status_t;
+
+/* ------------------------------------------------------------------------
+ * FFN shard (column-parallel W1 + GeLU, then row-parallel W2).
+ * ------------------------------------------------------------------------
+ * Computes, for this GPU i of t,
+ *     Y_i = GeLU(X * W1_i) * W2_i
+ * with GeLU(z) = 0.5 z (1 + erf(z / sqrt 2)) (the exact erf form) applied in
+ * fp32 to the fp32-accumulated product, and no biases.
+ *
+ *   X     [tokens, hidden]          full input, replicated on every GPU
+ *   W1_i  [hidden, ffn/t]           columns [i*ffn/t, (i+1)*ffn/t) of W1;
+ *                                   row stride ld_w1 elements: pass 0 or ffn/t
+ *                                   for a held shard, ffn for a zero-copy view
+ *                                   into a full W1 (pointer W1 + i*ffn/t)
+ *   W2_i  [ffn/t, hidden]           rows [i*ffn/t, (i+1)*ffn/t) of W2,
+ *                                   contiguous (pointer W2 + i*(ffn/t)*hidden)
+ *   Y_i   [tokens, hidden]          output partial, dtype out_dtype
+ *   ffn                             the FULL f; this shard has ffn/t columns
+ *   in_dtype                        dtype of X, W1_i, W2_i: TP_BF16 (bf16 MFMA,
+ *                                   fp32 accumulation, GeLU(Z) rounded to bf16
+ *                                   between the GEMMs) or TP_F32 (fp32 MFMA,
+ *                                   GeLU(Z) kept in fp32)
+ *   out_dtype                       TP_BF16 or TP_F32 (rounded once, nearest-even)
+ *   workspace                       device scratch of at least
+ *                                   tp_ffn_shard_workspace_bytes(...) bytes; it
+ *                                   holds GeLU(Z_i) [tokens, ffn/t] between the
+ *                                   two GEMMs (no gather: step 2 reads it as is)
+ * Shape rules: tokens >= 0 (0 enqueues nothing); hidden and ffn/t multiples
+ * of 8 (bf16) or 4 (fp32); ld_w1 >= ffn/t and a multiple of the same.
+ * Y_i must not overlap X, W1_i, W2_i or the workspace (TP_ERR_ALIAS).
+ * The shard index i only selects which pointers the caller passes; it is
+ * validated and reported in error messages.
+ */
+size_t tp_ffn_shard_workspace_bytes(int64_t tokens, int64_t hidden, int64_t ffn,
+                                    int32_t t, int32_t in_dtype);
+
+tp_status_t tp_ffn_shard(const void* X, const void* W1_i, const void* W2_i,
+                         void* Y_i, int64_t tokens, int64_t hidden, int64_t ffn,
+                         int32_t i, int32_t t, int64_t ld_w1, int32_t in_dtype,
+                         int32_t out_dtype, void* workspace,
+                         size_t workspace_bytes, void* stream);
+
+/* ------------------------------------------------------------------------
+ * Attention shard (QKV column-parallel by heads, per-head attention,
+ * row-parallel output projection).
+ * ------------------------------------------------------------------------
+ * With nl = n_heads/t local heads of dimension d = head_dim:
+ *     [Q | K | V] = X * Wqkv_i
+ *     O_h = softmax(Q_h K_h^T / sqrt(d), keys j <= query s if causal) V_h
+ *     Y_i = [O_0 | ... | O_{nl-1}] * Wo_i
+ * Attention runs within each of the `batch` sequences of length `seq`.
+ *
+ *   X       [batch*seq, hidden]     bf16, full input
+ *   Wqkv_i  [hidden, 3*nl*d]        bf16, columns laid out [W_Q,i | W_K,i |
+ *                                   W_V,i], each head-major (local head j in
+ *                                   columns j*d .. j*d+d-1 of its block); the
+ *                                   heads are [i*nl, (i+1)*nl) of the model
+ *   Wo_i    [nl*d, hidden]          bf16, rows of those heads in W_o
+ *   Y_i     [batch*seq, hidden]     output partial, out_dtype TP_F32 or TP_BF16
+ *   causal                          1: key j is kept for query s iff j <= s;
+ *                                   0: all keys kept
+ *   in_dtype                        TP_BF16 only
+ * Internals (exposed only through the workspace size): Q and K are kept as
+ * bf16 hi+lo pairs (hi = bf16(v), lo = bf16(v - hi)) and V as an fp16 hi+lo
+ * pair, so the score and value products carry about 16 significant bits;
+ * softmax runs in fp32 with the probabilities rounded to fp16; the head
+ * outputs O are kept as a bf16 hi+lo pair, which the output projection
+ * multiplies by Wo_i in two passes.
+ * Shape rules: batch, seq >= 0; head_dim == 128; hidden multiple of 8.
+ */
+size_t tp_attn_shard_workspace_bytes(int64_t batch, int64_t seq, int32_t n_heads,
+                                     int32_t head_dim, int32_t t);
+
+tp_status_t tp_attn_shard(const void* X, const void* Wqkv_i, const void* Wo_i,
+                          void* Y_i, int64_t batch, int64_t seq, int64_t hidden,
+                          int32_t n_heads, int32_t head_dim, int32_t i,
+                          int32_t t, int32_t causal, int32_t in_dtype,
+                          int32_t out_dtype, void* workspace,
+                          size_t workspace_bytes, void* stream);
+
+/* ------------------------------------------------------------------------
+ * Sum of the t partials plus the residual (one-GPU stand-in for the
+ * all-reduce of FFN step 3, followed by the residual add).
+ * ------------------------------------------------------------------------
+ *     out = (partials[0] + partials[1] + ... + partials[t-1]) + residual
+ * accumulated in fp32 in that fixed order (i ascending, residual last) and
+ * rounded once to out_dtype.
+ *
+ *   partials   HOST array of t device pointers, each [rows, cols] of
+ *              partial_dtype; 1 <= t <= TP_MAX_PARTIALS
+ *   residual   device [rows, cols] of residual_dtype, or NULL for none
+ *   out        device [rows, cols] of out_dtype; it MAY be the same buffer as
+ *              residual or partials[0] when the dtypes match (each element is
+ *              read before it is written); any other overlap is TP_ERR_ALIAS
+ * Shape rules: rows, cols >= 0; cols a multiple of 8.
+ */
+tp_status_t tp_partial_reduce(const void* const* partials, int32_t t,
+                              const void* residual, void* out, int64_t rows,
+                              int64_t cols, int32_t partial_dtype,
+                              int32_t residual_dtype, int32_t out_dtype,
+                              void* stream);
+
+/* Static text for a status code ("TP_SUCCESS", ...). Never NULL. */
+const char* tp_status_string(int32_t status);
+
+/* Thread-local detail of the last non-success return on this thread ("" if
+ * none).  Valid until the next call into the library on the same thread. */
+const char* tp_last_error_message(void);
+
+/* TP_ABI_VERSION of the built library. */
+int32_t tp_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* TP_SHARD_H */

@@ -1,0 +1,205 @@
+"""C ABI checks that need no GPU: the library loads, exports every function
+the header declares, and rejects bad arguments before any HIP call.
+
+Pointers here are fake but aligned host integers; the library only compares
+them (null, alignment, overlap) and never dereferences or launches on a
+rejected call.  No call in this file reaches a kernel launch.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+from attention_shards_amd import binding as B
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "tp_shard.h")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(B.LIB_PATH),
+                                reason="libtpshard.so not built")
+
+
+def header_text():
+    with open(HEADER) as f:
+        return f.read()
+
+
+def declared_functions():
+    src = re.sub(r"/\*.*?\*/", "", header_text(), flags=re.S)
+    return sorted(set(re.findall(r"\b(tp_[a-z0-9_]+)\s*\(", src)))
+
+
+def enum_values():
+    return {m.group(1): int(m.group(2))
+            for m in re.finditer(r"\b(TP_(?:SUCCESS|ERR_[A-Z_]+))\s*=\s*(\d+)", header_text())}
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return B.load()
+
+
+def test_every_declared_function_is_exported(lib):
+    names = declared_functions()
+    assert set(names) == set(B.SIGNATURES), names
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_version_and_status_strings(lib):
+    v = int(re.search(r"#define TP_ABI_VERSION (\d+)", header_text()).group(1))
+    assert lib.tp_abi_version() == v
+    vals = enum_values()
+    assert len(vals) == 11
+    for name, code in vals.items():
+        assert lib.tp_status_string(code).decode() == name
+        assert B.STATUS[code] == name
+    assert lib.tp_status_string(999).decode() == "TP_ERR_UNKNOWN_STATUS"
+
+
+def test_workspace_queries(lib):
+    assert lib.tp_ffn_shard_workspace_bytes(4096, 4096, 16384, 8, B.TP_BF16) == 4096 * 2048 * 2
+    assert lib.tp_ffn_shard_workspace_bytes(128, 1024, 4096, 1, B.TP_F32) == 128 * 4096 * 4
+    assert lib.tp_ffn_shard_workspace_bytes(3, 8, 24, 3, B.TP_BF16) == 256   # 256-byte granule
+    assert lib.tp_ffn_shard_workspace_bytes(10, 8, 20, 3, B.TP_BF16) == 0    # t does not divide f
+    assert lib.tp_ffn_shard_workspace_bytes(10, 8, 16, 0, B.TP_BF16) == 0
+    # attention: 6 x [heads, seq_pad, 128] + O hi/lo [tokens, 2*nl*128], 16-bit
+    want = 6 * 8 * 2048 * 128 * 2 + 2048 * 2 * 1024 * 2
+    assert lib.tp_attn_shard_workspace_bytes(1, 2048, 64, 128, 8) == want
+    ragged = lib.tp_attn_shard_workspace_bytes(2, 100, 4, 128, 2)
+    assert ragged == 6 * 2 * 2 * 128 * 128 * 2 + 2 * 100 * 2 * 256 * 2
+    assert lib.tp_attn_shard_workspace_bytes(1, 8, 6, 128, 4) == 0
+
+
+# fake, 16-byte aligned, non-overlapping device addresses
+X, W1, W2, Y, WS = (0x10_0000_0000 * k for k in range(1, 6))
+
+
+def ffn(lib, **kw):
+    a = dict(X=X, W1=W1, W2=W2, Y=Y, tokens=64, hidden=64, ffn=256, i=0, t=2,
+             ld=0, din=B.TP_BF16, dout=B.TP_BF16, ws=WS, wsb=1 << 30, stream=None)
+    a.update(kw)
+    st = lib.tp_ffn_shard(a["X"], a["W1"], a["W2"], a["Y"], a["tokens"], a["hidden"],
+                          a["ffn"], a["i"], a["t"], a["ld"], a["din"], a["dout"],
+                          a["ws"], a["wsb"], a["stream"])
+    return st, lib.tp_last_error_message().decode()
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(din=7), "TP_ERR_DTYPE"),
+    (dict(dout=-1), "TP_ERR_DTYPE"),
+    (dict(i=2), "TP_ERR_SHARD"),
+    (dict(i=-1), "TP_ERR_SHARD"),
+    (dict(t=0), "TP_ERR_SHARD"),
+    (dict(tokens=-1), "TP_ERR_SHAPE"),
+    (dict(hidden=0), "TP_ERR_SHAPE"),
+    (dict(ffn=255), "TP_ERR_DIVISIBILITY"),
+    (dict(hidden=60), "TP_ERR_SHAPE"),              # not a multiple of 8 bf16
+    (dict(ffn=2 * 36), "TP_ERR_SHAPE"),             # f/t = 36
+    (dict(ld=100), "TP_ERR_SHAPE"),                 # ld_w1 < f/t
+    (dict(ld=132), "TP_ERR_SHAPE"),                 # ld_w1 not a multiple of 8
+    (dict(X=None), "TP_ERR_NULL"),
+    (dict(Y=None), "TP_ERR_NULL"),
+    (dict(ws=None), "TP_ERR_WORKSPACE"),
+    (dict(wsb=64 * 128 * 2 - 1), "TP_ERR_WORKSPACE"),
+    (dict(W2=W2 + 8), "TP_ERR_ALIGNMENT"),
+    (dict(Y=X + 64), "TP_ERR_ALIAS"),               # output inside X
+    (dict(Y=WS), "TP_ERR_ALIAS"),                   # output on the workspace
+    (dict(ws=W1 + 1024), "TP_ERR_ALIAS"),           # workspace inside W1_i
+])
+def test_ffn_rejects(lib, kw, code):
+    st, msg = ffn(lib, **kw)
+    assert B.STATUS[st] == code, msg
+    assert msg
+
+
+def test_ffn_error_message_names_shard(lib):
+    st, msg = ffn(lib, X=None, i=1)
+    assert B.STATUS[st] == "TP_ERR_NULL" and "i=1" in msg
+
+
+def test_ffn_fp32_vector_rule(lib):
+    # 68 % 4 == 0 passes the shape rule and stops at the (later) NULL check
+    st, _ = ffn(lib, din=B.TP_F32, hidden=68, ffn=2 * 68, X=None)
+    assert B.STATUS[st] == "TP_ERR_NULL"
+    st, _ = ffn(lib, din=B.TP_F32, hidden=66, ffn=2 * 68)
+    assert B.STATUS[st] == "TP_ERR_SHAPE"
+
+
+def test_ffn_zero_tokens_is_a_no_op(lib):
+    st, msg = ffn(lib, tokens=0, X=None, Y=None, ws=None)
+    assert st == 0, msg
+
+
+def attn(lib, **kw):
+    a = dict(X=X, Wqkv=W1, Wo=W2, Y=Y, batch=1, seq=128, hidden=256, nh=4, d=128,
+             i=0, t=2, causal=1, din=B.TP_BF16, dout=B.TP_F32, ws=WS, wsb=1 << 30)
+    a.update(kw)
+    st = lib.tp_attn_shard(a["X"], a["Wqkv"], a["Wo"], a["Y"], a["batch"], a["seq"],
+                           a["hidden"], a["nh"], a["d"], a["i"], a["t"], a["causal"],
+                           a["din"], a["dout"], a["ws"], a["wsb"], None)
+    return st, lib.tp_last_error_message().decode()
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(din=B.TP_F32), "TP_ERR_UNSUPPORTED"),
+    (dict(dout=3), "TP_ERR_DTYPE"),
+    (dict(i=5), "TP_ERR_SHARD"),
+    (dict(nh=6, t=4), "TP_ERR_DIVISIBILITY"),
+    (dict(d=64), "TP_ERR_UNSUPPORTED"),
+    (dict(hidden=250), "TP_ERR_SHAPE"),
+    (dict(causal=2), "TP_ERR_SHAPE"),
+    (dict(seq=-3), "TP_ERR_SHAPE"),
+    (dict(Wo=None), "TP_ERR_NULL"),
+    (dict(wsb=1000), "TP_ERR_WORKSPACE"),
+    (dict(Y=X), "TP_ERR_ALIAS"),
+    (dict(ws=X + 4096), "TP_ERR_ALIAS"),
+    (dict(X=X + 2), "TP_ERR_ALIGNMENT"),
+])
+def test_attn_rejects(lib, kw, code):
+    st, msg = attn(lib, **kw)
+    assert B.STATUS[st] == code, msg
+
+
+def test_attn_empty_is_a_no_op(lib):
+    assert attn(lib, seq=0, X=None)[0] == 0
+    assert attn(lib, batch=0, ws=None)[0] == 0
+
+
+def reduce_call(lib, parts, t=None, R=None, out=Y, rows=32, cols=64, pdt=B.TP_BF16,
+                rdt=B.TP_BF16, odt=B.TP_F32):
+    t = len(parts) if t is None else t
+    arr = (ctypes.c_void_p * max(1, len(parts)))(*parts) if parts else None
+    st = lib.tp_partial_reduce(arr, t, R, out, rows, cols, pdt, rdt, odt, None)
+    return st, lib.tp_last_error_message().decode()
+
+
+def test_reduce_rejects(lib):
+    P = [X, W1, W2]
+    assert B.STATUS[reduce_call(lib, P, t=0)[0]] == "TP_ERR_SHARD"
+    assert B.STATUS[reduce_call(lib, P * 22, t=65)[0]] == "TP_ERR_SHARD"
+    assert B.STATUS[reduce_call(lib, P, cols=60)[0]] == "TP_ERR_SHAPE"
+    assert B.STATUS[reduce_call(lib, P, rows=-1)[0]] == "TP_ERR_SHAPE"
+    assert B.STATUS[reduce_call(lib, P, pdt=9)[0]] == "TP_ERR_DTYPE"
+    assert B.STATUS[reduce_call(lib, P, R=WS, rdt=4)[0]] == "TP_ERR_DTYPE"
+    assert B.STATUS[reduce_call(lib, [X, 0, W2])[0]] == "TP_ERR_NULL"
+    assert B.STATUS[reduce_call(lib, P, out=None)[0]] == "TP_ERR_NULL"
+    assert B.STATUS[reduce_call(lib, [X, W1 + 4])[0]] == "TP_ERR_ALIGNMENT"
+    # out overlapping a partial without being exactly it
+    assert B.STATUS[reduce_call(lib, [X, W1], out=W1 + 256)[0]] == "TP_ERR_ALIAS"
+    # same address but different element size (bf16 partial, fp32 out)
+    assert B.STATUS[reduce_call(lib, [X, W1], out=W1)[0]] == "TP_ERR_ALIAS"
+    assert B.STATUS[reduce_call(lib, [X], R=WS, out=WS + 16)[0]] == "TP_ERR_ALIAS"
+
+
+def test_reduce_empty_is_a_no_op(lib):
+    assert reduce_call(lib, [X, W1], rows=0)[0] == 0
+    assert reduce_call(lib, [X, W1], cols=0, out=None)[0] == 0
+
+
+def test_missing_library_fails_loudly(monkeypatch):
+    monkeypatch.setattr(B, "LIB_PATH", "/nonexistent/libtpshard.so")
+    monkeypatch.setattr(B, "_lib", None)
+    with pytest.raises(RuntimeError, match="not built"):
+        B.load()

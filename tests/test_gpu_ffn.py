@@ -1,0 +1,181 @@
+"""GPU parity of tp_ffn_shard (through the C ABI) against the fp64 oracle.
+
+Shapes: the FFN configurations of the workload (t=1 fp32; t=8 shard 3 at
+hidden 4096; points of the hidden-size sweep; the t=4 layer emulation at
+hidden 12288) plus ragged shapes that leave partial tiles on every edge.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from attention_shards_amd import synthetic as syn
+from parity import TOL_BF16, TOL_F32, bf16_floor, empty, from_dev, log, rel_err, to_dev
+
+pytestmark = pytest.mark.gpu
+
+
+def run_shard(gpu, d, i, t, out_dtype, view=True):
+    """Run shard i of t on the GPU; W1_i is a zero-copy column view of the
+    full W1 when view=True, a held (contiguous) shard otherwise."""
+    dt = d["dtype"]
+    f = d["W1"].shape[1]
+    cols = syn.column_slice(f, i, t)
+    X = to_dev(d["X"], dt)
+    if view:
+        W1 = to_dev(d["W1"], dt)
+        W1_i = W1[:, cols]
+    else:
+        W1_i = to_dev(np.ascontiguousarray(d["W1"][:, cols]), dt)
+    W2_i = to_dev(np.ascontiguousarray(d["W2"][cols, :]), dt)
+    Y = empty((X.shape[0], X.shape[1]), out_dtype)
+    gpu.tp_ffn_shard(X, W1_i, W2_i, Y, i, t)
+    torch.cuda.synchronize()
+    return from_dev(Y)
+
+
+def oracle_shard(d, i, t, rows=None):
+    dt = d["dtype"]
+    f = d["W1"].shape[1]
+    cols = syn.column_slice(f, i, t)
+    X = d["X"] if rows is None else d["X"][rows]
+    return oracle.ffn_shard(syn.to_f64(X, dt), syn.to_f64(d["W1"][:, cols], dt),
+                            syn.to_f64(d["W2"][cols, :], dt))
+
+
+def test_fp32_t1_full(gpu):
+    """t=1, X[128,1024], W1[1024,4096], W2[4096,1024], all fp32, fp32 out."""
+    d = syn.make_ffn_inputs(1, 128, 1024, 4096, syn.F32)
+    got = run_shard(gpu, d, 0, 1, syn.F32)
+    ref = oracle_shard(d, 0, 1)
+    e = rel_err(got, ref)
+    log(f"fp32 t=1: err {e:.3e}")
+    assert e <= TOL_F32
+
+
+def test_bf16_t8_shard3_full(gpu):
+    """t=8, i=3, X[4096,4096], W1_3 = W1[:, 6144:8192] of W1[4096,16384]
+    (zero-copy view, row stride 16384), W2_3 = W2[6144:8192, :]; bf16 out.
+    Whole tensor compared."""
+    d = syn.make_ffn_inputs(2, 4096, 4096, 16384, syn.BF16)
+    got = run_shard(gpu, d, 3, 8, syn.BF16)
+    ref = oracle_shard(d, 3, 8)
+    e, fl = rel_err(got, ref), bf16_floor(ref)
+    log(f"bf16 t=8 i=3 hidden 4096: err {e:.4f} (bf16 output floor {fl:.4f})")
+    assert e <= TOL_BF16
+
+
+@pytest.mark.parametrize("M,h,f,t,i,out,view", [
+    (300, 200, 3 * 424, 3, 1, syn.BF16, True),
+    (300, 200, 3 * 424, 3, 2, syn.F32, False),
+    (1, 64, 2 * 64, 2, 1, syn.F32, True),
+    (257, 264, 520, 1, 0, syn.BF16, False),
+    (513, 1032, 4 * 392, 4, 3, syn.F32, True),
+])
+def test_bf16_ragged(gpu, M, h, f, t, i, out, view):
+    d = syn.make_ffn_inputs(100 + M, M, h, f, syn.BF16)
+    got = run_shard(gpu, d, i, t, out, view)
+    ref = oracle_shard(d, i, t)
+    e = rel_err(got, ref)
+    log(f"ragged bf16 M={M} h={h} f={f} t={t} i={i} out={out}: err {e:.4f}")
+    assert e <= TOL_BF16
+
+
+@pytest.mark.parametrize("M,h,f,t,i", [(77, 100, 2 * 52, 2, 1), (130, 36, 3 * 68, 3, 0)])
+def test_fp32_ragged(gpu, M, h, f, t, i):
+    d = syn.make_ffn_inputs(200 + M, M, h, f, syn.F32)
+    got = run_shard(gpu, d, i, t, syn.F32)
+    e = rel_err(got, oracle_shard(d, i, t))
+    log(f"ragged fp32 M={M} h={h} f={f}: err {e:.3e}")
+    assert e <= TOL_F32
+
+
+def test_zero_tokens(gpu):
+    X = torch.empty((0, 64), dtype=torch.bfloat16, device="cuda")
+    W1 = torch.zeros((64, 128), dtype=torch.bfloat16, device="cuda")
+    W2 = torch.zeros((128, 64), dtype=torch.bfloat16, device="cuda")
+    Y = torch.empty((0, 64), dtype=torch.float32, device="cuda")
+    gpu.tp_ffn_shard(X, W1, W2, Y, 0, 1)
+    torch.cuda.synchronize()
+
+
+def test_bad_arguments_raise(gpu):
+    X = torch.zeros((8, 64), dtype=torch.bfloat16, device="cuda")
+    W1 = torch.zeros((64, 128), dtype=torch.bfloat16, device="cuda")
+    W2 = torch.zeros((128, 64), dtype=torch.bfloat16, device="cuda")
+    ws = torch.empty(16, dtype=torch.uint8, device="cuda")
+    with pytest.raises(gpu.TPError, match="TP_ERR_WORKSPACE"):
+        gpu.tp_ffn_shard(X, W1, W2, torch.empty((8, 64), device="cuda"), 0, 1, workspace=ws)
+    with pytest.raises(gpu.TPError, match="TP_ERR_ALIAS"):
+        gpu.tp_ffn_shard(X, W1, W2, X, 0, 1)
+    with pytest.raises(gpu.TPError, match="TP_ERR_SHARD"):
+        gpu.tp_ffn_shard(X, W1, W2, torch.empty((8, 64), device="cuda"), 2, 2)
+
+
+def test_sweep_small_point_full(gpu):
+    """Sweep point hidden 2048, t=8: X[2048,2048], W1_0 = W1[:, :1024]."""
+    h = 2048
+    d = syn.make_ffn_inputs(300 + h // 2048, 2048, h, 4 * h, syn.BF16)
+    got = run_shard(gpu, d, 0, 8, syn.F32)
+    e = rel_err(got, oracle_shard(d, 0, 8))
+    log(f"sweep h={h} t=8: err {e:.4f}")
+    assert e <= TOL_BF16
+
+
+def test_sweep_largest_point_sampled_rows(gpu):
+    """Sweep point hidden 22528, t=1 (W1[22528, 90112]); 16 seeded rows
+    (including the first and last) against the oracle.  An output row depends
+    only on its own input row, so the sample is exact for those rows; the
+    oracle's sum over the ffn dimension is taken shard by shard (8 column
+    blocks), which the shard-sum identity makes equal to the unsharded FFN."""
+    h = 22528
+    seed = 300 + h // 2048
+    d = syn.make_ffn_inputs(seed, 2048, h, 4 * h, syn.BF16)
+    got = run_shard(gpu, d, 0, 1, syn.F32, view=False)
+    rows = syn.sample_rows(seed, 2048, 16)
+    ref = sum(oracle_shard(d, j, 8, rows) for j in range(8))
+    e = rel_err(got[rows], ref)
+    log(f"sweep h={h} t=1 (16 rows): err {e:.4f}")
+    assert e <= TOL_BF16
+
+
+def test_layer_emulation_t4(gpu):
+    """hidden 12288, ffn 49152, 8192 tokens, t=4: all four shard partials
+    computed one after another on this GPU from zero-copy views of the full
+    weights (bf16 partials), then summed with the residual (fp32 out).
+    256 seeded rows against the oracle, and every element against the GPU's
+    own unsharded (t=1) run plus the residual."""
+    M, h, f, t = 8192, 12288, 49152, 4
+    d = syn.make_ffn_inputs(5, M, h, f, syn.BF16, residual=True)
+    X = to_dev(d["X"], syn.BF16)
+    W1 = to_dev(d["W1"], syn.BF16)
+    W2 = to_dev(d["W2"], syn.BF16)
+    R = to_dev(d["R"], syn.BF16)
+    parts = [empty((M, h), syn.BF16) for _ in range(t)]
+    fs = f // t
+    for i in range(t):
+        gpu.tp_ffn_shard(X, W1[:, i * fs:(i + 1) * fs], W2[i * fs:(i + 1) * fs], parts[i], i, t)
+    out = empty((M, h), syn.F32)
+    gpu.tp_partial_reduce(parts, R, out)
+    full = empty((M, h), syn.F32)
+    gpu.tp_ffn_shard(X, W1, W2, full, 0, 1)
+    torch.cuda.synchronize()
+    del parts
+    rows = syn.sample_rows(5, M, 256)
+    got = from_dev(out[torch.from_numpy(rows).cuda()])
+    ref = oracle.partial_reduce([oracle_shard(d, i, t, rows) for i in range(t)],
+                                syn.to_f64(d["R"][rows], syn.BF16))
+    e = rel_err(got, ref)
+    log(f"layer emulation t=4 (256 rows): err {e:.4f}")
+    assert e <= TOL_BF16
+    full += R.float()
+    e2 = (out - full).abs().max().item() / full.pow(2).mean().sqrt().item()
+    log(f"layer emulation: sum of shards + R vs t=1 + R (all elements): {e2:.4f}")
+    assert e2 <= TOL_BF16
+
+
+def test_deterministic(gpu):
+    d = syn.make_ffn_inputs(7, 1000, 1024, 4096, syn.BF16)
+    a = run_shard(gpu, d, 1, 2, syn.BF16)
+    b = run_shard(gpu, d, 1, 2, syn.BF16)
+    assert np.array_equal(a, b)

@@ -1,0 +1,90 @@
+"""GPU parity of tp_partial_reduce (through the C ABI) against the oracle.
+
+Bound used for fp32 accumulation: each of the t additions (t-1 partials and
+the residual) rounds once to fp32, so per element
+    |gpu - exact| <= t * 2^-24 * sum_i |term_i|     (fp32 output)
+and a bf16 output adds one rounding of at most 2^-8 |exact| (unit roundoff
+of an 8-bit significand).
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from attention_shards_amd import synthetic as syn
+from parity import empty, from_dev, log, to_dev
+
+pytestmark = pytest.mark.gpu
+
+
+def check_bound(got, parts, R, out_dtype):
+    exact = oracle.partial_reduce(parts, R)
+    mag = sum(np.abs(p) for p in parts) + (np.abs(R) if R is not None else 0)
+    t = len(parts) + (1 if R is not None else 0)
+    bound = t * 2.0 ** -24 * mag
+    if out_dtype == syn.BF16:
+        bound = bound * (1 + 2.0 ** -8) + 2.0 ** -8 * np.abs(exact)
+    assert np.all(np.abs(got - exact) <= bound + 1e-300)
+
+
+@pytest.mark.parametrize("t,pdt,rdt,odt,rows,cols", [
+    (4, syn.BF16, syn.BF16, syn.F32, 333, 264),
+    (8, syn.BF16, syn.BF16, syn.BF16, 64, 4096),
+    (3, syn.F32, syn.F32, syn.F32, 17, 8),
+    (1, syn.F32, None, syn.BF16, 5, 1000 * 8),
+    (13, syn.F32, syn.BF16, syn.F32, 100, 72),
+])
+def test_reduce_random(gpu, t, pdt, rdt, odt, rows, cols):
+    parts_h = [syn.normal_tensor(900 + t, k, (rows, cols), 0.5, pdt) for k in range(t)]
+    R_h = syn.normal_tensor(900 + t, 99, (rows, cols), 1.0, rdt) if rdt else None
+    out = empty((rows, cols), odt)
+    gpu.tp_partial_reduce([to_dev(p, pdt) for p in parts_h],
+                          to_dev(R_h, rdt) if rdt else None, out)
+    torch.cuda.synchronize()
+    parts = [syn.to_f64(p, pdt) for p in parts_h]
+    R = syn.to_f64(R_h, rdt) if rdt else None
+    check_bound(from_dev(out), parts, R, odt)
+
+
+def test_reduce_small_integers_exact(gpu):
+    rng = np.random.default_rng(5)
+    parts = [rng.integers(-100, 100, size=(64, 64)).astype(np.float32) for _ in range(8)]
+    R = rng.integers(-100, 100, size=(64, 64)).astype(np.float32)
+    out = empty((64, 64), syn.F32)
+    gpu.tp_partial_reduce([to_dev(p, syn.F32) for p in parts], to_dev(R, syn.F32), out)
+    torch.cuda.synchronize()
+    assert np.array_equal(from_dev(out), oracle.partial_reduce(parts, R))
+
+
+def test_reduce_copy_and_in_place(gpu):
+    p = torch.randn(40, 64, device="cuda").to(torch.bfloat16)
+    out = torch.empty_like(p)
+    gpu.tp_partial_reduce([p], None, out)
+    torch.cuda.synchronize()
+    assert torch.equal(out, p)                      # t=1, no residual: copy
+    a = torch.randn(40, 64, device="cuda")
+    b = torch.randn(40, 64, device="cuda")
+    r = torch.randn(40, 64, device="cuda")
+    r0 = from_dev(r)
+    gpu.tp_partial_reduce([a, b], r, r)             # out is the residual
+    torch.cuda.synchronize()
+    check_bound(from_dev(r), [from_dev(a), from_dev(b)], r0, syn.F32)
+    a2 = a.clone()
+    gpu.tp_partial_reduce([a2, b], None, a2)        # out is partials[0]
+    torch.cuda.synchronize()
+    assert torch.equal(a2, a + b)
+
+
+def test_reduce_layer_shape_sampled(gpu):
+    """t=4 bf16 partials [8192, 12288] + bf16 residual -> fp32 out; 256 rows."""
+    rows, cols, t = 8192, 12288, 4
+    parts_h = [syn.normal_tensor(55, k, (rows, cols), 0.5, syn.BF16) for k in range(t)]
+    R_h = syn.normal_tensor(55, 9, (rows, cols), 1.0, syn.BF16)
+    out = empty((rows, cols), syn.F32)
+    gpu.tp_partial_reduce([to_dev(p, syn.BF16) for p in parts_h], to_dev(R_h, syn.BF16), out)
+    torch.cuda.synchronize()
+    sel = syn.sample_rows(55, rows, 256)
+    got = from_dev(out[torch.from_numpy(sel).cuda()])
+    check_bound(got, [syn.to_f64(p[sel], syn.BF16) for p in parts_h],
+                syn.to_f64(R_h[sel], syn.BF16), syn.F32)
+    log("reduce t=4 [8192,12288] sampled rows within the fp32 bound")
