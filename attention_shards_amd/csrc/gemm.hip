@@ -149,25 +149,83 @@ __device__ __forceinline__ void tile_coords(int tiles_m, int tiles_n, int& tm,
 // ---------------------------------------------------------------------------
 // bf16 kernel
 // ---------------------------------------------------------------------------
+constexpr int BUF_FLAGS = 0x00020000;  // raw buffer, 32-bit data format
+constexpr int BK3 = 32;                // K per pipeline stage
+constexpr int PREF = 3;                // stages in flight in registers
+constexpr int OOB = 0x7FFFFFF0;        // offset past any buffer: reads return 0
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base,
+                                                            int64_t bytes) {
+  const int n = bytes <= 0 ? 0 : (bytes > (int64_t)OOB ? OOB : (int)bytes);
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, n, BUF_FLAGS);
+}
+
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+
+// s_waitcnt lgkmcnt(0) leaving the vector-memory counter unconstrained.
+#define TP_WAIT_LGKM0() __builtin_amdgcn_s_waitcnt(0xC07F)
+
+// Workgroup barrier that is also a compiler memory barrier but does not wait
+// for outstanding global loads (the register prefetch must stay in flight).
+__device__ __forceinline__ void stage_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+template <int N>
+struct IC {
+  static constexpr int value = N;
+};
+
+// Scheduling pipeline for the instruction scheduler: NM single MFMAs, each
+// followed by its share of NO instructions of class MASK (spread evenly), so
+// memory and LDS traffic issues between matrix instructions instead of
+// stalling behind a block of them (a wave cannot issue past an MFMA until
+// the matrix pipe accepts it).
+constexpr int SG_MFMA = 0x008, SG_VMEM_READ = 0x020, SG_DS_READ = 0x100, SG_DS_WRITE = 0x200;
+template <int MASK, int NM, int NO, int I = 0>
+__device__ __forceinline__ void interleave() {
+  if constexpr (I < NM) {
+    __builtin_amdgcn_sched_group_barrier(SG_MFMA, 1, 0);
+    constexpr int k = (I + 1) * NO / NM - I * NO / NM;
+    if constexpr (k > 0) __builtin_amdgcn_sched_group_barrier(MASK, k, 0);
+    interleave<MASK, NM, NO, I + 1>();
+  }
+}
+
 template <int BM, int BN, int WM, int WN, class Epi>
 __global__ void __launch_bounds__(WM * WN * 64)
 gemm_bf16_kernel(const uint16_t* __restrict__ A, int64_t lda,
                  const uint16_t* __restrict__ B, int64_t ldb, int M, int N,
                  int K, int kwrap, int tiles_m, int tiles_n, Epi epi) {
-  // Row gk of the K range reads B row (gk < kwrap ? gk : gk - kwrap); with
-  // kwrap < K (K <= 2 kwrap) the same B is used twice, which multiplies an
-  // A laid out as [A_hi | A_lo] by B in two passes.
+  // Stage kt reads B rows from (k0 < kwrap ? k0 : k0 - kwrap); with kwrap < K
+  // (K == 2 kwrap, kwrap % 32 == 0) the same B multiplies both halves of an
+  // A laid out as [A_hi | A_lo].
   constexpr int NT = WM * WN * 64;
-  constexpr int A_PASS = BM * 8 / NT;             // 16-byte chunks per thread
-  constexpr int B_BLOCKS = (BK / 8) * (BN / 8);      // 8x8 blocks per tile
-  constexpr int B_PASS = (B_BLOCKS + NT - 1) / NT;
+  constexpr int NW = WM * WN;
   constexpr int FM = BM / WM / 32;
   constexpr int FN = BN / WN / 32;
-  constexpr int STAGE = (BM + BN) * ROW_BYTES;
-  static_assert(A_PASS * NT == BM * 8, "A tile split");
+  constexpr int A_ROWB = BK3 * 2;          // 64-byte A rows in LDS (4 chunks)
+  constexpr int B_ROWB = BN * 2;           // B rows in LDS: natural [k][n]
+  constexpr int B_CH = B_ROWB / 16;        // 16-byte chunks per B row
+  constexpr int A_STAGE = BM * A_ROWB;
+  constexpr int B_STAGE = BK3 * B_ROWB;
+  constexpr int A_LD = A_STAGE / 16 / NT;  // 16-byte loads per thread per stage
+  constexpr int B_LD = B_STAGE / 16 / NT;
+  static_assert(A_LD * 16 * NT == A_STAGE && B_LD * 16 * NT == B_STAGE, "load split");
+  static_assert(B_CH >= 16, "B swizzle needs >= 16 chunks per row");
   static_assert(FM >= 1 && FN >= 1, "wave tile");
 
-  __shared__ __attribute__((aligned(16))) uint8_t smem[2 * STAGE];
+  // PREF LDS slots: slot s holds A at s*A_STAGE and B at PREF*A_STAGE +
+  // s*B_STAGE.  The same memory later stages the epilogue (NW regions of
+  // 32 x (BN/WN+4) floats).
+  constexpr int PIPE_BYTES = PREF * (A_STAGE + B_STAGE);
+  constexpr int EPI_BYTES = NW * 32 * (BN / WN + 4) * 4;
+  __shared__ __attribute__((aligned(16))) uint8_t
+      smem[PIPE_BYTES > EPI_BYTES ? PIPE_BYTES : EPI_BYTES];
+  uint8_t* const lds_a = smem;
+  uint8_t* const lds_b = smem + PREF * A_STAGE;
 
   int tm, tn;
   tile_coords(tiles_m, tiles_n, tm, tn);
@@ -175,9 +233,83 @@ gemm_bf16_kernel(const uint16_t* __restrict__ A, int64_t lda,
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wr0 = (wave / WN) * (BM / WM);
   const int wc0 = (wave % WN) * (BN / WN);
+  const int rows_valid = min(BM, M - m0);
+  const int cols_valid = min(BN, N - n0);
 
-  u32x4 ra[A_PASS];
-  u32x4 rb[B_PASS][8];
+  // ---- per-thread load offsets and LDS write positions.
+  // A: chunk c (8 K values) of tile row r is stored at position
+  //    c ^ ((r>>2)&3) of that row; B: chunk c of row k at c ^ ((k&3)<<2).
+  int a_goff[A_LD], a_col[A_LD], a_lds[A_LD];
+#pragma unroll
+  for (int j = 0; j < A_LD; ++j) {
+    const int idx = j * NT + tid;
+    const int r = idx >> 2, c = idx & 3;
+    a_goff[j] = r * (int)lda * 2 + c * 16;
+    a_col[j] = c * 8;
+    a_lds[j] = r * A_ROWB + ((c ^ ((r >> 2) & 3)) << 4);
+  }
+  int b_goff[B_LD], b_lds[B_LD];
+#pragma unroll
+  for (int j = 0; j < B_LD; ++j) {
+    const int idx = j * NT + tid;
+    const int k = idx / B_CH, c = idx % B_CH;
+    b_goff[j] = k * (int)ldb * 2 + c * 16;
+    b_lds[j] = k * B_ROWB + ((c ^ ((k & 3) << 2)) << 4);
+  }
+  u32x4 ra[PREF][A_LD], rb[PREF][B_LD];
+
+  auto gload = [&](int kt, auto SET) {
+    constexpr int set = decltype(SET)::value;
+    const int k0 = kt * BK3;
+    const __amdgpu_buffer_rsrc_t rsa =
+        make_rsrc(A + (int64_t)m0 * lda + k0, (int64_t)rows_valid * lda * 2 - (int64_t)k0 * 2);
+#pragma unroll
+    for (int j = 0; j < A_LD; ++j) {
+      const int off = (k0 + a_col[j] < K) ? a_goff[j] : OOB;
+      ra[set][j] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rsa, off, 0, 0));
+    }
+    const int bk0 = k0 < kwrap ? k0 : k0 - kwrap;
+    const int rows_left = (k0 < kwrap ? kwrap : K) - k0;
+    const __amdgpu_buffer_rsrc_t rsb =
+        make_rsrc(B + (int64_t)bk0 * ldb + n0,
+                  ((int64_t)rows_left - 1) * ldb * 2 + (int64_t)cols_valid * 2);
+#pragma unroll
+    for (int j = 0; j < B_LD; ++j)
+      rb[set][j] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rsb, b_goff[j], 0, 0));
+  };
+  auto lstore = [&](auto SET, auto SLOT) {
+    constexpr int set = decltype(SET)::value, slot = decltype(SLOT)::value;
+#pragma unroll
+    for (int j = 0; j < A_LD; ++j)
+      *reinterpret_cast<u32x4*>(lds_a + slot * A_STAGE + a_lds[j]) = ra[set][j];
+#pragma unroll
+    for (int j = 0; j < B_LD; ++j)
+      *reinterpret_cast<u32x4*>(lds_b + slot * B_STAGE + b_lds[j]) = rb[set][j];
+  };
+
+  // ---- fragment read addresses (byte offsets inside a slot).
+  // A (ds_read_b128): row wr0 + mi*32 + (lane&31), chunk 2ks + (lane>>5).
+  int a_rd[2];
+#pragma unroll
+  for (int ks = 0; ks < 2; ++ks) {
+    const int c = (2 * ks + (lane >> 5)) ^ (((lane & 31) >> 2) & 3);
+    a_rd[ks] = (wr0 + (lane & 31)) * A_ROWB + c * 16;
+  }
+  // B (ds_read_b64_tr_b16): in each 16-lane group G, input lane r points at
+  // row 8*(G>>1) + r/4 and columns 16*(G&1) + 4*(r&3) of the wave's 32-column
+  // block; the transposed read leaves lane l holding column l%32 with
+  // k = 8*(l/32) + 0..3; a second read 4 rows down gives k + 4..7.
+  int b_rd[FN];
+  {
+    const int G = lane >> 4, r = lane & 15;
+    const int krow = 8 * (G >> 1) + (r >> 2);
+#pragma unroll
+    for (int ni = 0; ni < FN; ++ni) {
+      const int c = (((wc0 + ni * 32) >> 3) + 2 * (G & 1) + ((r & 3) >> 1)) ^ ((r >> 2) << 2);
+      b_rd[ni] = krow * B_ROWB + c * 16 + (r & 1) * 8;
+    }
+  }
+
   f32x16 acc[FM][FN];
 #pragma unroll
   for (int mi = 0; mi < FM; ++mi)
@@ -186,98 +318,93 @@ gemm_bf16_kernel(const uint16_t* __restrict__ A, int64_t lda,
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[mi][ni][e] = 0.0f;
 
-  auto gload = [&](int k0) {
+  bf16x8 fa[2][FM], fb[2][FN];
+  auto read = [&](auto SLOT, int ks, int fset) {
+    constexpr int slot = decltype(SLOT)::value;
+    const uint8_t* la = lds_a + slot * A_STAGE;
+    const uint8_t* lb = lds_b + slot * B_STAGE + ks * 16 * B_ROWB;
 #pragma unroll
-    for (int p = 0; p < A_PASS; ++p) {
-      const int idx = p * NT + tid;
-      const int r = idx >> 3, c = idx & 7;
-      const int gr = m0 + r, gk = k0 + c * 8;
-      if (gr < M && gk < K)
-        ra[p] = *reinterpret_cast<const u32x4*>(A + (int64_t)gr * lda + gk);
-      else
-        ra[p] = u32x4{0, 0, 0, 0};
-    }
+    for (int mi = 0; mi < FM; ++mi)
+      fa[fset][mi] = *reinterpret_cast<const bf16x8*>(la + a_rd[ks] + mi * 32 * A_ROWB);
 #pragma unroll
-    for (int p = 0; p < B_PASS; ++p) {
-      const int idx = p * NT + tid;
-      const bool own = (B_BLOCKS % NT == 0) || idx < B_BLOCKS;
-      const int kg = idx / (BN / 8), ng = idx % (BN / 8);
-      const int gn = n0 + ng * 8;
-#pragma unroll
-      for (int jj = 0; jj < 8; ++jj) {
-        const int gk = k0 + kg * 8 + jj;
-        const int bk = gk < kwrap ? gk : gk - kwrap;
-        if (own && gk < K && gn < N)
-          rb[p][jj] = *reinterpret_cast<const u32x4*>(B + (int64_t)bk * ldb + gn);
-        else
-          rb[p][jj] = u32x4{0, 0, 0, 0};
-      }
+    for (int ni = 0; ni < FN; ++ni) {
+      const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (__attribute__((address_space(3))) s16x4*)(lb + b_rd[ni]));
+      const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (__attribute__((address_space(3))) s16x4*)(lb + b_rd[ni] + 4 * B_ROWB));
+      fb[fset][ni] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
     }
   };
-
-  auto lstore = [&](int stage) {
-    uint8_t* la = smem + stage * STAGE;
-    uint8_t* lb = la + BM * ROW_BYTES;
+  // Half h of one k-step's MFMAs: rows mi in [h*FM/2, (h+1)*FM/2) (all rows
+  // when FM == 1 and h == 0, none for h == 1).
+  auto mfma_half = [&](int fset, int h) {
 #pragma unroll
-    for (int p = 0; p < A_PASS; ++p) {
-      const int idx = p * NT + tid;
-      const int r = idx >> 3, c = idx & 7;
-      *reinterpret_cast<u32x4*>(la + r * ROW_BYTES + ((c ^ swz(r)) << 4)) = ra[p];
-    }
+    for (int mi = 0; mi < FM; ++mi) {
+      if (FM > 1 ? (mi / (FM / 2) != h) : (h != 0)) continue;
 #pragma unroll
-    for (int p = 0; p < B_PASS; ++p) {
-      const int idx = p * NT + tid;
-      if (B_BLOCKS % NT != 0 && idx >= B_BLOCKS) continue;
-      const int kg = idx / (BN / 8), ng = idx % (BN / 8);
-#pragma unroll
-      for (int n = 0; n < 8; ++n) {
-        const uint32_t sel = (n & 1) ? 0x07060302u : 0x05040100u;
-        u32x4 v;
-#pragma unroll
-        for (int q = 0; q < 4; ++q)
-          v[q] = __builtin_amdgcn_perm(rb[p][2 * q + 1][n >> 1], rb[p][2 * q][n >> 1], sel);
-        const int row = ng * 8 + n;
-        *reinterpret_cast<u32x4*>(lb + row * ROW_BYTES + ((kg ^ swz(row)) << 4)) = v;
-      }
+      for (int ni = 0; ni < FN; ++ni)
+        acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[fset][mi], fb[fset][ni],
+                                                              acc[mi][ni], 0, 0, 0);
     }
   };
+  constexpr int MH = FM > 1 ? FM * FN / 2 : FN;  // MFMAs per half (FM == 1: all in half 0)
+  constexpr int NRD = FM + 2 * FN;                // LDS fragment reads per k-step
+  constexpr int NLD = A_LD + B_LD;                // global loads / LDS stores per stage
 
-  auto compute = [&](int stage) {
-    const uint8_t* la = smem + stage * STAGE;
-    const uint8_t* lb = la + BM * ROW_BYTES;
-#pragma unroll
-    for (int ks = 0; ks < BK / 16; ++ks) {
-      const int ch = 2 * ks + (lane >> 5);
-      bf16x8 a[FM], b[FN];
-#pragma unroll
-      for (int mi = 0; mi < FM; ++mi) {
-        const int row = wr0 + mi * 32 + (lane & 31);
-        a[mi] = *reinterpret_cast<const bf16x8*>(la + row * ROW_BYTES + ((ch ^ swz(row)) << 4));
-      }
-#pragma unroll
-      for (int ni = 0; ni < FN; ++ni) {
-        const int row = wc0 + ni * 32 + (lane & 31);
-        b[ni] = *reinterpret_cast<const bf16x8*>(lb + row * ROW_BYTES + ((ch ^ swz(row)) << 4));
-      }
-#pragma unroll
-      for (int mi = 0; mi < FM; ++mi)
-#pragma unroll
-        for (int ni = 0; ni < FN; ++ni)
-          acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[mi], b[ni], acc[mi][ni], 0, 0, 0);
-    }
+  // Stages past the end of K load zeros (their offsets fall outside the
+  // buffers), so loads, LDS stores and barriers run unconditionally and the
+  // loop is padded to a multiple of PREF; only the MFMAs skip padded stages.
+  // (Uniform control flow keeps the compiler's vmcnt accounting exact.)
+  const int nk = (K + BK3 - 1) / BK3;
+  const int nk_pad = (nk + PREF - 1) / PREF * PREF;
+  // One pipeline step: compute stage kt (LDS slot kt%PREF) while stage
+  // kt+PREF is fetched into registers and stage kt+1 moves registers -> LDS.
+  // The stage's MFMAs are split into four groups, each carrying one kind of
+  // memory traffic:
+  //   1. k-step 0, first half  + global loads of stage kt+PREF
+  //   2. k-step 0, second half + LDS reads of k-step 1
+  //   3. k-step 1, first half  + LDS stores of stage kt+1
+  //      --- wait for the stores, barrier ---
+  //   4. k-step 1, second half + LDS reads of k-step 0 of stage kt+1
+  // Padded stages (kt >= nk) multiply zeros.
+  auto step = [&](int kt, auto U) {
+    constexpr int u = decltype(U)::value;  // kt % PREF
+    gload(kt + PREF, IC<u>{});
+    mfma_half(0, 0);
+    interleave<SG_VMEM_READ, MH, NLD>();
+    __builtin_amdgcn_sched_barrier(0);
+    read(IC<u>{}, 1, 1);
+    mfma_half(0, 1);
+    if constexpr (FM > 1) interleave<SG_DS_READ, MH, NRD>();
+    __builtin_amdgcn_sched_barrier(0);
+    // Slot (kt+1)%PREF was last read in step kt+1-PREF, which all waves left
+    // through an earlier barrier.
+    lstore(IC<(u + 1) % PREF>{}, IC<(u + 1) % PREF>{});
+    mfma_half(1, 0);
+    interleave<SG_DS_WRITE, MH, NLD>();
+    __builtin_amdgcn_sched_barrier(0);
+    TP_WAIT_LGKM0();
+    stage_barrier();
+    read(IC<(u + 1) % PREF>{}, 0, 0);
+    mfma_half(1, 1);
+    if constexpr (FM > 1) interleave<SG_DS_READ, MH, NRD>();
+    __builtin_amdgcn_sched_barrier(0);
   };
 
-  const int nk = (K + BK - 1) / BK;
-  gload(0);
-  lstore(0);
-  __syncthreads();
-  for (int kt = 0; kt < nk; ++kt) {
-    const int cur = kt & 1;
-    if (kt + 1 < nk) gload((kt + 1) * BK);
-    compute(cur);
-    if (kt + 1 < nk) lstore(cur ^ 1);
-    __syncthreads();
+  // Prologue: stages 0..PREF-1 into registers, stage 0 into LDS slot 0.
+  gload(0, IC<0>{});
+  gload(1, IC<1>{});
+  gload(2, IC<2>{});
+  lstore(IC<0>{}, IC<0>{});
+  TP_WAIT_LGKM0();
+  stage_barrier();
+  read(IC<0>{}, 0, 0);
+  for (int kt = 0; kt < nk_pad; kt += PREF) {
+    step(kt, IC<0>{});
+    step(kt + 1, IC<1>{});
+    step(kt + 2, IC<2>{});
   }
+  __syncthreads();
 
   // Epilogue through LDS: per 32-row slab, each wave parks its fp32
   // accumulators in its own LDS region (32 x WCOLS, padded), then reads them
@@ -286,7 +413,7 @@ gemm_bf16_kernel(const uint16_t* __restrict__ A, int64_t lda,
   // 8*(e/4) + 4*(l/32) + e%4 and column l%32 of the block.
   constexpr int WCOLS = BN / WN;
   constexpr int PITCH = WCOLS + 4;
-  static_assert(WM * WN * 32 * PITCH * 4 <= 2 * STAGE, "epilogue staging fits");
+  static_assert(NW * 32 * PITCH * 4 <= (int)sizeof(smem), "epilogue staging fits");
   float* stage_f = reinterpret_cast<float*>(smem) + wave * 32 * PITCH;
 #pragma unroll
   for (int mi = 0; mi < FM; ++mi) {
