@@ -361,27 +361,27 @@ gemm_bf16_kernel(const uint16_t* __restrict__ A, int64_t lda,
   // kt+PREF is fetched into registers and stage kt+1 moves registers -> LDS.
   // The stage's MFMAs are split into four groups, each carrying one kind of
   // memory traffic:
-  //   1. k-step 0, first half  + global loads of stage kt+PREF
+  //   1. k-step 0, first half  + LDS stores of stage kt+1 (slot (kt+1)%PREF
+  //      was last read in step kt+1-PREF, before an earlier barrier)
   //   2. k-step 0, second half + LDS reads of k-step 1
-  //   3. k-step 1, first half  + LDS stores of stage kt+1
+  //   3. k-step 1, first half  + global loads of stage kt+PREF
   //      --- wait for the stores, barrier ---
   //   4. k-step 1, second half + LDS reads of k-step 0 of stage kt+1
-  // Padded stages (kt >= nk) multiply zeros.
+  // The stores go first so they have drained by the barrier.  Padded stages
+  // (kt >= nk) multiply zeros.
   auto step = [&](int kt, auto U) {
     constexpr int u = decltype(U)::value;  // kt % PREF
-    gload(kt + PREF, IC<u>{});
+    lstore(IC<(u + 1) % PREF>{}, IC<(u + 1) % PREF>{});
     mfma_half(0, 0);
-    interleave<SG_VMEM_READ, MH, NLD>();
+    interleave<SG_DS_WRITE, MH, NLD>();
     __builtin_amdgcn_sched_barrier(0);
     read(IC<u>{}, 1, 1);
     mfma_half(0, 1);
     if constexpr (FM > 1) interleave<SG_DS_READ, MH, NRD>();
     __builtin_amdgcn_sched_barrier(0);
-    // Slot (kt+1)%PREF was last read in step kt+1-PREF, which all waves left
-    // through an earlier barrier.
-    lstore(IC<(u + 1) % PREF>{}, IC<(u + 1) % PREF>{});
+    gload(kt + PREF, IC<u>{});
     mfma_half(1, 0);
-    interleave<SG_DS_WRITE, MH, NLD>();
+    interleave<SG_VMEM_READ, MH, NLD>();
     __builtin_amdgcn_sched_barrier(0);
     TP_WAIT_LGKM0();
     stage_barrier();
