@@ -113,16 +113,17 @@ def cpu_baseline(d, budget_s=12.0):
     W2_i = syn.to_f64(d["W2"][cols, :], syn.BF16)
     rows_done, block = 0, 256
     t0 = time.perf_counter()
-    while rows_done < p["tokens"] and time.perf_counter() - t0 < budget_s:
-        Xb = syn.to_f64(d["X"][rows_done:rows_done + block], syn.BF16)
+    while time.perf_counter() - t0 < budget_s:
+        r0 = rows_done % p["tokens"]
+        Xb = syn.to_f64(d["X"][r0:r0 + block], syn.BF16)
         oracle.ffn_shard(Xb, W1_i, W2_i)
         rows_done += Xb.shape[0]
     dt = time.perf_counter() - t0
     fl = ffn_flops(rows_done, p["hidden"], p["ffn"], p["t"])
     return {"value": round(fl / dt / 1e12, 5), "unit": "TFLOP/s", "cores": int(cores),
             "kind": "oracle",
-            "sample": f"{rows_done} of {p['tokens']} token rows of the FFN shard "
-                      f"(fp64 numpy, {dt:.1f} s)"}
+            "sample": f"{rows_done} token rows ({rows_done / p['tokens']:.2f} passes over the "
+                      f"{p['tokens']} rows) of the FFN shard, fp64 numpy, {dt:.1f} s"}
 
 
 def sweep(path, steps, warmup):
@@ -155,14 +156,121 @@ def sweep(path, steps, warmup):
             torch.cuda.empty_cache()
 
 
+COPY_BYTES = 1 << 30
+
+
+def copy_calibration():
+    """One plain device-to-device copy of COPY_BYTES: the reference reading of
+    the FETCH_SIZE / WRITE_SIZE counters for a kernel of known traffic."""
+    import torch
+    a = torch.ones(COPY_BYTES // 2, dtype=torch.int16, device="cuda")
+    b = torch.empty_like(a)
+    torch.cuda.synchronize()
+    b.copy_(a)
+    torch.cuda.synchronize()
+
+
+def _read_counters(path):
+    """{kernel: {counter: [per-dispatch values]}} from a rocprofv3 counter CSV."""
+    import collections
+    import csv
+    per = collections.defaultdict(lambda: collections.defaultdict(float))
+    names = {}
+    with open(path) as f:
+        for r in csv.DictReader(f):
+            key = (r["Dispatch_Id"], r["Counter_Name"])
+            per[key[0]][key[1]] += float(r["Counter_Value"])
+            names[key[0]] = r["Kernel_Name"]
+    out = collections.defaultdict(lambda: collections.defaultdict(list))
+    for disp, counters in per.items():
+        for c, v in counters.items():
+            out[names[disp]][c].append(v)
+    return out
+
+
+def _short(name):
+    n = name.replace("tp::(anonymous namespace)::", "").replace("void ", "")
+    return n.split("(")[0] if "<" not in n.split("(")[0] else n[:n.index(">(") + 1]
+
+
+def summarize_profiles(stats_csv, fetch_csv, write_csv, cmd_stats, cmd_pmc):
+    """Write profiles/*.md and the traffic record bench.py reads."""
+    import csv
+    gemm_src = src_hash("gemm.hip")
+    rows = list(csv.DictReader(open(stats_csv)))
+    lines = ["# Kernel durations: FFN shard t=8 i=3, hidden 4096, ffn 16384, 4096 tokens",
+             "", "Command (from the repository root, on one MI355X):", "",
+             "```", cmd_stats, "```", "",
+             "| kernel | calls | avg us | min us | max us | share |",
+             "|---|---:|---:|---:|---:|---:|"]
+    for r in rows:
+        lines.append(f"| `{_short(r['Name'])}` | {r['Calls']} | {float(r['AverageNs'])/1e3:.1f} | "
+                     f"{float(r['MinNs'])/1e3:.1f} | {float(r['MaxNs'])/1e3:.1f} | "
+                     f"{float(r['Percentage']):.1f}% |")
+    with open(os.path.join(ROOT, "profiles", "kernel_stats_ffn_shard_h4096_t8.md"), "w") as f:
+        f.write("\n".join(lines) + "\n")
+
+    fe, wr = _read_counters(fetch_csv), _read_counters(write_csv)
+
+    def mean(d, kname, c):
+        vals = [v for k, cs in d.items() if kname in k for v in cs.get(c, [])]
+        return sum(vals) / len(vals) if vals else None
+    copy_fetch = mean(fe, "copyBuffer", "FETCH_SIZE")
+    copy_write = mean(wr, "copyBuffer", "WRITE_SIZE")
+    f_fac = (COPY_BYTES / 1024) / copy_fetch
+    w_fac = (COPY_BYTES / 1024) / copy_write
+    p = FFN
+    M, h, fs = p["tokens"], p["hidden"], p["ffn"] // p["t"]
+    kernels = {"GEMM1 + GeLU": "EpiGelu", "GEMM2": "EpiStore"}
+    table = ["# HBM traffic per launch: FFN shard t=8 i=3, hidden 4096, ffn 16384, 4096 tokens",
+             "", "Commands (from the repository root, one MI355X, one counter per run):", "",
+             "```", cmd_pmc.replace("COUNTER", "FETCH_SIZE"), cmd_pmc.replace("COUNTER", "WRITE_SIZE"),
+             "```", "",
+             f"Calibration: a {COPY_BYTES >> 20} MiB device copy read FETCH_SIZE {copy_fetch:.0f} KiB "
+             f"and WRITE_SIZE {copy_write:.0f} KiB, so the counters are scaled by "
+             f"{f_fac:.3f} (fetch) and {w_fac:.3f} (write).", "",
+             "| kernel | FETCH_SIZE KiB | WRITE_SIZE KiB | scaled MB read | scaled MB written |",
+             "|---|---:|---:|---:|---:|"]
+    total = 0.0
+    for label, tag in kernels.items():
+        fk = mean(fe, tag, "FETCH_SIZE")
+        wk = mean(wr, tag, "WRITE_SIZE")
+        rb_, wb_ = fk * 1024 * f_fac, wk * 1024 * w_fac
+        total += rb_ + wb_
+        table.append(f"| {label} | {fk:.0f} | {wk:.0f} | {rb_/1e6:.1f} | {wb_/1e6:.1f} |")
+    alg = 2 * (M * h + h * fs + M * fs) + 2 * (M * fs + fs * h) + 2 * M * h
+    table += ["", f"Sum for one tp_ffn_shard call: {total/1e6:.1f} MB of HBM traffic; the "
+              f"algorithmic minimum (X, W1_i, GeLU(Z) written and re-read, W2_i, bf16 Y) is "
+              f"{alg/1e6:.1f} MB.", "", f"GEMM source hash: `{gemm_src}`"]
+    with open(os.path.join(ROOT, "profiles", "traffic_ffn_shard_h4096_t8.md"), "w") as f:
+        f.write("\n".join(table) + "\n")
+    with open(TRAFFIC_FILE, "w") as f:
+        json.dump({"kernel_source_sha": gemm_src, "traffic_bytes": round(total),
+                   "fetch_factor": f_fac, "write_factor": w_fac,
+                   "algorithmic_bytes": alg}, f, indent=1)
+    print(f"wrote profiles (traffic {total/1e6:.1f} MB per call, algorithmic {alg/1e6:.1f} MB)")
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-attention", action="store_true",
+                    help="skip the attention row (profiling runs of the FFN step)")
     ap.add_argument("--sweep", metavar="OUT_JSONL", default=None)
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="run a 1 GiB device copy first (counter calibration)")
+    ap.add_argument("--summarize-profiles", nargs=3,
+                    metavar=("STATS_CSV", "FETCH_CSV", "WRITE_CSV"),
+                    help="write profiles/ summaries from rocprofv3 CSVs and exit")
+    ap.add_argument("--profile-commands", nargs=2, default=["", ""],
+                    metavar=("STATS_CMD", "PMC_CMD"))
     args = ap.parse_args()
+    if args.summarize_profiles:
+        summarize_profiles(*args.summarize_profiles, *args.profile_commands)
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU's shard only: this library runs on a single "
               "GPU and has no multi-GPU path; run with --gpus 1", file=sys.stderr)
@@ -177,6 +285,8 @@ def main():
         print("no GPU visible", file=sys.stderr)
         sys.exit(1)
 
+    if args.copy_calibration:
+        copy_calibration()
     if args.sweep:
         sweep(args.sweep, max(5, args.steps // 5), 3)
 
@@ -232,26 +342,31 @@ def main():
     torch.cuda.empty_cache()
 
     # ---------------- attention shard ----------------
-    a = ATTN
-    ad = syn.make_attn_inputs(a["seed"], a["batch"], a["seq"], a["hidden"], a["n_heads"],
-                              a["head_dim"])
-    nl = a["n_heads"] // a["t"]
-    Xa = dev_tensor(ad["X"], syn.BF16)
-    Wqkv = dev_tensor(syn.qkv_held_shard(ad["WQ"], ad["WK"], ad["WV"], a["n_heads"],
-                                         a["head_dim"], a["i"], a["t"]), syn.BF16)
-    Wo = dev_tensor(np.ascontiguousarray(
-        ad["WO"][syn.head_slice(a["n_heads"], a["head_dim"], a["i"], a["t"]), :]), syn.BF16)
-    Ya = torch.empty(a["batch"] * a["seq"], a["hidden"], dtype=torch.float32, device="cuda")
-    wsa = torch.empty(B.tp_attn_shard_workspace_bytes(a["batch"], a["seq"], a["n_heads"],
-                                                      a["head_dim"], a["t"]),
-                      dtype=torch.uint8, device="cuda")
-    attn_ms = time_events(lambda: B.tp_attn_shard(Xa, Wqkv, Wo, Ya, a["batch"], a["seq"],
-                                                  a["n_heads"], a["head_dim"], a["i"], a["t"],
-                                                  True, workspace=wsa),
-                          args.steps, args.warmup)
-    afl = attn_flops(a["batch"], a["seq"], a["hidden"], a["n_heads"], a["head_dim"], a["t"])
-    attn_tf = afl / (attn_ms * 1e-3) / 1e12
-    del ad
+    attn_row = None
+    if not args.no_attention:
+        a = ATTN
+        ad = syn.make_attn_inputs(a["seed"], a["batch"], a["seq"], a["hidden"], a["n_heads"],
+                                  a["head_dim"])
+        nl = a["n_heads"] // a["t"]
+        Xa = dev_tensor(ad["X"], syn.BF16)
+        Wqkv = dev_tensor(syn.qkv_held_shard(ad["WQ"], ad["WK"], ad["WV"], a["n_heads"],
+                                             a["head_dim"], a["i"], a["t"]), syn.BF16)
+        Wo = dev_tensor(np.ascontiguousarray(
+            ad["WO"][syn.head_slice(a["n_heads"], a["head_dim"], a["i"], a["t"]), :]), syn.BF16)
+        Ya = torch.empty(a["batch"] * a["seq"], a["hidden"], dtype=torch.float32, device="cuda")
+        wsa = torch.empty(B.tp_attn_shard_workspace_bytes(a["batch"], a["seq"], a["n_heads"],
+                                                          a["head_dim"], a["t"]),
+                          dtype=torch.uint8, device="cuda")
+        attn_ms = time_events(lambda: B.tp_attn_shard(Xa, Wqkv, Wo, Ya, a["batch"], a["seq"],
+                                                      a["n_heads"], a["head_dim"], a["i"], a["t"],
+                                                      True, workspace=wsa),
+                              args.steps, args.warmup)
+        afl = attn_flops(a["batch"], a["seq"], a["hidden"], a["n_heads"], a["head_dim"], a["t"])
+        attn_tf = afl / (attn_ms * 1e-3) / 1e12
+        del ad
+        attn_row = {"workload": "t8_i0_h8192_64x128heads_seq2048_causal",
+                    "ms": round(attn_ms, 5), "flop": afl, "tflops": round(attn_tf, 2),
+                    "frac_peak": round(attn_tf / PEAK_BF16_TFLOPS, 4)}
 
     traffic = load_traffic()
     res = {
@@ -282,10 +397,7 @@ def main():
                                "gbs": round(red_gbs, 1),
                                "frac_hbm_peak": round(red_gbs / PEAK_HBM_GBS, 4),
                                "bound": "hbm"},
-            "attn_shard": {"workload": "t8_i0_h8192_64x128heads_seq2048_causal",
-                           "ms": round(attn_ms, 5), "flop": afl,
-                           "tflops": round(attn_tf, 2),
-                           "frac_peak": round(attn_tf / PEAK_BF16_TFLOPS, 4)},
+            "attn_shard": attn_row,
         },
     }
     if not args.no_cpu_baseline:
