@@ -22,7 +22,7 @@ LIB = os.path.join(PKG, "libtpshard.so")
 SOURCES = ["gemm.hip", "attention.hip", "reduce.hip", "tp_shard.cpp"]
 
 # -packed-fp32-ops: no v_pk_{add,mul,fma}_f32 in generated code.
-COMMON = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
+COMMON = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-Wno-inline-asm",
           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
           "-I", os.path.join(ROOT, "include")]
 

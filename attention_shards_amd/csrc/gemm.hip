@@ -71,12 +71,30 @@ __device__ __forceinline__ void store_run4(void* C, int64_t ldc, int out, int ro
   }
 }
 
+// 8 consecutive columns (col0 % 8 == 0, the run inside the matrix).
+__device__ __forceinline__ void store_run8(void* C, int64_t ldc, int out, int row,
+                                           int col0, const float* v) {
+  if (out == OUT_F32) {
+    f32x4* c = reinterpret_cast<f32x4*>(static_cast<float*>(C) + (int64_t)row * ldc + col0);
+    c[0] = f32x4{v[0], v[1], v[2], v[3]};
+    c[1] = f32x4{v[4], v[5], v[6], v[7]};
+  } else {
+    uint16_t* c = static_cast<uint16_t*>(C) + (int64_t)row * ldc + col0;
+    *reinterpret_cast<u32x4*>(c) =
+        u32x4{f2bf(v[0]) | (f2bf(v[1]) << 16), f2bf(v[2]) | (f2bf(v[3]) << 16),
+              f2bf(v[4]) | (f2bf(v[5]) << 16), f2bf(v[6]) | (f2bf(v[7]) << 16)};
+  }
+}
+
 struct EpiStore {
   void* C;
   int64_t ldc;
   int out;  // OutType
   __device__ void store4(int row, int col0, const float* v) const {
     store_run4(C, ldc, out, row, col0, v);
+  }
+  __device__ void store8(int row, int col0, const float* v) const {
+    store_run8(C, ldc, out, row, col0, v);
   }
 };
 
@@ -90,11 +108,21 @@ struct EpiGelu {
     for (int r = 0; r < 4; ++r) g[r] = gelu_erf(v[r]);
     store_run4(C, ldc, out, row, col0, g);
   }
+  __device__ void store8(int row, int col0, const float* v) const {
+    float g[8];
+#pragma unroll
+    for (int r = 0; r < 8; ++r) g[r] = gelu_erf(v[r]);
+    store_run8(C, ldc, out, row, col0, g);
+  }
 };
 
 // Scatter of the QKV projection into the attention workspace (d == 128).
 struct EpiQkv {
   QkvOut q;
+  __device__ void store8(int row, int col0, const float* v) const {
+    store4(row, col0, v);
+    store4(row, col0 + 4, v + 4);
+  }
   __device__ void store4(int row, int col0, const float* v) const {
     const int hall = col0 >> 7;          // head index over [Q | K | V]
     const int dd = col0 & 127;
@@ -151,7 +179,7 @@ __device__ __forceinline__ void tile_coords(int tiles_m, int tiles_n, int& tm,
 // ---------------------------------------------------------------------------
 constexpr int BUF_FLAGS = 0x00020000;  // raw buffer, 32-bit data format
 constexpr int BK3 = 32;                // K per pipeline stage
-constexpr int PREF = 3;                // stages in flight in registers
+constexpr int NSLOT = 5;               // LDS ring: DMA runs NSLOT-1 stages ahead
 constexpr int OOB = 0x7FFFFFF0;        // offset past any buffer: reads return 0
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base,
@@ -161,12 +189,28 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base,
 }
 
 typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) uint8_t lds_u8;
 
-// s_waitcnt lgkmcnt(0) leaving the vector-memory counter unconstrained.
-#define TP_WAIT_LGKM0() __builtin_amdgcn_s_waitcnt(0xC07F)
+// Global -> LDS copy of 16 bytes per lane (buffer_load ... lds): lane l's
+// bytes land at LDS address lds_base + 16*l.  Issued from inline assembly so
+// the compiler does not treat later LDS reads as waiting on it; completion is
+// tracked explicitly with wait_vmcnt().  (m0 is set here and used by nothing
+// else in the kernels of this file.)
+__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t rsrc, int voffset,
+                                      uint32_t lds_base) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+               :
+               : "s"(__builtin_amdgcn_readfirstlane(lds_base)), "v"(voffset), "s"(rsrc)
+               : "memory", "m0");
+}
 
-// Workgroup barrier that is also a compiler memory barrier but does not wait
-// for outstanding global loads (the register prefetch must stay in flight).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+// Workgroup barrier that is also a compiler memory barrier but adds no wait.
 __device__ __forceinline__ void stage_barrier() {
   asm volatile("" ::: "memory");
   __builtin_amdgcn_s_barrier();
@@ -178,21 +222,6 @@ struct IC {
   static constexpr int value = N;
 };
 
-// Scheduling pipeline for the instruction scheduler: NM single MFMAs, each
-// followed by its share of NO instructions of class MASK (spread evenly), so
-// memory and LDS traffic issues between matrix instructions instead of
-// stalling behind a block of them (a wave cannot issue past an MFMA until
-// the matrix pipe accepts it).
-constexpr int SG_MFMA = 0x008, SG_VMEM_READ = 0x020, SG_DS_READ = 0x100, SG_DS_WRITE = 0x200;
-template <int MASK, int NM, int NO, int I = 0>
-__device__ __forceinline__ void interleave() {
-  if constexpr (I < NM) {
-    __builtin_amdgcn_sched_group_barrier(SG_MFMA, 1, 0);
-    constexpr int k = (I + 1) * NO / NM - I * NO / NM;
-    if constexpr (k > 0) __builtin_amdgcn_sched_group_barrier(MASK, k, 0);
-    interleave<MASK, NM, NO, I + 1>();
-  }
-}
 
 template <int BM, int BN, int WM, int WN, class Epi>
 __global__ void __launch_bounds__(WM * WN * 64)
@@ -202,7 +231,6 @@ gemm_bf16_kernel(const uint16_t* __restrict__ A, int64_t lda,
   // Stage kt reads B rows from (k0 < kwrap ? k0 : k0 - kwrap); with kwrap < K
   // (K == 2 kwrap, kwrap % 32 == 0) the same B multiplies both halves of an
   // A laid out as [A_hi | A_lo].
-  constexpr int NT = WM * WN * 64;
   constexpr int NW = WM * WN;
   constexpr int FM = BM / WM / 32;
   constexpr int FN = BN / WN / 32;
@@ -211,21 +239,23 @@ gemm_bf16_kernel(const uint16_t* __restrict__ A, int64_t lda,
   constexpr int B_CH = B_ROWB / 16;        // 16-byte chunks per B row
   constexpr int A_STAGE = BM * A_ROWB;
   constexpr int B_STAGE = BK3 * B_ROWB;
-  constexpr int A_LD = A_STAGE / 16 / NT;  // 16-byte loads per thread per stage
-  constexpr int B_LD = B_STAGE / 16 / NT;
-  static_assert(A_LD * 16 * NT == A_STAGE && B_LD * 16 * NT == B_STAGE, "load split");
+  constexpr int A_DMA = A_STAGE / 1024 / NW;  // 1 KiB DMAs per wave per stage
+  constexpr int B_DMA = B_STAGE / 1024 / NW;
+  constexpr int NDMA = A_DMA + B_DMA;
+  static_assert(A_DMA * 1024 * NW == A_STAGE && B_DMA * 1024 * NW == B_STAGE, "DMA split");
   static_assert(B_CH >= 16, "B swizzle needs >= 16 chunks per row");
   static_assert(FM >= 1 && FN >= 1, "wave tile");
 
-  // PREF LDS slots: slot s holds A at s*A_STAGE and B at PREF*A_STAGE +
-  // s*B_STAGE.  The same memory later stages the epilogue (NW regions of
-  // 32 x (BN/WN+4) floats).
-  constexpr int PIPE_BYTES = PREF * (A_STAGE + B_STAGE);
+  // LDS ring: slot s holds A at s*A_STAGE and B at NSLOT*A_STAGE + s*B_STAGE.
+  // The same memory later stages the epilogue (NW regions of 32 x (BN/WN+4)).
+  constexpr int PIPE_BYTES = NSLOT * (A_STAGE + B_STAGE);
   constexpr int EPI_BYTES = NW * 32 * (BN / WN + 4) * 4;
   __shared__ __attribute__((aligned(16))) uint8_t
       smem[PIPE_BYTES > EPI_BYTES ? PIPE_BYTES : EPI_BYTES];
   uint8_t* const lds_a = smem;
-  uint8_t* const lds_b = smem + PREF * A_STAGE;
+  uint8_t* const lds_b = smem + NSLOT * A_STAGE;
+  const uint32_t lds_a_addr = (uint32_t)(uintptr_t)(lds_u8*)lds_a;
+  const uint32_t lds_b_addr = (uint32_t)(uintptr_t)(lds_u8*)lds_b;
 
   int tm, tn;
   tile_coords(tiles_m, tiles_n, tm, tn);
@@ -236,55 +266,45 @@ gemm_bf16_kernel(const uint16_t* __restrict__ A, int64_t lda,
   const int rows_valid = min(BM, M - m0);
   const int cols_valid = min(BN, N - n0);
 
-  // ---- per-thread load offsets and LDS write positions.
-  // A: chunk c (8 K values) of tile row r is stored at position
-  //    c ^ ((r>>2)&3) of that row; B: chunk c of row k at c ^ ((k&3)<<2).
-  int a_goff[A_LD], a_col[A_LD], a_lds[A_LD];
+  // ---- DMA lane offsets.  A: 16 rows of 64 B per DMA; lane l fills row
+  // l/4, slot l%4 with logical chunk (l%4) ^ ((row>>2)&3).  B: 1024/B_ROWB
+  // rows per DMA; lane l fills slot l % B_CH with logical chunk
+  // slot ^ ((row&3)<<2).  The swizzles keep the fragment reads on distinct
+  // banks; they are applied to the global addresses.
+  int a_off[A_DMA], a_col[A_DMA];
 #pragma unroll
-  for (int j = 0; j < A_LD; ++j) {
-    const int idx = j * NT + tid;
-    const int r = idx >> 2, c = idx & 3;
-    a_goff[j] = r * (int)lda * 2 + c * 16;
+  for (int j = 0; j < A_DMA; ++j) {
+    const int row = 16 * (j * NW + wave) + (lane >> 2);
+    const int c = (lane & 3) ^ ((row >> 2) & 3);
+    a_off[j] = row * (int)lda * 2 + c * 16;
     a_col[j] = c * 8;
-    a_lds[j] = r * A_ROWB + ((c ^ ((r >> 2) & 3)) << 4);
   }
-  int b_goff[B_LD], b_lds[B_LD];
+  int b_off[B_DMA];
 #pragma unroll
-  for (int j = 0; j < B_LD; ++j) {
-    const int idx = j * NT + tid;
-    const int k = idx / B_CH, c = idx % B_CH;
-    b_goff[j] = k * (int)ldb * 2 + c * 16;
-    b_lds[j] = k * B_ROWB + ((c ^ ((k & 3) << 2)) << 4);
+  for (int j = 0; j < B_DMA; ++j) {
+    const int row = (j * NW + wave) * (1024 / B_ROWB) + lane / B_CH;
+    const int c = (lane % B_CH) ^ ((row & 3) << 2);
+    b_off[j] = row * (int)ldb * 2 + c * 16;
   }
-  u32x4 ra[PREF][A_LD], rb[PREF][B_LD];
 
-  auto gload = [&](int kt, auto SET) {
-    constexpr int set = decltype(SET)::value;
+  // DMA number j (0 <= j < NDMA) of stage kt into ring slot SLOT.
+  auto dma = [&](int kt, auto SLOT, int j) {
+    constexpr int slot = decltype(SLOT)::value;
     const int k0 = kt * BK3;
-    const __amdgpu_buffer_rsrc_t rsa =
-        make_rsrc(A + (int64_t)m0 * lda + k0, (int64_t)rows_valid * lda * 2 - (int64_t)k0 * 2);
-#pragma unroll
-    for (int j = 0; j < A_LD; ++j) {
-      const int off = (k0 + a_col[j] < K) ? a_goff[j] : OOB;
-      ra[set][j] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rsa, off, 0, 0));
+    if (j < A_DMA) {
+      const __amdgpu_buffer_rsrc_t ra =
+          make_rsrc(A + (int64_t)m0 * lda + k0, (int64_t)rows_valid * lda * 2 - (int64_t)k0 * 2);
+      const int off = (k0 + a_col[j] < K) ? a_off[j] : OOB;
+      dma16(ra, off, lds_a_addr + slot * A_STAGE + (j * NW + wave) * 1024);
+    } else {
+      const int jb = j - A_DMA;
+      const int bk0 = k0 < kwrap ? k0 : k0 - kwrap;
+      const int rows_left = (k0 < kwrap ? kwrap : K) - k0;
+      const __amdgpu_buffer_rsrc_t rb =
+          make_rsrc(B + (int64_t)bk0 * ldb + n0,
+                    ((int64_t)rows_left - 1) * ldb * 2 + (int64_t)cols_valid * 2);
+      dma16(rb, b_off[jb], lds_b_addr + slot * B_STAGE + (jb * NW + wave) * 1024);
     }
-    const int bk0 = k0 < kwrap ? k0 : k0 - kwrap;
-    const int rows_left = (k0 < kwrap ? kwrap : K) - k0;
-    const __amdgpu_buffer_rsrc_t rsb =
-        make_rsrc(B + (int64_t)bk0 * ldb + n0,
-                  ((int64_t)rows_left - 1) * ldb * 2 + (int64_t)cols_valid * 2);
-#pragma unroll
-    for (int j = 0; j < B_LD; ++j)
-      rb[set][j] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rsb, b_goff[j], 0, 0));
-  };
-  auto lstore = [&](auto SET, auto SLOT) {
-    constexpr int set = decltype(SET)::value, slot = decltype(SLOT)::value;
-#pragma unroll
-    for (int j = 0; j < A_LD; ++j)
-      *reinterpret_cast<u32x4*>(lds_a + slot * A_STAGE + a_lds[j]) = ra[set][j];
-#pragma unroll
-    for (int j = 0; j < B_LD; ++j)
-      *reinterpret_cast<u32x4*>(lds_b + slot * B_STAGE + b_lds[j]) = rb[set][j];
   };
 
   // ---- fragment read addresses (byte offsets inside a slot).
@@ -319,102 +339,122 @@ gemm_bf16_kernel(const uint16_t* __restrict__ A, int64_t lda,
       for (int e = 0; e < 16; ++e) acc[mi][ni][e] = 0.0f;
 
   bf16x8 fa[2][FM], fb[2][FN];
-  auto read = [&](auto SLOT, int ks, int fset) {
+  // Fragment read unit q of k-step ks from ring slot SLOT into set fset:
+  // units 0..FN-1 are B fragments (two transposed reads each), units
+  // FN..FN+FM-1 are A fragments.
+  auto read_unit = [&](auto SLOT, int ks, int fset, int q) {
     constexpr int slot = decltype(SLOT)::value;
-    const uint8_t* la = lds_a + slot * A_STAGE;
-    const uint8_t* lb = lds_b + slot * B_STAGE + ks * 16 * B_ROWB;
-#pragma unroll
-    for (int mi = 0; mi < FM; ++mi)
-      fa[fset][mi] = *reinterpret_cast<const bf16x8*>(la + a_rd[ks] + mi * 32 * A_ROWB);
-#pragma unroll
-    for (int ni = 0; ni < FN; ++ni) {
+    if (q < FN) {
+      const uint8_t* lb = lds_b + slot * B_STAGE + ks * 16 * B_ROWB + b_rd[q];
       const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-          (__attribute__((address_space(3))) s16x4*)(lb + b_rd[ni]));
+          (__attribute__((address_space(3))) s16x4*)lb);
       const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-          (__attribute__((address_space(3))) s16x4*)(lb + b_rd[ni] + 4 * B_ROWB));
-      fb[fset][ni] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+          (__attribute__((address_space(3))) s16x4*)(lb + 4 * B_ROWB));
+      fb[fset][q] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+    } else {
+      const int mi = q - FN;
+      fa[fset][mi] = *reinterpret_cast<const bf16x8*>(lds_a + slot * A_STAGE + a_rd[ks] +
+                                                     mi * 32 * A_ROWB);
     }
   };
-  // Half h of one k-step's MFMAs: rows mi in [h*FM/2, (h+1)*FM/2) (all rows
-  // when FM == 1 and h == 0, none for h == 1).
-  auto mfma_half = [&](int fset, int h) {
-#pragma unroll
-    for (int mi = 0; mi < FM; ++mi) {
-      if (FM > 1 ? (mi / (FM / 2) != h) : (h != 0)) continue;
-#pragma unroll
-      for (int ni = 0; ni < FN; ++ni)
-        acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[fset][mi], fb[fset][ni],
-                                                              acc[mi][ni], 0, 0, 0);
-    }
+  auto mfma1 = [&](int fset, int idx) {  // one MFMA of a k-step, idx in [0, FM*FN)
+    const int mi = idx / FN, ni = idx % FN;
+    acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[fset][mi], fb[fset][ni],
+                                                          acc[mi][ni], 0, 0, 0);
   };
-  constexpr int MH = FM > 1 ? FM * FN / 2 : FN;  // MFMAs per half (FM == 1: all in half 0)
-  constexpr int NRD = FM + 2 * FN;                // LDS fragment reads per k-step
-  constexpr int NLD = A_LD + B_LD;                // global loads / LDS stores per stage
+  constexpr int NMF = FM * FN;   // MFMAs per k-step
+  constexpr int NRU = FM + FN;   // fragment read units per k-step
 
-  // Stages past the end of K load zeros (their offsets fall outside the
-  // buffers), so loads, LDS stores and barriers run unconditionally and the
-  // loop is padded to a multiple of PREF; only the MFMAs skip padded stages.
-  // (Uniform control flow keeps the compiler's vmcnt accounting exact.)
+  // Stages past the end of K load zeros (offsets outside the buffers), so
+  // every main-loop step issues the same DMAs and the explicit vmcnt counts
+  // below are exact.
   const int nk = (K + BK3 - 1) / BK3;
-  const int nk_pad = (nk + PREF - 1) / PREF * PREF;
-  // One pipeline step: compute stage kt (LDS slot kt%PREF) while stage
-  // kt+PREF is fetched into registers and stage kt+1 moves registers -> LDS.
-  // The stage's MFMAs are split into four groups, each carrying one kind of
-  // memory traffic:
-  //   1. k-step 0, first half  + LDS stores of stage kt+1 (slot (kt+1)%PREF
-  //      was last read in step kt+1-PREF, before an earlier barrier)
-  //   2. k-step 0, second half + LDS reads of k-step 1
-  //   3. k-step 1, first half  + global loads of stage kt+PREF
-  //      --- wait for the stores, barrier ---
-  //   4. k-step 1, second half + LDS reads of k-step 0 of stage kt+1
-  // The stores go first so they have drained by the barrier.  Padded stages
-  // (kt >= nk) multiply zeros.
-  auto step = [&](int kt, auto U) {
-    constexpr int u = decltype(U)::value;  // kt % PREF
-    lstore(IC<(u + 1) % PREF>{}, IC<(u + 1) % PREF>{});
-    mfma_half(0, 0);
-    interleave<SG_DS_WRITE, MH, NLD>();
-    __builtin_amdgcn_sched_barrier(0);
-    read(IC<u>{}, 1, 1);
-    mfma_half(0, 1);
-    if constexpr (FM > 1) interleave<SG_DS_READ, MH, NRD>();
-    __builtin_amdgcn_sched_barrier(0);
-    gload(kt + PREF, IC<u>{});
-    mfma_half(1, 0);
-    interleave<SG_VMEM_READ, MH, NLD>();
-    __builtin_amdgcn_sched_barrier(0);
-    TP_WAIT_LGKM0();
+
+  // One pipeline step computes stage kt from ring slot u = kt % NSLOT.  Each
+  // MFMA is followed by at most one piece of memory traffic, pinned in place
+  // with scheduling barriers (a wave cannot issue past an MFMA until the
+  // matrix pipe accepts it, so traffic must sit between MFMAs to overlap):
+  //   k-step 0: DMAs of stage kt+NSLOT-1 (slot (u+NSLOT-1)%NSLOT, last read
+  //     in step kt-1, before its barrier), then the k-step 1 fragment reads;
+  //   wait until stage kt+1's DMAs have landed (NSLOT-2 later stages stay
+  //   in flight), barrier;
+  //   k-step 1: the fragment reads of k-step 0 of stage kt+1.
+  // The last nk % NSLOT stages run as tail steps: every stage they need is
+  // already in flight (stages up to kt+3 when the tail group starts at kt),
+  // so a tail step issues no DMA and waits until 2-u stages remain
+  // outstanding, i.e. until stage kt+u+1 has landed.
+  auto step = [&](int kt, auto U, auto TAIL) {
+    constexpr int u = decltype(U)::value;
+    constexpr bool tail = decltype(TAIL)::value != 0;
+    constexpr int nxt = (u + NSLOT - 1) % NSLOT;
+    static_assert(NDMA + NRU <= 2 * NMF, "traffic fits between the MFMAs");
+    // k-step 0
+#pragma unroll
+    for (int j = 0; j < NMF; ++j) {
+      mfma1(0, j);
+      __builtin_amdgcn_sched_barrier(0);
+      if (!tail && j < NDMA) dma(kt + NSLOT - 1, IC<nxt>{}, j);
+      if (j >= NMF - NRU) read_unit(IC<u>{}, 1, 1, j - (NMF - NRU));
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    if constexpr (tail)
+      wait_vmcnt<(u < 2 ? 2 - u : 0) * NDMA>();
+    else
+      wait_vmcnt<(NSLOT - 2) * NDMA>();
     stage_barrier();
-    read(IC<(u + 1) % PREF>{}, 0, 0);
-    mfma_half(1, 1);
-    if constexpr (FM > 1) interleave<SG_DS_READ, MH, NRD>();
-    __builtin_amdgcn_sched_barrier(0);
+    // k-step 1
+#pragma unroll
+    for (int j = 0; j < NMF; ++j) {
+      mfma1(1, j);
+      __builtin_amdgcn_sched_barrier(0);
+      if (j < NRU) read_unit(IC<(u + 1) % NSLOT>{}, 0, 0, j);
+      __builtin_amdgcn_sched_barrier(0);
+    }
   };
 
-  // Prologue: stages 0..PREF-1 into registers, stage 0 into LDS slot 0.
-  gload(0, IC<0>{});
-  gload(1, IC<1>{});
-  gload(2, IC<2>{});
-  lstore(IC<0>{}, IC<0>{});
-  TP_WAIT_LGKM0();
+  // Prologue: stages 0..NSLOT-2 in flight, wait for stage 0.
+#pragma unroll
+  for (int j = 0; j < NDMA; ++j) dma(0, IC<0>{}, j);
+#pragma unroll
+  for (int j = 0; j < NDMA; ++j) dma(1, IC<1>{}, j);
+#pragma unroll
+  for (int j = 0; j < NDMA; ++j) dma(2, IC<2>{}, j);
+#pragma unroll
+  for (int j = 0; j < NDMA; ++j) dma(3, IC<3>{}, j);
+  static_assert(NSLOT == 5, "prologue, loop and tail are written for 5 slots");
+  wait_vmcnt<(NSLOT - 2) * NDMA>();
   stage_barrier();
-  read(IC<0>{}, 0, 0);
-  for (int kt = 0; kt < nk_pad; kt += PREF) {
-    step(kt, IC<0>{});
-    step(kt + 1, IC<1>{});
-    step(kt + 2, IC<2>{});
+#pragma unroll
+  for (int q = 0; q < NRU; ++q) read_unit(IC<0>{}, 0, 0, q);
+  int kt = 0;
+  for (; kt + NSLOT <= nk; kt += NSLOT) {
+    step(kt, IC<0>{}, IC<0>{});
+    step(kt + 1, IC<1>{}, IC<0>{});
+    step(kt + 2, IC<2>{}, IC<0>{});
+    step(kt + 3, IC<3>{}, IC<0>{});
+    step(kt + 4, IC<4>{}, IC<0>{});
   }
+  const int rem = nk - kt;  // 0..NSLOT-1, uniform
+  if (rem > 0) step(kt, IC<0>{}, IC<1>{});
+  if (rem > 1) step(kt + 1, IC<1>{}, IC<1>{});
+  if (rem > 2) step(kt + 2, IC<2>{}, IC<1>{});
+  if (rem > 3) step(kt + 3, IC<3>{}, IC<1>{});
+  wait_vmcnt<0>();
   __syncthreads();
 
   // Epilogue through LDS: per 32-row slab, each wave parks its fp32
-  // accumulators in its own LDS region (32 x WCOLS, padded), then reads them
-  // back as runs of 4 consecutive columns for vector stores.
+  // accumulators in its own LDS region (32 x WCOLS, padded) and reads them
+  // back as runs of 8 consecutive columns for 16-byte stores.  A wave only
+  // touches its own region and LDS operations of one wave complete in order,
+  // so no barrier is needed between the slabs.
   // 32x32 accumulator layout: lane l, register e holds row
   // 8*(e/4) + 4*(l/32) + e%4 and column l%32 of the block.
   constexpr int WCOLS = BN / WN;
   constexpr int PITCH = WCOLS + 4;
   static_assert(NW * 32 * PITCH * 4 <= (int)sizeof(smem), "epilogue staging fits");
   float* stage_f = reinterpret_cast<float*>(smem) + wave * 32 * PITCH;
+  constexpr int RUNS = WCOLS / 8;           // 8-column runs per row
+  constexpr int ROWS_PER_PASS = 64 / RUNS;  // rows covered by one wave pass
 #pragma unroll
   for (int mi = 0; mi < FM; ++mi) {
 #pragma unroll
@@ -424,20 +464,21 @@ gemm_bf16_kernel(const uint16_t* __restrict__ A, int64_t lda,
         const int i = 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
         stage_f[i * PITCH + ni * 32 + (lane & 31)] = acc[mi][ni][e];
       }
-    __syncthreads();
-    constexpr int RUNS = WCOLS / 4;           // 4-column runs per row
-    constexpr int ROWS_PER_PASS = 64 / RUNS;  // rows covered by one wave pass
-    for (int rr = lane / RUNS; rr < 32; rr += ROWS_PER_PASS) {
-      const int c4 = (lane % RUNS) * 4;
+    asm volatile("" ::: "memory");  // keep the LDS writes before the reads
+#pragma unroll
+    for (int it = 0; it < 32 / ROWS_PER_PASS; ++it) {
+      const int rr = it * ROWS_PER_PASS + lane / RUNS;
+      const int c8 = (lane % RUNS) * 8;
       const int row = m0 + wr0 + mi * 32 + rr;
-      const int col0 = n0 + wc0 + c4;
+      const int col0 = n0 + wc0 + c8;
+      const f32x4 va = *reinterpret_cast<const f32x4*>(stage_f + rr * PITCH + c8);
+      const f32x4 vb = *reinterpret_cast<const f32x4*>(stage_f + rr * PITCH + c8 + 4);
       if (row < M && col0 < N) {
-        const f32x4 v4 = *reinterpret_cast<const f32x4*>(stage_f + rr * PITCH + c4);
-        float v[4] = {v4[0], v4[1], v4[2], v4[3]};
-        epi.store4(row, col0, v);
+        float v[8] = {va[0], va[1], va[2], va[3], vb[0], vb[1], vb[2], vb[3]};
+        epi.store8(row, col0, v);
       }
     }
-    __syncthreads();
+    asm volatile("" ::: "memory");  // and this slab's reads before the next writes
   }
 }
 

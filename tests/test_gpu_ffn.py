@@ -71,6 +71,8 @@ def test_bf16_t8_shard3_full(gpu):
     (1, 64, 2 * 64, 2, 1, syn.F32, True),
     (257, 264, 520, 1, 0, syn.BF16, False),
     (513, 1032, 4 * 392, 4, 3, syn.F32, True),
+    (190, 296, 2 * 160, 2, 1, syn.BF16, True),    # K stages a multiple of the ring
+    (70, 8, 2 * 8, 2, 0, syn.F32, False),         # K = 8: one partial stage
 ])
 def test_bf16_ragged(gpu, M, h, f, t, i, out, view):
     d = syn.make_ffn_inputs(100 + M, M, h, f, syn.BF16)
