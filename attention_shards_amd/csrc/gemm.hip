@@ -224,6 +224,10 @@ __device__ __forceinline__ void wait_vmcnt() {
   asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
 
+__device__ __forceinline__ void wait_lgkmcnt0() {
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+}
+
 // Workgroup barrier that is also a compiler memory barrier but adds no wait.
 __device__ __forceinline__ void stage_barrier() {
   asm volatile("" ::: "memory");
@@ -388,10 +392,13 @@ gemm_bf16_kernel(const uint16_t* __restrict__ A, int64_t lda,
   // MFMA is followed by at most one piece of memory traffic, pinned in place
   // with scheduling barriers (a wave cannot issue past an MFMA until the
   // matrix pipe accepts it, so traffic must sit between MFMAs to overlap):
-  //   k-step 0: DMAs of stage kt+NSLOT-1 (slot (u+NSLOT-1)%NSLOT, last read
-  //     in step kt-1, before its barrier), then the k-step 1 fragment reads;
+  //   k-step 0: the k-step 1 fragment reads, then the DMAs of stage
+  //     kt+NSLOT-1 (slot (u+NSLOT-1)%NSLOT, last read in step kt-1, before
+  //     its barrier);
   //   wait until stage kt+1's DMAs have landed (NSLOT-2 later stages stay
-  //   in flight), barrier;
+  //   in flight) and until this wave's own LDS reads are complete, so that
+  //   after the barrier no read of a slot about to be refilled is pending;
+  //   barrier;
   //   k-step 1: the fragment reads of k-step 0 of stage kt+1.
   // The last nk % NSLOT stages run as tail steps: every stage they need is
   // already in flight (stages up to kt+3 when the tail group starts at kt),
@@ -401,20 +408,21 @@ gemm_bf16_kernel(const uint16_t* __restrict__ A, int64_t lda,
     constexpr int u = decltype(U)::value;
     constexpr bool tail = decltype(TAIL)::value != 0;
     constexpr int nxt = (u + NSLOT - 1) % NSLOT;
-    static_assert(NDMA + NRU <= 2 * NMF, "traffic fits between the MFMAs");
+    static_assert(NDMA <= NMF && NRU <= NMF, "traffic fits between the MFMAs");
     // k-step 0
 #pragma unroll
     for (int j = 0; j < NMF; ++j) {
       mfma1(0, j);
       __builtin_amdgcn_sched_barrier(0);
-      if (!tail && j < NDMA) dma(kt + NSLOT - 1, IC<nxt>{}, j);
-      if (j >= NMF - NRU) read_unit(IC<u>{}, 1, 1, j - (NMF - NRU));
+      if (j < NRU) read_unit(IC<u>{}, 1, 1, j);
+      if (!tail && j >= NMF - NDMA) dma(kt + NSLOT - 1, IC<nxt>{}, j - (NMF - NDMA));
       __builtin_amdgcn_sched_barrier(0);
     }
     if constexpr (tail)
       wait_vmcnt<(u < 2 ? 2 - u : 0) * NDMA>();
     else
       wait_vmcnt<(NSLOT - 2) * NDMA>();
+    wait_lgkmcnt0();
     stage_barrier();
     // k-step 1
 #pragma unroll
