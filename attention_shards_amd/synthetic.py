@@ -154,6 +154,17 @@ def make_attn_inputs(seed: int, batch: int, seq: int, hidden: int,
     }
 
 
+def make_layer_inputs(seed: int, batch: int, seq: int, hidden: int,
+                      n_heads: int, head_dim: int, ffn: int, dtype: str = BF16) -> dict:
+    """One transformer layer: the attention inputs of make_attn_inputs
+    (streams 0..4) plus the full FFN weights W1[h,f], W2[f,h] ~ N(0, 0.02^2)
+    (streams 5, 6)."""
+    d = make_attn_inputs(seed, batch, seq, hidden, n_heads, head_dim, dtype)
+    d["W1"] = normal_tensor(seed, 5, (hidden, ffn), SIGMA_W, dtype)
+    d["W2"] = normal_tensor(seed, 6, (ffn, hidden), SIGMA_W, dtype)
+    return d
+
+
 def sample_rows(seed: int, n_rows: int, count: int) -> np.ndarray:
     """Seeded, sorted subset of row indices that always holds 0 and n_rows-1."""
     if count >= n_rows:

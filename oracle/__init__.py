@@ -10,7 +10,8 @@ What it follows: the page "Tensor Parallelism > Combining Column and Row
 Parallelism" (mbrenndoerfer.com), i.e. the FFN steps 1-3 (column-parallel
 W1 with a local GeLU, row-parallel W2 giving a partial sum, all-reduce), the
 multi-head attention decomposition (QKV split by heads, per-head attention,
-row-parallel output projection) and the residual added after each reduce.
+row-parallel output projection), the residual added after each reduce, and
+the layer that chains the two sub-layers.
 
 The method reaches the plain unsharded result exactly (up to rounding
 order), so every function here is that plain definition written out in
@@ -34,3 +35,4 @@ identity weights, prefix means) and brute force on tiny shapes.
 from .ffn import gelu, column_parallel, row_parallel, ffn_shard, ffn_full  # noqa: F401
 from .attention import attention_heads, attn_shard, attn_full  # noqa: F401
 from .reduce import partial_reduce  # noqa: F401
+from .layer import layer  # noqa: F401

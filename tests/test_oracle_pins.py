@@ -292,3 +292,66 @@ def test_reduce_copy_and_residual_once():
     # t partials each equal to c, residual r: out = t*c + r (r added once)
     assert np.array_equal(oracle.partial_reduce([ones * 3] * 4, ones * 5),
                           ones * 17)
+
+
+# ---------------------------------------------------------------------------
+# Layer: attention sub-layer, then FFN sub-layer, each + residual
+# ---------------------------------------------------------------------------
+
+def _layer(seed, batch, seq, h, nh, d, f):
+    a = syn.make_layer_inputs(seed, batch, seq, h, nh, d, f, dtype=syn.F32)
+    return [syn.to_f64(a[k], syn.F32) for k in ("X", "WQ", "WK", "WV", "WO", "W1", "W2")]
+
+
+def test_layer_zero_output_weights_is_identity():
+    """W_o = 0 and W2 = 0: both sub-layers add nothing, so X2 = X1 = X."""
+    X, WQ, WK, WV, WO, W1, W2 = _layer(31, 2, 5, 8, 2, 4, 16)
+    X1, X2 = oracle.layer(X, WQ, WK, WV, 0 * WO, W1, 0 * W2, 2, 5, 2, 4)
+    assert np.array_equal(X1, X) and np.array_equal(X2, X)
+
+
+@pytest.mark.parametrize("t", [1, 2, 4])
+def test_layer_is_two_sums_of_shard_partials(t):
+    """The page's layer with t GPUs: the attention partials of all shards
+    summed + X, then the FFN partials of all shards on that summed stream +
+    it.  Equals the unsharded layer up to fp64 reassociation."""
+    batch, seq, h, nh, d, f = 2, 9, 16, 4, 4, 32
+    X, WQ, WK, WV, WO, W1, W2 = _layer(32, batch, seq, h, nh, d, f)
+    X1s = oracle.partial_reduce(
+        [oracle.attn_shard(X, WQ, WK, WV, WO, batch, seq, nh, d, i, t) for i in range(t)], X)
+    fs = f // t
+    X2s = oracle.partial_reduce(
+        [oracle.ffn_shard(X1s, W1[:, i * fs:(i + 1) * fs], W2[i * fs:(i + 1) * fs])
+         for i in range(t)], X1s)
+    X1, X2 = oracle.layer(X, WQ, WK, WV, WO, W1, W2, batch, seq, nh, d)
+    assert rel_err(X1s, X1) < 1e-13 and rel_err(X2s, X2) < 1e-13
+
+
+def test_layer_brute_force_tiny():
+    """Scalar loops (math.exp, math.erf) on S=3, h=4, n_h=2, d=2, f=8."""
+    S, h, nh, d, f = 3, 4, 2, 2, 8
+    X, WQ, WK, WV, WO, W1, W2 = _layer(33, 1, S, h, nh, d, f)
+    x1 = [[float(X[r, c]) for c in range(h)] for r in range(S)]
+    for hh in range(nh):
+        cols = range(hh * d, (hh + 1) * d)
+        q = [[sum(X[r, k] * WQ[k, c] for k in range(h)) for c in cols] for r in range(S)]
+        kk = [[sum(X[r, k] * WK[k, c] for k in range(h)) for c in cols] for r in range(S)]
+        v = [[sum(X[r, k] * WV[k, c] for k in range(h)) for c in cols] for r in range(S)]
+        for r in range(S):
+            sc = [sum(q[r][e] * kk[j][e] for e in range(d)) / math.sqrt(d) for j in range(r + 1)]
+            mx = max(sc)
+            w = [math.exp(s - mx) for s in sc]
+            o = [sum(w[j] * v[j][e] for j in range(r + 1)) / sum(w) for e in range(d)]
+            for c in range(h):
+                x1[r][c] += sum(o[e] * WO[hh * d + e, c] for e in range(d))
+    x2 = [row[:] for row in x1]
+    for r in range(S):
+        g = []
+        for j in range(f):
+            z = sum(x1[r][k] * W1[k, j] for k in range(h))
+            g.append(0.5 * z * (1.0 + math.erf(z / math.sqrt(2.0))))
+        for c in range(h):
+            x2[r][c] += sum(g[j] * W2[j, c] for j in range(f))
+    X1, X2 = oracle.layer(X, WQ, WK, WV, WO, W1, W2, 1, S, nh, d)
+    assert np.max(np.abs(X1 - np.array(x1))) < 1e-13
+    assert np.max(np.abs(X2 - np.array(x2))) < 1e-13
