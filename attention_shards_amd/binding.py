@@ -39,6 +39,10 @@ SIGNATURES = {
                                _c_sz, _c_p]),
     "tp_partial_reduce": (_c_i32, [ctypes.POINTER(_c_p), _c_i32, _c_p, _c_p, _c_i64,
                                    _c_i64, _c_i32, _c_i32, _c_i32, _c_p]),
+    "tp_ffn_shard_reduce_workspace_bytes": (_c_sz, [_c_i64, _c_i64, _c_i64, _c_i32, _c_i32]),
+    "tp_ffn_shard_reduce": (_c_i32, [_c_p, _c_p, _c_p, ctypes.POINTER(_c_p), _c_p, _c_p,
+                                     _c_i64, _c_i64, _c_i64, _c_i32, _c_i32, _c_i64, _c_i32,
+                                     _c_i32, _c_i32, _c_i32, _c_p, _c_sz, _c_p]),
     "tp_status_string": (ctypes.c_char_p, [_c_i32]),
     "tp_last_error_message": (ctypes.c_char_p, []),
     "tp_abi_version": (_c_i32, []),
@@ -61,6 +65,10 @@ def load() -> ctypes.CDLL:
         if not os.path.exists(LIB_PATH):
             raise RuntimeError(
                 f"{LIB_PATH} is not built; run `python -m attention_shards_amd.build`")
+        # PyTorch ships its own HIP runtime with the same soname as the
+        # system one; importing it first makes this library bind to the
+        # runtime torch's tensors and streams live in.
+        _torch()
         lib = ctypes.CDLL(LIB_PATH)
         for name, (res, args) in SIGNATURES.items():
             fn = getattr(lib, name)
@@ -114,6 +122,11 @@ def tp_ffn_shard_workspace_bytes(tokens: int, hidden: int, ffn: int, t: int,
     return int(load().tp_ffn_shard_workspace_bytes(tokens, hidden, ffn, t, in_dtype))
 
 
+def tp_ffn_shard_reduce_workspace_bytes(tokens: int, hidden: int, ffn: int, t: int,
+                                        in_dtype: int) -> int:
+    return int(load().tp_ffn_shard_reduce_workspace_bytes(tokens, hidden, ffn, t, in_dtype))
+
+
 def tp_attn_shard_workspace_bytes(batch: int, seq: int, n_heads: int,
                                   head_dim: int, t: int) -> int:
     return int(load().tp_attn_shard_workspace_bytes(batch, seq, n_heads, head_dim, t))
@@ -160,6 +173,62 @@ def tp_ffn_shard(X, W1_i, W2_i, Y_i, i: int, t: int, workspace=None,
                                 W1_i.stride(0), in_dt, _dtype_code(Y_i),
                                 ws.data_ptr(), ws.numel(), _stream(stream)))
     return Y_i
+
+
+def tp_ffn_shard_reduce(X, W1_i, W2_i, peer_partials, residual, out, i: int,
+                        workspace=None, stream=None):
+    """out = (sum_{j != i} P_j + residual) + P_i with P_i = GeLU(X W1_i) W2_i
+    computed here and added unrounded; peer_partials is the list of the t
+    partials (entry i is not read and may be None).  Returns out."""
+    lib = load()
+    t = len(peer_partials)
+    if not 1 <= t <= TP_MAX_PARTIALS:
+        raise ValueError(f"need 1..{TP_MAX_PARTIALS} partials, got {t}")
+    _dense(X, "X")
+    _dense(W2_i, "W2_i")
+    _dense(out, "out")
+    _dev(W1_i, "W1_i")
+    if W1_i.dim() != 2 or W1_i.stride(1) != 1:
+        raise ValueError("W1_i must be 2-D with unit column stride")
+    tokens, hidden = X.shape
+    fs = W1_i.shape[1]
+    if W1_i.shape[0] != hidden or tuple(W2_i.shape) != (fs, hidden) or \
+            tuple(out.shape) != (tokens, hidden):
+        raise ValueError(f"shape mismatch: X{tuple(X.shape)} W1_i{tuple(W1_i.shape)} "
+                         f"W2_i{tuple(W2_i.shape)} out{tuple(out.shape)}")
+    in_dt = _dtype_code(X)
+    if _dtype_code(W1_i) != in_dt or _dtype_code(W2_i) != in_dt:
+        raise TypeError("X, W1_i and W2_i must share a dtype")
+    peers = [p for k, p in enumerate(peer_partials) if k != i]
+    pdt = TP_F32
+    for k, p in enumerate(peer_partials):
+        if k == i:
+            continue
+        _dense(p, f"peer_partials[{k}]")
+        if tuple(p.shape) != (tokens, hidden):
+            raise ValueError(f"peer_partials[{k}] shape {tuple(p.shape)} != {(tokens, hidden)}")
+    if peers:
+        pdt = _dtype_code(peers[0])
+        if any(_dtype_code(p) != pdt for p in peers):
+            raise TypeError("all peer partials must share a dtype")
+    rdt, rptr = TP_F32, None
+    if residual is not None:
+        _dense(residual, "residual")
+        if tuple(residual.shape) != (tokens, hidden):
+            raise ValueError("residual shape mismatch")
+        rdt, rptr = _dtype_code(residual), residual.data_ptr()
+    arr = (ctypes.c_void_p * t)(*[None if (k == i or p is None) else p.data_ptr()
+                                  for k, p in enumerate(peer_partials)])
+    ffn = fs * t
+    need = tp_ffn_shard_reduce_workspace_bytes(tokens, hidden, ffn, t, in_dt)
+    ws = _workspace(workspace, need, X.device)
+    torch = _torch()
+    with torch.cuda.device(X.device):
+        _check(lib.tp_ffn_shard_reduce(X.data_ptr(), W1_i.data_ptr(), W2_i.data_ptr(), arr,
+                                       rptr, out.data_ptr(), tokens, hidden, ffn, i, t,
+                                       W1_i.stride(0), in_dt, pdt, rdt, _dtype_code(out),
+                                       ws.data_ptr(), ws.numel(), _stream(stream)))
+    return out
 
 
 def tp_attn_shard(X, Wqkv_i, Wo_i, Y_i, batch: int, seq: int, n_heads: int,

@@ -130,6 +130,68 @@ struct EpiGelu {
   }
 };
 
+// out = S + acc: the product added to an fp32 matrix S (the pre-summed
+// other operands of a fused reduce), rounded once to the output type.
+struct EpiAdd {
+  const float* S;
+  void* out;
+  int64_t ld;  // row stride of S and out
+  int odt;     // OutType
+  __device__ void store4(int row, int col0, const float* v) const {
+    const f32x4 x = __builtin_nontemporal_load(
+        reinterpret_cast<const f32x4*>(S + (int64_t)row * ld + col0));
+    float s[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) s[e] = x[e] + v[e];
+    store_run4(out, ld, odt, row, col0, s);
+  }
+  __device__ void store8(int row, int col0, const float* v) const {
+    const f32x4* q = reinterpret_cast<const f32x4*>(S + (int64_t)row * ld + col0);
+    const f32x4 x0 = __builtin_nontemporal_load(q), x1 = __builtin_nontemporal_load(q + 1);
+    float s[8];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      s[e] = x0[e] + v[e];
+      s[4 + e] = x1[e] + v[4 + e];
+    }
+    store_run8(out, ld, odt, row, col0, s);
+  }
+  // RB rows of 8 columns (col0 < N): the loads of all rows are issued before
+  // any add, so 2*RB loads per lane are in flight; rows >= M read a clamped
+  // row and are not stored.
+  template <int RB>
+  __device__ void store8_rows(const int* row, int M, int col0, float (*v)[8]) const {
+    f32x4 x[RB][2];
+#pragma unroll
+    for (int b = 0; b < RB; ++b) {
+      const f32x4* q =
+          reinterpret_cast<const f32x4*>(S + (int64_t)min(row[b], M - 1) * ld + col0);
+      x[b][0] = __builtin_nontemporal_load(q);
+      x[b][1] = __builtin_nontemporal_load(q + 1);
+    }
+#pragma unroll
+    for (int b = 0; b < RB; ++b) {
+      float s[8];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        s[e] = x[b][0][e] + v[b][e];
+        s[4 + e] = x[b][1][e] + v[b][4 + e];
+      }
+      if (row[b] < M) store_run8(out, ld, odt, row[b], col0, s);
+    }
+  }
+};
+
+// Rows per epilogue call in the GEMM's store loop (see the kernel).
+template <class E>
+struct RowBatch {
+  static constexpr int value = 1;
+};
+template <>
+struct RowBatch<EpiAdd> {
+  static constexpr int value = 4;
+};
+
 // Scatter of the QKV projection into the attention workspace (d == 128).
 struct EpiQkv {
   QkvOut q;
@@ -487,17 +549,32 @@ gemm_bf16_kernel(const uint16_t* __restrict__ A, int64_t lda,
         stage_f[i * PITCH + ni * 32 + (lane & 31)] = acc[mi][ni][e];
       }
     asm volatile("" ::: "memory");  // keep the LDS writes before the reads
+    // An epilogue that reads memory takes RB rows per call so that the
+    // loads of several rows are in flight together.
+    constexpr int RB = RowBatch<Epi>::value;
+    static_assert((32 / ROWS_PER_PASS) % RB == 0, "row batches tile the slab");
 #pragma unroll 1
-    for (int it = 0; it < 32 / ROWS_PER_PASS; ++it) {
-      const int rr = it * ROWS_PER_PASS + lane / RUNS;
+    for (int it = 0; it < 32 / ROWS_PER_PASS; it += RB) {
       const int c8 = (lane % RUNS) * 8;
-      const int row = m0 + wr0 + mi * 32 + rr;
       const int col0 = n0 + wc0 + c8;
-      const f32x4 va = *reinterpret_cast<const f32x4*>(stage_f + rr * PITCH + c8);
-      const f32x4 vb = *reinterpret_cast<const f32x4*>(stage_f + rr * PITCH + c8 + 4);
-      if (row < M && col0 < N) {
-        float v[8] = {va[0], va[1], va[2], va[3], vb[0], vb[1], vb[2], vb[3]};
-        epi.store8(row, col0, v);
+      float v[RB][8];
+      int row[RB];
+#pragma unroll
+      for (int b = 0; b < RB; ++b) {
+        const int rr = (it + b) * ROWS_PER_PASS + lane / RUNS;
+        row[b] = m0 + wr0 + mi * 32 + rr;
+        const f32x4 va = *reinterpret_cast<const f32x4*>(stage_f + rr * PITCH + c8);
+        const f32x4 vb = *reinterpret_cast<const f32x4*>(stage_f + rr * PITCH + c8 + 4);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          v[b][e] = va[e];
+          v[b][4 + e] = vb[e];
+        }
+      }
+      if constexpr (RB == 1) {
+        if (row[0] < M && col0 < N) epi.store8(row[0], col0, v[0]);
+      } else {
+        if (col0 < N) epi.template store8_rows<RB>(row, M, col0, v);
       }
     }
     asm volatile("" ::: "memory");  // and this slab's reads before the next writes
@@ -671,6 +748,18 @@ hipError_t gemm_bf16_qkv(const uint16_t* A, int64_t lda, const uint16_t* B,
                          int64_t ldb, const QkvOut& q, int M, int N, int K,
                          hipStream_t s) {
   return dispatch_bf16(A, lda, B, ldb, M, N, K, K, EpiQkv{q}, s);
+}
+
+hipError_t gemm_bf16_add(const uint16_t* A, int64_t lda, const uint16_t* B, int64_t ldb,
+                         const float* S, void* C, int64_t ldc, OutType out, int M, int N,
+                         int K, hipStream_t s) {
+  return dispatch_bf16(A, lda, B, ldb, M, N, K, K, EpiAdd{S, C, ldc, (int)out}, s);
+}
+
+hipError_t gemm_f32_add(const float* A, int64_t lda, const float* B, int64_t ldb,
+                        const float* S, void* C, int64_t ldc, OutType out, int M, int N,
+                        int K, hipStream_t s) {
+  return launch_f32(A, lda, B, ldb, M, N, K, EpiAdd{S, C, ldc, (int)out}, s);
 }
 
 hipError_t gemm_f32(const float* A, int64_t lda, const float* B, int64_t ldb,

@@ -62,12 +62,23 @@ hipError_t gemm_f32(const float* A, int64_t lda, const float* B, int64_t ldb,
 hipError_t attention_fwd(const QkvOut& q, int batch, bool causal, uint16_t* O,
                          hipStream_t s);
 
-// out = sum_i P_i + R, fp32 accumulate.  n % 8 == 0.
+// out = sum_i P_i + R, fp32 accumulate, any n (the last n % 8 elements take
+// a scalar path).
 struct ReducePtrs {
   const void* p[64];
 };
 hipError_t partial_reduce(const ReducePtrs& ptrs, int t, int pdt,
                           const void* R, int rdt, void* out, int odt,
                           int64_t n, hipStream_t s);
+
+// C = S + A*B: the product added to an fp32 [M, N] matrix S (row stride
+// ldc, like C) and rounded once to the output type.  bf16 and fp32 inputs,
+// with the requirements of gemm_bf16_store / gemm_f32.
+hipError_t gemm_bf16_add(const uint16_t* A, int64_t lda, const uint16_t* B, int64_t ldb,
+                         const float* S, void* C, int64_t ldc, OutType out, int M, int N,
+                         int K, hipStream_t s);
+hipError_t gemm_f32_add(const float* A, int64_t lda, const float* B, int64_t ldb,
+                        const float* S, void* C, int64_t ldc, OutType out, int M, int N,
+                        int K, hipStream_t s);
 
 }  // namespace tp

@@ -61,10 +61,33 @@ __device__ __forceinline__ void store8(void* base, int64_t g, const float* v) {
   }
 }
 
+template <int DT>
+__device__ __forceinline__ float load1(const void* base, int64_t k) {
+  if (DT == DT_BF16)
+    return __uint_as_float((uint32_t)static_cast<const uint16_t*>(base)[k] << 16);
+  return static_cast<const float*>(base)[k];
+}
+
+template <int DT>
+__device__ __forceinline__ void store1(void* base, int64_t k, float v) {
+  if (DT == DT_BF16)
+    static_cast<uint16_t*>(base)[k] = (uint16_t)f2bf(v);
+  else
+    static_cast<float*>(base)[k] = v;
+}
+
 template <int PDT, int RDT, int ODT>
 __global__ void __launch_bounds__(256)
 reduce_kernel(ReducePtrs ptrs, int t, const void* R,
-              void* out, int64_t ngroups) {
+              void* out, int64_t ngroups, int tail) {
+  // the last `tail` (< 8) elements, one per thread of block 0, same order
+  if (blockIdx.x == 0 && (int)threadIdx.x < tail) {
+    const int64_t k = ngroups * 8 + threadIdx.x;
+    float acc = load1<PDT>(ptrs.p[0], k);
+    for (int i = 1; i < t; ++i) acc += load1<PDT>(ptrs.p[i], k);
+    if (RDT != DT_NONE) acc += load1<RDT>(R, k);
+    store1<ODT>(out, k, acc);
+  }
   const int64_t stride = (int64_t)gridDim.x * 256;
   for (int64_t gi = (int64_t)blockIdx.x * 256 + threadIdx.x; gi < ngroups; gi += stride) {
     float acc[8];
@@ -98,27 +121,29 @@ reduce_kernel(ReducePtrs ptrs, int t, const void* R,
 
 template <int PDT, int RDT, int ODT>
 hipError_t launch(const ReducePtrs& ptrs, int t, const void* R, void* out,
-                  int64_t ngroups, hipStream_t s) {
+                  int64_t n, hipStream_t s) {
+  const int64_t ngroups = n / 8;
   int64_t blocks = (ngroups + 255) / 256;
   if (blocks > 8192) blocks = 8192;
+  if (blocks < 1) blocks = 1;
   hipLaunchKernelGGL((reduce_kernel<PDT, RDT, ODT>), dim3((unsigned)blocks),
-                     dim3(256), 0, s, ptrs, t, R, out, ngroups);
+                     dim3(256), 0, s, ptrs, t, R, out, ngroups, (int)(n - ngroups * 8));
   return hipGetLastError();
 }
 
 template <int PDT, int RDT>
 hipError_t launch_o(const ReducePtrs& ptrs, int t, const void* R, void* out,
-                    int odt, int64_t ng, hipStream_t s) {
-  return odt == DT_BF16 ? launch<PDT, RDT, DT_BF16>(ptrs, t, R, out, ng, s)
-                        : launch<PDT, RDT, DT_F32>(ptrs, t, R, out, ng, s);
+                    int odt, int64_t n, hipStream_t s) {
+  return odt == DT_BF16 ? launch<PDT, RDT, DT_BF16>(ptrs, t, R, out, n, s)
+                        : launch<PDT, RDT, DT_F32>(ptrs, t, R, out, n, s);
 }
 
 template <int PDT>
 hipError_t launch_r(const ReducePtrs& ptrs, int t, const void* R, int rdt,
-                    void* out, int odt, int64_t ng, hipStream_t s) {
-  if (R == nullptr) return launch_o<PDT, DT_NONE>(ptrs, t, R, out, odt, ng, s);
-  return rdt == DT_BF16 ? launch_o<PDT, DT_BF16>(ptrs, t, R, out, odt, ng, s)
-                        : launch_o<PDT, DT_F32>(ptrs, t, R, out, odt, ng, s);
+                    void* out, int odt, int64_t n, hipStream_t s) {
+  if (R == nullptr) return launch_o<PDT, DT_NONE>(ptrs, t, R, out, odt, n, s);
+  return rdt == DT_BF16 ? launch_o<PDT, DT_BF16>(ptrs, t, R, out, odt, n, s)
+                        : launch_o<PDT, DT_F32>(ptrs, t, R, out, odt, n, s);
 }
 
 }  // namespace
@@ -127,9 +152,8 @@ hipError_t partial_reduce(const ReducePtrs& ptrs, int t, int pdt, const void* R,
                           int rdt, void* out, int odt, int64_t n,
                           hipStream_t s) {
   if (n == 0) return hipSuccess;
-  const int64_t ng = n / 8;
-  return pdt == DT_BF16 ? launch_r<DT_BF16>(ptrs, t, R, rdt, out, odt, ng, s)
-                        : launch_r<DT_F32>(ptrs, t, R, rdt, out, odt, ng, s);
+  return pdt == DT_BF16 ? launch_r<DT_BF16>(ptrs, t, R, rdt, out, odt, n, s)
+                        : launch_r<DT_F32>(ptrs, t, R, rdt, out, odt, n, s);
 }
 
 }  // namespace tp

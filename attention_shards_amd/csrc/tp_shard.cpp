@@ -10,6 +10,7 @@
 #include <cstdarg>
 #include <cstdint>
 #include <cstdio>
+#include <mutex>
 #include <string>
 
 #include "../../include/tp_shard.h"
@@ -113,79 +114,254 @@ size_t tp_ffn_shard_workspace_bytes(int64_t tokens, int64_t hidden, int64_t ffn,
   return (size_t)align256(tokens * (ffn / t) * esize(in_dtype));
 }
 
+}  // extern "C"
+
+namespace {
+
+// Checks shared by tp_ffn_shard and tp_ffn_shard_reduce, in the order the
+// ABI documents them.  On success *fs_out = ffn/t and *ld_w1 is resolved.
+// `out` / `out_bytes` is the output tensor checked against the inputs.
+tp_status_t check_ffn(const char* fn, const void* X, const void* W1_i, const void* W2_i,
+                      const void* out, int64_t out_bytes, int64_t tokens, int64_t hidden,
+                      int64_t ffn, int32_t i, int32_t t, int64_t* ld_w1, int32_t in_dtype,
+                      int32_t out_dtype, const void* workspace, size_t workspace_bytes,
+                      int64_t* fs_out) {
+  if (!valid_dtype(in_dtype) || !valid_dtype(out_dtype))
+    return fail(TP_ERR_DTYPE, "%s: dtype codes in=%d out=%d", fn, in_dtype, out_dtype);
+  if (t < 1 || i < 0 || i >= t) return fail(TP_ERR_SHARD, "%s: shard i=%d of t=%d", fn, i, t);
+  if (tokens < 0 || hidden <= 0 || ffn <= 0)
+    return fail(TP_ERR_SHAPE, "%s(i=%d): tokens=%lld hidden=%lld ffn=%lld", fn, i,
+                (long long)tokens, (long long)hidden, (long long)ffn);
+  if (ffn % t != 0)
+    return fail(TP_ERR_DIVISIBILITY, "%s(i=%d): ffn=%lld not divisible by t=%d", fn, i,
+                (long long)ffn, t);
+  const int64_t fs = ffn / t;
+  const int64_t es = esize(in_dtype);
+  const int64_t vec = 16 / es;
+  if (*ld_w1 == 0) *ld_w1 = fs;
+  if (hidden % vec || fs % vec || *ld_w1 % vec || *ld_w1 < fs)
+    return fail(TP_ERR_SHAPE,
+                "%s(i=%d): hidden=%lld, ffn/t=%lld and ld_w1=%lld must be multiples "
+                "of %lld with ld_w1 >= ffn/t",
+                fn, i, (long long)hidden, (long long)fs, (long long)*ld_w1, (long long)vec);
+  if (tokens > kInt32Max || hidden > kInt32Max || fs > kInt32Max)
+    return fail(TP_ERR_SHAPE, "%s(i=%d): a dimension exceeds 2^31-1", fn, i);
+  *fs_out = fs;
+  if (tokens == 0) return ok();
+  if (!X || !W1_i || !W2_i || !out)
+    return fail(TP_ERR_NULL, "%s(i=%d): NULL tensor pointer", fn, i);
+  if (!workspace) return fail(TP_ERR_WORKSPACE, "%s(i=%d): NULL workspace", fn, i);
+  if (!aligned16(X) || !aligned16(W1_i) || !aligned16(W2_i) || !aligned16(out) ||
+      !aligned16(workspace))
+    return fail(TP_ERR_ALIGNMENT, "%s(i=%d): pointers must be 16-byte aligned", fn, i);
+  const size_t need = tp_ffn_shard_workspace_bytes(tokens, hidden, ffn, t, in_dtype);
+  if (workspace_bytes < need)
+    return fail(TP_ERR_WORKSPACE, "%s(i=%d): workspace %zu bytes < %zu needed", fn, i,
+                workspace_bytes, need);
+  const Range rx = range_of(X, tokens * hidden * es);
+  const Range rw1 = range_of(W1_i, span_bytes(hidden, fs, *ld_w1, es));
+  const Range rw2 = range_of(W2_i, fs * hidden * es);
+  const Range ry = range_of(out, out_bytes);
+  const Range rws = range_of(workspace, tokens * fs * es);
+  if (overlap(ry, rx) || overlap(ry, rw1) || overlap(ry, rw2) || overlap(ry, rws))
+    return fail(TP_ERR_ALIAS, "%s(i=%d): the output overlaps an input or the workspace", fn, i);
+  if (overlap(rws, rx) || overlap(rws, rw1) || overlap(rws, rw2))
+    return fail(TP_ERR_ALIAS, "%s(i=%d): workspace overlaps an input", fn, i);
+  return ok();
+}
+
+// One side stream and two events per device for the fused FFN + reduce: the
+// sum of the other operands runs on the side stream while GEMM1 runs on the
+// caller's stream.  Created on first use, at the default priority, kept
+// until the process ends; `m` serializes the enqueue sequences of calls from
+// several host threads (the events are reused).
+struct SideStream {
+  std::mutex m;
+  bool ready = false;
+  hipStream_t s = nullptr;
+  hipEvent_t inputs_ready = nullptr, others_summed = nullptr;
+};
+constexpr int kMaxDevices = 64;
+SideStream g_side[kMaxDevices];
+
+hipError_t side_stream(int dev, SideStream** out) {
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  SideStream& ss = g_side[dev];
+  *out = &ss;
+  if (ss.ready) return hipSuccess;
+  hipError_t e = hipStreamCreateWithFlags(&ss.s, hipStreamNonBlocking);
+  if (e == hipSuccess) e = hipEventCreateWithFlags(&ss.inputs_ready, hipEventDisableTiming);
+  if (e == hipSuccess) e = hipEventCreateWithFlags(&ss.others_summed, hipEventDisableTiming);
+  if (e == hipSuccess) ss.ready = true;
+  return e;
+}
+
+// GEMM1 + GeLU into the workspace (both input dtypes).
+hipError_t ffn_gemm1(const void* X, const void* W1_i, int64_t ld_w1, void* workspace, int M,
+                     int H, int F, int32_t in_dtype, hipStream_t s) {
+  if (in_dtype == TP_BF16)
+    return tp::gemm_bf16_gelu(static_cast<const uint16_t*>(X), H,
+                              static_cast<const uint16_t*>(W1_i), ld_w1,
+                              static_cast<uint16_t*>(workspace), F, M, F, H, s);
+  return tp::gemm_f32(static_cast<const float*>(X), H, static_cast<const float*>(W1_i), ld_w1,
+                      workspace, F, tp::OUT_F32, true, M, F, H, s);
+}
+
+}  // namespace
+
+extern "C" {
+
 tp_status_t tp_ffn_shard(const void* X, const void* W1_i, const void* W2_i,
                          void* Y_i, int64_t tokens, int64_t hidden, int64_t ffn,
                          int32_t i, int32_t t, int64_t ld_w1, int32_t in_dtype,
                          int32_t out_dtype, void* workspace,
                          size_t workspace_bytes, void* stream) {
   try {
-    if (!valid_dtype(in_dtype) || !valid_dtype(out_dtype))
-      return fail(TP_ERR_DTYPE, "tp_ffn_shard: dtype codes in=%d out=%d", in_dtype, out_dtype);
-    if (t < 1 || i < 0 || i >= t)
-      return fail(TP_ERR_SHARD, "tp_ffn_shard: shard i=%d of t=%d", i, t);
-    if (tokens < 0 || hidden <= 0 || ffn <= 0)
-      return fail(TP_ERR_SHAPE, "tp_ffn_shard(i=%d): tokens=%lld hidden=%lld ffn=%lld", i,
-                  (long long)tokens, (long long)hidden, (long long)ffn);
-    if (ffn % t != 0)
-      return fail(TP_ERR_DIVISIBILITY, "tp_ffn_shard(i=%d): ffn=%lld not divisible by t=%d", i,
-                  (long long)ffn, t);
-    const int64_t fs = ffn / t;
-    const int64_t es = esize(in_dtype);
-    const int64_t vec = 16 / es;
-    if (ld_w1 == 0) ld_w1 = fs;
-    if (hidden % vec || fs % vec || ld_w1 % vec || ld_w1 < fs)
-      return fail(TP_ERR_SHAPE,
-                  "tp_ffn_shard(i=%d): hidden=%lld, ffn/t=%lld and ld_w1=%lld must be multiples "
-                  "of %lld with ld_w1 >= ffn/t",
-                  i, (long long)hidden, (long long)fs, (long long)ld_w1, (long long)vec);
-    if (tokens > kInt32Max || hidden > kInt32Max || fs > kInt32Max)
-      return fail(TP_ERR_SHAPE, "tp_ffn_shard(i=%d): a dimension exceeds 2^31-1", i);
-    if (tokens == 0) return ok();
-    if (!X || !W1_i || !W2_i || !Y_i)
-      return fail(TP_ERR_NULL, "tp_ffn_shard(i=%d): NULL tensor pointer", i);
-    if (!workspace)
-      return fail(TP_ERR_WORKSPACE, "tp_ffn_shard(i=%d): NULL workspace", i);
-    if (!aligned16(X) || !aligned16(W1_i) || !aligned16(W2_i) || !aligned16(Y_i) ||
-        !aligned16(workspace))
-      return fail(TP_ERR_ALIGNMENT, "tp_ffn_shard(i=%d): pointers must be 16-byte aligned", i);
-    const size_t need = tp_ffn_shard_workspace_bytes(tokens, hidden, ffn, t, in_dtype);
-    if (workspace_bytes < need)
-      return fail(TP_ERR_WORKSPACE, "tp_ffn_shard(i=%d): workspace %zu bytes < %zu needed", i,
-                  workspace_bytes, need);
-    const Range rx = range_of(X, tokens * hidden * es);
-    const Range rw1 = range_of(W1_i, span_bytes(hidden, fs, ld_w1, es));
-    const Range rw2 = range_of(W2_i, fs * hidden * es);
-    const Range ry = range_of(Y_i, tokens * hidden * esize(out_dtype));
-    const Range rws = range_of(workspace, tokens * fs * es);
-    if (overlap(ry, rx) || overlap(ry, rw1) || overlap(ry, rw2) || overlap(ry, rws))
-      return fail(TP_ERR_ALIAS, "tp_ffn_shard(i=%d): Y_i overlaps an input or the workspace", i);
-    if (overlap(rws, rx) || overlap(rws, rw1) || overlap(rws, rw2))
-      return fail(TP_ERR_ALIAS, "tp_ffn_shard(i=%d): workspace overlaps an input", i);
+    int64_t fs = 0;
+    const tp_status_t st =
+        check_ffn("tp_ffn_shard", X, W1_i, W2_i, Y_i, tokens * hidden * esize(out_dtype),
+                  tokens, hidden, ffn, i, t, &ld_w1, in_dtype, out_dtype, workspace,
+                  workspace_bytes, &fs);
+    if (st != TP_SUCCESS || tokens == 0) return st;
 
     hipStream_t s = static_cast<hipStream_t>(stream);
     (void)hipGetLastError();
     const int M = (int)tokens, H = (int)hidden, F = (int)fs;
-    hipError_t e;
-    if (in_dtype == TP_BF16) {
-      uint16_t* zh = static_cast<uint16_t*>(workspace);
-      e = tp::gemm_bf16_gelu(static_cast<const uint16_t*>(X), H,
-                             static_cast<const uint16_t*>(W1_i), ld_w1, zh, F, M, F, H, s);
-      if (e != hipSuccess) return hip_status(e, "tp_ffn_shard: GEMM1 launch");
-      e = tp::gemm_bf16_store(zh, F, static_cast<const uint16_t*>(W2_i), H, Y_i, H,
-                              out_dtype == TP_F32 ? tp::OUT_F32 : tp::OUT_BF16, M, H, F, s);
-      if (e != hipSuccess) return hip_status(e, "tp_ffn_shard: GEMM2 launch");
-    } else {
-      float* zh = static_cast<float*>(workspace);
-      e = tp::gemm_f32(static_cast<const float*>(X), H, static_cast<const float*>(W1_i), ld_w1,
-                       zh, F, tp::OUT_F32, true, M, F, H, s);
-      if (e != hipSuccess) return hip_status(e, "tp_ffn_shard: GEMM1 launch");
-      e = tp::gemm_f32(zh, F, static_cast<const float*>(W2_i), H, Y_i, H,
-                       out_dtype == TP_F32 ? tp::OUT_F32 : tp::OUT_BF16, false, M, H, F, s);
-      if (e != hipSuccess) return hip_status(e, "tp_ffn_shard: GEMM2 launch");
-    }
-    return ok();
+    hipError_t e = ffn_gemm1(X, W1_i, ld_w1, workspace, M, H, F, in_dtype, s);
+    if (e != hipSuccess) return hip_status(e, "tp_ffn_shard: GEMM1 launch");
+    const tp::OutType ot = out_dtype == TP_F32 ? tp::OUT_F32 : tp::OUT_BF16;
+    if (in_dtype == TP_BF16)
+      e = tp::gemm_bf16_store(static_cast<const uint16_t*>(workspace), F,
+                              static_cast<const uint16_t*>(W2_i), H, Y_i, H, ot, M, H, F, s);
+    else
+      e = tp::gemm_f32(static_cast<const float*>(workspace), F,
+                       static_cast<const float*>(W2_i), H, Y_i, H, ot, false, M, H, F, s);
+    return hip_status(e, "tp_ffn_shard: GEMM2 launch");
   } catch (...) {
     return fail(TP_ERR_HIP, "tp_ffn_shard: internal exception");
+  }
+}
+
+size_t tp_ffn_shard_reduce_workspace_bytes(int64_t tokens, int64_t hidden, int64_t ffn,
+                                           int32_t t, int32_t in_dtype) {
+  const size_t z = tp_ffn_shard_workspace_bytes(tokens, hidden, ffn, t, in_dtype);
+  if (z == 0 || hidden <= 0) return 0;
+  return z + (size_t)align256(tokens * hidden * 4);
+}
+
+tp_status_t tp_ffn_shard_reduce(const void* X, const void* W1_i, const void* W2_i,
+                                const void* const* peer_partials,
+                                const void* residual, void* out, int64_t tokens,
+                                int64_t hidden, int64_t ffn, int32_t i, int32_t t,
+                                int64_t ld_w1, int32_t in_dtype,
+                                int32_t partial_dtype, int32_t residual_dtype,
+                                int32_t out_dtype, void* workspace,
+                                size_t workspace_bytes, void* stream) {
+  const char* fn = "tp_ffn_shard_reduce";
+  try {
+    if (!valid_dtype(partial_dtype) || (residual && !valid_dtype(residual_dtype)))
+      return fail(TP_ERR_DTYPE, "%s: dtype codes partial=%d residual=%d", fn, partial_dtype,
+                  residual_dtype);
+    if (t > TP_MAX_PARTIALS)
+      return fail(TP_ERR_SHARD, "%s: t=%d above %d", fn, t, TP_MAX_PARTIALS);
+    int64_t fs = 0;
+    const int64_t n = tokens * hidden;
+    const int64_t ob = esize(out_dtype);
+    // the GEMM checks, with the Z part of the workspace
+    tp_status_t st = check_ffn(fn, X, W1_i, W2_i, out, n * ob, tokens, hidden, ffn, i, t,
+                               &ld_w1, in_dtype, out_dtype, workspace, workspace_bytes, &fs);
+    if (st != TP_SUCCESS || tokens == 0) return st;
+    const size_t need = tp_ffn_shard_reduce_workspace_bytes(tokens, hidden, ffn, t, in_dtype);
+    if (workspace_bytes < need)
+      return fail(TP_ERR_WORKSPACE, "%s(i=%d): workspace %zu bytes < %zu needed", fn, i,
+                  workspace_bytes, need);
+    if (t > 1 && !peer_partials) return fail(TP_ERR_NULL, "%s(i=%d): NULL peer array", fn, i);
+    const size_t z_bytes = tp_ffn_shard_workspace_bytes(tokens, hidden, ffn, t, in_dtype);
+    float* S = reinterpret_cast<float*>(static_cast<char*>(workspace) + z_bytes);
+    const Range ro = range_of(out, n * ob);
+    const Range rws = range_of(workspace, (int64_t)need);
+    if (overlap(ro, rws))
+      return fail(TP_ERR_ALIAS, "%s(i=%d): out overlaps the workspace", fn, i);
+    const int64_t pb = esize(partial_dtype);
+    tp::ReducePtrs ptrs;
+    int np = 0;  // the other shards' partials, in j order
+    for (int k = 0; k < t; ++k) {
+      if (k == i) continue;
+      const void* p = peer_partials[k];
+      if (!p) return fail(TP_ERR_NULL, "%s(i=%d): peer_partials[%d] is NULL", fn, i, k);
+      if (!aligned16(p))
+        return fail(TP_ERR_ALIGNMENT, "%s(i=%d): peer_partials[%d] not 16-byte aligned", fn,
+                    i, k);
+      const Range rp = range_of(p, n * pb);
+      if (overlap(ro, rp) && !(p == out && pb == ob))
+        return fail(TP_ERR_ALIAS, "%s(i=%d): out overlaps peer_partials[%d]", fn, i, k);
+      if (overlap(rws, rp))
+        return fail(TP_ERR_ALIAS, "%s(i=%d): workspace overlaps peer_partials[%d]", fn, i, k);
+      ptrs.p[np++] = p;
+    }
+    for (int k = np; k < TP_MAX_PARTIALS; ++k) ptrs.p[k] = nullptr;
+    if (residual) {
+      if (!aligned16(residual))
+        return fail(TP_ERR_ALIGNMENT, "%s(i=%d): residual not 16-byte aligned", fn, i);
+      const int64_t rb = esize(residual_dtype);
+      const Range rr = range_of(residual, n * rb);
+      if (overlap(ro, rr) && !(residual == out && rb == ob))
+        return fail(TP_ERR_ALIAS, "%s(i=%d): out overlaps the residual", fn, i);
+      if (overlap(rws, rr))
+        return fail(TP_ERR_ALIAS, "%s(i=%d): workspace overlaps the residual", fn, i);
+    }
+
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    (void)hipGetLastError();
+    const int M = (int)tokens, H = (int)hidden, F = (int)fs;
+    const tp::OutType ot = out_dtype == TP_F32 ? tp::OUT_F32 : tp::OUT_BF16;
+    auto gemm2_store = [&]() {
+      return in_dtype == TP_BF16
+                 ? tp::gemm_bf16_store(static_cast<const uint16_t*>(workspace), F,
+                                       static_cast<const uint16_t*>(W2_i), H, out, H, ot, M, H,
+                                       F, s)
+                 : tp::gemm_f32(static_cast<const float*>(workspace), F,
+                                static_cast<const float*>(W2_i), H, out, H, ot, false, M, H, F,
+                                s);
+    };
+    if (np == 0 && !residual) {  // nothing else to add: the plain shard
+      hipError_t e = ffn_gemm1(X, W1_i, ld_w1, workspace, M, H, F, in_dtype, s);
+      if (e == hipSuccess) e = gemm2_store();
+      return hip_status(e, "tp_ffn_shard_reduce: launch");
+    }
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_status(e, "tp_ffn_shard_reduce: hipGetDevice");
+    SideStream* ss = nullptr;
+    std::lock_guard<std::mutex> lock(g_side[dev < 0 || dev >= kMaxDevices ? 0 : dev].m);
+    e = side_stream(dev, &ss);
+    if (e != hipSuccess) return hip_status(e, "tp_ffn_shard_reduce: side stream");
+    // S = (other partials, j order) + residual on the side stream, once the
+    // caller's stream has reached this call; GEMM1 meanwhile on the caller's.
+    e = hipEventRecord(ss->inputs_ready, s);
+    if (e == hipSuccess) e = ffn_gemm1(X, W1_i, ld_w1, workspace, M, H, F, in_dtype, s);
+    if (e == hipSuccess) e = hipStreamWaitEvent(ss->s, ss->inputs_ready, 0);
+    if (e == hipSuccess) {
+      if (np > 0)
+        e = tp::partial_reduce(ptrs, np, partial_dtype, residual, residual_dtype, S, TP_F32, n,
+                               ss->s);
+      else {  // only the residual: S = residual in fp32
+        ptrs.p[0] = residual;
+        e = tp::partial_reduce(ptrs, 1, residual_dtype, nullptr, TP_F32, S, TP_F32, n, ss->s);
+      }
+    }
+    if (e == hipSuccess) e = hipEventRecord(ss->others_summed, ss->s);
+    if (e == hipSuccess) e = hipStreamWaitEvent(s, ss->others_summed, 0);
+    if (e == hipSuccess)
+      e = in_dtype == TP_BF16
+              ? tp::gemm_bf16_add(static_cast<const uint16_t*>(workspace), F,
+                                  static_cast<const uint16_t*>(W2_i), H, S, out, H, ot, M, H, F,
+                                  s)
+              : tp::gemm_f32_add(static_cast<const float*>(workspace), F,
+                                 static_cast<const float*>(W2_i), H, S, out, H, ot, M, H, F, s);
+    return hip_status(e, "tp_ffn_shard_reduce: launch");
+  } catch (...) {
+    return fail(TP_ERR_HIP, "tp_ffn_shard_reduce: internal exception");
   }
 }
 

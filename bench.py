@@ -13,7 +13,9 @@ Workload (one "step"): FFN shard i=3 of t=8 at hidden 4096, ffn 16384,
      before timing: they stand for what the peers would contribute.
 value = algorithmic FFN FLOPs of the shard (4*M*h*f/t) / wall time per step.
 
-The same run also times the attention shard (t=8, 8 of 64 heads of 128,
+The same run also times that step with the sum fused into the second GEMM's
+epilogue (tp_ffn_shard_reduce; rows.ffn_shard_reduce_fused), the attention
+shard (t=8, 8 of 64 heads of 128,
 hidden 8192, 2048 tokens, causal) and reports it under "rows", and, on rank 0
 at N=1, times the fp64 CPU oracle on a bounded sample of the FFN workload
 ("cpu_baseline").  Prints ONE JSON line.
@@ -157,6 +159,41 @@ def sweep(path, steps, warmup):
 
 
 COPY_BYTES = 1 << 30
+
+
+def fused_vs_unfused_large(steps, warmup):
+    """Timing only (device-generated inputs): the FFN step of the four-way
+    layer shape (8192 tokens, hidden 12288, ffn 49152, shard 0 of 4, bf16
+    partials and residual, fp32 out), unfused (tp_ffn_shard + reduce) and
+    fused (tp_ffn_shard_reduce)."""
+    import torch
+    from attention_shards_amd import binding as B
+    M, h, f, t, i = 8192, 12288, 49152, 4, 0
+    fs = f // t
+    g = torch.Generator(device="cuda").manual_seed(5)
+    X = torch.randn(M, h, device="cuda", generator=g).to(torch.bfloat16)
+    W1 = (torch.randn(h, fs, device="cuda", generator=g) * 0.02).to(torch.bfloat16)
+    W2 = (torch.randn(fs, h, device="cuda", generator=g) * 0.02).to(torch.bfloat16)
+    R = torch.randn(M, h, device="cuda", generator=g).to(torch.bfloat16)
+    parts = [torch.randn(M, h, device="cuda", generator=g).to(torch.bfloat16) for _ in range(t)]
+    out = torch.empty(M, h, device="cuda")
+    ws = torch.empty(B.tp_ffn_shard_reduce_workspace_bytes(M, h, f, t, B.TP_BF16),
+                     dtype=torch.uint8, device="cuda")
+
+    def unfused():
+        B.tp_ffn_shard(X, W1, W2, parts[i], i, t, workspace=ws)
+        B.tp_partial_reduce(parts, R, out)
+
+    peers = [None if j == i else parts[j] for j in range(t)]
+    un_ms = time_events(unfused, steps, warmup)
+    fu_ms = time_events(lambda: B.tp_ffn_shard_reduce(X, W1, W2, peers, R, out, i, workspace=ws),
+                        steps, warmup)
+    fl = ffn_flops(M, h, f, t)
+    del X, W1, W2, R, parts, peers, out, ws
+    torch.cuda.empty_cache()
+    return {"workload": "t4_i0_h12288_f49152_tokens8192", "unfused_ms": round(un_ms, 4),
+            "fused_ms": round(fu_ms, 4), "unfused_tflops": round(fl / (un_ms * 1e-3) / 1e12, 1),
+            "fused_tflops": round(fl / (fu_ms * 1e-3) / 1e12, 1)}
 
 
 def copy_calibration():
@@ -338,8 +375,21 @@ def main():
     ffn_tf = fl / (ffn_ms * 1e-3) / 1e12
     red_bytes = (t * 2 + 2 + 4) * M * h
     red_gbs = red_bytes / (red_ms * 1e-3) / 1e9
-    del parts, W1v, W2v, W1, W2, ws, out
+
+    # The same step with the sum fused into GEMM2's epilogue: this shard's
+    # partial is added from the accumulators and never stored or re-read.
+    peers = [None if j == i else parts[j] for j in range(t)]
+    wsf = torch.empty(B.tp_ffn_shard_reduce_workspace_bytes(M, h, f, t, B.TP_BF16),
+                      dtype=torch.uint8, device="cuda")
+    fused_ms = time_events(lambda: B.tp_ffn_shard_reduce(X, W1v[i], W2v[i], peers, R, out, i,
+                                                         workspace=wsf),
+                           args.steps, args.warmup)
+    fused_row = {"ms": round(fused_ms, 5), "tflops": round(fl / (fused_ms * 1e-3) / 1e12, 2),
+                 "unfused_ms": round(ffn_ms + red_ms, 5),
+                 "hbm_bytes_saved": 2 * 2 * M * h}
+    del parts, peers, W1v, W2v, W1, W2, ws, wsf, out
     torch.cuda.empty_cache()
+    fused_row["large"] = fused_vs_unfused_large(max(5, args.steps // 5), 3)
 
     # ---------------- attention shard ----------------
     attn_row = None
@@ -397,6 +447,7 @@ def main():
                                "gbs": round(red_gbs, 1),
                                "frac_hbm_peak": round(red_gbs / PEAK_HBM_GBS, 4),
                                "bound": "hbm"},
+            "ffn_shard_reduce_fused": fused_row,
             "attn_shard": attn_row,
         },
     }

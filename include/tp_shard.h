@@ -43,7 +43,7 @@
 extern "C" {
 #endif
 
-#define TP_ABI_VERSION 1
+#define TP_ABI_VERSION 2
 #define TP_MAX_PARTIALS 64
 
 /* Element types of tensors crossing the ABI. */
@@ -73,7 +73,9 @@ typedef enum {
  * Computes, for this GPU i of t,
  *     Y_i = GeLU(X * W1_i) * W2_i
  * with GeLU(z) = 0.5 z (1 + erf(z / sqrt 2)) (the exact erf form) applied in
- * fp32 to the fp32-accumulated product, and no biases.
+ * fp32 to the fp32-accumulated product, and no biases.  Phi(z) is evaluated
+ * with the erfc approximation of Abramowitz & Stegun 7.1.26, so the GeLU
+ * value is within 3.2e-7 |z| of the exact one.
  *
  *   X     [tokens, hidden]          full input, replicated on every GPU
  *   W1_i  [hidden, ffn/t]           columns [i*ffn/t, (i+1)*ffn/t) of W1;
@@ -167,6 +169,52 @@ tp_status_t tp_partial_reduce(const void* const* partials, int32_t t,
                               int64_t cols, int32_t partial_dtype,
                               int32_t residual_dtype, int32_t out_dtype,
                               void* stream);
+
+/* ------------------------------------------------------------------------
+ * FFN shard fused with the sum of the partials and the residual: the
+ * one-GPU counterpart of overlapping the row-parallel product with the
+ * all-reduce (the page's note on hiding communication behind the GEMMs).
+ * ------------------------------------------------------------------------
+ *     out = ((sum over j != i, in j order, of P_j) + residual) + P_i
+ * where P_i = GeLU(X * W1_i) * W2_i is computed as tp_ffn_shard computes
+ * Y_i but added from its fp32 accumulators (never rounded or stored), and
+ * P_j (j != i) are the other shards' partials, read from peer_partials[j].
+ * Accumulation is fp32 in the order written; out is rounded once to
+ * out_dtype.  The sum of the other operands runs on a second stream of the
+ * library (one per device, created on first use and kept until the process
+ * ends) concurrently with the first GEMM; the second GEMM's epilogue adds
+ * it, so neither Y_i nor a separate pass over all t partials goes through
+ * memory after the product.  Calls from several host threads are
+ * serialized while they enqueue.
+ *
+ *   X, W1_i, W2_i, tokens, hidden, ffn, i, t, ld_w1, in_dtype:
+ *                  as for tp_ffn_shard
+ *   peer_partials  HOST array of t device pointers, each [tokens, hidden] of
+ *                  partial_dtype; entry i is not read (may be NULL);
+ *                  1 <= t <= TP_MAX_PARTIALS (may be NULL when t == 1)
+ *   residual       device [tokens, hidden] of residual_dtype, or NULL
+ *   out            device [tokens, hidden] of out_dtype; it MAY be the same
+ *                  buffer as the residual or a peer partial when the element
+ *                  sizes match; any other overlap with an input, a peer
+ *                  partial, the residual or the workspace is TP_ERR_ALIAS,
+ *                  and so is a workspace that overlaps a peer partial or the
+ *                  residual
+ *   workspace      at least tp_ffn_shard_reduce_workspace_bytes(...) bytes:
+ *                  GeLU(Z_i) as for tp_ffn_shard, then the fp32 sum of the
+ *                  other operands [tokens, hidden]
+ * Shape rules: those of tp_ffn_shard.
+ */
+size_t tp_ffn_shard_reduce_workspace_bytes(int64_t tokens, int64_t hidden, int64_t ffn,
+                                           int32_t t, int32_t in_dtype);
+
+tp_status_t tp_ffn_shard_reduce(const void* X, const void* W1_i, const void* W2_i,
+                                const void* const* peer_partials,
+                                const void* residual, void* out, int64_t tokens,
+                                int64_t hidden, int64_t ffn, int32_t i, int32_t t,
+                                int64_t ld_w1, int32_t in_dtype,
+                                int32_t partial_dtype, int32_t residual_dtype,
+                                int32_t out_dtype, void* workspace,
+                                size_t workspace_bytes, void* stream);
 
 /* Static text for a status code ("TP_SUCCESS", ...). Never NULL. */
 const char* tp_status_string(int32_t status);

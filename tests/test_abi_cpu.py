@@ -203,3 +203,66 @@ def test_missing_library_fails_loudly(monkeypatch):
     monkeypatch.setattr(B, "_lib", None)
     with pytest.raises(RuntimeError, match="not built"):
         B.load()
+
+
+P1, P3, RR = (0x10_0000_0000 * k for k in range(7, 10))   # more fake addresses
+
+
+def ffn_reduce(lib, **kw):
+    a = dict(X=X, W1=W1, W2=W2, peers=[None, P1, 0x10_0000_0000 * 12, P3], R=RR, out=Y,
+             tokens=64, hidden=64, ffn=256, i=0, t=4, ld=0, din=B.TP_BF16,
+             pdt=B.TP_BF16, rdt=B.TP_BF16, odt=B.TP_F32, ws=WS, wsb=1 << 30)
+    a.update(kw)
+    peers = a["peers"]
+    arr = (ctypes.c_void_p * len(peers))(*peers) if peers is not None else None
+    st = lib.tp_ffn_shard_reduce(a["X"], a["W1"], a["W2"], arr, a["R"], a["out"],
+                                 a["tokens"], a["hidden"], a["ffn"], a["i"], a["t"], a["ld"],
+                                 a["din"], a["pdt"], a["rdt"], a["odt"], a["ws"], a["wsb"],
+                                 None)
+    return st, lib.tp_last_error_message().decode()
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(pdt=5), "TP_ERR_DTYPE"),
+    (dict(rdt=5), "TP_ERR_DTYPE"),
+    (dict(odt=5), "TP_ERR_DTYPE"),
+    (dict(t=65, ffn=65 * 8, peers=[P1] * 65), "TP_ERR_SHARD"),
+    (dict(i=4), "TP_ERR_SHARD"),
+    (dict(ffn=250), "TP_ERR_DIVISIBILITY"),
+    (dict(hidden=60), "TP_ERR_SHAPE"),
+    (dict(X=None), "TP_ERR_NULL"),
+    (dict(peers=None), "TP_ERR_NULL"),
+    (dict(peers=[None, P1, None, P3]), "TP_ERR_NULL"),     # a peer other than i missing
+    (dict(ws=None), "TP_ERR_WORKSPACE"),
+    (dict(peers=[None, P1 + 4, P1 + (1 << 20), P3]), "TP_ERR_ALIGNMENT"),
+    (dict(R=RR + 8), "TP_ERR_ALIGNMENT"),
+    (dict(out=X + 64), "TP_ERR_ALIAS"),                    # output inside X
+    (dict(out=P1 + 256), "TP_ERR_ALIAS"),                  # output inside a peer
+    (dict(out=P1), "TP_ERR_ALIAS"),                        # same address, fp32 over bf16
+    (dict(out=RR + 16), "TP_ERR_ALIAS"),                   # output inside the residual
+    (dict(ws=P3 + 1024), "TP_ERR_ALIAS"),                  # workspace inside a peer
+    (dict(ws=RR), "TP_ERR_ALIAS"),                         # workspace on the residual
+    (dict(out=WS + 64 * 64 * 2 + 512), "TP_ERR_ALIAS"),    # output on the fp32 sum area
+])
+def test_ffn_reduce_rejects(lib, kw, code):
+    st, msg = ffn_reduce(lib, **kw)
+    assert B.STATUS[st] == code, msg
+    assert msg
+
+
+def test_ffn_reduce_workspace_query(lib):
+    z = 4096 * 2048 * 2
+    assert lib.tp_ffn_shard_reduce_workspace_bytes(4096, 4096, 16384, 8, B.TP_BF16) == \
+        z + 4096 * 4096 * 4
+    assert lib.tp_ffn_shard_reduce_workspace_bytes(10, 8, 20, 3, B.TP_BF16) == 0
+
+
+def test_ffn_reduce_small_workspace(lib):
+    need = lib.tp_ffn_shard_reduce_workspace_bytes(64, 64, 256, 4, B.TP_BF16)
+    st, msg = ffn_reduce(lib, wsb=need - 1)
+    assert B.STATUS[st] == "TP_ERR_WORKSPACE", msg
+
+
+def test_ffn_reduce_zero_tokens_is_a_no_op(lib):
+    st, msg = ffn_reduce(lib, tokens=0, X=None, out=None, ws=None, peers=None)
+    assert st == 0, msg
