@@ -56,10 +56,25 @@ hipError_t gemm_f32(const float* A, int64_t lda, const float* B, int64_t ldb,
                     void* C, int64_t ldc, OutType out, bool gelu, int M, int N,
                     int K, hipStream_t s);
 
+// How the attention kernel splits its work: query blocks of 128, key ranges
+// cut into chunks of `ch` tiles of 64 keys, one workgroup per (query block,
+// chunk, sequence*head).  The same function sizes the workspace and
+// launches the kernel.
+struct AttnSplit {
+  int32_t nqb;      // query blocks per sequence
+  int32_t ch;       // key tiles per chunk
+  int32_t n_items;  // workgroups of the attention kernel
+  int32_t nbh;      // batch * local heads
+};
+AttnSplit attn_split(int batch, int seq, int nl, bool causal);
+// Bytes for the chunks' partial results (the larger of causal and full).
+int64_t attn_partial_bytes(int batch, int seq, int nl);
+
 // Causal / full attention over the QKV workspace; writes O as a bf16 hi/lo
 // pair [batch*seq, 2*nl*d]: O_hi in columns [0, nl*d), O_lo in
-// [nl*d, 2*nl*d).  d must be 128.
-hipError_t attention_fwd(const QkvOut& q, int batch, bool causal, uint16_t* O,
+// [nl*d, 2*nl*d).  d must be 128.  `part` (attn_partial_bytes, 16-byte
+// aligned) holds the partial results of split query blocks.
+hipError_t attention_fwd(const QkvOut& q, int batch, bool causal, uint16_t* O, float* part,
                          hipStream_t s);
 
 // out = sum_i P_i + R, fp32 accumulate, any n (the last n % 8 elements take

@@ -67,15 +67,17 @@ int64_t align256(int64_t b) { return (b + 255) / 256 * 256; }
 
 // Attention workspace: six [batch*nl, seq_pad, d] 16-bit arrays (Q, K, V^T as
 // hi/lo pairs) followed by O [batch*seq, 2*nl*d] bf16 (hi half, lo half).
+// ... followed by the partial results of split query blocks (fp32).
 struct AttnLayout {
-  int64_t seq_pad, part_bytes, o_bytes, total;
+  int64_t seq_pad, part_bytes, o_bytes, split_bytes, total;
 };
 AttnLayout attn_layout(int64_t batch, int64_t seq, int64_t nl, int64_t d) {
   AttnLayout L;
   L.seq_pad = (seq + kAttnKeyTile - 1) / kAttnKeyTile * kAttnKeyTile;
   L.part_bytes = align256(batch * nl * L.seq_pad * d * 2);
   L.o_bytes = align256(batch * seq * 2 * nl * d * 2);
-  L.total = 6 * L.part_bytes + L.o_bytes;
+  L.split_bytes = align256(tp::attn_partial_bytes((int)batch, (int)seq, (int)nl));
+  L.total = 6 * L.part_bytes + L.o_bytes + L.split_bytes;
   return L;
 }
 
@@ -449,7 +451,8 @@ tp_status_t tp_attn_shard(const void* X, const void* Wqkv_i, const void* Wo_i,
                                      static_cast<const uint16_t*>(Wqkv_i), nqkv, q,
                                      (int)tokens, (int)nqkv, (int)hidden, s);
     if (e != hipSuccess) return hip_status(e, "tp_attn_shard: QKV launch");
-    e = tp::attention_fwd(q, (int)batch, causal != 0, O, s);
+    float* part = reinterpret_cast<float*>(ws + 6 * L.part_bytes + L.o_bytes);
+    e = tp::attention_fwd(q, (int)batch, causal != 0, O, part, s);
     if (e != hipSuccess) return hip_status(e, "tp_attn_shard: attention launch");
     e = tp::gemm_bf16_store_split_a(O, 2 * nl * head_dim, static_cast<const uint16_t*>(Wo_i),
                                     hidden, Y_i, hidden,

@@ -64,11 +64,16 @@ def test_workspace_queries(lib):
     assert lib.tp_ffn_shard_workspace_bytes(3, 8, 24, 3, B.TP_BF16) == 256   # 256-byte granule
     assert lib.tp_ffn_shard_workspace_bytes(10, 8, 20, 3, B.TP_BF16) == 0    # t does not divide f
     assert lib.tp_ffn_shard_workspace_bytes(10, 8, 16, 0, B.TP_BF16) == 0
-    # attention: 6 x [heads, seq_pad, 128] + O hi/lo [tokens, 2*nl*128], 16-bit
-    want = 6 * 8 * 2048 * 128 * 2 + 2048 * 2 * 1024 * 2
+    # attention: 6 x [heads, seq_pad, 128] + O hi/lo [tokens, 2*nl*128], 16-bit,
+    # then fp32 partial results (128 x (128 + 2) floats) for every workgroup of
+    # the larger split: at seq 2048, 8 heads, the full (non-causal) one has
+    # 16 query blocks x 8 chunks of 4 key tiles x 8 heads = 1024 workgroups
+    split = 1024 * 128 * 130 * 4
+    want = 6 * 8 * 2048 * 128 * 2 + 2048 * 2 * 1024 * 2 + split
     assert lib.tp_attn_shard_workspace_bytes(1, 2048, 64, 128, 8) == want
     ragged = lib.tp_attn_shard_workspace_bytes(2, 100, 4, 128, 2)
-    assert ragged == 6 * 2 * 2 * 128 * 128 * 2 + 2 * 100 * 2 * 256 * 2
+    # one query block, one chunk, 2 sequences x 2 heads = 4 workgroups
+    assert ragged == 6 * 2 * 2 * 128 * 128 * 2 + 2 * 100 * 2 * 256 * 2 + 4 * 128 * 130 * 4
     assert lib.tp_attn_shard_workspace_bytes(1, 8, 6, 128, 4) == 0
 
 
