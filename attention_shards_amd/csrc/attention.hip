@@ -68,20 +68,44 @@ __device__ __forceinline__ int vswz(int r) { return (r ^ (r >> 3)) & 7; }
 
 __host__ __device__ inline int div_up(int a, int b) { return (a + b - 1) / b; }
 
+constexpr int OOB = 0x7FFFFFF0;  // buffer size cap; reads past a buffer return 0
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int64_t bytes) {
+  const int n = bytes <= 0 ? 0 : (bytes > (int64_t)OOB ? OOB : (int)bytes);
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, n, 0x00020000);
+}
+
+// Global -> LDS copy of 16 bytes per lane (buffer_load ... lds): lane l's
+// bytes land at LDS address lds_base + 16*l.  Issued from inline assembly,
+// with completion tracked by wait_vmcnt() (m0 is set here and used by
+// nothing else in this file's kernels).
+__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t rsrc, int voffset,
+                                      uint32_t lds_base) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+               :
+               : "s"(__builtin_amdgcn_readfirstlane(lds_base)), "v"(voffset), "s"(rsrc)
+               : "memory", "m0");
+}
+
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
 // Key tiles a query block needs.
 __host__ __device__ inline int ntile_of(int qb, int seq, int causal) {
   const int kend = causal ? (QB * (qb + 1) < seq ? QB * (qb + 1) : seq) : seq;
   return div_up(kend, KT);
 }
 
-__global__ void __launch_bounds__(256)
+// One workgroup per CU (128 KiB of LDS), so the compiler may spend the whole
+// register file on keeping fragment reads in flight.
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
 attn_fwd_kernel(QkvOut q, int causal, uint16_t* __restrict__ O, float* __restrict__ part,
                 AttnSplit sp, float scale_log2) {
-  __shared__ __attribute__((aligned(16))) uint8_t smem[4 * TILE];
-  uint8_t* sKh = smem;
-  uint8_t* sKl = smem + TILE;
-  uint8_t* sVh = smem + 2 * TILE;
-  uint8_t* sVl = smem + 3 * TILE;
+  // Two LDS buffers of K hi, K lo, V^T hi, V^T lo tiles: one is read by the
+  // products while the next tile is staged into the other.
+  __shared__ __attribute__((aligned(16))) uint8_t smem[2 * 4 * TILE];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int S = q.seq, Sp = q.seq_pad;
@@ -135,123 +159,149 @@ attn_fwd_kernel(QkvOut q, int causal, uint16_t* __restrict__ O, float* __restric
   float m_run[2] = {-__builtin_inff(), -__builtin_inff()};
   float l_run[2] = {0.0f, 0.0f};
 
-  // Tile loads go through registers one tile ahead: the global loads of
-  // tile kt+1 are issued before tile kt's products and land in LDS after
-  // them.  K hi/lo: 64 rows x 16 chunks each; V^T hi/lo: 128 rows x 8
-  // chunks each; every thread moves 4 chunks of each array.
-  u32x4 rkh[4], rkl[4], rvh[4], rvl[4];
-  auto gload = [&](int k0) {
+  // Tiles go from global memory straight into LDS (buffer loads that write
+  // LDS): while tile kt is multiplied from one buffer, tile kt+1 lands in
+  // the other.  Each 1 KiB DMA covers 4 K rows (256 B) or 8 V^T rows
+  // (128 B); lane l writes bytes 16l..16l+15 of it, so the chunk swizzles
+  // are applied to the global addresses.  K rows past the sequence fall
+  // outside the buffer descriptor and read as zero; V^T columns past it are
+  // zero in the workspace (see attention_fwd).  16 DMAs per wave per tile.
+  const uint32_t lds0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t*)smem;
+  int k_off[4], v_off[4];
 #pragma unroll
-    for (int p = 0; p < 4; ++p) {
-      const int idx = p * 256 + tid;
-      const int r = idx >> 4, cc = idx & 15;
-      rkh[p] = u32x4{0, 0, 0, 0};
-      rkl[p] = rkh[p];
-      if (k0 + r < S) {
-        rkh[p] = *reinterpret_cast<const u32x4*>(Kh + (int64_t)(k0 + r) * D + cc * 8);
-        rkl[p] = *reinterpret_cast<const u32x4*>(Kl + (int64_t)(k0 + r) * D + cc * 8);
-      }
-    }
+  for (int j = 0; j < 4; ++j) {
+    const int i = j * 4 + wave;  // 1 KiB block of the array
+    const int rk = 4 * i + (lane >> 4), pk = lane & 15;
+    k_off[j] = rk * K_ROW + ((pk ^ kswz(rk)) << 4);
+    const int rv = 8 * i + (lane >> 3), pv = lane & 7;
+    v_off[j] = rv * Sp * 2 + ((pv ^ vswz(rv)) << 4);
+  }
+  auto stage = [&](int k0, int buf) {
+    const uint32_t base = lds0 + buf * 4 * TILE;
+    const int64_t kbytes = (int64_t)(S - k0) * D * 2;
+    const int64_t vbytes = ((int64_t)D * Sp - k0) * 2;
+    const __amdgpu_buffer_rsrc_t rkh = make_rsrc(Kh + (int64_t)k0 * D, kbytes);
+    const __amdgpu_buffer_rsrc_t rkl = make_rsrc(Kl + (int64_t)k0 * D, kbytes);
+    const __amdgpu_buffer_rsrc_t rvh = make_rsrc(Vh + k0, vbytes);
+    const __amdgpu_buffer_rsrc_t rvl = make_rsrc(Vl + k0, vbytes);
 #pragma unroll
-    for (int p = 0; p < 4; ++p) {
-      const int idx = p * 256 + tid;
-      const int r = idx >> 3, cc = idx & 7;
-      const int key0 = k0 + cc * 8;
-      rvh[p] = u32x4{0, 0, 0, 0};
-      rvl[p] = rvh[p];
-      if (key0 < S) {
-        rvh[p] = *reinterpret_cast<const u32x4*>(Vh + (int64_t)r * Sp + key0);
-        rvl[p] = *reinterpret_cast<const u32x4*>(Vl + (int64_t)r * Sp + key0);
-      }
-    }
-  };
-  auto sstore = [&](int k0) {
-#pragma unroll
-    for (int p = 0; p < 4; ++p) {
-      const int idx = p * 256 + tid;
-      const int r = idx >> 4, cc = idx & 15;
-      const int off = r * K_ROW + ((cc ^ kswz(r)) << 4);
-      *reinterpret_cast<u32x4*>(sKh + off) = rkh[p];
-      *reinterpret_cast<u32x4*>(sKl + off) = rkl[p];
-    }
-#pragma unroll
-    for (int p = 0; p < 4; ++p) {
-      const int idx = p * 256 + tid;
-      const int r = idx >> 3, cc = idx & 7;
-      const int key0 = k0 + cc * 8;
-      u32x4 vh = rvh[p], vl = rvl[p];
-      if (key0 < S && key0 + 8 > S) {  // ragged tail: zero the keys past the sequence
-#pragma unroll
-        for (int w = 0; w < 4; ++w) {
-          const int kk = key0 + 2 * w;
-          const uint32_t keep = (kk + 1 < S) ? 0xFFFFFFFFu : (kk < S ? 0x0000FFFFu : 0u);
-          vh[w] &= keep;
-          vl[w] &= keep;
-        }
-      }
-      const int off = r * V_ROW + ((cc ^ vswz(r)) << 4);
-      *reinterpret_cast<u32x4*>(sVh + off) = vh;
-      *reinterpret_cast<u32x4*>(sVl + off) = vl;
+    for (int j = 0; j < 4; ++j) {
+      const uint32_t blk = (j * 4 + wave) * 1024;
+      dma16(rkh, k_off[j], base + blk);
+      dma16(rkl, k_off[j], base + TILE + blk);
+      dma16(rvh, v_off[j], base + 2 * TILE + blk);
+      dma16(rvl, v_off[j], base + 3 * TILE + blk);
     }
   };
 
-  gload(kt0 * KT);
+  stage(kt0 * KT, 0);
+  wait_vmcnt<0>();
+  __syncthreads();
   for (int kt = kt0; kt < kt1; ++kt) {
     const int k0 = kt * KT;
-    __syncthreads();  // the previous tile is no longer read
-    sstore(k0);
-    __syncthreads();
-    if (kt + 1 < kt1) gload(k0 + KT);
+    const int cur = (kt - kt0) & 1;
+    // Tile kt+1 into the other buffer; its last reader, tile kt-1, finished
+    // before the barrier that ended the previous step.
+    if (kt + 1 < kt1) stage(k0 + KT, cur ^ 1);
+    const uint8_t* const sKh = smem + cur * 4 * TILE;
+    const uint8_t* const sKl = sKh + TILE;
+    const uint8_t* const sVh = sKh + 2 * TILE;
+    const uint8_t* const sVl = sKh + 3 * TILE;
 
     // ---- scores S^T for four 16-key blocks (chunk kc, half hb) ----
+    // The eight K fragments of 32-dim slice dc+1 are read while slice dc's
+    // 24 MFMAs run (two register sets), and the MFMAs cycle over the eight
+    // independent accumulators, so neither LDS latency nor an MFMA result
+    // holds the matrix pipe.
     f32x4 s[2][2][2];  // [query group][kc][hb]
 #pragma unroll
-    for (int kc = 0; kc < 2; ++kc)
+    for (int qg = 0; qg < 2; ++qg)
 #pragma unroll
-      for (int hb = 0; hb < 2; ++hb) {
-        const int i = lane & 15;
-        const int krow = kc * 32 + 8 * (i >> 2) + 4 * hb + (i & 3);
-        f32x4 a0 = {0, 0, 0, 0}, a1 = {0, 0, 0, 0};
+      for (int kc = 0; kc < 2; ++kc)
 #pragma unroll
-        for (int dc = 0; dc < 4; ++dc) {
-          const int ch = dc * 4 + g;
-          const int off = krow * K_ROW + ((ch ^ kswz(krow)) << 4);
-          const bf16x8 kh = *reinterpret_cast<const bf16x8*>(sKh + off);
-          const bf16x8 kl = *reinterpret_cast<const bf16x8*>(sKl + off);
-          a0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kh, qh[0][dc], a0, 0, 0, 0);
-          a1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kh, qh[1][dc], a1, 0, 0, 0);
-          a0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kh, ql[0][dc], a0, 0, 0, 0);
-          a1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kh, ql[1][dc], a1, 0, 0, 0);
-          a0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kl, qh[0][dc], a0, 0, 0, 0);
-          a1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kl, qh[1][dc], a1, 0, 0, 0);
+        for (int hb = 0; hb < 2; ++hb) s[qg][kc][hb] = f32x4{0, 0, 0, 0};
+    bf16x8 kh[2][2][2], kl[2][2][2];  // [set][kc][hb]
+    auto kread = [&](int set, int dc) {
+#pragma unroll
+      for (int kc = 0; kc < 2; ++kc)
+#pragma unroll
+        for (int hb = 0; hb < 2; ++hb) {
+          const int i = lane & 15;
+          const int krow = kc * 32 + 8 * (i >> 2) + 4 * hb + (i & 3);
+          const int off = krow * K_ROW + (((dc * 4 + g) ^ kswz(krow)) << 4);
+          kh[set][kc][hb] = *reinterpret_cast<const bf16x8*>(sKh + off);
+          kl[set][kc][hb] = *reinterpret_cast<const bf16x8*>(sKl + off);
         }
-        s[0][kc][hb] = a0;
-        s[1][kc][hb] = a1;
+    };
+    kread(0, 0);
+#pragma unroll
+    for (int dc = 0; dc < 4; ++dc) {
+      const int set = dc & 1;
+      if (dc + 1 < 4) kread(set ^ 1, dc + 1);
+#pragma unroll
+      for (int pass = 0; pass < 3; ++pass)
+#pragma unroll
+        for (int kc = 0; kc < 2; ++kc)
+#pragma unroll
+          for (int hb = 0; hb < 2; ++hb)
+#pragma unroll
+            for (int qg = 0; qg < 2; ++qg) {
+              const bf16x8 a = pass == 2 ? kl[set][kc][hb] : kh[set][kc][hb];
+              const bf16x8 bq = pass == 1 ? ql[qg][dc] : qh[qg][dc];
+              s[qg][kc][hb] =
+                  __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, bq, s[qg][kc][hb], 0, 0, 0);
+            }
+    }
+
+    // V fragments of the first PV group, read during the softmax below.
+    f16x8 vh[2][4], vl[2][4];  // [set][db within the group]
+    auto vread = [&](int set, int grp) {  // grp = kc*2 + half of the head dims
+      const int kc = grp >> 1;
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int db = (grp & 1) * 4 + u;
+        const int drow = db * 16 + (lane & 15);
+        const int off = drow * V_ROW + (((kc * 4 + g) ^ vswz(drow)) << 4);
+        vh[set][u] = *reinterpret_cast<const f16x8*>(sVh + off);
+        vl[set][u] = *reinterpret_cast<const f16x8*>(sVl + off);
       }
+    };
+    vread(0, 0);
 
     // ---- online softmax; lane owns query myq[qg] and keys
-    //      k0 + kc*32 + 8g + 4hb + e ----
+    //      k0 + kc*32 + 8g + 4hb + e.  Only the last key tile (keys past the
+    //      sequence) and tiles reaching past the wave's first query (causal)
+    //      need the mask.  Scores stay unscaled; the scale goes into the
+    //      exponent's multiply-add.  The O rescale is skipped when no query
+    //      of the wave raised its running max (alpha == 1 everywhere). ----
+    const bool mask_tile = (k0 + KT > S) || (causal && k0 + KT - 1 > qb * QB + wave * QW);
     f16x8 pb[2][2];
 #pragma unroll
     for (int qg = 0; qg < 2; ++qg) {
       float mt = -__builtin_inff();
+      if (mask_tile) {
 #pragma unroll
-      for (int kc = 0; kc < 2; ++kc)
+        for (int kc = 0; kc < 2; ++kc)
 #pragma unroll
-        for (int hb = 0; hb < 2; ++hb)
+          for (int hb = 0; hb < 2; ++hb)
 #pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const int key = k0 + kc * 32 + 8 * g + 4 * hb + e;
-            float v = s[qg][kc][hb][e] * scale_log2;
-            if (key >= S || (causal && key > myq[qg])) v = -__builtin_inff();
-            s[qg][kc][hb][e] = v;
-            mt = fmaxf(mt, v);
-          }
+            for (int e = 0; e < 4; ++e) {
+              const int key = k0 + kc * 32 + 8 * g + 4 * hb + e;
+              if (key >= S || (causal && key > myq[qg])) s[qg][kc][hb][e] = -__builtin_inff();
+              mt = fmaxf(mt, s[qg][kc][hb][e]);
+            }
+      } else {
+#pragma unroll
+        for (int kc = 0; kc < 2; ++kc)
+#pragma unroll
+          for (int hb = 0; hb < 2; ++hb)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) mt = fmaxf(mt, s[qg][kc][hb][e]);
+      }
       mt = fmaxf(mt, __shfl_xor(mt, 16));
       mt = fmaxf(mt, __shfl_xor(mt, 32));
-      const float m_new = fmaxf(m_run[qg], mt);
+      const float m_new = fmaxf(m_run[qg], mt * scale_log2);
       const float m_use = (m_new == -__builtin_inff()) ? 0.0f : m_new;
-      const float alpha = __builtin_amdgcn_exp2f(m_run[qg] - m_use);
       float psum = 0.0f;
 #pragma unroll
       for (int kc = 0; kc < 2; ++kc)
@@ -259,32 +309,43 @@ attn_fwd_kernel(QkvOut q, int causal, uint16_t* __restrict__ O, float* __restric
         for (int hb = 0; hb < 2; ++hb)
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
-            const _Float16 p = (_Float16)__builtin_amdgcn_exp2f(s[qg][kc][hb][e] - m_use);
+            const _Float16 p = (_Float16)__builtin_amdgcn_exp2f(
+                __builtin_fmaf(s[qg][kc][hb][e], scale_log2, -m_use));
             psum += (float)p;
             pb[qg][kc][hb * 4 + e] = p;
           }
-      l_run[qg] = l_run[qg] * alpha + psum;
-      m_run[qg] = m_new;
+      if (__builtin_amdgcn_ballot_w64(m_new != m_run[qg]) != 0) {
+        const float alpha = __builtin_amdgcn_exp2f(m_run[qg] - m_use);
+        l_run[qg] = l_run[qg] * alpha + psum;
 #pragma unroll
-      for (int db = 0; db < 8; ++db) o[qg][db] *= alpha;
+        for (int db = 0; db < 8; ++db) o[qg][db] *= alpha;
+      } else {
+        l_run[qg] += psum;
+      }
+      m_run[qg] = m_new;
     }
 
     // ---- O^T += V^T P^T ----
+    // Four groups (key half kc x half of the head dims) of eight V
+    // fragments; group grp+1 is read while group grp's 16 MFMAs run, which
+    // cycle over 8 independent accumulators.
 #pragma unroll
-    for (int db = 0; db < 8; ++db) {
-      const int drow = db * 16 + (lane & 15);
+    for (int grp = 0; grp < 4; ++grp) {
+      const int set = grp & 1, kc = grp >> 1;
+      if (grp + 1 < 4) vread(set ^ 1, grp + 1);
 #pragma unroll
-      for (int kc = 0; kc < 2; ++kc) {
-        const int ch = kc * 4 + g;
-        const int off = drow * V_ROW + ((ch ^ vswz(drow)) << 4);
-        const f16x8 vh = *reinterpret_cast<const f16x8*>(sVh + off);
-        const f16x8 vl = *reinterpret_cast<const f16x8*>(sVl + off);
-        o[0][db] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vh, pb[0][kc], o[0][db], 0, 0, 0);
-        o[1][db] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vh, pb[1][kc], o[1][db], 0, 0, 0);
-        o[0][db] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vl, pb[0][kc], o[0][db], 0, 0, 0);
-        o[1][db] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vl, pb[1][kc], o[1][db], 0, 0, 0);
-      }
+      for (int pass = 0; pass < 2; ++pass)
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+#pragma unroll
+          for (int qg = 0; qg < 2; ++qg) {
+            const int db = (grp & 1) * 4 + u;
+            o[qg][db] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pass ? vl[set][u] : vh[set][u],
+                                                               pb[qg][kc], o[qg][db], 0, 0, 0);
+          }
     }
+    wait_vmcnt<0>();  // tile kt+1 has landed (this wave's part of it)
+    __syncthreads();  // ... everyone's; and tile kt is no longer read
   }
 
   const int hd = q.nl * D;
@@ -394,6 +455,21 @@ attn_combine_kernel(QkvOut q, int causal, uint16_t* __restrict__ O,
                                                lo[4] | (lo[5] << 16), lo[6] | (lo[7] << 16)};
 }
 
+// Zeroes V^T columns [seq, seq_pad) of every (sequence*head, dim) row, hi
+// and lo: the probabilities of those keys are 0, but 0 times whatever the
+// workspace held there need not be.
+__global__ void __launch_bounds__(256)
+vt_pad_zero_kernel(QkvOut q, int rows) {
+  const int pad = q.seq_pad - q.seq;
+  const int64_t n = (int64_t)rows * pad;
+  for (int64_t k = (int64_t)blockIdx.x * 256 + threadIdx.x; k < n; k += (int64_t)gridDim.x * 256) {
+    const int64_t r = k / pad;
+    const int64_t at = r * q.seq_pad + q.seq + (k - r * pad);
+    q.vt_hi[at] = 0;
+    q.vt_lo[at] = 0;
+  }
+}
+
 }  // namespace
 
 AttnSplit attn_split(int batch, int seq, int nl, bool causal) {
@@ -425,6 +501,14 @@ hipError_t attention_fwd(const QkvOut& q, int batch, bool causal, uint16_t* O, f
   if (batch == 0 || q.seq == 0 || q.nl == 0) return hipSuccess;
   const AttnSplit sp = attn_split(batch, q.seq, q.nl, causal);
   const float scale_log2 = 1.4426950408889634f / sqrtf((float)q.d);
+  if (q.seq_pad > q.seq) {
+    const int rows = sp.nbh * D;
+    const int64_t n = (int64_t)rows * (q.seq_pad - q.seq);
+    const int blocks = (int)((n + 255) / 256 < 4096 ? (n + 255) / 256 : 4096);
+    hipLaunchKernelGGL(vt_pad_zero_kernel, dim3(blocks), dim3(256), 0, s, q, rows);
+    const hipError_t e0 = hipGetLastError();
+    if (e0 != hipSuccess) return e0;
+  }
   hipLaunchKernelGGL(attn_fwd_kernel, dim3(sp.n_items), dim3(256), 0, s, q, causal ? 1 : 0, O,
                      part, sp, scale_log2);
   hipError_t e = hipGetLastError();
