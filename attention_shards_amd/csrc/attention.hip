@@ -23,18 +23,18 @@
 // prefixes makes max|Y|/RMS(Y) large (row 0 is v_0 itself), which is what
 // rules out single bf16 roundings of P and O here.
 //
-// Layout per wave (32 queries as two groups of 16, v_mfma_f32_16x16x32_bf16):
+// Layout: a workgroup has 8 waves (two per SIMD, so one wave's LDS waits
+// overlap the other's MFMAs) of 16 queries each; per wave, with
+// v_mfma_f32_16x16x32_bf16:
 //   * scores are computed transposed, S^T = K Q^T: A = K rows (keys),
-//     B = Q (queries), so each lane ends up owning one query (lane % 16) of
-//     each group and four keys per 16-key block.  K rows are fed in the
-//     order that gives lane group g = lane/16 the keys 8g..8g+7 of each
-//     32-key chunk, which is exactly the B operand of the next product.
-//     Each K fragment read from LDS feeds both query groups;
+//     B = Q (queries), so each lane ends up owning one query (lane % 16)
+//     and four keys per 16-key block.  K rows are fed in the order that
+//     gives lane group g = lane/16 the keys 8g..8g+7 of each 32-key chunk,
+//     which is exactly the B operand of the next product;
 //   * O^T = V^T P^T: A = V^T rows (head dims, keys contiguous in the V^T
 //     workspace), B = P^T straight from the score registers.  The query of
 //     every accumulator is again lane % 16, so softmax rescales are lane-local
-//     and only the row max needs two cross-lane exchanges.  Each V fragment
-//     read feeds both query groups.
+//     and only the row max needs two cross-lane exchanges.
 #include "internal.h"
 
 namespace tp {
@@ -46,8 +46,12 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int D = 128;    // head dim
-constexpr int QW = 32;    // queries per wave (two groups of 16)
-constexpr int QB = 128;   // queries per workgroup (4 waves)
+constexpr int NQG = 1;    // 16-query groups per wave
+constexpr int NWAVE = 8;  // waves per workgroup: two per SIMD, so one wave's
+                          // LDS waits overlap the other's MFMAs
+constexpr int QW = 16 * NQG;     // queries per wave
+constexpr int QB = NWAVE * QW;   // queries per workgroup (128)
+constexpr int NT = NWAVE * 64;   // threads per workgroup
 constexpr int KT = 64;    // keys per tile
 constexpr int K_ROW = D * 2;      // 256-byte K rows (16 chunks)
 constexpr int V_ROW = KT * 2;     // 128-byte V^T rows (8 chunks)
@@ -98,9 +102,7 @@ __host__ __device__ inline int ntile_of(int qb, int seq, int causal) {
   return div_up(kend, KT);
 }
 
-// One workgroup per CU (128 KiB of LDS), so the compiler may spend the whole
-// register file on keeping fragment reads in flight.
-__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
+__global__ void __launch_bounds__(NT)
 attn_fwd_kernel(QkvOut q, int causal, uint16_t* __restrict__ O, float* __restrict__ part,
                 AttnSplit sp, float scale_log2) {
   // Two LDS buffers of K hi, K lo, V^T hi, V^T lo tiles: one is read by the
@@ -131,14 +133,14 @@ attn_fwd_kernel(QkvOut q, int causal, uint16_t* __restrict__ O, float* __restric
   const uint16_t* Vl = q.vt_lo + hoff;
 
   const int g = lane >> 4;  // lane group
-  int myq[2];
+  int myq[NQG];
 #pragma unroll
-  for (int qg = 0; qg < 2; ++qg) myq[qg] = qb * QB + wave * QW + qg * 16 + (lane & 15);
+  for (int qg = 0; qg < NQG; ++qg) myq[qg] = qb * QB + wave * QW + qg * 16 + (lane & 15);
 
   // Q as the B operand: query myq, head dims dc*32 + 8g .. +7.
-  bf16x8 qh[2][4], ql[2][4];
+  bf16x8 qh[NQG][4], ql[NQG][4];
 #pragma unroll
-  for (int qg = 0; qg < 2; ++qg)
+  for (int qg = 0; qg < NQG; ++qg)
 #pragma unroll
     for (int dc = 0; dc < 4; ++dc) {
       if (myq[qg] < S) {
@@ -151,13 +153,17 @@ attn_fwd_kernel(QkvOut q, int causal, uint16_t* __restrict__ O, float* __restric
       }
     }
 
-  f32x4 o[2][8];
+  f32x4 o[NQG][8];
 #pragma unroll
-  for (int qg = 0; qg < 2; ++qg)
+  for (int qg = 0; qg < NQG; ++qg)
 #pragma unroll
     for (int db = 0; db < 8; ++db) o[qg][db] = f32x4{0, 0, 0, 0};
-  float m_run[2] = {-__builtin_inff(), -__builtin_inff()};
-  float l_run[2] = {0.0f, 0.0f};
+  float m_run[NQG], l_run[NQG];
+#pragma unroll
+  for (int qg = 0; qg < NQG; ++qg) {
+    m_run[qg] = -__builtin_inff();
+    l_run[qg] = 0.0f;
+  }
 
   // Tiles go from global memory straight into LDS (buffer loads that write
   // LDS): while tile kt is multiplied from one buffer, tile kt+1 lands in
@@ -165,12 +171,13 @@ attn_fwd_kernel(QkvOut q, int causal, uint16_t* __restrict__ O, float* __restric
   // (128 B); lane l writes bytes 16l..16l+15 of it, so the chunk swizzles
   // are applied to the global addresses.  K rows past the sequence fall
   // outside the buffer descriptor and read as zero; V^T columns past it are
-  // zero in the workspace (see attention_fwd).  16 DMAs per wave per tile.
+  // zero in the workspace (see attention_fwd).
   const uint32_t lds0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t*)smem;
-  int k_off[4], v_off[4];
+  constexpr int NDW = 16 / NWAVE;  // DMAs per wave per array
+  int k_off[NDW], v_off[NDW];
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int i = j * 4 + wave;  // 1 KiB block of the array
+  for (int j = 0; j < NDW; ++j) {
+    const int i = j * NWAVE + wave;  // 1 KiB block of the array
     const int rk = 4 * i + (lane >> 4), pk = lane & 15;
     k_off[j] = rk * K_ROW + ((pk ^ kswz(rk)) << 4);
     const int rv = 8 * i + (lane >> 3), pv = lane & 7;
@@ -185,8 +192,8 @@ attn_fwd_kernel(QkvOut q, int causal, uint16_t* __restrict__ O, float* __restric
     const __amdgpu_buffer_rsrc_t rvh = make_rsrc(Vh + k0, vbytes);
     const __amdgpu_buffer_rsrc_t rvl = make_rsrc(Vl + k0, vbytes);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const uint32_t blk = (j * 4 + wave) * 1024;
+    for (int j = 0; j < NDW; ++j) {
+      const uint32_t blk = (j * NWAVE + wave) * 1024;
       dma16(rkh, k_off[j], base + blk);
       dma16(rkl, k_off[j], base + TILE + blk);
       dma16(rvh, v_off[j], base + 2 * TILE + blk);
@@ -213,9 +220,9 @@ attn_fwd_kernel(QkvOut q, int causal, uint16_t* __restrict__ O, float* __restric
     // 24 MFMAs run (two register sets), and the MFMAs cycle over the eight
     // independent accumulators, so neither LDS latency nor an MFMA result
     // holds the matrix pipe.
-    f32x4 s[2][2][2];  // [query group][kc][hb]
+    f32x4 s[NQG][2][2];  // [query group][kc][hb]
 #pragma unroll
-    for (int qg = 0; qg < 2; ++qg)
+    for (int qg = 0; qg < NQG; ++qg)
 #pragma unroll
       for (int kc = 0; kc < 2; ++kc)
 #pragma unroll
@@ -245,7 +252,7 @@ attn_fwd_kernel(QkvOut q, int causal, uint16_t* __restrict__ O, float* __restric
 #pragma unroll
           for (int hb = 0; hb < 2; ++hb)
 #pragma unroll
-            for (int qg = 0; qg < 2; ++qg) {
+            for (int qg = 0; qg < NQG; ++qg) {
               const bf16x8 a = pass == 2 ? kl[set][kc][hb] : kh[set][kc][hb];
               const bf16x8 bq = pass == 1 ? ql[qg][dc] : qh[qg][dc];
               s[qg][kc][hb] =
@@ -275,9 +282,9 @@ attn_fwd_kernel(QkvOut q, int causal, uint16_t* __restrict__ O, float* __restric
     //      exponent's multiply-add.  The O rescale is skipped when no query
     //      of the wave raised its running max (alpha == 1 everywhere). ----
     const bool mask_tile = (k0 + KT > S) || (causal && k0 + KT - 1 > qb * QB + wave * QW);
-    f16x8 pb[2][2];
+    f16x8 pb[NQG][2];
 #pragma unroll
-    for (int qg = 0; qg < 2; ++qg) {
+    for (int qg = 0; qg < NQG; ++qg) {
       float mt = -__builtin_inff();
       if (mask_tile) {
 #pragma unroll
@@ -338,7 +345,7 @@ attn_fwd_kernel(QkvOut q, int causal, uint16_t* __restrict__ O, float* __restric
 #pragma unroll
         for (int u = 0; u < 4; ++u)
 #pragma unroll
-          for (int qg = 0; qg < 2; ++qg) {
+          for (int qg = 0; qg < NQG; ++qg) {
             const int db = (grp & 1) * 4 + u;
             o[qg][db] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pass ? vl[set][u] : vh[set][u],
                                                                pb[qg][kc], o[qg][db], 0, 0, 0);
@@ -350,7 +357,7 @@ attn_fwd_kernel(QkvOut q, int causal, uint16_t* __restrict__ O, float* __restric
 
   const int hd = q.nl * D;
 #pragma unroll
-  for (int qg = 0; qg < 2; ++qg) {
+  for (int qg = 0; qg < NQG; ++qg) {
     float l_tot = l_run[qg] + __shfl_xor(l_run[qg], 16);
     l_tot += __shfl_xor(l_tot, 32);
     // O^T layout: lane owns head dims db*16 + 4g + e, e = 0..3
@@ -509,7 +516,7 @@ hipError_t attention_fwd(const QkvOut& q, int batch, bool causal, uint16_t* O, f
     const hipError_t e0 = hipGetLastError();
     if (e0 != hipSuccess) return e0;
   }
-  hipLaunchKernelGGL(attn_fwd_kernel, dim3(sp.n_items), dim3(256), 0, s, q, causal ? 1 : 0, O,
+  hipLaunchKernelGGL(attn_fwd_kernel, dim3(sp.n_items), dim3(NT), 0, s, q, causal ? 1 : 0, O,
                      part, sp, scale_log2);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
