@@ -296,6 +296,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-attention", action="store_true",
                     help="skip the attention row (profiling runs of the FFN step)")
+    ap.add_argument("--no-fused", action="store_true",
+                    help="skip the fused-step rows (profiling runs of the FFN step)")
     ap.add_argument("--sweep", metavar="OUT_JSONL", default=None)
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run a 1 GiB device copy first (counter calibration)")
@@ -378,18 +380,23 @@ def main():
 
     # The same step with the sum fused into GEMM2's epilogue: this shard's
     # partial is added from the accumulators and never stored or re-read.
-    peers = [None if j == i else parts[j] for j in range(t)]
-    wsf = torch.empty(B.tp_ffn_shard_reduce_workspace_bytes(M, h, f, t, B.TP_BF16),
-                      dtype=torch.uint8, device="cuda")
-    fused_ms = time_events(lambda: B.tp_ffn_shard_reduce(X, W1v[i], W2v[i], peers, R, out, i,
-                                                         workspace=wsf),
-                           args.steps, args.warmup)
-    fused_row = {"ms": round(fused_ms, 5), "tflops": round(fl / (fused_ms * 1e-3) / 1e12, 2),
-                 "unfused_ms": round(ffn_ms + red_ms, 5),
-                 "hbm_bytes_saved": 2 * 2 * M * h}
-    del parts, peers, W1v, W2v, W1, W2, ws, wsf, out
+    fused_row = None
+    if not args.no_fused:
+        peers = [None if j == i else parts[j] for j in range(t)]
+        wsf = torch.empty(B.tp_ffn_shard_reduce_workspace_bytes(M, h, f, t, B.TP_BF16),
+                          dtype=torch.uint8, device="cuda")
+        fused_ms = time_events(lambda: B.tp_ffn_shard_reduce(X, W1v[i], W2v[i], peers, R, out,
+                                                             i, workspace=wsf),
+                               args.steps, args.warmup)
+        fused_row = {"ms": round(fused_ms, 5),
+                     "tflops": round(fl / (fused_ms * 1e-3) / 1e12, 2),
+                     "unfused_ms": round(ffn_ms + red_ms, 5),
+                     "hbm_bytes_saved": 2 * 2 * M * h}
+        del peers, wsf
+    del parts, W1v, W2v, W1, W2, ws, out
     torch.cuda.empty_cache()
-    fused_row["large"] = fused_vs_unfused_large(max(5, args.steps // 5), 3)
+    if fused_row is not None:
+        fused_row["large"] = fused_vs_unfused_large(max(5, args.steps // 5), 3)
 
     # ---------------- attention shard ----------------
     attn_row = None
