@@ -254,8 +254,6 @@ __device__ __forceinline__ void tile_coords(int tiles_m, int tiles_n, int& tm,
 // bf16 kernel
 // ---------------------------------------------------------------------------
 constexpr int BUF_FLAGS = 0x00020000;  // raw buffer, 32-bit data format
-constexpr int BK3 = 32;                // K per pipeline stage
-constexpr int NSLOT = 5;               // LDS ring: DMA runs NSLOT-1 stages ahead
 constexpr int OOB = 0x7FFFFFF0;        // offset past any buffer: reads return 0
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base,
@@ -302,23 +300,42 @@ struct IC {
   static constexpr int value = N;
 };
 
+// f(IC<I>{}), f(IC<I+1>{}), ..., f(IC<E-1>{}), unrolled at compile time.
+template <int I, int E, class F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (I < E) {
+    f(IC<I>{});
+    static_for<I + 1, E>(f);
+  }
+}
 
-template <int BM, int BN, int WM, int WN, class Epi>
+
+// KS MFMA k-steps of 16 per pipeline stage (stage K = BK = 16 KS) and an LDS
+// ring of NSL stages.  KS = 2 gives 64-byte A rows per stage; KS = 4 gives
+// 128-byte A rows (a whole cache line per row per DMA), at the price of
+// fewer, larger ring slots.
+template <int BM, int BN, int WM, int WN, int KS, int NSL, class Epi>
 __global__ void __launch_bounds__(WM * WN * 64)
 gemm_bf16_kernel(const uint16_t* __restrict__ A, int64_t lda,
                  const uint16_t* __restrict__ B, int64_t ldb, int M, int N,
                  int K, int kwrap, int tiles_m, int tiles_n, Epi epi) {
   // Stage kt reads B rows from (k0 < kwrap ? k0 : k0 - kwrap); with kwrap < K
-  // (K == 2 kwrap, kwrap % 32 == 0) the same B multiplies both halves of an
-  // A laid out as [A_hi | A_lo].
+  // (K == 2 kwrap, kwrap a multiple of BK) the same B multiplies both halves
+  // of an A laid out as [A_hi | A_lo].
+  static_assert(KS == 2 || KS == 4, "k-steps per stage");
+  static_assert(NSL >= 3 && NSL <= 6, "ring slots");
+  constexpr int BK = 16 * KS;
   constexpr int NW = WM * WN;
   constexpr int FM = BM / WM / 32;
   constexpr int FN = BN / WN / 32;
-  constexpr int A_ROWB = BK3 * 2;          // 64-byte A rows in LDS (4 chunks)
+  constexpr int A_ROWB = BK * 2;           // A rows in LDS: 64 or 128 bytes
+  constexpr int CPR = A_ROWB / 16;         // 16-byte chunks per A row (4 or 8)
+  constexpr int RPD = 64 / CPR;            // A rows per 1 KiB DMA
+  constexpr int ASH = CPR == 4 ? 2 : 1;    // A swizzle: chunk ^ ((row >> ASH) & (CPR-1))
   constexpr int B_ROWB = BN * 2;           // B rows in LDS: natural [k][n]
   constexpr int B_CH = B_ROWB / 16;        // 16-byte chunks per B row
   constexpr int A_STAGE = BM * A_ROWB;
-  constexpr int B_STAGE = BK3 * B_ROWB;
+  constexpr int B_STAGE = BK * B_ROWB;
   constexpr int A_DMA = A_STAGE / 1024 / NW;  // 1 KiB DMAs per wave per stage
   constexpr int B_DMA = B_STAGE / 1024 / NW;
   constexpr int NDMA = A_DMA + B_DMA;
@@ -326,14 +343,14 @@ gemm_bf16_kernel(const uint16_t* __restrict__ A, int64_t lda,
   static_assert(B_CH >= 16, "B swizzle needs >= 16 chunks per row");
   static_assert(FM >= 1 && FN >= 1, "wave tile");
 
-  // LDS ring: slot s holds A at s*A_STAGE and B at NSLOT*A_STAGE + s*B_STAGE.
+  // LDS ring: slot s holds A at s*A_STAGE and B at NSL*A_STAGE + s*B_STAGE.
   // The same memory later stages the epilogue (NW regions of 32 x (BN/WN+4)).
-  constexpr int PIPE_BYTES = NSLOT * (A_STAGE + B_STAGE);
+  constexpr int PIPE_BYTES = NSL * (A_STAGE + B_STAGE);
   constexpr int EPI_BYTES = NW * 32 * (BN / WN + 4) * 4;
   __shared__ __attribute__((aligned(16))) uint8_t
       smem[PIPE_BYTES > EPI_BYTES ? PIPE_BYTES : EPI_BYTES];
   uint8_t* const lds_a = smem;
-  uint8_t* const lds_b = smem + NSLOT * A_STAGE;
+  uint8_t* const lds_b = smem + NSL * A_STAGE;
   const uint32_t lds_a_addr = (uint32_t)(uintptr_t)(lds_u8*)lds_a;
   const uint32_t lds_b_addr = (uint32_t)(uintptr_t)(lds_u8*)lds_b;
 
@@ -346,16 +363,18 @@ gemm_bf16_kernel(const uint16_t* __restrict__ A, int64_t lda,
   const int rows_valid = min(BM, M - m0);
   const int cols_valid = min(BN, N - n0);
 
-  // ---- DMA lane offsets.  A: 16 rows of 64 B per DMA; lane l fills row
-  // l/4, slot l%4 with logical chunk (l%4) ^ ((row>>2)&3).  B: 1024/B_ROWB
-  // rows per DMA; lane l fills slot l % B_CH with logical chunk
-  // slot ^ ((row&3)<<2).  The swizzles keep the fragment reads on distinct
-  // banks; they are applied to the global addresses.
+  // ---- DMA lane offsets.  A: RPD rows of A_ROWB bytes per DMA; lane l
+  // fills row l/CPR, physical chunk l%CPR with logical chunk
+  // (l%CPR) ^ ((row >> ASH) & (CPR-1)).  B: 1024/B_ROWB rows per DMA; lane l
+  // fills slot l % B_CH with logical chunk slot ^ ((row&3)<<2).  The
+  // swizzles keep the fragment reads on distinct banks (any 16 consecutive
+  // rows at one logical chunk cover 16 distinct 16-byte bank groups); they
+  // are applied to the global addresses.
   int a_off[A_DMA], a_col[A_DMA];
 #pragma unroll
   for (int j = 0; j < A_DMA; ++j) {
-    const int row = 16 * (j * NW + wave) + (lane >> 2);
-    const int c = (lane & 3) ^ ((row >> 2) & 3);
+    const int row = RPD * (j * NW + wave) + lane / CPR;
+    const int c = (lane % CPR) ^ ((row >> ASH) & (CPR - 1));
     a_off[j] = row * (int)lda * 2 + c * 16;
     a_col[j] = c * 8;
   }
@@ -370,7 +389,7 @@ gemm_bf16_kernel(const uint16_t* __restrict__ A, int64_t lda,
   // DMA number j (0 <= j < NDMA) of stage kt into ring slot SLOT.
   auto dma = [&](int kt, auto SLOT, int j) {
     constexpr int slot = decltype(SLOT)::value;
-    const int k0 = kt * BK3;
+    const int k0 = kt * BK;
     if (j < A_DMA) {
       const __amdgpu_buffer_rsrc_t ra =
           make_rsrc(A + (int64_t)m0 * lda + k0, (int64_t)rows_valid * lda * 2 - (int64_t)k0 * 2);
@@ -389,10 +408,10 @@ gemm_bf16_kernel(const uint16_t* __restrict__ A, int64_t lda,
 
   // ---- fragment read addresses (byte offsets inside a slot).
   // A (ds_read_b128): row wr0 + mi*32 + (lane&31), chunk 2ks + (lane>>5).
-  int a_rd[2];
+  int a_rd[KS];
 #pragma unroll
-  for (int ks = 0; ks < 2; ++ks) {
-    const int c = (2 * ks + (lane >> 5)) ^ (((lane & 31) >> 2) & 3);
+  for (int ks = 0; ks < KS; ++ks) {
+    const int c = (2 * ks + (lane >> 5)) ^ (((lane & 31) >> ASH) & (CPR - 1));
     a_rd[ks] = (wr0 + (lane & 31)) * A_ROWB + c * 16;
   }
   // B (ds_read_b64_tr_b16): in each 16-lane group G, input lane r points at
@@ -442,87 +461,76 @@ gemm_bf16_kernel(const uint16_t* __restrict__ A, int64_t lda,
     acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[fset][mi], fb[fset][ni],
                                                           acc[mi][ni], 0, 0, 0);
   };
-  constexpr int NMF = FM * FN;   // MFMAs per k-step
-  constexpr int NRU = FM + FN;   // fragment read units per k-step
 
   // Stages past the end of K load zeros (offsets outside the buffers), so
-  // every main-loop step issues the same DMAs and the explicit vmcnt counts
-  // below are exact.
-  const int nk = (K + BK3 - 1) / BK3;
+  // every step issues the same DMAs and the explicit vmcnt counts below are
+  // exact.
+  const int nk = (K + BK - 1) / BK;
 
-  // One pipeline step computes stage kt from ring slot u = kt % NSLOT.  Each
-  // MFMA is followed by at most one piece of memory traffic, pinned in place
+  // One pipeline step computes stage kt from ring slot u = kt % NSL.  Each
+  // MFMA is followed by at most one DMA and one fragment read unit, pinned
   // with scheduling barriers (a wave cannot issue past an MFMA until the
   // matrix pipe accepts it, so traffic must sit between MFMAs to overlap):
-  //   k-step 0: the k-step 1 fragment reads, then the DMAs of stage
-  //     kt+NSLOT-1 (slot (u+NSLOT-1)%NSLOT, last read in step kt-1, before
-  //     its barrier);
-  //   wait until stage kt+1's DMAs have landed (NSLOT-2 later stages stay
-  //   in flight) and until this wave's own LDS reads are complete, so that
+  //   k-steps 0..KS-2: at their start the fragment reads of the next
+  //     k-step; the DMAs of stage kt+NSL-1 (slot (u+NSL-1)%NSL, last read in
+  //     step kt-1 before its barrier) at the end of k-step 0 (KS = 2) or
+  //     spread over these k-steps (KS = 4);
+  //   wait until stage kt+1's DMAs have landed (NSL-2 later stages stay in
+  //   flight) and until this wave's own LDS reads are complete, so that
   //   after the barrier no read of a slot about to be refilled is pending;
   //   barrier;
-  //   k-step 1: the fragment reads of k-step 0 of stage kt+1.
-  // The last nk % NSLOT stages run as tail steps: every stage they need is
-  // already in flight (stages up to kt+3 when the tail group starts at kt),
-  // so a tail step issues no DMA and waits until 2-u stages remain
-  // outstanding, i.e. until stage kt+u+1 has landed.
-  auto step = [&](int kt, auto U, auto TAIL) {
+  //   k-step KS-1: the fragment reads of k-step 0 of stage kt+1.
+  // Fragment register sets alternate with the k-step's parity (KS even).
+  constexpr int NMF = FM * FN;   // MFMAs per k-step
+  constexpr int NRU = FM + FN;   // fragment read units per k-step
+  constexpr int DSLOTS = (KS - 1) * NMF;
+  static_assert(NDMA <= DSLOTS && NRU <= NMF, "traffic fits between the MFMAs");
+  // MFMA slot after which DMA d of a step is issued
+  auto dma_slot = [](int d) { return KS == 2 ? NMF - NDMA + d : d * DSLOTS / NDMA; };
+  auto step = [&](int kt, auto U) __attribute__((always_inline)) {
     constexpr int u = decltype(U)::value;
-    constexpr bool tail = decltype(TAIL)::value != 0;
-    constexpr int nxt = (u + NSLOT - 1) % NSLOT;
-    static_assert(NDMA <= NMF && NRU <= NMF, "traffic fits between the MFMAs");
-    // k-step 0
+    constexpr int nxt = (u + NSL - 1) % NSL;
 #pragma unroll
-    for (int j = 0; j < NMF; ++j) {
-      mfma1(0, j);
-      __builtin_amdgcn_sched_barrier(0);
-      if (j < NRU) read_unit(IC<u>{}, 1, 1, j);
-      if (!tail && j >= NMF - NDMA) dma(kt + NSLOT - 1, IC<nxt>{}, j - (NMF - NDMA));
-      __builtin_amdgcn_sched_barrier(0);
+    for (int ksi = 0; ksi < KS - 1; ++ksi) {
+#pragma unroll
+      for (int j = 0; j < NMF; ++j) {
+        mfma1(ksi & 1, j);
+        __builtin_amdgcn_sched_barrier(0);
+        if (j < NRU) read_unit(IC<u>{}, ksi + 1, (ksi + 1) & 1, j);
+#pragma unroll
+        for (int d = 0; d < NDMA; ++d)
+          if (dma_slot(d) == ksi * NMF + j) dma(kt + NSL - 1, IC<nxt>{}, d);
+        __builtin_amdgcn_sched_barrier(0);
+      }
     }
-    if constexpr (tail)
-      wait_vmcnt<(u < 2 ? 2 - u : 0) * NDMA>();
-    else
-      wait_vmcnt<(NSLOT - 2) * NDMA>();
+    wait_vmcnt<(NSL - 2) * NDMA>();
     wait_lgkmcnt0();
     stage_barrier();
-    // k-step 1
 #pragma unroll
     for (int j = 0; j < NMF; ++j) {
-      mfma1(1, j);
+      mfma1((KS - 1) & 1, j);
       __builtin_amdgcn_sched_barrier(0);
-      if (j < NRU) read_unit(IC<(u + 1) % NSLOT>{}, 0, 0, j);
+      if (j < NRU) read_unit(IC<(u + 1) % NSL>{}, 0, 0, j);
       __builtin_amdgcn_sched_barrier(0);
     }
   };
 
-  // Prologue: stages 0..NSLOT-2 in flight, wait for stage 0.
+  // Prologue: stages 0..NSL-2 in flight, wait for stage 0.
+  static_for<0, NSL - 1>([&](auto S) __attribute__((always_inline)) {
 #pragma unroll
-  for (int j = 0; j < NDMA; ++j) dma(0, IC<0>{}, j);
-#pragma unroll
-  for (int j = 0; j < NDMA; ++j) dma(1, IC<1>{}, j);
-#pragma unroll
-  for (int j = 0; j < NDMA; ++j) dma(2, IC<2>{}, j);
-#pragma unroll
-  for (int j = 0; j < NDMA; ++j) dma(3, IC<3>{}, j);
-  static_assert(NSLOT == 5, "prologue, loop and tail are written for 5 slots");
-  wait_vmcnt<(NSLOT - 2) * NDMA>();
+    for (int j = 0; j < NDMA; ++j) dma(decltype(S)::value, S, j);
+  });
+  wait_vmcnt<(NSL - 2) * NDMA>();
   stage_barrier();
 #pragma unroll
   for (int q = 0; q < NRU; ++q) read_unit(IC<0>{}, 0, 0, q);
   int kt = 0;
-  for (; kt + NSLOT <= nk; kt += NSLOT) {
-    step(kt, IC<0>{}, IC<0>{});
-    step(kt + 1, IC<1>{}, IC<0>{});
-    step(kt + 2, IC<2>{}, IC<0>{});
-    step(kt + 3, IC<3>{}, IC<0>{});
-    step(kt + 4, IC<4>{}, IC<0>{});
-  }
-  const int rem = nk - kt;  // 0..NSLOT-1, uniform
-  if (rem > 0) step(kt, IC<0>{}, IC<1>{});
-  if (rem > 1) step(kt + 1, IC<1>{}, IC<1>{});
-  if (rem > 2) step(kt + 2, IC<2>{}, IC<1>{});
-  if (rem > 3) step(kt + 3, IC<3>{}, IC<1>{});
+  for (; kt + NSL <= nk; kt += NSL)
+    static_for<0, NSL>([&](auto U) __attribute__((always_inline)) { step(kt + decltype(U)::value, U); });
+  const int rem = nk - kt;  // 0..NSL-1, uniform; these steps' DMAs read zeros
+  static_for<0, NSL - 1>([&](auto U) __attribute__((always_inline)) {
+    if (rem > decltype(U)::value) step(kt + decltype(U)::value, U);
+  });
   wait_vmcnt<0>();
   __syncthreads();
 
@@ -590,7 +598,7 @@ struct TileChoice {
 
 TileChoice choose_bf16_tile(int M, int N) {
   const TileChoice cand[3] = {{256, 256}, {256, 128}, {128, 128}};
-  const double eff[3] = {1.0, 0.88, 0.72};
+  const double eff[3] = {1.0, 0.95, 0.78};
   int best = 0;
   double best_cost = 1e300;
   for (int c = 0; c < 3; ++c) {
@@ -606,12 +614,12 @@ TileChoice choose_bf16_tile(int M, int N) {
   return cand[best];
 }
 
-template <int BM, int BN, int WM, int WN, class Epi>
+template <int BM, int BN, int WM, int WN, int KS, int NSL, class Epi>
 hipError_t launch_bf16(const uint16_t* A, int64_t lda, const uint16_t* B,
                        int64_t ldb, int M, int N, int K, int kwrap,
                        const Epi& epi, hipStream_t s) {
   const int tm = (M + BM - 1) / BM, tn = (N + BN - 1) / BN;
-  hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, WM, WN, Epi>), dim3(tm * tn),
+  hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, WM, WN, KS, NSL, Epi>), dim3(tm * tn),
                      dim3(WM * WN * 64), 0, s, A, lda, B, ldb, M, N, K, kwrap,
                      tm, tn, epi);
   return hipGetLastError();
@@ -624,10 +632,10 @@ hipError_t dispatch_bf16(const uint16_t* A, int64_t lda, const uint16_t* B,
   if (M == 0 || N == 0) return hipSuccess;
   const TileChoice t = choose_bf16_tile(M, N);
   if (t.bm == 256 && t.bn == 256)
-    return launch_bf16<256, 256, 2, 2>(A, lda, B, ldb, M, N, K, kwrap, epi, s);
+    return launch_bf16<256, 256, 2, 2, 2, 5>(A, lda, B, ldb, M, N, K, kwrap, epi, s);
   if (t.bm == 256 && t.bn == 128)
-    return launch_bf16<256, 128, 2, 2>(A, lda, B, ldb, M, N, K, kwrap, epi, s);
-  return launch_bf16<128, 128, 2, 2>(A, lda, B, ldb, M, N, K, kwrap, epi, s);
+    return launch_bf16<256, 128, 2, 2, 4, 3>(A, lda, B, ldb, M, N, K, kwrap, epi, s);
+  return launch_bf16<128, 128, 2, 2, 4, 3>(A, lda, B, ldb, M, N, K, kwrap, epi, s);
 }
 
 // ---------------------------------------------------------------------------
@@ -735,6 +743,7 @@ hipError_t gemm_bf16_store_split_a(const uint16_t* A2, int64_t lda,
                                    const uint16_t* B, int64_t ldb, void* C,
                                    int64_t ldc, OutType out, int M, int N, int K,
                                    hipStream_t s) {
+  if (K % 64) return hipErrorInvalidValue;  // each half a whole number of stages
   return dispatch_bf16(A2, lda, B, ldb, M, N, 2 * K, K, EpiStore{C, ldc, (int)out}, s);
 }
 

@@ -41,7 +41,7 @@ hipError_t gemm_bf16_gelu(const uint16_t* A, int64_t lda, const uint16_t* B,
                           int64_t ldb, uint16_t* C, int64_t ldc, int M, int N,
                           int K, hipStream_t s);
 // C = [A_hi | A_lo] * B: A2 is [M, 2K] (row stride lda), the same B[K,N]
-// multiplies both halves (two MFMA passes over K).
+// multiplies both halves (two MFMA passes over K); K a multiple of 64.
 hipError_t gemm_bf16_store_split_a(const uint16_t* A2, int64_t lda,
                                    const uint16_t* B, int64_t ldb, void* C,
                                    int64_t ldc, OutType out, int M, int N, int K,
