@@ -12,6 +12,8 @@ Workload (one "step"): FFN shard i=3 of t=8 at hidden 4096, ffn 16384,
      The other seven partials are the other shards' results, computed once
      before timing: they stand for what the peers would contribute.
 value = algorithmic FFN FLOPs of the shard (4*M*h*f/t) / wall time per step.
+Every timed row starts after about 0.1 s of the same work, untimed, so that
+the GPU has left its idle clock state, then W warmup steps.
 
 The same run also times that step with the sum fused into the second GEMM's
 epilogue (tp_ffn_shard_reduce; rows.ffn_shard_reduce_fused), the attention
@@ -84,8 +86,22 @@ def dev_tensor(np_arr, dtype):
     return torch.from_numpy(np.ascontiguousarray(np_arr)).cuda()
 
 
+def settle(fn, seconds=0.1):
+    """Run fn untimed for about `seconds` of wall time.  An idle MI355X needs
+    about 10 ms of sustained work to leave its low clock state (the first 50
+    FFN steps after an idle second run ~35% slower than the rest), so every
+    timed row starts from a settled clock; W warmup steps follow."""
+    import torch
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < seconds:
+        for _ in range(10):
+            fn()
+        torch.cuda.synchronize()
+
+
 def time_events(fn, steps, warmup):
     import torch
+    settle(fn)
     for _ in range(warmup):
         fn()
     torch.cuda.synchronize()
@@ -291,8 +307,8 @@ def summarize_profiles(stats_csv, fetch_csv, write_csv, cmd_stats, cmd_pmc):
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-attention", action="store_true",
                     help="skip the attention row (profiling runs of the FFN step)")
@@ -354,13 +370,22 @@ def main():
     def red():
         B.tp_partial_reduce(parts, R, out)
 
+    settle(lambda: (ffn(), red()))
     for _ in range(args.warmup):
         ffn()
         red()
     torch.cuda.synchronize()
+    # The K timed steps: launches only, nothing else on the stream.
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        ffn()
+        red()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_step = wall / args.steps * 1e3
+    # Per-call durations: the same K steps again with events around each call.
     ev = [tuple(torch.cuda.Event(enable_timing=True) for _ in range(3))
           for _ in range(args.steps)]
-    t0 = time.perf_counter()
     for e0, e1, e2 in ev:
         e0.record()
         ffn()
@@ -368,8 +393,6 @@ def main():
         red()
         e2.record()
     torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    ms_step = wall / args.steps * 1e3
     ffn_ms = sum(a.elapsed_time(b) for a, b, _ in ev) / args.steps
     red_ms = sum(b.elapsed_time(c) for _, b, c in ev) / args.steps
     fl = ffn_flops(M, h, f, t)
