@@ -8,18 +8,21 @@
 // the row-parallel output projection (page "Tensor Parallelism > Combining
 // Column and Row Parallelism", FFN steps 1-2 and the attention paragraphs).
 //
-// bf16 kernel layout
-//   * A (activations) is K-contiguous; B (weights, "X W" orientation) is
-//     N-contiguous.  Both MFMA operands want 8 consecutive K values per lane,
-//     so B is transposed on its way into LDS: each thread loads an 8(k) x 8(n)
-//     block with eight 16-byte loads and repacks it with v_perm_b32 into eight
-//     16-byte k-runs.
-//   * LDS holds A as [BM][64] and B^T as [BN][64] bf16 (128-byte rows of eight
-//     16-byte chunks).  Chunk c of row r lives at chunk c ^ ((r ^ r>>3) & 7),
-//     which keeps the 16-byte operand reads of 8 (or 16) consecutive rows on
-//     distinct banks.
-//   * Two LDS stages: while the MFMAs consume stage k, the global loads for
-//     stage k+1 are in flight into registers; one barrier per K step.
+// bf16 kernels
+//   * Both operands go from memory straight into an LDS ring with buffer
+//     loads that write LDS (1 KiB per instruction), tracked with explicit
+//     vmcnt waits.  A (activations, K-contiguous) is stored as K-rows with a
+//     16-byte-chunk XOR swizzle and read with ds_read_b128; B (weights,
+//     N-contiguous) keeps its [k][n] layout with a 64-byte-block swizzle and
+//     is read with ds_read_b64_tr_b16, which transposes it into the MFMA
+//     operand.
+//   * gemm_bf16_kernel: 4 waves, 256x128 or 128x128 tiles, K = 64 per stage
+//     through a 3-slot ring, DMAs and fragment reads interleaved between the
+//     MFMAs of each wave.
+//   * gemm_bf16_pp_kernel: 8 waves, 256x256 tiles, K = 32 per stage through
+//     a 5-slot ring; two groups of waves alternate between a memory phase and
+//     an MFMA-only phase, one phase apart, so each SIMD's matrix pipe is fed
+//     by one wave or the other.
 //   * Workgroup ids are remapped so each XCD (dispatch is round-robin over
 //     the 8 XCDs) receives a contiguous run of tiles, ordered in groups of 8
 //     tile-rows so neighbouring tiles share A and B panels in that XCD's L2.

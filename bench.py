@@ -57,10 +57,15 @@ def attn_flops(batch, seq, hidden, n_heads, head_dim, t):
 
 
 def src_hash(*names):
+    """Hash of the code in csrc/ files: `//` comments, blank lines and
+    surrounding whitespace are dropped, so editing comments keeps the hash."""
     h = hashlib.sha256()
     for n in names:
-        with open(os.path.join(ROOT, "attention_shards_amd", "csrc", n), "rb") as f:
-            h.update(f.read())
+        with open(os.path.join(ROOT, "attention_shards_amd", "csrc", n)) as f:
+            for line in f:
+                code = line.split("//", 1)[0].strip()
+                if code:
+                    h.update(code.encode() + b"\n")
     return h.hexdigest()[:16]
 
 
