@@ -229,6 +229,51 @@ struct EpiQkv {
       }
     }
   }
+  // V^T written down the columns: true when the 64 columns at c0 are all V
+  // and 8-token groups never cross a sequence (seq a multiple of 8), so
+  // store_col8 can write 8 consecutive tokens of one head dim as one
+  // 16-byte vector (wave-uniform).
+  __device__ bool column_tile(int c0) const {
+    return (q.seq & 7) == 0 && (c0 >> 7) >= 2 * q.nl;
+  }
+  // Rows row..row+7 (tokens; row a multiple of 8) of V column col.
+  __device__ void store_col8(int row, int col, int M, const float* v) const {
+    const int dd = col & 127;
+    const int head = (col >> 7) - 2 * q.nl;
+    const int b = row / q.seq;
+    const int s = row - b * q.seq;
+    const int64_t off = (((int64_t)b * q.nl + head) * 128 + dd) * q.seq_pad + s;
+    uint32_t hi[8], lo[8];
+#pragma unroll
+    for (int r = 0; r < 8; ++r) {
+      const _Float16 vh = (_Float16)v[r];
+      const _Float16 vl = (_Float16)(v[r] - (float)vh);
+      hi[r] = __builtin_bit_cast(uint16_t, vh);
+      lo[r] = __builtin_bit_cast(uint16_t, vl);
+    }
+    if (row + 8 <= M) {
+      *reinterpret_cast<u32x4*>(q.vt_hi + off) =
+          u32x4{hi[0] | (hi[1] << 16), hi[2] | (hi[3] << 16), hi[4] | (hi[5] << 16), hi[6] | (hi[7] << 16)};
+      *reinterpret_cast<u32x4*>(q.vt_lo + off) =
+          u32x4{lo[0] | (lo[1] << 16), lo[2] | (lo[3] << 16), lo[4] | (lo[5] << 16), lo[6] | (lo[7] << 16)};
+    } else {
+      for (int r = 0; r < 8 && row + r < M; ++r) {
+        q.vt_hi[off + r] = (uint16_t)hi[r];
+        q.vt_lo[off + r] = (uint16_t)lo[r];
+      }
+    }
+  }
+};
+
+// Epilogues that can write some tiles down the columns (column_tile,
+// store_col8) instead of along the rows.
+template <class E>
+struct ColumnRuns {
+  static constexpr bool value = false;
+};
+template <>
+struct ColumnRuns<EpiQkv> {
+  static constexpr bool value = true;
 };
 
 // Tile index with the XCD-contiguous remap and grouped (8 tile-rows) order.
@@ -336,6 +381,20 @@ __device__ __forceinline__ void epilogue_lds(uint8_t* smem, f32x16 (&acc)[FM][FN
         stage_f[i * PITCH + ni * 32 + (lane & 31)] = acc[mi][ni][e];
       }
     asm volatile("" ::: "memory");  // keep the LDS writes before the reads
+    if constexpr (ColumnRuns<Epi>::value && WCOLS == 64) {
+      if (epi.column_tile(c0)) {  // lane = column, 8 rows per store
+#pragma unroll
+        for (int g8 = 0; g8 < 4; ++g8) {
+          const int row = r0 + mi * 32 + 8 * g8;
+          float v[8];
+#pragma unroll
+          for (int i = 0; i < 8; ++i) v[i] = stage_f[(8 * g8 + i) * PITCH + lane];
+          if (row < M && c0 + lane < N) epi.store_col8(row, c0 + lane, M, v);
+        }
+        asm volatile("" ::: "memory");
+        continue;
+      }
+    }
     // An epilogue that reads memory takes RB rows per call so that the
     // loads of several rows are in flight together.
     constexpr int RB = RowBatch<Epi>::value;
