@@ -176,12 +176,10 @@ template <int PDT, int RDT, int ODT, int C>
 hipError_t launch_c(const ReducePtrs& ptrs, int t, const void* R, void* out,
                     int64_t n, hipStream_t s) {
   const int64_t ngroups = n / 8;
-  // One 8-element group per thread when a thread has few loads in flight;
-  // with many partials, a grid of at most 4096 blocks that loops (measured
-  // on MI355X: t=4 [8192,12288] 6.2 vs 5.5 TB/s, t=8 [4096,4096] 5.9 vs
-  // 5.5 TB/s for the other choice).
+  // One 8-element group per thread (measured on MI355X with inputs rotated
+  // through more memory than the caches hold: t=8 bf16 [4096,4096] 5.9 TB/s
+  // vs 5.7 TB/s for a grid capped at 4096 looping blocks).
   int64_t blocks = (ngroups + 255) / 256;
-  if (t >= 6 && blocks > 4096) blocks = 4096;
   if (blocks > (int64_t)1 << 30) blocks = (int64_t)1 << 30;
   if (blocks < 1) blocks = 1;
   hipLaunchKernelGGL((reduce_kernel<PDT, RDT, ODT, C>), dim3((unsigned)blocks),
@@ -189,13 +187,16 @@ hipError_t launch_c(const ReducePtrs& ptrs, int t, const void* R, void* out,
   return hipGetLastError();
 }
 
-// Chunk size: the smallest of 1, 2, 4, 8 that holds the t-1 later partials.
+// Chunk size: the smallest of 1, 2, 4, 7, 8 that holds the t-1 later
+// partials (7 for t = 8, so no load is a duplicate: fp32 partials 5.7 vs
+// 5.3 TB/s at t=8 [2048,8192]).
 template <int PDT, int RDT, int ODT>
 hipError_t launch(const ReducePtrs& ptrs, int t, const void* R, void* out,
                   int64_t n, hipStream_t s) {
   if (t <= 2) return launch_c<PDT, RDT, ODT, 1>(ptrs, t, R, out, n, s);
   if (t <= 3) return launch_c<PDT, RDT, ODT, 2>(ptrs, t, R, out, n, s);
   if (t <= 5) return launch_c<PDT, RDT, ODT, 4>(ptrs, t, R, out, n, s);
+  if (t == 8) return launch_c<PDT, RDT, ODT, 7>(ptrs, t, R, out, n, s);
   return launch_c<PDT, RDT, ODT, 8>(ptrs, t, R, out, n, s);
 }
 

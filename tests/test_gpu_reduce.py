@@ -33,6 +33,8 @@ def check_bound(got, parts, R, out_dtype):
     (3, syn.F32, syn.F32, syn.F32, 17, 8),
     (1, syn.F32, None, syn.BF16, 5, 1000 * 8),
     (13, syn.F32, syn.BF16, syn.F32, 100, 72),
+    (8, syn.F32, syn.BF16, syn.F32, 37, 104),   # one chunk of 7 partials
+    (7, syn.BF16, None, syn.F32, 33, 200),      # clamped chunk of 8
 ])
 def test_reduce_random(gpu, t, pdt, rdt, odt, rows, cols):
     parts_h = [syn.normal_tensor(900 + t, k, (rows, cols), 0.5, pdt) for k in range(t)]
