@@ -34,34 +34,34 @@ namespace {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
-// fp32 -> bf16, round to nearest even (finite values).
-__device__ __forceinline__ uint32_t f2bf(float f) {
-  uint32_t u = __float_as_uint(f);
-  u += 0x7FFFu + ((u >> 16) & 1u);
-  return u >> 16;
-}
-__device__ __forceinline__ float bf2f(uint32_t b) {
-  return __uint_as_float(b << 16);
+// Two fp32 values rounded to bf16 (nearest even) and packed, low half
+// first: one v_cvt_pk_bf16_f32.
+__device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{a, b}, bf16x2));
 }
 
-// GeLU(z) = z * Phi(z), Phi the standard normal CDF.  Phi comes from erfc
+// GeLU(z) = z * Phi(z), Phi the standard normal CDF, with Phi from erfc
 // through the rational approximation of Abramowitz & Stegun, Handbook of
 // Mathematical Functions, formula 7.1.26 (|error of erf| <= 1.5e-7 for
-// x >= 0), taken at x = |z|/sqrt(2) and reflected: Phi(z) = 1 - erfc(x)/2
-// for z >= 0 and erfc(x)/2 for z < 0.  Branch-free: one reciprocal, one
-// exponential and seven multiply-adds, so |GeLU error| <= |z| * 1e-7 plus
-// fp32 rounding.
+// x >= 0): erfc(x) = t P(t) exp(-x^2), t = 1/(1 + 0.3275911 x), taken at
+// x = |z|/sqrt(2).  With E = z erfc(x)/2 (the sign of z), GeLU = z - E for
+// z >= 0 and E for z < 0, i.e. max(z, 0) - |E|.  Branch-free: one
+// reciprocal, one exponential, ten multiply(-add)s, a max and a subtract;
+// P/2's coefficients are P's halved (exact), so |GeLU error| <= |z| * 1e-7
+// plus fp32 rounding.
 __device__ __forceinline__ float gelu_erf(float z) {
-  const float x = fabsf(z) * 0.70710678118654752f;
-  const float t = __builtin_amdgcn_rcpf(fmaf(0.3275911f, x, 1.0f));
-  float p = fmaf(1.061405429f, t, -1.453152027f);
-  p = fmaf(p, t, 1.421413741f);
-  p = fmaf(p, t, -0.284496736f);
-  p = fmaf(p, t, 0.254829592f);
-  const float half_erfc = 0.5f * p * t * __expf(-x * x);
-  return z * (z >= 0.0f ? 1.0f - half_erfc : half_erfc);
+  const float t = __builtin_amdgcn_rcpf(fmaf(fabsf(z), 0.3275911f * 0.70710678118654752f, 1.0f));
+  float p = fmaf(0.5307027145f, t, -0.7265760135f);
+  p = fmaf(p, t, 0.7107068705f);
+  p = fmaf(p, t, -0.142248368f);
+  p = fmaf(p, t, 0.127414796f);
+  const float e = __builtin_amdgcn_exp2f(z * z * (-0.5f * 1.4426950408889634f));
+  const float E = z * (p * t * e);
+  return fmaxf(z, 0.0f) - fabsf(E);
 }
 
 // ---------------------------------------------------------------------------
@@ -76,10 +76,7 @@ __device__ __forceinline__ void store_run4(void* C, int64_t ldc, int out, int ro
     *reinterpret_cast<f32x4*>(c) = f32x4{v[0], v[1], v[2], v[3]};
   } else {
     uint16_t* c = static_cast<uint16_t*>(C) + (int64_t)row * ldc + col0;
-    uint2 w;
-    w.x = f2bf(v[0]) | (f2bf(v[1]) << 16);
-    w.y = f2bf(v[2]) | (f2bf(v[3]) << 16);
-    *reinterpret_cast<uint2*>(c) = w;
+    *reinterpret_cast<uint2*>(c) = uint2{pack_bf16(v[0], v[1]), pack_bf16(v[2], v[3])};
   }
 }
 
@@ -92,9 +89,8 @@ __device__ __forceinline__ void store_run8(void* C, int64_t ldc, int out, int ro
     c[1] = f32x4{v[4], v[5], v[6], v[7]};
   } else {
     uint16_t* c = static_cast<uint16_t*>(C) + (int64_t)row * ldc + col0;
-    *reinterpret_cast<u32x4*>(c) =
-        u32x4{f2bf(v[0]) | (f2bf(v[1]) << 16), f2bf(v[2]) | (f2bf(v[3]) << 16),
-              f2bf(v[4]) | (f2bf(v[5]) << 16), f2bf(v[6]) | (f2bf(v[7]) << 16)};
+    *reinterpret_cast<u32x4*>(c) = u32x4{pack_bf16(v[0], v[1]), pack_bf16(v[2], v[3]),
+                                         pack_bf16(v[4], v[5]), pack_bf16(v[6], v[7])};
   }
 }
 
@@ -205,18 +201,18 @@ struct EpiQkv {
     const int b = row / q.seq;
     const int s = row - b * q.seq;
     const int64_t bh = (int64_t)b * q.nl + head;
-    uint32_t hi[4], lo[4];
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      hi[r] = f2bf(v[r]);
-      lo[r] = f2bf(v[r] - bf2f(hi[r]));
-    }
     if (sec < 2) {
+      // bf16 hi/lo pair: hi = bf16(v), lo = bf16(v - hi)
+      const uint32_t h01 = pack_bf16(v[0], v[1]), h23 = pack_bf16(v[2], v[3]);
+      const uint32_t l01 = pack_bf16(v[0] - __uint_as_float(h01 << 16),
+                                     v[1] - __uint_as_float(h01 & 0xFFFF0000u));
+      const uint32_t l23 = pack_bf16(v[2] - __uint_as_float(h23 << 16),
+                                     v[3] - __uint_as_float(h23 & 0xFFFF0000u));
       const int64_t off = (bh * q.seq_pad + s) * 128 + dd;
       uint16_t* ph = sec == 0 ? q.q_hi : q.k_hi;
       uint16_t* pl = sec == 0 ? q.q_lo : q.k_lo;
-      *reinterpret_cast<uint2*>(ph + off) = uint2{hi[0] | (hi[1] << 16), hi[2] | (hi[3] << 16)};
-      *reinterpret_cast<uint2*>(pl + off) = uint2{lo[0] | (lo[1] << 16), lo[2] | (lo[3] << 16)};
+      *reinterpret_cast<uint2*>(ph + off) = uint2{h01, h23};
+      *reinterpret_cast<uint2*>(pl + off) = uint2{l01, l23};
     } else {
       // V: fp16 hi/lo pair (the probabilities multiplying it are fp16)
       const int64_t off = (bh * 128 + dd) * q.seq_pad + s;
