@@ -837,7 +837,7 @@ struct TileChoice {
 
 TileChoice choose_bf16_tile(int M, int N) {
   const TileChoice cand[3] = {{256, 256}, {256, 128}, {128, 128}};
-  const double eff[3] = {1.0, 0.95, 0.78};
+  const double eff[3] = {1.0, 0.95, 0.70};
   int best = 0;
   double best_cost = 1e300;
   for (int c = 0; c < 3; ++c) {

@@ -170,8 +170,13 @@ def sweep(path, steps, warmup):
                 ms = time_events(lambda: B.tp_ffn_shard(X, W1, W2, Y, 0, t, workspace=ws),
                                  steps, warmup)
                 tf = ffn_flops(2048, h, f, t) / (ms * 1e-3) / 1e12
+                # context: the same shard through torch (hipBLASLt GEMMs, a
+                # separate exact-erf GeLU kernel, bf16 between them)
+                tms = time_events(lambda: torch.nn.functional.gelu(X @ W1) @ W2, steps, warmup)
                 rec = {"hidden": h, "t": t, "ms": round(ms, 5), "tflops": round(tf, 2),
-                       "frac_peak": round(tf / PEAK_BF16_TFLOPS, 4)}
+                       "frac_peak": round(tf / PEAK_BF16_TFLOPS, 4),
+                       "torch_ms": round(tms, 5),
+                       "torch_tflops": round(ffn_flops(2048, h, f, t) / (tms * 1e-3) / 1e12, 2)}
                 out.write(json.dumps(rec) + "\n")
                 print(json.dumps(rec), file=sys.stderr, flush=True)
                 del W1, W2, Y, ws
@@ -309,6 +314,38 @@ def summarize_profiles(stats_csv, fetch_csv, write_csv, cmd_stats, cmd_pmc):
     print(f"wrote profiles (traffic {total/1e6:.1f} MB per call, algorithmic {alg/1e6:.1f} MB)")
 
 
+def summarize_sweep(path, cmd):
+    """Write profiles/sweep_ffn_shard_tokens2048.md from a --sweep JSONL file."""
+    recs = [json.loads(line) for line in open(path) if line.strip()]
+    by = {}
+    for r in recs:
+        by.setdefault(r["hidden"], {})[r["t"]] = r
+    ts = sorted({r["t"] for r in recs})
+    lines = ["# FFN shard TFLOP/s vs hidden size (2048 tokens, ffn = 4h, bf16, shard 0 of t)",
+             "", "Command (from the repository root, on one MI355X):", "", "```", cmd, "```", "",
+             "Each cell: this library's `tp_ffn_shard` (GEMM1 + fused GeLU, GEMM2) / the same",
+             "shard through torch (hipBLASLt GEMMs and a separate exact-erf GeLU kernel), in",
+             "TFLOP/s of the algorithmic 4·M·h·f/t FLOPs; device-seeded inputs, HIP-event",
+             "timing of each call. Fraction of the 2516.6 TFLOP/s bf16 peak in brackets.", "",
+             "| hidden | " + " | ".join(f"t={t}" for t in ts) + " |",
+             "|---:|" + "---:|" * len(ts)]
+    for h in sorted(by):
+        cells = []
+        for t in ts:
+            r = by[h].get(t)
+            cells.append("" if r is None else
+                         f"{r['tflops']:.0f} / {r['torch_tflops']:.0f} ({r['frac_peak']:.2f})")
+        lines.append(f"| {h} | " + " | ".join(cells) + " |")
+    wins = sum(1 for r in recs if r["tflops"] > r["torch_tflops"])
+    best = max(recs, key=lambda r: r["tflops"])
+    lines += ["", f"This library is faster at {wins} of {len(recs)} points; its best point is "
+              f"{best['tflops']:.0f} TFLOP/s ({best['frac_peak']:.1%} of peak) at hidden "
+              f"{best['hidden']}, t={best['t']}."]
+    with open(os.path.join(ROOT, "profiles", "sweep_ffn_shard_tokens2048.md"), "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print(f"wrote profiles/sweep_ffn_shard_tokens2048.md ({len(recs)} points)")
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -322,12 +359,17 @@ def main():
     ap.add_argument("--sweep", metavar="OUT_JSONL", default=None)
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run a 1 GiB device copy first (counter calibration)")
+    ap.add_argument("--summarize-sweep", metavar="SWEEP_JSONL", default=None,
+                    help="write profiles/sweep_*.md from a --sweep output and exit")
     ap.add_argument("--summarize-profiles", nargs=3,
                     metavar=("STATS_CSV", "FETCH_CSV", "WRITE_CSV"),
                     help="write profiles/ summaries from rocprofv3 CSVs and exit")
     ap.add_argument("--profile-commands", nargs=2, default=["", ""],
                     metavar=("STATS_CMD", "PMC_CMD"))
     args = ap.parse_args()
+    if args.summarize_sweep:
+        summarize_sweep(args.summarize_sweep, args.profile_commands[0])
+        return
     if args.summarize_profiles:
         summarize_profiles(*args.summarize_profiles, *args.profile_commands)
         return
