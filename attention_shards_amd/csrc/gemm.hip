@@ -869,6 +869,8 @@ hipError_t dispatch_bf16(const uint16_t* A, int64_t lda, const uint16_t* B,
                          int64_t ldb, int M, int N, int K, int kwrap,
                          const Epi& epi, hipStream_t s) {
   if (M == 0 || N == 0) return hipSuccess;
+  // tiles are addressed with 32-bit byte offsets: 256 rows of A, 64 of B
+  if (lda >= ((int64_t)1 << 22) || ldb >= ((int64_t)1 << 24)) return hipErrorInvalidValue;
   const TileChoice t = choose_bf16_tile(M, N);
   if (t.bm == 256 && t.bn == 256) {
     const int tm = (M + 255) / 256, tn = (N + 255) / 256;

@@ -60,6 +60,13 @@ tp_status_t hip_status(hipError_t e, const char* what) {
 }
 
 constexpr int64_t kInt32Max = 2147483647;
+// The bf16 GEMMs address a tile through a buffer descriptor with 32-bit byte
+// offsets: up to 256 rows of A (row stride lda) and 64 rows of B (ldb) per
+// tile, so lda < 2^22 and ldb < 2^24 elements.  The attention kernel reads
+// 128 V^T rows of seq_pad keys the same way, so seq_pad < 2^23.
+constexpr int64_t kMaxLdA = int64_t(1) << 22;
+constexpr int64_t kMaxLdB = int64_t(1) << 24;
+constexpr int64_t kMaxSeqPad = int64_t(1) << 23;
 constexpr int64_t kAttnHeadDim = 128;
 constexpr int64_t kAttnKeyTile = 64;
 
@@ -148,6 +155,11 @@ tp_status_t check_ffn(const char* fn, const void* X, const void* W1_i, const voi
                 fn, i, (long long)hidden, (long long)fs, (long long)*ld_w1, (long long)vec);
   if (tokens > kInt32Max || hidden > kInt32Max || fs > kInt32Max)
     return fail(TP_ERR_SHAPE, "%s(i=%d): a dimension exceeds 2^31-1", fn, i);
+  if (in_dtype == TP_BF16 && (hidden >= kMaxLdA || fs >= kMaxLdA || *ld_w1 >= kMaxLdB))
+    return fail(TP_ERR_SHAPE,
+                "%s(i=%d): bf16 needs hidden and ffn/t below 2^22 and ld_w1 below 2^24 "
+                "(hidden=%lld ffn/t=%lld ld_w1=%lld)",
+                fn, i, (long long)hidden, (long long)fs, (long long)*ld_w1);
   *fs_out = fs;
   if (tokens == 0) return ok();
   if (!X || !W1_i || !W2_i || !out)
@@ -409,6 +421,12 @@ tp_status_t tp_attn_shard(const void* X, const void* Wqkv_i, const void* Wo_i,
     if (tokens > kInt32Max || hidden > kInt32Max || 3 * nl * head_dim > kInt32Max ||
         batch * nl * ((seq + 63) / 64) > kInt32Max)
       return fail(TP_ERR_SHAPE, "tp_attn_shard(i=%d): a dimension exceeds 2^31-1", i);
+    if (hidden >= kMaxLdA || 2 * nl * head_dim >= kMaxLdA ||
+        (seq + kAttnKeyTile - 1) / kAttnKeyTile * kAttnKeyTile >= kMaxSeqPad)
+      return fail(TP_ERR_SHAPE,
+                  "tp_attn_shard(i=%d): needs hidden and 2*(n_heads/t)*head_dim below 2^22 and "
+                  "seq below 2^23 (hidden=%lld n_heads/t=%lld seq=%lld)",
+                  i, (long long)hidden, (long long)nl, (long long)seq);
     if (tokens == 0) return ok();
     if (!X || !Wqkv_i || !Wo_i || !Y_i)
       return fail(TP_ERR_NULL, "tp_attn_shard(i=%d): NULL tensor pointer", i);
@@ -480,8 +498,11 @@ tp_status_t tp_partial_reduce(const void* const* partials, int32_t t,
                   residual_dtype, out_dtype);
     if (t < 1 || t > TP_MAX_PARTIALS)
       return fail(TP_ERR_SHARD, "tp_partial_reduce: t=%d outside [1, %d]", t, TP_MAX_PARTIALS);
-    if (rows < 0 || cols < 0 || cols % 8 != 0)
-      return fail(TP_ERR_SHAPE, "tp_partial_reduce: rows=%lld cols=%lld (cols multiple of 8)",
+    if (rows < 0 || cols < 0 || cols % 8 != 0 ||
+        (rows > 0 && cols > (int64_t(1) << 60) / rows))
+      return fail(TP_ERR_SHAPE,
+                  "tp_partial_reduce: rows=%lld cols=%lld (cols a multiple of 8, "
+                  "rows*cols at most 2^60)",
                   (long long)rows, (long long)cols);
     const int64_t n = rows * cols;
     if (n == 0) return ok();

@@ -96,7 +96,9 @@ typedef enum {
  *                                   holds GeLU(Z_i) [tokens, ffn/t] between the
  *                                   two GEMMs (no gather: step 2 reads it as is)
  * Shape rules: tokens >= 0 (0 enqueues nothing); hidden and ffn/t multiples
- * of 8 (bf16) or 4 (fp32); ld_w1 >= ffn/t and a multiple of the same.
+ * of 8 (bf16) or 4 (fp32); ld_w1 >= ffn/t and a multiple of the same; every
+ * dimension below 2^31; with bf16 inputs also hidden, ffn/t < 2^22 and
+ * ld_w1 < 2^24 (row strides the GEMM tiles address with 32-bit offsets).
  * Y_i must not overlap X, W1_i, W2_i or the workspace (TP_ERR_ALIAS).
  * The shard index i only selects which pointers the caller passes; it is
  * validated and reported in error messages.
@@ -136,7 +138,9 @@ tp_status_t tp_ffn_shard(const void* X, const void* W1_i, const void* W2_i,
  * softmax runs in fp32 with the probabilities rounded to fp16; the head
  * outputs O are kept as a bf16 hi+lo pair, which the output projection
  * multiplies by Wo_i in two passes.
- * Shape rules: batch, seq >= 0; head_dim == 128; hidden multiple of 8.
+ * Shape rules: batch, seq >= 0; head_dim == 128; hidden multiple of 8;
+ * batch*seq below 2^31; hidden and 2*(n_heads/t)*head_dim below 2^22; seq
+ * below 2^23 (32-bit tile offsets in the GEMMs and the attention kernel).
  */
 size_t tp_attn_shard_workspace_bytes(int64_t batch, int64_t seq, int32_t n_heads,
                                      int32_t head_dim, int32_t t);
@@ -162,7 +166,7 @@ tp_status_t tp_attn_shard(const void* X, const void* Wqkv_i, const void* Wo_i,
  *   out        device [rows, cols] of out_dtype; it MAY be the same buffer as
  *              residual or partials[0] when the dtypes match (each element is
  *              read before it is written); any other overlap is TP_ERR_ALIAS
- * Shape rules: rows, cols >= 0; cols a multiple of 8.
+ * Shape rules: rows, cols >= 0; cols a multiple of 8; rows*cols <= 2^60.
  */
 tp_status_t tp_partial_reduce(const void* const* partials, int32_t t,
                               const void* residual, void* out, int64_t rows,

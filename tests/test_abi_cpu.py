@@ -104,6 +104,9 @@ def ffn(lib, **kw):
     (dict(ffn=2 * 36), "TP_ERR_SHAPE"),             # f/t = 36
     (dict(ld=100), "TP_ERR_SHAPE"),                 # ld_w1 < f/t
     (dict(ld=132), "TP_ERR_SHAPE"),                 # ld_w1 not a multiple of 8
+    (dict(hidden=1 << 22, ffn=2 << 22), "TP_ERR_SHAPE"),  # bf16 row stride limits
+    (dict(ffn=2 << 22), "TP_ERR_SHAPE"),
+    (dict(ld=1 << 24), "TP_ERR_SHAPE"),
     (dict(X=None), "TP_ERR_NULL"),
     (dict(Y=None), "TP_ERR_NULL"),
     (dict(ws=None), "TP_ERR_WORKSPACE"),
@@ -156,6 +159,8 @@ def attn(lib, **kw):
     (dict(hidden=250), "TP_ERR_SHAPE"),
     (dict(causal=2), "TP_ERR_SHAPE"),
     (dict(seq=-3), "TP_ERR_SHAPE"),
+    (dict(seq=1 << 23), "TP_ERR_SHAPE"),            # V^T rows addressed with 32-bit offsets
+    (dict(hidden=1 << 22), "TP_ERR_SHAPE"),
     (dict(Wo=None), "TP_ERR_NULL"),
     (dict(wsb=1000), "TP_ERR_WORKSPACE"),
     (dict(Y=X), "TP_ERR_ALIAS"),
@@ -186,6 +191,7 @@ def test_reduce_rejects(lib):
     assert B.STATUS[reduce_call(lib, P * 22, t=65)[0]] == "TP_ERR_SHARD"
     assert B.STATUS[reduce_call(lib, P, cols=60)[0]] == "TP_ERR_SHAPE"
     assert B.STATUS[reduce_call(lib, P, rows=-1)[0]] == "TP_ERR_SHAPE"
+    assert B.STATUS[reduce_call(lib, P, rows=1 << 40, cols=1 << 40)[0]] == "TP_ERR_SHAPE"
     assert B.STATUS[reduce_call(lib, P, pdt=9)[0]] == "TP_ERR_DTYPE"
     assert B.STATUS[reduce_call(lib, P, R=WS, rdt=4)[0]] == "TP_ERR_DTYPE"
     assert B.STATUS[reduce_call(lib, [X, 0, W2])[0]] == "TP_ERR_NULL"
