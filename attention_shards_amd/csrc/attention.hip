@@ -35,6 +35,13 @@
 //     workspace), B = P^T straight from the score registers.  The query of
 //     every accumulator is again lane % 16, so softmax rescales are lane-local
 //     and only the row max needs two cross-lane exchanges.
+#include <functional>
+#include <map>
+#include <mutex>
+#include <queue>
+#include <tuple>
+#include <vector>
+
 #include "internal.h"
 
 namespace tp {
@@ -56,7 +63,7 @@ constexpr int KT = 64;    // keys per tile
 constexpr int K_ROW = D * 2;      // 256-byte K rows (16 chunks)
 constexpr int V_ROW = KT * 2;     // 128-byte V^T rows (8 chunks)
 constexpr int TILE = KT * D * 2;  // 16 KiB per array
-constexpr int TARGET_ITEMS = 1024;  // aim for about four workgroups per CU
+constexpr int MAX_ITEMS = 4096;  // bounds the partial-result workspace
 
 __device__ __forceinline__ uint32_t f2bf(float f) {
   uint32_t u = __float_as_uint(f);
@@ -477,20 +484,98 @@ vt_pad_zero_kernel(QkvOut q, int rows) {
   }
 }
 
+// Estimated time, in units of one key tile of one workgroup, of the
+// attention kernel with chunks of `ch` tiles: workgroups are dispatched in
+// grid order (longest query blocks first) onto NCU compute units, one at a
+// time each (the LDS holds one), and cost ITEM_COST (the start-up of a
+// workgroup: Q load, first tile round trip, partial write) plus their tiles;
+// splitting a query block adds MERGE_COST per split workgroup and the merge
+// kernel's MERGE_LAUNCH.  Fitted to measured kernel times at 1024-8192
+// tokens and 8-24 local heads (about 10% RMS error).
+constexpr int NCU = 256;
+constexpr double ITEM_COST = 4.0;
+constexpr double MERGE_COST = 0.004;
+constexpr double MERGE_LAUNCH = 2.0;
+
+double split_cost(int nqb, int nbh, int seq, int causal, int ch) {
+  std::priority_queue<double, std::vector<double>, std::greater<double>> cu;
+  for (int k = 0; k < NCU; ++k) cu.push(0.0);
+  double end = 0.0;
+  int64_t split = 0;
+  for (int qb = nqb - 1; qb >= 0; --qb) {
+    const int nt = ntile_of(qb, seq, causal);
+    const int nc = div_up(nt, ch);
+    if (nc > 1) split += (int64_t)nc * nbh;
+    for (int c = 0; c < nc; ++c) {
+      const int tiles = nt - c * ch < ch ? nt - c * ch : ch;
+      for (int bh = 0; bh < nbh; ++bh) {
+        const double t0 = cu.top();
+        cu.pop();
+        const double t1 = t0 + ITEM_COST + tiles;
+        cu.push(t1);
+        if (t1 > end) end = t1;
+      }
+    }
+  }
+  return end + MERGE_COST * (double)split + (split ? MERGE_LAUNCH : 0.0);
+}
+
+int64_t count_items(int nqb, int seq, int causal, int ch) {
+  int64_t items = 0;
+  for (int qb = 0; qb < nqb; ++qb) items += div_up(ntile_of(qb, seq, causal), ch);
+  return items;
+}
+
+// Chunk size.  The default aims at about 1024 workgroups with chunks of at
+// least 4 tiles.  Small problems pay for that in workgroup start-ups: when
+// the estimate above finds a chunk of at most 16 tiles (grid within
+// MAX_ITEMS) at least 10% cheaper, that one is used instead (8 heads, 2048
+// causal tokens: 10 tiles, 272 workgroups, 54 us vs 68 us).  Larger chunks
+// are not searched: there the estimate is least reliable and measured times
+// vary by up to 40% between neighbouring sizes.  Memoised per shape.
+int choose_chunk(int nqb, int nbh, int seq, int causal) {
+  static std::mutex m;
+  static std::map<std::tuple<int, int, int, int>, int> memo;
+  const auto key = std::make_tuple(nqb, nbh, seq, causal);
+  {
+    std::lock_guard<std::mutex> lock(m);
+    const auto it = memo.find(key);
+    if (it != memo.end()) return it->second;
+  }
+  int64_t tiles = 0;
+  for (int qb = 0; qb < nqb; ++qb) tiles += ntile_of(qb, seq, causal);
+  tiles *= nbh;
+  const int64_t dflt = (tiles + 1023) / 1024;
+  int best = (int)(dflt < 4 ? 4 : dflt);
+  const int max_nt = ntile_of(nqb - 1, seq, causal);  // the longest key range
+  if (count_items(nqb, seq, causal, 16 < max_nt ? 16 : max_nt) * nbh <= MAX_ITEMS) {
+    const double base = split_cost(nqb, nbh, seq, causal, best);
+    double best_cost = base;
+    int pick = best;
+    for (int ch = 1; ch <= 16 && ch <= max_nt; ++ch) {
+      if (count_items(nqb, seq, causal, ch) * nbh > MAX_ITEMS) continue;
+      const double cost = split_cost(nqb, nbh, seq, causal, ch);
+      if (cost < best_cost * 0.999) {
+        best_cost = cost;
+        pick = ch;
+      }
+    }
+    if (best_cost <= 0.9 * base) best = pick;
+  }
+  std::lock_guard<std::mutex> lock(m);
+  if (memo.size() > 1024) memo.clear();
+  memo[key] = best;
+  return best;
+}
+
 }  // namespace
 
 AttnSplit attn_split(int batch, int seq, int nl, bool causal) {
   AttnSplit sp;
   sp.nbh = batch * nl;
   sp.nqb = div_up(seq, QB);
-  int64_t tiles = 0;
-  for (int qb = 0; qb < sp.nqb; ++qb) tiles += ntile_of(qb, seq, causal ? 1 : 0);
-  tiles *= sp.nbh;
-  int64_t ch = (tiles + TARGET_ITEMS - 1) / TARGET_ITEMS;
-  sp.ch = (int)(ch < 4 ? 4 : ch);
-  int64_t items = 0;
-  for (int qb = 0; qb < sp.nqb; ++qb) items += div_up(ntile_of(qb, seq, causal ? 1 : 0), sp.ch);
-  sp.n_items = (int)(items * sp.nbh);
+  sp.ch = choose_chunk(sp.nqb, sp.nbh, seq, causal ? 1 : 0);
+  sp.n_items = (int)(count_items(sp.nqb, seq, causal ? 1 : 0, sp.ch) * sp.nbh);
   return sp;
 }
 
