@@ -408,8 +408,10 @@ attn_fwd_kernel(QkvOut q, int causal, uint16_t* __restrict__ O, float* __restric
 // blockIdx.x / 8, and 8 workgroups of 256 threads cover its 128 queries x
 // 16 dim groups.  The weights exp2(m_c - max m) need every chunk's m first;
 // the O loads of all chunks are then issued before the first multiply-add.
-constexpr int MAXC = 16;  // chunks merged per pass (more are merged in passes)
-
+// MAXC chunks are merged per pass (more in several passes); the host picks
+// the smallest of 4, 8, 16 that covers the largest chunk count, so a pass
+// issues no more loads than it needs.
+template <int MAXC>
 __global__ void __launch_bounds__(256)
 attn_combine_kernel(QkvOut q, int causal, uint16_t* __restrict__ O,
                     const float* __restrict__ part, AttnSplit sp) {
@@ -606,8 +608,17 @@ hipError_t attention_fwd(const QkvOut& q, int batch, bool causal, uint16_t* O, f
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (sp.n_items == sp.nqb * sp.nbh) return hipSuccess;  // no query block was split
-  hipLaunchKernelGGL(attn_combine_kernel, dim3(sp.nqb * sp.nbh * 8), dim3(256), 0, s, q,
-                     causal ? 1 : 0, O, part, sp);
+  const int max_nc = div_up(ntile_of(sp.nqb - 1, q.seq, causal ? 1 : 0), sp.ch);
+  const dim3 grid(sp.nqb * sp.nbh * 8);
+  if (max_nc <= 4)
+    hipLaunchKernelGGL(attn_combine_kernel<4>, grid, dim3(256), 0, s, q, causal ? 1 : 0, O, part,
+                       sp);
+  else if (max_nc <= 8)
+    hipLaunchKernelGGL(attn_combine_kernel<8>, grid, dim3(256), 0, s, q, causal ? 1 : 0, O, part,
+                       sp);
+  else
+    hipLaunchKernelGGL(attn_combine_kernel<16>, grid, dim3(256), 0, s, q, causal ? 1 : 0, O,
+                       part, sp);
   return hipGetLastError();
 }
 

@@ -47,6 +47,8 @@ def test_attention_shard_t8_full(gpu):
     (1, 513, 1024, 8, 4, 3, True, syn.F32),
     (2, 200, 256, 4, 2, 1, True, syn.F32),     # V^T stored down the columns, sequence
     (3, 40, 384, 6, 3, 2, False, syn.F32),     # boundaries inside one 256-row tile
+    (1, 1100, 256, 2, 2, 1, True, syn.F32),    # one-tile chunks: 18 merged in two passes
+    (1, 1200, 256, 2, 2, 0, False, syn.F32),   # 19 chunks, full attention
 ])
 def test_attention_small(gpu, batch, seq, hidden, nh, t, i, causal, out):
     a = syn.make_attn_inputs(40 + seq, batch, seq, hidden, nh, 128)
