@@ -39,6 +39,9 @@ SIGNATURES = {
                                _c_sz, _c_p]),
     "tp_partial_reduce": (_c_i32, [ctypes.POINTER(_c_p), _c_i32, _c_p, _c_p, _c_i64,
                                    _c_i64, _c_i32, _c_i32, _c_i32, _c_p]),
+    "tp_partial_reduce_slice": (_c_i32, [ctypes.POINTER(_c_p), _c_i32, _c_p, _c_p, _c_i64,
+                                         _c_i64, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32,
+                                         _c_p]),
     "tp_ffn_shard_reduce_workspace_bytes": (_c_sz, [_c_i64, _c_i64, _c_i64, _c_i32, _c_i32]),
     "tp_ffn_shard_reduce": (_c_i32, [_c_p, _c_p, _c_p, ctypes.POINTER(_c_p), _c_p, _c_p,
                                      _c_i64, _c_i64, _c_i64, _c_i32, _c_i32, _c_i64, _c_i32,
@@ -262,8 +265,10 @@ def tp_attn_shard(X, Wqkv_i, Wo_i, Y_i, batch: int, seq: int, n_heads: int,
     return Y_i
 
 
-def tp_partial_reduce(partials, residual, out, stream=None):
-    """out = sum(partials) + residual (residual may be None).  Returns out."""
+def tp_partial_reduce(partials, residual, out, stream=None, slice_of=None):
+    """out = sum(partials) + residual (residual may be None).  Returns out.
+    slice_of=(slice, nslices) computes only that row block (see
+    tp_partial_reduce_slice)."""
     lib = load()
     t = len(partials)
     if not 1 <= t <= TP_MAX_PARTIALS:
@@ -288,6 +293,18 @@ def tp_partial_reduce(partials, residual, out, stream=None):
     arr = (ctypes.c_void_p * t)(*[p.data_ptr() for p in partials])
     torch = _torch()
     with torch.cuda.device(out.device):
-        _check(lib.tp_partial_reduce(arr, t, rptr, out.data_ptr(), rows, cols, pdt,
-                                     rdt, _dtype_code(out), _stream(stream)))
+        if slice_of is None:
+            _check(lib.tp_partial_reduce(arr, t, rptr, out.data_ptr(), rows, cols, pdt,
+                                         rdt, _dtype_code(out), _stream(stream)))
+        else:
+            slice_, nslices = slice_of
+            _check(lib.tp_partial_reduce_slice(arr, t, rptr, out.data_ptr(), rows, cols,
+                                               slice_, nslices, pdt, rdt, _dtype_code(out),
+                                               _stream(stream)))
     return out
+
+
+def tp_partial_reduce_slice(partials, residual, out, slice_, nslices, stream=None):
+    """Rows block `slice_` of `nslices` of sum(partials) + residual, written into
+    the same rows of out (the reduce-scatter half of the all-reduce).  Returns out."""
+    return tp_partial_reduce(partials, residual, out, stream, slice_of=(slice_, nslices))

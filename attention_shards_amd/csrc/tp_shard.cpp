@@ -486,37 +486,39 @@ tp_status_t tp_attn_shard(const void* X, const void* Wqkv_i, const void* Wo_i,
 // ---------------------------------------------------------------------------
 // Partial reduce
 // ---------------------------------------------------------------------------
-tp_status_t tp_partial_reduce(const void* const* partials, int32_t t,
-                              const void* residual, void* out, int64_t rows,
-                              int64_t cols, int32_t partial_dtype,
-                              int32_t residual_dtype, int32_t out_dtype,
-                              void* stream) {
+}  // extern "C"
+
+namespace {
+
+tp_status_t reduce_checked(const char* fn, const void* const* partials, int32_t t,
+                          const void* residual, void* out, int64_t rows, int64_t cols,
+                          int32_t partial_dtype, int32_t residual_dtype, int32_t out_dtype,
+                          void* stream) {
   try {
     if (!valid_dtype(partial_dtype) || !valid_dtype(out_dtype) ||
         (residual && !valid_dtype(residual_dtype)))
-      return fail(TP_ERR_DTYPE, "tp_partial_reduce: dtype codes p=%d r=%d o=%d", partial_dtype,
+      return fail(TP_ERR_DTYPE, "%s: dtype codes p=%d r=%d o=%d", fn, partial_dtype,
                   residual_dtype, out_dtype);
     if (t < 1 || t > TP_MAX_PARTIALS)
-      return fail(TP_ERR_SHARD, "tp_partial_reduce: t=%d outside [1, %d]", t, TP_MAX_PARTIALS);
+      return fail(TP_ERR_SHARD, "%s: t=%d outside [1, %d]", fn, t, TP_MAX_PARTIALS);
     if (rows < 0 || cols < 0 || cols % 8 != 0 ||
         (rows > 0 && cols > (int64_t(1) << 60) / rows))
       return fail(TP_ERR_SHAPE,
-                  "tp_partial_reduce: rows=%lld cols=%lld (cols a multiple of 8, "
-                  "rows*cols at most 2^60)",
-                  (long long)rows, (long long)cols);
+                  "%s: rows=%lld cols=%lld (cols a multiple of 8, rows*cols at most 2^60)",
+                  fn, (long long)rows, (long long)cols);
     const int64_t n = rows * cols;
     if (n == 0) return ok();
-    if (!partials || !out) return fail(TP_ERR_NULL, "tp_partial_reduce: NULL pointer");
+    if (!partials || !out) return fail(TP_ERR_NULL, "%s: NULL pointer", fn);
     tp::ReducePtrs ptrs;
     for (int k = 0; k < t; ++k) {
-      if (!partials[k]) return fail(TP_ERR_NULL, "tp_partial_reduce: partials[%d] is NULL", k);
+      if (!partials[k]) return fail(TP_ERR_NULL, "%s: partials[%d] is NULL", fn, k);
       if (!aligned16(partials[k]))
-        return fail(TP_ERR_ALIGNMENT, "tp_partial_reduce: partials[%d] not 16-byte aligned", k);
+        return fail(TP_ERR_ALIGNMENT, "%s: partials[%d] not 16-byte aligned", fn, k);
       ptrs.p[k] = partials[k];
     }
     for (int k = t; k < TP_MAX_PARTIALS; ++k) ptrs.p[k] = nullptr;
     if (!aligned16(out) || (residual && !aligned16(residual)))
-      return fail(TP_ERR_ALIGNMENT, "tp_partial_reduce: pointers must be 16-byte aligned");
+      return fail(TP_ERR_ALIGNMENT, "%s: pointers must be 16-byte aligned", fn);
     // out may be exactly one of the inputs (same address, same element size):
     // every element group is read in full by the thread that writes it.
     const int64_t ob = esize(out_dtype);
@@ -524,20 +526,75 @@ tp_status_t tp_partial_reduce(const void* const* partials, int32_t t,
     for (int k = 0; k < t; ++k) {
       const int64_t pb = esize(partial_dtype);
       if (overlap(ro, range_of(partials[k], n * pb)) && !(partials[k] == out && pb == ob))
-        return fail(TP_ERR_ALIAS, "tp_partial_reduce: out overlaps partials[%d]", k);
+        return fail(TP_ERR_ALIAS, "%s: out overlaps partials[%d]", fn, k);
     }
     if (residual) {
       const int64_t rb = esize(residual_dtype);
       if (overlap(ro, range_of(residual, n * rb)) && !(residual == out && rb == ob))
-        return fail(TP_ERR_ALIAS, "tp_partial_reduce: out overlaps the residual");
+        return fail(TP_ERR_ALIAS, "%s: out overlaps the residual", fn);
     }
     hipStream_t s = static_cast<hipStream_t>(stream);
     (void)hipGetLastError();
     const hipError_t e = tp::partial_reduce(ptrs, t, partial_dtype, residual, residual_dtype,
                                             out, out_dtype, n, s);
-    return hip_status(e, "tp_partial_reduce: launch");
+    return hip_status(e, fn);
   } catch (...) {
-    return fail(TP_ERR_HIP, "tp_partial_reduce: internal exception");
+    return fail(TP_ERR_HIP, "%s: internal exception", fn);
+  }
+}
+
+}  // namespace
+
+extern "C" {
+
+tp_status_t tp_partial_reduce(const void* const* partials, int32_t t,
+                              const void* residual, void* out, int64_t rows,
+                              int64_t cols, int32_t partial_dtype,
+                              int32_t residual_dtype, int32_t out_dtype,
+                              void* stream) {
+  return reduce_checked("tp_partial_reduce", partials, t, residual, out, rows, cols,
+                        partial_dtype, residual_dtype, out_dtype, stream);
+}
+
+tp_status_t tp_partial_reduce_slice(const void* const* partials, int32_t t,
+                                    const void* residual, void* out, int64_t rows,
+                                    int64_t cols, int32_t slice, int32_t nslices,
+                                    int32_t partial_dtype, int32_t residual_dtype,
+                                    int32_t out_dtype, void* stream) {
+  const char* fn = "tp_partial_reduce_slice";
+  try {
+    if (!valid_dtype(partial_dtype) || !valid_dtype(out_dtype) ||
+        (residual && !valid_dtype(residual_dtype)))
+      return fail(TP_ERR_DTYPE, "%s: dtype codes p=%d r=%d o=%d", fn, partial_dtype,
+                  residual_dtype, out_dtype);
+    if (t < 1 || t > TP_MAX_PARTIALS)
+      return fail(TP_ERR_SHARD, "%s: t=%d outside [1, %d]", fn, t, TP_MAX_PARTIALS);
+    if (nslices < 1 || slice < 0 || slice >= nslices)
+      return fail(TP_ERR_SHARD, "%s: slice %d of %d", fn, slice, nslices);
+    if (rows < 0 || cols < 0 || (rows > 0 && cols > (int64_t(1) << 60) / rows))
+      return fail(TP_ERR_SHAPE, "%s: rows=%lld cols=%lld (rows*cols at most 2^60)", fn,
+                  (long long)rows, (long long)cols);
+    // balanced row blocks: the first rows % nslices slices hold one more row
+    const int64_t base = rows / nslices, extra = rows % nslices;
+    const int64_t r0 = slice * base + (slice < extra ? slice : extra);
+    const int64_t r1 = r0 + base + (slice < extra ? 1 : 0);
+    if (r1 == r0 || cols == 0) return reduce_checked(fn, partials, t, residual, out, 0, cols,
+                                                     partial_dtype, residual_dtype, out_dtype,
+                                                     stream);
+    if (!partials || !out) return fail(TP_ERR_NULL, "%s: NULL pointer", fn);
+    const int64_t off = r0 * cols;
+    const void* p[TP_MAX_PARTIALS];
+    for (int k = 0; k < t; ++k) {
+      if (!partials[k]) return fail(TP_ERR_NULL, "%s: partials[%d] is NULL", fn, k);
+      p[k] = static_cast<const char*>(partials[k]) + off * esize(partial_dtype);
+    }
+    const void* r =
+        residual ? static_cast<const char*>(residual) + off * esize(residual_dtype) : nullptr;
+    void* o = static_cast<char*>(out) + off * esize(out_dtype);
+    return reduce_checked(fn, p, t, r, o, r1 - r0, cols, partial_dtype, residual_dtype,
+                          out_dtype, stream);
+  } catch (...) {
+    return fail(TP_ERR_HIP, "%s: internal exception", fn);
   }
 }
 

@@ -15,8 +15,10 @@ value = algorithmic FFN FLOPs of the shard (4*M*h*f/t) / wall time per step.
 Every timed row starts after about 0.1 s of the same work, untimed, so that
 the GPU has left its idle clock state, then W warmup steps.
 
-The same run also times that step with the sum fused into the second GEMM's
-epilogue (tp_ffn_shard_reduce; rows.ffn_shard_reduce_fused), the attention
+The same run also times the reduce-scatter block shard i would own
+(tp_partial_reduce_slice; rows.partial_reduce_slice), that step with the sum
+fused into the second GEMM's epilogue (tp_ffn_shard_reduce;
+rows.ffn_shard_reduce_fused), the attention
 shard (t=8, 8 of 64 heads of 128,
 hidden 8192, 2048 tokens, causal) and reports it under "rows", and, on rank 0
 at N=1, times the fp64 CPU oracle on a bounded sample of the FFN workload
@@ -118,6 +120,26 @@ def time_events(fn, steps, warmup):
         b.record()
     torch.cuda.synchronize()
     return sum(a.elapsed_time(b) for a, b in ev) / steps
+
+
+def time_batched(fn, steps, warmup):
+    """Milliseconds per call of `steps` back-to-back calls between one pair of
+    events, for calls shorter than the host's time to issue them: a GPU spin
+    of about 10 ms holds the stream while the host enqueues all of them, so
+    the events time the kernels, not the Python binding."""
+    import torch
+    settle(fn)
+    for _ in range(warmup):
+        fn()
+    steps = min(steps, 200)
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda._sleep(20_000_000)
+    a.record()
+    for _ in range(steps):
+        fn()
+    b.record()
+    torch.cuda.synchronize()
+    return a.elapsed_time(b) / steps
 
 
 def cpu_baseline(d, budget_s=12.0):
@@ -448,6 +470,23 @@ def main():
     red_bytes = (t * 2 + 2 + 4) * M * h
     red_gbs = red_bytes / (red_ms * 1e-3) / 1e9
 
+    # The reduce-scatter half of the all-reduce on this GPU: one row block
+    # (rows [j*M/t, (j+1)*M/t) of every partial) per call, j rotating over the
+    # t blocks so that successive calls do not find their inputs in the
+    # Infinity Cache (one block is 46 MB; all t together 369 MB).
+    nxt = [0]
+
+    def one_slice():
+        B.tp_partial_reduce_slice(parts, R, out, nxt[0] % t, t)
+        nxt[0] += 1
+
+    slice_ms = time_batched(one_slice, args.steps, args.warmup)
+    slice_bytes = (t * 2 + 2 + 4) * (M // t) * h
+    slice_row = {"slices": "rotating 0..t-1", "nslices": t, "ms": round(slice_ms, 5),
+                 "bytes": slice_bytes,
+                 "gbs": round(slice_bytes / (slice_ms * 1e-3) / 1e9, 1),
+                 "frac_hbm_peak": round(slice_bytes / (slice_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}
+
     # The same step with the sum fused into GEMM2's epilogue: this shard's
     # partial is added from the accumulators and never stored or re-read.
     fused_row = None
@@ -524,6 +563,7 @@ def main():
                                "gbs": round(red_gbs, 1),
                                "frac_hbm_peak": round(red_gbs / PEAK_HBM_GBS, 4),
                                "bound": "hbm"},
+            "partial_reduce_slice": slice_row,
             "ffn_shard_reduce_fused": fused_row,
             "attn_shard": attn_row,
         },

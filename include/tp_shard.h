@@ -43,7 +43,7 @@
 extern "C" {
 #endif
 
-#define TP_ABI_VERSION 2
+#define TP_ABI_VERSION 3
 #define TP_MAX_PARTIALS 64
 
 /* Element types of tensors crossing the ABI. */
@@ -173,6 +173,31 @@ tp_status_t tp_partial_reduce(const void* const* partials, int32_t t,
                               int64_t cols, int32_t partial_dtype,
                               int32_t residual_dtype, int32_t out_dtype,
                               void* stream);
+
+/* ------------------------------------------------------------------------
+ * One row block of that sum: the reduce-scatter half of the all-reduce
+ * (each of nslices GPUs reduces its own row block of all t partials, read
+ * in place, before an all-gather of the blocks; page "Tensor Parallelism >
+ * Combining Column and Row Parallelism", FFN step 3).
+ * ------------------------------------------------------------------------
+ * The pointers and rows, cols describe the full [rows, cols] tensors, as for
+ * tp_partial_reduce.  Only rows [r0, r1) of out are written, with
+ *     r0 = slice * (rows / nslices) + min(slice, rows % nslices),
+ *     r1 = r0 + rows / nslices + (slice < rows % nslices ? 1 : 0),
+ * so the nslices blocks tile [0, rows) and differ by at most one row; each
+ * element is computed exactly as tp_partial_reduce computes it (the same
+ * order and rounding), so the blocks of all slices together equal the full
+ * reduce bit for bit.  The partial pointers may belong to other devices
+ * (peer-mapped memory); nothing else is read or written.
+ *   slice, nslices  0 <= slice < nslices (TP_ERR_SHARD otherwise)
+ * Other arguments, aliasing and shape rules: those of tp_partial_reduce,
+ * applied to the block.  An empty block (rows < nslices) enqueues nothing.
+ */
+tp_status_t tp_partial_reduce_slice(const void* const* partials, int32_t t,
+                                    const void* residual, void* out, int64_t rows,
+                                    int64_t cols, int32_t slice, int32_t nslices,
+                                    int32_t partial_dtype, int32_t residual_dtype,
+                                    int32_t out_dtype, void* stream);
 
 /* ------------------------------------------------------------------------
  * FFN shard fused with the sum of the partials and the residual: the

@@ -206,6 +206,33 @@ def test_reduce_rejects(lib):
     assert B.STATUS[reduce_call(lib, [X], R=WS, out=WS + 16)[0]] == "TP_ERR_ALIAS"
 
 
+def reduce_slice_call(lib, parts, slice_, nslices, R=None, out=Y, rows=32, cols=64,
+                      pdt=B.TP_BF16, rdt=B.TP_BF16, odt=B.TP_F32):
+    arr = (ctypes.c_void_p * max(1, len(parts)))(*parts) if parts else None
+    st = lib.tp_partial_reduce_slice(arr, len(parts), R, out, rows, cols, slice_, nslices,
+                                     pdt, rdt, odt, None)
+    return st, lib.tp_last_error_message().decode()
+
+
+def test_reduce_slice_rejects(lib):
+    P = [X, W1, W2]
+    for s, n in [(-1, 4), (4, 4), (0, 0)]:
+        st, msg = reduce_slice_call(lib, P, s, n)
+        assert B.STATUS[st] == "TP_ERR_SHARD" and "tp_partial_reduce_slice" in msg
+    assert B.STATUS[reduce_slice_call(lib, P, 0, 2, cols=60)[0]] == "TP_ERR_SHAPE"
+    assert B.STATUS[reduce_slice_call(lib, P, 0, 2, pdt=5)[0]] == "TP_ERR_DTYPE"
+    assert B.STATUS[reduce_slice_call(lib, [X, 0], 1, 2)[0]] == "TP_ERR_NULL"
+    # slice 1 of 2 covers rows 16..31: partials[1]'s block is W1 + [2048, 4096)
+    # bytes; a bf16 out at W1 + 1024 has its block at W1 + [3072, 5120)
+    assert B.STATUS[reduce_slice_call(lib, [X, W1], 1, 2, out=W1 + 1024,
+                                      odt=B.TP_BF16)[0]] == "TP_ERR_ALIAS"
+
+
+def test_reduce_slice_empty_block_is_a_no_op(lib):
+    # rows = 2 split 4 ways: slices 2 and 3 are empty and touch nothing
+    assert reduce_slice_call(lib, [None], 3, 4, out=None, rows=2)[0] == 0
+
+
 def test_reduce_empty_is_a_no_op(lib):
     assert reduce_call(lib, [X, W1], rows=0)[0] == 0
     assert reduce_call(lib, [X, W1], cols=0, out=None)[0] == 0

@@ -90,3 +90,37 @@ def test_reduce_layer_shape_sampled(gpu):
     check_bound(got, [syn.to_f64(p[sel], syn.BF16) for p in parts_h],
                 syn.to_f64(R_h[sel], syn.BF16), syn.F32)
     log("reduce t=4 [8192,12288] sampled rows within the fp32 bound")
+
+
+@pytest.mark.parametrize("t,pdt,odt,rows,cols,nslices", [
+    (8, syn.BF16, syn.F32, 1000, 264, 8),    # 1000 = 8 x 125
+    (8, syn.BF16, syn.BF16, 1003, 64, 3),    # ragged: blocks of 335, 334, 334 rows
+    (4, syn.F32, syn.F32, 5, 16, 8),         # more slices than rows: 3 empty blocks
+])
+def test_reduce_slices_tile_the_full_reduce(gpu, t, pdt, odt, rows, cols, nslices):
+    """The row blocks of all slices, each written by its own call into an
+    output pre-filled with NaN, equal the full reduce bit for bit; a single
+    call writes only its own rows; one block against the oracle's bound."""
+    parts_h = [syn.normal_tensor(950 + t, k, (rows, cols), 0.5, pdt) for k in range(t)]
+    R_h = syn.normal_tensor(950 + t, 99, (rows, cols), 1.0, syn.BF16)
+    parts = [to_dev(p, pdt) for p in parts_h]
+    R = to_dev(R_h, syn.BF16)
+    full = empty((rows, cols), odt)
+    gpu.tp_partial_reduce(parts, R, full)
+    sliced = empty((rows, cols), odt).fill_(float("nan"))
+    for s in range(nslices):
+        gpu.tp_partial_reduce_slice(parts, R, sliced, s, nslices)
+    one = empty((rows, cols), odt).fill_(float("nan"))
+    s1 = nslices // 2
+    gpu.tp_partial_reduce_slice(parts, R, one, s1, nslices)
+    torch.cuda.synchronize()
+    assert torch.equal(sliced, full)
+    base, extra = divmod(rows, nslices)
+    r0 = s1 * base + min(s1, extra)
+    r1 = r0 + base + (1 if s1 < extra else 0)
+    assert torch.equal(one[r0:r1], full[r0:r1])
+    assert torch.isnan(one[:r0]).all() and torch.isnan(one[r1:]).all()
+    log(f"reduce slices t={t} rows={rows} nslices={nslices}: block {s1} = rows [{r0}, {r1})")
+    if r1 > r0:
+        check_bound(from_dev(one[r0:r1]), [syn.to_f64(p[r0:r1], pdt) for p in parts_h],
+                    syn.to_f64(R_h[r0:r1], syn.BF16), odt)
