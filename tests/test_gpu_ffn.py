@@ -204,3 +204,14 @@ def test_deterministic(gpu):
     a = run_shard(gpu, d, 1, 2, syn.BF16)
     b = run_shard(gpu, d, 1, 2, syn.BF16)
     assert np.array_equal(a, b)
+
+
+def test_bf16_output_is_rne_of_fp32_output(gpu):
+    """The bf16-output epilogue rounds to nearest even: the same shard (the
+    same accumulation; only the store differs) with fp32 output, rounded on
+    the host, equals the bf16 output bit for bit."""
+    d = syn.make_ffn_inputs(17, 600, 512, 4 * 512, syn.BF16)
+    y32 = run_shard(gpu, d, 1, 4, syn.F32).astype(np.float32)
+    y16 = run_shard(gpu, d, 1, 4, syn.BF16)
+    host = syn.bf16_bits_to_f32(syn.f32_to_bf16_bits(y32))
+    assert np.array_equal(y16.astype(np.float32).view(np.uint32), host.view(np.uint32))

@@ -124,3 +124,18 @@ def test_reduce_slices_tile_the_full_reduce(gpu, t, pdt, odt, rows, cols, nslice
     if r1 > r0:
         check_bound(from_dev(one[r0:r1]), [syn.to_f64(p[r0:r1], pdt) for p in parts_h],
                     syn.to_f64(R_h[r0:r1], syn.BF16), odt)
+
+
+def test_reduce_bf16_output_is_rne(gpu):
+    """One fp32 partial, no residual, bf16 output is a pure conversion: it
+    equals round-to-nearest-even on the host bit for bit (ties included)."""
+    rng = np.random.default_rng(12)
+    p = rng.standard_normal((64, 256)).astype(np.float32)
+    # exact ties: bit patterns ending in 0x8000 round to even
+    p.view(np.uint32)[0, :64] = (p.view(np.uint32)[0, :64] & 0xFFFF0000) | 0x8000
+    out = empty((64, 256), syn.BF16)
+    gpu.tp_partial_reduce([to_dev(p, syn.F32)], None, out)
+    torch.cuda.synchronize()
+    got = from_dev(out).astype(np.float32)
+    host = syn.bf16_bits_to_f32(syn.f32_to_bf16_bits(p))
+    assert np.array_equal(got.view(np.uint32), host.view(np.uint32))
