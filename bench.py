@@ -20,7 +20,8 @@ The same run also times the reduce-scatter block shard i would own
 fused into the second GEMM's epilogue (tp_ffn_shard_reduce;
 rows.ffn_shard_reduce_fused), the attention
 shard (t=8, 8 of 64 heads of 128,
-hidden 8192, 2048 tokens, causal) and reports it under "rows", and, on rank 0
+hidden 8192, 2048 tokens, causal) and a whole layer of four shards on this
+GPU (hidden 12288, 96 heads, 8192 tokens) and reports them under "rows", and, on rank 0
 at N=1, times the fp64 CPU oracle on a bounded sample of the FFN workload
 ("cpu_baseline").  Prints ONE JSON line.
 """
@@ -242,6 +243,41 @@ def fused_vs_unfused_large(steps, warmup):
     return {"workload": "t4_i0_h12288_f49152_tokens8192", "unfused_ms": round(un_ms, 4),
             "fused_ms": round(fu_ms, 4), "unfused_tflops": round(fl / (un_ms * 1e-3) / 1e12, 1),
             "fused_tflops": round(fl / (fu_ms * 1e-3) / 1e12, 1)}
+
+
+def layer_row(steps, warmup):
+    """Timing only (device-generated inputs): a whole layer on one GPU
+    (attention_shards_amd.layer.layer_forward) at the four-way layer shape:
+    hidden 12288, 96 heads of 128, ffn 49152, 4 sequences of 2048 tokens,
+    causal, t = 4; all four attention shards, their sum + residual, all four
+    FFN shards (bf16 partials), their sum + residual."""
+    import torch
+    from attention_shards_amd.layer import layer_forward
+    batch, seq, h, nh, d, f, t = 4, 2048, 12288, 96, 128, 49152, 4
+    M, nl, fs = batch * seq, nh // t, f // t
+    g = torch.Generator(device="cuda").manual_seed(6)
+
+    def w(*shape):
+        return (torch.randn(*shape, device="cuda", generator=g) * 0.02).to(torch.bfloat16)
+
+    X = torch.randn(M, h, device="cuda", generator=g).to(torch.bfloat16)
+    Wqkv = [w(h, 3 * nl * d) for _ in range(t)]
+    Wo = [w(nl * d, h) for _ in range(t)]
+    W1 = w(h, f)
+    W1v = [W1[:, j * fs:(j + 1) * fs] for j in range(t)]
+    W2v = [w(fs, h) for _ in range(t)]
+
+    def step():
+        layer_forward(X, Wqkv, Wo, W1v, W2v, batch, seq, nh, d, True,
+                      ffn_partial_dtype=torch.bfloat16)
+
+    ms = time_events(step, steps, warmup)
+    fl = t * attn_flops(batch, seq, h, nh, d, t) + t * ffn_flops(M, h, f, t)
+    del X, Wqkv, Wo, W1, W1v, W2v
+    torch.cuda.empty_cache()
+    return {"workload": "layer_t4_h12288_96x128heads_f49152_b4x2048_causal",
+            "ms": round(ms, 3), "flop": fl, "tflops": round(fl / (ms * 1e-3) / 1e12, 1),
+            "frac_peak": round(fl / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)}
 
 
 def copy_calibration():
@@ -534,6 +570,8 @@ def main():
                     "ms": round(attn_ms, 5), "flop": afl, "tflops": round(attn_tf, 2),
                     "frac_peak": round(attn_tf / PEAK_BF16_TFLOPS, 4)}
 
+    layer = None if args.no_attention else layer_row(max(3, args.steps // 40), 2)
+
     traffic = load_traffic()
     res = {
         "metric": METRIC,
@@ -566,6 +604,7 @@ def main():
             "partial_reduce_slice": slice_row,
             "ffn_shard_reduce_fused": fused_row,
             "attn_shard": attn_row,
+            "layer": layer,
         },
     }
     if not args.no_cpu_baseline:
