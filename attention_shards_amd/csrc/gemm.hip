@@ -16,9 +16,10 @@
 //     N-contiguous) keeps its [k][n] layout with a 64-byte-block swizzle and
 //     is read with ds_read_b64_tr_b16, which transposes it into the MFMA
 //     operand.
-//   * gemm_bf16_kernel: 4 waves, 256x128 or 128x128 tiles, K = 64 per stage
-//     through a 3-slot ring, DMAs and fragment reads interleaved between the
-//     MFMAs of each wave.
+//   * gemm_bf16_kernel: 4 waves, 256x128, 128x192 or 128x128 tiles, K = 64
+//     per stage through a 3-slot ring, DMAs and fragment reads interleaved
+//     between the MFMAs of each wave.  (128x192 fills all 256 CUs where
+//     256x128 would leave a quarter idle, e.g. 2048 x 3072 outputs.)
 //   * gemm_bf16_pp_kernel: 8 waves, 256x256 tiles, K = 32 per stage through
 //     a 5-slot ring; two groups of waves alternate between a memory phase and
 //     an MFMA-only phase, one phase apart, so each SIMD's matrix pipe is fed
@@ -365,8 +366,15 @@ __device__ __forceinline__ void epilogue_lds(uint8_t* smem, f32x16 (&acc)[FM][FN
   static_assert(WCOLS == FN * 32, "wave tile width");
   constexpr int PITCH = WCOLS + 4;
   float* stage_f = reinterpret_cast<float*>(smem) + wave * 32 * PITCH;
-  constexpr int RUNS = WCOLS / 8;           // 8-column runs per row
-  constexpr int ROWS_PER_PASS = 64 / RUNS;  // rows covered by one wave pass
+  constexpr int RUNS = WCOLS / 8;                 // 8-column runs per row
+  constexpr int PASSES = 32 * RUNS / 64;          // wave passes per slab
+  static_assert(PASSES * 64 == 32 * RUNS, "runs tile the slab");
+  // An epilogue that reads memory takes RB passes per call so that the
+  // loads of several rows are in flight together.
+  // The passes of one call share a column only when 64 is a multiple of
+  // the runs per row.
+  constexpr int RB0 = RowBatch<Epi>::value;
+  constexpr int RB = (64 % RUNS == 0 && PASSES % RB0 == 0) ? RB0 : 1;
 #pragma unroll
   for (int mi = 0; mi < FM; ++mi) {
 #pragma unroll
@@ -377,46 +385,59 @@ __device__ __forceinline__ void epilogue_lds(uint8_t* smem, f32x16 (&acc)[FM][FN
         stage_f[i * PITCH + ni * 32 + (lane & 31)] = acc[mi][ni][e];
       }
     asm volatile("" ::: "memory");  // keep the LDS writes before the reads
-    if constexpr (ColumnRuns<Epi>::value && WCOLS == 64) {
-      if (epi.column_tile(c0)) {  // lane = column, 8 rows per store
+    bool rows_left = true;
+    if constexpr (ColumnRuns<Epi>::value) {
+      // 32-column groups the epilogue writes down the columns: lane l takes
+      // column l%32 and, per store, 8 rows, the two lane halves adjacent
+      // 8-row runs (16 rows per store, 32 per group).
+      rows_left = false;
 #pragma unroll
-        for (int g8 = 0; g8 < 4; ++g8) {
-          const int row = r0 + mi * 32 + 8 * g8;
+      for (int ni = 0; ni < FN; ++ni) {
+        const int cg = c0 + ni * 32;
+        if (!epi.column_tile(cg)) {
+          rows_left = true;
+          continue;
+        }
+#pragma unroll
+        for (int g = 0; g < 2; ++g) {
+          const int rr = 16 * g + 8 * (lane >> 5);
+          const int row = r0 + mi * 32 + rr;
           float v[8];
 #pragma unroll
-          for (int i = 0; i < 8; ++i) v[i] = stage_f[(8 * g8 + i) * PITCH + lane];
-          if (row < M && c0 + lane < N) epi.store_col8(row, c0 + lane, M, v);
+          for (int i = 0; i < 8; ++i) v[i] = stage_f[(rr + i) * PITCH + ni * 32 + (lane & 31)];
+          if (row < M && cg + (lane & 31) < N) epi.store_col8(row, cg + (lane & 31), M, v);
         }
-        asm volatile("" ::: "memory");
-        continue;
       }
     }
-    // An epilogue that reads memory takes RB rows per call so that the
-    // loads of several rows are in flight together.
-    constexpr int RB = RowBatch<Epi>::value;
-    static_assert((32 / ROWS_PER_PASS) % RB == 0, "row batches tile the slab");
+    if (rows_left) {
 #pragma unroll 1
-    for (int it = 0; it < 32 / ROWS_PER_PASS; it += RB) {
-      const int c8 = (lane % RUNS) * 8;
-      const int col0 = c0 + c8;
-      float v[RB][8];
-      int row[RB];
+      for (int it = 0; it < PASSES; it += RB) {
+        float v[RB][8];
+        int row[RB], col0[RB];
 #pragma unroll
-      for (int b = 0; b < RB; ++b) {
-        const int rr = (it + b) * ROWS_PER_PASS + lane / RUNS;
-        row[b] = r0 + mi * 32 + rr;
-        const f32x4 va = *reinterpret_cast<const f32x4*>(stage_f + rr * PITCH + c8);
-        const f32x4 vb = *reinterpret_cast<const f32x4*>(stage_f + rr * PITCH + c8 + 4);
+        for (int b = 0; b < RB; ++b) {
+          const int q = (it + b) * 64 + lane;
+          const int rr = q / RUNS, c8 = (q % RUNS) * 8;
+          row[b] = r0 + mi * 32 + rr;
+          col0[b] = c0 + c8;
+          const f32x4 va = *reinterpret_cast<const f32x4*>(stage_f + rr * PITCH + c8);
+          const f32x4 vb = *reinterpret_cast<const f32x4*>(stage_f + rr * PITCH + c8 + 4);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          v[b][e] = va[e];
-          v[b][4 + e] = vb[e];
+          for (int e = 0; e < 4; ++e) {
+            v[b][e] = va[e];
+            v[b][4 + e] = vb[e];
+          }
         }
-      }
-      if constexpr (RB == 1) {
-        if (row[0] < M && col0 < N) epi.store8(row[0], col0, v[0]);
-      } else {
-        if (col0 < N) epi.template store8_rows<RB>(row, M, col0, v);
+        if constexpr (RB == 1) {
+          // (groups written down the columns above are skipped; c0 is a
+          // multiple of 32, so a run's group starts at col0 & ~31)
+          bool done = false;
+          if constexpr (ColumnRuns<Epi>::value) done = epi.column_tile(col0[0] & ~31);
+          if (row[0] < M && col0[0] < N && !done) epi.store8(row[0], col0[0], v[0]);
+        } else {
+          static_assert(!ColumnRuns<Epi>::value, "row batches write every run");
+          if (col0[0] < N) epi.template store8_rows<RB>(row, M, col0[0], v);
+        }
       }
     }
     asm volatile("" ::: "memory");  // and this slab's reads before the next writes
@@ -453,7 +474,7 @@ gemm_bf16_kernel(const uint16_t* __restrict__ A, int64_t lda,
   constexpr int B_DMA = B_STAGE / 1024 / NW;
   constexpr int NDMA = A_DMA + B_DMA;
   static_assert(A_DMA * 1024 * NW == A_STAGE && B_DMA * 1024 * NW == B_STAGE, "DMA split");
-  static_assert(B_CH >= 16, "B swizzle needs >= 16 chunks per row");
+  static_assert(B_CH % 16 == 0 || B_CH == 24, "B swizzle: 256-byte multiple or 384-byte rows");
   static_assert(FM >= 1 && FN >= 1, "wave tile");
 
   // LDS ring: slot s holds A at s*A_STAGE and B at NSL*A_STAGE + s*B_STAGE.
@@ -478,10 +499,12 @@ gemm_bf16_kernel(const uint16_t* __restrict__ A, int64_t lda,
 
   // ---- DMA lane offsets.  A: RPD rows of A_ROWB bytes per DMA; lane l
   // fills row l/CPR, physical chunk l%CPR with logical chunk
-  // (l%CPR) ^ ((row >> ASH) & (CPR-1)).  B: 1024/B_ROWB rows per DMA; lane l
-  // fills slot l % B_CH with logical chunk slot ^ ((row&3)<<2).  The
-  // swizzles keep the fragment reads on distinct banks (any 16 consecutive
-  // rows at one logical chunk cover 16 distinct 16-byte bank groups); they
+  // (l%CPR) ^ ((row >> ASH) & (CPR-1)).  B: the DMAs fill the packed rows
+  // in order, 16-byte chunk q = 64*(DMA index) + l landing in row q/B_CH,
+  // slot q%B_CH, which holds logical chunk slot ^ bswz(row).  The swizzles
+  // keep the fragment reads on distinct banks (any 16 consecutive A rows at
+  // one logical chunk cover 16 distinct 16-byte bank groups; the four B rows
+  // of one transposed read land in four distinct 64-byte bank ranges); they
   // are applied to the global addresses.
   int a_off[A_DMA], a_col[A_DMA];
 #pragma unroll
@@ -491,11 +514,16 @@ gemm_bf16_kernel(const uint16_t* __restrict__ A, int64_t lda,
     a_off[j] = row * (int)lda * 2 + c * 16;
     a_col[j] = c * 8;
   }
+  // B rows a multiple of 256 bytes apart start on the same bank, so the
+  // rows of a read are spread by 64-byte blocks; 384-byte rows alternate
+  // between two bank halves, so only row bit 1 selects the block.
+  auto bswz = [](int row) { return B_CH == 24 ? ((row >> 1) & 1) << 2 : (row & 3) << 2; };
   int b_off[B_DMA];
 #pragma unroll
   for (int j = 0; j < B_DMA; ++j) {
-    const int row = (j * NW + wave) * (1024 / B_ROWB) + lane / B_CH;
-    const int c = (lane % B_CH) ^ ((row & 3) << 2);
+    const int q = (j * NW + wave) * 64 + lane;
+    const int row = q / B_CH;
+    const int c = (q % B_CH) ^ bswz(row);
     b_off[j] = row * (int)ldb * 2 + c * 16;
   }
 
@@ -537,7 +565,8 @@ gemm_bf16_kernel(const uint16_t* __restrict__ A, int64_t lda,
     const int krow = 8 * (G >> 1) + (r >> 2);
 #pragma unroll
     for (int ni = 0; ni < FN; ++ni) {
-      const int c = (((wc0 + ni * 32) >> 3) + 2 * (G & 1) + ((r & 3) >> 1)) ^ ((r >> 2) << 2);
+      // (the rows read, krow + 4 and + 16*ks, all have krow's low two bits)
+      const int c = (((wc0 + ni * 32) >> 3) + 2 * (G & 1) + ((r & 3) >> 1)) ^ bswz(krow);
       b_rd[ni] = krow * B_ROWB + c * 16 + (r & 1) * 8;
     }
   }
@@ -836,11 +865,11 @@ struct TileChoice {
 };
 
 TileChoice choose_bf16_tile(int M, int N) {
-  const TileChoice cand[3] = {{256, 256}, {256, 128}, {128, 128}};
-  const double eff[3] = {1.0, 0.95, 0.70};
+  const TileChoice cand[4] = {{256, 256}, {256, 128}, {128, 192}, {128, 128}};
+  const double eff[4] = {1.0, 0.95, 0.80, 0.70};
   int best = 0;
   double best_cost = 1e300;
-  for (int c = 0; c < 3; ++c) {
+  for (int c = 0; c < 4; ++c) {
     const int64_t tiles = (int64_t)((M + cand[c].bm - 1) / cand[c].bm) *
                           ((N + cand[c].bn - 1) / cand[c].bn);
     const double waves = (double)((tiles + 255) / 256);
@@ -880,6 +909,8 @@ hipError_t dispatch_bf16(const uint16_t* A, int64_t lda, const uint16_t* B,
   }
   if (t.bm == 256 && t.bn == 128)
     return launch_bf16<256, 128, 2, 2, 4, 3>(A, lda, B, ldb, M, N, K, kwrap, epi, s);
+  if (t.bm == 128 && t.bn == 192)
+    return launch_bf16<128, 192, 2, 2, 4, 3>(A, lda, B, ldb, M, N, K, kwrap, epi, s);
   return launch_bf16<128, 128, 2, 2, 4, 3>(A, lda, B, ldb, M, N, K, kwrap, epi, s);
 }
 

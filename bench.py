@@ -318,16 +318,26 @@ def summarize_profiles(stats_csv, fetch_csv, write_csv, cmd_stats, cmd_pmc):
     """Write profiles/*.md and the traffic record bench.py reads."""
     import csv
     gemm_src = src_hash("gemm.hip")
-    rows = list(csv.DictReader(open(stats_csv)))
+    # Per-dispatch durations from the kernel trace next to the stats file,
+    # grouped by kernel and grid size (the bench launches the reduce kernel
+    # both over whole tensors and over row blocks).
+    trace_csv = stats_csv.replace("kernel_stats", "kernel_trace")
+    groups = {}
+    for r in csv.DictReader(open(trace_csv)):
+        key = (_short(r["Kernel_Name"]), int(r["Grid_Size_X"]) // int(r["Workgroup_Size_X"]))
+        groups.setdefault(key, []).append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+    total_us = sum(sum(v) for v in groups.values())
     lines = ["# Kernel durations: FFN shard t=8 i=3, hidden 4096, ffn 16384, 4096 tokens",
              "", "Command (from the repository root, on one MI355X):", "",
              "```", cmd_stats, "```", "",
-             "| kernel | calls | avg us | min us | max us | share |",
-             "|---|---:|---:|---:|---:|---:|"]
-    for r in rows:
-        lines.append(f"| `{_short(r['Name'])}` | {r['Calls']} | {float(r['AverageNs'])/1e3:.1f} | "
-                     f"{float(r['MinNs'])/1e3:.1f} | {float(r['MaxNs'])/1e3:.1f} | "
-                     f"{float(r['Percentage']):.1f}% |")
+             "Per-dispatch durations from the kernel trace of the same run, grouped by kernel",
+             "and number of workgroups (the partial reduce runs over the whole 4096 x 4096",
+             "output and, in the block row, over one eighth of its rows).", "",
+             "| kernel | workgroups | calls | avg us | min us | max us | share |",
+             "|---|---:|---:|---:|---:|---:|---:|"]
+    for (name, wgs), v in sorted(groups.items(), key=lambda kv: -sum(kv[1])):
+        lines.append(f"| `{name}` | {wgs} | {len(v)} | {sum(v)/len(v):.1f} | {min(v):.1f} | "
+                     f"{max(v):.1f} | {100*sum(v)/total_us:.1f}% |")
     with open(os.path.join(ROOT, "profiles", "kernel_stats_ffn_shard_h4096_t8.md"), "w") as f:
         f.write("\n".join(lines) + "\n")
 
@@ -370,6 +380,63 @@ def summarize_profiles(stats_csv, fetch_csv, write_csv, cmd_stats, cmd_pmc):
                    "fetch_factor": f_fac, "write_factor": w_fac,
                    "algorithmic_bytes": alg}, f, indent=1)
     print(f"wrote profiles (traffic {total/1e6:.1f} MB per call, algorithmic {alg/1e6:.1f} MB)")
+
+
+def summarize_attn_profile(trace_csv, cmd):
+    """Write profiles/kernel_stats_attn_shard_h8192_t8.md from a rocprofv3
+    kernel trace of a bench run: the kernels of each tp_attn_shard call at the
+    attention configuration (QKV projection, attention, merge, output
+    projection), told apart from the layer row's larger calls by grid size."""
+    import csv
+    import statistics
+    rows = sorted(csv.DictReader(open(trace_csv)), key=lambda r: int(r["Start_Timestamp"]))
+    wg = lambda r: int(r["Grid_Size_X"]) // int(r["Workgroup_Size_X"])
+    dur = lambda r: (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3
+    a = ATTN
+    S, h, nl, d = a["batch"] * a["seq"], a["hidden"], a["n_heads"] // a["t"], a["head_dim"]
+    qkv_tiles = None
+    per, grids, calls = {}, {}, []
+    for k in range(len(rows) - 3):
+        seq = rows[k:k + 4]
+        if "EpiQkv" not in seq[0]["Kernel_Name"] or "attn_fwd" not in seq[1]["Kernel_Name"]:
+            continue
+        if "attn_combine" not in seq[2]["Kernel_Name"] or "EpiStore" not in seq[3]["Kernel_Name"]:
+            continue
+        if qkv_tiles is None:
+            qkv_tiles = wg(seq[0])
+        if wg(seq[0]) != qkv_tiles:
+            continue
+        for x in seq:
+            per.setdefault(_short(x["Kernel_Name"]), []).append(dur(x))
+            grids[_short(x["Kernel_Name"])] = wg(x)
+        calls.append((int(seq[3]["End_Timestamp"]) - int(seq[0]["Start_Timestamp"])) / 1e3)
+    role = {"EpiQkv": f"QKV projection [{S} x {h}] x [{h} x {3 * nl * d}], Q/K hi/lo rows, "
+                      "V^T hi/lo as 16-byte runs along the sequence",
+            "attn_fwd": "causal attention (128 queries x up to a chunk of 64-key tiles each)",
+            "attn_combine": "merge of the split query blocks",
+            "EpiStore": f"output projection [{S} x {2 * nl * d} (O hi, O lo)] x [{nl * d} x {h}], "
+                        "fp32 partial"}
+    flop = 2 * S * h * 3 * nl * d + 4 * d * S * (S + 1) // 2 * nl + 2 * S * nl * d * h
+    med = statistics.median(calls)
+    lines = [f"# Kernel durations: attention shard t={a['t']} i={a['i']}, hidden {h}, "
+             f"{nl} of {a['n_heads']} heads of {d}, {S} tokens, causal", "",
+             "Command (from the repository root, on one MI355X):", "", "```", cmd, "```", "",
+             f"Per-dispatch durations from the kernel trace: the four kernels of each of the "
+             f"{len(calls)} `tp_attn_shard` calls at this configuration (the run also times the "
+             "FFN step and the layer row, whose kernels are left out).", "",
+             "| kernel | role | workgroups | calls | avg us | min us | max us |",
+             "|---|---|---:|---:|---:|---:|---:|"]
+    for n, v in per.items():
+        r = next((t for key, t in role.items() if key in n), "")
+        lines.append(f"| `{n}` | {r} | {grids[n]} | {len(v)} | {statistics.mean(v):.1f} | "
+                     f"{min(v):.1f} | {max(v):.1f} |")
+    lines += ["", f"One attention shard call, first kernel start to last kernel end: {med:.1f} us "
+              f"median ({statistics.mean(calls):.1f} us mean); {flop/1e9:.1f} GFLOP algorithmic "
+              f"work, {flop/med/1e6:.0f} TFLOP/s at the median, {flop/med/1e6/2516.6:.1%} of the "
+              "bf16 MFMA peak."]
+    with open(os.path.join(ROOT, "profiles", "kernel_stats_attn_shard_h8192_t8.md"), "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print(f"wrote attention profile ({len(calls)} calls, median {med:.1f} us)")
 
 
 def summarize_sweep(path, cmd):
@@ -417,6 +484,8 @@ def main():
     ap.add_argument("--sweep", metavar="OUT_JSONL", default=None)
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run a 1 GiB device copy first (counter calibration)")
+    ap.add_argument("--summarize-attn-profile", metavar="KERNEL_TRACE_CSV", default=None,
+                    help="write the attention-shard kernel table from a rocprofv3 trace")
     ap.add_argument("--summarize-sweep", metavar="SWEEP_JSONL", default=None,
                     help="write profiles/sweep_*.md from a --sweep output and exit")
     ap.add_argument("--summarize-profiles", nargs=3,
@@ -425,6 +494,9 @@ def main():
     ap.add_argument("--profile-commands", nargs=2, default=["", ""],
                     metavar=("STATS_CMD", "PMC_CMD"))
     args = ap.parse_args()
+    if args.summarize_attn_profile:
+        summarize_attn_profile(args.summarize_attn_profile, args.profile_commands[0])
+        return
     if args.summarize_sweep:
         summarize_sweep(args.summarize_sweep, args.profile_commands[0])
         return

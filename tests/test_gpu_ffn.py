@@ -74,6 +74,7 @@ def test_bf16_t8_shard3_full(gpu):
     (190, 296, 2 * 160, 2, 1, syn.BF16, True),    # K stages a multiple of the ring
     (70, 8, 2 * 8, 2, 0, syn.F32, False),         # K = 8: one partial stage
     (4000, 4000, 2 * 1000, 2, 1, syn.BF16, True),  # 256x256 W2 tiles, ragged edges and K
+    (2000, 3000, 2936, 1, 0, syn.BF16, False),     # 128x192 tiles (both GEMMs), ragged edges and K
 ])
 def test_bf16_ragged(gpu, M, h, f, t, i, out, view):
     d = syn.make_ffn_inputs(100 + M, M, h, f, syn.BF16)

@@ -89,7 +89,8 @@ def test_fused_fp32_inputs(gpu):
 
 
 @pytest.mark.parametrize("M,h,f,t,i,pdt", [(300, 200, 3 * 424, 3, 2, syn.F32),
-                                            (4096, 4096, 16384, 8, 3, syn.BF16)])
+                                            (4096, 4096, 16384, 8, 3, syn.BF16),
+                                            (2000, 3000, 2 * 2936, 2, 1, syn.BF16)])
 def test_fused_equals_unfused_bitwise(gpu, M, h, f, t, i, pdt):
     """The fused call and the same sums done by the unfused calls (the other
     partials + R first, then + Y_i in fp32) agree bit for bit."""
