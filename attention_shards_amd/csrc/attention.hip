@@ -1,8 +1,9 @@
 // Per-head softmax attention over a GPU's local heads (heads never talk to
 // each other: page "Tensor Parallelism > Combining Column and Row
 // Parallelism", the attention paragraphs).  Flash-style: a workgroup owns
-// 128 queries of one (sequence, head) and streams 64-key tiles of K and V
-// through LDS with an online softmax, so the score matrix never reaches HBM.
+// a block of 128 or 256 queries of one (sequence, head) and streams 64-key
+// tiles of K and V through LDS with an online softmax, so the score matrix
+// never reaches HBM.
 //
 // Work split: a query block's key range is cut into chunks of `ch` tiles,
 // one workgroup per (query block, chunk, head), longest query blocks first.
@@ -11,7 +12,9 @@
 // blocks finish; chunks keep every workgroup's work within `ch` tiles.  A
 // query block with one chunk writes O directly; otherwise each chunk writes
 // its unnormalised O, running max and denominator, and a second kernel
-// merges the chunks (the usual rescale by exp2(m_c - max m)).
+// merges the chunks (the usual rescale by exp2(m_c - max m)).  The host
+// picks the block size (256 when a dispatch estimate says it is faster:
+// long sequences or many heads) and the chunk size per shape.
 //
 // Precision: Q and K arrive as bf16 hi/lo pairs, V as an fp16 hi/lo pair.
 // Scores use three bf16 MFMA passes (Khi.Qhi + Khi.Qlo + Klo.Qhi, ~16
@@ -24,8 +27,8 @@
 // rules out single bf16 roundings of P and O here.
 //
 // Layout: a workgroup has 8 waves (two per SIMD, so one wave's LDS waits
-// overlap the other's MFMAs) of 16 queries each; per wave, with
-// v_mfma_f32_16x16x32_bf16:
+// overlap the other's MFMAs) of one or two groups of 16 queries each; per
+// 16-query group, with v_mfma_f32_16x16x32_bf16:
 //   * scores are computed transposed, S^T = K Q^T: A = K rows (keys),
 //     B = Q (queries), so each lane ends up owning one query (lane % 16)
 //     and four keys per 16-key block.  K rows are fed in the order that
@@ -36,10 +39,12 @@
 //     every accumulator is again lane % 16, so softmax rescales are lane-local
 //     and only the row max needs two cross-lane exchanges.
 #include <functional>
+#include <climits>
 #include <map>
 #include <mutex>
 #include <queue>
 #include <tuple>
+#include <utility>
 #include <vector>
 
 #include "internal.h"
@@ -53,12 +58,12 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int D = 128;    // head dim
-constexpr int NQG = 1;    // 16-query groups per wave
 constexpr int NWAVE = 8;  // waves per workgroup: two per SIMD, so one wave's
                           // LDS waits overlap the other's MFMAs
-constexpr int QW = 16 * NQG;     // queries per wave
-constexpr int QB = NWAVE * QW;   // queries per workgroup (128)
 constexpr int NT = NWAVE * 64;   // threads per workgroup
+// Each wave holds NQG groups of 16 queries (NQG = 1 or 2), so a workgroup
+// covers a query block of 128 or 256 queries; the larger block reuses each
+// K and V^T fragment read from LDS for twice the queries.
 constexpr int KT = 64;    // keys per tile
 constexpr int K_ROW = D * 2;      // 256-byte K rows (16 chunks)
 constexpr int V_ROW = KT * 2;     // 128-byte V^T rows (8 chunks)
@@ -106,15 +111,18 @@ __device__ __forceinline__ void wait_vmcnt() {
   asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
 
-// Key tiles a query block needs.
-__host__ __device__ inline int ntile_of(int qb, int seq, int causal) {
+// Key tiles query block qb (of QB queries) needs.
+__host__ __device__ inline int ntile_of(int qb, int seq, int causal, int QB) {
   const int kend = causal ? (QB * (qb + 1) < seq ? QB * (qb + 1) : seq) : seq;
   return div_up(kend, KT);
 }
 
+template <int NQG>
 __global__ void __launch_bounds__(NT)
 attn_fwd_kernel(QkvOut q, int causal, uint16_t* __restrict__ O, float* __restrict__ part,
                 AttnSplit sp, float scale_log2) {
+  constexpr int QW = 16 * NQG;    // queries per wave
+  constexpr int QB = NWAVE * QW;  // queries per workgroup
   // Two LDS buffers of K hi, K lo, V^T hi, V^T lo tiles: one is read by the
   // products while the next tile is staged into the other.
   __shared__ __attribute__((aligned(16))) uint8_t smem[2 * 4 * TILE];
@@ -124,13 +132,13 @@ attn_fwd_kernel(QkvOut q, int causal, uint16_t* __restrict__ O, float* __restric
   // workgroup -> (query block qb, chunk c, sequence*head bh)
   int rem = blockIdx.x, qb = sp.nqb - 1, nc = 1;
   for (;; --qb) {
-    nc = div_up(ntile_of(qb, S, causal), sp.ch);
+    nc = div_up(ntile_of(qb, S, causal, QB), sp.ch);
     if (rem < nc * sp.nbh || qb == 0) break;
     rem -= nc * sp.nbh;
   }
   const int c = rem / sp.nbh, bh = rem - c * sp.nbh;
   const int b = bh / q.nl, head = bh - b * q.nl;
-  const int ntile = ntile_of(qb, S, causal);
+  const int ntile = ntile_of(qb, S, causal, QB);
   const int kt0 = c * sp.ch;
   const int kt1 = kt0 + sp.ch < ntile ? kt0 + sp.ch : ntile;
 
@@ -408,8 +416,8 @@ attn_fwd_kernel(QkvOut q, int causal, uint16_t* __restrict__ O, float* __restric
 
 // Merge of the chunks of query blocks split in more than one.  A thread
 // owns 8 head dims of one query: (query block, sequence*head) is
-// blockIdx.x / 8, and 8 workgroups of 256 threads cover its 128 queries x
-// 16 dim groups.  The weights exp2(m_c - max m) need every chunk's m first;
+// blockIdx.x / (qb/16), and qb/16 workgroups of 256 threads cover its qb
+// queries x 16 dim groups.  The weights exp2(m_c - max m) need every chunk's m first;
 // the O loads of all chunks are then issued before the first multiply-add.
 // MAXC chunks are merged per pass (more in several passes); the host picks
 // the smallest of 4, 8, 16 that covers the largest chunk count, so a pass
@@ -418,15 +426,16 @@ template <int MAXC>
 __global__ void __launch_bounds__(256)
 attn_combine_kernel(QkvOut q, int causal, uint16_t* __restrict__ O,
                     const float* __restrict__ part, AttnSplit sp) {
-  const int grp = blockIdx.x >> 3;
+  const int QB = sp.qb, wpg = QB / 16;
+  const int grp = blockIdx.x / wpg;
   const int qb = grp / sp.nbh, bh = grp - qb * sp.nbh;
   const int S = q.seq;
-  const int nc = div_up(ntile_of(qb, S, causal), sp.ch);
+  const int nc = div_up(ntile_of(qb, S, causal, QB), sp.ch);
   if (nc == 1) return;
   int base = 0;  // first workgroup of this query block
-  for (int x = sp.nqb - 1; x > qb; --x) base += div_up(ntile_of(x, S, causal), sp.ch) * sp.nbh;
-  const int t = (blockIdx.x & 7) * 256 + threadIdx.x;  // 0..2047
-  const int qi = t >> 4, dg = t & 15;                   // query in block, 8-dim group
+  for (int x = sp.nqb - 1; x > qb; --x) base += div_up(ntile_of(x, S, causal, QB), sp.ch) * sp.nbh;
+  const int t = (blockIdx.x - grp * wpg) * 256 + threadIdx.x;  // 0..16*QB-1
+  const int qi = t >> 4, dg = t & 15;                           // query in block, 8-dim group
   const int myq = qb * QB + qi;
   if (myq >= S) return;
   const float* ml = part + (int64_t)sp.n_items * QB * D;
@@ -489,26 +498,35 @@ vt_pad_zero_kernel(QkvOut q, int rows) {
   }
 }
 
-// Estimated time, in units of one key tile of one workgroup, of the
-// attention kernel with chunks of `ch` tiles: workgroups are dispatched in
-// grid order (longest query blocks first) onto NCU compute units, one at a
-// time each (the LDS holds one), and cost ITEM_COST (the start-up of a
-// workgroup: Q load, first tile round trip, partial write) plus their tiles;
-// splitting a query block adds MERGE_COST per split workgroup and the merge
-// kernel's MERGE_LAUNCH.  Fitted to measured kernel times at 1024-8192
-// tokens and 8-24 local heads (about 10% RMS error).
+// Estimated time, in units of one 64-key tile of a 128-query workgroup, of
+// the attention kernel with query blocks of QB queries and chunks of `ch`
+// tiles: workgroups are dispatched in grid order (longest query blocks
+// first) onto NCU compute units, one at a time each (the LDS holds one), and
+// cost a start-up (Q load, first tile round trip, partial write) plus their
+// tiles; splitting a query block adds MERGE_COST per split workgroup and the
+// merge kernel's MERGE_LAUNCH.  Per-variant costs: 128-query blocks start up
+// in 4 tile units; 256-query blocks in 5, and a 256-query tile costs 1.6 (it
+// reads the same K and V^T fragments from LDS for twice the queries).
+// Fitted to measured kernel times at 200-8192 tokens and 2-24 local heads
+// (about 10% RMS error; the sign of the difference between the two variants
+// right at every measured shape).
 constexpr int NCU = 256;
-constexpr double ITEM_COST = 4.0;
 constexpr double MERGE_COST = 0.004;
 constexpr double MERGE_LAUNCH = 2.0;
+struct VariantCost {
+  int qb;
+  double item, tile;
+};
+constexpr VariantCost VAR128 = {128, 4.0, 1.0};
+constexpr VariantCost VAR256 = {256, 5.0, 1.6};
 
-double split_cost(int nqb, int nbh, int seq, int causal, int ch) {
+double split_cost(const VariantCost& v, int nqb, int nbh, int seq, int causal, int ch) {
   std::priority_queue<double, std::vector<double>, std::greater<double>> cu;
   for (int k = 0; k < NCU; ++k) cu.push(0.0);
   double end = 0.0;
   int64_t split = 0;
   for (int qb = nqb - 1; qb >= 0; --qb) {
-    const int nt = ntile_of(qb, seq, causal);
+    const int nt = ntile_of(qb, seq, causal, v.qb);
     const int nc = div_up(nt, ch);
     if (nc > 1) split += (int64_t)nc * nbh;
     for (int c = 0; c < nc; ++c) {
@@ -516,7 +534,7 @@ double split_cost(int nqb, int nbh, int seq, int causal, int ch) {
       for (int bh = 0; bh < nbh; ++bh) {
         const double t0 = cu.top();
         cu.pop();
-        const double t1 = t0 + ITEM_COST + tiles;
+        const double t1 = t0 + v.item + v.tile * tiles;
         cu.push(t1);
         if (t1 > end) end = t1;
       }
@@ -525,72 +543,91 @@ double split_cost(int nqb, int nbh, int seq, int causal, int ch) {
   return end + MERGE_COST * (double)split + (split ? MERGE_LAUNCH : 0.0);
 }
 
-int64_t count_items(int nqb, int seq, int causal, int ch) {
+int64_t count_items(int qbs, int nqb, int seq, int causal, int ch) {
   int64_t items = 0;
-  for (int qb = 0; qb < nqb; ++qb) items += div_up(ntile_of(qb, seq, causal), ch);
+  for (int qb = 0; qb < nqb; ++qb) items += div_up(ntile_of(qb, seq, causal, qbs), ch);
   return items;
 }
 
-// Chunk size.  The default aims at about 1024 workgroups with chunks of at
-// least 4 tiles.  Small problems pay for that in workgroup start-ups: when
-// the estimate above finds a chunk of at most 16 tiles (grid within
-// MAX_ITEMS) at least 10% cheaper, that one is used instead (8 heads, 2048
-// causal tokens: 10 tiles, 272 workgroups, 54 us vs 68 us).  Larger chunks
-// are not searched: there the estimate is least reliable and measured times
-// vary by up to 40% between neighbouring sizes.  Memoised per shape.
-int choose_chunk(int nqb, int nbh, int seq, int causal) {
-  static std::mutex m;
-  static std::map<std::tuple<int, int, int, int>, int> memo;
-  const auto key = std::make_tuple(nqb, nbh, seq, causal);
-  {
-    std::lock_guard<std::mutex> lock(m);
-    const auto it = memo.find(key);
-    if (it != memo.end()) return it->second;
-  }
+// Chunk size for one variant, and its estimated time.  The default aims at
+// about 1024 workgroups with chunks of at least 4 tiles.  Small problems pay
+// for that in workgroup start-ups: when the estimate above finds a chunk of
+// at most 16 tiles (grid within MAX_ITEMS) at least 10% cheaper, that one is
+// used instead (8 heads, 2048 causal tokens, 128-query blocks: 10 tiles, 272
+// workgroups, 54 us vs 68 us).  Larger chunks are not searched: there the
+// estimate is least reliable and measured times vary by up to 40% between
+// neighbouring sizes.
+std::pair<int, double> choose_chunk(const VariantCost& v, int nqb, int nbh, int seq, int causal) {
   int64_t tiles = 0;
-  for (int qb = 0; qb < nqb; ++qb) tiles += ntile_of(qb, seq, causal);
+  for (int qb = 0; qb < nqb; ++qb) tiles += ntile_of(qb, seq, causal, v.qb);
   tiles *= nbh;
   const int64_t dflt = (tiles + 1023) / 1024;
   int best = (int)(dflt < 4 ? 4 : dflt);
-  const int max_nt = ntile_of(nqb - 1, seq, causal);  // the longest key range
-  if (count_items(nqb, seq, causal, 16 < max_nt ? 16 : max_nt) * nbh <= MAX_ITEMS) {
-    const double base = split_cost(nqb, nbh, seq, causal, best);
+  const double base = split_cost(v, nqb, nbh, seq, causal, best);
+  double est = base;
+  const int max_nt = ntile_of(nqb - 1, seq, causal, v.qb);  // the longest key range
+  if (count_items(v.qb, nqb, seq, causal, 16 < max_nt ? 16 : max_nt) * nbh <= MAX_ITEMS) {
     double best_cost = base;
     int pick = best;
     for (int ch = 1; ch <= 16 && ch <= max_nt; ++ch) {
-      if (count_items(nqb, seq, causal, ch) * nbh > MAX_ITEMS) continue;
-      const double cost = split_cost(nqb, nbh, seq, causal, ch);
+      if (count_items(v.qb, nqb, seq, causal, ch) * nbh > MAX_ITEMS) continue;
+      const double cost = split_cost(v, nqb, nbh, seq, causal, ch);
       if (cost < best_cost * 0.999) {
         best_cost = cost;
         pick = ch;
       }
     }
-    if (best_cost <= 0.9 * base) best = pick;
+    if (best_cost <= 0.9 * base) {
+      best = pick;
+      est = best_cost;
+    }
   }
+  return {best, est};
+}
+
+// Query block size and chunk size: 256-query blocks when their estimate is
+// at least 3% below the 128-query one (long sequences and many heads; short
+// ones have too few 256-query blocks to fill the GPU).  Memoised per shape.
+AttnSplit choose_split(int batch, int seq, int nl, int causal) {
+  static std::mutex m;
+  static std::map<std::tuple<int, int, int, int>, AttnSplit> memo;
+  const auto key = std::make_tuple(batch, seq, nl, causal);
+  {
+    std::lock_guard<std::mutex> lock(m);
+    const auto it = memo.find(key);
+    if (it != memo.end()) return it->second;
+  }
+  AttnSplit sp;
+  sp.nbh = batch * nl;
+  const int nqb128 = div_up(seq, 128), nqb256 = div_up(seq, 256);
+  const auto c128 = choose_chunk(VAR128, nqb128, sp.nbh, seq, causal);
+  const auto c256 = choose_chunk(VAR256, nqb256, sp.nbh, seq, causal);
+  const bool big = c256.second <= 0.97 * c128.second &&
+                   count_items(256, nqb256, seq, causal, c256.first) * sp.nbh <= INT32_MAX;
+  sp.qb = big ? 256 : 128;
+  sp.nqb = big ? nqb256 : nqb128;
+  sp.ch = big ? c256.first : c128.first;
+  sp.n_items = (int)(count_items(sp.qb, sp.nqb, seq, causal, sp.ch) * sp.nbh);
   std::lock_guard<std::mutex> lock(m);
   if (memo.size() > 1024) memo.clear();
-  memo[key] = best;
-  return best;
+  memo[key] = sp;
+  return sp;
 }
 
 }  // namespace
 
 AttnSplit attn_split(int batch, int seq, int nl, bool causal) {
-  AttnSplit sp;
-  sp.nbh = batch * nl;
-  sp.nqb = div_up(seq, QB);
-  sp.ch = choose_chunk(sp.nqb, sp.nbh, seq, causal ? 1 : 0);
-  sp.n_items = (int)(count_items(sp.nqb, seq, causal ? 1 : 0, sp.ch) * sp.nbh);
-  return sp;
+  return choose_split(batch, seq, nl, causal ? 1 : 0);
 }
 
 int64_t attn_partial_bytes(int batch, int seq, int nl) {
-  int64_t items = 0;
+  int64_t bytes = 0;
   for (int c = 0; c < 2; ++c) {
     const AttnSplit sp = attn_split(batch, seq, nl, c != 0);
-    if (sp.n_items > items) items = sp.n_items;
+    const int64_t b = (int64_t)sp.n_items * sp.qb * (D + 2) * 4;
+    if (b > bytes) bytes = b;
   }
-  return items * QB * (D + 2) * 4;
+  return bytes;
 }
 
 hipError_t attention_fwd(const QkvOut& q, int batch, bool causal, uint16_t* O, float* part,
@@ -606,13 +643,17 @@ hipError_t attention_fwd(const QkvOut& q, int batch, bool causal, uint16_t* O, f
     const hipError_t e0 = hipGetLastError();
     if (e0 != hipSuccess) return e0;
   }
-  hipLaunchKernelGGL(attn_fwd_kernel, dim3(sp.n_items), dim3(NT), 0, s, q, causal ? 1 : 0, O,
-                     part, sp, scale_log2);
+  if (sp.qb == 256)
+    hipLaunchKernelGGL(attn_fwd_kernel<2>, dim3(sp.n_items), dim3(NT), 0, s, q, causal ? 1 : 0,
+                       O, part, sp, scale_log2);
+  else
+    hipLaunchKernelGGL(attn_fwd_kernel<1>, dim3(sp.n_items), dim3(NT), 0, s, q, causal ? 1 : 0,
+                       O, part, sp, scale_log2);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (sp.n_items == sp.nqb * sp.nbh) return hipSuccess;  // no query block was split
-  const int max_nc = div_up(ntile_of(sp.nqb - 1, q.seq, causal ? 1 : 0), sp.ch);
-  const dim3 grid(sp.nqb * sp.nbh * 8);
+  const int max_nc = div_up(ntile_of(sp.nqb - 1, q.seq, causal ? 1 : 0, sp.qb), sp.ch);
+  const dim3 grid(sp.nqb * sp.nbh * (sp.qb / 16));
   if (max_nc <= 4)
     hipLaunchKernelGGL(attn_combine_kernel<4>, grid, dim3(256), 0, s, q, causal ? 1 : 0, O, part,
                        sp);

@@ -61,6 +61,7 @@ hipError_t gemm_f32(const float* A, int64_t lda, const float* B, int64_t ldb,
 // chunk, sequence*head).  The same function sizes the workspace and
 // launches the kernel.
 struct AttnSplit {
+  int32_t qb;       // queries per block (128 or 256)
   int32_t nqb;      // query blocks per sequence
   int32_t ch;       // key tiles per chunk
   int32_t n_items;  // workgroups of the attention kernel

@@ -65,12 +65,12 @@ def test_workspace_queries(lib):
     assert lib.tp_ffn_shard_workspace_bytes(10, 8, 20, 3, B.TP_BF16) == 0    # t does not divide f
     assert lib.tp_ffn_shard_workspace_bytes(10, 8, 16, 0, B.TP_BF16) == 0
     # attention: 6 x [heads, seq_pad, 128] + O hi/lo [tokens, 2*nl*128], 16-bit,
-    # then fp32 partial results (128 x (128 + 2) floats) for every workgroup of
-    # the larger split: at seq 2048, 8 heads, the causal one cuts the key
-    # ranges (2, 4, ..., 32 tiles) into chunks of 10 tiles: 34 chunks x 8
-    # heads = 272 workgroups (the full one: 16 query blocks x 2 chunks of 16
-    # tiles x 8 heads = 256)
-    split = 272 * 128 * 130 * 4
+    # then fp32 partial results (qb x (128 + 2) floats) for every workgroup of
+    # the larger split: at seq 2048, 8 heads, both use 256-query blocks; the
+    # causal one cuts the key ranges (4, 8, ..., 32 tiles) into chunks of 5
+    # tiles: 32 chunks x 8 heads = 256 workgroups (the full one: 8 query
+    # blocks x 4 chunks of 8 tiles x 8 heads = 256)
+    split = 256 * 256 * 130 * 4
     want = 6 * 8 * 2048 * 128 * 2 + 2048 * 2 * 1024 * 2 + split
     assert lib.tp_attn_shard_workspace_bytes(1, 2048, 64, 128, 8) == want
     ragged = lib.tp_attn_shard_workspace_bytes(2, 100, 4, 128, 2)

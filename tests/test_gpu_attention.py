@@ -50,7 +50,9 @@ def test_attention_shard_t8_full(gpu):
     (1, 1100, 256, 2, 2, 1, True, syn.F32),    # one-tile chunks: 18 merged in two passes
     (1, 1200, 256, 2, 2, 0, False, syn.F32),   # 19 chunks, full attention
     (2, 1000, 512, 16, 2, 1, True, syn.F32),   # QKV in 128x192 tiles: a wave's 96 columns
-    (1, 2001, 512, 16, 2, 0, False, syn.F32),  # cross the K|V boundary; ragged rows
+    (1, 2001, 512, 16, 2, 0, False, syn.F32),  # cross the K|V boundary; ragged rows; 256-query blocks
+    (2, 1500, 512, 16, 2, 1, True, syn.F32),   # 256-query blocks, ragged, up to 4 chunks merged
+    (1, 4000, 512, 8, 2, 0, True, syn.F32),    # 256-query blocks, up to 7 chunks merged
 ])
 def test_attention_small(gpu, batch, seq, hidden, nh, t, i, causal, out):
     a = syn.make_attn_inputs(40 + seq, batch, seq, hidden, nh, 128)
