@@ -412,7 +412,7 @@ def summarize_attn_profile(trace_csv, cmd):
         calls.append((int(seq[3]["End_Timestamp"]) - int(seq[0]["Start_Timestamp"])) / 1e3)
     role = {"EpiQkv": f"QKV projection [{S} x {h}] x [{h} x {3 * nl * d}], Q/K hi/lo rows, "
                       "V^T hi/lo as 16-byte runs along the sequence",
-            "attn_fwd": "causal attention (128 queries x up to a chunk of 64-key tiles each)",
+            "attn_fwd": "causal attention (query blocks of 128 or 256 x up to a chunk of 64-key tiles each)",
             "attn_combine": "merge of the split query blocks",
             "EpiStore": f"output projection [{S} x {2 * nl * d} (O hi, O lo)] x [{nl * d} x {h}], "
                         "fp32 partial"}
