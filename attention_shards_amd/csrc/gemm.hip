@@ -107,21 +107,40 @@ struct EpiStore {
   }
 };
 
+// GeLU(acc), row-major (row stride ldc) or, with kb_shift > 0 and bf16
+// output, K-blocked for the next product: column c of row r at
+// ((c >> kb_shift) * rows + r) * kb + c % kb, kb = 1 << kb_shift, so that
+// each kb-column block of all rows is one contiguous [rows][kb] slab.
 struct EpiGelu {
   void* C;
   int64_t ldc;
   int out;
+  int rows;
+  int kb_shift;
+  __device__ int64_t kblock_at(int row, int col0) const {
+    const int kb = 1 << kb_shift;
+    return ((int64_t)(col0 >> kb_shift) * rows + row) * kb + (col0 & (kb - 1));
+  }
   __device__ void store4(int row, int col0, const float* v) const {
     float g[4];
 #pragma unroll
     for (int r = 0; r < 4; ++r) g[r] = gelu_erf(v[r]);
-    store_run4(C, ldc, out, row, col0, g);
+    if (kb_shift)
+      *reinterpret_cast<uint2*>(static_cast<uint16_t*>(C) + kblock_at(row, col0)) =
+          uint2{pack_bf16(g[0], g[1]), pack_bf16(g[2], g[3])};
+    else
+      store_run4(C, ldc, out, row, col0, g);
   }
   __device__ void store8(int row, int col0, const float* v) const {
     float g[8];
 #pragma unroll
     for (int r = 0; r < 8; ++r) g[r] = gelu_erf(v[r]);
-    store_run8(C, ldc, out, row, col0, g);
+    if (kb_shift)
+      *reinterpret_cast<u32x4*>(static_cast<uint16_t*>(C) + kblock_at(row, col0)) =
+          u32x4{pack_bf16(g[0], g[1]), pack_bf16(g[2], g[3]), pack_bf16(g[4], g[5]),
+                pack_bf16(g[6], g[7])};
+    else
+      store_run8(C, ldc, out, row, col0, g);
   }
 };
 
@@ -448,14 +467,16 @@ __device__ __forceinline__ void epilogue_lds(uint8_t* smem, f32x16 (&acc)[FM][FN
 // ring of NSL stages.  KS = 2 gives 64-byte A rows per stage; KS = 4 gives
 // 128-byte A rows (a whole cache line per row per DMA), at the price of
 // fewer, larger ring slots.
-template <int BM, int BN, int WM, int WN, int KS, int NSL, class Epi>
+template <int BM, int BN, int WM, int WN, int KS, int NSL, class Epi, bool AKB>
 __global__ void __launch_bounds__(WM * WN * 64)
 gemm_bf16_kernel(const uint16_t* __restrict__ A, int64_t lda,
                  const uint16_t* __restrict__ B, int64_t ldb, int M, int N,
                  int K, int kwrap, int tiles_m, int tiles_n, Epi epi) {
   // Stage kt reads B rows from (k0 < kwrap ? k0 : k0 - kwrap); with kwrap < K
   // (K == 2 kwrap, kwrap a multiple of BK) the same B multiplies both halves
-  // of an A laid out as [A_hi | A_lo].
+  // of an A laid out as [A_hi | A_lo].  With AKB, A is K-blocked by the
+  // stage depth BK: [ceil(K/BK)][lda][BK], lda the padded row count, so a
+  // stage's A tile is one contiguous run of rows.
   static_assert(KS == 2 || KS == 4, "k-steps per stage");
   static_assert(NSL >= 3 && NSL <= 6, "ring slots");
   constexpr int BK = 16 * KS;
@@ -511,7 +532,7 @@ gemm_bf16_kernel(const uint16_t* __restrict__ A, int64_t lda,
   for (int j = 0; j < A_DMA; ++j) {
     const int row = RPD * (j * NW + wave) + lane / CPR;
     const int c = (lane % CPR) ^ ((row >> ASH) & (CPR - 1));
-    a_off[j] = row * (int)lda * 2 + c * 16;
+    a_off[j] = AKB ? row * A_ROWB + c * 16 : row * (int)lda * 2 + c * 16;
     a_col[j] = c * 8;
   }
   // B rows a multiple of 256 bytes apart start on the same bank, so the
@@ -533,7 +554,8 @@ gemm_bf16_kernel(const uint16_t* __restrict__ A, int64_t lda,
     const int k0 = kt * BK;
     if (j < A_DMA) {
       const __amdgpu_buffer_rsrc_t ra =
-          make_rsrc(A + (int64_t)m0 * lda + k0, (int64_t)rows_valid * lda * 2 - (int64_t)k0 * 2);
+          AKB ? make_rsrc(A + ((int64_t)kt * lda + m0) * BK, (int64_t)rows_valid * A_ROWB)
+              : make_rsrc(A + (int64_t)m0 * lda + k0, (int64_t)rows_valid * lda * 2 - (int64_t)k0 * 2);
       const int off = (k0 + a_col[j] < K) ? a_off[j] : OOB;
       dma16(ra, off, lds_a_addr + slot * A_STAGE + (j * NW + wave) * 1024);
     } else {
@@ -698,7 +720,7 @@ gemm_bf16_kernel(const uint16_t* __restrict__ A, int64_t lda,
 // before the barrier that ends its mem phase, and is refilled (stage s+5)
 // from phase 2s+2 on; stage s+1 is read from phase 2s+2 on and every wave has
 // waited for its share of it by the end of phase 2s+1.
-template <class Epi>
+template <class Epi, bool AKB>
 __global__ void __launch_bounds__(512)
 gemm_bf16_pp_kernel(const uint16_t* __restrict__ A, int64_t lda,
                     const uint16_t* __restrict__ B, int64_t ldb, int M, int N,
@@ -741,7 +763,7 @@ gemm_bf16_pp_kernel(const uint16_t* __restrict__ A, int64_t lda,
   for (int j = 0; j < A_DMA; ++j) {
     const int row = RPD * (j * NW + wave) + lane / CPR;
     const int c = (lane % CPR) ^ ((row >> ASH) & (CPR - 1));
-    a_off[j] = row * (int)lda * 2 + c * 16;
+    a_off[j] = AKB ? row * A_ROWB + c * 16 : row * (int)lda * 2 + c * 16;
     a_col[j] = c * 8;
   }
   int b_off[B_DMA];
@@ -755,7 +777,8 @@ gemm_bf16_pp_kernel(const uint16_t* __restrict__ A, int64_t lda,
   auto dma_stage = [&](int kt, int slot) __attribute__((always_inline)) {
     const int k0 = kt * BK;
     const __amdgpu_buffer_rsrc_t ra =
-        make_rsrc(A + (int64_t)m0 * lda + k0, (int64_t)rows_valid * lda * 2 - (int64_t)k0 * 2);
+        AKB ? make_rsrc(A + ((int64_t)kt * lda + m0) * BK, (int64_t)rows_valid * A_ROWB)
+            : make_rsrc(A + (int64_t)m0 * lda + k0, (int64_t)rows_valid * lda * 2 - (int64_t)k0 * 2);
 #pragma unroll
     for (int j = 0; j < A_DMA; ++j) {
       const int off = (k0 + a_col[j] < K) ? a_off[j] : OOB;
@@ -882,36 +905,43 @@ TileChoice choose_bf16_tile(int M, int N) {
   return cand[best];
 }
 
-template <int BM, int BN, int WM, int WN, int KS, int NSL, class Epi>
+template <int BM, int BN, int WM, int WN, int KS, int NSL, bool AKB, class Epi>
 hipError_t launch_bf16(const uint16_t* A, int64_t lda, const uint16_t* B,
                        int64_t ldb, int M, int N, int K, int kwrap,
                        const Epi& epi, hipStream_t s) {
   const int tm = (M + BM - 1) / BM, tn = (N + BN - 1) / BN;
-  hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, WM, WN, KS, NSL, Epi>), dim3(tm * tn),
+  hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, WM, WN, KS, NSL, Epi, AKB>), dim3(tm * tn),
                      dim3(WM * WN * 64), 0, s, A, lda, B, ldb, M, N, K, kwrap,
                      tm, tn, epi);
   return hipGetLastError();
 }
 
-template <class Epi>
+// K block (stage depth) of the kernel the dispatch picks for an [M, N]
+// output: 32 for the 256x256 ping-pong kernel, 64 for the others.
+int a_block(const TileChoice& t) { return t.bm == 256 && t.bn == 256 ? 32 : 64; }
+
+// AKB: A is K-blocked by the chosen kernel's stage depth (see
+// gemm_bf16_kernel), lda its row count; the caller has checked the block.
+template <bool AKB, class Epi>
 hipError_t dispatch_bf16(const uint16_t* A, int64_t lda, const uint16_t* B,
                          int64_t ldb, int M, int N, int K, int kwrap,
                          const Epi& epi, hipStream_t s) {
   if (M == 0 || N == 0) return hipSuccess;
   // tiles are addressed with 32-bit byte offsets: 256 rows of A, 64 of B
-  if (lda >= ((int64_t)1 << 22) || ldb >= ((int64_t)1 << 24)) return hipErrorInvalidValue;
+  // (K-blocked A tiles are at most 32 KiB)
+  if ((!AKB && lda >= ((int64_t)1 << 22)) || ldb >= ((int64_t)1 << 24)) return hipErrorInvalidValue;
   const TileChoice t = choose_bf16_tile(M, N);
   if (t.bm == 256 && t.bn == 256) {
     const int tm = (M + 255) / 256, tn = (N + 255) / 256;
-    hipLaunchKernelGGL((gemm_bf16_pp_kernel<Epi>), dim3(tm * tn), dim3(512), 0, s, A, lda,
+    hipLaunchKernelGGL((gemm_bf16_pp_kernel<Epi, AKB>), dim3(tm * tn), dim3(512), 0, s, A, lda,
                        B, ldb, M, N, K, kwrap, tm, tn, epi);
     return hipGetLastError();
   }
   if (t.bm == 256 && t.bn == 128)
-    return launch_bf16<256, 128, 2, 2, 4, 3>(A, lda, B, ldb, M, N, K, kwrap, epi, s);
+    return launch_bf16<256, 128, 2, 2, 4, 3, AKB>(A, lda, B, ldb, M, N, K, kwrap, epi, s);
   if (t.bm == 128 && t.bn == 192)
-    return launch_bf16<128, 192, 2, 2, 4, 3>(A, lda, B, ldb, M, N, K, kwrap, epi, s);
-  return launch_bf16<128, 128, 2, 2, 4, 3>(A, lda, B, ldb, M, N, K, kwrap, epi, s);
+    return launch_bf16<128, 192, 2, 2, 4, 3, AKB>(A, lda, B, ldb, M, N, K, kwrap, epi, s);
+  return launch_bf16<128, 128, 2, 2, 4, 3, AKB>(A, lda, B, ldb, M, N, K, kwrap, epi, s);
 }
 
 // ---------------------------------------------------------------------------
@@ -1012,7 +1042,16 @@ hipError_t launch_f32(const float* A, int64_t lda, const float* B, int64_t ldb,
 hipError_t gemm_bf16_store(const uint16_t* A, int64_t lda, const uint16_t* B,
                            int64_t ldb, void* C, int64_t ldc, OutType out,
                            int M, int N, int K, hipStream_t s) {
-  return dispatch_bf16(A, lda, B, ldb, M, N, K, K, EpiStore{C, ldc, (int)out}, s);
+  return dispatch_bf16<false>(A, lda, B, ldb, M, N, K, K, EpiStore{C, ldc, (int)out}, s);
+}
+
+int gemm_bf16_a_block(int M, int N) { return a_block(choose_bf16_tile(M, N)); }
+
+hipError_t gemm_bf16_store_kb(const uint16_t* A, int kb, const uint16_t* B, int64_t ldb,
+                              void* C, int64_t ldc, OutType out, int M, int N, int K,
+                              hipStream_t s) {
+  if (M > 0 && N > 0 && kb != a_block(choose_bf16_tile(M, N))) return hipErrorInvalidValue;
+  return dispatch_bf16<true>(A, M, B, ldb, M, N, K, K, EpiStore{C, ldc, (int)out}, s);
 }
 
 hipError_t gemm_bf16_store_split_a(const uint16_t* A2, int64_t lda,
@@ -1020,25 +1059,34 @@ hipError_t gemm_bf16_store_split_a(const uint16_t* A2, int64_t lda,
                                    int64_t ldc, OutType out, int M, int N, int K,
                                    hipStream_t s) {
   if (K % 64) return hipErrorInvalidValue;  // each half a whole number of stages
-  return dispatch_bf16(A2, lda, B, ldb, M, N, 2 * K, K, EpiStore{C, ldc, (int)out}, s);
+  return dispatch_bf16<false>(A2, lda, B, ldb, M, N, 2 * K, K, EpiStore{C, ldc, (int)out}, s);
 }
 
 hipError_t gemm_bf16_gelu(const uint16_t* A, int64_t lda, const uint16_t* B,
                           int64_t ldb, uint16_t* C, int64_t ldc, int M, int N,
-                          int K, hipStream_t s) {
-  return dispatch_bf16(A, lda, B, ldb, M, N, K, K, EpiGelu{C, ldc, (int)OUT_BF16}, s);
+                          int K, int kb, hipStream_t s) {
+  if (kb != 0 && kb != 32 && kb != 64) return hipErrorInvalidValue;
+  const int sh = kb == 32 ? 5 : (kb == 64 ? 6 : 0);
+  return dispatch_bf16<false>(A, lda, B, ldb, M, N, K, K, EpiGelu{C, ldc, (int)OUT_BF16, M, sh}, s);
 }
 
 hipError_t gemm_bf16_qkv(const uint16_t* A, int64_t lda, const uint16_t* B,
                          int64_t ldb, const QkvOut& q, int M, int N, int K,
                          hipStream_t s) {
-  return dispatch_bf16(A, lda, B, ldb, M, N, K, K, EpiQkv{q}, s);
+  return dispatch_bf16<false>(A, lda, B, ldb, M, N, K, K, EpiQkv{q}, s);
 }
 
 hipError_t gemm_bf16_add(const uint16_t* A, int64_t lda, const uint16_t* B, int64_t ldb,
                          const float* S, void* C, int64_t ldc, OutType out, int M, int N,
                          int K, hipStream_t s) {
-  return dispatch_bf16(A, lda, B, ldb, M, N, K, K, EpiAdd{S, C, ldc, (int)out}, s);
+  return dispatch_bf16<false>(A, lda, B, ldb, M, N, K, K, EpiAdd{S, C, ldc, (int)out}, s);
+}
+
+hipError_t gemm_bf16_add_kb(const uint16_t* A, int kb, const uint16_t* B, int64_t ldb,
+                            const float* S, void* C, int64_t ldc, OutType out, int M, int N,
+                            int K, hipStream_t s) {
+  if (M > 0 && N > 0 && kb != a_block(choose_bf16_tile(M, N))) return hipErrorInvalidValue;
+  return dispatch_bf16<true>(A, M, B, ldb, M, N, K, K, EpiAdd{S, C, ldc, (int)out}, s);
 }
 
 hipError_t gemm_f32_add(const float* A, int64_t lda, const float* B, int64_t ldb,

@@ -36,10 +36,19 @@ struct QkvOut {
 hipError_t gemm_bf16_store(const uint16_t* A, int64_t lda, const uint16_t* B,
                            int64_t ldb, void* C, int64_t ldc, OutType out,
                            int M, int N, int K, hipStream_t s);
-// Same product, C = bf16(GeLU_erf(acc)).
+// Same product, C = bf16(GeLU_erf(acc)): row-major (row stride ldc) for
+// kb == 0, else K-blocked for a following product, [ceil(N/kb)][M][kb]
+// (kb = 32 or 64; columns past N in the last block are not written).
 hipError_t gemm_bf16_gelu(const uint16_t* A, int64_t lda, const uint16_t* B,
                           int64_t ldb, uint16_t* C, int64_t ldc, int M, int N,
-                          int K, hipStream_t s);
+                          int K, int kb, hipStream_t s);
+// K block the kernel chosen for an [M, N] output reads a K-blocked A in.
+int gemm_bf16_a_block(int M, int N);
+// gemm_bf16_store / gemm_bf16_add with A K-blocked, [ceil(K/kb)][M][kb];
+// kb must be gemm_bf16_a_block(M, N) (else hipErrorInvalidValue).
+hipError_t gemm_bf16_store_kb(const uint16_t* A, int kb, const uint16_t* B, int64_t ldb,
+                              void* C, int64_t ldc, OutType out, int M, int N, int K,
+                              hipStream_t s);
 // C = [A_hi | A_lo] * B: A2 is [M, 2K] (row stride lda), the same B[K,N]
 // multiplies both halves (two MFMA passes over K); K a multiple of 64.
 hipError_t gemm_bf16_store_split_a(const uint16_t* A2, int64_t lda,
@@ -93,6 +102,9 @@ hipError_t partial_reduce(const ReducePtrs& ptrs, int t, int pdt,
 hipError_t gemm_bf16_add(const uint16_t* A, int64_t lda, const uint16_t* B, int64_t ldb,
                          const float* S, void* C, int64_t ldc, OutType out, int M, int N,
                          int K, hipStream_t s);
+hipError_t gemm_bf16_add_kb(const uint16_t* A, int kb, const uint16_t* B, int64_t ldb,
+                            const float* S, void* C, int64_t ldc, OutType out, int M, int N,
+                            int K, hipStream_t s);
 hipError_t gemm_f32_add(const float* A, int64_t lda, const float* B, int64_t ldb,
                         const float* S, void* C, int64_t ldc, OutType out, int M, int N,
                         int K, hipStream_t s);

@@ -67,6 +67,10 @@ constexpr int64_t kInt32Max = 2147483647;
 constexpr int64_t kMaxLdA = int64_t(1) << 22;
 constexpr int64_t kMaxLdB = int64_t(1) << 24;
 constexpr int64_t kMaxSeqPad = int64_t(1) << 23;
+// bf16 FFN workspace: GeLU(Z_i) is kept K-blocked, [ceil(F/kb)][tokens][kb]
+// with kb = 32 or 64 (the second product's stage depth), so its column count
+// is rounded up to a multiple of 64.
+constexpr int64_t kZBlock = 64;
 constexpr int64_t kAttnHeadDim = 128;
 constexpr int64_t kAttnKeyTile = 64;
 
@@ -120,7 +124,9 @@ size_t tp_ffn_shard_workspace_bytes(int64_t tokens, int64_t hidden, int64_t ffn,
                                     int32_t t, int32_t in_dtype) {
   (void)hidden;
   if (tokens < 0 || ffn <= 0 || t < 1 || ffn % t != 0 || !valid_dtype(in_dtype)) return 0;
-  return (size_t)align256(tokens * (ffn / t) * esize(in_dtype));
+  // bf16: GeLU(Z_i) K-blocked in blocks of up to 64 columns (kZBlock)
+  const int64_t cols = in_dtype == TP_BF16 ? (ffn / t + kZBlock - 1) / kZBlock * kZBlock : ffn / t;
+  return (size_t)align256(tokens * cols * esize(in_dtype));
 }
 
 }  // extern "C"
@@ -211,12 +217,16 @@ hipError_t side_stream(int dev, SideStream** out) {
 }
 
 // GEMM1 + GeLU into the workspace (both input dtypes).
+// GEMM1 + GeLU into the workspace.  bf16: GeLU(Z_i) is stored K-blocked
+// in the block depth of the kernel GEMM2 will run (its A tiles are then
+// contiguous runs of memory); fp32: row-major.
 hipError_t ffn_gemm1(const void* X, const void* W1_i, int64_t ld_w1, void* workspace, int M,
                      int H, int F, int32_t in_dtype, hipStream_t s) {
   if (in_dtype == TP_BF16)
     return tp::gemm_bf16_gelu(static_cast<const uint16_t*>(X), H,
                               static_cast<const uint16_t*>(W1_i), ld_w1,
-                              static_cast<uint16_t*>(workspace), F, M, F, H, s);
+                              static_cast<uint16_t*>(workspace), F, M, F, H,
+                              tp::gemm_bf16_a_block(M, H), s);
   return tp::gemm_f32(static_cast<const float*>(X), H, static_cast<const float*>(W1_i), ld_w1,
                       workspace, F, tp::OUT_F32, true, M, F, H, s);
 }
@@ -245,8 +255,9 @@ tp_status_t tp_ffn_shard(const void* X, const void* W1_i, const void* W2_i,
     if (e != hipSuccess) return hip_status(e, "tp_ffn_shard: GEMM1 launch");
     const tp::OutType ot = out_dtype == TP_F32 ? tp::OUT_F32 : tp::OUT_BF16;
     if (in_dtype == TP_BF16)
-      e = tp::gemm_bf16_store(static_cast<const uint16_t*>(workspace), F,
-                              static_cast<const uint16_t*>(W2_i), H, Y_i, H, ot, M, H, F, s);
+      e = tp::gemm_bf16_store_kb(static_cast<const uint16_t*>(workspace),
+                                 tp::gemm_bf16_a_block(M, H),
+                                 static_cast<const uint16_t*>(W2_i), H, Y_i, H, ot, M, H, F, s);
     else
       e = tp::gemm_f32(static_cast<const float*>(workspace), F,
                        static_cast<const float*>(W2_i), H, Y_i, H, ot, false, M, H, F, s);
@@ -331,9 +342,10 @@ tp_status_t tp_ffn_shard_reduce(const void* X, const void* W1_i, const void* W2_
     const tp::OutType ot = out_dtype == TP_F32 ? tp::OUT_F32 : tp::OUT_BF16;
     auto gemm2_store = [&]() {
       return in_dtype == TP_BF16
-                 ? tp::gemm_bf16_store(static_cast<const uint16_t*>(workspace), F,
-                                       static_cast<const uint16_t*>(W2_i), H, out, H, ot, M, H,
-                                       F, s)
+                 ? tp::gemm_bf16_store_kb(static_cast<const uint16_t*>(workspace),
+                                          tp::gemm_bf16_a_block(M, H),
+                                          static_cast<const uint16_t*>(W2_i), H, out, H, ot, M,
+                                          H, F, s)
                  : tp::gemm_f32(static_cast<const float*>(workspace), F,
                                 static_cast<const float*>(W2_i), H, out, H, ot, false, M, H, F,
                                 s);
@@ -368,9 +380,10 @@ tp_status_t tp_ffn_shard_reduce(const void* X, const void* W1_i, const void* W2_
     if (e == hipSuccess) e = hipStreamWaitEvent(s, ss->others_summed, 0);
     if (e == hipSuccess)
       e = in_dtype == TP_BF16
-              ? tp::gemm_bf16_add(static_cast<const uint16_t*>(workspace), F,
-                                  static_cast<const uint16_t*>(W2_i), H, S, out, H, ot, M, H, F,
-                                  s)
+              ? tp::gemm_bf16_add_kb(static_cast<const uint16_t*>(workspace),
+                                     tp::gemm_bf16_a_block(M, H),
+                                     static_cast<const uint16_t*>(W2_i), H, S, out, H, ot, M, H,
+                                     F, s)
               : tp::gemm_f32_add(static_cast<const float*>(workspace), F,
                                  static_cast<const float*>(W2_i), H, S, out, H, ot, M, H, F, s);
     return hip_status(e, "tp_ffn_shard_reduce: launch");

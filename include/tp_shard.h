@@ -43,7 +43,7 @@
 extern "C" {
 #endif
 
-#define TP_ABI_VERSION 3
+#define TP_ABI_VERSION 4
 #define TP_MAX_PARTIALS 64
 
 /* Element types of tensors crossing the ABI. */
@@ -94,7 +94,11 @@ typedef enum {
  *   workspace                       device scratch of at least
  *                                   tp_ffn_shard_workspace_bytes(...) bytes; it
  *                                   holds GeLU(Z_i) [tokens, ffn/t] between the
- *                                   two GEMMs (no gather: step 2 reads it as is)
+ *                                   two GEMMs (no gather: step 2 reads it as is),
+ *                                   bf16 in an internal K-blocked layout
+ *                                   (tokens x ffn/t rounded up to 64 columns),
+ *                                   fp32 row-major; contents are not part of the
+ *                                   interface
  * Shape rules: tokens >= 0 (0 enqueues nothing); hidden and ffn/t multiples
  * of 8 (bf16) or 4 (fp32); ld_w1 >= ffn/t and a multiple of the same; every
  * dimension below 2^31; with bf16 inputs also hidden, ffn/t < 2^22 and

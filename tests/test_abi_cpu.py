@@ -61,7 +61,11 @@ def test_version_and_status_strings(lib):
 def test_workspace_queries(lib):
     assert lib.tp_ffn_shard_workspace_bytes(4096, 4096, 16384, 8, B.TP_BF16) == 4096 * 2048 * 2
     assert lib.tp_ffn_shard_workspace_bytes(128, 1024, 4096, 1, B.TP_F32) == 128 * 4096 * 4
-    assert lib.tp_ffn_shard_workspace_bytes(3, 8, 24, 3, B.TP_BF16) == 256   # 256-byte granule
+    # bf16: GeLU(Z_i) columns rounded up to a multiple of 64 (its K-blocked
+    # layout), then a 256-byte granule: 3 x 64 x 2 = 384 -> 512
+    assert lib.tp_ffn_shard_workspace_bytes(3, 8, 24, 3, B.TP_BF16) == 512
+    assert lib.tp_ffn_shard_workspace_bytes(2000, 3000, 2936, 1, B.TP_BF16) == 2000 * 2944 * 2
+    assert lib.tp_ffn_shard_workspace_bytes(3, 8, 24, 3, B.TP_F32) == 256    # fp32: row-major
     assert lib.tp_ffn_shard_workspace_bytes(10, 8, 20, 3, B.TP_BF16) == 0    # t does not divide f
     assert lib.tp_ffn_shard_workspace_bytes(10, 8, 16, 0, B.TP_BF16) == 0
     # attention: 6 x [heads, seq_pad, 128] + O hi/lo [tokens, 2*nl*128], 16-bit,
