@@ -111,6 +111,15 @@ __device__ __forceinline__ void wait_vmcnt() {
   asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
 
+// Element offset of O[row][col] in the O buffer ([rows][two_hd] bf16):
+// row-major for kbs == 0, else K-blocked by kb = 1 << kbs for the output
+// projection, [two_hd / kb][rows][kb].  col..col+3 (col % 4 == 0) stay
+// contiguous either way.
+__device__ __forceinline__ int64_t o_at(int64_t row, int col, int64_t rows, int two_hd, int kbs) {
+  return kbs ? ((int64_t)(col >> kbs) * rows + row) * (1 << kbs) + (col & ((1 << kbs) - 1))
+             : row * two_hd + col;
+}
+
 // Key tiles query block qb (of QB queries) needs.
 __host__ __device__ inline int ntile_of(int qb, int seq, int causal, int QB) {
   const int kend = causal ? (QB * (qb + 1) < seq ? QB * (qb + 1) : seq) : seq;
@@ -119,8 +128,8 @@ __host__ __device__ inline int ntile_of(int qb, int seq, int causal, int QB) {
 
 template <int NQG>
 __global__ void __launch_bounds__(NT)
-attn_fwd_kernel(QkvOut q, int causal, uint16_t* __restrict__ O, float* __restrict__ part,
-                AttnSplit sp, float scale_log2) {
+attn_fwd_kernel(QkvOut q, int causal, uint16_t* __restrict__ O, int o_kbs,
+                float* __restrict__ part, AttnSplit sp, float scale_log2) {
   constexpr int QW = 16 * NQG;    // queries per wave
   constexpr int QB = NWAVE * QW;  // queries per workgroup
   // Two LDS buffers of K hi, K lo, V^T hi, V^T lo tiles: one is read by the
@@ -382,19 +391,23 @@ attn_fwd_kernel(QkvOut q, int causal, uint16_t* __restrict__ O, float* __restric
     if (nc == 1) {
       if (myq[qg] < S) {
         const float inv = 1.0f / l_tot;
-        uint16_t* orow = O + ((int64_t)b * S + myq[qg]) * (2 * hd) + head * D;
+        const int64_t orow = (int64_t)b * S + myq[qg], rows = (int64_t)(sp.nbh / q.nl) * S;
 #pragma unroll
         for (int db = 0; db < 8; ++db) {
           uint32_t hi[4], lo[4];
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
-            const float v = o[qg][db][e] * inv;
-            hi[e] = f2bf(v);
-            lo[e] = f2bf(v - __uint_as_float(hi[e] << 16));
+            // hi = bf16(o * inv); lo = bf16 of the exact residual o * inv - hi
+            // (one fma, written out so the rounding does not depend on the
+            // compiler's contraction choices)
+            const float x = o[qg][db][e];
+            hi[e] = f2bf(x * inv);
+            lo[e] = f2bf(__builtin_fmaf(x, inv, -__uint_as_float(hi[e] << 16)));
           }
-          *reinterpret_cast<uint2*>(orow + db * 16 + 4 * g) =
+          const int col = head * D + db * 16 + 4 * g;
+          *reinterpret_cast<uint2*>(O + o_at(orow, col, rows, 2 * hd, o_kbs)) =
               uint2{hi[0] | (hi[1] << 16), hi[2] | (hi[3] << 16)};
-          *reinterpret_cast<uint2*>(orow + hd + db * 16 + 4 * g) =
+          *reinterpret_cast<uint2*>(O + o_at(orow, hd + col, rows, 2 * hd, o_kbs)) =
               uint2{lo[0] | (lo[1] << 16), lo[2] | (lo[3] << 16)};
         }
       }
@@ -424,7 +437,7 @@ attn_fwd_kernel(QkvOut q, int causal, uint16_t* __restrict__ O, float* __restric
 // issues no more loads than it needs.
 template <int MAXC>
 __global__ void __launch_bounds__(256)
-attn_combine_kernel(QkvOut q, int causal, uint16_t* __restrict__ O,
+attn_combine_kernel(QkvOut q, int causal, uint16_t* __restrict__ O, int o_kbs,
                     const float* __restrict__ part, AttnSplit sp) {
   const int QB = sp.qb, wpg = QB / 16;
   const int grp = blockIdx.x / wpg;
@@ -469,18 +482,21 @@ attn_combine_kernel(QkvOut q, int causal, uint16_t* __restrict__ O,
   const float inv = 1.0f / L;
   const int b = bh / q.nl, head = bh - b * q.nl;
   const int hd = q.nl * D;
-  uint16_t* orow = O + ((int64_t)b * S + myq) * (2 * hd) + head * D + dg * 8;
+  const int64_t orow = (int64_t)b * S + myq, rows = (int64_t)(sp.nbh / q.nl) * S;
   uint32_t hi[8], lo[8];
 #pragma unroll
   for (int e = 0; e < 8; ++e) {
-    const float v = (e < 4 ? a0[e] : a1[e - 4]) * inv;
-    hi[e] = f2bf(v);
-    lo[e] = f2bf(v - __uint_as_float(hi[e] << 16));
+    const float x = e < 4 ? a0[e] : a1[e - 4];
+    hi[e] = f2bf(x * inv);  // hi/lo as in attn_fwd_kernel
+    lo[e] = f2bf(__builtin_fmaf(x, inv, -__uint_as_float(hi[e] << 16)));
   }
-  *reinterpret_cast<u32x4*>(orow) = u32x4{hi[0] | (hi[1] << 16), hi[2] | (hi[3] << 16),
-                                          hi[4] | (hi[5] << 16), hi[6] | (hi[7] << 16)};
-  *reinterpret_cast<u32x4*>(orow + hd) = u32x4{lo[0] | (lo[1] << 16), lo[2] | (lo[3] << 16),
-                                               lo[4] | (lo[5] << 16), lo[6] | (lo[7] << 16)};
+  const int col = head * D + dg * 8;
+  *reinterpret_cast<u32x4*>(O + o_at(orow, col, rows, 2 * hd, o_kbs)) =
+      u32x4{hi[0] | (hi[1] << 16), hi[2] | (hi[3] << 16), hi[4] | (hi[5] << 16),
+            hi[6] | (hi[7] << 16)};
+  *reinterpret_cast<u32x4*>(O + o_at(orow, hd + col, rows, 2 * hd, o_kbs)) =
+      u32x4{lo[0] | (lo[1] << 16), lo[2] | (lo[3] << 16), lo[4] | (lo[5] << 16),
+            lo[6] | (lo[7] << 16)};
 }
 
 // Zeroes V^T columns [seq, seq_pad) of every (sequence*head, dim) row, hi
@@ -630,8 +646,10 @@ int64_t attn_partial_bytes(int batch, int seq, int nl) {
   return bytes;
 }
 
-hipError_t attention_fwd(const QkvOut& q, int batch, bool causal, uint16_t* O, float* part,
-                         hipStream_t s) {
+hipError_t attention_fwd(const QkvOut& q, int batch, bool causal, uint16_t* O, int o_kb,
+                         float* part, hipStream_t s) {
+  if (o_kb != 0 && o_kb != 32 && o_kb != 64) return hipErrorInvalidValue;
+  const int o_kbs = o_kb == 32 ? 5 : (o_kb == 64 ? 6 : 0);
   if (batch == 0 || q.seq == 0 || q.nl == 0) return hipSuccess;
   const AttnSplit sp = attn_split(batch, q.seq, q.nl, causal);
   const float scale_log2 = 1.4426950408889634f / sqrtf((float)q.d);
@@ -645,23 +663,23 @@ hipError_t attention_fwd(const QkvOut& q, int batch, bool causal, uint16_t* O, f
   }
   if (sp.qb == 256)
     hipLaunchKernelGGL(attn_fwd_kernel<2>, dim3(sp.n_items), dim3(NT), 0, s, q, causal ? 1 : 0,
-                       O, part, sp, scale_log2);
+                       O, o_kbs, part, sp, scale_log2);
   else
     hipLaunchKernelGGL(attn_fwd_kernel<1>, dim3(sp.n_items), dim3(NT), 0, s, q, causal ? 1 : 0,
-                       O, part, sp, scale_log2);
+                       O, o_kbs, part, sp, scale_log2);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (sp.n_items == sp.nqb * sp.nbh) return hipSuccess;  // no query block was split
   const int max_nc = div_up(ntile_of(sp.nqb - 1, q.seq, causal ? 1 : 0, sp.qb), sp.ch);
   const dim3 grid(sp.nqb * sp.nbh * (sp.qb / 16));
   if (max_nc <= 4)
-    hipLaunchKernelGGL(attn_combine_kernel<4>, grid, dim3(256), 0, s, q, causal ? 1 : 0, O, part,
-                       sp);
+    hipLaunchKernelGGL(attn_combine_kernel<4>, grid, dim3(256), 0, s, q, causal ? 1 : 0, O, o_kbs,
+                       part, sp);
   else if (max_nc <= 8)
-    hipLaunchKernelGGL(attn_combine_kernel<8>, grid, dim3(256), 0, s, q, causal ? 1 : 0, O, part,
-                       sp);
+    hipLaunchKernelGGL(attn_combine_kernel<8>, grid, dim3(256), 0, s, q, causal ? 1 : 0, O, o_kbs,
+                       part, sp);
   else
-    hipLaunchKernelGGL(attn_combine_kernel<16>, grid, dim3(256), 0, s, q, causal ? 1 : 0, O,
+    hipLaunchKernelGGL(attn_combine_kernel<16>, grid, dim3(256), 0, s, q, causal ? 1 : 0, O, o_kbs,
                        part, sp);
   return hipGetLastError();
 }

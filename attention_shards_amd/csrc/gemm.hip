@@ -1062,6 +1062,14 @@ hipError_t gemm_bf16_store_split_a(const uint16_t* A2, int64_t lda,
   return dispatch_bf16<false>(A2, lda, B, ldb, M, N, 2 * K, K, EpiStore{C, ldc, (int)out}, s);
 }
 
+hipError_t gemm_bf16_store_split_a_kb(const uint16_t* A2, int kb, const uint16_t* B,
+                                      int64_t ldb, void* C, int64_t ldc, OutType out, int M,
+                                      int N, int K, hipStream_t s) {
+  if (K % 64) return hipErrorInvalidValue;
+  if (M > 0 && N > 0 && kb != a_block(choose_bf16_tile(M, N))) return hipErrorInvalidValue;
+  return dispatch_bf16<true>(A2, M, B, ldb, M, N, 2 * K, K, EpiStore{C, ldc, (int)out}, s);
+}
+
 hipError_t gemm_bf16_gelu(const uint16_t* A, int64_t lda, const uint16_t* B,
                           int64_t ldb, uint16_t* C, int64_t ldc, int M, int N,
                           int K, int kb, hipStream_t s) {

@@ -55,6 +55,10 @@ hipError_t gemm_bf16_store_split_a(const uint16_t* A2, int64_t lda,
                                    const uint16_t* B, int64_t ldb, void* C,
                                    int64_t ldc, OutType out, int M, int N, int K,
                                    hipStream_t s);
+// The same with A2 K-blocked, [2K/kb][M][kb], kb = gemm_bf16_a_block(M, N).
+hipError_t gemm_bf16_store_split_a_kb(const uint16_t* A2, int kb, const uint16_t* B,
+                                      int64_t ldb, void* C, int64_t ldc, OutType out, int M,
+                                      int N, int K, hipStream_t s);
 // Same product scattered into the attention workspace (N == 3*nl*d).
 hipError_t gemm_bf16_qkv(const uint16_t* A, int64_t lda, const uint16_t* B,
                          int64_t ldb, const QkvOut& q, int M, int N, int K,
@@ -82,10 +86,12 @@ int64_t attn_partial_bytes(int batch, int seq, int nl);
 
 // Causal / full attention over the QKV workspace; writes O as a bf16 hi/lo
 // pair [batch*seq, 2*nl*d]: O_hi in columns [0, nl*d), O_lo in
-// [nl*d, 2*nl*d).  d must be 128.  `part` (attn_partial_bytes, 16-byte
-// aligned) holds the partial results of split query blocks.
-hipError_t attention_fwd(const QkvOut& q, int batch, bool causal, uint16_t* O, float* part,
-                         hipStream_t s);
+// [nl*d, 2*nl*d), row-major for o_kb == 0 or K-blocked for the output
+// projection, [2*nl*d/o_kb][batch*seq][o_kb] (o_kb = 32 or 64).  d must be
+// 128.  `part` (attn_partial_bytes, 16-byte aligned) holds the partial
+// results of split query blocks.
+hipError_t attention_fwd(const QkvOut& q, int batch, bool causal, uint16_t* O, int o_kb,
+                         float* part, hipStream_t s);
 
 // out = sum_i P_i + R, fp32 accumulate, any n (the last n % 8 elements take
 // a scalar path).

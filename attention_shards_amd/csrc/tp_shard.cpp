@@ -483,12 +483,14 @@ tp_status_t tp_attn_shard(const void* X, const void* Wqkv_i, const void* Wo_i,
                                      (int)tokens, (int)nqkv, (int)hidden, s);
     if (e != hipSuccess) return hip_status(e, "tp_attn_shard: QKV launch");
     float* part = reinterpret_cast<float*>(ws + 6 * L.part_bytes + L.o_bytes);
-    e = tp::attention_fwd(q, (int)batch, causal != 0, O, part, s);
+    // O is written K-blocked in the stage depth of the output projection's
+    // kernel, so each of its A stages is one contiguous run.
+    const int o_kb = tp::gemm_bf16_a_block((int)tokens, (int)hidden);
+    e = tp::attention_fwd(q, (int)batch, causal != 0, O, o_kb, part, s);
     if (e != hipSuccess) return hip_status(e, "tp_attn_shard: attention launch");
-    e = tp::gemm_bf16_store_split_a(O, 2 * nl * head_dim, static_cast<const uint16_t*>(Wo_i),
-                                    hidden, Y_i, hidden,
-                                    out_dtype == TP_F32 ? tp::OUT_F32 : tp::OUT_BF16,
-                                    (int)tokens, (int)hidden, (int)(nl * head_dim), s);
+    e = tp::gemm_bf16_store_split_a_kb(O, o_kb, static_cast<const uint16_t*>(Wo_i), hidden, Y_i,
+                                       hidden, out_dtype == TP_F32 ? tp::OUT_F32 : tp::OUT_BF16,
+                                       (int)tokens, (int)hidden, (int)(nl * head_dim), s);
     if (e != hipSuccess) return hip_status(e, "tp_attn_shard: output projection launch");
     return ok();
   } catch (...) {
