@@ -39,7 +39,6 @@
 //     every accumulator is again lane % 16, so softmax rescales are lane-local
 //     and only the row max needs two cross-lane exchanges.
 #include <functional>
-#include <climits>
 #include <map>
 #include <mutex>
 #include <queue>
@@ -618,8 +617,7 @@ AttnSplit choose_split(int batch, int seq, int nl, int causal) {
   const int nqb128 = div_up(seq, 128), nqb256 = div_up(seq, 256);
   const auto c128 = choose_chunk(VAR128, nqb128, sp.nbh, seq, causal);
   const auto c256 = choose_chunk(VAR256, nqb256, sp.nbh, seq, causal);
-  const bool big = c256.second <= 0.97 * c128.second &&
-                   count_items(256, nqb256, seq, causal, c256.first) * sp.nbh <= INT32_MAX;
+  const bool big = c256.second <= 0.97 * c128.second;
   sp.qb = big ? 256 : 128;
   sp.nqb = big ? nqb256 : nqb128;
   sp.ch = big ? c256.first : c128.first;
