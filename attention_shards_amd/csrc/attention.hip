@@ -429,8 +429,9 @@ attn_fwd_kernel(QkvOut q, int causal, uint16_t* __restrict__ O, int o_kbs,
 // Merge of the chunks of query blocks split in more than one.  A thread
 // owns 8 head dims of one query: (query block, sequence*head) is
 // blockIdx.x / (qb/16), and qb/16 workgroups of 256 threads cover its qb
-// queries x 16 dim groups.  The weights exp2(m_c - max m) need every chunk's m first;
-// the O loads of all chunks are then issued before the first multiply-add.
+// queries x 16 dim groups.  The weights exp2(m_c - max m) need every chunk's
+// m: when all chunks fit one pass, their O runs and (m, l) pairs are loaded
+// together and the weights follow; otherwise the maxima are read first.
 // MAXC chunks are merged per pass (more in several passes); the host picks
 // the smallest of 4, 8, 16 that covers the largest chunk count, so a pass
 // issues no more loads than it needs.
@@ -451,31 +452,66 @@ attn_combine_kernel(QkvOut q, int causal, uint16_t* __restrict__ O, int o_kbs,
   const int myq = qb * QB + qi;
   if (myq >= S) return;
   const float* ml = part + (int64_t)sp.n_items * QB * D;
-  float M = -__builtin_inff();
-  for (int c = 0; c < nc; ++c) {
-    const int item = base + c * sp.nbh + bh;
-    M = fmaxf(M, ml[((int64_t)item * QB + qi) * 2]);
-  }
+  // chunk c's row of partial results (O run, then max and denominator in ml)
+  auto row_of = [&](int c) { return (int64_t)(base + c * sp.nbh + bh) * QB + qi; };
+  // one chunk's contribution, in chunk order: L += w l_c, a += w O_c
   float L = 0.0f;
   f32x4 a0 = {0, 0, 0, 0}, a1 = {0, 0, 0, 0};
-  for (int c0 = 0; c0 < nc; c0 += MAXC) {
+  auto accumulate = [&](float w, float lc, const f32x4& x0, const f32x4& x1) {
+    L = __builtin_fmaf(w, lc, L);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      a0[e] = __builtin_fmaf(w, x0[e], a0[e]);
+      a1[e] = __builtin_fmaf(w, x1[e], a1[e]);
+    }
+  };
+  if (nc <= MAXC) {
+    // One pass (the host sizes MAXC to the largest chunk count): every
+    // chunk's O run, max and denominator are loaded together, then the
+    // weights exp2(m_c - max m) follow from the loaded maxima.
     f32x4 x0[MAXC], x1[MAXC];
-    float w[MAXC];
+    float mc[MAXC], lc[MAXC];
 #pragma unroll
     for (int u = 0; u < MAXC; ++u) {
-      const int c = c0 + u < nc ? c0 + u : nc - 1;  // past the end: re-read, weight 0
-      const int64_t row = (int64_t)(base + c * sp.nbh + bh) * QB + qi;
+      const int64_t row = row_of(u < nc ? u : nc - 1);  // past the end: re-read, weight 0
       const f32x4* po = reinterpret_cast<const f32x4*>(part + row * D + dg * 8);
       x0[u] = po[0];
       x1[u] = po[1];
-      const float mc = ml[row * 2];
-      w[u] = (c0 + u >= nc || mc == -__builtin_inff()) ? 0.0f : __builtin_amdgcn_exp2f(mc - M);
-      L += w[u] * ml[row * 2 + 1];
+      mc[u] = ml[row * 2];
+      lc[u] = ml[row * 2 + 1];
     }
+    float M = -__builtin_inff();
+#pragma unroll
+    for (int u = 0; u < MAXC; ++u) M = fmaxf(M, mc[u]);
 #pragma unroll
     for (int u = 0; u < MAXC; ++u) {
-      a0 += w[u] * x0[u];
-      a1 += w[u] * x1[u];
+      const float w =
+          (u >= nc || mc[u] == -__builtin_inff()) ? 0.0f : __builtin_amdgcn_exp2f(mc[u] - M);
+      accumulate(w, lc[u], x0[u], x1[u]);
+    }
+  } else {
+    // Several passes of MAXC chunks: the maxima first.
+    float M = -__builtin_inff();
+    for (int c = 0; c < nc; ++c) M = fmaxf(M, ml[row_of(c) * 2]);
+    for (int c0 = 0; c0 < nc; c0 += MAXC) {
+      f32x4 x0[MAXC], x1[MAXC];
+      float mc[MAXC], lc[MAXC];
+#pragma unroll
+      for (int u = 0; u < MAXC; ++u) {
+        const int64_t row = row_of(c0 + u < nc ? c0 + u : nc - 1);
+        const f32x4* po = reinterpret_cast<const f32x4*>(part + row * D + dg * 8);
+        x0[u] = po[0];
+        x1[u] = po[1];
+        mc[u] = ml[row * 2];
+        lc[u] = ml[row * 2 + 1];
+      }
+#pragma unroll
+      for (int u = 0; u < MAXC; ++u) {
+        const float w = (c0 + u >= nc || mc[u] == -__builtin_inff())
+                            ? 0.0f
+                            : __builtin_amdgcn_exp2f(mc[u] - M);
+        accumulate(w, lc[u], x0[u], x1[u]);
+      }
     }
   }
   const float inv = 1.0f / L;
