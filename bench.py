@@ -439,6 +439,44 @@ def summarize_attn_profile(trace_csv, cmd):
     print(f"wrote attention profile ({len(calls)} calls, median {med:.1f} us)")
 
 
+def summarize_counters(counter_csv, cmd):
+    """Write profiles/counters_mfma_lds_ffn_attn.md from a rocprofv3 --pmc run
+    of MfmaUtil, SQ_VALU_MFMA_BUSY_CYCLES, GRBM_GUI_ACTIVE, SQ_LDS_BANK_CONFLICT
+    and SQ_INSTS_LDS over a bench run: per kernel (and grid size), the mean of
+    rocprofv3's MfmaUtil and the LDS bank-conflict cycles per LDS instruction."""
+    import csv
+    per = {}
+    for r in csv.DictReader(open(counter_csv)):
+        d = per.setdefault(r["Dispatch_Id"], {"name": _short(r["Kernel_Name"]),
+                                              "wg": int(r["Grid_Size"]) // int(r["Workgroup_Size"])})
+        d[r["Counter_Name"]] = d.get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
+    groups = {}
+    for d in per.values():
+        if d["name"].startswith("at::") or "copyBuffer" in d["name"]:
+            continue
+        groups.setdefault((d["name"], d["wg"]), []).append(d)
+    lines = ["# MFMA utilisation and LDS bank conflicts per kernel (FFN step and attention shard)",
+             "", "Command (from the repository root, on one MI355X):", "", "```", cmd, "```", "",
+             "`MfmaUtil` is rocprofv3's derived metric: the summed per-SIMD "
+             "`SQ_VALU_MFMA_BUSY_CYCLES` over `GRBM_GUI_ACTIVE` times the SIMD count, in "
+             "percent (the GPU-busy cycles count at the reference clock, so it is close to the "
+             "fraction of the nominal MFMA peak). Conflicts: `SQ_LDS_BANK_CONFLICT` cycles per "
+             "`SQ_INSTS_LDS` instruction. Means over the run's dispatches of each kernel and "
+             "grid size.", "",
+             "| kernel | workgroups | dispatches | MfmaUtil % | LDS conflict cycles / LDS instr |",
+             "|---|---:|---:|---:|---:|"]
+    for (name, wg), ds in sorted(groups.items(), key=lambda kv: -sum(x.get("GRBM_GUI_ACTIVE", 0)
+                                                                      for x in kv[1])):
+        mu = sum(x.get("MfmaUtil", 0.0) for x in ds) / len(ds)
+        conf = sum(x.get("SQ_LDS_BANK_CONFLICT", 0.0) for x in ds)
+        insts = sum(x.get("SQ_INSTS_LDS", 0.0) for x in ds)
+        lines.append(f"| `{name}` | {wg} | {len(ds)} | {mu:.1f} | "
+                     f"{(conf / insts if insts else 0.0):.3f} |")
+    with open(os.path.join(ROOT, "profiles", "counters_mfma_lds_ffn_attn.md"), "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print(f"wrote profiles/counters_mfma_lds_ffn_attn.md ({len(per)} dispatches)")
+
+
 def summarize_sweep(path, cmd):
     """Write profiles/sweep_ffn_shard_tokens2048.md from a --sweep JSONL file."""
     recs = [json.loads(line) for line in open(path) if line.strip()]
@@ -484,6 +522,8 @@ def main():
     ap.add_argument("--sweep", metavar="OUT_JSONL", default=None)
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run a 1 GiB device copy first (counter calibration)")
+    ap.add_argument("--summarize-counters", metavar="COUNTER_CSV", default=None,
+                    help="write the MFMA-utilisation / LDS-conflict table from a --pmc run")
     ap.add_argument("--summarize-attn-profile", metavar="KERNEL_TRACE_CSV", default=None,
                     help="write the attention-shard kernel table from a rocprofv3 trace")
     ap.add_argument("--summarize-sweep", metavar="SWEEP_JSONL", default=None,
@@ -494,6 +534,9 @@ def main():
     ap.add_argument("--profile-commands", nargs=2, default=["", ""],
                     metavar=("STATS_CMD", "PMC_CMD"))
     args = ap.parse_args()
+    if args.summarize_counters:
+        summarize_counters(args.summarize_counters, args.profile_commands[0])
+        return
     if args.summarize_attn_profile:
         summarize_attn_profile(args.summarize_attn_profile, args.profile_commands[0])
         return
