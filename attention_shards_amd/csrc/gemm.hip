@@ -1039,12 +1039,6 @@ hipError_t launch_f32(const float* A, int64_t lda, const float* B, int64_t ldb,
 
 }  // namespace
 
-hipError_t gemm_bf16_store(const uint16_t* A, int64_t lda, const uint16_t* B,
-                           int64_t ldb, void* C, int64_t ldc, OutType out,
-                           int M, int N, int K, hipStream_t s) {
-  return dispatch_bf16<false>(A, lda, B, ldb, M, N, K, K, EpiStore{C, ldc, (int)out}, s);
-}
-
 int gemm_bf16_a_block(int M, int N) { return a_block(choose_bf16_tile(M, N)); }
 
 hipError_t gemm_bf16_store_kb(const uint16_t* A, int kb, const uint16_t* B, int64_t ldb,
@@ -1052,14 +1046,6 @@ hipError_t gemm_bf16_store_kb(const uint16_t* A, int kb, const uint16_t* B, int6
                               hipStream_t s) {
   if (M > 0 && N > 0 && kb != a_block(choose_bf16_tile(M, N))) return hipErrorInvalidValue;
   return dispatch_bf16<true>(A, M, B, ldb, M, N, K, K, EpiStore{C, ldc, (int)out}, s);
-}
-
-hipError_t gemm_bf16_store_split_a(const uint16_t* A2, int64_t lda,
-                                   const uint16_t* B, int64_t ldb, void* C,
-                                   int64_t ldc, OutType out, int M, int N, int K,
-                                   hipStream_t s) {
-  if (K % 64) return hipErrorInvalidValue;  // each half a whole number of stages
-  return dispatch_bf16<false>(A2, lda, B, ldb, M, N, 2 * K, K, EpiStore{C, ldc, (int)out}, s);
 }
 
 hipError_t gemm_bf16_store_split_a_kb(const uint16_t* A2, int kb, const uint16_t* B,
@@ -1082,12 +1068,6 @@ hipError_t gemm_bf16_qkv(const uint16_t* A, int64_t lda, const uint16_t* B,
                          int64_t ldb, const QkvOut& q, int M, int N, int K,
                          hipStream_t s) {
   return dispatch_bf16<false>(A, lda, B, ldb, M, N, K, K, EpiQkv{q}, s);
-}
-
-hipError_t gemm_bf16_add(const uint16_t* A, int64_t lda, const uint16_t* B, int64_t ldb,
-                         const float* S, void* C, int64_t ldc, OutType out, int M, int N,
-                         int K, hipStream_t s) {
-  return dispatch_bf16<false>(A, lda, B, ldb, M, N, K, K, EpiAdd{S, C, ldc, (int)out}, s);
 }
 
 hipError_t gemm_bf16_add_kb(const uint16_t* A, int kb, const uint16_t* B, int64_t ldb,

@@ -29,14 +29,12 @@ struct QkvOut {
   int32_t d;        // head dim
 };
 
-// C[M,N] = A[M,K] * B[K,N] with bf16 inputs and fp32 accumulation.
-// A is K-contiguous (row stride lda), B is N-contiguous (row stride ldb).
-// Requirements checked by the caller: K % 8 == 0, N % 8 == 0, lda/ldb % 8 == 0,
-// 16-byte aligned A and B.
-hipError_t gemm_bf16_store(const uint16_t* A, int64_t lda, const uint16_t* B,
-                           int64_t ldb, void* C, int64_t ldc, OutType out,
-                           int M, int N, int K, hipStream_t s);
-// Same product, C = bf16(GeLU_erf(acc)): row-major (row stride ldc) for
+// bf16 products C[M,N] = A[M,K] * B[K,N] with fp32 accumulation.  A is
+// K-contiguous (row stride lda, or K-blocked where stated), B is
+// N-contiguous (row stride ldb).  Requirements checked by the caller:
+// K % 8 == 0, N % 8 == 0, lda/ldb % 8 == 0, 16-byte aligned A and B.
+//
+// C = bf16(GeLU_erf(acc)): row-major (row stride ldc) for
 // kb == 0, else K-blocked for a following product, [ceil(N/kb)][M][kb]
 // (kb = 32 or 64; columns past N in the last block are not written).
 hipError_t gemm_bf16_gelu(const uint16_t* A, int64_t lda, const uint16_t* B,
@@ -44,18 +42,14 @@ hipError_t gemm_bf16_gelu(const uint16_t* A, int64_t lda, const uint16_t* B,
                           int K, int kb, hipStream_t s);
 // K block the kernel chosen for an [M, N] output reads a K-blocked A in.
 int gemm_bf16_a_block(int M, int N);
-// gemm_bf16_store / gemm_bf16_add with A K-blocked, [ceil(K/kb)][M][kb];
+// C = acc stored as `out` (row stride ldc), A K-blocked, [ceil(K/kb)][M][kb];
 // kb must be gemm_bf16_a_block(M, N) (else hipErrorInvalidValue).
 hipError_t gemm_bf16_store_kb(const uint16_t* A, int kb, const uint16_t* B, int64_t ldb,
                               void* C, int64_t ldc, OutType out, int M, int N, int K,
                               hipStream_t s);
-// C = [A_hi | A_lo] * B: A2 is [M, 2K] (row stride lda), the same B[K,N]
-// multiplies both halves (two MFMA passes over K); K a multiple of 64.
-hipError_t gemm_bf16_store_split_a(const uint16_t* A2, int64_t lda,
-                                   const uint16_t* B, int64_t ldb, void* C,
-                                   int64_t ldc, OutType out, int M, int N, int K,
-                                   hipStream_t s);
-// The same with A2 K-blocked, [2K/kb][M][kb], kb = gemm_bf16_a_block(M, N).
+// C = [A_hi | A_lo] * B: A2 is [M, 2K], the same B[K,N] multiplies both
+// halves (two MFMA passes over K); K a multiple of 64; A2 K-blocked,
+// [2K/kb][M][kb], kb = gemm_bf16_a_block(M, N).
 hipError_t gemm_bf16_store_split_a_kb(const uint16_t* A2, int kb, const uint16_t* B,
                                       int64_t ldb, void* C, int64_t ldc, OutType out, int M,
                                       int N, int K, hipStream_t s);
@@ -103,11 +97,8 @@ hipError_t partial_reduce(const ReducePtrs& ptrs, int t, int pdt,
                           int64_t n, hipStream_t s);
 
 // C = S + A*B: the product added to an fp32 [M, N] matrix S (row stride
-// ldc, like C) and rounded once to the output type.  bf16 and fp32 inputs,
-// with the requirements of gemm_bf16_store / gemm_f32.
-hipError_t gemm_bf16_add(const uint16_t* A, int64_t lda, const uint16_t* B, int64_t ldb,
-                         const float* S, void* C, int64_t ldc, OutType out, int M, int N,
-                         int K, hipStream_t s);
+// ldc, like C) and rounded once to the output type.  bf16 (A K-blocked as
+// for gemm_bf16_store_kb) and fp32 inputs (requirements of gemm_f32).
 hipError_t gemm_bf16_add_kb(const uint16_t* A, int kb, const uint16_t* B, int64_t ldb,
                             const float* S, void* C, int64_t ldc, OutType out, int M, int N,
                             int K, hipStream_t s);

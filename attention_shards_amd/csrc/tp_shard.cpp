@@ -125,7 +125,8 @@ size_t tp_ffn_shard_workspace_bytes(int64_t tokens, int64_t hidden, int64_t ffn,
   (void)hidden;
   if (tokens < 0 || ffn <= 0 || t < 1 || ffn % t != 0 || !valid_dtype(in_dtype)) return 0;
   // bf16: GeLU(Z_i) K-blocked in blocks of up to 64 columns (kZBlock)
-  const int64_t cols = in_dtype == TP_BF16 ? (ffn / t + kZBlock - 1) / kZBlock * kZBlock : ffn / t;
+  const int64_t fs = ffn / t;
+  const int64_t cols = in_dtype == TP_BF16 ? (fs + kZBlock - 1) / kZBlock * kZBlock : fs;
   return (size_t)align256(tokens * cols * esize(in_dtype));
 }
 
@@ -216,7 +217,6 @@ hipError_t side_stream(int dev, SideStream** out) {
   return e;
 }
 
-// GEMM1 + GeLU into the workspace (both input dtypes).
 // GEMM1 + GeLU into the workspace.  bf16: GeLU(Z_i) is stored K-blocked
 // in the block depth of the kernel GEMM2 will run (its A tiles are then
 // contiguous runs of memory); fp32: row-major.
