@@ -81,7 +81,8 @@ def test_bf16_ragged(gpu, M, h, f, t, i, out, view):
     got = run_shard(gpu, d, i, t, out, view)
     ref = oracle_shard(d, i, t)
     e = rel_err(got, ref)
-    log(f"ragged bf16 M={M} h={h} f={f} t={t} i={i} out={out}: err {e:.4f}")
+    floor = f" (bf16 output floor {bf16_floor(ref):.4f})" if out == syn.BF16 else ""
+    log(f"ragged bf16 M={M} h={h} f={f} t={t} i={i} out={out}: err {e:.4f}{floor}")
     assert e <= TOL_BF16
 
 
