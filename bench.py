@@ -3,6 +3,8 @@
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
                     [--sweep OUT.jsonl]
+    python bench.py --summarize-{profiles,attn-profile,counters,sweep} ...
+                    (write profiles/*.md from rocprofv3 output or a sweep)
 
 Workload (one "step"): FFN shard i=3 of t=8 at hidden 4096, ffn 16384,
 4096 tokens (2 sequences of 2048), bf16 inputs with fp32 accumulation:
@@ -15,15 +17,14 @@ value = algorithmic FFN FLOPs of the shard (4*M*h*f/t) / wall time per step.
 Every timed row starts after about 0.1 s of the same work, untimed, so that
 the GPU has left its idle clock state, then W warmup steps.
 
-The same run also times the reduce-scatter block shard i would own
-(tp_partial_reduce_slice; rows.partial_reduce_slice), that step with the sum
-fused into the second GEMM's epilogue (tp_ffn_shard_reduce;
-rows.ffn_shard_reduce_fused), the attention
-shard (t=8, 8 of 64 heads of 128,
-hidden 8192, 2048 tokens, causal) and a whole layer of four shards on this
-GPU (hidden 12288, 96 heads, 8192 tokens) and reports them under "rows", and, on rank 0
-at N=1, times the fp64 CPU oracle on a bounded sample of the FFN workload
-("cpu_baseline").  Prints ONE JSON line.
+The same run also times, under "rows": the reduce-scatter block shard i
+would own (tp_partial_reduce_slice; rows.partial_reduce_slice), the step
+with the sum fused into the second GEMM's epilogue (tp_ffn_shard_reduce;
+rows.ffn_shard_reduce_fused), the attention shard (t=8, 8 of 64 heads of
+128, hidden 8192, 2048 tokens, causal; rows.attn_shard) and a whole layer
+of four shards on this GPU (hidden 12288, 96 heads, 8192 tokens;
+rows.layer).  On rank 0 at N=1 it also times the fp64 CPU oracle on a
+bounded sample of the FFN workload ("cpu_baseline").  Prints ONE JSON line.
 """
 from __future__ import annotations
 
