@@ -187,17 +187,23 @@ hipError_t launch_c(const ReducePtrs& ptrs, int t, const void* R, void* out,
   return hipGetLastError();
 }
 
-// Chunk size: the smallest of 1, 2, 4, 7, 8 that holds the t-1 later
-// partials (7 for t = 8, so no load is a duplicate: fp32 partials 5.7 vs
-// 5.3 TB/s at t=8 [2048,8192]).
+// Chunk size: t-1 for t <= 8, so the first chunk holds exactly the later
+// partials and no load is a duplicate (fp32 partials at t=8 [2048,8192]:
+// 5.7 vs 5.3 TB/s with one duplicate per group); chunks of 8 beyond.
 template <int PDT, int RDT, int ODT>
 hipError_t launch(const ReducePtrs& ptrs, int t, const void* R, void* out,
                   int64_t n, hipStream_t s) {
-  if (t <= 2) return launch_c<PDT, RDT, ODT, 1>(ptrs, t, R, out, n, s);
-  if (t <= 3) return launch_c<PDT, RDT, ODT, 2>(ptrs, t, R, out, n, s);
-  if (t <= 5) return launch_c<PDT, RDT, ODT, 4>(ptrs, t, R, out, n, s);
-  if (t == 8) return launch_c<PDT, RDT, ODT, 7>(ptrs, t, R, out, n, s);
-  return launch_c<PDT, RDT, ODT, 8>(ptrs, t, R, out, n, s);
+  switch (t) {
+    case 1:
+    case 2: return launch_c<PDT, RDT, ODT, 1>(ptrs, t, R, out, n, s);
+    case 3: return launch_c<PDT, RDT, ODT, 2>(ptrs, t, R, out, n, s);
+    case 4: return launch_c<PDT, RDT, ODT, 3>(ptrs, t, R, out, n, s);
+    case 5: return launch_c<PDT, RDT, ODT, 4>(ptrs, t, R, out, n, s);
+    case 6: return launch_c<PDT, RDT, ODT, 5>(ptrs, t, R, out, n, s);
+    case 7: return launch_c<PDT, RDT, ODT, 6>(ptrs, t, R, out, n, s);
+    case 8: return launch_c<PDT, RDT, ODT, 7>(ptrs, t, R, out, n, s);
+    default: return launch_c<PDT, RDT, ODT, 8>(ptrs, t, R, out, n, s);
+  }
 }
 
 template <int PDT, int RDT>
