@@ -53,6 +53,8 @@ def test_attention_shard_t8_full(gpu):
     (1, 2001, 512, 16, 2, 0, False, syn.F32),  # cross the K|V boundary; ragged rows; 256-query blocks
     (2, 1500, 512, 16, 2, 1, True, syn.F32),   # 256-query blocks, ragged, up to 4 chunks merged
     (1, 4000, 512, 8, 2, 0, True, syn.F32),    # 256-query blocks, up to 7 chunks merged
+    (3, 1000, 512, 32, 2, 1, False, syn.F32),  # 256-query blocks over three sequences, full
+    (3, 1300, 512, 32, 2, 0, True, syn.F32),   # ... causal, seq not a multiple of 8 (V^T by rows)
 ])
 def test_attention_small(gpu, batch, seq, hidden, nh, t, i, causal, out):
     a = syn.make_attn_inputs(40 + seq, batch, seq, hidden, nh, 128)
