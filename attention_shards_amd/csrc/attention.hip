@@ -135,7 +135,8 @@ attn_fwd_kernel(QkvOut q, int causal, uint16_t* __restrict__ O, int o_kbs,
   // products while the next tile is staged into the other.
   __shared__ __attribute__((aligned(16))) uint8_t smem[2 * 4 * TILE];
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform per wave
   const int S = q.seq, Sp = q.seq_pad;
   // workgroup -> (query block qb, chunk c, sequence*head bh)
   int rem = blockIdx.x, qb = sp.nqb - 1, nc = 1;
@@ -236,6 +237,14 @@ attn_fwd_kernel(QkvOut q, int causal, uint16_t* __restrict__ O, int o_kbs,
     // Tile kt+1 into the other buffer; its last reader, tile kt-1, finished
     // before the barrier that ended the previous step.
     if (kt + 1 < kt1) stage(k0 + KT, cur ^ 1);
+    // Causal: a tile that starts after this wave's last query is masked for
+    // all of its queries and changes neither their softmax state nor O, so
+    // the wave only takes part in the tile's loads and its closing barrier.
+    if (causal && k0 > qb * QB + wave * QW + QW - 1) {
+      wait_vmcnt<0>();
+      __syncthreads();
+      continue;
+    }
     const uint8_t* const sKh = smem + cur * 4 * TILE;
     const uint8_t* const sKl = sKh + TILE;
     const uint8_t* const sVh = sKh + 2 * TILE;
