@@ -1086,7 +1086,7 @@ hipError_t gemm_f32_add(const float* A, int64_t lda, const float* B, int64_t ldb
 hipError_t gemm_f32(const float* A, int64_t lda, const float* B, int64_t ldb,
                     void* C, int64_t ldc, OutType out, bool gelu, int M, int N,
                     int K, hipStream_t s) {
-  if (gelu) return launch_f32(A, lda, B, ldb, M, N, K, EpiGelu{C, ldc, (int)out}, s);
+  if (gelu) return launch_f32(A, lda, B, ldb, M, N, K, EpiGelu{C, ldc, (int)out, 0, 0}, s);
   return launch_f32(A, lda, B, ldb, M, N, K, EpiStore{C, ldc, (int)out}, s);
 }
 
