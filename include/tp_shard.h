@@ -74,8 +74,9 @@ typedef enum {
  *     Y_i = GeLU(X * W1_i) * W2_i
  * with GeLU(z) = 0.5 z (1 + erf(z / sqrt 2)) (the exact erf form) applied in
  * fp32 to the fp32-accumulated product, and no biases.  Phi(z) is evaluated
- * with the erfc approximation of Abramowitz & Stegun 7.1.26, so the GeLU
- * value is within 3.2e-7 |z| of the exact one.
+ * with the Chebyshev erfc fit of Numerical Recipes (section 6.2, erfcc), so
+ * the GeLU value is within 2.5e-7 |z| of the exact one and within a relative
+ * 1e-5 of it for every z (also deep in the negative tail).
  *
  *   X     [tokens, hidden]          full input, replicated on every GPU
  *   W1_i  [hidden, ffn/t]           columns [i*ffn/t, (i+1)*ffn/t) of W1;

@@ -6,7 +6,7 @@ Follows "Tensor Parallelism > Combining Column and Row Parallelism"
 from __future__ import annotations
 
 import numpy as np
-from scipy.special import erf
+from scipy.special import erfc
 
 
 def gelu(z: np.ndarray) -> np.ndarray:
@@ -14,10 +14,13 @@ def gelu(z: np.ndarray) -> np.ndarray:
 
     The page applies "GeLU" element-wise between the two linear layers
     (FFN step 1 and the paragraph on where the nonlinearity fits); the exact
-    erf form is the reading taken (not the tanh approximation).
+    erf form is the reading taken (not the tanh approximation).  Evaluated
+    as 0.5 * z * erfc(-z / sqrt(2)), the same function (1 + erf(u) =
+    erfc(-u)) without the cancellation of 1 + erf for z << 0, so the value
+    is relatively accurate in the negative tail as well.
     """
     z = np.asarray(z, dtype=np.float64)
-    return 0.5 * z * (1.0 + erf(z / np.sqrt(2.0)))
+    return 0.5 * z * erfc(-z / np.sqrt(2.0))
 
 
 def column_parallel(X: np.ndarray, W1_i: np.ndarray) -> np.ndarray:

@@ -45,9 +45,11 @@ def _decimal_pi():
     return 16 * arctan_inv(5) - 4 * arctan_inv(239)
 
 
-def _phi_taylor(x: float) -> float:
-    """Standard normal CDF from the Maclaurin series of erf, 60 digits."""
-    getcontext().prec = 60
+def _phi_taylor(x: float, prec: int = 60) -> float:
+    """Standard normal CDF from the Maclaurin series of erf, `prec` digits
+    (the terms reach about exp(x^2/2) before they cancel, so the negative
+    tail needs more digits than the default)."""
+    getcontext().prec = prec
     u = Decimal(x) / Decimal(2).sqrt()
     term = u
     s = u
@@ -57,7 +59,7 @@ def _phi_taylor(x: float) -> float:
         term = -term * u * u / n
         add = term / (2 * n + 1)
         s += add
-        if abs(add) < Decimal(10) ** -55:
+        if abs(add) < Decimal(10) ** -(prec - 5):
             break
     erf = 2 / _decimal_pi().sqrt() * s
     return float((1 + erf) / 2)
@@ -78,6 +80,16 @@ def test_gelu_equals_z_phi(z):
     want = z * _phi_taylor(z)
     got = float(oracle.gelu(np.array([z]))[0])
     assert abs(got - want) <= 4e-16 * max(1.0, abs(z)), (z, got, want)
+
+
+@pytest.mark.parametrize("z", [-12.0, -10.0, -8.0, -6.0, -4.5])
+def test_gelu_relative_accuracy_in_the_negative_tail(z):
+    """GeLU(z) for z << 0 is z * Phi(z) with Phi down to ~2e-33; the oracle
+    must hold its relative accuracy there (1 + erf cancels, erfc does not)."""
+    want = z * _phi_taylor(z, prec=140)
+    got = float(oracle.gelu(np.array([z]))[0])
+    assert want < 0.0
+    assert abs(got - want) <= 1e-13 * abs(want), (z, got, want)
 
 
 def test_gelu_special_values():
