@@ -114,10 +114,21 @@ def _dense(t, name: str):
     return t
 
 
-def _stream(stream) -> int:
+def _stream_of(stream, device):
+    """The torch stream the call is enqueued on: the current stream of
+    `device` for None, a torch stream as given, or a raw hipStream_t handle
+    (int; 0 is the device's default stream) wrapped as an external stream.
+    Temporaries a call allocates (its workspace) are allocated while this
+    stream is current, so the caching allocator only hands their memory out
+    again in this stream's order, after the call's kernels."""
+    torch = _torch()
     if stream is None:
-        return _torch().cuda.current_stream().cuda_stream
-    return int(getattr(stream, "cuda_stream", stream))
+        return torch.cuda.current_stream(device)
+    if isinstance(stream, int):
+        if stream == 0:
+            return torch.cuda.default_stream(device)
+        return torch.cuda.ExternalStream(stream, device=device)
+    return stream
 
 
 def tp_ffn_shard_workspace_bytes(tokens: int, hidden: int, ffn: int, t: int,
@@ -168,13 +179,14 @@ def tp_ffn_shard(X, W1_i, W2_i, Y_i, i: int, t: int, workspace=None,
         raise TypeError("X, W1_i and W2_i must share a dtype")
     ffn = fs * t
     need = tp_ffn_shard_workspace_bytes(tokens, hidden, ffn, t, in_dt)
-    ws = _workspace(workspace, need, X.device)
     torch = _torch()
-    with torch.cuda.device(X.device):
+    s = _stream_of(stream, X.device)
+    with torch.cuda.device(X.device), torch.cuda.stream(s):
+        ws = _workspace(workspace, need, X.device)
         _check(lib.tp_ffn_shard(X.data_ptr(), W1_i.data_ptr(), W2_i.data_ptr(),
                                 Y_i.data_ptr(), tokens, hidden, ffn, i, t,
                                 W1_i.stride(0), in_dt, _dtype_code(Y_i),
-                                ws.data_ptr(), ws.numel(), _stream(stream)))
+                                ws.data_ptr(), ws.numel(), s.cuda_stream))
     return Y_i
 
 
@@ -224,13 +236,14 @@ def tp_ffn_shard_reduce(X, W1_i, W2_i, peer_partials, residual, out, i: int,
                                   for k, p in enumerate(peer_partials)])
     ffn = fs * t
     need = tp_ffn_shard_reduce_workspace_bytes(tokens, hidden, ffn, t, in_dt)
-    ws = _workspace(workspace, need, X.device)
     torch = _torch()
-    with torch.cuda.device(X.device):
+    s = _stream_of(stream, X.device)
+    with torch.cuda.device(X.device), torch.cuda.stream(s):
+        ws = _workspace(workspace, need, X.device)
         _check(lib.tp_ffn_shard_reduce(X.data_ptr(), W1_i.data_ptr(), W2_i.data_ptr(), arr,
                                        rptr, out.data_ptr(), tokens, hidden, ffn, i, t,
                                        W1_i.stride(0), in_dt, pdt, rdt, _dtype_code(out),
-                                       ws.data_ptr(), ws.numel(), _stream(stream)))
+                                       ws.data_ptr(), ws.numel(), s.cuda_stream))
     return out
 
 
@@ -253,15 +266,16 @@ def tp_attn_shard(X, Wqkv_i, Wo_i, Y_i, batch: int, seq: int, n_heads: int,
             tuple(Y_i.shape) != (batch * seq, hidden):
         raise ValueError(f"shape mismatch: X{tuple(X.shape)} Wqkv_i{tuple(Wqkv_i.shape)} "
                          f"Wo_i{tuple(Wo_i.shape)} Y_i{tuple(Y_i.shape)}")
-    need = tp_attn_shard_workspace_bytes(batch, seq, n_heads, head_dim, t)
-    ws = _workspace(workspace, need, X.device)
     torch = _torch()
-    with torch.cuda.device(X.device):
+    s = _stream_of(stream, X.device)
+    with torch.cuda.device(X.device), torch.cuda.stream(s):
+        need = tp_attn_shard_workspace_bytes(batch, seq, n_heads, head_dim, t)
+        ws = _workspace(workspace, need, X.device)
         _check(lib.tp_attn_shard(X.data_ptr(), Wqkv_i.data_ptr(), Wo_i.data_ptr(),
                                  Y_i.data_ptr(), batch, seq, hidden, n_heads,
                                  head_dim, i, t, 1 if causal else 0,
                                  _dtype_code(X), _dtype_code(Y_i), ws.data_ptr(),
-                                 ws.numel(), _stream(stream)))
+                                 ws.numel(), s.cuda_stream))
     return Y_i
 
 
@@ -292,15 +306,16 @@ def tp_partial_reduce(partials, residual, out, stream=None, slice_of=None):
         rptr = residual.data_ptr()
     arr = (ctypes.c_void_p * t)(*[p.data_ptr() for p in partials])
     torch = _torch()
+    s = _stream_of(stream, out.device)
     with torch.cuda.device(out.device):
         if slice_of is None:
             _check(lib.tp_partial_reduce(arr, t, rptr, out.data_ptr(), rows, cols, pdt,
-                                         rdt, _dtype_code(out), _stream(stream)))
+                                         rdt, _dtype_code(out), s.cuda_stream))
         else:
             slice_, nslices = slice_of
             _check(lib.tp_partial_reduce_slice(arr, t, rptr, out.data_ptr(), rows, cols,
                                                slice_, nslices, pdt, rdt, _dtype_code(out),
-                                               _stream(stream)))
+                                               s.cuda_stream))
     return out
 
 

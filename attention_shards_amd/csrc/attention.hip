@@ -547,7 +547,7 @@ attn_combine_kernel(QkvOut q, int causal, uint16_t* __restrict__ O, int o_kbs,
 // and lo: the probabilities of those keys are 0, but 0 times whatever the
 // workspace held there need not be.
 __global__ void __launch_bounds__(256)
-vt_pad_zero_kernel(QkvOut q, int rows) {
+vt_pad_zero_kernel(QkvOut q, int64_t rows) {
   const int pad = q.seq_pad - q.seq;
   const int64_t n = (int64_t)rows * pad;
   for (int64_t k = (int64_t)blockIdx.x * 256 + threadIdx.x; k < n; k += (int64_t)gridDim.x * 256) {
@@ -561,7 +561,7 @@ vt_pad_zero_kernel(QkvOut q, int rows) {
 // Estimated time, in units of one 64-key tile of a 128-query workgroup, of
 // the attention kernel with query blocks of QB queries and chunks of `ch`
 // tiles: workgroups are dispatched in grid order (longest query blocks
-// first) onto NCU compute units, one at a time each (the LDS holds one), and
+// first) onto the device's compute units, one at a time each (the LDS holds one), and
 // cost a start-up (Q load, first tile round trip, partial write) plus their
 // tiles; splitting a query block adds MERGE_COST per split workgroup and the
 // merge kernel's MERGE_LAUNCH.  Per-variant costs: 128-query blocks start up
@@ -570,7 +570,6 @@ vt_pad_zero_kernel(QkvOut q, int rows) {
 // Fitted to measured kernel times at 200-8192 tokens and 2-24 local heads
 // (about 10% RMS error; the sign of the difference between the two variants
 // right at every measured shape).
-constexpr int NCU = 256;
 constexpr double MERGE_COST = 0.004;
 constexpr double MERGE_LAUNCH = 2.0;
 struct VariantCost {
@@ -580,9 +579,10 @@ struct VariantCost {
 constexpr VariantCost VAR128 = {128, 4.0, 1.0};
 constexpr VariantCost VAR256 = {256, 5.0, 1.6};
 
-double split_cost(const VariantCost& v, int nqb, int nbh, int seq, int causal, int ch) {
+double split_cost(const VariantCost& v, int nqb, int nbh, int seq, int causal, int ch,
+                  int ncu) {
   std::priority_queue<double, std::vector<double>, std::greater<double>> cu;
-  for (int k = 0; k < NCU; ++k) cu.push(0.0);
+  for (int k = 0; k < ncu; ++k) cu.push(0.0);
   double end = 0.0;
   int64_t split = 0;
   for (int qb = nqb - 1; qb >= 0; --qb) {
@@ -617,13 +617,14 @@ int64_t count_items(int qbs, int nqb, int seq, int causal, int ch) {
 // workgroups, 54 us vs 68 us).  Larger chunks are not searched: there the
 // estimate is least reliable and measured times vary by up to 40% between
 // neighbouring sizes.
-std::pair<int, double> choose_chunk(const VariantCost& v, int nqb, int nbh, int seq, int causal) {
+std::pair<int, double> choose_chunk(const VariantCost& v, int nqb, int nbh, int seq, int causal,
+                                    int ncu) {
   int64_t tiles = 0;
   for (int qb = 0; qb < nqb; ++qb) tiles += ntile_of(qb, seq, causal, v.qb);
   tiles *= nbh;
   const int64_t dflt = (tiles + 1023) / 1024;
   int best = (int)(dflt < 4 ? 4 : dflt);
-  const double base = split_cost(v, nqb, nbh, seq, causal, best);
+  const double base = split_cost(v, nqb, nbh, seq, causal, best, ncu);
   double est = base;
   const int max_nt = ntile_of(nqb - 1, seq, causal, v.qb);  // the longest key range
   if (count_items(v.qb, nqb, seq, causal, 16 < max_nt ? 16 : max_nt) * nbh <= MAX_ITEMS) {
@@ -631,7 +632,7 @@ std::pair<int, double> choose_chunk(const VariantCost& v, int nqb, int nbh, int 
     int pick = best;
     for (int ch = 1; ch <= 16 && ch <= max_nt; ++ch) {
       if (count_items(v.qb, nqb, seq, causal, ch) * nbh > MAX_ITEMS) continue;
-      const double cost = split_cost(v, nqb, nbh, seq, causal, ch);
+      const double cost = split_cost(v, nqb, nbh, seq, causal, ch, ncu);
       if (cost < best_cost * 0.999) {
         best_cost = cost;
         pick = ch;
@@ -650,8 +651,9 @@ std::pair<int, double> choose_chunk(const VariantCost& v, int nqb, int nbh, int 
 // ones have too few 256-query blocks to fill the GPU).  Memoised per shape.
 AttnSplit choose_split(int batch, int seq, int nl, int causal) {
   static std::mutex m;
-  static std::map<std::tuple<int, int, int, int>, AttnSplit> memo;
-  const auto key = std::make_tuple(batch, seq, nl, causal);
+  static std::map<std::tuple<int, int, int, int, int>, AttnSplit> memo;
+  const int ncu = device_cu_count();
+  const auto key = std::make_tuple(batch, seq, nl, causal, ncu);
   {
     std::lock_guard<std::mutex> lock(m);
     const auto it = memo.find(key);
@@ -660,8 +662,8 @@ AttnSplit choose_split(int batch, int seq, int nl, int causal) {
   AttnSplit sp;
   sp.nbh = batch * nl;
   const int nqb128 = div_up(seq, 128), nqb256 = div_up(seq, 256);
-  const auto c128 = choose_chunk(VAR128, nqb128, sp.nbh, seq, causal);
-  const auto c256 = choose_chunk(VAR256, nqb256, sp.nbh, seq, causal);
+  const auto c128 = choose_chunk(VAR128, nqb128, sp.nbh, seq, causal, ncu);
+  const auto c256 = choose_chunk(VAR256, nqb256, sp.nbh, seq, causal, ncu);
   const bool big = c256.second <= 0.97 * c128.second;
   sp.qb = big ? 256 : 128;
   sp.nqb = big ? nqb256 : nqb128;
@@ -697,7 +699,7 @@ hipError_t attention_fwd(const QkvOut& q, int batch, bool causal, uint16_t* O, i
   const AttnSplit sp = attn_split(batch, q.seq, q.nl, causal);
   const float scale_log2 = 1.4426950408889634f / sqrtf((float)q.d);
   if (q.seq_pad > q.seq) {
-    const int rows = sp.nbh * D;
+    const int64_t rows = (int64_t)sp.nbh * D;
     const int64_t n = (int64_t)rows * (q.seq_pad - q.seq);
     const int blocks = (int)((n + 255) / 256 < 4096 ? (n + 255) / 256 : 4096);
     hipLaunchKernelGGL(vt_pad_zero_kernel, dim3(blocks), dim3(256), 0, s, q, rows);

@@ -27,6 +27,8 @@
 //   * Workgroup ids are remapped so each XCD (dispatch is round-robin over
 //     the 8 XCDs) receives a contiguous run of tiles, ordered in groups of 8
 //     tile-rows so neighbouring tiles share A and B panels in that XCD's L2.
+#include <atomic>
+
 #include "internal.h"
 
 namespace tp {
@@ -897,7 +899,7 @@ gemm_bf16_pp_kernel(const uint16_t* __restrict__ A, int64_t lda,
 }
 
 // Tile configurations.  The choice minimises the estimated time: full
-// 256-CU waves of tiles times the tile's cost, the larger tiles being
+// waves of tiles over the device's compute units times the tile's cost, the larger tiles being
 // cheaper per element (less LDS and L2 traffic per MFMA).
 struct TileChoice {
   int bm, bn;
@@ -906,12 +908,13 @@ struct TileChoice {
 TileChoice choose_bf16_tile(int M, int N) {
   const TileChoice cand[4] = {{256, 256}, {256, 128}, {128, 192}, {128, 128}};
   const double eff[4] = {1.0, 0.95, 0.80, 0.70};
+  const int64_t ncu = device_cu_count();
   int best = 0;
   double best_cost = 1e300;
   for (int c = 0; c < 4; ++c) {
     const int64_t tiles = (int64_t)((M + cand[c].bm - 1) / cand[c].bm) *
                           ((N + cand[c].bn - 1) / cand[c].bn);
-    const double waves = (double)((tiles + 255) / 256);
+    const double waves = (double)((tiles + ncu - 1) / ncu);
     const double cost = waves * cand[c].bm * cand[c].bn / eff[c];
     if (cost < best_cost * 0.999) {
       best_cost = cost;
@@ -1054,6 +1057,25 @@ hipError_t launch_f32(const float* A, int64_t lda, const float* B, int64_t ldb,
 }
 
 }  // namespace
+
+int device_cu_count() {
+  constexpr int kMaxDev = 64;
+  static std::atomic<int> cached[kMaxDev];  // 0: not yet queried
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDev) {
+    (void)hipGetLastError();
+    return 256;
+  }
+  int n = cached[dev].load(std::memory_order_relaxed);
+  if (n > 0) return n;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+      n <= 0) {
+    (void)hipGetLastError();
+    n = 256;
+  }
+  cached[dev].store(n, std::memory_order_relaxed);
+  return n;
+}
 
 int gemm_bf16_a_block(int M, int N) { return a_block(choose_bf16_tile(M, N)); }
 

@@ -7,6 +7,11 @@
 
 namespace tp {
 
+// Compute units of the current device (hipDeviceAttributeMultiprocessorCount,
+// cached per device); 256 (a full MI355X) when no device can be queried.
+// The tile and work-split choices size their waves of workgroups by it.
+int device_cu_count();
+
 // Output element type of a GEMM epilogue.
 enum OutType { OUT_F32 = 0, OUT_BF16 = 1 };
 

@@ -179,8 +179,10 @@ hipError_t launch_c(const ReducePtrs& ptrs, int t, const void* R, void* out,
   // One 8-element group per thread (measured on MI355X with inputs rotated
   // through more memory than the caches hold: t=8 bf16 [4096,4096] 5.9 TB/s
   // vs 5.7 TB/s for a grid capped at 4096 looping blocks).
+  // The grid-stride loop covers what a grid of at most 2^24 - 1 blocks
+  // (below the 2^32 work-items a dispatch may hold) does not.
   int64_t blocks = (ngroups + 255) / 256;
-  if (blocks > (int64_t)1 << 30) blocks = (int64_t)1 << 30;
+  if (blocks > ((int64_t)1 << 24) - 1) blocks = ((int64_t)1 << 24) - 1;
   if (blocks < 1) blocks = 1;
   hipLaunchKernelGGL((reduce_kernel<PDT, RDT, ODT, C>), dim3((unsigned)blocks),
                      dim3(256), 0, s, ptrs, t, R, out, ngroups, (int)(n - ngroups * 8));

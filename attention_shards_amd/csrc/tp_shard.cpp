@@ -2,9 +2,11 @@
 // sequencing for one GPU's share of a tensor-parallel transformer sub-layer
 // (page "Tensor Parallelism > Combining Column and Row Parallelism").
 //
-// Every check runs before the first HIP call, so a rejected call enqueues
-// nothing and touches no device state; this file's only HIP calls are the
-// kernel launches (through the tp:: launchers) and error queries.
+// Every check runs before the first kernel launch, so a rejected call
+// enqueues nothing and changes no device state; besides the launches
+// (through the tp:: launchers) and error queries, the only HIP calls are
+// reads of the current device and its compute-unit count, which the
+// attention work split (and so its workspace size) depends on.
 #include <hip/hip_runtime.h>
 
 #include <cstdarg>
@@ -183,7 +185,9 @@ tp_status_t check_ffn(const char* fn, const void* X, const void* W1_i, const voi
   const Range rw1 = range_of(W1_i, span_bytes(hidden, fs, *ld_w1, es));
   const Range rw2 = range_of(W2_i, fs * hidden * es);
   const Range ry = range_of(out, out_bytes);
-  const Range rws = range_of(workspace, tokens * fs * es);
+  // the extent GEMM1 writes: with bf16 inputs GeLU(Z_i) is K-blocked over
+  // ffn/t rounded up to 64 columns, which the size query covers
+  const Range rws = range_of(workspace, (int64_t)need);
   if (overlap(ry, rx) || overlap(ry, rw1) || overlap(ry, rw2) || overlap(ry, rws))
     return fail(TP_ERR_ALIAS, "%s(i=%d): the output overlaps an input or the workspace", fn, i);
   if (overlap(rws, rx) || overlap(rws, rw1) || overlap(rws, rw2))

@@ -31,17 +31,20 @@ def layer_forward(X, Wqkv, Wo, W1, W2, batch: int, seq: int, n_heads: int,
     M, h = X.shape
     dev = X.device
     pdt = ffn_partial_dtype or torch.float32
-    attn = [torch.empty(M, h, device=dev, dtype=torch.float32) for _ in range(t)]
-    for i in range(t):
-        B.tp_attn_shard(X, Wqkv[i], Wo[i], attn[i], batch, seq, n_heads, head_dim, i, t,
-                        causal, stream=stream)
-    X1 = torch.empty(M, h, device=dev, dtype=torch.float32)
-    B.tp_partial_reduce(attn, X, X1, stream=stream)
-    X1b = torch.empty(M, h, device=dev, dtype=torch.bfloat16)
-    B.tp_partial_reduce([X1], None, X1b, stream=stream)
-    ffn = [torch.empty(M, h, device=dev, dtype=pdt) for _ in range(t)]
-    for i in range(t):
-        B.tp_ffn_shard(X1b, W1[i], W2[i], ffn[i], i, t, stream=stream)
-    X2 = torch.empty(M, h, device=dev, dtype=torch.float32)
-    B.tp_partial_reduce(ffn, X1, X2, stream=stream)
+    s = B._stream_of(stream, dev)
+    # every tensor below is allocated, used and freed in the order of `s`
+    with torch.cuda.device(dev), torch.cuda.stream(s):
+        attn = [torch.empty(M, h, device=dev, dtype=torch.float32) for _ in range(t)]
+        for i in range(t):
+            B.tp_attn_shard(X, Wqkv[i], Wo[i], attn[i], batch, seq, n_heads, head_dim, i, t,
+                            causal, stream=s)
+        X1 = torch.empty(M, h, device=dev, dtype=torch.float32)
+        B.tp_partial_reduce(attn, X, X1, stream=s)
+        X1b = torch.empty(M, h, device=dev, dtype=torch.bfloat16)
+        B.tp_partial_reduce([X1], None, X1b, stream=s)
+        ffn = [torch.empty(M, h, device=dev, dtype=pdt) for _ in range(t)]
+        for i in range(t):
+            B.tp_ffn_shard(X1b, W1[i], W2[i], ffn[i], i, t, stream=s)
+        X2 = torch.empty(M, h, device=dev, dtype=torch.float32)
+        B.tp_partial_reduce(ffn, X1, X2, stream=s)
     return X1, X2

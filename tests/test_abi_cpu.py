@@ -16,8 +16,12 @@ from attention_shards_amd import binding as B
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "tp_shard.h")
 
-pytestmark = pytest.mark.skipif(not os.path.exists(B.LIB_PATH),
-                                reason="libtpshard.so not built")
+
+
+def test_library_is_built():
+    """The library must exist: a missing build fails here instead of
+    leaving the rest of this file unrun."""
+    assert os.path.exists(B.LIB_PATH), f"{B.LIB_PATH} is not built"
 
 
 def header_text():
@@ -126,6 +130,19 @@ def test_ffn_rejects(lib, kw, code):
     st, msg = ffn(lib, **kw)
     assert B.STATUS[st] == code, msg
     assert msg
+
+
+def test_ffn_output_in_the_padded_workspace_tail_is_an_alias(lib):
+    """bf16 GeLU(Z_i) is written K-blocked over ffn/t rounded up to 64
+    columns: with ffn/t = 72 the workspace extent is tokens x 128 columns,
+    so an output placed just past tokens x 72 columns still overlaps it."""
+    tokens, fs = 64, 72
+    need = lib.tp_ffn_shard_workspace_bytes(tokens, 64, 2 * fs, 2, B.TP_BF16)
+    assert need == tokens * 128 * 2
+    st, msg = ffn(lib, ffn=2 * fs, Y=WS + tokens * fs * 2)
+    assert B.STATUS[st] == "TP_ERR_ALIAS", msg
+    st, msg = ffn(lib, ffn=2 * fs, Y=WS + need, tokens=0)
+    assert st == 0, msg
 
 
 def test_ffn_error_message_names_shard(lib):
