@@ -243,3 +243,101 @@ def test_bf16_output_is_rne_of_fp32_output(gpu, M, h, f, t, i, seed):
     y16 = run_shard(gpu, d, i, t, syn.BF16)
     host = syn.bf16_bits_to_f32(syn.f32_to_bf16_bits(y32))
     assert np.array_equal(y16.astype(np.float32).view(np.uint32), host.view(np.uint32))
+
+
+def _bf16_grid(lo_mag: float, hi_mag: float) -> np.ndarray:
+    """Every bf16 value with lo_mag <= |v| <= hi_mag, both signs, as bits."""
+    bits = np.arange(1 << 15, dtype=np.uint32)
+    v = (bits << 16).view(np.float32)
+    keep = bits[(np.abs(v) >= lo_mag) & (np.abs(v) <= hi_mag) & np.isfinite(v)]
+    return np.concatenate([keep, keep | 0x8000]).astype(np.uint16)
+
+
+def test_gelu_epilogue_identity_weights_bf16(gpu):
+    """With h = ffn, t = 1 and W1 = W2 = I the shard returns GeLU(X) itself
+    (every product is one exact term plus zeros): the GeLU the GEMM epilogue
+    applies, rounded to bf16 between the products, element by element.  X
+    holds every bf16 value with 1e-30 <= |z| <= 12, and 0.  Each output must
+    be within one bf16 ulp of the oracle's GeLU rounded to nearest even."""
+    h = 1024
+    vals = np.concatenate([_bf16_grid(1e-30, 12.0), np.array([0], np.uint16)])
+    M = (len(vals) + h - 1) // h
+    X = np.zeros(M * h, np.uint16)
+    X[:len(vals)] = vals
+    X = X.reshape(M, h)
+    eye = syn.f32_to_bf16_bits(np.eye(h, dtype=np.float32))
+    Y = empty((M, h), syn.F32)
+    gpu.tp_ffn_shard(to_dev(X, syn.BF16), to_dev(eye, syn.BF16), to_dev(eye, syn.BF16), Y, 0, 1)
+    torch.cuda.synchronize()
+    got = from_dev(Y).astype(np.float32)
+    z = syn.to_f64(X, syn.BF16)
+    want = syn.bf16_bits_to_f32(syn.f32_to_bf16_bits(oracle.gelu(z).astype(np.float32)))
+    # bf16 values of one sign are ordered like their bit patterns
+    gb = got.view(np.uint32).astype(np.int64) >> 16
+    wb = want.view(np.uint32).astype(np.int64) >> 16
+    same_sign = (np.signbit(got) == np.signbit(want)) | (got == 0) | (want == 0)
+    ulps = np.where(same_sign, np.abs(gb - wb), 1 << 20)
+    zero = want == 0
+    ulps[zero] = np.where(got[zero] == 0, 0, 1 << 20)
+    k = int(np.argmax(ulps))
+    log(f"GeLU bf16 over {len(vals)} values: max {ulps.max()} bf16 ulp "
+        f"(at z={z.flat[k]:.6g}: got {got.flat[k]:.6g}, want {want.flat[k]:.6g})")
+    assert not np.isnan(got).any()
+    assert ulps.max() <= 1
+
+
+def test_gelu_epilogue_identity_weights_fp32(gpu):
+    """The fp32 path (GeLU(Z) kept in fp32 between the products) with
+    identity weights returns the epilogue's GeLU in fp32: every bf16-grid
+    value of [-12, 12] down to 1e-30, 0, and a dense fp32 grid of [-12, 12].
+    Bound: |error| <= 3.2e-7 |z| + 2 ulp of the exact value."""
+    h = 1024
+    grid = syn.bf16_bits_to_f32(_bf16_grid(1e-30, 12.0))
+    dense = np.linspace(-12.0, 12.0, 200001, dtype=np.float32)
+    vals = np.concatenate([grid, dense, np.array([0.0], np.float32)])
+    M = (len(vals) + h - 1) // h
+    X = np.zeros(M * h, np.float32)
+    X[:len(vals)] = vals
+    X = X.reshape(M, h)
+    eye = np.eye(h, dtype=np.float32)
+    Y = empty((M, h), syn.F32)
+    gpu.tp_ffn_shard(to_dev(X, syn.F32), to_dev(eye, syn.F32), to_dev(eye, syn.F32), Y, 0, 1)
+    torch.cuda.synchronize()
+    got = from_dev(Y)
+    z = X.astype(np.float64)
+    want = oracle.gelu(z)
+    ulp = np.spacing(np.abs(want).astype(np.float32)).astype(np.float64)
+    bound = 3.2e-7 * np.abs(z) + 2 * ulp
+    err = np.abs(got - want)
+    k = int(np.argmax(err / bound))
+    log(f"GeLU fp32 over {X.size} values: max error / bound {(err / bound).max():.3f} "
+        f"(z={z.flat[k]:.6g}); max |error|/|z| "
+        f"{np.max(err[z != 0] / np.abs(z[z != 0])):.3e}")
+    assert np.all(err <= bound)
+
+
+def test_non_current_stream_matches_default(gpu):
+    """A call enqueued on a stream that is not the current one, with the
+    workspace allocated by the binding, gives the default-stream result bit
+    for bit (the workspace lives in that stream's order, so work queued on
+    the current stream meanwhile cannot reuse its memory)."""
+    d = syn.make_ffn_inputs(31, 1000, 1024, 4096, syn.BF16)
+    ref = run_shard(gpu, d, 1, 2, syn.F32)
+    cols = syn.column_slice(4096, 1, 2)
+    X = to_dev(d["X"], syn.BF16)
+    W1_i = to_dev(np.ascontiguousarray(d["W1"][:, cols]), syn.BF16)
+    W2_i = to_dev(np.ascontiguousarray(d["W2"][cols, :]), syn.BF16)
+    outs = []
+    for handle in (False, True):
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        Y = empty((1000, 1024), syn.F32)
+        torch.cuda._sleep(5_000_000)   # hold the current stream behind the side one's work
+        gpu.tp_ffn_shard(X, W1_i, W2_i, Y, 1, 2, stream=side.cuda_stream if handle else side)
+        junk = torch.full((1000 * 2048 * 2,), 255, dtype=torch.uint8, device="cuda")
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        outs.append(from_dev(Y))
+        del junk
+    for o in outs:
+        assert np.array_equal(o, ref)
