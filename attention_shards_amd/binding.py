@@ -46,6 +46,8 @@ SIGNATURES = {
     "tp_ffn_shard_reduce": (_c_i32, [_c_p, _c_p, _c_p, ctypes.POINTER(_c_p), _c_p, _c_p,
                                      _c_i64, _c_i64, _c_i64, _c_i32, _c_i32, _c_i64, _c_i32,
                                      _c_i32, _c_i32, _c_i32, _c_p, _c_sz, _c_p]),
+    "tp_ffn_shard_noalloc": (_c_i32, [_c_p, _c_p, _c_p, _c_p, _c_i64, _c_i64, _c_i64,
+                                      _c_i32, _c_i32, _c_i64, _c_i32, _c_i32, _c_p]),
     "tp_status_string": (ctypes.c_char_p, [_c_i32]),
     "tp_last_error_message": (ctypes.c_char_p, []),
     "tp_abi_version": (_c_i32, []),
@@ -187,6 +189,39 @@ def tp_ffn_shard(X, W1_i, W2_i, Y_i, i: int, t: int, workspace=None,
                                 Y_i.data_ptr(), tokens, hidden, ffn, i, t,
                                 W1_i.stride(0), in_dt, _dtype_code(Y_i),
                                 ws.data_ptr(), ws.numel(), s.cuda_stream))
+    return Y_i
+
+
+TP_FFN_NOALLOC_MAX_WORKSPACE = 64 << 20
+
+
+def tp_ffn_shard_noalloc(X, W1_i, W2_i, Y_i, i: int, t: int, stream=None):
+    """Y_i = GeLU(X W1_i) W2_i through tp_ffn_shard_noalloc: no workspace,
+    nothing allocated (GeLU(Z_i) lives in the library's own device array of
+    TP_FFN_NOALLOC_MAX_WORKSPACE bytes).  Returns Y_i."""
+    lib = load()
+    _dense(X, "X")
+    _dense(W2_i, "W2_i")
+    _dense(Y_i, "Y_i")
+    _dev(W1_i, "W1_i")
+    if W1_i.dim() != 2 or W1_i.stride(1) != 1:
+        raise ValueError("W1_i must be 2-D with unit column stride")
+    tokens, hidden = X.shape
+    fs = W1_i.shape[1]
+    if W1_i.shape[0] != hidden or tuple(W2_i.shape) != (fs, hidden) or \
+            tuple(Y_i.shape) != (tokens, hidden):
+        raise ValueError(f"shape mismatch: X{tuple(X.shape)} W1_i{tuple(W1_i.shape)} "
+                         f"W2_i{tuple(W2_i.shape)} Y_i{tuple(Y_i.shape)}")
+    in_dt = _dtype_code(X)
+    if _dtype_code(W1_i) != in_dt or _dtype_code(W2_i) != in_dt:
+        raise TypeError("X, W1_i and W2_i must share a dtype")
+    torch = _torch()
+    s = _stream_of(stream, X.device)
+    with torch.cuda.device(X.device):
+        _check(lib.tp_ffn_shard_noalloc(X.data_ptr(), W1_i.data_ptr(), W2_i.data_ptr(),
+                                        Y_i.data_ptr(), tokens, hidden, fs * t, i, t,
+                                        W1_i.stride(0), in_dt, _dtype_code(Y_i),
+                                        s.cuda_stream))
     return Y_i
 
 

@@ -19,7 +19,7 @@ CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libtpshard.so")
 
-SOURCES = ["gemm.hip", "attention.hip", "reduce.hip", "tp_shard.cpp"]
+SOURCES = ["gemm.hip", "attention.hip", "reduce.hip", "tp_shard.cpp", "ffn_noalloc.hip"]
 
 # -packed-fp32-ops: no v_pk_{add,mul,fma}_f32 in generated code.
 COMMON = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-Wno-inline-asm",

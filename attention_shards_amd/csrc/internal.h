@@ -5,6 +5,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "../../include/tp_shard.h"
+
 namespace tp {
 
 // Compute units of the current device (hipDeviceAttributeMultiprocessorCount,
@@ -110,5 +112,14 @@ hipError_t gemm_bf16_add_kb(const uint16_t* A, int kb, const uint16_t* B, int64_
 hipError_t gemm_f32_add(const float* A, int64_t lda, const float* B, int64_t ldb,
                         const float* S, void* C, int64_t ldc, OutType out, int M, int N,
                         int K, hipStream_t s);
+
+// The argument checks of tp_ffn_shard without the workspace ones (for an
+// entry point that supplies its own memory); sets the error message.
+tp_status_t ffn_check_args(const char* fn, const void* X, const void* W1_i, const void* W2_i,
+                           const void* Y_i, int64_t tokens, int64_t hidden, int64_t ffn,
+                           int32_t i, int32_t t, int64_t ld_w1, int32_t in_dtype,
+                           int32_t out_dtype);
+// Records `msg` as the thread's last error and returns st.
+tp_status_t set_error(tp_status_t st, const char* msg);
 
 }  // namespace tp

@@ -139,11 +139,13 @@ namespace {
 // Checks shared by tp_ffn_shard and tp_ffn_shard_reduce, in the order the
 // ABI documents them.  On success *fs_out = ffn/t and *ld_w1 is resolved.
 // `out` / `out_bytes` is the output tensor checked against the inputs.
+// With check_ws false the workspace checks (NULL, alignment, size, overlap)
+// are skipped: the argument checks of a caller that brings its own memory.
 tp_status_t check_ffn(const char* fn, const void* X, const void* W1_i, const void* W2_i,
                       const void* out, int64_t out_bytes, int64_t tokens, int64_t hidden,
                       int64_t ffn, int32_t i, int32_t t, int64_t* ld_w1, int32_t in_dtype,
                       int32_t out_dtype, const void* workspace, size_t workspace_bytes,
-                      int64_t* fs_out) {
+                      int64_t* fs_out, bool check_ws = true) {
   if (!valid_dtype(in_dtype) || !valid_dtype(out_dtype))
     return fail(TP_ERR_DTYPE, "%s: dtype codes in=%d out=%d", fn, in_dtype, out_dtype);
   if (t < 1 || i < 0 || i >= t) return fail(TP_ERR_SHARD, "%s: shard i=%d of t=%d", fn, i, t);
@@ -173,18 +175,23 @@ tp_status_t check_ffn(const char* fn, const void* X, const void* W1_i, const voi
   if (tokens == 0) return ok();
   if (!X || !W1_i || !W2_i || !out)
     return fail(TP_ERR_NULL, "%s(i=%d): NULL tensor pointer", fn, i);
-  if (!workspace) return fail(TP_ERR_WORKSPACE, "%s(i=%d): NULL workspace", fn, i);
+  if (check_ws && !workspace) return fail(TP_ERR_WORKSPACE, "%s(i=%d): NULL workspace", fn, i);
   if (!aligned16(X) || !aligned16(W1_i) || !aligned16(W2_i) || !aligned16(out) ||
-      !aligned16(workspace))
+      (check_ws && !aligned16(workspace)))
     return fail(TP_ERR_ALIGNMENT, "%s(i=%d): pointers must be 16-byte aligned", fn, i);
   const size_t need = tp_ffn_shard_workspace_bytes(tokens, hidden, ffn, t, in_dtype);
-  if (workspace_bytes < need)
+  if (check_ws && workspace_bytes < need)
     return fail(TP_ERR_WORKSPACE, "%s(i=%d): workspace %zu bytes < %zu needed", fn, i,
                 workspace_bytes, need);
   const Range rx = range_of(X, tokens * hidden * es);
   const Range rw1 = range_of(W1_i, span_bytes(hidden, fs, *ld_w1, es));
   const Range rw2 = range_of(W2_i, fs * hidden * es);
   const Range ry = range_of(out, out_bytes);
+  if (!check_ws) {
+    if (overlap(ry, rx) || overlap(ry, rw1) || overlap(ry, rw2))
+      return fail(TP_ERR_ALIAS, "%s(i=%d): the output overlaps an input", fn, i);
+    return ok();
+  }
   // the extent GEMM1 writes: with bf16 inputs GeLU(Z_i) is K-blocked over
   // ffn/t rounded up to 64 columns, which the size query covers
   const Range rws = range_of(workspace, (int64_t)need);
@@ -194,6 +201,30 @@ tp_status_t check_ffn(const char* fn, const void* X, const void* W1_i, const voi
     return fail(TP_ERR_ALIAS, "%s(i=%d): workspace overlaps an input", fn, i);
   return ok();
 }
+
+}  // namespace
+
+namespace tp {
+
+tp_status_t ffn_check_args(const char* fn, const void* X, const void* W1_i, const void* W2_i,
+                           const void* Y_i, int64_t tokens, int64_t hidden, int64_t ffn,
+                           int32_t i, int32_t t, int64_t ld_w1, int32_t in_dtype,
+                           int32_t out_dtype) {
+  try {
+    int64_t fs = 0;
+    return check_ffn(fn, X, W1_i, W2_i, Y_i,
+                     valid_dtype(out_dtype) ? tokens * hidden * esize(out_dtype) : 0, tokens,
+                     hidden, ffn, i, t, &ld_w1, in_dtype, out_dtype, nullptr, 0, &fs, false);
+  } catch (...) {
+    return fail(TP_ERR_HIP, "%s: internal exception", fn);
+  }
+}
+
+tp_status_t set_error(tp_status_t st, const char* msg) { return fail(st, "%s", msg); }
+
+}  // namespace tp
+
+namespace {
 
 // One side stream and two events per device for the fused FFN + reduce: the
 // sum of the other operands runs on the side stream while GEMM1 runs on the

@@ -118,6 +118,34 @@ tp_status_t tp_ffn_shard(const void* X, const void* W1_i, const void* W2_i,
                          size_t workspace_bytes, void* stream);
 
 /* ------------------------------------------------------------------------
+ * FFN shard without allocation, for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc).
+ * ------------------------------------------------------------------------
+ * The same computation and kernels as tp_ffn_shard (bit-identical results),
+ * with no workspace argument: GeLU(Z_i) lives in a file-scope device array
+ * of TP_FFN_NOALLOC_MAX_WORKSPACE bytes inside the library, one per GPU,
+ * held from the library's first use on that GPU until the process ends.
+ * The call allocates nothing (no hipMalloc, no allocating library routine).
+ *   - Shapes whose tp_ffn_shard_workspace_bytes(...) exceeds
+ *     TP_FFN_NOALLOC_MAX_WORKSPACE are rejected with TP_ERR_WORKSPACE.
+ *   - Every other rule and status is tp_ffn_shard's; the first call on a
+ *     device also looks up the array's device address (a failure there is
+ *     TP_ERR_HIP).  A rejected call enqueues nothing.
+ *   - Every call on one GPU shares that GPU's array, which keeps the last
+ *     call's contents (nothing in it needs to start at zero: GeLU(Z_i) is
+ *     written in full before it is read).  Calls that overlap in time on
+ *     one GPU (different streams or host threads without ordering) race on
+ *     it: order them on one stream.
+ */
+#define TP_FFN_NOALLOC_MAX_WORKSPACE ((size_t)64 << 20)
+
+tp_status_t tp_ffn_shard_noalloc(const void* X, const void* W1_i, const void* W2_i,
+                                 void* Y_i, int64_t tokens, int64_t hidden, int64_t ffn,
+                                 int32_t i, int32_t t, int64_t ld_w1, int32_t in_dtype,
+                                 int32_t out_dtype, void* stream);
+
+/* ------------------------------------------------------------------------
  * Attention shard (QKV column-parallel by heads, per-head attention,
  * row-parallel output projection).
  * ------------------------------------------------------------------------

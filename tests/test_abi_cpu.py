@@ -327,3 +327,43 @@ def test_ffn_reduce_small_workspace(lib):
 def test_ffn_reduce_zero_tokens_is_a_no_op(lib):
     st, msg = ffn_reduce(lib, tokens=0, X=None, out=None, ws=None, peers=None)
     assert st == 0, msg
+
+
+def noalloc(lib, **kw):
+    a = dict(X=X, W1=W1, W2=W2, Y=Y, tokens=64, hidden=64, ffn=256, i=0, t=2,
+             ld=0, din=B.TP_BF16, dout=B.TP_BF16)
+    a.update(kw)
+    st = lib.tp_ffn_shard_noalloc(a["X"], a["W1"], a["W2"], a["Y"], a["tokens"], a["hidden"],
+                                  a["ffn"], a["i"], a["t"], a["ld"], a["din"], a["dout"], None)
+    return st, lib.tp_last_error_message().decode()
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(din=7), "TP_ERR_DTYPE"),
+    (dict(i=2), "TP_ERR_SHARD"),
+    (dict(ffn=255), "TP_ERR_DIVISIBILITY"),
+    (dict(hidden=60), "TP_ERR_SHAPE"),
+    (dict(X=None), "TP_ERR_NULL"),
+    (dict(W2=W2 + 8), "TP_ERR_ALIGNMENT"),
+    (dict(Y=X + 64), "TP_ERR_ALIAS"),
+    # GeLU(Z_i) of 8192 x 8192 bf16 = 128 MiB, above the 64 MiB array
+    (dict(tokens=8192, ffn=8192, t=1), "TP_ERR_WORKSPACE"),
+])
+def test_ffn_noalloc_rejects_before_any_hip_call(lib, kw, code):
+    st, msg = noalloc(lib, **kw)
+    assert B.STATUS[st] == code, msg
+    assert msg
+
+
+def test_ffn_noalloc_limit_matches_header(lib):
+    m = re.search(r"#define TP_FFN_NOALLOC_MAX_WORKSPACE \(\(size_t\)(\d+) << (\d+)\)",
+                  header_text())
+    assert int(m.group(1)) << int(m.group(2)) == B.TP_FFN_NOALLOC_MAX_WORKSPACE
+    # the largest shape that fits: 2048 tokens x 16384 bf16 columns = 64 MiB
+    assert lib.tp_ffn_shard_workspace_bytes(2048, 64, 16384, 1, B.TP_BF16) == \
+        B.TP_FFN_NOALLOC_MAX_WORKSPACE
+
+
+def test_ffn_noalloc_zero_tokens_is_a_no_op(lib):
+    st, msg = noalloc(lib, tokens=0, X=None, Y=None)
+    assert st == 0, msg
