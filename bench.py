@@ -2,29 +2,42 @@
 """Throughput of one GPU's share of a tensor-parallel FFN sub-layer on MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
-                    [--sweep OUT.jsonl]
-    python bench.py --summarize-{profiles,attn-profile,counters,sweep} ...
-                    (write profiles/*.md from rocprofv3 output or a sweep)
+                    [--headline-only] [--reduce-only] [--copy-calibration]
+    python bench.py --summarize-{profiles,reduce-traffic,attn-profile,counters,sweep} ...
+                    (write profiles/*.md from rocprofv3 output)
 
-Workload (one "step"): FFN shard i=3 of t=8 at hidden 4096, ffn 16384,
-4096 tokens (2 sequences of 2048), bf16 inputs with fp32 accumulation:
-  1. tp_ffn_shard: Z_3 = X W1_3 (W1_3 a zero-copy column view of the full W1),
-     GeLU in the epilogue, Y_3 = GeLU(Z_3) W2_3 -> bf16 partial;
-  2. tp_partial_reduce: out = sum of the 8 partials + residual (fp32 out).
-     The other seven partials are the other shards' results, computed once
-     before timing: they stand for what the peers would contribute.
-value = algorithmic FFN FLOPs of the shard (4*M*h*f/t) / wall time per step.
-Every timed row starts after about 0.1 s of the same work, untimed, so that
-the GPU has left its idle clock state, then W warmup steps.
+Headline workload (one "step"): the FFN shard of the hidden-size sweep's
+largest point, t=1 (the TP:1 end of the throughput-vs-hidden-size chart):
+hidden 22528, ffn 90112, 2048 tokens, shard 0 of 1, bf16 inputs from the
+seeded generator (seed 311: X ~ N(0,1), W1, W2 ~ N(0, 0.02^2)), fp32
+accumulation, fp32 output:
+    tp_ffn_shard: Z = X W1, GeLU in the epilogue, Y = GeLU(Z) W2.
+value = algorithmic FFN FLOPs of the shard (4*M*h*f/t) / median time of one
+call (HIP events on the stream the call is launched on).  Every timed row
+starts after about 0.1 s of the same work, untimed, so that the GPU has left
+its idle clock state, then W warmup calls.
 
-The same run also times, under "rows": the reduce-scatter block shard i
-would own (tp_partial_reduce_slice; rows.partial_reduce_slice), the step
-with the sum fused into the second GEMM's epilogue (tp_ffn_shard_reduce;
-rows.ffn_shard_reduce_fused), the attention shard (t=8, 8 of 64 heads of
-128, hidden 8192, 2048 tokens, causal; rows.attn_shard) and a whole layer
-of four shards on this GPU (hidden 12288, 96 heads, 8192 tokens;
-rows.layer).  On rank 0 at N=1 it also times the fp64 CPU oracle on a
-bounded sample of the FFN workload ("cpu_baseline").  Prints ONE JSON line.
+The same run times, under "rows":
+  * sweep: all 44 points of hidden 2048..22528 x t in {1,2,4,8} (2048
+    tokens, shard 0, device-seeded inputs), each next to the same shard
+    through torch (hipBLASLt GEMMs and a separate exact-erf GeLU kernel);
+  * ffn_step_h4096_t8: the FFN sub-layer of shard 3 of 8 at hidden 4096,
+    ffn 16384, 4096 tokens, bf16 partial, then the reduce of the 8 partials
+    plus the residual (fp32 out); the other seven partials are computed once
+    before timing and stand for what the peers would contribute;
+  * partial_reduce_t8_h4096 / partial_reduce_t4_h12288: the reduce alone at
+    those two shapes with the calls rotating over 3 buffer sets of 369 MB /
+    1.41 GB each (more than the 256 MB Infinity Cache), so it reads HBM;
+  * partial_reduce_slice: one row block of the t=8 reduce (the
+    reduce-scatter half), blocks rotating;
+  * ffn_shard_reduce_fused: the t=8 step with the sum fused into the second
+    GEMM's epilogue, and the same comparison at the t=4 hidden-12288 shape;
+  * attn_shard: the attention shard (t=8, 8 of 64 heads of 128, hidden
+    8192, 2048 tokens, causal);
+  * layer: a whole layer of four shards on this GPU (hidden 12288, 96 heads,
+    8192 tokens).
+On rank 0 at N=1 it also times the fp64 CPU oracle on a bounded sample of the
+headline workload ("cpu_baseline").  Prints ONE JSON line.
 """
 from __future__ import annotations
 
@@ -32,6 +45,7 @@ import argparse
 import hashlib
 import json
 import os
+import statistics
 import sys
 import time
 
@@ -41,10 +55,19 @@ sys.path.insert(0, ROOT)
 PEAK_BF16_TFLOPS = 2516.6     # MI355X dense bf16 MFMA (256 CU x 2.4 GHz x 4096 FLOP/clk)
 PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
 METRIC = "TP-shard FFN TFLOP/s vs hidden size (bf16, 1 GPU); % of MFMA peak"
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_ffn_shard_h4096_t8.json")
 
+HEADLINE = dict(tokens=2048, hidden=22528, ffn=4 * 22528, t=1, i=0, seed=300 + 22528 // 2048)
 FFN = dict(tokens=4096, hidden=4096, ffn=16384, t=8, i=3, seed=2)
 ATTN = dict(batch=1, seq=2048, hidden=8192, n_heads=64, head_dim=128, t=8, i=0, seed=4)
+SWEEP_HIDDEN = list(range(2048, 22528 + 1, 2048))
+SWEEP_T = (1, 2, 4, 8)
+
+
+def _tag(p):
+    return f"h{p['hidden']}_t{p['t']}"
+
+
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", f"traffic_ffn_shard_{_tag(HEADLINE)}.json")
 
 
 def ffn_flops(M, h, f, t):
@@ -58,6 +81,10 @@ def attn_flops(batch, seq, hidden, n_heads, head_dim, t):
     core = 4.0 * head_dim * (S * (S + 1) / 2) * nl * batch      # causal pairs only
     out = 2.0 * batch * S * nl * head_dim * hidden
     return qkv + core + out
+
+
+def reduce_bytes(t, rows, cols, pb=2, rb=2, ob=4):
+    return (t * pb + rb + ob) * rows * cols
 
 
 def src_hash(*names):
@@ -74,8 +101,8 @@ def src_hash(*names):
 
 
 def load_traffic():
-    """HBM bytes per FFN-shard call from the committed rocprofv3 counter runs,
-    or None when the kernels changed since those counters were taken."""
+    """HBM bytes per headline FFN-shard call from the committed rocprofv3
+    counter runs, or None when the kernels changed since they were taken."""
     try:
         with open(TRAFFIC_FILE) as f:
             rec = json.load(f)
@@ -99,16 +126,18 @@ def settle(fn, seconds=0.1):
     """Run fn untimed for about `seconds` of wall time.  An idle MI355X needs
     about 10 ms of sustained work to leave its low clock state (the first 50
     FFN steps after an idle second run ~35% slower than the rest), so every
-    timed row starts from a settled clock; W warmup steps follow."""
+    timed row starts from a settled clock; W warmup calls follow."""
     import torch
     t0 = time.perf_counter()
     while time.perf_counter() - t0 < seconds:
-        for _ in range(10):
+        for _ in range(4):
             fn()
         torch.cuda.synchronize()
 
 
-def time_events(fn, steps, warmup):
+def time_calls(fn, steps, warmup):
+    """Per-call durations in ms: HIP events recorded on the current stream
+    (the stream the binding launches on) around each of `steps` calls."""
     import torch
     settle(fn)
     for _ in range(warmup):
@@ -121,7 +150,12 @@ def time_events(fn, steps, warmup):
         fn()
         b.record()
     torch.cuda.synchronize()
-    return sum(a.elapsed_time(b) for a, b in ev) / steps
+    return [a.elapsed_time(b) for a, b in ev]
+
+
+def stats(ms):
+    return {"median_ms": round(statistics.median(ms), 5), "min_ms": round(min(ms), 5),
+            "mean_ms": round(statistics.mean(ms), 5)}
 
 
 def time_batched(fn, steps, warmup):
@@ -144,71 +178,209 @@ def time_batched(fn, steps, warmup):
     return a.elapsed_time(b) / steps
 
 
+def host_info():
+    """CPU model and the cores this process may run on."""
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    try:
+        cores = len(os.sched_getaffinity(0))
+    except AttributeError:
+        cores = os.cpu_count() or 1
+    return model, cores
+
+
+def headline_inputs():
+    """The headline shard's inputs from the seeded generator (the same bytes
+    the sweep parity test checks at this point)."""
+    from attention_shards_amd import synthetic as syn
+    p = HEADLINE
+    return syn.make_ffn_inputs(p["seed"], p["tokens"], p["hidden"], p["ffn"], syn.BF16)
+
+
 def cpu_baseline(d, budget_s=12.0):
-    """fp64 oracle on a bounded row sample of the FFN shard workload."""
+    """The fp64 oracle, as it stands, on a bounded sample of the headline
+    shard: blocks of 256 token rows times the first of eight column blocks
+    of W1 (and the matching rows of W2), repeated for about `budget_s`."""
     import numpy as np
     import oracle
     from attention_shards_amd import synthetic as syn
+    model, cores = host_info()
     try:
         from threadpoolctl import threadpool_info
-        cores = max((i.get("num_threads", 1) for i in threadpool_info()), default=1)
+        blas = max((i.get("num_threads", 1) for i in threadpool_info()), default=None)
     except Exception:
-        cores = 1
-    p = FFN
-    cols = syn.column_slice(p["ffn"], p["i"], p["t"])
-    W1_i = syn.to_f64(d["W1"][:, cols], syn.BF16)
-    W2_i = syn.to_f64(d["W2"][cols, :], syn.BF16)
+        blas = None
+    p = HEADLINE
+    cols = syn.column_slice(p["ffn"], 0, 8)
+    W1b = syn.to_f64(d["W1"][:, cols], syn.BF16)
+    W2b = syn.to_f64(d["W2"][cols, :], syn.BF16)
     rows_done, block = 0, 256
     t0 = time.perf_counter()
     while time.perf_counter() - t0 < budget_s:
         r0 = rows_done % p["tokens"]
         Xb = syn.to_f64(d["X"][r0:r0 + block], syn.BF16)
-        oracle.ffn_shard(Xb, W1_i, W2_i)
+        oracle.ffn_shard(Xb, W1b, W2b)
         rows_done += Xb.shape[0]
     dt = time.perf_counter() - t0
-    fl = ffn_flops(rows_done, p["hidden"], p["ffn"], p["t"])
-    return {"value": round(fl / dt / 1e12, 5), "unit": "TFLOP/s", "cores": int(cores),
-            "kind": "oracle",
-            "sample": f"{rows_done} token rows ({rows_done / p['tokens']:.2f} passes over the "
-                      f"{p['tokens']} rows) of the FFN shard, fp64 numpy, {dt:.1f} s"}
+    fl = 4.0 * rows_done * p["hidden"] * (cols.stop - cols.start)
+    used = blas if blas else cores
+    return {"value": round(fl / dt / 1e12, 5), "unit": "TFLOP/s", "cores": int(used),
+            "kind": "oracle", "cpu_model": model, "cores_available": cores,
+            "sample": f"{rows_done} token rows (256-row blocks over the {p['tokens']}) x ffn "
+                      f"columns {cols.start}..{cols.stop - 1} of {p['ffn']} (1/8 of the shard) "
+                      f"of the hidden-{p['hidden']} t=1 FFN shard, fp64 numpy "
+                      f"({used} BLAS threads), {dt:.1f} s; extrapolated full shard "
+                      f"{ffn_flops(p['tokens'], p['hidden'], p['ffn'], 1) / (fl / dt):.0f} s"}
 
 
-def sweep(path, steps, warmup):
-    """Hidden-size sweep h = 2048..22528 step 2048, t in {1,2,4,8}, 2048 tokens.
-    Timing only (device-seeded inputs); parity of sweep points is in tests."""
+def sweep_rows(steps, warmup, with_torch=True, log=None):
+    """All 44 sweep points, timing only (device-seeded inputs; parity of
+    every point is in the tests)."""
     import torch
     from attention_shards_amd import binding as B
     g = torch.Generator(device="cuda")
-    with open(path, "w") as out:
-        for h in range(2048, 22528 + 1, 2048):
-            g.manual_seed(300 + h // 2048)
-            f = 4 * h
-            X = torch.randn(2048, h, device="cuda", generator=g).to(torch.bfloat16)
-            for t in (1, 2, 4, 8):
-                fs = f // t
-                W1 = (torch.randn(h, fs, device="cuda", generator=g) * 0.02).to(torch.bfloat16)
-                W2 = (torch.randn(fs, h, device="cuda", generator=g) * 0.02).to(torch.bfloat16)
-                Y = torch.empty(2048, h, device="cuda")
-                ws = torch.empty(B.tp_ffn_shard_workspace_bytes(2048, h, f, t, B.TP_BF16),
-                                 dtype=torch.uint8, device="cuda")
-                ms = time_events(lambda: B.tp_ffn_shard(X, W1, W2, Y, 0, t, workspace=ws),
-                                 steps, warmup)
-                tf = ffn_flops(2048, h, f, t) / (ms * 1e-3) / 1e12
-                # context: the same shard through torch (hipBLASLt GEMMs, a
-                # separate exact-erf GeLU kernel, bf16 between them)
-                tms = time_events(lambda: torch.nn.functional.gelu(X @ W1) @ W2, steps, warmup)
-                rec = {"hidden": h, "t": t, "ms": round(ms, 5), "tflops": round(tf, 2),
-                       "frac_peak": round(tf / PEAK_BF16_TFLOPS, 4),
-                       "torch_ms": round(tms, 5),
-                       "torch_tflops": round(ffn_flops(2048, h, f, t) / (tms * 1e-3) / 1e12, 2)}
-                out.write(json.dumps(rec) + "\n")
-                print(json.dumps(rec), file=sys.stderr, flush=True)
-                del W1, W2, Y, ws
-            del X
-            torch.cuda.empty_cache()
+    out = []
+    for h in SWEEP_HIDDEN:
+        g.manual_seed(300 + h // 2048)
+        f = 4 * h
+        X = torch.randn(2048, h, device="cuda", generator=g).to(torch.bfloat16)
+        W1 = (torch.randn(h, f, device="cuda", generator=g) * 0.02).to(torch.bfloat16)
+        W2 = (torch.randn(f, h, device="cuda", generator=g) * 0.02).to(torch.bfloat16)
+        Y = torch.empty(2048, h, device="cuda")
+        for t in SWEEP_T:
+            fs = f // t
+            W1_0, W2_0 = W1[:, :fs], W2[:fs]
+            ws = torch.empty(B.tp_ffn_shard_workspace_bytes(2048, h, f, t, B.TP_BF16),
+                             dtype=torch.uint8, device="cuda")
+            ms = time_calls(lambda: B.tp_ffn_shard(X, W1_0, W2_0, Y, 0, t, workspace=ws),
+                            steps, warmup)
+            fl = ffn_flops(2048, h, f, t)
+            med = statistics.median(ms)
+            rec = {"hidden": h, "t": t, **stats(ms),
+                   "tflops": round(fl / (med * 1e-3) / 1e12, 1),
+                   "frac_peak": round(fl / (med * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)}
+            if with_torch:
+                W1c = W1_0.contiguous()
+                tms = statistics.median(time_calls(
+                    lambda: torch.nn.functional.gelu(X @ W1c) @ W2_0, steps, warmup))
+                rec["torch_median_ms"] = round(tms, 5)
+                rec["torch_tflops"] = round(fl / (tms * 1e-3) / 1e12, 1)
+                del W1c
+            out.append(rec)
+            if log:
+                log(json.dumps(rec))
+            del ws
+        del X, W1, W2, Y
+        torch.cuda.empty_cache()
+    return out
 
 
-COPY_BYTES = 1 << 30
+def reduce_rotated(t, rows, cols, steps, warmup, nsets=3):
+    """tp_partial_reduce of t bf16 partials plus a bf16 residual into an fp32
+    output, the calls rotating over `nsets` buffer sets (device-generated
+    values), so every call reads its inputs from HBM, not the cache."""
+    import torch
+    from attention_shards_amd import binding as B
+    g = torch.Generator(device="cuda").manual_seed(7 + t)
+    sets = []
+    for _ in range(nsets):
+        parts = [torch.randn(rows, cols, device="cuda", generator=g).to(torch.bfloat16)
+                 for _ in range(t)]
+        R = torch.randn(rows, cols, device="cuda", generator=g).to(torch.bfloat16)
+        out = torch.empty(rows, cols, device="cuda")
+        sets.append((parts, R, out))
+    nxt = [0]
+
+    def call():
+        parts, R, out = sets[nxt[0] % nsets]
+        nxt[0] += 1
+        B.tp_partial_reduce(parts, R, out)
+
+    ms = time_calls(call, steps, warmup)
+    by = reduce_bytes(t, rows, cols)
+    med = statistics.median(ms)
+    del sets
+    torch.cuda.empty_cache()
+    return {"t": t, "rows": rows, "cols": cols, "dtypes": "bf16 partials, bf16 residual, fp32 out",
+            "buffer_sets": nsets, "bytes_per_set": by, **stats(ms), "bytes": by,
+            "gbs": round(by / (med * 1e-3) / 1e9, 1),
+            "frac_hbm_peak": round(by / (med * 1e-3) / 1e9 / PEAK_HBM_GBS, 4), "bound": "hbm"}
+
+
+def ffn_step_row(steps, warmup, fused=True):
+    """FFN shard 3 of 8 at hidden 4096 (bf16 partial) + reduce of the 8
+    partials and the residual; the fused variant; the reduce-scatter block."""
+    import torch
+    from attention_shards_amd import binding as B
+    from attention_shards_amd import synthetic as syn
+    p = FFN
+    M, h, f, t, i = p["tokens"], p["hidden"], p["ffn"], p["t"], p["i"]
+    fs = f // t
+    d = syn.make_ffn_inputs(p["seed"], M, h, f, syn.BF16, residual=True)
+    X, W1, W2, R = (dev_tensor(d[k], syn.BF16) for k in ("X", "W1", "W2", "R"))
+    del d
+    parts = [torch.empty(M, h, dtype=torch.bfloat16, device="cuda") for _ in range(t)]
+    ws = torch.empty(B.tp_ffn_shard_workspace_bytes(M, h, f, t, B.TP_BF16),
+                     dtype=torch.uint8, device="cuda")
+    out = torch.empty(M, h, dtype=torch.float32, device="cuda")
+    W1v = [W1[:, j * fs:(j + 1) * fs] for j in range(t)]
+    W2v = [W2[j * fs:(j + 1) * fs] for j in range(t)]
+    for j in range(t):                      # the peers' partials, once
+        B.tp_ffn_shard(X, W1v[j], W2v[j], parts[j], j, t, workspace=ws)
+    torch.cuda.synchronize()
+
+    def ffn():
+        B.tp_ffn_shard(X, W1v[i], W2v[i], parts[i], i, t, workspace=ws)
+
+    def red():
+        B.tp_partial_reduce(parts, R, out)
+
+    ffn_ms = time_calls(ffn, steps, warmup)
+    step_ms = time_calls(lambda: (ffn(), red()), steps, warmup)
+    fl = ffn_flops(M, h, f, t)
+    row = {"workload": "ffn_shard_t8_i3_h4096_f16384_tokens4096_plus_reduce8",
+           "ffn": {**stats(ffn_ms),
+                   "tflops": round(fl / (statistics.median(ffn_ms) * 1e-3) / 1e12, 1),
+                   "frac_peak": round(fl / (statistics.median(ffn_ms) * 1e-3) / 1e12
+                                      / PEAK_BF16_TFLOPS, 4)},
+           "step_ffn_plus_reduce": {**stats(step_ms),
+                                    "tflops": round(fl / (statistics.median(step_ms) * 1e-3)
+                                                    / 1e12, 1)}}
+    # The reduce-scatter half of the all-reduce on this GPU: one row block
+    # (rows [j*M/t, (j+1)*M/t) of every partial) per call, j rotating over the
+    # t blocks so that successive calls do not find their inputs in the
+    # Infinity Cache (one block is 46 MB; all t together 369 MB).
+    nxt = [0]
+
+    def one_slice():
+        B.tp_partial_reduce_slice(parts, R, out, nxt[0] % t, t)
+        nxt[0] += 1
+
+    slice_ms = time_batched(one_slice, steps, warmup)
+    sb = reduce_bytes(t, M // t, h)
+    row_slice = {"slices": "rotating 0..t-1", "nslices": t, "ms": round(slice_ms, 5),
+                 "bytes": sb, "gbs": round(sb / (slice_ms * 1e-3) / 1e9, 1),
+                 "frac_hbm_peak": round(sb / (slice_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}
+    fused_row = None
+    if fused:
+        peers = [None if j == i else parts[j] for j in range(t)]
+        wsf = torch.empty(B.tp_ffn_shard_reduce_workspace_bytes(M, h, f, t, B.TP_BF16),
+                          dtype=torch.uint8, device="cuda")
+        fu = time_calls(lambda: B.tp_ffn_shard_reduce(X, W1v[i], W2v[i], peers, R, out, i,
+                                                      workspace=wsf), steps, warmup)
+        fused_row = {**stats(fu), "unfused_median_ms": row["step_ffn_plus_reduce"]["median_ms"],
+                     "hbm_bytes_saved": 2 * 2 * M * h}
+        del peers, wsf
+    del parts, W1v, W2v, W1, W2, ws, out, X, R
+    torch.cuda.empty_cache()
+    return row, row_slice, fused_row
 
 
 def fused_vs_unfused_large(steps, warmup):
@@ -235,15 +407,45 @@ def fused_vs_unfused_large(steps, warmup):
         B.tp_partial_reduce(parts, R, out)
 
     peers = [None if j == i else parts[j] for j in range(t)]
-    un_ms = time_events(unfused, steps, warmup)
-    fu_ms = time_events(lambda: B.tp_ffn_shard_reduce(X, W1, W2, peers, R, out, i, workspace=ws),
-                        steps, warmup)
+    un = statistics.median(time_calls(unfused, steps, warmup))
+    fu = statistics.median(time_calls(
+        lambda: B.tp_ffn_shard_reduce(X, W1, W2, peers, R, out, i, workspace=ws), steps, warmup))
     fl = ffn_flops(M, h, f, t)
     del X, W1, W2, R, parts, peers, out, ws
     torch.cuda.empty_cache()
-    return {"workload": "t4_i0_h12288_f49152_tokens8192", "unfused_ms": round(un_ms, 4),
-            "fused_ms": round(fu_ms, 4), "unfused_tflops": round(fl / (un_ms * 1e-3) / 1e12, 1),
-            "fused_tflops": round(fl / (fu_ms * 1e-3) / 1e12, 1)}
+    return {"workload": "t4_i0_h12288_f49152_tokens8192", "unfused_median_ms": round(un, 4),
+            "fused_median_ms": round(fu, 4), "unfused_tflops": round(fl / (un * 1e-3) / 1e12, 1),
+            "fused_tflops": round(fl / (fu * 1e-3) / 1e12, 1)}
+
+
+def attn_row(steps, warmup):
+    import numpy as np
+    import torch
+    from attention_shards_amd import binding as B
+    from attention_shards_amd import synthetic as syn
+    a = ATTN
+    ad = syn.make_attn_inputs(a["seed"], a["batch"], a["seq"], a["hidden"], a["n_heads"],
+                              a["head_dim"])
+    Xa = dev_tensor(ad["X"], syn.BF16)
+    Wqkv = dev_tensor(syn.qkv_held_shard(ad["WQ"], ad["WK"], ad["WV"], a["n_heads"],
+                                         a["head_dim"], a["i"], a["t"]), syn.BF16)
+    Wo = dev_tensor(np.ascontiguousarray(
+        ad["WO"][syn.head_slice(a["n_heads"], a["head_dim"], a["i"], a["t"]), :]), syn.BF16)
+    del ad
+    Ya = torch.empty(a["batch"] * a["seq"], a["hidden"], dtype=torch.float32, device="cuda")
+    wsa = torch.empty(B.tp_attn_shard_workspace_bytes(a["batch"], a["seq"], a["n_heads"],
+                                                      a["head_dim"], a["t"]),
+                      dtype=torch.uint8, device="cuda")
+    ms = time_calls(lambda: B.tp_attn_shard(Xa, Wqkv, Wo, Ya, a["batch"], a["seq"],
+                                            a["n_heads"], a["head_dim"], a["i"], a["t"],
+                                            True, workspace=wsa), steps, warmup)
+    afl = attn_flops(a["batch"], a["seq"], a["hidden"], a["n_heads"], a["head_dim"], a["t"])
+    med = statistics.median(ms)
+    del Xa, Wqkv, Wo, Ya, wsa
+    torch.cuda.empty_cache()
+    return {"workload": "t8_i0_h8192_64x128heads_seq2048_causal", **stats(ms), "flop": afl,
+            "tflops": round(afl / (med * 1e-3) / 1e12, 1),
+            "frac_peak": round(afl / (med * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)}
 
 
 def layer_row(steps, warmup):
@@ -272,13 +474,17 @@ def layer_row(steps, warmup):
         layer_forward(X, Wqkv, Wo, W1v, W2v, batch, seq, nh, d, True,
                       ffn_partial_dtype=torch.bfloat16)
 
-    ms = time_events(step, steps, warmup)
+    ms = time_calls(step, steps, warmup)
     fl = t * attn_flops(batch, seq, h, nh, d, t) + t * ffn_flops(M, h, f, t)
+    med = statistics.median(ms)
     del X, Wqkv, Wo, W1, W1v, W2v
     torch.cuda.empty_cache()
-    return {"workload": "layer_t4_h12288_96x128heads_f49152_b4x2048_causal",
-            "ms": round(ms, 3), "flop": fl, "tflops": round(fl / (ms * 1e-3) / 1e12, 1),
-            "frac_peak": round(fl / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)}
+    return {"workload": "layer_t4_h12288_96x128heads_f49152_b4x2048_causal", **stats(ms),
+            "flop": fl, "tflops": round(fl / (med * 1e-3) / 1e12, 1),
+            "frac_peak": round(fl / (med * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)}
+
+
+COPY_BYTES = 1 << 30
 
 
 def copy_calibration():
@@ -293,21 +499,19 @@ def copy_calibration():
 
 
 def _read_counters(path):
-    """{kernel: {counter: [per-dispatch values]}} from a rocprofv3 counter CSV."""
+    """{kernel: {counter: [per-dispatch values]}} and {dispatch: grid} from a
+    rocprofv3 counter CSV."""
     import collections
     import csv
     per = collections.defaultdict(lambda: collections.defaultdict(float))
-    names = {}
+    names, grids = {}, {}
     with open(path) as f:
         for r in csv.DictReader(f):
             key = (r["Dispatch_Id"], r["Counter_Name"])
             per[key[0]][key[1]] += float(r["Counter_Value"])
             names[key[0]] = r["Kernel_Name"]
-    out = collections.defaultdict(lambda: collections.defaultdict(list))
-    for disp, counters in per.items():
-        for c, v in counters.items():
-            out[names[disp]][c].append(v)
-    return out
+            grids[key[0]] = int(r["Grid_Size"]) // max(1, int(r["Workgroup_Size"]))
+    return per, names, grids
 
 
 def _short(name):
@@ -315,72 +519,134 @@ def _short(name):
     return n.split("(")[0] if "<" not in n.split("(")[0] else n[:n.index(">(") + 1]
 
 
-def summarize_profiles(stats_csv, fetch_csv, write_csv, cmd_stats, cmd_pmc):
-    """Write profiles/*.md and the traffic record bench.py reads."""
+def _trace_groups(trace_csv):
     import csv
-    gemm_src = src_hash("gemm.hip")
-    # Per-dispatch durations from the kernel trace next to the stats file,
-    # grouped by kernel and grid size (the bench launches the reduce kernel
-    # both over whole tensors and over row blocks).
-    trace_csv = stats_csv.replace("kernel_stats", "kernel_trace")
     groups = {}
     for r in csv.DictReader(open(trace_csv)):
         key = (_short(r["Kernel_Name"]), int(r["Grid_Size_X"]) // int(r["Workgroup_Size_X"]))
         groups.setdefault(key, []).append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+    return groups
+
+
+def _copy_factors(per, names):
+    def mean(counter):
+        vals = [c[counter] for d, c in per.items() if "copyBuffer" in names[d] and counter in c]
+        return sum(vals) / len(vals) if vals else None
+    return mean
+
+
+def summarize_profiles(trace_csv, fetch_csv, write_csv, cmd_stats, cmd_pmc):
+    """Write profiles/kernel_stats_ffn_shard_<tag>.md, traffic_ffn_shard_<tag>.md
+    and the traffic record bench.py reads, for the headline FFN shard."""
+    p = HEADLINE
+    tag = _tag(p)
+    M, h, fs = p["tokens"], p["hidden"], p["ffn"] // p["t"]
+    gemm_src = src_hash("gemm.hip")
+    groups = {k: v for k, v in _trace_groups(trace_csv).items()
+              if not k[0].startswith("at::") and "copyBuffer" not in k[0]}
     total_us = sum(sum(v) for v in groups.values())
-    lines = ["# Kernel durations: FFN shard t=8 i=3, hidden 4096, ffn 16384, 4096 tokens",
+    fl = ffn_flops(M, h, p["ffn"], p["t"])
+    lines = [f"# Kernel durations: FFN shard t={p['t']} i={p['i']}, hidden {h}, ffn {p['ffn']}, "
+             f"{M} tokens (bf16 in, fp32 out)",
              "", "Command (from the repository root, on one MI355X):", "",
              "```", cmd_stats, "```", "",
              "Per-dispatch durations from the kernel trace of the same run, grouped by kernel",
-             "and number of workgroups (the partial reduce runs over the whole 4096 x 4096",
-             "output and, in the block row, over one eighth of its rows).", "",
+             "and number of workgroups.", "",
              "| kernel | workgroups | calls | avg us | min us | max us | share |",
              "|---|---:|---:|---:|---:|---:|---:|"]
+    avg_pair = 0.0
     for (name, wgs), v in sorted(groups.items(), key=lambda kv: -sum(kv[1])):
         lines.append(f"| `{name}` | {wgs} | {len(v)} | {sum(v)/len(v):.1f} | {min(v):.1f} | "
                      f"{max(v):.1f} | {100*sum(v)/total_us:.1f}% |")
-    with open(os.path.join(ROOT, "profiles", "kernel_stats_ffn_shard_h4096_t8.md"), "w") as f:
+        avg_pair += sum(v) / len(v)
+    lines += ["", f"One tp_ffn_shard call = the two kernels above: {avg_pair:.1f} us on average, "
+              f"{fl/1e12:.2f} TFLOP algorithmic, {fl/(avg_pair*1e-6)/1e12:.0f} TFLOP/s = "
+              f"{fl/(avg_pair*1e-6)/1e12/PEAK_BF16_TFLOPS:.1%} of the {PEAK_BF16_TFLOPS} TFLOP/s "
+              "bf16 peak.", "", f"GEMM source hash: `{gemm_src}`"]
+    with open(os.path.join(ROOT, "profiles", f"kernel_stats_ffn_shard_{tag}.md"), "w") as f:
         f.write("\n".join(lines) + "\n")
 
-    fe, wr = _read_counters(fetch_csv), _read_counters(write_csv)
-
-    def mean(d, kname, c):
-        vals = [v for k, cs in d.items() if kname in k for v in cs.get(c, [])]
-        return sum(vals) / len(vals) if vals else None
-    copy_fetch = mean(fe, "copyBuffer", "FETCH_SIZE")
-    copy_write = mean(wr, "copyBuffer", "WRITE_SIZE")
+    fe, fe_names, _ = _read_counters(fetch_csv)
+    wr, wr_names, _ = _read_counters(write_csv)
+    copy_fetch = _copy_factors(fe, fe_names)("FETCH_SIZE")
+    copy_write = _copy_factors(wr, wr_names)("WRITE_SIZE")
     f_fac = (COPY_BYTES / 1024) / copy_fetch
     w_fac = (COPY_BYTES / 1024) / copy_write
-    p = FFN
-    M, h, fs = p["tokens"], p["hidden"], p["ffn"] // p["t"]
-    kernels = {"GEMM1 + GeLU": "EpiGelu", "GEMM2": "EpiStore"}
-    table = ["# HBM traffic per launch: FFN shard t=8 i=3, hidden 4096, ffn 16384, 4096 tokens",
-             "", "Commands (from the repository root, one MI355X, one counter per run):", "",
-             "```", cmd_pmc.replace("COUNTER", "FETCH_SIZE"), cmd_pmc.replace("COUNTER", "WRITE_SIZE"),
-             "```", "",
+
+    def kmean(per, names, tag_, counter):
+        vals = [c[counter] for d, c in per.items() if tag_ in names[d] and counter in c]
+        return sum(vals) / len(vals)
+    table = [f"# HBM traffic per launch: FFN shard t={p['t']} i={p['i']}, hidden {h}, ffn "
+             f"{p['ffn']}, {M} tokens", "",
+             "Commands (from the repository root, one MI355X, one counter per run):", "",
+             "```", cmd_pmc.replace("COUNTER", "FETCH_SIZE"),
+             cmd_pmc.replace("COUNTER", "WRITE_SIZE"), "```", "",
              f"Calibration: a {COPY_BYTES >> 20} MiB device copy read FETCH_SIZE {copy_fetch:.0f} KiB "
              f"and WRITE_SIZE {copy_write:.0f} KiB, so the counters are scaled by "
              f"{f_fac:.3f} (fetch) and {w_fac:.3f} (write).", "",
              "| kernel | FETCH_SIZE KiB | WRITE_SIZE KiB | scaled MB read | scaled MB written |",
              "|---|---:|---:|---:|---:|"]
     total = 0.0
-    for label, tag in kernels.items():
-        fk = mean(fe, tag, "FETCH_SIZE")
-        wk = mean(wr, tag, "WRITE_SIZE")
+    for label, k in {"GEMM1 + GeLU": "EpiGelu", "GEMM2": "EpiStore"}.items():
+        fk, wk = kmean(fe, fe_names, k, "FETCH_SIZE"), kmean(wr, wr_names, k, "WRITE_SIZE")
         rb_, wb_ = fk * 1024 * f_fac, wk * 1024 * w_fac
         total += rb_ + wb_
         table.append(f"| {label} | {fk:.0f} | {wk:.0f} | {rb_/1e6:.1f} | {wb_/1e6:.1f} |")
-    alg = 2 * (M * h + h * fs + M * fs) + 2 * (M * fs + fs * h) + 2 * M * h
+    alg = 2 * (M * h + h * fs + M * fs) + 2 * (M * fs + fs * h) + 4 * M * h
     table += ["", f"Sum for one tp_ffn_shard call: {total/1e6:.1f} MB of HBM traffic; the "
-              f"algorithmic minimum (X, W1_i, GeLU(Z) written and re-read, W2_i, bf16 Y) is "
-              f"{alg/1e6:.1f} MB.", "", f"GEMM source hash: `{gemm_src}`"]
-    with open(os.path.join(ROOT, "profiles", "traffic_ffn_shard_h4096_t8.md"), "w") as f:
+              f"algorithmic minimum (X, W1, GeLU(Z) written and re-read, W2, fp32 Y) is "
+              f"{alg/1e6:.1f} MB ({total/alg:.2f}x).", "", f"GEMM source hash: `{gemm_src}`"]
+    with open(os.path.join(ROOT, "profiles", f"traffic_ffn_shard_{tag}.md"), "w") as f:
         f.write("\n".join(table) + "\n")
     with open(TRAFFIC_FILE, "w") as f:
         json.dump({"kernel_source_sha": gemm_src, "traffic_bytes": round(total),
-                   "fetch_factor": f_fac, "write_factor": w_fac,
-                   "algorithmic_bytes": alg}, f, indent=1)
-    print(f"wrote profiles (traffic {total/1e6:.1f} MB per call, algorithmic {alg/1e6:.1f} MB)")
+                   "fetch_factor": f_fac, "write_factor": w_fac, "algorithmic_bytes": alg,
+                   "avg_call_us_trace": round(avg_pair, 2)}, f, indent=1)
+    print(f"wrote profiles for {tag} (call {avg_pair:.1f} us; traffic {total/1e6:.1f} MB, "
+          f"algorithmic {alg/1e6:.1f} MB)")
+
+
+REDUCE_SHAPES = ((8, 4096, 4096), (4, 8192, 12288))
+
+
+def summarize_reduce_traffic(trace_csv, fetch_csv, write_csv, cmd_stats, cmd_pmc):
+    """profiles/reduce_rotated.md: per-launch durations and HBM bytes of
+    reduce_kernel at the two rotated reduce shapes (told apart by grid size)."""
+    groups = _trace_groups(trace_csv)
+    fe, fe_names, fe_grid = _read_counters(fetch_csv)
+    wr, wr_names, wr_grid = _read_counters(write_csv)
+    copy_fetch = _copy_factors(fe, fe_names)("FETCH_SIZE")
+    copy_write = _copy_factors(wr, wr_names)("WRITE_SIZE")
+    f_fac = (COPY_BYTES / 1024) / copy_fetch
+    w_fac = (COPY_BYTES / 1024) / copy_write
+    lines = ["# Partial reduce with inputs rotated over 3 buffer sets (HBM, not cache)", "",
+             "Commands (from the repository root, one MI355X):", "", "```", cmd_stats,
+             cmd_pmc.replace("COUNTER", "FETCH_SIZE"), cmd_pmc.replace("COUNTER", "WRITE_SIZE"),
+             "```", "",
+             f"Counters scaled by a {COPY_BYTES >> 20} MiB device copy: FETCH x {f_fac:.3f}, "
+             f"WRITE x {w_fac:.3f}. Algorithmic bytes: t bf16 partials + bf16 residual read, "
+             "fp32 output written.", "",
+             "| shape | workgroups | launches | avg us | min us | algorithmic MB | TB/s (avg) | "
+             "scaled MB read | scaled MB written | counted / algorithmic |",
+             "|---|---:|---:|---:|---:|---:|---:|---:|---:|---:|"]
+    for t, rows, cols in REDUCE_SHAPES:
+        wgs = (rows * cols // 8 + 255) // 256
+        durs = [v for (n, g), vs in groups.items() if "reduce_kernel" in n and g == wgs for v in vs]
+        fvals = [c["FETCH_SIZE"] for d, c in fe.items()
+                 if "reduce_kernel" in fe_names[d] and fe_grid[d] == wgs]
+        wvals = [c["WRITE_SIZE"] for d, c in wr.items()
+                 if "reduce_kernel" in wr_names[d] and wr_grid[d] == wgs]
+        alg = reduce_bytes(t, rows, cols)
+        avg = sum(durs) / len(durs)
+        rd = sum(fvals) / len(fvals) * 1024 * f_fac
+        wt = sum(wvals) / len(wvals) * 1024 * w_fac
+        lines.append(f"| t={t} [{rows},{cols}] | {wgs} | {len(durs)} | {avg:.1f} | {min(durs):.1f} "
+                     f"| {alg/1e6:.1f} | {alg/(avg*1e-6)/1e12:.2f} | {rd/1e6:.1f} | {wt/1e6:.1f} | "
+                     f"{(rd + wt)/alg:.3f} |")
+    lines += ["", f"Reduce source hash: `{src_hash('reduce.hip')}`"]
+    with open(os.path.join(ROOT, "profiles", "reduce_rotated_t8_h4096_t4_h12288.md"), "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print("wrote profiles/reduce_rotated_t8_h4096_t4_h12288.md")
 
 
 def summarize_attn_profile(trace_csv, cmd):
@@ -510,28 +776,30 @@ def summarize_sweep(path, cmd):
     print(f"wrote profiles/sweep_ffn_shard_tokens2048.md ({len(recs)} points)")
 
 
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=200)
-    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--no-attention", action="store_true",
-                    help="skip the attention row (profiling runs of the FFN step)")
-    ap.add_argument("--no-fused", action="store_true",
-                    help="skip the fused-step rows (profiling runs of the FFN step)")
-    ap.add_argument("--sweep", metavar="OUT_JSONL", default=None)
+    ap.add_argument("--headline-only", action="store_true",
+                    help="time the headline FFN shard only (profiling runs)")
+    ap.add_argument("--reduce-only", action="store_true",
+                    help="time the two rotated reduce rows only (profiling runs)")
+    ap.add_argument("--no-sweep-torch", action="store_true",
+                    help="skip the torch (hipBLASLt) comparison at each sweep point")
+    ap.add_argument("--sweep-out", metavar="JSONL", default=None,
+                    help="also write the sweep records to this file")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run a 1 GiB device copy first (counter calibration)")
-    ap.add_argument("--summarize-counters", metavar="COUNTER_CSV", default=None,
-                    help="write the MFMA-utilisation / LDS-conflict table from a --pmc run")
-    ap.add_argument("--summarize-attn-profile", metavar="KERNEL_TRACE_CSV", default=None,
-                    help="write the attention-shard kernel table from a rocprofv3 trace")
-    ap.add_argument("--summarize-sweep", metavar="SWEEP_JSONL", default=None,
-                    help="write profiles/sweep_*.md from a --sweep output and exit")
-    ap.add_argument("--summarize-profiles", nargs=3,
-                    metavar=("STATS_CSV", "FETCH_CSV", "WRITE_CSV"),
-                    help="write profiles/ summaries from rocprofv3 CSVs and exit")
+    ap.add_argument("--summarize-counters", metavar="COUNTER_CSV", default=None)
+    ap.add_argument("--summarize-attn-profile", metavar="KERNEL_TRACE_CSV", default=None)
+    ap.add_argument("--summarize-sweep", metavar="SWEEP_JSONL", default=None)
+    ap.add_argument("--summarize-profiles", nargs=3, metavar=("TRACE_CSV", "FETCH_CSV", "WRITE_CSV"))
+    ap.add_argument("--summarize-reduce-traffic", nargs=3,
+                    metavar=("TRACE_CSV", "FETCH_CSV", "WRITE_CSV"))
     ap.add_argument("--profile-commands", nargs=2, default=["", ""],
                     metavar=("STATS_CMD", "PMC_CMD"))
     args = ap.parse_args()
@@ -547,183 +815,125 @@ def main():
     if args.summarize_profiles:
         summarize_profiles(*args.summarize_profiles, *args.profile_commands)
         return
+    if args.summarize_reduce_traffic:
+        summarize_reduce_traffic(*args.summarize_reduce_traffic, *args.profile_commands)
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU's shard only: this library runs on a single "
               "GPU and has no multi-GPU path; run with --gpus 1", file=sys.stderr)
         sys.exit(2)
 
-    import numpy as np
     import torch
     from attention_shards_amd import binding as B
-    from attention_shards_amd import synthetic as syn
     B.load()
     if not torch.cuda.is_available():
         print("no GPU visible", file=sys.stderr)
         sys.exit(1)
 
+    def log(msg):
+        print(msg, file=sys.stderr, flush=True)
+
+    K, W = args.steps, args.warmup
     if args.copy_calibration:
         copy_calibration()
-    if args.sweep:
-        sweep(args.sweep, max(5, args.steps // 5), 3)
+    if args.reduce_only:
+        for t, rows, cols in REDUCE_SHAPES:
+            log(json.dumps(reduce_rotated(t, rows, cols, K, W)))
+        return
 
-    # ---------------- FFN sub-layer step ----------------
-    p = FFN
+    # ---------------- headline: the sweep's hidden-22528, t=1 FFN shard ----------------
+    p = HEADLINE
     M, h, f, t, i = p["tokens"], p["hidden"], p["ffn"], p["t"], p["i"]
-    fs = f // t
-    d = syn.make_ffn_inputs(p["seed"], M, h, f, syn.BF16, residual=True)
+    log(f"headline inputs: hidden {h}, ffn {f}, {M} tokens (seed {p['seed']})")
+    d = headline_inputs()
+    from attention_shards_amd import synthetic as syn
     X = dev_tensor(d["X"], syn.BF16)
     W1 = dev_tensor(d["W1"], syn.BF16)
     W2 = dev_tensor(d["W2"], syn.BF16)
-    R = dev_tensor(d["R"], syn.BF16)
-    parts = [torch.empty(M, h, dtype=torch.bfloat16, device="cuda") for _ in range(t)]
+    Y = torch.empty(M, h, dtype=torch.float32, device="cuda")
     ws = torch.empty(B.tp_ffn_shard_workspace_bytes(M, h, f, t, B.TP_BF16),
                      dtype=torch.uint8, device="cuda")
-    out = torch.empty(M, h, dtype=torch.float32, device="cuda")
-    W1v = [W1[:, j * fs:(j + 1) * fs] for j in range(t)]
-    W2v = [W2[j * fs:(j + 1) * fs] for j in range(t)]
-    for j in range(t):                      # the peers' partials, once
-        B.tp_ffn_shard(X, W1v[j], W2v[j], parts[j], j, t, workspace=ws)
-    torch.cuda.synchronize()
 
     def ffn():
-        B.tp_ffn_shard(X, W1v[i], W2v[i], parts[i], i, t, workspace=ws)
+        B.tp_ffn_shard(X, W1, W2, Y, i, t, workspace=ws)
 
-    def red():
-        B.tp_partial_reduce(parts, R, out)
-
-    settle(lambda: (ffn(), red()))
-    for _ in range(args.warmup):
+    settle(ffn)
+    for _ in range(W):
         ffn()
-        red()
     torch.cuda.synchronize()
-    # The K timed steps: launches only, nothing else on the stream.
+    # the K timed steps: launches only, nothing else on the stream
     t0 = time.perf_counter()
-    for _ in range(args.steps):
+    for _ in range(K):
         ffn()
-        red()
     torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    ms_step = wall / args.steps * 1e3
-    # Per-call durations: the same K steps again with events around each call.
-    ev = [tuple(torch.cuda.Event(enable_timing=True) for _ in range(3))
-          for _ in range(args.steps)]
-    for e0, e1, e2 in ev:
-        e0.record()
-        ffn()
-        e1.record()
-        red()
-        e2.record()
-    torch.cuda.synchronize()
-    ffn_ms = sum(a.elapsed_time(b) for a, b, _ in ev) / args.steps
-    red_ms = sum(b.elapsed_time(c) for _, b, c in ev) / args.steps
+    ms_step = (time.perf_counter() - t0) / K * 1e3
+    # per-call durations: the same K steps again with events around each call
+    ms = time_calls(ffn, K, 2)
     fl = ffn_flops(M, h, f, t)
-    value = fl / (ms_step * 1e-3) / 1e12
-    ffn_tf = fl / (ffn_ms * 1e-3) / 1e12
-    red_bytes = (t * 2 + 2 + 4) * M * h
-    red_gbs = red_bytes / (red_ms * 1e-3) / 1e9
-
-    # The reduce-scatter half of the all-reduce on this GPU: one row block
-    # (rows [j*M/t, (j+1)*M/t) of every partial) per call, j rotating over the
-    # t blocks so that successive calls do not find their inputs in the
-    # Infinity Cache (one block is 46 MB; all t together 369 MB).
-    nxt = [0]
-
-    def one_slice():
-        B.tp_partial_reduce_slice(parts, R, out, nxt[0] % t, t)
-        nxt[0] += 1
-
-    slice_ms = time_batched(one_slice, args.steps, args.warmup)
-    slice_bytes = (t * 2 + 2 + 4) * (M // t) * h
-    slice_row = {"slices": "rotating 0..t-1", "nslices": t, "ms": round(slice_ms, 5),
-                 "bytes": slice_bytes,
-                 "gbs": round(slice_bytes / (slice_ms * 1e-3) / 1e9, 1),
-                 "frac_hbm_peak": round(slice_bytes / (slice_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}
-
-    # The same step with the sum fused into GEMM2's epilogue: this shard's
-    # partial is added from the accumulators and never stored or re-read.
-    fused_row = None
-    if not args.no_fused:
-        peers = [None if j == i else parts[j] for j in range(t)]
-        wsf = torch.empty(B.tp_ffn_shard_reduce_workspace_bytes(M, h, f, t, B.TP_BF16),
-                          dtype=torch.uint8, device="cuda")
-        fused_ms = time_events(lambda: B.tp_ffn_shard_reduce(X, W1v[i], W2v[i], peers, R, out,
-                                                             i, workspace=wsf),
-                               args.steps, args.warmup)
-        fused_row = {"ms": round(fused_ms, 5),
-                     "tflops": round(fl / (fused_ms * 1e-3) / 1e12, 2),
-                     "unfused_ms": round(ffn_ms + red_ms, 5),
-                     "hbm_bytes_saved": 2 * 2 * M * h}
-        del peers, wsf
-    del parts, W1v, W2v, W1, W2, ws, out
+    med, mean = statistics.median(ms), statistics.mean(ms)
+    value = fl / (med * 1e-3) / 1e12
+    log(f"headline: median {med:.4f} ms, min {min(ms):.4f} ms, {value:.1f} TFLOP/s")
+    del X, W1, W2, Y, ws
     torch.cuda.empty_cache()
-    if fused_row is not None:
-        fused_row["large"] = fused_vs_unfused_large(max(5, args.steps // 5), 3)
 
-    # ---------------- attention shard ----------------
-    attn_row = None
-    if not args.no_attention:
-        a = ATTN
-        ad = syn.make_attn_inputs(a["seed"], a["batch"], a["seq"], a["hidden"], a["n_heads"],
-                                  a["head_dim"])
-        nl = a["n_heads"] // a["t"]
-        Xa = dev_tensor(ad["X"], syn.BF16)
-        Wqkv = dev_tensor(syn.qkv_held_shard(ad["WQ"], ad["WK"], ad["WV"], a["n_heads"],
-                                             a["head_dim"], a["i"], a["t"]), syn.BF16)
-        Wo = dev_tensor(np.ascontiguousarray(
-            ad["WO"][syn.head_slice(a["n_heads"], a["head_dim"], a["i"], a["t"]), :]), syn.BF16)
-        Ya = torch.empty(a["batch"] * a["seq"], a["hidden"], dtype=torch.float32, device="cuda")
-        wsa = torch.empty(B.tp_attn_shard_workspace_bytes(a["batch"], a["seq"], a["n_heads"],
-                                                          a["head_dim"], a["t"]),
-                          dtype=torch.uint8, device="cuda")
-        attn_ms = time_events(lambda: B.tp_attn_shard(Xa, Wqkv, Wo, Ya, a["batch"], a["seq"],
-                                                      a["n_heads"], a["head_dim"], a["i"], a["t"],
-                                                      True, workspace=wsa),
-                              args.steps, args.warmup)
-        afl = attn_flops(a["batch"], a["seq"], a["hidden"], a["n_heads"], a["head_dim"], a["t"])
-        attn_tf = afl / (attn_ms * 1e-3) / 1e12
-        del ad
-        attn_row = {"workload": "t8_i0_h8192_64x128heads_seq2048_causal",
-                    "ms": round(attn_ms, 5), "flop": afl, "tflops": round(attn_tf, 2),
-                    "frac_peak": round(attn_tf / PEAK_BF16_TFLOPS, 4)}
-
-    layer = None if args.no_attention else layer_row(max(3, args.steps // 40), 2)
-
-    traffic = load_traffic()
     res = {
         "metric": METRIC,
         "value": round(value, 2),
         "unit": "TFLOP/s",
         "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
+        "steps": K,
+        "warmup": W,
         "ms_per_step": round(ms_step, 5),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic (seeded PCG64 normals: activations N(0,1), weights N(0,0.02^2))",
-        "config": {"workload": "ffn_shard_t8_i3_h4096_f16384_tokens4096_plus_reduce8",
-                   "tokens": M, "hidden": h, "ffn": f, "t": t, "i": i,
-                   "partial_dtype": "bf16", "reduce_out_dtype": "f32"},
+        "config": {"workload": f"ffn_shard_t{t}_i{i}_h{h}_f{f}_tokens{M}",
+                   "tokens": M, "hidden": h, "ffn": f, "t": t, "i": i, "seed": p["seed"],
+                   "in_dtype": "bf16", "out_dtype": "f32",
+                   "timing": "value = FLOPs / median per-call time (HIP events)",
+                   **stats(ms)},
         "roofline": {"bound": "mfma", "kernel": "tp_ffn_shard (GEMM1+GeLU, GEMM2)",
-                     "achieved": round(ffn_tf, 2), "peak": PEAK_BF16_TFLOPS,
-                     "unit": "TFLOP/s", "frac": round(ffn_tf / PEAK_BF16_TFLOPS, 4),
-                     "traffic": traffic, "per_launch_flop": fl,
-                     "avg_launch_ms": round(ffn_ms, 5)},
-        "rows": {
-            "ffn_shard": {"ms": round(ffn_ms, 5), "tflops": round(ffn_tf, 2),
-                          "frac_peak": round(ffn_tf / PEAK_BF16_TFLOPS, 4)},
-            "partial_reduce": {"ms": round(red_ms, 5), "bytes": red_bytes,
-                               "gbs": round(red_gbs, 1),
-                               "frac_hbm_peak": round(red_gbs / PEAK_HBM_GBS, 4),
-                               "bound": "hbm"},
-            "partial_reduce_slice": slice_row,
-            "ffn_shard_reduce_fused": fused_row,
-            "attn_shard": attn_row,
-            "layer": layer,
-        },
+                     "achieved": round(fl / (mean * 1e-3) / 1e12, 2), "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(fl / (mean * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+                     "traffic": load_traffic(), "per_launch_flop": fl,
+                     "avg_launch_ms": round(mean, 5)},
+        "rows": {},
     }
-    if not args.no_cpu_baseline:
+    if not args.headline_only:
+        rows = res["rows"]
+        log("sweep (44 points)")
+        sw = sweep_rows(max(5, K // 5), 3, with_torch=not args.no_sweep_torch, log=log)
+        rows["sweep"] = sw
+        if args.sweep_out:
+            with open(args.sweep_out, "w") as fo:
+                for r in sw:
+                    fo.write(json.dumps(r) + "\n")
+        rows["sweep_summary"] = {
+            "points": len(sw), "min_tflops": min(r["tflops"] for r in sw),
+            "max_tflops": max(r["tflops"] for r in sw),
+            "points_at_or_above_60pct": sum(1 for r in sw if r["frac_peak"] >= 0.6),
+            "points_faster_than_torch": sum(1 for r in sw if r["tflops"] >= r.get("torch_tflops", 0))}
+        log("FFN step (t=8, hidden 4096) and reduce")
+        step, sl, fused = ffn_step_row(K, W)
+        rows["ffn_step_h4096_t8"] = step
+        rows["partial_reduce_slice"] = sl
+        for t_, r_, c_ in REDUCE_SHAPES:
+            log(f"reduce rotated t={t_} [{r_},{c_}]")
+            rows[f"partial_reduce_t{t_}_h{c_}"] = reduce_rotated(t_, r_, c_, K, W)
+        if fused is not None:
+            fused["large"] = fused_vs_unfused_large(max(5, K // 5), 3)
+        rows["ffn_shard_reduce_fused"] = fused
+        log("attention shard")
+        rows["attn_shard"] = attn_row(K, W)
+        log("layer")
+        rows["layer"] = layer_row(max(3, K // 10), 2)
+        rows["device"] = {"name": torch.cuda.get_device_name(0),
+                          "compute_units": torch.cuda.get_device_properties(0).multi_processor_count,
+                          "hip": torch.version.hip}
+    if not args.no_cpu_baseline and not args.headline_only:
+        log("cpu baseline (oracle)")
         res["cpu_baseline"] = cpu_baseline(d)
     print(json.dumps(res), flush=True)
 
