@@ -963,6 +963,27 @@ hipError_t dispatch_bf16(const uint16_t* A, int64_t lda, const uint16_t* B,
   return launch_bf16<128, 128, 2, 2, 4, 3, AKB>(A, lda, B, ldb, M, N, K, kwrap, epi, s);
 }
 
+// X [M, K] row-major (row stride lda) -> K-blocked [ceil(K/kb)][M][kb]
+// (kb = 32 or 64; zeros in the columns past K of the last block), the A
+// layout whose stage tiles are contiguous runs.  A wave moves 8 rows x 64
+// columns, 16 bytes per lane: it reads whole 128-byte row segments and
+// writes, per kb-column block, 8 consecutive rows as one contiguous run.
+__global__ void __launch_bounds__(256)
+kblock_kernel(const uint16_t* __restrict__ A, int64_t lda, uint16_t* __restrict__ out, int M,
+              int K, int kb, int64_t units, int kunits) {
+  const int64_t u = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (u >= units) return;
+  const int lane = threadIdx.x & 63;
+  const int rg = (int)(u / kunits), kg = (int)(u - (int64_t)rg * kunits);
+  const int row = rg * 8 + (lane >> 3);
+  const int k = kg * 64 + (lane & 7) * 8;
+  const int kpad = (K + kb - 1) / kb * kb;
+  if (row >= M || k >= kpad) return;
+  u32x4 v = {0, 0, 0, 0};
+  if (k < K) v = *reinterpret_cast<const u32x4*>(A + (int64_t)row * lda + k);
+  *reinterpret_cast<u32x4*>(out + ((int64_t)(k / kb) * M + row) * kb + (k % kb)) = v;
+}
+
 // ---------------------------------------------------------------------------
 // fp32 kernel: 64x64 tiles, 4 waves of 32x32, v_mfma_f32_16x16x4_f32.
 // ---------------------------------------------------------------------------
@@ -1092,6 +1113,28 @@ hipError_t gemm_bf16_store_split_a_kb(const uint16_t* A2, int kb, const uint16_t
   if (K % 64) return hipErrorInvalidValue;
   if (M > 0 && N > 0 && kb != a_block(choose_bf16_tile(M, N))) return hipErrorInvalidValue;
   return dispatch_bf16<true>(A2, M, B, ldb, M, N, 2 * K, K, EpiStore{C, ldc, (int)out}, s);
+}
+
+hipError_t kblock_bf16(const uint16_t* A, int64_t lda, uint16_t* out, int M, int K, int kb,
+                       hipStream_t s) {
+  if ((kb != 32 && kb != 64) || K % 8 || lda % 8) return hipErrorInvalidValue;
+  if (M == 0 || K == 0) return hipSuccess;
+  const int kpad = (K + kb - 1) / kb * kb;
+  const int kunits = (kpad + 63) / 64;
+  const int64_t units = (int64_t)((M + 7) / 8) * kunits;
+  const int64_t blocks = (units + 3) / 4;
+  if (blocks > ((int64_t)1 << 24) - 1) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(kblock_kernel, dim3((unsigned)blocks), dim3(256), 0, s, A, lda, out, M, K,
+                     kb, units, kunits);
+  return hipGetLastError();
+}
+
+hipError_t gemm_bf16_gelu_akb(const uint16_t* Akb, int kb, const uint16_t* B, int64_t ldb,
+                              uint16_t* C, int M, int N, int K, int kb_out, hipStream_t s) {
+  if (kb_out != 32 && kb_out != 64) return hipErrorInvalidValue;
+  if (M > 0 && N > 0 && kb != a_block(choose_bf16_tile(M, N))) return hipErrorInvalidValue;
+  const int sh = kb_out == 32 ? 5 : 6;
+  return dispatch_bf16<true>(Akb, M, B, ldb, M, N, K, K, EpiGelu{C, 0, (int)OUT_BF16, M, sh}, s);
 }
 
 hipError_t gemm_bf16_gelu(const uint16_t* A, int64_t lda, const uint16_t* B,

@@ -47,6 +47,15 @@ struct QkvOut {
 hipError_t gemm_bf16_gelu(const uint16_t* A, int64_t lda, const uint16_t* B,
                           int64_t ldb, uint16_t* C, int64_t ldc, int M, int N,
                           int K, int kb, hipStream_t s);
+// The same with A already K-blocked, [ceil(K/kb)][M][kb], kb =
+// gemm_bf16_a_block(M, N) (else hipErrorInvalidValue); C K-blocked by
+// kb_out (32 or 64).
+hipError_t gemm_bf16_gelu_akb(const uint16_t* Akb, int kb, const uint16_t* B, int64_t ldb,
+                              uint16_t* C, int M, int N, int K, int kb_out, hipStream_t s);
+// A [M, K] row-major (row stride lda) copied K-blocked into out,
+// [ceil(K/kb)][M][kb] (kb = 32 or 64), zeros past K.  K, lda multiples of 8.
+hipError_t kblock_bf16(const uint16_t* A, int64_t lda, uint16_t* out, int M, int K, int kb,
+                       hipStream_t s);
 // K block the kernel chosen for an [M, N] output reads a K-blocked A in.
 int gemm_bf16_a_block(int M, int N);
 // C = acc stored as `out` (row stride ldc), A K-blocked, [ceil(K/kb)][M][kb];

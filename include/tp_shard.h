@@ -43,7 +43,7 @@
 extern "C" {
 #endif
 
-#define TP_ABI_VERSION 4
+#define TP_ABI_VERSION 5
 #define TP_MAX_PARTIALS 64
 
 /* Element types of tensors crossing the ABI. */
@@ -98,8 +98,11 @@ typedef enum {
  *                                   two GEMMs (no gather: step 2 reads it as is),
  *                                   bf16 in an internal K-blocked layout
  *                                   (tokens x ffn/t rounded up to 64 columns),
- *                                   fp32 row-major; contents are not part of the
- *                                   interface
+ *                                   fp32 row-major; with bf16 inputs and
+ *                                   ffn/t >= 8192 also a K-blocked copy of X
+ *                                   (tokens x hidden rounded up to 64 columns)
+ *                                   that the first GEMM reads; contents are not
+ *                                   part of the interface
  * Shape rules: tokens >= 0 (0 enqueues nothing); hidden and ffn/t multiples
  * of 8 (bf16) or 4 (fp32); ld_w1 >= ffn/t and a multiple of the same; every
  * dimension below 2^31; with bf16 inputs also hidden, ffn/t < 2^22 and
