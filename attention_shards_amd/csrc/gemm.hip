@@ -16,14 +16,14 @@
 //     N-contiguous) keeps its [k][n] layout with a 64-byte-block swizzle and
 //     is read with ds_read_b64_tr_b16, which transposes it into the MFMA
 //     operand.
-//   * gemm_bf16_kernel: 4 waves, 256x128, 128x192 or 128x128 tiles, K = 64
-//     per stage through a 3-slot ring, DMAs and fragment reads interleaved
-//     between the MFMAs of each wave.  (128x192 fills all 256 CUs where
-//     256x128 would leave a quarter idle, e.g. 2048 x 3072 outputs.)
-//   * gemm_bf16_pp_kernel: 8 waves, 256x256 tiles, K = 32 per stage through
-//     a 5-slot ring; two groups of waves alternate between a memory phase and
-//     an MFMA-only phase, one phase apart, so each SIMD's matrix pipe is fed
-//     by one wave or the other.
+//   * gemm_bf16_kernel: 4 waves (one per SIMD), DMAs and fragment reads
+//     interleaved between the MFMAs of each wave.  256x256 tiles: each wave
+//     owns a 128x128 block (256 accumulator registers), K = 32 per stage
+//     through a 5-slot ring (160 KB); the wide wave block halves the LDS
+//     fragment reads per MFMA of a 128x64 block.  256x128, 128x192 and
+//     128x128 tiles: K = 64 per stage through a 3-slot ring.  (128x192
+//     fills all 256 CUs where 256x128 would leave a quarter idle, e.g.
+//     2048 x 3072 outputs.)
 //   * Workgroup ids are remapped so each XCD (dispatch is round-robin over
 //     the 8 XCDs) receives a contiguous run of tiles, ordered in groups of 8
 //     tile-rows so neighbouring tiles share A and B panels in that XCD's L2.
@@ -719,185 +719,6 @@ gemm_bf16_kernel(const uint16_t* __restrict__ A, int64_t lda,
   epilogue_lds<BN / WN>(smem, acc, epi, M, N, m0 + wr0, n0 + wc0, wave, lane);
 }
 
-// 256x256 tiles with eight waves in two groups that take turns on the
-// matrix cores ("ping-pong").  Waves w and w+4 share SIMD w%4; group 0
-// (waves 0-3) owns output rows 0-127 and group 1 rows 128-255, each wave a
-// 128x64 block (4x2 accumulator blocks of v_mfma_f32_32x32x16_bf16).  K
-// advances in stages of 32 through a five-slot LDS ring (32 KB per stage,
-// the same layout and swizzles as gemm_bf16_kernel with KS = 2).  Every wave
-// alternates two phases separated by workgroup barriers:
-//   mem(s):  issue its share of the DMAs of stage s+4 (into the slot that
-//            stage s-1 freed), read all of its fragments of stage s, then
-//            wait until its own DMAs of stage s+1 and its LDS reads are done;
-//   comp(s): 16 MFMAs on those fragments and nothing else.
-// Group 1 starts one phase late, so while one wave of a SIMD runs its MFMAs
-// the other loads; the matrix pipe is fed by one wave or the other in every
-// phase.  With phases numbered from 0, group 0 runs mem(s) in phase 2s and
-// comp(s) in 2s+1, group 1 one phase later.  Ring safety: slot s%5 is read in
-// phases 2s (group 0) and 2s+1 (group 1), each wave waiting for its reads
-// before the barrier that ends its mem phase, and is refilled (stage s+5)
-// from phase 2s+2 on; stage s+1 is read from phase 2s+2 on and every wave has
-// waited for its share of it by the end of phase 2s+1.
-template <class Epi, bool AKB>
-__global__ void __launch_bounds__(512)
-gemm_bf16_pp_kernel(const uint16_t* __restrict__ A, int64_t lda,
-                    const uint16_t* __restrict__ B, int64_t ldb, int M, int N,
-                    int K, int kwrap, int tiles_m, int tiles_n, Epi epi) {
-  constexpr int BM = 256, BN = 256, NW = 8, WN = 4;
-  constexpr int BK = 32, NSL = 5;
-  constexpr int FM = 4, FN = 2;            // 128 x 64 per wave
-  constexpr int A_ROWB = BK * 2;           // 64-byte A rows
-  constexpr int CPR = 4, RPD = 16, ASH = 2;
-  constexpr int B_ROWB = BN * 2;           // 512-byte B rows
-  constexpr int B_CH = B_ROWB / 16;
-  constexpr int A_STAGE = BM * A_ROWB;     // 16 KB
-  constexpr int B_STAGE = BK * B_ROWB;     // 16 KB
-  constexpr int A_DMA = A_STAGE / 1024 / NW;  // 2
-  constexpr int B_DMA = B_STAGE / 1024 / NW;  // 2
-  constexpr int NDMA = A_DMA + B_DMA;
-  static_assert(A_DMA * 1024 * NW == A_STAGE && B_DMA * 1024 * NW == B_STAGE, "DMA split");
-
-  __shared__ __attribute__((aligned(16))) uint8_t smem[NSL * (A_STAGE + B_STAGE)];
-  static_assert(NW * 32 * (BN / WN + 4) * 4 <= (int)sizeof(smem), "epilogue staging fits");
-  uint8_t* const lds_a = smem;
-  uint8_t* const lds_b = smem + NSL * A_STAGE;
-  const uint32_t lds_a_addr = (uint32_t)(uintptr_t)(lds_u8*)lds_a;
-  const uint32_t lds_b_addr = (uint32_t)(uintptr_t)(lds_u8*)lds_b;
-
-  int tm, tn;
-  tile_coords(tiles_m, tiles_n, tm, tn);
-  const int m0 = tm * BM, n0 = tn * BN;
-  const int tid = threadIdx.x, lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int grp = wave >> 2;
-  const int wr0 = grp * 128;
-  const int wc0 = (wave & 3) * 64;
-  const int rows_valid = min(BM, M - m0);
-  const int cols_valid = min(BN, N - n0);
-
-  // DMA lane offsets (as in gemm_bf16_kernel).
-  int a_off[A_DMA], a_col[A_DMA];
-#pragma unroll
-  for (int j = 0; j < A_DMA; ++j) {
-    const int row = RPD * (j * NW + wave) + lane / CPR;
-    const int c = (lane % CPR) ^ ((row >> ASH) & (CPR - 1));
-    a_off[j] = AKB ? row * A_ROWB + c * 16 : row * (int)lda * 2 + c * 16;
-    a_col[j] = c * 8;
-  }
-  int b_off[B_DMA];
-#pragma unroll
-  for (int j = 0; j < B_DMA; ++j) {
-    const int row = (j * NW + wave) * (1024 / B_ROWB) + lane / B_CH;
-    const int c = (lane % B_CH) ^ ((row & 3) << 2);
-    b_off[j] = row * (int)ldb * 2 + c * 16;
-  }
-  // All of this wave's DMAs of stage kt into ring slot `slot`.
-  auto dma_stage = [&](int kt, int slot) __attribute__((always_inline)) {
-    const int k0 = kt * BK;
-    const __amdgpu_buffer_rsrc_t ra =
-        AKB ? make_rsrc(A + ((int64_t)kt * lda + m0) * BK, (int64_t)rows_valid * A_ROWB)
-            : make_rsrc(A + (int64_t)m0 * lda + k0, (int64_t)rows_valid * lda * 2 - (int64_t)k0 * 2);
-#pragma unroll
-    for (int j = 0; j < A_DMA; ++j) {
-      const int off = (k0 + a_col[j] < K) ? a_off[j] : OOB;
-      dma16(ra, off, lds_a_addr + slot * A_STAGE + (j * NW + wave) * 1024);
-    }
-    const int bk0 = k0 < kwrap ? k0 : k0 - kwrap;
-    const int rows_left = (k0 < kwrap ? kwrap : K) - k0;
-    const __amdgpu_buffer_rsrc_t rb =
-        make_rsrc(B + (int64_t)bk0 * ldb + n0,
-                  ((int64_t)rows_left - 1) * ldb * 2 + (int64_t)cols_valid * 2);
-#pragma unroll
-    for (int j = 0; j < B_DMA; ++j)
-      dma16(rb, b_off[j], lds_b_addr + slot * B_STAGE + (j * NW + wave) * 1024);
-  };
-
-  // Fragment read offsets inside a slot (as in gemm_bf16_kernel).
-  int a_rd[2];
-#pragma unroll
-  for (int ks = 0; ks < 2; ++ks) {
-    const int c = (2 * ks + (lane >> 5)) ^ (((lane & 31) >> ASH) & (CPR - 1));
-    a_rd[ks] = (wr0 + (lane & 31)) * A_ROWB + c * 16;
-  }
-  int b_rd[FN];
-  {
-    const int G = lane >> 4, r = lane & 15;
-    const int krow = 8 * (G >> 1) + (r >> 2);
-#pragma unroll
-    for (int ni = 0; ni < FN; ++ni) {
-      const int c = (((wc0 + ni * 32) >> 3) + 2 * (G & 1) + ((r & 3) >> 1)) ^ ((r >> 2) << 2);
-      b_rd[ni] = krow * B_ROWB + c * 16 + (r & 1) * 8;
-    }
-  }
-
-  f32x16 acc[FM][FN];
-#pragma unroll
-  for (int mi = 0; mi < FM; ++mi)
-#pragma unroll
-    for (int ni = 0; ni < FN; ++ni)
-#pragma unroll
-      for (int e = 0; e < 16; ++e) acc[mi][ni][e] = 0.0f;
-
-  bf16x8 fa[2][FM], fb[2][FN];
-  auto read_stage = [&](int slot) __attribute__((always_inline)) {
-    const uint8_t* la = lds_a + slot * A_STAGE;
-    const uint8_t* lb = lds_b + slot * B_STAGE;
-#pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-#pragma unroll
-      for (int mi = 0; mi < FM; ++mi)
-        fa[ks][mi] = *reinterpret_cast<const bf16x8*>(la + a_rd[ks] + mi * 32 * A_ROWB);
-#pragma unroll
-      for (int ni = 0; ni < FN; ++ni) {
-        const uint8_t* p = lb + ks * 16 * B_ROWB + b_rd[ni];
-        const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (__attribute__((address_space(3))) s16x4*)p);
-        const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (__attribute__((address_space(3))) s16x4*)(p + 4 * B_ROWB));
-        fb[ks][ni] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-      }
-    }
-  };
-
-  const int nk = (K + BK - 1) / BK;
-
-  // Prologue: stages 0..NSL-2 in flight, wait for stage 0.
-#pragma unroll
-  for (int q = 0; q < NSL - 1; ++q) dma_stage(q, q);
-  wait_vmcnt<(NSL - 2) * NDMA>();
-  stage_barrier();
-  if (grp == 1) stage_barrier();
-  int slot = 0;                 // s % NSL
-  int fill = NSL - 1;           // (s + NSL - 1) % NSL
-  for (int s = 0; s < nk; ++s) {
-    // mem(s)
-    dma_stage(s + NSL - 1, fill);
-    read_stage(slot);
-    wait_vmcnt<(NSL - 2) * NDMA>();
-    wait_lgkmcnt0();
-    stage_barrier();
-    __builtin_amdgcn_sched_barrier(0);
-    // comp(s)
-#pragma unroll
-    for (int ks = 0; ks < 2; ++ks)
-#pragma unroll
-      for (int mi = 0; mi < FM; ++mi)
-#pragma unroll
-        for (int ni = 0; ni < FN; ++ni)
-          acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[ks][mi], fb[ks][ni],
-                                                                acc[mi][ni], 0, 0, 0);
-    __builtin_amdgcn_sched_barrier(0);
-    stage_barrier();
-    slot = slot == NSL - 1 ? 0 : slot + 1;
-    fill = fill == NSL - 1 ? 0 : fill + 1;
-  }
-  if (grp == 0) stage_barrier();
-  wait_vmcnt<0>();
-  __syncthreads();
-
-  epilogue_lds<BN / WN>(smem, acc, epi, M, N, m0 + wr0, n0 + wc0, wave, lane);
-}
-
 // Tile configurations.  The choice minimises the estimated time: full
 // waves of tiles over the device's compute units times the tile's cost, the larger tiles being
 // cheaper per element (less LDS and L2 traffic per MFMA).
@@ -936,7 +757,8 @@ hipError_t launch_bf16(const uint16_t* A, int64_t lda, const uint16_t* B,
 }
 
 // K block (stage depth) of the kernel the dispatch picks for an [M, N]
-// output: 32 for the 256x256 ping-pong kernel, 64 for the others.
+// output: 32 for 256x256 tiles (five 32 KB stages fill the LDS), 64 for the
+// others.
 int a_block(const TileChoice& t) { return t.bm == 256 && t.bn == 256 ? 32 : 64; }
 
 // AKB: A is K-blocked by the chosen kernel's stage depth (see
@@ -950,12 +772,8 @@ hipError_t dispatch_bf16(const uint16_t* A, int64_t lda, const uint16_t* B,
   // (K-blocked A tiles are at most 32 KiB)
   if ((!AKB && lda >= ((int64_t)1 << 22)) || ldb >= ((int64_t)1 << 24)) return hipErrorInvalidValue;
   const TileChoice t = choose_bf16_tile(M, N);
-  if (t.bm == 256 && t.bn == 256) {
-    const int tm = (M + 255) / 256, tn = (N + 255) / 256;
-    hipLaunchKernelGGL((gemm_bf16_pp_kernel<Epi, AKB>), dim3(tm * tn), dim3(512), 0, s, A, lda,
-                       B, ldb, M, N, K, kwrap, tm, tn, epi);
-    return hipGetLastError();
-  }
+  if (t.bm == 256 && t.bn == 256)
+    return launch_bf16<256, 256, 2, 2, 2, 5, AKB>(A, lda, B, ldb, M, N, K, kwrap, epi, s);
   if (t.bm == 256 && t.bn == 128)
     return launch_bf16<256, 128, 2, 2, 4, 3, AKB>(A, lda, B, ldb, M, N, K, kwrap, epi, s);
   if (t.bm == 128 && t.bn == 192)
