@@ -16,19 +16,20 @@
 // picks the block size (256 when a dispatch estimate says it is faster:
 // long sequences or many heads) and the chunk size per shape.
 //
-// Precision: Q and K arrive as bf16 hi/lo pairs, V as an fp16 hi/lo pair.
-// Scores use three bf16 MFMA passes (Khi.Qhi + Khi.Qlo + Klo.Qhi, ~16
-// significant bits); the softmax runs in fp32 with exp2; probabilities are
-// rounded to fp16 (values in [0, 1], 11 significant bits) and the running
-// denominator sums exactly those rounded values; P.V uses two fp16 MFMA
-// passes (P.Vhi + P.Vlo).  O is written as a bf16 hi/lo pair, so the output
-// projection sees it with ~16 significant bits.  Causal attention over short
-// prefixes makes max|Y|/RMS(Y) large (row 0 is v_0 itself), which is what
-// rules out single bf16 roundings of P and O here.
+// Precision: Q and K arrive as fp16 values (11 significant bits), V as an
+// fp16 hi/lo pair.  Scores use one fp16 MFMA pass; the softmax runs in fp32
+// with exp2; probabilities are rounded to fp16 (values in [0, 1], 11
+// significant bits) and the running denominator sums exactly those rounded
+// values; P.V uses two fp16 MFMA passes (P.Vhi + P.Vlo).  O is written as a
+// bf16 hi/lo pair, so the output projection sees it with ~16 significant
+// bits.  Causal attention over short prefixes makes max|Y|/RMS(Y) large (row
+// 0 is v_0 itself), which is what rules out single roundings of V and O
+// here (an emulation of these rounding points on the CPU chose the split).
+// Q, K and V must lie within the fp16 range (|x| < 65504).
 //
 // Layout: a workgroup has 8 waves (two per SIMD, so one wave's LDS waits
 // overlap the other's MFMAs) of one or two groups of 16 queries each; per
-// 16-query group, with v_mfma_f32_16x16x32_bf16:
+// 16-query group, with v_mfma_f32_16x16x32_f16:
 //   * scores are computed transposed, S^T = K Q^T: A = K rows (keys),
 //     B = Q (queries), so each lane ends up owning one query (lane % 16)
 //     and four keys per 16-key block.  K rows are fed in the order that
@@ -51,7 +52,6 @@
 namespace tp {
 namespace {
 
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
@@ -67,6 +67,8 @@ constexpr int KT = 64;    // keys per tile
 constexpr int K_ROW = D * 2;      // 256-byte K rows (16 chunks)
 constexpr int V_ROW = KT * 2;     // 128-byte V^T rows (8 chunks)
 constexpr int TILE = KT * D * 2;  // 16 KiB per array
+constexpr int NARR = 3;           // arrays per key tile: K, V^T hi, V^T lo
+constexpr int NBUF = 3;           // key tiles in LDS: one multiplied, two landing
 constexpr int MAX_ITEMS = 4096;  // bounds the partial-result workspace
 
 __device__ __forceinline__ uint32_t f2bf(float f) {
@@ -131,9 +133,9 @@ attn_fwd_kernel(QkvOut q, int causal, uint16_t* __restrict__ O, int o_kbs,
                 float* __restrict__ part, AttnSplit sp, float scale_log2) {
   constexpr int QW = 16 * NQG;    // queries per wave
   constexpr int QB = NWAVE * QW;  // queries per workgroup
-  // Two LDS buffers of K hi, K lo, V^T hi, V^T lo tiles: one is read by the
-  // products while the next tile is staged into the other.
-  __shared__ __attribute__((aligned(16))) uint8_t smem[2 * 4 * TILE];
+  // Three LDS buffers of K, V^T hi, V^T lo tiles (144 KB): one is read by
+  // the products while the next two tiles land in the others.
+  __shared__ __attribute__((aligned(16))) uint8_t smem[NBUF * NARR * TILE];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform per wave
@@ -152,10 +154,8 @@ attn_fwd_kernel(QkvOut q, int causal, uint16_t* __restrict__ O, int o_kbs,
   const int kt1 = kt0 + sp.ch < ntile ? kt0 + sp.ch : ntile;
 
   const int64_t hoff = (int64_t)bh * Sp * D;
-  const uint16_t* Qh = q.q_hi + hoff;
-  const uint16_t* Ql = q.q_lo + hoff;
-  const uint16_t* Kh = q.k_hi + hoff;
-  const uint16_t* Kl = q.k_lo + hoff;
+  const uint16_t* Qp = q.q + hoff;
+  const uint16_t* Kp = q.k + hoff;
   const uint16_t* Vh = q.vt_hi + hoff;
   const uint16_t* Vl = q.vt_lo + hoff;
 
@@ -165,18 +165,16 @@ attn_fwd_kernel(QkvOut q, int causal, uint16_t* __restrict__ O, int o_kbs,
   for (int qg = 0; qg < NQG; ++qg) myq[qg] = qb * QB + wave * QW + qg * 16 + (lane & 15);
 
   // Q as the B operand: query myq, head dims dc*32 + 8g .. +7.
-  bf16x8 qh[NQG][4], ql[NQG][4];
+  f16x8 qf[NQG][4];
 #pragma unroll
   for (int qg = 0; qg < NQG; ++qg)
 #pragma unroll
     for (int dc = 0; dc < 4; ++dc) {
       if (myq[qg] < S) {
-        qh[qg][dc] = *reinterpret_cast<const bf16x8*>(Qh + (int64_t)myq[qg] * D + dc * 32 + 8 * g);
-        ql[qg][dc] = *reinterpret_cast<const bf16x8*>(Ql + (int64_t)myq[qg] * D + dc * 32 + 8 * g);
+        qf[qg][dc] = *reinterpret_cast<const f16x8*>(Qp + (int64_t)myq[qg] * D + dc * 32 + 8 * g);
       } else {
         const u32x4 z = {0, 0, 0, 0};
-        qh[qg][dc] = __builtin_bit_cast(bf16x8, z);
-        ql[qg][dc] = qh[qg][dc];
+        qf[qg][dc] = __builtin_bit_cast(f16x8, z);
       }
     }
 
@@ -193,8 +191,8 @@ attn_fwd_kernel(QkvOut q, int causal, uint16_t* __restrict__ O, int o_kbs,
   }
 
   // Tiles go from global memory straight into LDS (buffer loads that write
-  // LDS): while tile kt is multiplied from one buffer, tile kt+1 lands in
-  // the other.  Each 1 KiB DMA covers 4 K rows (256 B) or 8 V^T rows
+  // LDS): while tile kt is multiplied from one buffer, tiles kt+1 and kt+2
+  // land in the other two.  Each 1 KiB DMA covers 4 K rows (256 B) or 8 V^T rows
   // (128 B); lane l writes bytes 16l..16l+15 of it, so the chunk swizzles
   // are applied to the global addresses.  K rows past the sequence fall
   // outside the buffer descriptor and read as zero; V^T columns past it are
@@ -211,50 +209,59 @@ attn_fwd_kernel(QkvOut q, int causal, uint16_t* __restrict__ O, int o_kbs,
     v_off[j] = rv * Sp * 2 + ((pv ^ vswz(rv)) << 4);
   }
   auto stage = [&](int k0, int buf) {
-    const uint32_t base = lds0 + buf * 4 * TILE;
+    const uint32_t base = lds0 + buf * NARR * TILE;
     const int64_t kbytes = (int64_t)(S - k0) * D * 2;
     const int64_t vbytes = ((int64_t)D * Sp - k0) * 2;
-    const __amdgpu_buffer_rsrc_t rkh = make_rsrc(Kh + (int64_t)k0 * D, kbytes);
-    const __amdgpu_buffer_rsrc_t rkl = make_rsrc(Kl + (int64_t)k0 * D, kbytes);
+    const __amdgpu_buffer_rsrc_t rk = make_rsrc(Kp + (int64_t)k0 * D, kbytes);
     const __amdgpu_buffer_rsrc_t rvh = make_rsrc(Vh + k0, vbytes);
     const __amdgpu_buffer_rsrc_t rvl = make_rsrc(Vl + k0, vbytes);
 #pragma unroll
     for (int j = 0; j < NDW; ++j) {
       const uint32_t blk = (j * NWAVE + wave) * 1024;
-      dma16(rkh, k_off[j], base + blk);
-      dma16(rkl, k_off[j], base + TILE + blk);
-      dma16(rvh, v_off[j], base + 2 * TILE + blk);
-      dma16(rvl, v_off[j], base + 3 * TILE + blk);
+      dma16(rk, k_off[j], base + blk);
+      dma16(rvh, v_off[j], base + TILE + blk);
+      dma16(rvl, v_off[j], base + 2 * TILE + blk);
     }
   };
+  // This wave's DMAs per key tile; waiting until at most that many are in
+  // flight leaves exactly the latest tile's loads outstanding.
+  constexpr int TILE_DMAS = NARR * NDW;
 
   stage(kt0 * KT, 0);
-  wait_vmcnt<0>();
+  if (kt0 + 1 < kt1) {
+    stage((kt0 + 1) * KT, 1);
+    wait_vmcnt<TILE_DMAS>();
+  } else {
+    wait_vmcnt<0>();
+  }
   __syncthreads();
   for (int kt = kt0; kt < kt1; ++kt) {
     const int k0 = kt * KT;
-    const int cur = (kt - kt0) & 1;
-    // Tile kt+1 into the other buffer; its last reader, tile kt-1, finished
+    const int cur = (kt - kt0) % NBUF;
+    // Tile kt+2 into the third buffer; its last reader, tile kt-1, finished
     // before the barrier that ended the previous step.
-    if (kt + 1 < kt1) stage(k0 + KT, cur ^ 1);
+    const bool ahead2 = kt + 2 < kt1;
+    if (ahead2) stage(k0 + 2 * KT, cur == 0 ? 2 : cur - 1);
     // Causal: a tile that starts after this wave's last query is masked for
     // all of its queries and changes neither their softmax state nor O, so
     // the wave only takes part in the tile's loads and its closing barrier.
     if (causal && k0 > qb * QB + wave * QW + QW - 1) {
-      wait_vmcnt<0>();
+      if (ahead2)
+        wait_vmcnt<TILE_DMAS>();
+      else
+        wait_vmcnt<0>();
       __syncthreads();
       continue;
     }
-    const uint8_t* const sKh = smem + cur * 4 * TILE;
-    const uint8_t* const sKl = sKh + TILE;
-    const uint8_t* const sVh = sKh + 2 * TILE;
-    const uint8_t* const sVl = sKh + 3 * TILE;
+    const uint8_t* const sK = smem + cur * NARR * TILE;
+    const uint8_t* const sVh = sK + TILE;
+    const uint8_t* const sVl = sK + 2 * TILE;
 
     // ---- scores S^T for four 16-key blocks (chunk kc, half hb) ----
-    // The eight K fragments of 32-dim slice dc+1 are read while slice dc's
-    // 24 MFMAs run (two register sets), and the MFMAs cycle over the eight
-    // independent accumulators, so neither LDS latency nor an MFMA result
-    // holds the matrix pipe.
+    // The four K fragments of 32-dim slice dc+1 are read while slice dc's
+    // MFMAs run (two register sets), and the MFMAs cycle over independent
+    // accumulators, so neither LDS latency nor an MFMA result holds the
+    // matrix pipe.
     f32x4 s[NQG][2][2];  // [query group][kc][hb]
 #pragma unroll
     for (int qg = 0; qg < NQG; ++qg)
@@ -262,7 +269,7 @@ attn_fwd_kernel(QkvOut q, int causal, uint16_t* __restrict__ O, int o_kbs,
       for (int kc = 0; kc < 2; ++kc)
 #pragma unroll
         for (int hb = 0; hb < 2; ++hb) s[qg][kc][hb] = f32x4{0, 0, 0, 0};
-    bf16x8 kh[2][2][2], kl[2][2][2];  // [set][kc][hb]
+    f16x8 kf[2][2][2];  // [set][kc][hb]
     auto kread = [&](int set, int dc) {
 #pragma unroll
       for (int kc = 0; kc < 2; ++kc)
@@ -271,8 +278,7 @@ attn_fwd_kernel(QkvOut q, int causal, uint16_t* __restrict__ O, int o_kbs,
           const int i = lane & 15;
           const int krow = kc * 32 + 8 * (i >> 2) + 4 * hb + (i & 3);
           const int off = krow * K_ROW + (((dc * 4 + g) ^ kswz(krow)) << 4);
-          kh[set][kc][hb] = *reinterpret_cast<const bf16x8*>(sKh + off);
-          kl[set][kc][hb] = *reinterpret_cast<const bf16x8*>(sKl + off);
+          kf[set][kc][hb] = *reinterpret_cast<const f16x8*>(sK + off);
         }
     };
     kread(0, 0);
@@ -281,18 +287,13 @@ attn_fwd_kernel(QkvOut q, int causal, uint16_t* __restrict__ O, int o_kbs,
       const int set = dc & 1;
       if (dc + 1 < 4) kread(set ^ 1, dc + 1);
 #pragma unroll
-      for (int pass = 0; pass < 3; ++pass)
+      for (int kc = 0; kc < 2; ++kc)
 #pragma unroll
-        for (int kc = 0; kc < 2; ++kc)
+        for (int hb = 0; hb < 2; ++hb)
 #pragma unroll
-          for (int hb = 0; hb < 2; ++hb)
-#pragma unroll
-            for (int qg = 0; qg < NQG; ++qg) {
-              const bf16x8 a = pass == 2 ? kl[set][kc][hb] : kh[set][kc][hb];
-              const bf16x8 bq = pass == 1 ? ql[qg][dc] : qh[qg][dc];
-              s[qg][kc][hb] =
-                  __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, bq, s[qg][kc][hb], 0, 0, 0);
-            }
+          for (int qg = 0; qg < NQG; ++qg)
+            s[qg][kc][hb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kf[set][kc][hb], qf[qg][dc],
+                                                                  s[qg][kc][hb], 0, 0, 0);
     }
 
     // V fragments of the first PV group, read during the softmax below.
@@ -386,7 +387,12 @@ attn_fwd_kernel(QkvOut q, int causal, uint16_t* __restrict__ O, int o_kbs,
                                                                pb[qg][kc], o[qg][db], 0, 0, 0);
           }
     }
-    wait_vmcnt<0>();  // tile kt+1 has landed (this wave's part of it)
+    // tile kt+1 has landed (this wave's part of it; tile kt+2's may still
+    // be in flight) ...
+    if (ahead2)
+      wait_vmcnt<TILE_DMAS>();
+    else
+      wait_vmcnt<0>();
     __syncthreads();  // ... everyone's; and tile kt is no longer read
   }
 

@@ -240,17 +240,13 @@ struct EpiQkv {
     const int s = row - b * q.seq;
     const int64_t bh = (int64_t)b * q.nl + head;
     if (sec < 2) {
-      // bf16 hi/lo pair: hi = bf16(v), lo = bf16(v - hi)
-      const uint32_t h01 = pack_bf16(v[0], v[1]), h23 = pack_bf16(v[2], v[3]);
-      const uint32_t l01 = pack_bf16(v[0] - __uint_as_float(h01 << 16),
-                                     v[1] - __uint_as_float(h01 & 0xFFFF0000u));
-      const uint32_t l23 = pack_bf16(v[2] - __uint_as_float(h23 << 16),
-                                     v[3] - __uint_as_float(h23 & 0xFFFF0000u));
+      // Q, K: fp16, rounded to nearest even
+      uint32_t w[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) w[r] = __builtin_bit_cast(uint16_t, (_Float16)v[r]);
       const int64_t off = (bh * q.seq_pad + s) * 128 + dd;
-      uint16_t* ph = sec == 0 ? q.q_hi : q.k_hi;
-      uint16_t* pl = sec == 0 ? q.q_lo : q.k_lo;
-      *reinterpret_cast<uint2*>(ph + off) = uint2{h01, h23};
-      *reinterpret_cast<uint2*>(pl + off) = uint2{l01, l23};
+      *reinterpret_cast<uint2*>((sec == 0 ? q.q : q.k) + off) =
+          uint2{w[0] | (w[1] << 16), w[2] | (w[3] << 16)};
     } else {
       // V: fp16 hi/lo pair (the probabilities multiplying it are fp16)
       const int64_t off = (bh * 128 + dd) * q.seq_pad + s;

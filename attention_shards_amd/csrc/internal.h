@@ -18,16 +18,14 @@ int device_cu_count();
 enum OutType { OUT_F32 = 0, OUT_BF16 = 1 };
 
 // Where the QKV projection's epilogue scatters its columns.  All buffers are
-// 16-bit words.  Q and K are [batch][nl][seq_pad][d] (d contiguous), each a
-// bf16 hi/lo pair: hi = bf16(v), lo = bf16(v - hi).  V is stored transposed,
-// [batch][nl][d][seq_pad] (sequence contiguous), because it is the row
-// operand of the probability-times-value product, as an fp16 hi/lo pair
-// (the probabilities are fp16).
+// 16-bit words.  Q and K are fp16, [batch][nl][seq_pad][d] (d contiguous).
+// V is stored transposed, [batch][nl][d][seq_pad] (sequence contiguous),
+// because it is the row operand of the probability-times-value product, as
+// an fp16 hi/lo pair (the probabilities are fp16): hi = fp16(v),
+// lo = fp16(v - hi).
 struct QkvOut {
-  uint16_t* q_hi;
-  uint16_t* q_lo;
-  uint16_t* k_hi;
-  uint16_t* k_lo;
+  uint16_t* q;
+  uint16_t* k;
   uint16_t* vt_hi;
   uint16_t* vt_lo;
   int32_t seq;      // tokens per sequence

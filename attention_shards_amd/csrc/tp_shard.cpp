@@ -90,9 +90,10 @@ constexpr int64_t kAttnKeyTile = 64;
 
 int64_t align256(int64_t b) { return (b + 255) / 256 * 256; }
 
-// Attention workspace: six [batch*nl, seq_pad, d] 16-bit arrays (Q, K, V^T as
-// hi/lo pairs) followed by O [batch*seq, 2*nl*d] bf16 (hi half, lo half).
-// ... followed by the partial results of split query blocks (fp32).
+// Attention workspace: four [batch*nl, seq_pad, d] 16-bit arrays (Q, K in
+// fp16, V^T as an fp16 hi/lo pair) followed by O [batch*seq, 2*nl*d] bf16
+// (hi half, lo half), then the partial results of split query blocks (fp32).
+constexpr int64_t kAttnParts = 4;
 struct AttnLayout {
   int64_t seq_pad, part_bytes, o_bytes, split_bytes, total;
 };
@@ -102,7 +103,7 @@ AttnLayout attn_layout(int64_t batch, int64_t seq, int64_t nl, int64_t d) {
   L.part_bytes = align256(batch * nl * L.seq_pad * d * 2);
   L.o_bytes = align256(batch * seq * 2 * nl * d * 2);
   L.split_bytes = align256(tp::attn_partial_bytes((int)batch, (int)seq, (int)nl));
-  L.total = 6 * L.part_bytes + L.o_bytes + L.split_bytes;
+  L.total = kAttnParts * L.part_bytes + L.o_bytes + L.split_bytes;
   return L;
 }
 
@@ -524,17 +525,15 @@ tp_status_t tp_attn_shard(const void* X, const void* Wqkv_i, const void* Wo_i,
 
     uint8_t* ws = static_cast<uint8_t*>(workspace);
     tp::QkvOut q;
-    q.q_hi = reinterpret_cast<uint16_t*>(ws + 0 * L.part_bytes);
-    q.q_lo = reinterpret_cast<uint16_t*>(ws + 1 * L.part_bytes);
-    q.k_hi = reinterpret_cast<uint16_t*>(ws + 2 * L.part_bytes);
-    q.k_lo = reinterpret_cast<uint16_t*>(ws + 3 * L.part_bytes);
-    q.vt_hi = reinterpret_cast<uint16_t*>(ws + 4 * L.part_bytes);
-    q.vt_lo = reinterpret_cast<uint16_t*>(ws + 5 * L.part_bytes);
+    q.q = reinterpret_cast<uint16_t*>(ws + 0 * L.part_bytes);
+    q.k = reinterpret_cast<uint16_t*>(ws + 1 * L.part_bytes);
+    q.vt_hi = reinterpret_cast<uint16_t*>(ws + 2 * L.part_bytes);
+    q.vt_lo = reinterpret_cast<uint16_t*>(ws + 3 * L.part_bytes);
     q.seq = (int32_t)seq;
     q.seq_pad = (int32_t)L.seq_pad;
     q.nl = (int32_t)nl;
     q.d = head_dim;
-    uint16_t* O = reinterpret_cast<uint16_t*>(ws + 6 * L.part_bytes);
+    uint16_t* O = reinterpret_cast<uint16_t*>(ws + kAttnParts * L.part_bytes);
 
     hipStream_t s = static_cast<hipStream_t>(stream);
     (void)hipGetLastError();
@@ -542,7 +541,7 @@ tp_status_t tp_attn_shard(const void* X, const void* Wqkv_i, const void* Wo_i,
                                      static_cast<const uint16_t*>(Wqkv_i), nqkv, q,
                                      (int)tokens, (int)nqkv, (int)hidden, s);
     if (e != hipSuccess) return hip_status(e, "tp_attn_shard: QKV launch");
-    float* part = reinterpret_cast<float*>(ws + 6 * L.part_bytes + L.o_bytes);
+    float* part = reinterpret_cast<float*>(ws + kAttnParts * L.part_bytes + L.o_bytes);
     // O is written K-blocked in the stage depth of the output projection's
     // kernel, so each of its A stages is one contiguous run.
     const int o_kb = tp::gemm_bf16_a_block((int)tokens, (int)hidden);

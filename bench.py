@@ -788,6 +788,8 @@ def main():
                     help="time the headline FFN shard only (profiling runs)")
     ap.add_argument("--reduce-only", action="store_true",
                     help="time the two rotated reduce rows only (profiling runs)")
+    ap.add_argument("--attn-only", action="store_true",
+                    help="time the attention shard row only (profiling runs)")
     ap.add_argument("--no-sweep-torch", action="store_true",
                     help="skip the torch (hipBLASLt) comparison at each sweep point")
     ap.add_argument("--sweep-out", metavar="JSONL", default=None,
@@ -839,6 +841,9 @@ def main():
     if args.reduce_only:
         for t, rows, cols in REDUCE_SHAPES:
             log(json.dumps(reduce_rotated(t, rows, cols, K, W)))
+        return
+    if args.attn_only:
+        log(json.dumps(attn_row(K, W)))
         return
 
     # ---------------- headline: the sweep's hidden-22528, t=1 FFN shard ----------------

@@ -168,12 +168,14 @@ tp_status_t tp_ffn_shard_noalloc(const void* X, const void* W1_i, const void* W2
  *   causal                          1: key j is kept for query s iff j <= s;
  *                                   0: all keys kept
  *   in_dtype                        TP_BF16 only
- * Internals (exposed only through the workspace size): Q and K are kept as
- * bf16 hi+lo pairs (hi = bf16(v), lo = bf16(v - hi)) and V as an fp16 hi+lo
- * pair, so the score and value products carry about 16 significant bits;
- * softmax runs in fp32 with the probabilities rounded to fp16; the head
- * outputs O are kept as a bf16 hi+lo pair, which the output projection
- * multiplies by Wo_i in two passes.
+ * Internals (exposed only through the workspace size): Q and K are kept in
+ * fp16 (11 significant bits) and V as an fp16 hi+lo pair (hi = fp16(v),
+ * lo = fp16(v - hi)), so the value product carries about 22 significant
+ * bits; softmax runs in fp32 with the probabilities rounded to fp16; the
+ * head outputs O are kept as a bf16 hi+lo pair, which the output projection
+ * multiplies by Wo_i in two passes.  Q, K and V must lie within the fp16
+ * range (|value| < 65504).  The workspace size depends on the current
+ * device's compute-unit count (the attention work split does).
  * Shape rules: batch, seq >= 0; head_dim == 128; hidden multiple of 8;
  * batch*seq below 2^31; hidden and 2*(n_heads/t)*head_dim below 2^22; seq
  * below 2^23 (32-bit tile offsets in the GEMMs and the attention kernel).
