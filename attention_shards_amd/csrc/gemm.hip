@@ -480,19 +480,21 @@ __device__ __forceinline__ void epilogue_lds(uint8_t* smem, f32x16 (&acc)[FM][FN
 // KS MFMA k-steps of 16 per pipeline stage (stage K = BK = 16 KS) and an LDS
 // ring of NSL stages.  KS = 2 gives 64-byte A rows per stage; KS = 4 gives
 // 128-byte A rows (a whole cache line per row per DMA), at the price of
-// fewer, larger ring slots.
-template <int BM, int BN, int WM, int WN, int KS, int NSL, class Epi, bool AKB>
+// fewer, larger ring slots.  NA = 2: C = (A_1 + A_2) B with A = [A_1 | A_2]
+// K-blocked, [2 ceil(K/BK)][lda][BK], A_2's blocks after A_1's: every stage
+// brings the two A tiles and one B tile, and both products use the same B
+// fragments (half the B traffic of two passes over K).
+template <int BM, int BN, int WM, int WN, int KS, int NSL, class Epi, bool AKB, int NA = 1>
 __global__ void __launch_bounds__(WM * WN * 64)
 gemm_bf16_kernel(const uint16_t* __restrict__ A, int64_t lda,
                  const uint16_t* __restrict__ B, int64_t ldb, int M, int N,
-                 int K, int kwrap, int tiles_m, int tiles_n, Epi epi) {
-  // Stage kt reads B rows from (k0 < kwrap ? k0 : k0 - kwrap); with kwrap < K
-  // (K == 2 kwrap, kwrap a multiple of BK) the same B multiplies both halves
-  // of an A laid out as [A_hi | A_lo].  With AKB, A is K-blocked by the
-  // stage depth BK: [ceil(K/BK)][lda][BK], lda the padded row count, so a
-  // stage's A tile is one contiguous run of rows.
+                 int K, int tiles_m, int tiles_n, Epi epi) {
+  // With AKB, A is K-blocked by the stage depth BK: [ceil(K/BK)][lda][BK],
+  // lda the padded row count, so a stage's A tile is one contiguous run of
+  // rows.
   static_assert(KS == 2 || KS == 4, "k-steps per stage");
   static_assert(NSL >= 3 && NSL <= 6, "ring slots");
+  static_assert(NA == 1 || (NA == 2 && AKB), "paired A operands are K-blocked");
   constexpr int BK = 16 * KS;
   constexpr int NW = WM * WN;
   constexpr int FM = BM / WM / 32;
@@ -507,19 +509,20 @@ gemm_bf16_kernel(const uint16_t* __restrict__ A, int64_t lda,
   constexpr int B_STAGE = BK * B_ROWB;
   constexpr int A_DMA = A_STAGE / 1024 / NW;  // 1 KiB DMAs per wave per stage
   constexpr int B_DMA = B_STAGE / 1024 / NW;
-  constexpr int NDMA = A_DMA + B_DMA;
+  constexpr int NDMA = NA * A_DMA + B_DMA;
   static_assert(A_DMA * 1024 * NW == A_STAGE && B_DMA * 1024 * NW == B_STAGE, "DMA split");
   static_assert(B_CH % 16 == 0 || B_CH == 24, "B swizzle: 256-byte multiple or 384-byte rows");
   static_assert(FM >= 1 && FN >= 1, "wave tile");
 
-  // LDS ring: slot s holds A at s*A_STAGE and B at NSL*A_STAGE + s*B_STAGE.
-  // The same memory later stages the epilogue (NW regions of 32 x (BN/WN+4)).
-  constexpr int PIPE_BYTES = NSL * (A_STAGE + B_STAGE);
+  // LDS ring: slot s holds A operand o at (s*NA + o)*A_STAGE and B at
+  // NSL*NA*A_STAGE + s*B_STAGE.  The same memory later stages the epilogue
+  // (NW regions of 32 x (BN/WN+4)).
+  constexpr int PIPE_BYTES = NSL * (NA * A_STAGE + B_STAGE);
   constexpr int EPI_BYTES = NW * 32 * (BN / WN + 4) * 4;
   __shared__ __attribute__((aligned(16))) uint8_t
       smem[PIPE_BYTES > EPI_BYTES ? PIPE_BYTES : EPI_BYTES];
   uint8_t* const lds_a = smem;
-  uint8_t* const lds_b = smem + NSL * A_STAGE;
+  uint8_t* const lds_b = smem + NSL * NA * A_STAGE;
   const uint32_t lds_a_addr = (uint32_t)(uintptr_t)(lds_u8*)lds_a;
   const uint32_t lds_b_addr = (uint32_t)(uintptr_t)(lds_u8*)lds_b;
 
@@ -562,23 +565,25 @@ gemm_bf16_kernel(const uint16_t* __restrict__ A, int64_t lda,
     b_off[j] = row * (int)ldb * 2 + c * 16;
   }
 
+  // K blocks of each A operand (A_2's blocks start after A_1's)
+  const int a_blocks = (K + BK - 1) / BK;
   // DMA number j (0 <= j < NDMA) of stage kt into ring slot SLOT.
   auto dma = [&](int kt, auto SLOT, int j) {
     constexpr int slot = decltype(SLOT)::value;
     const int k0 = kt * BK;
-    if (j < A_DMA) {
+    if (j < NA * A_DMA) {
+      const int op = j / A_DMA, ja = j - op * A_DMA;
+      const int blk = kt + op * a_blocks;
       const __amdgpu_buffer_rsrc_t ra =
-          AKB ? make_rsrc(A + ((int64_t)kt * lda + m0) * BK, (int64_t)rows_valid * A_ROWB)
+          AKB ? make_rsrc(A + ((int64_t)blk * lda + m0) * BK, (int64_t)rows_valid * A_ROWB)
               : make_rsrc(A + (int64_t)m0 * lda + k0, (int64_t)rows_valid * lda * 2 - (int64_t)k0 * 2);
-      const int off = (k0 + a_col[j] < K) ? a_off[j] : OOB;
-      dma16(ra, off, lds_a_addr + slot * A_STAGE + (j * NW + wave) * 1024);
+      const int off = (k0 + a_col[ja] < K) ? a_off[ja] : OOB;
+      dma16(ra, off, lds_a_addr + (slot * NA + op) * A_STAGE + (ja * NW + wave) * 1024);
     } else {
-      const int jb = j - A_DMA;
-      const int bk0 = k0 < kwrap ? k0 : k0 - kwrap;
-      const int rows_left = (k0 < kwrap ? kwrap : K) - k0;
+      const int jb = j - NA * A_DMA;
       const __amdgpu_buffer_rsrc_t rb =
-          make_rsrc(B + (int64_t)bk0 * ldb + n0,
-                    ((int64_t)rows_left - 1) * ldb * 2 + (int64_t)cols_valid * 2);
+          make_rsrc(B + (int64_t)k0 * ldb + n0,
+                    ((int64_t)(K - k0) - 1) * ldb * 2 + (int64_t)cols_valid * 2);
       dma16(rb, b_off[jb], lds_b_addr + slot * B_STAGE + (jb * NW + wave) * 1024);
     }
   };
@@ -615,10 +620,10 @@ gemm_bf16_kernel(const uint16_t* __restrict__ A, int64_t lda,
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[mi][ni][e] = 0.0f;
 
-  bf16x8 fa[2][FM], fb[2][FN];
+  bf16x8 fa[2][NA][FM], fb[2][FN];
   // Fragment read unit q of k-step ks from ring slot SLOT into set fset:
   // units 0..FN-1 are B fragments (two transposed reads each), units
-  // FN..FN+FM-1 are A fragments.
+  // FN..FN+NA*FM-1 are A fragments (operand by operand).
   auto read_unit = [&](auto SLOT, int ks, int fset, int q) {
     constexpr int slot = decltype(SLOT)::value;
     if (q < FN) {
@@ -629,14 +634,17 @@ gemm_bf16_kernel(const uint16_t* __restrict__ A, int64_t lda,
           (__attribute__((address_space(3))) s16x4*)(lb + 4 * B_ROWB));
       fb[fset][q] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
     } else {
-      const int mi = q - FN;
-      fa[fset][mi] = *reinterpret_cast<const bf16x8*>(lds_a + slot * A_STAGE + a_rd[ks] +
-                                                     mi * 32 * A_ROWB);
+      const int op = (q - FN) / FM, mi = (q - FN) - op * FM;
+      fa[fset][op][mi] = *reinterpret_cast<const bf16x8*>(
+          lds_a + (slot * NA + op) * A_STAGE + a_rd[ks] + mi * 32 * A_ROWB);
     }
   };
-  auto mfma1 = [&](int fset, int idx) {  // one MFMA of a k-step, idx in [0, FM*FN)
-    const int mi = idx / FN, ni = idx % FN;
-    acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[fset][mi], fb[fset][ni],
+  // one MFMA of a k-step, idx in [0, NA*FM*FN): operand by operand, so an
+  // accumulator's two products of a k-step are FM*FN MFMAs apart
+  auto mfma1 = [&](int fset, int idx) {
+    const int op = idx / (FM * FN), r = idx - op * (FM * FN);
+    const int mi = r / FN, ni = r % FN;
+    acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[fset][op][mi], fb[fset][ni],
                                                           acc[mi][ni], 0, 0, 0);
   };
 
@@ -659,8 +667,8 @@ gemm_bf16_kernel(const uint16_t* __restrict__ A, int64_t lda,
   //   barrier;
   //   k-step KS-1: the fragment reads of k-step 0 of stage kt+1.
   // Fragment register sets alternate with the k-step's parity (KS even).
-  constexpr int NMF = FM * FN;   // MFMAs per k-step
-  constexpr int NRU = FM + FN;   // fragment read units per k-step
+  constexpr int NMF = NA * FM * FN;  // MFMAs per k-step
+  constexpr int NRU = NA * FM + FN;  // fragment read units per k-step
   constexpr int DSLOTS = (KS - 1) * NMF;
   static_assert(NDMA <= DSLOTS && NRU <= NMF, "traffic fits between the MFMAs");
   // MFMA slot after which DMA d of a step is issued
@@ -741,14 +749,12 @@ TileChoice choose_bf16_tile(int M, int N) {
   return cand[best];
 }
 
-template <int BM, int BN, int WM, int WN, int KS, int NSL, bool AKB, class Epi>
+template <int BM, int BN, int WM, int WN, int KS, int NSL, bool AKB, class Epi, int NA = 1>
 hipError_t launch_bf16(const uint16_t* A, int64_t lda, const uint16_t* B,
-                       int64_t ldb, int M, int N, int K, int kwrap,
-                       const Epi& epi, hipStream_t s) {
+                       int64_t ldb, int M, int N, int K, const Epi& epi, hipStream_t s) {
   const int tm = (M + BM - 1) / BM, tn = (N + BN - 1) / BN;
-  hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, WM, WN, KS, NSL, Epi, AKB>), dim3(tm * tn),
-                     dim3(WM * WN * 64), 0, s, A, lda, B, ldb, M, N, K, kwrap,
-                     tm, tn, epi);
+  hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, WM, WN, KS, NSL, Epi, AKB, NA>), dim3(tm * tn),
+                     dim3(WM * WN * 64), 0, s, A, lda, B, ldb, M, N, K, tm, tn, epi);
   return hipGetLastError();
 }
 
@@ -761,20 +767,19 @@ int a_block(const TileChoice& t) { return t.bm == 256 && t.bn == 256 ? 32 : 64; 
 // gemm_bf16_kernel), lda its row count; the caller has checked the block.
 template <bool AKB, class Epi>
 hipError_t dispatch_bf16(const uint16_t* A, int64_t lda, const uint16_t* B,
-                         int64_t ldb, int M, int N, int K, int kwrap,
-                         const Epi& epi, hipStream_t s) {
+                         int64_t ldb, int M, int N, int K, const Epi& epi, hipStream_t s) {
   if (M == 0 || N == 0) return hipSuccess;
   // tiles are addressed with 32-bit byte offsets: 256 rows of A, 64 of B
   // (K-blocked A tiles are at most 32 KiB)
   if ((!AKB && lda >= ((int64_t)1 << 22)) || ldb >= ((int64_t)1 << 24)) return hipErrorInvalidValue;
   const TileChoice t = choose_bf16_tile(M, N);
   if (t.bm == 256 && t.bn == 256)
-    return launch_bf16<256, 256, 2, 2, 2, 5, AKB>(A, lda, B, ldb, M, N, K, kwrap, epi, s);
+    return launch_bf16<256, 256, 2, 2, 2, 5, AKB>(A, lda, B, ldb, M, N, K, epi, s);
   if (t.bm == 256 && t.bn == 128)
-    return launch_bf16<256, 128, 2, 2, 4, 3, AKB>(A, lda, B, ldb, M, N, K, kwrap, epi, s);
+    return launch_bf16<256, 128, 2, 2, 4, 3, AKB>(A, lda, B, ldb, M, N, K, epi, s);
   if (t.bm == 128 && t.bn == 192)
-    return launch_bf16<128, 192, 2, 2, 4, 3, AKB>(A, lda, B, ldb, M, N, K, kwrap, epi, s);
-  return launch_bf16<128, 128, 2, 2, 4, 3, AKB>(A, lda, B, ldb, M, N, K, kwrap, epi, s);
+    return launch_bf16<128, 192, 2, 2, 4, 3, AKB>(A, lda, B, ldb, M, N, K, epi, s);
+  return launch_bf16<128, 128, 2, 2, 4, 3, AKB>(A, lda, B, ldb, M, N, K, epi, s);
 }
 
 // X [M, K] row-major (row stride lda) -> K-blocked [ceil(K/kb)][M][kb]
@@ -918,15 +923,7 @@ hipError_t gemm_bf16_store_kb(const uint16_t* A, int kb, const uint16_t* B, int6
                               void* C, int64_t ldc, OutType out, int M, int N, int K,
                               hipStream_t s) {
   if (M > 0 && N > 0 && kb != a_block(choose_bf16_tile(M, N))) return hipErrorInvalidValue;
-  return dispatch_bf16<true>(A, M, B, ldb, M, N, K, K, EpiStore{C, ldc, (int)out}, s);
-}
-
-hipError_t gemm_bf16_store_split_a_kb(const uint16_t* A2, int kb, const uint16_t* B,
-                                      int64_t ldb, void* C, int64_t ldc, OutType out, int M,
-                                      int N, int K, hipStream_t s) {
-  if (K % 64) return hipErrorInvalidValue;
-  if (M > 0 && N > 0 && kb != a_block(choose_bf16_tile(M, N))) return hipErrorInvalidValue;
-  return dispatch_bf16<true>(A2, M, B, ldb, M, N, 2 * K, K, EpiStore{C, ldc, (int)out}, s);
+  return dispatch_bf16<true>(A, M, B, ldb, M, N, K, EpiStore{C, ldc, (int)out}, s);
 }
 
 hipError_t kblock_bf16(const uint16_t* A, int64_t lda, uint16_t* out, int M, int K, int kb,
@@ -948,7 +945,31 @@ hipError_t gemm_bf16_gelu_akb(const uint16_t* Akb, int kb, const uint16_t* B, in
   if (kb_out != 32 && kb_out != 64) return hipErrorInvalidValue;
   if (M > 0 && N > 0 && kb != a_block(choose_bf16_tile(M, N))) return hipErrorInvalidValue;
   const int sh = kb_out == 32 ? 5 : 6;
-  return dispatch_bf16<true>(Akb, M, B, ldb, M, N, K, K, EpiGelu{C, 0, (int)OUT_BF16, M, sh}, s);
+  return dispatch_bf16<true>(Akb, M, B, ldb, M, N, K, EpiGelu{C, 0, (int)OUT_BF16, M, sh}, s);
+}
+
+// The paired product's tiles: 256x256 (three 48 KB slots) or 256x128 (four
+// 40 KB slots), both K = 32 per stage; the same cost estimate as the plain
+// products (full waves of tiles times the tile's cost).
+TileChoice choose_pair_tile(int M, int N) {
+  const int64_t ncu = device_cu_count();
+  const int64_t t256 = (int64_t)((M + 255) / 256) * ((N + 255) / 256);
+  const int64_t t128 = (int64_t)((M + 255) / 256) * ((N + 127) / 128);
+  const double c256 = (double)((t256 + ncu - 1) / ncu) * 256 * 256 / 1.0;
+  const double c128 = (double)((t128 + ncu - 1) / ncu) * 256 * 128 / 0.95;
+  return c256 <= c128 * 1.001 ? TileChoice{256, 256} : TileChoice{256, 128};
+}
+
+hipError_t gemm_bf16_store_pair_kb(const uint16_t* A2, const uint16_t* B, int64_t ldb, void* C,
+                                   int64_t ldc, OutType out, int M, int N, int K,
+                                   hipStream_t s) {
+  if (K % 32 || ldb >= ((int64_t)1 << 24)) return hipErrorInvalidValue;
+  if (M == 0 || N == 0) return hipSuccess;
+  const EpiStore epi{C, ldc, (int)out};
+  const TileChoice t = choose_pair_tile(M, N);
+  if (t.bn == 256)
+    return launch_bf16<256, 256, 2, 2, 2, 3, true, EpiStore, 2>(A2, M, B, ldb, M, N, K, epi, s);
+  return launch_bf16<256, 128, 2, 2, 2, 4, true, EpiStore, 2>(A2, M, B, ldb, M, N, K, epi, s);
 }
 
 hipError_t gemm_bf16_gelu(const uint16_t* A, int64_t lda, const uint16_t* B,
@@ -956,20 +977,20 @@ hipError_t gemm_bf16_gelu(const uint16_t* A, int64_t lda, const uint16_t* B,
                           int K, int kb, hipStream_t s) {
   if (kb != 0 && kb != 32 && kb != 64) return hipErrorInvalidValue;
   const int sh = kb == 32 ? 5 : (kb == 64 ? 6 : 0);
-  return dispatch_bf16<false>(A, lda, B, ldb, M, N, K, K, EpiGelu{C, ldc, (int)OUT_BF16, M, sh}, s);
+  return dispatch_bf16<false>(A, lda, B, ldb, M, N, K, EpiGelu{C, ldc, (int)OUT_BF16, M, sh}, s);
 }
 
 hipError_t gemm_bf16_qkv(const uint16_t* A, int64_t lda, const uint16_t* B,
                          int64_t ldb, const QkvOut& q, int M, int N, int K,
                          hipStream_t s) {
-  return dispatch_bf16<false>(A, lda, B, ldb, M, N, K, K, EpiQkv{q}, s);
+  return dispatch_bf16<false>(A, lda, B, ldb, M, N, K, EpiQkv{q}, s);
 }
 
 hipError_t gemm_bf16_add_kb(const uint16_t* A, int kb, const uint16_t* B, int64_t ldb,
                             const float* S, void* C, int64_t ldc, OutType out, int M, int N,
                             int K, hipStream_t s) {
   if (M > 0 && N > 0 && kb != a_block(choose_bf16_tile(M, N))) return hipErrorInvalidValue;
-  return dispatch_bf16<true>(A, M, B, ldb, M, N, K, K, EpiAdd{S, C, ldc, (int)out}, s);
+  return dispatch_bf16<true>(A, M, B, ldb, M, N, K, EpiAdd{S, C, ldc, (int)out}, s);
 }
 
 hipError_t gemm_f32_add(const float* A, int64_t lda, const float* B, int64_t ldb,

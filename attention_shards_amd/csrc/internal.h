@@ -61,12 +61,13 @@ int gemm_bf16_a_block(int M, int N);
 hipError_t gemm_bf16_store_kb(const uint16_t* A, int kb, const uint16_t* B, int64_t ldb,
                               void* C, int64_t ldc, OutType out, int M, int N, int K,
                               hipStream_t s);
-// C = [A_hi | A_lo] * B: A2 is [M, 2K], the same B[K,N] multiplies both
-// halves (two MFMA passes over K); K a multiple of 64; A2 K-blocked,
-// [2K/kb][M][kb], kb = gemm_bf16_a_block(M, N).
-hipError_t gemm_bf16_store_split_a_kb(const uint16_t* A2, int kb, const uint16_t* B,
-                                      int64_t ldb, void* C, int64_t ldc, OutType out, int M,
-                                      int N, int K, hipStream_t s);
+// C = (A_hi + A_lo) * B in one pass over K: every stage brings A_hi's and
+// A_lo's tiles and one B tile, both products use the same B fragments.  A2 is
+// K-blocked by 32, [2K/32][M][32] (A_hi's blocks, then A_lo's); K a multiple
+// of 32.
+hipError_t gemm_bf16_store_pair_kb(const uint16_t* A2, const uint16_t* B, int64_t ldb, void* C,
+                                   int64_t ldc, OutType out, int M, int N, int K,
+                                   hipStream_t s);
 // Same product scattered into the attention workspace (N == 3*nl*d).
 hipError_t gemm_bf16_qkv(const uint16_t* A, int64_t lda, const uint16_t* B,
                          int64_t ldb, const QkvOut& q, int M, int N, int K,
