@@ -28,6 +28,7 @@
 //     the 8 XCDs) receives a contiguous run of tiles, ordered in groups of 8
 //     tile-rows so neighbouring tiles share A and B panels in that XCD's L2.
 #include <atomic>
+#include <numeric>
 
 #include "internal.h"
 
@@ -488,10 +489,11 @@ template <int BM, int BN, int WM, int WN, int KS, int NSL, class Epi, bool AKB, 
 __global__ void __launch_bounds__(WM * WN * 64)
 gemm_bf16_kernel(const uint16_t* __restrict__ A, int64_t lda,
                  const uint16_t* __restrict__ B, int64_t ldb, int M, int N,
-                 int K, int tiles_m, int tiles_n, Epi epi) {
+                 int K, int tiles_m, int tiles_n, int n_base, Epi epi) {
   // With AKB, A is K-blocked by the stage depth BK: [ceil(K/BK)][lda][BK],
   // lda the padded row count, so a stage's A tile is one contiguous run of
-  // rows.
+  // rows.  The grid covers output columns [n_base, N) (tiles_n tiles wide);
+  // all coordinates are absolute.
   static_assert(KS == 2 || KS == 4, "k-steps per stage");
   static_assert(NSL >= 3 && NSL <= 6, "ring slots");
   static_assert(NA == 1 || (NA == 2 && AKB), "paired A operands are K-blocked");
@@ -528,7 +530,7 @@ gemm_bf16_kernel(const uint16_t* __restrict__ A, int64_t lda,
 
   int tm, tn;
   tile_coords(tiles_m, tiles_n, tm, tn);
-  const int m0 = tm * BM, n0 = tn * BN;
+  const int m0 = tm * BM, n0 = n_base + tn * BN;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wr0 = (wave / WN) * (BM / WM);
   const int wc0 = (wave % WN) * (BN / WN);
@@ -723,48 +725,105 @@ gemm_bf16_kernel(const uint16_t* __restrict__ A, int64_t lda,
   epilogue_lds<BN / WN>(smem, acc, epi, M, N, m0 + wr0, n0 + wc0, wave, lane);
 }
 
-// Tile configurations.  The choice minimises the estimated time: full
-// waves of tiles over the device's compute units times the tile's cost, the larger tiles being
-// cheaper per element (less LDS and L2 traffic per MFMA).
-struct TileChoice {
-  int bm, bn;
+// Tile kinds of the plain products: rows, columns, stage depth (the K
+// block of a K-blocked A) and a relative efficiency per output element (the
+// larger tiles are cheaper: less LDS and L2 traffic per MFMA).
+struct TileKind {
+  int bm, bn, bk;
+  double eff;
+};
+constexpr int NKIND = 5;
+constexpr TileKind kKinds[NKIND] = {{256, 256, 32, 1.0},
+                                    {256, 192, 32, 0.95},
+                                    {256, 128, 64, 0.95},
+                                    {128, 192, 64, 0.80},
+                                    {128, 128, 64, 0.70}};
+
+// How an [M, N] output is covered: columns [0, n1) by tiles of kind k1,
+// columns [n1, N) by tiles of kind k2 (k2 < 0: kind k1 covers all of N).
+struct Plan {
+  int k1, k2, n1;
 };
 
-TileChoice choose_bf16_tile(int M, int N) {
-  const TileChoice cand[4] = {{256, 256}, {256, 128}, {128, 192}, {128, 128}};
-  const double eff[4] = {1.0, 0.95, 0.80, 0.70};
+// Estimated time of `tiles` tiles of kind k: full waves over the compute
+// units times the tile's cost.
+double kind_cost(int k, int64_t tiles, int64_t ncu) {
+  return (double)((tiles + ncu - 1) / ncu) * kKinds[k].bm * kKinds[k].bn / kKinds[k].eff;
+}
+
+// The cheapest plan by that estimate.  A single kind leaves its last wave
+// partly idle when the tile count is not a multiple of the CU count (2048 x
+// 22528 in 256x256 tiles: 704 tiles = 2.75 waves); two rectangles avoid it:
+// whole waves of kind k1 over the first columns, then the remaining columns
+// in a kind whose tiles fill about one wave (there: 512 tiles of 256x256,
+// then 256 tiles of 256x192).  Both kinds share the stage depth, so one
+// K-blocked A serves both; a split plan is kept only when it is estimated
+// at least 3% cheaper than the best single kind.
+Plan plan_bf16(int M, int N) {
   const int64_t ncu = device_cu_count();
-  int best = 0;
+  Plan best{0, -1, N};
   double best_cost = 1e300;
-  for (int c = 0; c < 4; ++c) {
-    const int64_t tiles = (int64_t)((M + cand[c].bm - 1) / cand[c].bm) *
-                          ((N + cand[c].bn - 1) / cand[c].bn);
-    const double waves = (double)((tiles + ncu - 1) / ncu);
-    const double cost = waves * cand[c].bm * cand[c].bn / eff[c];
-    if (cost < best_cost * 0.999) {
-      best_cost = cost;
-      best = c;
+  for (int k = 0; k < NKIND; ++k) {
+    const TileKind& t = kKinds[k];
+    const int64_t tiles = (int64_t)((M + t.bm - 1) / t.bm) * ((N + t.bn - 1) / t.bn);
+    const double c = kind_cost(k, tiles, ncu);
+    if (c < best_cost * 0.999) {
+      best_cost = c;
+      best = Plan{k, -1, N};
     }
   }
-  return cand[best];
+  const double single = best_cost;
+  for (int k1 = 0; k1 < NKIND; ++k1) {
+    const TileKind& t1 = kKinds[k1];
+    const int64_t tm1 = (M + t1.bm - 1) / t1.bm;
+    const int64_t step = ncu / std::gcd(ncu, tm1);  // tile columns per whole waves
+    int64_t cols1 = (N / t1.bn) / step * step;
+    if (cols1 * t1.bn >= N) cols1 -= step;
+    if (cols1 <= 0) continue;
+    const int n1 = (int)(cols1 * t1.bn);
+    const double c1 = (double)(tm1 * cols1 / ncu) * t1.bm * t1.bn / t1.eff;
+    for (int k2 = 0; k2 < NKIND; ++k2) {
+      const TileKind& t2 = kKinds[k2];
+      if (t2.bk != t1.bk) continue;
+      const int64_t tiles2 = (int64_t)((M + t2.bm - 1) / t2.bm) * ((N - n1 + t2.bn - 1) / t2.bn);
+      const double c = c1 + kind_cost(k2, tiles2, ncu);
+      if (c < best_cost * 0.999 && c <= 0.97 * single) {
+        best_cost = c;
+        best = Plan{k1, k2, n1};
+      }
+    }
+  }
+  return best;
 }
 
 template <int BM, int BN, int WM, int WN, int KS, int NSL, bool AKB, class Epi, int NA = 1>
-hipError_t launch_bf16(const uint16_t* A, int64_t lda, const uint16_t* B,
-                       int64_t ldb, int M, int N, int K, const Epi& epi, hipStream_t s) {
-  const int tm = (M + BM - 1) / BM, tn = (N + BN - 1) / BN;
+hipError_t launch_bf16(const uint16_t* A, int64_t lda, const uint16_t* B, int64_t ldb, int M,
+                       int N, int K, const Epi& epi, hipStream_t s, int n_base = 0) {
+  const int tm = (M + BM - 1) / BM, tn = (N - n_base + BN - 1) / BN;
   hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, WM, WN, KS, NSL, Epi, AKB, NA>), dim3(tm * tn),
-                     dim3(WM * WN * 64), 0, s, A, lda, B, ldb, M, N, K, tm, tn, epi);
+                     dim3(WM * WN * 64), 0, s, A, lda, B, ldb, M, N, K, tm, tn, n_base, epi);
   return hipGetLastError();
 }
 
-// K block (stage depth) of the kernel the dispatch picks for an [M, N]
-// output: 32 for 256x256 tiles (five 32 KB stages fill the LDS), 64 for the
-// others.
-int a_block(const TileChoice& t) { return t.bm == 256 && t.bn == 256 ? 32 : 64; }
+// Output columns [n_base, n_end) in tiles of kind k.
+template <bool AKB, class Epi>
+hipError_t launch_kind(int k, const uint16_t* A, int64_t lda, const uint16_t* B, int64_t ldb,
+                       int M, int n_base, int n_end, int K, const Epi& epi, hipStream_t s) {
+  switch (k) {
+    case 0: return launch_bf16<256, 256, 2, 2, 2, 5, AKB>(A, lda, B, ldb, M, n_end, K, epi, s, n_base);
+    case 1: return launch_bf16<256, 192, 2, 2, 2, 5, AKB>(A, lda, B, ldb, M, n_end, K, epi, s, n_base);
+    case 2: return launch_bf16<256, 128, 2, 2, 4, 3, AKB>(A, lda, B, ldb, M, n_end, K, epi, s, n_base);
+    case 3: return launch_bf16<128, 192, 2, 2, 4, 3, AKB>(A, lda, B, ldb, M, n_end, K, epi, s, n_base);
+    default: return launch_bf16<128, 128, 2, 2, 4, 3, AKB>(A, lda, B, ldb, M, n_end, K, epi, s, n_base);
+  }
+}
 
-// AKB: A is K-blocked by the chosen kernel's stage depth (see
-// gemm_bf16_kernel), lda its row count; the caller has checked the block.
+// K block (stage depth) of the plan for an [M, N] output: 32 for 256x256
+// and 256x192 tiles (five stages fill the LDS), 64 for the others.
+int a_block(int M, int N) { return kKinds[plan_bf16(M, N).k1].bk; }
+
+// AKB: A is K-blocked by the plan's stage depth (see gemm_bf16_kernel), lda
+// its row count; the caller has checked the block.
 template <bool AKB, class Epi>
 hipError_t dispatch_bf16(const uint16_t* A, int64_t lda, const uint16_t* B,
                          int64_t ldb, int M, int N, int K, const Epi& epi, hipStream_t s) {
@@ -772,15 +831,18 @@ hipError_t dispatch_bf16(const uint16_t* A, int64_t lda, const uint16_t* B,
   // tiles are addressed with 32-bit byte offsets: 256 rows of A, 64 of B
   // (K-blocked A tiles are at most 32 KiB)
   if ((!AKB && lda >= ((int64_t)1 << 22)) || ldb >= ((int64_t)1 << 24)) return hipErrorInvalidValue;
-  const TileChoice t = choose_bf16_tile(M, N);
-  if (t.bm == 256 && t.bn == 256)
-    return launch_bf16<256, 256, 2, 2, 2, 5, AKB>(A, lda, B, ldb, M, N, K, epi, s);
-  if (t.bm == 256 && t.bn == 128)
-    return launch_bf16<256, 128, 2, 2, 4, 3, AKB>(A, lda, B, ldb, M, N, K, epi, s);
-  if (t.bm == 128 && t.bn == 192)
-    return launch_bf16<128, 192, 2, 2, 4, 3, AKB>(A, lda, B, ldb, M, N, K, epi, s);
-  return launch_bf16<128, 128, 2, 2, 4, 3, AKB>(A, lda, B, ldb, M, N, K, epi, s);
+  const Plan p = plan_bf16(M, N);
+  hipError_t e = launch_kind<AKB>(p.k1, A, lda, B, ldb, M, 0, p.n1, K, epi, s);
+  if (e == hipSuccess && p.k2 >= 0) e = launch_kind<AKB>(p.k2, A, lda, B, ldb, M, p.n1, N, K, epi, s);
+  return e;
 }
+
+// The paired product's tiles: 256x256 (three 48 KB slots) or 256x128 (four
+// 40 KB slots), both K = 32 per stage; the same cost estimate as the plain
+// products (full waves of tiles times the tile's cost).
+struct TileChoice {
+  int bm, bn;
+};
 
 // X [M, K] row-major (row stride lda) -> K-blocked [ceil(K/kb)][M][kb]
 // (kb = 32 or 64; zeros in the columns past K of the last block), the A
@@ -917,12 +979,12 @@ int device_cu_count() {
   return n;
 }
 
-int gemm_bf16_a_block(int M, int N) { return a_block(choose_bf16_tile(M, N)); }
+int gemm_bf16_a_block(int M, int N) { return a_block(M, N); }
 
 hipError_t gemm_bf16_store_kb(const uint16_t* A, int kb, const uint16_t* B, int64_t ldb,
                               void* C, int64_t ldc, OutType out, int M, int N, int K,
                               hipStream_t s) {
-  if (M > 0 && N > 0 && kb != a_block(choose_bf16_tile(M, N))) return hipErrorInvalidValue;
+  if (M > 0 && N > 0 && kb != a_block(M, N)) return hipErrorInvalidValue;
   return dispatch_bf16<true>(A, M, B, ldb, M, N, K, EpiStore{C, ldc, (int)out}, s);
 }
 
@@ -943,14 +1005,11 @@ hipError_t kblock_bf16(const uint16_t* A, int64_t lda, uint16_t* out, int M, int
 hipError_t gemm_bf16_gelu_akb(const uint16_t* Akb, int kb, const uint16_t* B, int64_t ldb,
                               uint16_t* C, int M, int N, int K, int kb_out, hipStream_t s) {
   if (kb_out != 32 && kb_out != 64) return hipErrorInvalidValue;
-  if (M > 0 && N > 0 && kb != a_block(choose_bf16_tile(M, N))) return hipErrorInvalidValue;
+  if (M > 0 && N > 0 && kb != a_block(M, N)) return hipErrorInvalidValue;
   const int sh = kb_out == 32 ? 5 : 6;
   return dispatch_bf16<true>(Akb, M, B, ldb, M, N, K, EpiGelu{C, 0, (int)OUT_BF16, M, sh}, s);
 }
 
-// The paired product's tiles: 256x256 (three 48 KB slots) or 256x128 (four
-// 40 KB slots), both K = 32 per stage; the same cost estimate as the plain
-// products (full waves of tiles times the tile's cost).
 TileChoice choose_pair_tile(int M, int N) {
   const int64_t ncu = device_cu_count();
   const int64_t t256 = (int64_t)((M + 255) / 256) * ((N + 255) / 256);
@@ -989,7 +1048,7 @@ hipError_t gemm_bf16_qkv(const uint16_t* A, int64_t lda, const uint16_t* B,
 hipError_t gemm_bf16_add_kb(const uint16_t* A, int kb, const uint16_t* B, int64_t ldb,
                             const float* S, void* C, int64_t ldc, OutType out, int M, int N,
                             int K, hipStream_t s) {
-  if (M > 0 && N > 0 && kb != a_block(choose_bf16_tile(M, N))) return hipErrorInvalidValue;
+  if (M > 0 && N > 0 && kb != a_block(M, N)) return hipErrorInvalidValue;
   return dispatch_bf16<true>(A, M, B, ldb, M, N, K, EpiAdd{S, C, ldc, (int)out}, s);
 }
 
