@@ -11,7 +11,9 @@ Parallelism" (mbrenndoerfer.com), i.e. the FFN steps 1-3 (column-parallel
 W1 with a local GeLU, row-parallel W2 giving a partial sum, all-reduce), the
 multi-head attention decomposition (QKV split by heads, per-head attention,
 row-parallel output projection), the residual added after each reduce, and
-the layer that chains the two sub-layers.
+the layer that chains the two sub-layers, and the sequence-parallel
+variant of the sum for the operations the page says are not split across
+GPUs (LayerNorm over a row's features): the rows are split instead.
 
 The method reaches the plain unsharded result exactly (up to rounding
 order), so every function here is that plain definition written out in
@@ -36,3 +38,4 @@ from .ffn import gelu, column_parallel, row_parallel, ffn_shard, ffn_full  # noq
 from .attention import attention_heads, attn_shard, attn_full  # noqa: F401
 from .reduce import partial_reduce  # noqa: F401
 from .layer import layer  # noqa: F401
+from .sequence import layernorm, reduce_layernorm  # noqa: F401

@@ -341,3 +341,25 @@ def test_non_current_stream_matches_default(gpu):
         del junk
     for o in outs:
         assert np.array_equal(o, ref)
+
+
+@pytest.mark.parametrize("M,h,fs,what", [
+    (1800, 12296, 1000, "GEMM2: whole waves of 256x256, then 256x192 over ragged columns"),
+    (1000, 8200, 1000, "GEMM2: 256x192 tiles, ragged rows and columns"),
+    (1800, 6152, 1000, "GEMM2: 256x128 waves, then 128x128 (64-deep stages)"),
+    (3000, 8200, 1000, "GEMM2: 128x192 waves, then 256x128"),
+    (1800, 256, 12296, "GEMM1 with K-blocked X: 256x256 waves, then 256x192 over ragged columns"),
+    (1000, 512, 8200, "GEMM1 with K-blocked X: 256x192 tiles, ragged"),
+])
+def test_tile_plans_ragged(gpu, M, h, fs, what):
+    """Shapes whose output is covered by two tile kinds (whole waves of one,
+    the remaining ragged columns by another) or by the 256x192 kind, in
+    both products; fp32 output, 48 seeded rows (first and last included)
+    against the oracle."""
+    seed = 700 + M + h
+    d = syn.make_ffn_inputs(seed, M, h, fs, syn.BF16)
+    got = run_shard(gpu, d, 0, 1, syn.F32, view=False)
+    rows = syn.sample_rows(seed, M, 48)
+    e = rel_err(got[rows], oracle_shard(d, 0, 1, rows))
+    log(f"{what}: M={M} h={h} ffn={fs}: err {e:.4f}")
+    assert e <= TOL_BF16

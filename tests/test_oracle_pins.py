@@ -367,3 +367,88 @@ def test_layer_brute_force_tiny():
     X1, X2 = oracle.layer(X, WQ, WK, WV, WO, W1, W2, 1, S, nh, d)
     assert np.max(np.abs(X1 - np.array(x1))) < 1e-13
     assert np.max(np.abs(X2 - np.array(x2))) < 1e-13
+
+
+# ---------------------------------------------------------------------------
+# Sequence-parallel sum + LayerNorm: closed forms, invariants, brute force
+# ---------------------------------------------------------------------------
+
+def test_layernorm_two_features_closed_form():
+    # [a, b]: mean (a+b)/2, biased variance ((a-b)/2)^2, so with eps = 0 the
+    # row becomes [sign(a-b), -sign(a-b)]; with eps the magnitude is
+    # d / sqrt(d^2 + eps), d = |a-b|/2
+    x = np.array([[3.0, 1.0], [-2.0, 5.0], [0.5, 0.5 + 1e-3]])
+    y = oracle.layernorm(x, eps=0.0)
+    assert np.allclose(y, [[1, -1], [-1, 1], [-1, 1]], atol=1e-12, rtol=0)
+    ye = oracle.layernorm(x, eps=0.25)
+    d = np.abs(x[:, 0] - x[:, 1]) / 2
+    assert np.allclose(np.abs(ye[:, 0]), d / np.sqrt(d * d + 0.25), atol=1e-15, rtol=0)
+
+
+def test_layernorm_rows_have_zero_mean_and_shrunk_unit_variance():
+    x = np.random.default_rng(3).normal(2.0, 3.0, size=(7, 96))
+    eps = 0.5
+    y = oracle.layernorm(x, eps=eps)
+    var = x.var(axis=1)
+    assert np.max(np.abs(y.mean(axis=1))) < 1e-14
+    assert np.allclose(y.var(axis=1), var / (var + eps), rtol=1e-13, atol=0)
+
+
+def test_layernorm_shift_and_scale_invariance():
+    rng = np.random.default_rng(4)
+    x = rng.normal(size=(5, 64))
+    c = rng.normal(size=(5, 1)) * 10
+    assert np.allclose(oracle.layernorm(x + c), oracle.layernorm(x), atol=1e-12, rtol=0)
+    a = rng.uniform(0.5, 4.0, size=(5, 1))
+    assert np.allclose(oracle.layernorm(a * x, eps=0.0), oracle.layernorm(x, eps=0.0),
+                       atol=1e-12, rtol=0)
+    # ... and a different per-row scale does change it when eps > 0
+    assert not np.allclose(oracle.layernorm(a * x, eps=1.0), oracle.layernorm(x, eps=1.0),
+                           atol=1e-6)
+
+
+def test_layernorm_affine_is_applied_per_feature():
+    rng = np.random.default_rng(5)
+    x = rng.normal(size=(4, 32))
+    g, b = rng.normal(size=32), rng.normal(size=32)
+    assert np.allclose(oracle.layernorm(x, g, b), g * oracle.layernorm(x) + b,
+                       atol=1e-14, rtol=0)
+
+
+def test_reduce_layernorm_brute_force_tiny():
+    rng = np.random.default_rng(6)
+    rows, cols, t, eps = 3, 5, 3, 1e-3
+    parts = [rng.normal(size=(rows, cols)) for _ in range(t)]
+    R = rng.normal(size=(rows, cols))
+    g, b = rng.normal(size=cols), rng.normal(size=cols)
+    x, y = oracle.reduce_layernorm(parts, R, g, b, eps)
+    for r in range(rows):
+        xs = [sum(parts[i][r][c] for i in range(t)) + R[r][c] for c in range(cols)]
+        mu = sum(xs) / cols
+        var = sum((v - mu) * (v - mu) for v in xs) / cols
+        for c in range(cols):
+            assert abs(x[r][c] - xs[c]) < 1e-14
+            want = (xs[c] - mu) / math.sqrt(var + eps) * g[c] + b[c]
+            assert abs(y[r][c] - want) < 1e-13
+
+
+@pytest.mark.parametrize("t", [2, 4, 8])
+def test_row_blocks_assemble_the_unsharded_result(t):
+    """Reduce-scatter by rows, LayerNorm per block, all-gather = the sum and
+    LayerNorm of the whole matrix (both act row by row)."""
+    rng = np.random.default_rng(7 + t)
+    rows, cols = 37, 24
+    parts = [rng.normal(size=(rows, cols)) for _ in range(t)]
+    R = rng.normal(size=(rows, cols))
+    x, y = oracle.reduce_layernorm(parts, R)
+    base, extra = divmod(rows, t)
+    r0 = 0
+    xs, ys = [], []
+    for j in range(t):
+        r1 = r0 + base + (1 if j < extra else 0)
+        xb, yb = oracle.reduce_layernorm([p[r0:r1] for p in parts], R[r0:r1])
+        xs.append(xb)
+        ys.append(yb)
+        r0 = r1
+    assert np.array_equal(np.concatenate(xs), x)
+    assert np.array_equal(np.concatenate(ys), y)
