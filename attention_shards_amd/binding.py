@@ -48,6 +48,9 @@ SIGNATURES = {
                                      _c_i32, _c_i32, _c_i32, _c_p, _c_sz, _c_p]),
     "tp_ffn_shard_noalloc": (_c_i32, [_c_p, _c_p, _c_p, _c_p, _c_i64, _c_i64, _c_i64,
                                       _c_i32, _c_i32, _c_i64, _c_i32, _c_i32, _c_p]),
+    "tp_sp_reduce_layernorm": (_c_i32, [ctypes.POINTER(_c_p), _c_i32, _c_p, _c_p, _c_p, _c_p,
+                                        _c_p, ctypes.c_float, _c_i64, _c_i64, _c_i32, _c_i32,
+                                        _c_i32, _c_i32, _c_i32, _c_i32, _c_p]),
     "tp_status_string": (ctypes.c_char_p, [_c_i32]),
     "tp_last_error_message": (ctypes.c_char_p, []),
     "tp_abi_version": (_c_i32, []),
@@ -358,3 +361,53 @@ def tp_partial_reduce_slice(partials, residual, out, slice_, nslices, stream=Non
     """Rows block `slice_` of `nslices` of sum(partials) + residual, written into
     the same rows of out (the reduce-scatter half of the all-reduce).  Returns out."""
     return tp_partial_reduce(partials, residual, out, stream, slice_of=(slice_, nslices))
+
+
+def tp_sp_reduce_layernorm(partials, residual, x_out, ln_out, gamma=None, beta=None,
+                           eps: float = 1e-5, slice_of=(0, 1), stream=None):
+    """Rows block slice_of = (slice, nslices) of x = sum(partials) + residual and
+    y = LayerNorm(x) (per row; gamma/beta fp32 [cols] or None), written into
+    the same rows of x_out (may be None) and ln_out.  Returns ln_out."""
+    lib = load()
+    t = len(partials)
+    if not 1 <= t <= TP_MAX_PARTIALS:
+        raise ValueError(f"need 1..{TP_MAX_PARTIALS} partials, got {t}")
+    _dense(ln_out, "ln_out")
+    rows, cols = ln_out.shape
+    for k, p in enumerate(partials):
+        _dense(p, f"partials[{k}]")
+        if tuple(p.shape) != (rows, cols):
+            raise ValueError(f"partials[{k}] shape {tuple(p.shape)} != {(rows, cols)}")
+    pdt = _dtype_code(partials[0])
+    if any(_dtype_code(p) != pdt for p in partials):
+        raise TypeError("all partials must share a dtype")
+    rdt, rptr = TP_F32, None
+    if residual is not None:
+        _dense(residual, "residual")
+        if tuple(residual.shape) != (rows, cols):
+            raise ValueError("residual shape mismatch")
+        rdt, rptr = _dtype_code(residual), residual.data_ptr()
+    xdt, xptr = TP_F32, None
+    if x_out is not None:
+        _dense(x_out, "x_out")
+        if tuple(x_out.shape) != (rows, cols):
+            raise ValueError("x_out shape mismatch")
+        xdt, xptr = _dtype_code(x_out), x_out.data_ptr()
+    torch = _torch()
+    gb = []
+    for name, v in (("gamma", gamma), ("beta", beta)):
+        if v is None:
+            gb.append(None)
+            continue
+        _dense(v, name)
+        if v.dtype != torch.float32 or tuple(v.shape) != (cols,):
+            raise ValueError(f"{name} must be float32 [{cols}]")
+        gb.append(v.data_ptr())
+    arr = (ctypes.c_void_p * t)(*[p.data_ptr() for p in partials])
+    s = _stream_of(stream, ln_out.device)
+    slice_, nslices = slice_of
+    with torch.cuda.device(ln_out.device):
+        _check(lib.tp_sp_reduce_layernorm(arr, t, rptr, xptr, ln_out.data_ptr(), gb[0], gb[1],
+                                          float(eps), rows, cols, slice_, nslices, pdt, rdt,
+                                          xdt, _dtype_code(ln_out), s.cuda_stream))
+    return ln_out

@@ -111,6 +111,16 @@ hipError_t partial_reduce(const ReducePtrs& ptrs, int t, int pdt,
                           const void* R, int rdt, void* out, int odt,
                           int64_t n, hipStream_t s);
 
+// Rows [0, rows) of x = sum_i P_i + R (fp32, fixed order; R nullable) and
+// y = LayerNorm(x) per row: (x - mean) / sqrt(var + eps) * gamma + beta,
+// biased variance, gamma/beta fp32 [cols] (nullable: 1 and 0).  xout is
+// nullable (x not stored).  cols a multiple of 8, at most kLnMaxCols.
+constexpr int kLnMaxCols = 256 * 8 * 16;
+hipError_t reduce_layernorm(const ReducePtrs& ptrs, int t, int pdt, const void* R, int rdt,
+                            void* xout, int xdt, void* yout, int ydt, const float* gamma,
+                            const float* beta, float eps, int64_t rows, int cols,
+                            hipStream_t s);
+
 // C = S + A*B: the product added to an fp32 [M, N] matrix S (row stride
 // ldc, like C) and rounded once to the output type.  bf16 (A K-blocked as
 // for gemm_bf16_store_kb) and fp32 inputs (requirements of gemm_f32).

@@ -233,4 +233,183 @@ hipError_t partial_reduce(const ReducePtrs& ptrs, int t, int pdt, const void* R,
                         : launch_r<DT_F32>(ptrs, t, R, rdt, out, odt, n, s);
 }
 
+
+// ---------------------------------------------------------------------------
+// Sequence-parallel sum + LayerNorm: a block of rows of out = sum_i P_i + R
+// (the reduce-scatter half of the all-reduce, split by rows), then LayerNorm
+// over each of those full-width rows (page "Tensor Parallelism > Combining
+// Column and Row Parallelism": LayerNorm reduces over all features, so it is
+// not split by columns; the rows are split instead).
+//
+// One workgroup of 256 threads per row; thread k owns the 8-element groups
+// k, k + 256, ... (G of them), loads them from every partial (a partial's G
+// loads in flight together), sums in the fixed order P_0 + ... + P_{t-1} + R
+// in fp32 and keeps the row in registers.  Mean, then the biased variance
+// of (x - mean), each as a fixed-order block sum (wave shuffles, then the
+// four waves' sums in order); y = (x - mean) * rsqrt(var + eps) * gamma +
+// beta.  HBM-bound: t partials + residual read, x and y written.
+// ---------------------------------------------------------------------------
+namespace {
+
+__device__ __forceinline__ float block_sum256(float v, float* red) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o);
+  const int wave = threadIdx.x >> 6;
+  __syncthreads();  // red[] free (a previous sum's readers are done)
+  if ((threadIdx.x & 63) == 0) red[wave] = v;
+  __syncthreads();
+  return ((red[0] + red[1]) + red[2]) + red[3];
+}
+
+template <int DT>
+__device__ __forceinline__ void store8_dyn(void* base, int64_t g, const float* v) {
+  if (DT == DT_BF16) {
+    u32x4 w;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) w[k] = f2bf(v[2 * k]) | (f2bf(v[2 * k + 1]) << 16);
+    __builtin_nontemporal_store(w, reinterpret_cast<u32x4*>(base) + g);
+  } else {
+    f32x4* p = reinterpret_cast<f32x4*>(base) + 2 * g;
+    __builtin_nontemporal_store(f32x4{v[0], v[1], v[2], v[3]}, p);
+    __builtin_nontemporal_store(f32x4{v[4], v[5], v[6], v[7]}, p + 1);
+  }
+}
+
+template <int PDT, int G>
+__global__ void __launch_bounds__(256)
+reduce_ln_kernel(ReducePtrs ptrs, int t, const void* R, int rdt, void* xout, int xdt,
+                 void* yout, int ydt, const float* gamma, const float* beta, float eps,
+                 int64_t rows, int cols) {
+  __shared__ float red[4];
+  const int ng = cols / 8;  // 8-element groups per row
+  for (int64_t row = blockIdx.x; row < rows; row += gridDim.x) {
+    float v[G][8];
+    const int64_t g0 = row * ng;
+#pragma unroll
+    for (int j = 0; j < G; ++j)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) v[j][e] = 0.0f;
+    for (int i = 0; i < t; ++i) {
+      Raw8 r[G];
+#pragma unroll
+      for (int j = 0; j < G; ++j) {
+        const int g = threadIdx.x + 256 * j;
+        if (g < ng) r[j] = rawload8<PDT>(ptrs.p[i], g0 + g);
+      }
+#pragma unroll
+      for (int j = 0; j < G; ++j)
+        if (threadIdx.x + 256 * j < ng) add8<PDT>(r[j], v[j]);
+    }
+    if (R != nullptr) {
+#pragma unroll
+      for (int j = 0; j < G; ++j) {
+        const int g = threadIdx.x + 256 * j;
+        if (g < ng) {
+          if (rdt == DT_BF16)
+            add8<DT_BF16>(rawload8<DT_BF16>(R, g0 + g), v[j]);
+          else
+            add8<DT_F32>(rawload8<DT_F32>(R, g0 + g), v[j]);
+        }
+      }
+    }
+    float s = 0.0f;
+#pragma unroll
+    for (int j = 0; j < G; ++j)
+      if (threadIdx.x + 256 * j < ng)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) s += v[j][e];
+    const float mean = block_sum256(s, red) / (float)cols;
+    float q = 0.0f;
+#pragma unroll
+    for (int j = 0; j < G; ++j)
+      if (threadIdx.x + 256 * j < ng)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const float d = v[j][e] - mean;
+          q = __builtin_fmaf(d, d, q);
+        }
+    const float var = block_sum256(q, red) / (float)cols;
+    const float rstd = 1.0f / sqrtf(var + eps);
+#pragma unroll
+    for (int j = 0; j < G; ++j) {
+      const int g = threadIdx.x + 256 * j;
+      if (g >= ng) continue;
+      if (xout != nullptr) {
+        if (xdt == DT_BF16)
+          store8_dyn<DT_BF16>(xout, g0 + g, v[j]);
+        else
+          store8_dyn<DT_F32>(xout, g0 + g, v[j]);
+      }
+      float gm[8], bt[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        gm[e] = 1.0f;
+        bt[e] = 0.0f;
+      }
+      if (gamma != nullptr) {
+        const f32x4* pg = reinterpret_cast<const f32x4*>(gamma) + 2 * g;
+        const f32x4 a = pg[0], b = pg[1];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          gm[e] = a[e];
+          gm[4 + e] = b[e];
+        }
+      }
+      if (beta != nullptr) {
+        const f32x4* pb = reinterpret_cast<const f32x4*>(beta) + 2 * g;
+        const f32x4 a = pb[0], b = pb[1];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          bt[e] = a[e];
+          bt[4 + e] = b[e];
+        }
+      }
+      float y[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) y[e] = __builtin_fmaf((v[j][e] - mean) * rstd, gm[e], bt[e]);
+      if (ydt == DT_BF16)
+        store8_dyn<DT_BF16>(yout, g0 + g, y);
+      else
+        store8_dyn<DT_F32>(yout, g0 + g, y);
+    }
+  }
+}
+
+template <int PDT, int G>
+hipError_t launch_ln(const ReducePtrs& ptrs, int t, const void* R, int rdt, void* xout, int xdt,
+                     void* yout, int ydt, const float* gamma, const float* beta, float eps,
+                     int64_t rows, int cols, hipStream_t s) {
+  const int64_t blocks = rows < ((int64_t)1 << 24) - 1 ? rows : ((int64_t)1 << 24) - 1;
+  hipLaunchKernelGGL((reduce_ln_kernel<PDT, G>), dim3((unsigned)blocks), dim3(256), 0, s, ptrs,
+                     t, R, rdt, xout, xdt, yout, ydt, gamma, beta, eps, rows, cols);
+  return hipGetLastError();
+}
+
+template <int PDT>
+hipError_t launch_ln_g(const ReducePtrs& ptrs, int t, const void* R, int rdt, void* xout,
+                       int xdt, void* yout, int ydt, const float* gamma, const float* beta,
+                       float eps, int64_t rows, int cols, hipStream_t s) {
+  const int groups = (cols / 8 + 255) / 256;  // 8-element groups per thread
+  if (groups <= 1) return launch_ln<PDT, 1>(ptrs, t, R, rdt, xout, xdt, yout, ydt, gamma, beta, eps, rows, cols, s);
+  if (groups <= 2) return launch_ln<PDT, 2>(ptrs, t, R, rdt, xout, xdt, yout, ydt, gamma, beta, eps, rows, cols, s);
+  if (groups <= 4) return launch_ln<PDT, 4>(ptrs, t, R, rdt, xout, xdt, yout, ydt, gamma, beta, eps, rows, cols, s);
+  if (groups <= 8) return launch_ln<PDT, 8>(ptrs, t, R, rdt, xout, xdt, yout, ydt, gamma, beta, eps, rows, cols, s);
+  if (groups <= 16) return launch_ln<PDT, 16>(ptrs, t, R, rdt, xout, xdt, yout, ydt, gamma, beta, eps, rows, cols, s);
+  return hipErrorInvalidValue;
+}
+
+}  // namespace
+
+hipError_t reduce_layernorm(const ReducePtrs& ptrs, int t, int pdt, const void* R, int rdt,
+                            void* xout, int xdt, void* yout, int ydt, const float* gamma,
+                            const float* beta, float eps, int64_t rows, int cols,
+                            hipStream_t s) {
+  if (rows == 0) return hipSuccess;
+  if (cols % 8 || cols > kLnMaxCols) return hipErrorInvalidValue;
+  return pdt == DT_BF16 ? launch_ln_g<DT_BF16>(ptrs, t, R, rdt, xout, xdt, yout, ydt, gamma,
+                                               beta, eps, rows, cols, s)
+                        : launch_ln_g<DT_F32>(ptrs, t, R, rdt, xout, xdt, yout, ydt, gamma,
+                                              beta, eps, rows, cols, s);
+}
+
 }  // namespace tp

@@ -674,3 +674,89 @@ tp_status_t tp_partial_reduce_slice(const void* const* partials, int32_t t,
 }
 
 }  // extern "C"
+
+// ---------------------------------------------------------------------------
+// Sequence-parallel sum + LayerNorm
+// ---------------------------------------------------------------------------
+extern "C" {
+
+tp_status_t tp_sp_reduce_layernorm(const void* const* partials, int32_t t, const void* residual,
+                                   void* x_out, void* ln_out, const float* gamma,
+                                   const float* beta, float eps, int64_t rows, int64_t cols,
+                                   int32_t slice, int32_t nslices, int32_t partial_dtype,
+                                   int32_t residual_dtype, int32_t x_dtype, int32_t ln_dtype,
+                                   void* stream) {
+  const char* fn = "tp_sp_reduce_layernorm";
+  try {
+    if (!valid_dtype(partial_dtype) || !valid_dtype(ln_dtype) ||
+        (residual && !valid_dtype(residual_dtype)) || (x_out && !valid_dtype(x_dtype)))
+      return fail(TP_ERR_DTYPE, "%s: dtype codes p=%d r=%d x=%d y=%d", fn, partial_dtype,
+                  residual_dtype, x_dtype, ln_dtype);
+    if (t < 1 || t > TP_MAX_PARTIALS)
+      return fail(TP_ERR_SHARD, "%s: t=%d outside [1, %d]", fn, t, TP_MAX_PARTIALS);
+    if (nslices < 1 || slice < 0 || slice >= nslices)
+      return fail(TP_ERR_SHARD, "%s: slice %d of %d", fn, slice, nslices);
+    if (rows < 0 || cols < 0 || cols % 8 != 0 || cols > tp::kLnMaxCols ||
+        (rows > 0 && cols > (int64_t(1) << 60) / rows))
+      return fail(TP_ERR_SHAPE,
+                  "%s: rows=%lld cols=%lld (cols a multiple of 8, at most %d)", fn,
+                  (long long)rows, (long long)cols, tp::kLnMaxCols);
+    if (!(eps >= 0.0f) || eps > 3.0e38f)
+      return fail(TP_ERR_SHAPE, "%s: eps=%g must be finite and >= 0", fn, (double)eps);
+    const int64_t base = rows / nslices, extra = rows % nslices;
+    const int64_t r0 = slice * base + (slice < extra ? slice : extra);
+    const int64_t nr = base + (slice < extra ? 1 : 0);
+    if (nr == 0 || cols == 0) return ok();
+    if (!partials || !ln_out) return fail(TP_ERR_NULL, "%s: NULL pointer", fn);
+    const int64_t pb = esize(partial_dtype), yb = esize(ln_dtype);
+    const int64_t n = rows * cols;
+    tp::ReducePtrs ptrs;
+    for (int k = 0; k < t; ++k) {
+      if (!partials[k]) return fail(TP_ERR_NULL, "%s: partials[%d] is NULL", fn, k);
+      if (!aligned16(partials[k]))
+        return fail(TP_ERR_ALIGNMENT, "%s: partials[%d] not 16-byte aligned", fn, k);
+      ptrs.p[k] = static_cast<const char*>(partials[k]) + r0 * cols * pb;
+    }
+    for (int k = t; k < TP_MAX_PARTIALS; ++k) ptrs.p[k] = nullptr;
+    if (!aligned16(ln_out) || (residual && !aligned16(residual)) ||
+        (x_out && !aligned16(x_out)) || (gamma && !aligned16(gamma)) ||
+        (beta && !aligned16(beta)))
+      return fail(TP_ERR_ALIGNMENT, "%s: pointers must be 16-byte aligned", fn);
+    // ln_out overlaps nothing; x_out may be exactly one of the inputs of the
+    // same element size (each row is read in full before it is written)
+    const Range ry = range_of(ln_out, n * yb);
+    const int64_t rb = esize(residual_dtype), xb = esize(x_dtype);
+    for (int k = 0; k < t; ++k) {
+      const Range rp = range_of(partials[k], n * pb);
+      if (overlap(ry, rp)) return fail(TP_ERR_ALIAS, "%s: ln_out overlaps partials[%d]", fn, k);
+      if (x_out && overlap(range_of(x_out, n * xb), rp) && !(partials[k] == x_out && pb == xb))
+        return fail(TP_ERR_ALIAS, "%s: x_out overlaps partials[%d]", fn, k);
+    }
+    if (residual) {
+      const Range rr = range_of(residual, n * rb);
+      if (overlap(ry, rr)) return fail(TP_ERR_ALIAS, "%s: ln_out overlaps the residual", fn);
+      if (x_out && overlap(range_of(x_out, n * xb), rr) && !(residual == x_out && rb == xb))
+        return fail(TP_ERR_ALIAS, "%s: x_out overlaps the residual", fn);
+    }
+    if (x_out && overlap(ry, range_of(x_out, n * xb)))
+      return fail(TP_ERR_ALIAS, "%s: ln_out overlaps x_out", fn);
+    if ((gamma && overlap(ry, range_of(gamma, cols * 4))) ||
+        (beta && overlap(ry, range_of(beta, cols * 4))) ||
+        (x_out && gamma && overlap(range_of(x_out, n * xb), range_of(gamma, cols * 4))) ||
+        (x_out && beta && overlap(range_of(x_out, n * xb), range_of(beta, cols * 4))))
+      return fail(TP_ERR_ALIAS, "%s: an output overlaps gamma or beta", fn);
+    const void* R = residual ? static_cast<const char*>(residual) + r0 * cols * rb : nullptr;
+    void* X = x_out ? static_cast<char*>(x_out) + r0 * cols * xb : nullptr;
+    void* Y = static_cast<char*>(ln_out) + r0 * cols * yb;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    (void)hipGetLastError();
+    const hipError_t e = tp::reduce_layernorm(ptrs, t, partial_dtype, R, residual_dtype, X,
+                                              x_dtype, Y, ln_dtype, gamma, beta, eps, nr,
+                                              (int)cols, s);
+    return hip_status(e, fn);
+  } catch (...) {
+    return fail(TP_ERR_HIP, "%s: internal exception", fn);
+  }
+}
+
+}  // extern "C"

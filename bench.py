@@ -30,6 +30,9 @@ The same run times, under "rows":
     1.41 GB each (more than the 256 MB Infinity Cache), so it reads HBM;
   * partial_reduce_slice: one row block of the t=8 reduce (the
     reduce-scatter half), blocks rotating;
+  * sp_reduce_layernorm_t4_h12288: the sequence-parallel sum + LayerNorm
+    (4 bf16 partials + residual, fp32 x, bf16 LayerNorm out) over all rows
+    of [8192, 12288], rotating over 3 buffer sets;
   * ffn_shard_reduce_fused: the t=8 step with the sum fused into the second
     GEMM's epilogue, and the same comparison at the t=4 hidden-12288 shape;
   * attn_shard: the attention shard (t=8, 8 of 64 heads of 128, hidden
@@ -310,6 +313,41 @@ def reduce_rotated(t, rows, cols, steps, warmup, nsets=3):
     torch.cuda.empty_cache()
     return {"t": t, "rows": rows, "cols": cols, "dtypes": "bf16 partials, bf16 residual, fp32 out",
             "buffer_sets": nsets, "bytes_per_set": by, **stats(ms), "bytes": by,
+            "gbs": round(by / (med * 1e-3) / 1e9, 1),
+            "frac_hbm_peak": round(by / (med * 1e-3) / 1e9 / PEAK_HBM_GBS, 4), "bound": "hbm"}
+
+
+def sp_layernorm_rotated(t, rows, cols, steps, warmup, nsets=3):
+    """tp_sp_reduce_layernorm over all rows (one call = every row block):
+    t bf16 partials + bf16 residual in, fp32 x and bf16 LayerNorm out, the
+    calls rotating over `nsets` buffer sets (device-generated values)."""
+    import torch
+    from attention_shards_amd import binding as B
+    g = torch.Generator(device="cuda").manual_seed(11 + t)
+    sets = []
+    for _ in range(nsets):
+        parts = [torch.randn(rows, cols, device="cuda", generator=g).to(torch.bfloat16)
+                 for _ in range(t)]
+        R = torch.randn(rows, cols, device="cuda", generator=g).to(torch.bfloat16)
+        sets.append((parts, R, torch.empty(rows, cols, device="cuda"),
+                     torch.empty(rows, cols, device="cuda", dtype=torch.bfloat16)))
+    gamma = torch.ones(cols, device="cuda")
+    beta = torch.zeros(cols, device="cuda")
+    nxt = [0]
+
+    def call():
+        parts, R, x, y = sets[nxt[0] % nsets]
+        nxt[0] += 1
+        B.tp_sp_reduce_layernorm(parts, R, x, y, gamma, beta, 1e-5)
+
+    ms = time_calls(call, steps, warmup)
+    by = (t * 2 + 2 + 4 + 2) * rows * cols
+    med = statistics.median(ms)
+    del sets
+    torch.cuda.empty_cache()
+    return {"t": t, "rows": rows, "cols": cols,
+            "dtypes": "bf16 partials, bf16 residual, fp32 x, bf16 LayerNorm out",
+            "buffer_sets": nsets, **stats(ms), "bytes": by,
             "gbs": round(by / (med * 1e-3) / 1e9, 1),
             "frac_hbm_peak": round(by / (med * 1e-3) / 1e9 / PEAK_HBM_GBS, 4), "bound": "hbm"}
 
@@ -841,6 +879,7 @@ def main():
     if args.reduce_only:
         for t, rows, cols in REDUCE_SHAPES:
             log(json.dumps(reduce_rotated(t, rows, cols, K, W)))
+        log(json.dumps(sp_layernorm_rotated(4, 8192, 12288, K, W)))
         return
     if args.attn_only:
         log(json.dumps(attn_row(K, W)))
@@ -927,6 +966,8 @@ def main():
         for t_, r_, c_ in REDUCE_SHAPES:
             log(f"reduce rotated t={t_} [{r_},{c_}]")
             rows[f"partial_reduce_t{t_}_h{c_}"] = reduce_rotated(t_, r_, c_, K, W)
+        log("sequence-parallel sum + LayerNorm t=4 [8192,12288]")
+        rows["sp_reduce_layernorm_t4_h12288"] = sp_layernorm_rotated(4, 8192, 12288, K, W)
         if fused is not None:
             fused["large"] = fused_vs_unfused_large(max(5, K // 5), 3)
         rows["ffn_shard_reduce_fused"] = fused

@@ -43,7 +43,7 @@
 extern "C" {
 #endif
 
-#define TP_ABI_VERSION 5
+#define TP_ABI_VERSION 6
 #define TP_MAX_PARTIALS 64
 
 /* Element types of tensors crossing the ABI. */
@@ -236,6 +236,40 @@ tp_status_t tp_partial_reduce_slice(const void* const* partials, int32_t t,
                                     int64_t cols, int32_t slice, int32_t nslices,
                                     int32_t partial_dtype, int32_t residual_dtype,
                                     int32_t out_dtype, void* stream);
+
+/* ------------------------------------------------------------------------
+ * Sequence-parallel sum + LayerNorm (the operations the page "Combining
+ * Column and Row Parallelism" names as reductions over the whole feature
+ * dimension, which are not split across GPUs by columns; the rows are split
+ * instead).
+ * ------------------------------------------------------------------------
+ * For the rows [r0, r1) of block `slice` of `nslices` (balanced blocks as in
+ * tp_partial_reduce_slice), with all rows full width:
+ *     x = (partials[0] + ... + partials[t-1]) + residual      (as the reduce)
+ *     y = (x - mean(x)) / sqrt(var(x) + eps) * gamma + beta   (per row)
+ * mean and the biased variance over the row's `cols` features, in fp32;
+ * that is the reduce-scatter half of the all-reduce, LayerNorm on this GPU's
+ * rows, and -- since block j writes rows [r0, r1) of x_out and ln_out in
+ * place -- the all-gather half when the blocks of all slices land in the
+ * same buffers.
+ *
+ *   partials   HOST array of t device pointers, each [rows, cols] of
+ *              partial_dtype (the whole matrices; only the block is read)
+ *   residual   [rows, cols] of residual_dtype, or NULL
+ *   x_out      [rows, cols] of x_dtype, or NULL (x not stored); may be
+ *              exactly one of the inputs of the same element size
+ *   ln_out     [rows, cols] of ln_dtype; overlaps nothing else
+ *   gamma,beta fp32 [cols] device arrays, or NULL (1 and 0)
+ *   eps        added to the variance inside the square root, >= 0
+ * Shape rules: cols a multiple of 8 and at most 32768 (one row stays in the
+ * registers of a workgroup); rows * cols at most 2^60.
+ */
+tp_status_t tp_sp_reduce_layernorm(const void* const* partials, int32_t t, const void* residual,
+                                   void* x_out, void* ln_out, const float* gamma,
+                                   const float* beta, float eps, int64_t rows, int64_t cols,
+                                   int32_t slice, int32_t nslices, int32_t partial_dtype,
+                                   int32_t residual_dtype, int32_t x_dtype, int32_t ln_dtype,
+                                   void* stream);
 
 /* ------------------------------------------------------------------------
  * FFN shard fused with the sum of the partials and the residual: the

@@ -378,3 +378,36 @@ def test_ffn_noalloc_limit_matches_header(lib):
 def test_ffn_noalloc_zero_tokens_is_a_no_op(lib):
     st, msg = noalloc(lib, tokens=0, X=None, Y=None)
     assert st == 0, msg
+
+
+def sp_call(lib, partials, R=None, x=None, y=Y, g=None, b=None, eps=1e-5, rows=64, cols=64,
+            slice_=0, nslices=1, pdt=B.TP_BF16, rdt=B.TP_BF16, xdt=B.TP_F32, ydt=B.TP_BF16):
+    arr = (ctypes.c_void_p * len(partials))(*partials)
+    st = lib.tp_sp_reduce_layernorm(arr, len(partials), R, x, y, g, b, eps, rows, cols, slice_,
+                                    nslices, pdt, rdt, xdt, ydt, None)
+    return B.STATUS[st], lib.tp_last_error_message().decode()
+
+
+def test_sp_reduce_layernorm_rejects(lib):
+    assert sp_call(lib, [X, W1], pdt=9)[0] == "TP_ERR_DTYPE"
+    assert sp_call(lib, [X, W1], x=WS, xdt=9)[0] == "TP_ERR_DTYPE"
+    assert sp_call(lib, [])[0] == "TP_ERR_SHARD"
+    assert sp_call(lib, [X], slice_=1, nslices=1)[0] == "TP_ERR_SHARD"
+    assert sp_call(lib, [X], cols=60)[0] == "TP_ERR_SHAPE"            # not a multiple of 8
+    assert sp_call(lib, [X], cols=32768 + 8)[0] == "TP_ERR_SHAPE"     # wider than a workgroup's row
+    assert sp_call(lib, [X], eps=-1.0)[0] == "TP_ERR_SHAPE"
+    assert sp_call(lib, [X], eps=float("nan"))[0] == "TP_ERR_SHAPE"
+    assert sp_call(lib, [X, 0])[0] == "TP_ERR_NULL"
+    assert sp_call(lib, [X], y=None)[0] == "TP_ERR_NULL"
+    assert sp_call(lib, [X + 8])[0] == "TP_ERR_ALIGNMENT"
+    assert sp_call(lib, [X], g=W2 + 4)[0] == "TP_ERR_ALIGNMENT"
+    assert sp_call(lib, [X], y=X + 64)[0] == "TP_ERR_ALIAS"           # ln_out inside a partial
+    assert sp_call(lib, [X], R=W1, y=W1)[0] == "TP_ERR_ALIAS"         # ln_out on the residual
+    assert sp_call(lib, [X], x=Y + 16, y=Y)[0] == "TP_ERR_ALIAS"      # x_out overlaps ln_out
+    assert sp_call(lib, [X], g=Y + 64, y=Y)[0] == "TP_ERR_ALIAS"      # gamma inside ln_out
+    assert sp_call(lib, [X], x=X + 16)[0] == "TP_ERR_ALIAS"           # x_out partly over a partial
+
+
+def test_sp_reduce_layernorm_empty_is_a_no_op(lib):
+    assert sp_call(lib, [X], rows=0)[0] == "TP_SUCCESS"
+    assert sp_call(lib, [X], rows=3, slice_=5, nslices=8)[0] == "TP_SUCCESS"   # empty block
