@@ -241,28 +241,32 @@ hipError_t partial_reduce(const ReducePtrs& ptrs, int t, int pdt, const void* R,
 // Column and Row Parallelism": LayerNorm reduces over all features, so it is
 // not split by columns; the rows are split instead).
 //
-// One workgroup of 256 threads per row; thread k owns the 8-element groups
-// k, k + 256, ... (G of them), loads them from every partial (a partial's G
-// loads in flight together), sums in the fixed order P_0 + ... + P_{t-1} + R
-// in fp32 and keeps the row in registers.  Mean, then the biased variance
-// of (x - mean), each as a fixed-order block sum (wave shuffles, then the
-// four waves' sums in order); y = (x - mean) * rsqrt(var + eps) * gamma +
-// beta.  HBM-bound: t partials + residual read, x and y written.
+// One workgroup per row, nt threads (a multiple of 64, at most 1024); thread
+// k owns the 8-element groups k, k + nt, ... (G of them) and loads each the
+// way reduce_kernel loads its group: partial 0 and the next C partials (with
+// the last chunk, the residual) all in flight before the first add, so a
+// group costs a few memory round trips, not one per partial; the sum follows
+// the fixed order P_0 + ... + P_{t-1} + R in fp32 and the row stays in
+// registers.  Mean, then the biased variance of (x - mean), each a
+// fixed-order block sum (wave shuffles, then the waves' sums in order);
+// y = (x - mean) * rsqrt(var + eps) * gamma + beta.  HBM-bound: t partials
+// and the residual read, x and y written.
 // ---------------------------------------------------------------------------
 namespace {
 
-__device__ __forceinline__ float block_sum256(float v, float* red) {
+__device__ __forceinline__ float block_sum(float v, float* red, int nw) {
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o);
-  const int wave = threadIdx.x >> 6;
   __syncthreads();  // red[] free (a previous sum's readers are done)
-  if ((threadIdx.x & 63) == 0) red[wave] = v;
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
   __syncthreads();
-  return ((red[0] + red[1]) + red[2]) + red[3];
+  float s = red[0];
+  for (int w = 1; w < nw; ++w) s += red[w];
+  return s;
 }
 
 template <int DT>
-__device__ __forceinline__ void store8_dyn(void* base, int64_t g, const float* v) {
+__device__ __forceinline__ void store8_nt(void* base, int64_t g, const float* v) {
   if (DT == DT_BF16) {
     u32x4 w;
 #pragma unroll
@@ -275,71 +279,98 @@ __device__ __forceinline__ void store8_dyn(void* base, int64_t g, const float* v
   }
 }
 
-template <int PDT, int G>
-__global__ void __launch_bounds__(256)
+// The residual's group, its element type chosen at run time (uniform).
+__device__ __forceinline__ Raw8 rawload8_dyn(const void* base, int dt, int64_t g) {
+  return dt == DT_BF16 ? rawload8<DT_BF16>(base, g) : rawload8<DT_F32>(base, g);
+}
+__device__ __forceinline__ void add8_dyn(const Raw8& r, int dt, float* acc) {
+  if (dt == DT_BF16)
+    add8<DT_BF16>(r, acc);
+  else
+    add8<DT_F32>(r, acc);
+}
+
+// Launch bound by groups per thread: wider rows get fewer, larger threads.
+template <int G>
+struct LnThreads {
+  static constexpr int value = G <= 2 ? 1024 : (G == 4 ? 768 : 512);
+};
+
+template <int PDT, int C, int G>
+__global__ void __launch_bounds__(LnThreads<G>::value)
 reduce_ln_kernel(ReducePtrs ptrs, int t, const void* R, int rdt, void* xout, int xdt,
                  void* yout, int ydt, const float* gamma, const float* beta, float eps,
                  int64_t rows, int cols) {
-  __shared__ float red[4];
+  __shared__ float red[16];
   const int ng = cols / 8;  // 8-element groups per row
+  const int nt = blockDim.x, nw = nt >> 6;
   for (int64_t row = blockIdx.x; row < rows; row += gridDim.x) {
-    float v[G][8];
     const int64_t g0 = row * ng;
+    // slot j: group threadIdx.x + nt*j of the row, if it exists (a missing
+    // one re-reads the row's first group and is neither summed nor stored)
+    auto ok = [&](int j) { return (int)threadIdx.x + nt * j < ng; };
+    auto gi = [&](int j) { return g0 + (ok(j) ? (int)threadIdx.x + nt * j : 0); };
+    // Slot by slot (a row spans 1024 threads at most, so a workgroup has
+    // 16 KB x (C + 2) of loads in flight per chunk even one slot at a
+    // time), chunk by chunk: partial 0, partials 1..C and, with the last
+    // chunk, the residual are loaded before the first add.
+    float v[G][8];
 #pragma unroll
-    for (int j = 0; j < G; ++j)
+    for (int j = 0; j < G; ++j) {
+      {
+        const bool last = 1 + C >= t;
+        Raw8 pv[C], rr;
+        const Raw8 r0 = rawload8<PDT>(ptrs.p[0], gi(j));
 #pragma unroll
-      for (int e = 0; e < 8; ++e) v[j][e] = 0.0f;
-    for (int i = 0; i < t; ++i) {
-      Raw8 r[G];
+        for (int u = 0; u < C; ++u) pv[u] = rawload8<PDT>(ptrs.p[1 + u < t ? 1 + u : t - 1], gi(j));
+        if (R != nullptr && last) rr = rawload8_dyn(R, rdt, gi(j));
+        unpack8<PDT>(r0, v[j]);
 #pragma unroll
-      for (int j = 0; j < G; ++j) {
-        const int g = threadIdx.x + 256 * j;
-        if (g < ng) r[j] = rawload8<PDT>(ptrs.p[i], g0 + g);
+        for (int u = 0; u < C; ++u)
+          if (1 + u < t) add8<PDT>(pv[u], v[j]);
+        if (R != nullptr && last) add8_dyn(rr, rdt, v[j]);
       }
+      for (int i0 = 1 + C; i0 < t; i0 += C) {
+        const bool last = i0 + C >= t;
+        Raw8 pv[C], rr;
 #pragma unroll
-      for (int j = 0; j < G; ++j)
-        if (threadIdx.x + 256 * j < ng) add8<PDT>(r[j], v[j]);
-    }
-    if (R != nullptr) {
+        for (int u = 0; u < C; ++u) pv[u] = rawload8<PDT>(ptrs.p[i0 + u < t ? i0 + u : t - 1], gi(j));
+        if (R != nullptr && last) rr = rawload8_dyn(R, rdt, gi(j));
 #pragma unroll
-      for (int j = 0; j < G; ++j) {
-        const int g = threadIdx.x + 256 * j;
-        if (g < ng) {
-          if (rdt == DT_BF16)
-            add8<DT_BF16>(rawload8<DT_BF16>(R, g0 + g), v[j]);
-          else
-            add8<DT_F32>(rawload8<DT_F32>(R, g0 + g), v[j]);
-        }
+        for (int u = 0; u < C; ++u)
+          if (i0 + u < t) add8<PDT>(pv[u], v[j]);
+        if (R != nullptr && last) add8_dyn(rr, rdt, v[j]);
       }
     }
     float s = 0.0f;
 #pragma unroll
     for (int j = 0; j < G; ++j)
-      if (threadIdx.x + 256 * j < ng)
+      if (ok(j))
 #pragma unroll
         for (int e = 0; e < 8; ++e) s += v[j][e];
-    const float mean = block_sum256(s, red) / (float)cols;
+    const float mean = block_sum(s, red, nw) / (float)cols;
     float q = 0.0f;
 #pragma unroll
     for (int j = 0; j < G; ++j)
-      if (threadIdx.x + 256 * j < ng)
+      if (ok(j))
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
           const float d = v[j][e] - mean;
           q = __builtin_fmaf(d, d, q);
         }
-    const float var = block_sum256(q, red) / (float)cols;
+    const float var = block_sum(q, red, nw) / (float)cols;
     const float rstd = 1.0f / sqrtf(var + eps);
 #pragma unroll
     for (int j = 0; j < G; ++j) {
-      const int g = threadIdx.x + 256 * j;
-      if (g >= ng) continue;
+      if (!ok(j)) continue;
+      const int64_t g = gi(j);
       if (xout != nullptr) {
         if (xdt == DT_BF16)
-          store8_dyn<DT_BF16>(xout, g0 + g, v[j]);
+          store8_nt<DT_BF16>(xout, g, v[j]);
         else
-          store8_dyn<DT_F32>(xout, g0 + g, v[j]);
+          store8_nt<DT_F32>(xout, g, v[j]);
       }
+      const int c8 = (int)(g - g0);  // group within the row
       float gm[8], bt[8];
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
@@ -347,7 +378,7 @@ reduce_ln_kernel(ReducePtrs ptrs, int t, const void* R, int rdt, void* xout, int
         bt[e] = 0.0f;
       }
       if (gamma != nullptr) {
-        const f32x4* pg = reinterpret_cast<const f32x4*>(gamma) + 2 * g;
+        const f32x4* pg = reinterpret_cast<const f32x4*>(gamma) + 2 * c8;
         const f32x4 a = pg[0], b = pg[1];
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
@@ -356,7 +387,7 @@ reduce_ln_kernel(ReducePtrs ptrs, int t, const void* R, int rdt, void* xout, int
         }
       }
       if (beta != nullptr) {
-        const f32x4* pb = reinterpret_cast<const f32x4*>(beta) + 2 * g;
+        const f32x4* pb = reinterpret_cast<const f32x4*>(beta) + 2 * c8;
         const f32x4 a = pb[0], b = pb[1];
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
@@ -368,34 +399,57 @@ reduce_ln_kernel(ReducePtrs ptrs, int t, const void* R, int rdt, void* xout, int
 #pragma unroll
       for (int e = 0; e < 8; ++e) y[e] = __builtin_fmaf((v[j][e] - mean) * rstd, gm[e], bt[e]);
       if (ydt == DT_BF16)
-        store8_dyn<DT_BF16>(yout, g0 + g, y);
+        store8_nt<DT_BF16>(yout, g, y);
       else
-        store8_dyn<DT_F32>(yout, g0 + g, y);
+        store8_nt<DT_F32>(yout, g, y);
     }
   }
 }
 
-template <int PDT, int G>
+template <int PDT, int C, int G>
 hipError_t launch_ln(const ReducePtrs& ptrs, int t, const void* R, int rdt, void* xout, int xdt,
                      void* yout, int ydt, const float* gamma, const float* beta, float eps,
                      int64_t rows, int cols, hipStream_t s) {
+  const int ng = cols / 8;
+  const int nt = 64 * ((ng + 64 * G - 1) / (64 * G));  // threads per row: G groups each
   const int64_t blocks = rows < ((int64_t)1 << 24) - 1 ? rows : ((int64_t)1 << 24) - 1;
-  hipLaunchKernelGGL((reduce_ln_kernel<PDT, G>), dim3((unsigned)blocks), dim3(256), 0, s, ptrs,
+  hipLaunchKernelGGL((reduce_ln_kernel<PDT, C, G>), dim3((unsigned)blocks), dim3(nt), 0, s, ptrs,
                      t, R, rdt, xout, xdt, yout, ydt, gamma, beta, eps, rows, cols);
   return hipGetLastError();
 }
 
-template <int PDT>
+// Groups per thread: the fewest (1, 2, 4, 8) that keep a row within the
+// kernel's thread bound (1024, 1024, 768, 512 threads).
+template <int PDT, int C>
 hipError_t launch_ln_g(const ReducePtrs& ptrs, int t, const void* R, int rdt, void* xout,
                        int xdt, void* yout, int ydt, const float* gamma, const float* beta,
                        float eps, int64_t rows, int cols, hipStream_t s) {
-  const int groups = (cols / 8 + 255) / 256;  // 8-element groups per thread
-  if (groups <= 1) return launch_ln<PDT, 1>(ptrs, t, R, rdt, xout, xdt, yout, ydt, gamma, beta, eps, rows, cols, s);
-  if (groups <= 2) return launch_ln<PDT, 2>(ptrs, t, R, rdt, xout, xdt, yout, ydt, gamma, beta, eps, rows, cols, s);
-  if (groups <= 4) return launch_ln<PDT, 4>(ptrs, t, R, rdt, xout, xdt, yout, ydt, gamma, beta, eps, rows, cols, s);
-  if (groups <= 8) return launch_ln<PDT, 8>(ptrs, t, R, rdt, xout, xdt, yout, ydt, gamma, beta, eps, rows, cols, s);
-  if (groups <= 16) return launch_ln<PDT, 16>(ptrs, t, R, rdt, xout, xdt, yout, ydt, gamma, beta, eps, rows, cols, s);
+  const int ng = cols / 8;
+  if (ng <= 1024) return launch_ln<PDT, C, 1>(ptrs, t, R, rdt, xout, xdt, yout, ydt, gamma, beta, eps, rows, cols, s);
+  if (ng <= 2048) return launch_ln<PDT, C, 2>(ptrs, t, R, rdt, xout, xdt, yout, ydt, gamma, beta, eps, rows, cols, s);
+  if (ng <= 3072) return launch_ln<PDT, C, 4>(ptrs, t, R, rdt, xout, xdt, yout, ydt, gamma, beta, eps, rows, cols, s);
+  if (ng <= 4096) return launch_ln<PDT, C, 8>(ptrs, t, R, rdt, xout, xdt, yout, ydt, gamma, beta, eps, rows, cols, s);
   return hipErrorInvalidValue;
+}
+
+// Chunk size as for the reduce: t-1 for t <= 8 (no duplicate loads), 8 beyond.
+template <int PDT>
+hipError_t launch_ln_c(const ReducePtrs& ptrs, int t, const void* R, int rdt, void* xout,
+                       int xdt, void* yout, int ydt, const float* gamma, const float* beta,
+                       float eps, int64_t rows, int cols, hipStream_t s) {
+#define TP_LN_ARGS ptrs, t, R, rdt, xout, xdt, yout, ydt, gamma, beta, eps, rows, cols, s
+  switch (t) {
+    case 1:
+    case 2: return launch_ln_g<PDT, 1>(TP_LN_ARGS);
+    case 3: return launch_ln_g<PDT, 2>(TP_LN_ARGS);
+    case 4: return launch_ln_g<PDT, 3>(TP_LN_ARGS);
+    case 5: return launch_ln_g<PDT, 4>(TP_LN_ARGS);
+    case 6: return launch_ln_g<PDT, 5>(TP_LN_ARGS);
+    case 7: return launch_ln_g<PDT, 6>(TP_LN_ARGS);
+    case 8: return launch_ln_g<PDT, 7>(TP_LN_ARGS);
+    default: return launch_ln_g<PDT, 8>(TP_LN_ARGS);
+  }
+#undef TP_LN_ARGS
 }
 
 }  // namespace
@@ -406,9 +460,9 @@ hipError_t reduce_layernorm(const ReducePtrs& ptrs, int t, int pdt, const void* 
                             hipStream_t s) {
   if (rows == 0) return hipSuccess;
   if (cols % 8 || cols > kLnMaxCols) return hipErrorInvalidValue;
-  return pdt == DT_BF16 ? launch_ln_g<DT_BF16>(ptrs, t, R, rdt, xout, xdt, yout, ydt, gamma,
+  return pdt == DT_BF16 ? launch_ln_c<DT_BF16>(ptrs, t, R, rdt, xout, xdt, yout, ydt, gamma,
                                                beta, eps, rows, cols, s)
-                        : launch_ln_g<DT_F32>(ptrs, t, R, rdt, xout, xdt, yout, ydt, gamma,
+                        : launch_ln_c<DT_F32>(ptrs, t, R, rdt, xout, xdt, yout, ydt, gamma,
                                               beta, eps, rows, cols, s);
 }
 
