@@ -592,28 +592,35 @@ def summarize_profiles(trace_csv, fetch_csv, write_csv, cmd_stats, cmd_pmc):
              "and number of workgroups.", "",
              "| kernel | workgroups | calls | avg us | min us | max us | share |",
              "|---|---:|---:|---:|---:|---:|---:|"]
-    avg_pair = 0.0
+    avg_call = 0.0
     for (name, wgs), v in sorted(groups.items(), key=lambda kv: -sum(kv[1])):
         lines.append(f"| `{name}` | {wgs} | {len(v)} | {sum(v)/len(v):.1f} | {min(v):.1f} | "
                      f"{max(v):.1f} | {100*sum(v)/total_us:.1f}% |")
-        avg_pair += sum(v) / len(v)
-    lines += ["", f"One tp_ffn_shard call = the two kernels above: {avg_pair:.1f} us on average, "
-              f"{fl/1e12:.2f} TFLOP algorithmic, {fl/(avg_pair*1e-6)/1e12:.0f} TFLOP/s = "
-              f"{fl/(avg_pair*1e-6)/1e12/PEAK_BF16_TFLOPS:.1%} of the {PEAK_BF16_TFLOPS} TFLOP/s "
+        avg_call += sum(v) / len(v)
+    lines += ["", f"One tp_ffn_shard call = one dispatch of each kernel above (the K-blocking copy "
+              f"of X, GEMM1 with the GeLU epilogue, GEMM2 over its tile plan): {avg_call:.1f} us "
+              f"on average, {fl/1e12:.2f} TFLOP algorithmic, {fl/(avg_call*1e-6)/1e12:.0f} TFLOP/s = "
+              f"{fl/(avg_call*1e-6)/1e12/PEAK_BF16_TFLOPS:.1%} of the {PEAK_BF16_TFLOPS} TFLOP/s "
               "bf16 peak.", "", f"GEMM source hash: `{gemm_src}`"]
     with open(os.path.join(ROOT, "profiles", f"kernel_stats_ffn_shard_{tag}.md"), "w") as f:
         f.write("\n".join(lines) + "\n")
 
-    fe, fe_names, _ = _read_counters(fetch_csv)
-    wr, wr_names, _ = _read_counters(write_csv)
+    fe, fe_names, fe_grid = _read_counters(fetch_csv)
+    wr, wr_names, wr_grid = _read_counters(write_csv)
     copy_fetch = _copy_factors(fe, fe_names)("FETCH_SIZE")
     copy_write = _copy_factors(wr, wr_names)("WRITE_SIZE")
     f_fac = (COPY_BYTES / 1024) / copy_fetch
     w_fac = (COPY_BYTES / 1024) / copy_write
 
-    def kmean(per, names, tag_, counter):
-        vals = [c[counter] for d, c in per.items() if tag_ in names[d] and counter in c]
-        return sum(vals) / len(vals)
+    def by_kernel(per, names, grid, counter):
+        out = {}
+        for d, c in per.items():
+            n = _short(names[d])
+            if n.startswith("at::") or "copyBuffer" in n or "fillBuffer" in n or counter not in c:
+                continue
+            out.setdefault((n, grid[d]), []).append(c[counter])
+        return {k: sum(v) / len(v) for k, v in out.items()}
+    fk, wk = by_kernel(fe, fe_names, fe_grid, "FETCH_SIZE"), by_kernel(wr, wr_names, wr_grid, "WRITE_SIZE")
     table = [f"# HBM traffic per launch: FFN shard t={p['t']} i={p['i']}, hidden {h}, ffn "
              f"{p['ffn']}, {M} tokens", "",
              "Commands (from the repository root, one MI355X, one counter per run):", "",
@@ -622,25 +629,25 @@ def summarize_profiles(trace_csv, fetch_csv, write_csv, cmd_stats, cmd_pmc):
              f"Calibration: a {COPY_BYTES >> 20} MiB device copy read FETCH_SIZE {copy_fetch:.0f} KiB "
              f"and WRITE_SIZE {copy_write:.0f} KiB, so the counters are scaled by "
              f"{f_fac:.3f} (fetch) and {w_fac:.3f} (write).", "",
-             "| kernel | FETCH_SIZE KiB | WRITE_SIZE KiB | scaled MB read | scaled MB written |",
-             "|---|---:|---:|---:|---:|"]
+             "| kernel | workgroups | FETCH_SIZE KiB | WRITE_SIZE KiB | scaled MB read | scaled MB written |",
+             "|---|---:|---:|---:|---:|---:|"]
     total = 0.0
-    for label, k in {"GEMM1 + GeLU": "EpiGelu", "GEMM2": "EpiStore"}.items():
-        fk, wk = kmean(fe, fe_names, k, "FETCH_SIZE"), kmean(wr, wr_names, k, "WRITE_SIZE")
-        rb_, wb_ = fk * 1024 * f_fac, wk * 1024 * w_fac
+    for key in sorted(fk, key=lambda k: -fk[k]):
+        f_, w_ = fk[key], wk.get(key, 0.0)
+        rb_, wb_ = f_ * 1024 * f_fac, w_ * 1024 * w_fac
         total += rb_ + wb_
-        table.append(f"| {label} | {fk:.0f} | {wk:.0f} | {rb_/1e6:.1f} | {wb_/1e6:.1f} |")
+        table.append(f"| `{key[0]}` | {key[1]} | {f_:.0f} | {w_:.0f} | {rb_/1e6:.1f} | {wb_/1e6:.1f} |")
     alg = 2 * (M * h + h * fs + M * fs) + 2 * (M * fs + fs * h) + 4 * M * h
-    table += ["", f"Sum for one tp_ffn_shard call: {total/1e6:.1f} MB of HBM traffic; the "
-              f"algorithmic minimum (X, W1, GeLU(Z) written and re-read, W2, fp32 Y) is "
-              f"{alg/1e6:.1f} MB ({total/alg:.2f}x).", "", f"GEMM source hash: `{gemm_src}`"]
+    table += ["", f"Sum for one tp_ffn_shard call (one dispatch of each kernel): {total/1e6:.1f} MB "
+              f"of HBM traffic; the algorithmic minimum (X, W1, GeLU(Z) written and re-read, W2, "
+              f"fp32 Y) is {alg/1e6:.1f} MB ({total/alg:.2f}x).", "", f"GEMM source hash: `{gemm_src}`"]
     with open(os.path.join(ROOT, "profiles", f"traffic_ffn_shard_{tag}.md"), "w") as f:
         f.write("\n".join(table) + "\n")
     with open(TRAFFIC_FILE, "w") as f:
         json.dump({"kernel_source_sha": gemm_src, "traffic_bytes": round(total),
                    "fetch_factor": f_fac, "write_factor": w_fac, "algorithmic_bytes": alg,
-                   "avg_call_us_trace": round(avg_pair, 2)}, f, indent=1)
-    print(f"wrote profiles for {tag} (call {avg_pair:.1f} us; traffic {total/1e6:.1f} MB, "
+                   "avg_call_us_trace": round(avg_call, 2)}, f, indent=1)
+    print(f"wrote profiles for {tag} (call {avg_call:.1f} us; traffic {total/1e6:.1f} MB, "
           f"algorithmic {alg/1e6:.1f} MB)")
 
 
@@ -715,12 +722,12 @@ def summarize_attn_profile(trace_csv, cmd):
             per.setdefault(_short(x["Kernel_Name"]), []).append(dur(x))
             grids[_short(x["Kernel_Name"])] = wg(x)
         calls.append((int(seq[3]["End_Timestamp"]) - int(seq[0]["Start_Timestamp"])) / 1e3)
-    role = {"EpiQkv": f"QKV projection [{S} x {h}] x [{h} x {3 * nl * d}], Q/K hi/lo rows, "
-                      "V^T hi/lo as 16-byte runs along the sequence",
+    role = {"EpiQkv": f"QKV projection [{S} x {h}] x [{h} x {3 * nl * d}], Q and K fp16 rows, "
+                      "V^T as an fp16 hi/lo pair in 16-byte runs along the sequence",
             "attn_fwd": "causal attention (query blocks of 128 or 256 x up to a chunk of 64-key tiles each)",
             "attn_combine": "merge of the split query blocks",
-            "EpiStore": f"output projection [{S} x {2 * nl * d} (O hi, O lo)] x [{nl * d} x {h}], "
-                        "fp32 partial"}
+            "EpiStore": f"output projection [{S} x {nl * d}] x [{nl * d} x {h}] with O as a bf16 "
+                        "hi/lo pair (both halves against the same W_o tile per stage), fp32 partial"}
     flop = 2 * S * h * 3 * nl * d + 4 * d * S * (S + 1) // 2 * nl + 2 * S * nl * d * h
     med = statistics.median(calls)
     lines = [f"# Kernel durations: attention shard t={a['t']} i={a['i']}, hidden {h}, "
@@ -782,6 +789,69 @@ def summarize_counters(counter_csv, cmd):
     print(f"wrote profiles/counters_mfma_lds_ffn_attn.md ({len(per)} dispatches)")
 
 
+def summarize_clock_counters(csvs, cmd):
+    """profiles/counters_mfma_clock.md from one rocprofv3 run with --pmc
+    SQ_VALU_MFMA_BUSY_CYCLES GRBM_GUI_ACTIVE SQ_BUSY_CYCLES SQ_INSTS_LDS
+    SQ_LDS_BANK_CONFLICT and --kernel-trace over the headline, the t=8 step
+    and the attention shard: per kernel and grid, the duration, the MFMA busy
+    fraction at the measured clock and at the nominal 2.4 GHz, and the
+    shader clock implied by GRBM_GUI_ACTIVE."""
+    import csv
+    import statistics
+    per, names, grids, dur = {}, {}, {}, {}
+    for k in range(0, len(csvs) - 1, 2):   # dispatch ids are per run: prefix the run
+        p_, n_, g_ = _read_counters(csvs[k])
+        per.update({f"{k}:{d}": v for d, v in p_.items()})
+        names.update({f"{k}:{d}": v for d, v in n_.items()})
+        grids.update({f"{k}:{d}": v for d, v in g_.items()})
+        for r in csv.DictReader(open(csvs[k + 1])):
+            dur[f"{k}:{r['Dispatch_Id']}"] = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) * 1e-9
+    groups = {}
+    for d, c in per.items():
+        n = _short(names[d])
+        if n.startswith("at::") or "copyBuffer" in n or "fillBuffer" in n or d not in dur:
+            continue
+        groups.setdefault((n, grids[d]), []).append((dur[d], c))
+    simds = 256 * 4
+    lines = ["# MFMA utilisation and shader clock per kernel", "",
+             "Command (from the repository root, on one MI355X):", "", "```", cmd, "```", "",
+             "Per dispatch: duration from the kernel trace of the same run; `GRBM_GUI_ACTIVE` "
+             "counts GPU clock cycles while the GPU is busy, summed over the 8 XCDs, so "
+             "`GRBM_GUI_ACTIVE / 8 / duration` is the shader clock the kernel ran at (memory-bound "
+             "kernels read 2.1-2.3 GHz this way, against the nominal 2.4 GHz); the counting "
+             "window is a few microseconds longer than the kernel, so the clock (and the busy "
+             "fraction at it) is given only for kernels of a millisecond or more. "
+             "`SQ_VALU_MFMA_BUSY_CYCLES` is the matrix pipes' busy cycles summed over the "
+             "1024 SIMDs (a 32x32x16 bf16 MFMA keeps a SIMD's pipe busy 32 cycles), so "
+             "busy / (1024 x cycles at the measured clock) is the fraction of time the matrix "
+             "pipes worked, and busy / (1024 x duration x 2.4 GHz) the fraction of the nominal "
+             "peak. LDS bank conflicts per LDS instruction from `SQ_LDS_BANK_CONFLICT / "
+             "SQ_INSTS_LDS`. Medians over the run's dispatches of each kernel and grid.", "",
+             "| kernel | workgroups | dispatches | median us | clock GHz | MFMA busy at clock | "
+             "MFMA busy at 2.4 GHz | LDS conflict cycles / instr |",
+             "|---|---:|---:|---:|---:|---:|---:|---:|"]
+    for (n, wg), v in sorted(groups.items(), key=lambda kv: -sum(x[0] for x in kv[1])):
+        d = statistics.median(x[0] for x in v)
+        clk = statistics.median(x[1].get("GRBM_GUI_ACTIVE", 0) / 8 / x[0] for x in v)
+        busy = statistics.median(x[1].get("SQ_VALU_MFMA_BUSY_CYCLES", 0) for x in v)
+        at_clk = busy / (simds * d * clk) if clk else 0.0
+        nominal = busy / (simds * d * 2.4e9)
+        ins = sum(x[1].get("SQ_INSTS_LDS", 0) for x in v)
+        conf = sum(x[1].get("SQ_LDS_BANK_CONFLICT", 0) for x in v)
+        # the counting window exceeds the kernel by a few us: the clock is
+        # read only for kernels of a millisecond or more
+        long_ = d >= 1e-3
+        lines.append(f"| `{n}` | {wg} | {len(v)} | {d*1e6:.1f} | "
+                     f"{(f'{clk/1e9:.2f}' if long_ else '-')} | "
+                     f"{(f'{at_clk:.1%}' if long_ else '-')} | "
+                     f"{nominal:.1%} | {(conf / ins if ins else 0.0):.3f} |")
+    lines += ["", f"GEMM source hash: `{src_hash('gemm.hip')}`, attention: "
+              f"`{src_hash('attention.hip')}`"]
+    with open(os.path.join(ROOT, "profiles", "counters_mfma_clock.md"), "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print("wrote profiles/counters_mfma_clock.md")
+
+
 def summarize_sweep(path, cmd):
     """Write profiles/sweep_ffn_shard_tokens2048.md from a --sweep JSONL file."""
     recs = [json.loads(line) for line in open(path) if line.strip()]
@@ -828,6 +898,11 @@ def main():
                     help="time the two rotated reduce rows only (profiling runs)")
     ap.add_argument("--attn-only", action="store_true",
                     help="time the attention shard row only (profiling runs)")
+    ap.add_argument("--step-only", action="store_true",
+                    help="time the t=8 hidden-4096 FFN step row only (profiling runs)")
+    ap.add_argument("--summarize-clock-counters", nargs="+", metavar="CSV",
+                    help="COUNTER_CSV TRACE_CSV pairs (one per run): write the per-kernel "
+                         "MFMA-utilisation / clock table")
     ap.add_argument("--no-sweep-torch", action="store_true",
                     help="skip the torch (hipBLASLt) comparison at each sweep point")
     ap.add_argument("--sweep-out", metavar="JSONL", default=None,
@@ -854,6 +929,9 @@ def main():
         return
     if args.summarize_profiles:
         summarize_profiles(*args.summarize_profiles, *args.profile_commands)
+        return
+    if args.summarize_clock_counters:
+        summarize_clock_counters(args.summarize_clock_counters, args.profile_commands[0])
         return
     if args.summarize_reduce_traffic:
         summarize_reduce_traffic(*args.summarize_reduce_traffic, *args.profile_commands)
@@ -883,6 +961,9 @@ def main():
         return
     if args.attn_only:
         log(json.dumps(attn_row(K, W)))
+        return
+    if args.step_only:
+        log(json.dumps(ffn_step_row(K, W, fused=False)[0]))
         return
 
     # ---------------- headline: the sweep's hidden-22528, t=1 FFN shard ----------------
