@@ -53,7 +53,9 @@ namespace tp {
 namespace {
 
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int D = 128;    // head dim
@@ -164,19 +166,19 @@ attn_fwd_kernel(QkvOut q, int causal, uint16_t* __restrict__ O, int o_kbs,
 #pragma unroll
   for (int qg = 0; qg < NQG; ++qg) myq[qg] = qb * QB + wave * QW + qg * 16 + (lane & 15);
 
-  // Q as the B operand: query myq, head dims dc*32 + 8g .. +7.
+  // Q as the B operand: query myq, head dims dc*32 + 8g .. +7.  Buffer loads:
+  // queries past the sequence read as zero, so no load waits on a select.
   f16x8 qf[NQG][4];
+  {
+    const __amdgpu_buffer_rsrc_t rq = make_rsrc(Qp, (int64_t)S * D * 2);
 #pragma unroll
-  for (int qg = 0; qg < NQG; ++qg)
+    for (int qg = 0; qg < NQG; ++qg)
 #pragma unroll
-    for (int dc = 0; dc < 4; ++dc) {
-      if (myq[qg] < S) {
-        qf[qg][dc] = *reinterpret_cast<const f16x8*>(Qp + (int64_t)myq[qg] * D + dc * 32 + 8 * g);
-      } else {
-        const u32x4 z = {0, 0, 0, 0};
-        qf[qg][dc] = __builtin_bit_cast(f16x8, z);
+      for (int dc = 0; dc < 4; ++dc) {
+        const int off = myq[qg] < S ? (myq[qg] * D + dc * 32 + 8 * g) * 2 : OOB;
+        qf[qg][dc] = __builtin_bit_cast(f16x8, __builtin_amdgcn_raw_buffer_load_b128(rq, off, 0, 0));
       }
-    }
+  }
 
   f32x4 o[NQG][8];
 #pragma unroll
@@ -228,12 +230,18 @@ attn_fwd_kernel(QkvOut q, int causal, uint16_t* __restrict__ O, int o_kbs,
   constexpr int TILE_DMAS = NARR * NDW;
 
   stage(kt0 * KT, 0);
-  if (kt0 + 1 < kt1) {
-    stage((kt0 + 1) * KT, 1);
-    wait_vmcnt<TILE_DMAS>();
-  } else {
-    wait_vmcnt<0>();
-  }
+  // The Q fragments came from ordinary loads, which the compiler tracks; the
+  // tile DMAs and their waits are inline assembly it cannot see.  Reading the
+  // fragments here makes it wait for them (and, loads completing in order,
+  // for tile kt0) once, before the loop; otherwise it leaves their wait to
+  // the loop's first MFMA and, not knowing how many loads follow them, waits
+  // for all of them there, draining the prefetch of tile kt+2 on every tile.
+#pragma unroll
+  for (int qg = 0; qg < NQG; ++qg)
+#pragma unroll
+    for (int dc = 0; dc < 4; ++dc) asm volatile("" ::"v"(qf[qg][dc]));
+  wait_vmcnt<0>();
+  if (kt0 + 1 < kt1) stage((kt0 + 1) * KT, 1);
   __syncthreads();
   for (int kt = kt0; kt < kt1; ++kt) {
     const int k0 = kt * KT;
@@ -345,17 +353,24 @@ attn_fwd_kernel(QkvOut q, int causal, uint16_t* __restrict__ O, int o_kbs,
       mt = fmaxf(mt, __shfl_xor(mt, 32));
       const float m_new = fmaxf(m_run[qg], mt * scale_log2);
       const float m_use = (m_new == -__builtin_inff()) ? 0.0f : m_new;
+      // probabilities rounded to fp16 in pairs; the denominator adds exactly
+      // those rounded values, two per packed dot product with (1, 1)
       float psum = 0.0f;
+      const f16x2 ones = {(_Float16)1.0f, (_Float16)1.0f};
 #pragma unroll
       for (int kc = 0; kc < 2; ++kc)
 #pragma unroll
         for (int hb = 0; hb < 2; ++hb)
 #pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const _Float16 p = (_Float16)__builtin_amdgcn_exp2f(
+          for (int e = 0; e < 4; e += 2) {
+            const float pa = __builtin_amdgcn_exp2f(
                 __builtin_fmaf(s[qg][kc][hb][e], scale_log2, -m_use));
-            psum += (float)p;
-            pb[qg][kc][hb * 4 + e] = p;
+            const float pc = __builtin_amdgcn_exp2f(
+                __builtin_fmaf(s[qg][kc][hb][e + 1], scale_log2, -m_use));
+            const f16x2 p2 = __builtin_convertvector(f32x2{pa, pc}, f16x2);
+            psum = __builtin_amdgcn_fdot2(p2, ones, psum, false);
+            pb[qg][kc][hb * 4 + e] = p2[0];
+            pb[qg][kc][hb * 4 + e + 1] = p2[1];
           }
       if (__builtin_amdgcn_ballot_w64(m_new != m_run[qg]) != 0) {
         const float alpha = __builtin_amdgcn_exp2f(m_run[qg] - m_use);
