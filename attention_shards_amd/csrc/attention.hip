@@ -637,7 +637,12 @@ int64_t count_items(int qbs, int nqb, int seq, int causal, int ch) {
 // used instead (8 heads, 2048 causal tokens, 128-query blocks: 10 tiles, 272
 // workgroups, 54 us vs 68 us).  Larger chunks are not searched: there the
 // estimate is least reliable and measured times vary by up to 40% between
-// neighbouring sizes.
+// neighbouring sizes.  The one exception is the unsplit key range (one
+// workgroup per query block, nothing to merge), taken when its estimate is
+// at least 10% below the chosen chunk's: with many query blocks per CU the
+// longest-first order pairs long and short ranges evenly (8 heads, 8192
+// causal tokens, 128-query blocks: shard 939 us vs 986 us; 4 x 2048 tokens,
+// 24 heads, 256-query blocks: 2820 us vs 2882 us).
 std::pair<int, double> choose_chunk(const VariantCost& v, int nqb, int nbh, int seq, int causal,
                                     int ncu) {
   int64_t tiles = 0;
@@ -662,6 +667,13 @@ std::pair<int, double> choose_chunk(const VariantCost& v, int nqb, int nbh, int 
     if (best_cost <= 0.9 * base) {
       best = pick;
       est = best_cost;
+    }
+  }
+  if (max_nt > best && count_items(v.qb, nqb, seq, causal, max_nt) * nbh <= MAX_ITEMS) {
+    const double whole = split_cost(v, nqb, nbh, seq, causal, max_nt, ncu);
+    if (whole <= 0.9 * est) {
+      best = max_nt;
+      est = whole;
     }
   }
   return {best, est};
