@@ -3,7 +3,7 @@
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
                     [--headline-only] [--reduce-only] [--copy-calibration]
-    python bench.py --summarize-{profiles,reduce-traffic,attn-profile,counters,sweep} ...
+    python bench.py --summarize-{profiles,reduce-traffic,attn-profile,sweep,tile-sweep} ...
                     (write profiles/*.md from rocprofv3 output)
 
 Headline workload (one "step"): the FFN shard of the hidden-size sweep's
@@ -751,42 +751,122 @@ def summarize_attn_profile(trace_csv, cmd):
     print(f"wrote attention profile ({len(calls)} calls, median {med:.1f} us)")
 
 
-def summarize_counters(counter_csv, cmd):
-    """Write profiles/counters_mfma_lds_ffn_attn.md from a rocprofv3 --pmc run
-    of MfmaUtil, SQ_VALU_MFMA_BUSY_CYCLES, GRBM_GUI_ACTIVE, SQ_LDS_BANK_CONFLICT
-    and SQ_INSTS_LDS over a bench run: per kernel (and grid size), the mean of
-    rocprofv3's MfmaUtil and the LDS bank-conflict cycles per LDS instruction."""
+# First products of FFN shards (t = 1) whose tile plans are single kinds of
+# one tile per CU: [tokens, ffn] -> 128x192, 256x192, 256x256 (X K-blocked,
+# ffn >= 8192) and 256x128 tiles; K (the hidden size) from 2048 to 16384.
+TILE_SWEEP = ((2048, 3072), (2048, 6144), (2048, 8192), (4096, 2048))
+TILE_SWEEP_K = (2048, 4096, 8192, 16384)
+TILE_SWEEP_CALLS = 12
+
+
+def tile_sweep(k_values):
+    """The workload of --summarize-tile-sweep: TILE_SWEEP_CALLS calls of the
+    FFN shard (t = 1, bf16 out) per [tokens, ffn] of TILE_SWEEP and hidden in
+    k_values, in that order, on device-seeded inputs."""
+    import torch
+    from attention_shards_amd import binding as B
+    g = torch.Generator(device="cuda").manual_seed(5)
+    for tok, fs in TILE_SWEEP:
+        for h in k_values:
+            X = torch.randn(tok, h, device="cuda", generator=g).to(torch.bfloat16)
+            W1 = (torch.randn(h, fs, device="cuda", generator=g) * 0.02).to(torch.bfloat16)
+            W2 = (torch.randn(fs, h, device="cuda", generator=g) * 0.02).to(torch.bfloat16)
+            Y = torch.empty(tok, h, device="cuda", dtype=torch.bfloat16)
+            ws = torch.empty(max(16, B.tp_ffn_shard_workspace_bytes(tok, h, fs, 1, B.TP_BF16)),
+                             dtype=torch.uint8, device="cuda")
+            for _ in range(TILE_SWEEP_CALLS):
+                B.tp_ffn_shard(X, W1, W2, Y, 0, 1, workspace=ws)
+            torch.cuda.synchronize()
+            print(f"tile sweep: tokens {tok}, ffn {fs}, hidden {h}", file=sys.stderr, flush=True)
+            del X, W1, W2, Y, ws
+
+
+def _gelu_groups(rows, n_groups):
+    """The first-product (GeLU epilogue) dispatches of a tile-sweep run, in
+    order, cut into n_groups groups of TILE_SWEEP_CALLS (one per shape)."""
+    g1 = [r for r in rows if "EpiGelu" in r["Kernel_Name"]]
+    if len(g1) != n_groups * TILE_SWEEP_CALLS:
+        raise SystemExit(f"expected {n_groups * TILE_SWEEP_CALLS} first-product dispatches, "
+                         f"found {len(g1)}")
+    return [g1[k * TILE_SWEEP_CALLS:(k + 1) * TILE_SWEEP_CALLS] for k in range(n_groups)]
+
+
+def summarize_tile_sweep(trace_csv, counter_csv, cmd_trace, cmd_pmc):
+    """profiles/gemm_tile_kinds_one_tile_per_cu.md from a kernel trace of
+    --tile-sweep (all K) and a --pmc run of --tile-sweep --tile-sweep-k 16384:
+    per tile kind, the first product's median time at each K, a straight-line
+    fit time = fixed + K x per-K (the per-tile costs that do not grow with K,
+    and the steady rate of the main loop), and, at K = 16384, the per-CU
+    vector-memory counters (TA/TD busy, TA stalled by the L1, mean L2 read
+    latency) with the matrix pipes' busy fraction at the measured clock."""
     import csv
-    per = {}
-    for r in csv.DictReader(open(counter_csv)):
-        d = per.setdefault(r["Dispatch_Id"], {"name": _short(r["Kernel_Name"]),
-                                              "wg": int(r["Grid_Size"]) // int(r["Workgroup_Size"])})
-        d[r["Counter_Name"]] = d.get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
-    groups = {}
-    for d in per.values():
-        if d["name"].startswith("at::") or "copyBuffer" in d["name"]:
-            continue
-        groups.setdefault((d["name"], d["wg"]), []).append(d)
-    lines = ["# MFMA utilisation and LDS bank conflicts per kernel (FFN step and attention shard)",
-             "", "Command (from the repository root, on one MI355X):", "", "```", cmd, "```", "",
-             "`MfmaUtil` is rocprofv3's derived metric: the summed per-SIMD "
-             "`SQ_VALU_MFMA_BUSY_CYCLES` over `GRBM_GUI_ACTIVE` times the SIMD count, in "
-             "percent (the GPU-busy cycles count at the reference clock, so it is close to the "
-             "fraction of the nominal MFMA peak). Conflicts: `SQ_LDS_BANK_CONFLICT` cycles per "
-             "`SQ_INSTS_LDS` instruction. Means over the run's dispatches of each kernel and "
-             "grid size.", "",
-             "| kernel | workgroups | dispatches | MfmaUtil % | LDS conflict cycles / LDS instr |",
-             "|---|---:|---:|---:|---:|"]
-    for (name, wg), ds in sorted(groups.items(), key=lambda kv: -sum(x.get("GRBM_GUI_ACTIVE", 0)
-                                                                      for x in kv[1])):
-        mu = sum(x.get("MfmaUtil", 0.0) for x in ds) / len(ds)
-        conf = sum(x.get("SQ_LDS_BANK_CONFLICT", 0.0) for x in ds)
-        insts = sum(x.get("SQ_INSTS_LDS", 0.0) for x in ds)
-        lines.append(f"| `{name}` | {wg} | {len(ds)} | {mu:.1f} | "
-                     f"{(conf / insts if insts else 0.0):.3f} |")
-    with open(os.path.join(ROOT, "profiles", "counters_mfma_lds_ffn_attn.md"), "w") as f:
+    import numpy as np
+    rows = sorted(csv.DictReader(open(trace_csv)), key=lambda r: int(r["Start_Timestamp"]))
+    groups = _gelu_groups(rows, len(TILE_SWEEP) * len(TILE_SWEEP_K))
+    dur = lambda r: (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3  # us
+    ncu = 256
+    lines = ["# First product of one-tile-per-CU FFN shards: fixed and steady cost per tile "
+             "kind, per-CU memory-path counters", "",
+             "Commands (from the repository root, on one MI355X): the kernel trace", "", "```",
+             cmd_trace, "```", "", "and the counters (K = 16384 only):", "", "```", cmd_pmc,
+             "```", "",
+             "Each shape is the FFN shard at t = 1 ([tokens, hidden] x [hidden, ffn], GeLU "
+             "epilogue, bf16 out); its tile plan is one kind with one tile per CU (256 tiles). "
+             "Times: median of the last 10 of 12 dispatches of the first product. The fit "
+             "time = fixed + per-K x K over K = 2048..16384 separates what each tile pays "
+             "once (launch, first loads, the epilogue) from the main loop's steady rate.", "",
+             "| tile (A operand) | tokens x ffn | " +
+             " | ".join(f"K={k} us" for k in TILE_SWEEP_K) + " | fixed us | steady TFLOP/s |",
+             "|---|---|" + "---:|" * (len(TILE_SWEEP_K) + 2)]
+    kinds = {}
+    for s_i, (tok, fs) in enumerate(TILE_SWEEP):
+        ts = []
+        for k_i, K in enumerate(TILE_SWEEP_K):
+            grp = groups[s_i * len(TILE_SWEEP_K) + k_i]
+            ts.append(statistics.median(dur(r) for r in grp[2:]))
+        kind = _short(groups[s_i * len(TILE_SWEEP_K)][0]["Kernel_Name"])
+        tile = "x".join(kind.split("<")[1].split(",")[:2]).replace(" ", "")
+        a_op = "K-blocked" if kind.rstrip(">").split(",")[-2].strip() == "true" else "row-major"
+        kinds[(tok, fs)] = (tile, a_op)
+        slope, fixed = np.polyfit(np.array(TILE_SWEEP_K, float), np.array(ts), 1)
+        steady = 2 * tok * fs / (slope * 1e-6) / 1e12
+        lines.append(f"| {tile} ({a_op}) | {tok} x {fs} | " + " | ".join(f"{t:.1f}" for t in ts) +
+                     f" | {fixed:.1f} | {steady:.0f} |")
+    if counter_csv:
+        per, names, grids = _read_counters(counter_csv)
+        ids = sorted(per, key=int)
+        cgroups = _gelu_groups([{"Kernel_Name": names[d], "id": d} for d in ids], len(TILE_SWEEP))
+        lines += ["", "Counters at K = 16384 (mean of the last 10 of 12 dispatches; per CU = the "
+                  "summed counter / 256 CUs; cycles = `GRBM_GUI_ACTIVE` / 8 XCDs). TA: the "
+                  "texture addresser, which takes every vector-memory instruction's addresses "
+                  "(a 1 KiB buffer load to LDS needs at least 16 of its cycles at 64 B/clk); "
+                  "TD: the data return path that writes the loads into LDS; the L1's misses go "
+                  "to L2 with the latency shown. Bytes per CU-cycle: the tile's operands "
+                  "(K x (rows + columns) x 2 B) over the cycles.", "",
+                  "| tile (A operand) | tokens x ffn | clock GHz | operand B/CU-cycle | TA busy | "
+                  "TA stalled by L1 | TD busy | mean L2 read latency (cycles) | MFMA busy at clock |",
+                  "|---|---|---:|---:|---:|---:|---:|---:|---:|"]
+        trace_k = {(tok, fs): statistics.median(
+            dur(r) for r in groups[s_i * len(TILE_SWEEP_K) + len(TILE_SWEEP_K) - 1][2:])
+            for s_i, (tok, fs) in enumerate(TILE_SWEEP)}
+        for s_i, (tok, fs) in enumerate(TILE_SWEEP):
+            ds = [per[r["id"]] for r in cgroups[s_i][2:]]
+            m = lambda c: sum(d.get(c, 0.0) for d in ds) / len(ds)
+            cyc = m("GRBM_GUI_ACTIVE") / 8
+            tile, a_op = kinds[(tok, fs)]
+            bm, bn = (int(x) for x in tile.split("x"))
+            clk = cyc / (trace_k[(tok, fs)] * 1e-6) / 1e9
+            opb = TILE_SWEEP_K[-1] * (bm + bn) * 2 / cyc
+            lat = m("TCP_TCC_READ_REQ_LATENCY_sum") / max(1.0, m("TCP_TCC_READ_REQ_sum"))
+            lines.append(f"| {tile} ({a_op}) | {tok} x {fs} | {clk:.2f} | {opb:.1f} | "
+                         f"{m('TA_TA_BUSY_sum') / ncu / cyc:.0%} | "
+                         f"{m('TA_ADDR_STALLED_BY_TC_CYCLES_sum') / ncu / cyc:.0%} | "
+                         f"{m('TD_TD_BUSY_sum') / ncu / cyc:.0%} | {lat:.0f} | "
+                         f"{m('SQ_VALU_MFMA_BUSY_CYCLES') / (4 * ncu) / cyc:.0%} |")
+    lines += ["", f"GEMM source hash: `{src_hash('gemm.hip')}`"]
+    with open(os.path.join(ROOT, "profiles", "gemm_tile_kinds_one_tile_per_cu.md"), "w") as f:
         f.write("\n".join(lines) + "\n")
-    print(f"wrote profiles/counters_mfma_lds_ffn_attn.md ({len(per)} dispatches)")
+    print("wrote profiles/gemm_tile_kinds_one_tile_per_cu.md")
 
 
 def summarize_clock_counters(csvs, cmd):
@@ -909,7 +989,10 @@ def main():
                     help="also write the sweep records to this file")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run a 1 GiB device copy first (counter calibration)")
-    ap.add_argument("--summarize-counters", metavar="COUNTER_CSV", default=None)
+    ap.add_argument("--tile-sweep", action="store_true",
+                    help="run the one-tile-per-CU first-product workload only (profiling runs)")
+    ap.add_argument("--tile-sweep-k", type=int, nargs="+", default=list(TILE_SWEEP_K))
+    ap.add_argument("--summarize-tile-sweep", nargs=2, metavar=("TRACE_CSV", "COUNTER_CSV"))
     ap.add_argument("--summarize-attn-profile", metavar="KERNEL_TRACE_CSV", default=None)
     ap.add_argument("--summarize-sweep", metavar="SWEEP_JSONL", default=None)
     ap.add_argument("--summarize-profiles", nargs=3, metavar=("TRACE_CSV", "FETCH_CSV", "WRITE_CSV"))
@@ -918,8 +1001,8 @@ def main():
     ap.add_argument("--profile-commands", nargs=2, default=["", ""],
                     metavar=("STATS_CMD", "PMC_CMD"))
     args = ap.parse_args()
-    if args.summarize_counters:
-        summarize_counters(args.summarize_counters, args.profile_commands[0])
+    if args.summarize_tile_sweep:
+        summarize_tile_sweep(*args.summarize_tile_sweep, *args.profile_commands)
         return
     if args.summarize_attn_profile:
         summarize_attn_profile(args.summarize_attn_profile, args.profile_commands[0])
@@ -964,6 +1047,9 @@ def main():
         return
     if args.step_only:
         log(json.dumps(ffn_step_row(K, W, fused=False)[0]))
+        return
+    if args.tile_sweep:
+        tile_sweep(args.tile_sweep_k)
         return
 
     # ---------------- headline: the sweep's hidden-22528, t=1 FFN shard ----------------
