@@ -28,11 +28,14 @@ The same run times, under "rows":
   * partial_reduce_t8_h4096 / partial_reduce_t4_h12288: the reduce alone at
     those two shapes with the calls rotating over 3 buffer sets of 369 MB /
     1.41 GB each (more than the 256 MB Infinity Cache), so it reads HBM;
+    per-call event times (median, min) and, for "gbs", the time per call of
+    back-to-back calls between one pair of events (a 60 us kernel between
+    its own events also carries the events' overhead);
   * partial_reduce_slice: one row block of the t=8 reduce (the
     reduce-scatter half), blocks rotating;
   * sp_reduce_layernorm_t4_h12288: the sequence-parallel sum + LayerNorm
     (4 bf16 partials + residual, fp32 x, bf16 LayerNorm out) over all rows
-    of [8192, 12288], rotating over 3 buffer sets;
+    of [8192, 12288], rotating over 3 buffer sets, timed like the reduce;
   * ffn_shard_reduce_fused: the t=8 step with the sum fused into the second
     GEMM's epilogue, and the same comparison at the t=4 hidden-12288 shape;
   * attn_shard: the attention shard (t=8, 8 of 64 heads of 128, hidden
@@ -307,14 +310,17 @@ def reduce_rotated(t, rows, cols, steps, warmup, nsets=3):
         B.tp_partial_reduce(parts, R, out)
 
     ms = time_calls(call, steps, warmup)
+    batched = time_batched(call, steps, warmup)
     by = reduce_bytes(t, rows, cols)
     med = statistics.median(ms)
     del sets
     torch.cuda.empty_cache()
     return {"t": t, "rows": rows, "cols": cols, "dtypes": "bf16 partials, bf16 residual, fp32 out",
             "buffer_sets": nsets, "bytes_per_set": by, **stats(ms), "bytes": by,
-            "gbs": round(by / (med * 1e-3) / 1e9, 1),
-            "frac_hbm_peak": round(by / (med * 1e-3) / 1e9 / PEAK_HBM_GBS, 4), "bound": "hbm"}
+            "batched_ms": round(batched, 5),
+            "gbs": round(by / (batched * 1e-3) / 1e9, 1),
+            "frac_hbm_peak": round(by / (batched * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+            "gbs_per_call_events": round(by / (med * 1e-3) / 1e9, 1), "bound": "hbm"}
 
 
 def sp_layernorm_rotated(t, rows, cols, steps, warmup, nsets=3):
@@ -341,15 +347,17 @@ def sp_layernorm_rotated(t, rows, cols, steps, warmup, nsets=3):
         B.tp_sp_reduce_layernorm(parts, R, x, y, gamma, beta, 1e-5)
 
     ms = time_calls(call, steps, warmup)
+    batched = time_batched(call, steps, warmup)
     by = (t * 2 + 2 + 4 + 2) * rows * cols
     med = statistics.median(ms)
     del sets
     torch.cuda.empty_cache()
     return {"t": t, "rows": rows, "cols": cols,
             "dtypes": "bf16 partials, bf16 residual, fp32 x, bf16 LayerNorm out",
-            "buffer_sets": nsets, **stats(ms), "bytes": by,
-            "gbs": round(by / (med * 1e-3) / 1e9, 1),
-            "frac_hbm_peak": round(by / (med * 1e-3) / 1e9 / PEAK_HBM_GBS, 4), "bound": "hbm"}
+            "buffer_sets": nsets, **stats(ms), "bytes": by, "batched_ms": round(batched, 5),
+            "gbs": round(by / (batched * 1e-3) / 1e9, 1),
+            "frac_hbm_peak": round(by / (batched * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+            "gbs_per_call_events": round(by / (med * 1e-3) / 1e9, 1), "bound": "hbm"}
 
 
 def ffn_step_row(steps, warmup, fused=True):
