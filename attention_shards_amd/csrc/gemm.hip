@@ -23,7 +23,9 @@
 //     fragment reads per MFMA of a 128x64 block.  256x128, 128x192 and
 //     128x128 tiles: K = 64 per stage through a 3-slot ring.  (128x192
 //     fills all 256 CUs where 256x128 would leave a quarter idle, e.g.
-//     2048 x 3072 outputs.)
+//     2048 x 3072 outputs.)  The K = 32 kinds over a row-major A keep A in
+//     two slots of 128-byte rows, each the K columns of two stages, beside a
+//     4-slot B ring, so that A's DMAs read whole lines of its rows.
 //   * Workgroup ids are remapped so each XCD (dispatch is round-robin over
 //     the 8 XCDs) receives a contiguous run of tiles, ordered in groups of 8
 //     tile-rows so neighbouring tiles share A and B panels in that XCD's L2.
@@ -485,7 +487,14 @@ __device__ __forceinline__ void epilogue_lds(uint8_t* smem, f32x16 (&acc)[FM][FN
 // K-blocked, [2 ceil(K/BK)][lda][BK], A_2's blocks after A_1's: every stage
 // brings the two A tiles and one B tile, and both products use the same B
 // fragments (half the B traffic of two passes over K).
-template <int BM, int BN, int WM, int WN, int KS, int NSL, class Epi, bool AKB, int NA = 1>
+// AP (A pairs; KS = 2, row-major A, NSL = 4): A goes into two slots of
+// 128-byte rows, each holding the K columns of two consecutive stages, so
+// every A DMA reads whole 128-byte lines of A's rows (a stage's 64-byte row
+// pieces would cost a half-used line each); B keeps its ring of NSL
+// stages.  Even steps load the A pair of the stages two and three ahead
+// with their B, odd steps B alone.
+template <int BM, int BN, int WM, int WN, int KS, int NSL, class Epi, bool AKB, int NA = 1,
+          bool AP = false>
 __global__ void __launch_bounds__(WM * WN * 64)
 gemm_bf16_kernel(const uint16_t* __restrict__ A, int64_t lda,
                  const uint16_t* __restrict__ B, int64_t ldb, int M, int N,
@@ -497,34 +506,36 @@ gemm_bf16_kernel(const uint16_t* __restrict__ A, int64_t lda,
   static_assert(KS == 2 || KS == 4, "k-steps per stage");
   static_assert(NSL >= 3 && NSL <= 6, "ring slots");
   static_assert(NA == 1 || (NA == 2 && AKB), "paired A operands are K-blocked");
+  static_assert(!AP || (KS == 2 && !AKB && NA == 1 && NSL == 4), "A pairs: the layout below");
   constexpr int BK = 16 * KS;
   constexpr int NW = WM * WN;
   constexpr int FM = BM / WM / 32;
   constexpr int FN = BN / WN / 32;
-  constexpr int A_ROWB = BK * 2;           // A rows in LDS: 64 or 128 bytes
+  constexpr int A_ROWB = AP ? 128 : BK * 2;  // A rows in LDS: 64 or 128 bytes
   constexpr int CPR = A_ROWB / 16;         // 16-byte chunks per A row (4 or 8)
   constexpr int RPD = 64 / CPR;            // A rows per 1 KiB DMA
   constexpr int ASH = CPR == 4 ? 2 : 1;    // A swizzle: chunk ^ ((row >> ASH) & (CPR-1))
   constexpr int B_ROWB = BN * 2;           // B rows in LDS: natural [k][n]
   constexpr int B_CH = B_ROWB / 16;        // 16-byte chunks per B row
-  constexpr int A_STAGE = BM * A_ROWB;
+  constexpr int A_STAGE = BM * A_ROWB;        // one A slot (AP: a pair of stages)
   constexpr int B_STAGE = BK * B_ROWB;
-  constexpr int A_DMA = A_STAGE / 1024 / NW;  // 1 KiB DMAs per wave per stage
+  constexpr int A_DMA = A_STAGE / 1024 / NW;  // 1 KiB DMAs per wave per A slot
   constexpr int B_DMA = B_STAGE / 1024 / NW;
-  constexpr int NDMA = NA * A_DMA + B_DMA;
+  constexpr int NDMA = NA * A_DMA + B_DMA;     // AP: even steps; odd steps B_DMA
+  constexpr int A_SLOTS = AP ? 2 : NSL;
   static_assert(A_DMA * 1024 * NW == A_STAGE && B_DMA * 1024 * NW == B_STAGE, "DMA split");
   static_assert(B_CH % 16 == 0 || B_CH == 24, "B swizzle: 256-byte multiple or 384-byte rows");
   static_assert(FM >= 1 && FN >= 1, "wave tile");
 
-  // LDS ring: slot s holds A operand o at (s*NA + o)*A_STAGE and B at
-  // NSL*NA*A_STAGE + s*B_STAGE.  The same memory later stages the epilogue
-  // (NW regions of 32 x (BN/WN+4)).
-  constexpr int PIPE_BYTES = NSL * (NA * A_STAGE + B_STAGE);
+  // LDS ring: slot s holds A operand o at (s*NA + o)*A_STAGE (AP: pair slot
+  // s at s*A_STAGE) and B at A_SLOTS*NA*A_STAGE + s*B_STAGE.  The same memory
+  // later stages the epilogue (NW regions of 32 x (BN/WN+4)).
+  constexpr int PIPE_BYTES = A_SLOTS * NA * A_STAGE + NSL * B_STAGE;
   constexpr int EPI_BYTES = NW * 32 * (BN / WN + 4) * 4;
   __shared__ __attribute__((aligned(16))) uint8_t
       smem[PIPE_BYTES > EPI_BYTES ? PIPE_BYTES : EPI_BYTES];
   uint8_t* const lds_a = smem;
-  uint8_t* const lds_b = smem + NSL * NA * A_STAGE;
+  uint8_t* const lds_b = smem + A_SLOTS * NA * A_STAGE;
   const uint32_t lds_a_addr = (uint32_t)(uintptr_t)(lds_u8*)lds_a;
   const uint32_t lds_b_addr = (uint32_t)(uintptr_t)(lds_u8*)lds_b;
 
@@ -569,6 +580,16 @@ gemm_bf16_kernel(const uint16_t* __restrict__ A, int64_t lda,
 
   // K blocks of each A operand (A_2's blocks start after A_1's)
   const int a_blocks = (K + BK - 1) / BK;
+  // AP: the A DMA number ja (0 <= ja < A_DMA) of pair p (K columns 64p ..
+  // 64p+63) into pair slot PS.
+  auto dma_a_pair = [&](int p, auto PS, int ja) {
+    constexpr int ps = decltype(PS)::value;
+    const int k0 = p * 2 * BK;
+    const __amdgpu_buffer_rsrc_t ra =
+        make_rsrc(A + (int64_t)m0 * lda + k0, (int64_t)rows_valid * lda * 2 - (int64_t)k0 * 2);
+    const int off = (k0 + a_col[ja] < K) ? a_off[ja] : OOB;
+    dma16(ra, off, lds_a_addr + ps * A_STAGE + (ja * NW + wave) * 1024);
+  };
   // DMA number j (0 <= j < NDMA) of stage kt into ring slot SLOT.
   auto dma = [&](int kt, auto SLOT, int j) {
     constexpr int slot = decltype(SLOT)::value;
@@ -591,13 +612,17 @@ gemm_bf16_kernel(const uint16_t* __restrict__ A, int64_t lda,
   };
 
   // ---- fragment read addresses (byte offsets inside a slot).
-  // A (ds_read_b128): row wr0 + mi*32 + (lane&31), chunk 2ks + (lane>>5).
-  int a_rd[KS];
+  // A (ds_read_b128): row wr0 + mi*32 + (lane&31), chunk 2ks + (lane>>5)
+  // (AP: of half h of the pair slot, chunk 2(h KS + ks) + (lane>>5)).
+  constexpr int AH = AP ? 2 : 1;
+  int a_rd[AH][KS];
 #pragma unroll
-  for (int ks = 0; ks < KS; ++ks) {
-    const int c = (2 * ks + (lane >> 5)) ^ (((lane & 31) >> ASH) & (CPR - 1));
-    a_rd[ks] = (wr0 + (lane & 31)) * A_ROWB + c * 16;
-  }
+  for (int h = 0; h < AH; ++h)
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      const int c = (2 * (h * KS + ks) + (lane >> 5)) ^ (((lane & 31) >> ASH) & (CPR - 1));
+      a_rd[h][ks] = (wr0 + (lane & 31)) * A_ROWB + c * 16;
+    }
   // B (ds_read_b64_tr_b16): in each 16-lane group G, input lane r points at
   // row 8*(G>>1) + r/4 and columns 16*(G&1) + 4*(r&3) of the wave's 32-column
   // block; the transposed read leaves lane l holding column l%32 with
@@ -635,10 +660,15 @@ gemm_bf16_kernel(const uint16_t* __restrict__ A, int64_t lda,
       const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
           (__attribute__((address_space(3))) s16x4*)(lb + 4 * B_ROWB));
       fb[fset][q] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+    } else if constexpr (AP) {
+      // stage kt in B slot kt % 4: A pair slot (kt / 2) % 2, half kt % 2
+      const int mi = q - FN;
+      fa[fset][0][mi] = *reinterpret_cast<const bf16x8*>(
+          lds_a + ((slot >> 1) & 1) * A_STAGE + a_rd[slot & 1][ks] + mi * 32 * A_ROWB);
     } else {
       const int op = (q - FN) / FM, mi = (q - FN) - op * FM;
       fa[fset][op][mi] = *reinterpret_cast<const bf16x8*>(
-          lds_a + (slot * NA + op) * A_STAGE + a_rd[ks] + mi * 32 * A_ROWB);
+          lds_a + (slot * NA + op) * A_STAGE + a_rd[0][ks] + mi * 32 * A_ROWB);
     }
   };
   // one MFMA of a k-step, idx in [0, NA*FM*FN): operand by operand, so an
@@ -673,11 +703,18 @@ gemm_bf16_kernel(const uint16_t* __restrict__ A, int64_t lda,
   constexpr int NRU = NA * FM + FN;  // fragment read units per k-step
   constexpr int DSLOTS = (KS - 1) * NMF;
   static_assert(NDMA <= DSLOTS && NRU <= NMF, "traffic fits between the MFMAs");
-  // MFMA slot after which DMA d of a step is issued
-  auto dma_slot = [](int d) { return KS == 2 ? NMF - NDMA + d : d * DSLOTS / NDMA; };
+  // AP: step kt (kt % 4 == u) issues, on even u, the A pair kt/2 + 1 (the
+  // stages two and three ahead) into pair slot (kt/2 + 1) % 2, then B of
+  // stage kt+3; on odd u, B alone.  Stage kt+1 then needs the B issued three
+  // steps back and the A pair issued at the last even step, so the loads
+  // that may stay in flight are those of step kt-1 after its A pair (B) and
+  // of step kt (odd u), or those after step kt-2's B (even u).
   auto step = [&](int kt, auto U) __attribute__((always_inline)) {
     constexpr int u = decltype(U)::value;
     constexpr int nxt = (u + NSL - 1) % NSL;
+    constexpr int nd = AP ? ((u & 1) ? B_DMA : A_DMA + B_DMA) : NDMA;  // DMAs this step
+    // MFMA slot after which DMA d of the step is issued
+    auto dma_slot = [](int d) { return KS == 2 ? NMF - nd + d : d * DSLOTS / nd; };
 #pragma unroll
     for (int ksi = 0; ksi < KS - 1; ++ksi) {
 #pragma unroll
@@ -686,12 +723,24 @@ gemm_bf16_kernel(const uint16_t* __restrict__ A, int64_t lda,
         __builtin_amdgcn_sched_barrier(0);
         if (j < NRU) read_unit(IC<u>{}, ksi + 1, (ksi + 1) & 1, j);
 #pragma unroll
-        for (int d = 0; d < NDMA; ++d)
-          if (dma_slot(d) == ksi * NMF + j) dma(kt + NSL - 1, IC<nxt>{}, d);
+        for (int d = 0; d < nd; ++d)
+          if (dma_slot(d) == ksi * NMF + j) {
+            if constexpr (AP) {
+              if (!(u & 1) && d < A_DMA)
+                dma_a_pair(kt / 2 + 1, IC<((u >> 1) + 1) & 1>{}, d);
+              else
+                dma(kt + NSL - 1, IC<nxt>{}, NA * A_DMA + d - ((u & 1) ? 0 : A_DMA));
+            } else {
+              dma(kt + NSL - 1, IC<nxt>{}, d);
+            }
+          }
         __builtin_amdgcn_sched_barrier(0);
       }
     }
-    wait_vmcnt<(NSL - 2) * NDMA>();
+    if constexpr (AP)
+      wait_vmcnt<(u & 1) ? 2 * B_DMA : A_DMA + 2 * B_DMA>();
+    else
+      wait_vmcnt<(NSL - 2) * NDMA>();
     wait_lgkmcnt0();
     stage_barrier();
 #pragma unroll
@@ -703,12 +752,26 @@ gemm_bf16_kernel(const uint16_t* __restrict__ A, int64_t lda,
     }
   };
 
-  // Prologue: stages 0..NSL-2 in flight, wait for stage 0.
-  static_for<0, NSL - 1>([&](auto S) __attribute__((always_inline)) {
+  // Prologue: stages 0..NSL-2 in flight, wait for stage 0.  AP: the loads
+  // steps -3, -2, -1 would have issued (B of stage 0; A pair 0 and B of
+  // stage 1; B of stage 2), then wait for A pair 0 and B of stage 0.
+  if constexpr (AP) {
 #pragma unroll
-    for (int j = 0; j < NDMA; ++j) dma(decltype(S)::value, S, j);
-  });
-  wait_vmcnt<(NSL - 2) * NDMA>();
+    for (int j = 0; j < B_DMA; ++j) dma(0, IC<0>{}, NA * A_DMA + j);
+#pragma unroll
+    for (int j = 0; j < A_DMA; ++j) dma_a_pair(0, IC<0>{}, j);
+#pragma unroll
+    for (int j = 0; j < B_DMA; ++j) dma(1, IC<1>{}, NA * A_DMA + j);
+#pragma unroll
+    for (int j = 0; j < B_DMA; ++j) dma(2, IC<2>{}, NA * A_DMA + j);
+    wait_vmcnt<2 * B_DMA>();
+  } else {
+    static_for<0, NSL - 1>([&](auto S) __attribute__((always_inline)) {
+#pragma unroll
+      for (int j = 0; j < NDMA; ++j) dma(decltype(S)::value, S, j);
+    });
+    wait_vmcnt<(NSL - 2) * NDMA>();
+  }
   stage_barrier();
 #pragma unroll
   for (int q = 0; q < NRU; ++q) read_unit(IC<0>{}, 0, 0, q);
@@ -796,11 +859,12 @@ Plan plan_bf16(int M, int N) {
   return best;
 }
 
-template <int BM, int BN, int WM, int WN, int KS, int NSL, bool AKB, class Epi, int NA = 1>
+template <int BM, int BN, int WM, int WN, int KS, int NSL, bool AKB, class Epi, int NA = 1,
+          bool AP = false>
 hipError_t launch_bf16(const uint16_t* A, int64_t lda, const uint16_t* B, int64_t ldb, int M,
                        int N, int K, const Epi& epi, hipStream_t s, int n_base = 0) {
   const int tm = (M + BM - 1) / BM, tn = (N - n_base + BN - 1) / BN;
-  hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, WM, WN, KS, NSL, Epi, AKB, NA>), dim3(tm * tn),
+  hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, WM, WN, KS, NSL, Epi, AKB, NA, AP>), dim3(tm * tn),
                      dim3(WM * WN * 64), 0, s, A, lda, B, ldb, M, N, K, tm, tn, n_base, epi);
   return hipGetLastError();
 }
@@ -809,9 +873,21 @@ hipError_t launch_bf16(const uint16_t* A, int64_t lda, const uint16_t* B, int64_
 template <bool AKB, class Epi>
 hipError_t launch_kind(int k, const uint16_t* A, int64_t lda, const uint16_t* B, int64_t ldb,
                        int M, int n_base, int n_end, int K, const Epi& epi, hipStream_t s) {
+  // K = 32 stages over a row-major A read it through A pairs (whole 128-byte
+  // lines of its rows)
   switch (k) {
-    case 0: return launch_bf16<256, 256, 2, 2, 2, 5, AKB>(A, lda, B, ldb, M, n_end, K, epi, s, n_base);
-    case 1: return launch_bf16<256, 192, 2, 2, 2, 5, AKB>(A, lda, B, ldb, M, n_end, K, epi, s, n_base);
+    case 0:
+      if constexpr (AKB)
+        return launch_bf16<256, 256, 2, 2, 2, 5, AKB>(A, lda, B, ldb, M, n_end, K, epi, s, n_base);
+      else
+        return launch_bf16<256, 256, 2, 2, 2, 4, AKB, Epi, 1, true>(A, lda, B, ldb, M, n_end, K,
+                                                                   epi, s, n_base);
+    case 1:
+      if constexpr (AKB)
+        return launch_bf16<256, 192, 2, 2, 2, 5, AKB>(A, lda, B, ldb, M, n_end, K, epi, s, n_base);
+      else
+        return launch_bf16<256, 192, 2, 2, 2, 4, AKB, Epi, 1, true>(A, lda, B, ldb, M, n_end, K,
+                                                                   epi, s, n_base);
     case 2: return launch_bf16<256, 128, 2, 2, 4, 3, AKB>(A, lda, B, ldb, M, n_end, K, epi, s, n_base);
     case 3: return launch_bf16<128, 192, 2, 2, 4, 3, AKB>(A, lda, B, ldb, M, n_end, K, epi, s, n_base);
     default: return launch_bf16<128, 128, 2, 2, 4, 3, AKB>(A, lda, B, ldb, M, n_end, K, epi, s, n_base);

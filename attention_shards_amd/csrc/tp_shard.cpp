@@ -75,10 +75,13 @@ constexpr int64_t kMaxSeqPad = int64_t(1) << 23;
 constexpr int64_t kZBlock = 64;
 // For shards of at least this many ffn columns GEMM1 reads X K-blocked too
 // (a copy of X in the workspace, [ceil(h/kb)][tokens][kb]): every stage's A
-// tile is then one contiguous run instead of 64-byte pieces of 256 rows.
-// The copy moves 4 tokens h bytes; the product's main loop gains about 9%
-// per stage, which pays for it once ffn/t is a few thousand columns.
-constexpr int64_t kXBlockMinCols = 8192;
+// tile is then one contiguous run instead of 128-byte pieces of 256 rows.
+// The copy moves 4 tokens h bytes, the main loop gains 2-3% over reading X
+// row-major (same-box first products: 6302 vs 6520 us at 2048 x 22528 x
+// 90112, 422 vs 431 us at 2048 x 16384 x 8192, 1898 vs 1904 us at 8192 x
+// 12288 x 12288; the copies 30, 23, 60 us), which pays for the copy from
+// about 20 000 columns on.
+constexpr int64_t kXBlockMinCols = 20480;
 
 // Bytes of the K-blocked copy of X (0 when GEMM1 reads X as given).
 int64_t x_kblock_bytes(int64_t tokens, int64_t hidden, int64_t fs, int32_t in_dtype) {

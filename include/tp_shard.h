@@ -99,7 +99,7 @@ typedef enum {
  *                                   bf16 in an internal K-blocked layout
  *                                   (tokens x ffn/t rounded up to 64 columns),
  *                                   fp32 row-major; with bf16 inputs and
- *                                   ffn/t >= 8192 also a K-blocked copy of X
+ *                                   ffn/t >= 20480 also a K-blocked copy of X
  *                                   (tokens x hidden rounded up to 64 columns)
  *                                   that the first GEMM reads; contents are not
  *                                   part of the interface

@@ -70,14 +70,14 @@ def test_workspace_queries(lib):
     assert lib.tp_ffn_shard_workspace_bytes(3, 8, 24, 3, B.TP_BF16) == 512
     assert lib.tp_ffn_shard_workspace_bytes(2000, 3000, 2936, 1, B.TP_BF16) == 2000 * 2944 * 2
     assert lib.tp_ffn_shard_workspace_bytes(3, 8, 24, 3, B.TP_F32) == 256    # fp32: row-major
-    # bf16 shards of at least 8192 ffn columns also hold X K-blocked (hidden
+    # bf16 shards of at least 20480 ffn columns also hold X K-blocked (hidden
     # rounded up to 64 columns): 2048 x 22528 x 2 after GeLU(Z) of 2048 x 90112
     assert lib.tp_ffn_shard_workspace_bytes(2048, 22528, 90112, 1, B.TP_BF16) == \
         2048 * 90112 * 2 + 2048 * 22528 * 2
-    assert lib.tp_ffn_shard_workspace_bytes(100, 1000, 8192, 1, B.TP_BF16) == \
-        (100 * 8192 * 2 + 255) // 256 * 256 + (100 * 1024 * 2 + 255) // 256 * 256
-    assert lib.tp_ffn_shard_workspace_bytes(100, 1000, 8184 * 2, 2, B.TP_BF16) == \
-        (100 * 8192 * 2 + 255) // 256 * 256                      # 8184 < 8192 columns
+    assert lib.tp_ffn_shard_workspace_bytes(100, 1000, 20480, 1, B.TP_BF16) == \
+        (100 * 20480 * 2 + 255) // 256 * 256 + (100 * 1024 * 2 + 255) // 256 * 256
+    assert lib.tp_ffn_shard_workspace_bytes(100, 1000, 20472 * 2, 2, B.TP_BF16) == \
+        (100 * 20480 * 2 + 255) // 256 * 256                     # 20472 < 20480 columns
     assert lib.tp_ffn_shard_workspace_bytes(10, 8, 20, 3, B.TP_BF16) == 0    # t does not divide f
     assert lib.tp_ffn_shard_workspace_bytes(10, 8, 16, 0, B.TP_BF16) == 0
     # attention: 4 x [heads, seq_pad, 128] (Q, K, V^T hi, V^T lo) + O hi/lo [tokens, 2*nl*128], 16-bit,
@@ -367,12 +367,15 @@ def test_ffn_noalloc_limit_matches_header(lib):
     m = re.search(r"#define TP_FFN_NOALLOC_MAX_WORKSPACE \(\(size_t\)(\d+) << (\d+)\)",
                   header_text())
     assert int(m.group(1)) << int(m.group(2)) == B.TP_FFN_NOALLOC_MAX_WORKSPACE
-    # 4096 tokens x 8128 bf16 columns fit; 2048 x 16384 (64 MiB of GeLU(Z)
-    # plus the K-blocked copy of X) do not
-    assert lib.tp_ffn_shard_workspace_bytes(4096, 64, 8128, 1, B.TP_BF16) <= \
+    # 2048 tokens x 16384 bf16 columns of GeLU(Z) fill the 64 MiB exactly;
+    # 2048 x 16448 do not fit, nor do 1024 x 22528 (44 MiB of GeLU(Z) plus
+    # the K-blocked copy of 1024 x 16384 X, 32 MiB)
+    assert lib.tp_ffn_shard_workspace_bytes(2048, 64, 16384, 1, B.TP_BF16) == \
         B.TP_FFN_NOALLOC_MAX_WORKSPACE
-    assert lib.tp_ffn_shard_workspace_bytes(2048, 64, 16384, 1, B.TP_BF16) > \
+    assert lib.tp_ffn_shard_workspace_bytes(2048, 64, 16448, 1, B.TP_BF16) > \
         B.TP_FFN_NOALLOC_MAX_WORKSPACE
+    assert lib.tp_ffn_shard_workspace_bytes(1024, 16384, 22528, 1, B.TP_BF16) == \
+        1024 * 22528 * 2 + 1024 * 16384 * 2 > B.TP_FFN_NOALLOC_MAX_WORKSPACE
 
 
 def test_ffn_noalloc_zero_tokens_is_a_no_op(lib):
