@@ -760,8 +760,9 @@ def summarize_attn_profile(trace_csv, cmd):
 
 
 # First products of FFN shards (t = 1) whose tile plans are single kinds of
-# one tile per CU: [tokens, ffn] -> 128x192, 256x192, 256x256 (X K-blocked,
-# ffn >= 8192) and 256x128 tiles; K (the hidden size) from 2048 to 16384.
+# one tile per CU: [tokens, ffn] -> 128x192, 256x192, 256x256 and 256x128
+# tiles (X read as given: the K = 32 kinds through A pairs); K (the hidden
+# size) from 2048 to 16384.
 TILE_SWEEP = ((2048, 3072), (2048, 6144), (2048, 8192), (4096, 2048))
 TILE_SWEEP_K = (2048, 4096, 8192, 16384)
 TILE_SWEEP_CALLS = 12
@@ -833,8 +834,11 @@ def summarize_tile_sweep(trace_csv, counter_csv, cmd_trace, cmd_pmc):
             grp = groups[s_i * len(TILE_SWEEP_K) + k_i]
             ts.append(statistics.median(dur(r) for r in grp[2:]))
         kind = _short(groups[s_i * len(TILE_SWEEP_K)][0]["Kernel_Name"])
-        tile = "x".join(kind.split("<")[1].split(",")[:2]).replace(" ", "")
-        a_op = "K-blocked" if kind.rstrip(">").split(",")[-2].strip() == "true" else "row-major"
+        # <BM, BN, WM, WN, KS, NSL, Epi, AKB, NA, AP>
+        prm = [x.strip() for x in kind.split("<")[1].rstrip(">").split(",")]
+        tile = f"{prm[0]}x{prm[1]}"
+        a_op = ("K-blocked" if prm[7] == "true" else
+                "row-major, A pairs" if len(prm) > 9 and prm[9] == "true" else "row-major")
         kinds[(tok, fs)] = (tile, a_op)
         slope, fixed = np.polyfit(np.array(TILE_SWEEP_K, float), np.array(ts), 1)
         steady = 2 * tok * fs / (slope * 1e-6) / 1e12
