@@ -115,7 +115,7 @@ hipError_t partial_reduce(const ReducePtrs& ptrs, int t, int pdt,
 // y = LayerNorm(x) per row: (x - mean) / sqrt(var + eps) * gamma + beta,
 // biased variance, gamma/beta fp32 [cols] (nullable: 1 and 0).  xout is
 // nullable (x not stored).  cols a multiple of 8, at most kLnMaxCols.
-constexpr int kLnMaxCols = 256 * 8 * 16;
+constexpr int kLnMaxCols = 512 * 8 * 8;  // 512 threads x 8 groups x 8 columns
 hipError_t reduce_layernorm(const ReducePtrs& ptrs, int t, int pdt, const void* R, int rdt,
                             void* xout, int xdt, void* yout, int ydt, const float* gamma,
                             const float* beta, float eps, int64_t rows, int cols,

@@ -290,10 +290,14 @@ __device__ __forceinline__ void add8_dyn(const Raw8& r, int dt, float* acc) {
     add8<DT_F32>(r, acc);
 }
 
-// Launch bound by groups per thread: wider rows get fewer, larger threads.
+// At most 512 threads (8 waves) per row: with the registers of up to three
+// groups per thread two rows' workgroups share a CU, so one row's loads
+// overlap the other's reductions and stores (a 768-thread row at 87
+// registers left one row per CU: 4.85 -> 5.43 TB/s at 12288 columns, 4.47
+// -> 5.31 at 8192).
 template <int G>
 struct LnThreads {
-  static constexpr int value = G <= 2 ? 1024 : (G == 4 ? 768 : 512);
+  static constexpr int value = 512;
 };
 
 template <int PDT, int C, int G>
@@ -310,8 +314,8 @@ reduce_ln_kernel(ReducePtrs ptrs, int t, const void* R, int rdt, void* xout, int
     // one re-reads the row's first group and is neither summed nor stored)
     auto ok = [&](int j) { return (int)threadIdx.x + nt * j < ng; };
     auto gi = [&](int j) { return g0 + (ok(j) ? (int)threadIdx.x + nt * j : 0); };
-    // Slot by slot (a row spans 1024 threads at most, so a workgroup has
-    // 16 KB x (C + 2) of loads in flight per chunk even one slot at a
+    // Slot by slot (a row spans 512 threads at most, so a workgroup has
+    // 8 KB x (C + 2) of loads in flight per chunk even one slot at a
     // time), chunk by chunk: partial 0, partials 1..C and, with the last
     // chunk, the residual are loaded before the first add.
     float v[G][8];
@@ -418,18 +422,23 @@ hipError_t launch_ln(const ReducePtrs& ptrs, int t, const void* R, int rdt, void
   return hipGetLastError();
 }
 
-// Groups per thread: the fewest (1, 2, 4, 8) that keep a row within the
-// kernel's thread bound (1024, 1024, 768, 512 threads).
+// Groups per thread: the fewest of 1, 2, 3, 4, 6, 8 that keep a row within
+// 512 threads.
 template <int PDT, int C>
 hipError_t launch_ln_g(const ReducePtrs& ptrs, int t, const void* R, int rdt, void* xout,
                        int xdt, void* yout, int ydt, const float* gamma, const float* beta,
                        float eps, int64_t rows, int cols, hipStream_t s) {
+#define TP_LN_G(G) \
+  launch_ln<PDT, C, G>(ptrs, t, R, rdt, xout, xdt, yout, ydt, gamma, beta, eps, rows, cols, s)
   const int ng = cols / 8;
-  if (ng <= 1024) return launch_ln<PDT, C, 1>(ptrs, t, R, rdt, xout, xdt, yout, ydt, gamma, beta, eps, rows, cols, s);
-  if (ng <= 2048) return launch_ln<PDT, C, 2>(ptrs, t, R, rdt, xout, xdt, yout, ydt, gamma, beta, eps, rows, cols, s);
-  if (ng <= 3072) return launch_ln<PDT, C, 4>(ptrs, t, R, rdt, xout, xdt, yout, ydt, gamma, beta, eps, rows, cols, s);
-  if (ng <= 4096) return launch_ln<PDT, C, 8>(ptrs, t, R, rdt, xout, xdt, yout, ydt, gamma, beta, eps, rows, cols, s);
+  if (ng <= 512) return TP_LN_G(1);
+  if (ng <= 1024) return TP_LN_G(2);
+  if (ng <= 1536) return TP_LN_G(3);
+  if (ng <= 2048) return TP_LN_G(4);
+  if (ng <= 3072) return TP_LN_G(6);
+  if (ng <= 4096) return TP_LN_G(8);
   return hipErrorInvalidValue;
+#undef TP_LN_G
 }
 
 // Chunk size as for the reduce: t-1 for t <= 8 (no duplicate loads), 8 beyond.

@@ -51,7 +51,9 @@ def _run(gpu, parts, R, g, b, pdt, rdt, xdt, ydt, eps, slice_of=(0, 1)):
     (3, 37, 72, syn.BF16, syn.BF16, syn.F32, syn.F32, True),
     (4, 300, 12288, syn.BF16, syn.BF16, syn.F32, syn.F32, True),
     (2, 64, 32768, syn.F32, syn.F32, syn.F32, syn.F32, False),    # widest row (8 groups per thread)
-    (4, 40, 20000, syn.BF16, syn.BF16, syn.F32, syn.BF16, True),  # 4 groups per thread, ragged
+    (4, 40, 20000, syn.BF16, syn.BF16, syn.F32, syn.BF16, True),  # 6 groups per thread, ragged
+    (5, 33, 14000, syn.BF16, syn.F32, syn.F32, syn.F32, True),    # 4 groups per thread, ragged
+    (2, 16, 8192, syn.F32, syn.BF16, syn.BF16, syn.F32, False),   # 2 groups per thread
     (1, 5, 8, syn.F32, None, None, syn.F32, True),                # one group per row
     (8, 129, 4104, syn.BF16, syn.F32, syn.BF16, syn.F32, True),   # ragged groups per thread
 ])
