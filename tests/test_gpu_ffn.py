@@ -348,14 +348,18 @@ def test_non_current_stream_matches_default(gpu):
     (1000, 8200, 1000, "GEMM2: 256x192 tiles, ragged rows and columns"),
     (1800, 6152, 1000, "GEMM2: 256x128 waves, then 128x128 (64-deep stages)"),
     (3000, 8200, 1000, "GEMM2: 128x192 waves, then 256x128"),
-    (1800, 256, 12296, "GEMM1 with K-blocked X: 256x256 waves, then 256x192 over ragged columns"),
-    (1000, 512, 8200, "GEMM1 with K-blocked X: 256x192 tiles, ragged"),
+    (1800, 264, 12296, "GEMM1 over row-major X through A pairs: 256x256 waves, then 256x192 "
+                       "over ragged columns; K = 264 ends 8 columns into a pair's first stage"),
+    (1000, 1000, 8200, "GEMM1 through A pairs: 256x192 tiles, ragged rows, columns and K "
+                       "(the last pair's second stage holds 8 columns)"),
+    (600, 520, 20488, "GEMM1 with K-blocked X (ffn/t >= 20480): ragged K and columns"),
 ])
 def test_tile_plans_ragged(gpu, M, h, fs, what):
     """Shapes whose output is covered by two tile kinds (whole waves of one,
     the remaining ragged columns by another) or by the 256x192 kind, in
-    both products; fp32 output, 48 seeded rows (first and last included)
-    against the oracle."""
+    both products, and the first product's two ways of reading X (row-major
+    through A pairs, K-blocked copy) with K ending inside a stage; fp32
+    output, 48 seeded rows (first and last included) against the oracle."""
     seed = 700 + M + h
     d = syn.make_ffn_inputs(seed, M, h, fs, syn.BF16)
     got = run_shard(gpu, d, 0, 1, syn.F32, view=False)
