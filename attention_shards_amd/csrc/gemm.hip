@@ -19,13 +19,13 @@
 //   * gemm_bf16_kernel: 4 waves (one per SIMD), DMAs and fragment reads
 //     interleaved between the MFMAs of each wave.  256x256 tiles: each wave
 //     owns a 128x128 block (256 accumulator registers), K = 32 per stage
-//     through a 5-slot ring (160 KB); the wide wave block halves the LDS
-//     fragment reads per MFMA of a 128x64 block.  256x128, 128x192 and
-//     128x128 tiles: K = 64 per stage through a 3-slot ring.  (128x192
-//     fills all 256 CUs where 256x128 would leave a quarter idle, e.g.
-//     2048 x 3072 outputs.)  The K = 32 kinds over a row-major A keep A in
-//     two slots of 128-byte rows, each the K columns of two stages, beside a
-//     4-slot B ring, so that A's DMAs read whole lines of its rows.
+//     through a 5-slot ring (160 KB) over a K-blocked A; the wide wave block
+//     halves the LDS fragment reads per MFMA of a 128x64 block.  256x128,
+//     128x192 and 128x128 tiles: K = 64 per stage through a 3-slot ring.
+//     (128x192 fills all 256 CUs where 256x128 would leave a quarter idle,
+//     e.g. 2048 x 3072 outputs.)  The K = 32 kinds over a row-major A keep A
+//     in two slots of 128-byte rows, each the K columns of two stages,
+//     beside a 4-slot B ring, so that A's DMAs read whole lines of its rows.
 //   * Workgroup ids are remapped so each XCD (dispatch is round-robin over
 //     the 8 XCDs) receives a contiguous run of tiles, ordered in groups of 8
 //     tile-rows so neighbouring tiles share A and B panels in that XCD's L2.
