@@ -184,6 +184,31 @@ def time_batched(fn, steps, warmup):
     return a.elapsed_time(b) / steps
 
 
+def device_info():
+    """Name, compute units, the maximum shader and memory clocks the device
+    reports, and the HIP / ROCm versions (the clock the GEMMs run at under
+    load is measured with counters: profiles/counters_mfma_clock.md)."""
+    import ctypes
+    import torch
+    prop = torch.cuda.get_device_properties(0)
+    info = {"name": torch.cuda.get_device_name(0), "compute_units": prop.multi_processor_count,
+            "hip": torch.version.hip}
+    try:   # hipDeviceGetAttribute: hipDeviceAttributeClockRate = 5, MemoryClockRate = 60 (kHz)
+        hip = ctypes.CDLL("libamdhip64.so")
+        for key, attr in (("max_sclk_mhz", 5), ("max_mclk_mhz", 60)):
+            v = ctypes.c_int(0)
+            if hip.hipDeviceGetAttribute(ctypes.byref(v), attr, torch.cuda.current_device()) == 0:
+                info[key] = round(v.value / 1000)
+    except OSError:
+        pass
+    try:
+        with open("/opt/rocm/.info/version") as f:
+            info["rocm"] = f.read().strip()
+    except OSError:
+        pass
+    return info
+
+
 def host_info():
     """CPU model and the cores this process may run on."""
     model = "unknown"
@@ -1154,9 +1179,7 @@ def main():
         rows["attn_shard"] = attn_row(K, W)
         log("layer")
         rows["layer"] = layer_row(max(3, K // 10), 2)
-        rows["device"] = {"name": torch.cuda.get_device_name(0),
-                          "compute_units": torch.cuda.get_device_properties(0).multi_processor_count,
-                          "hip": torch.version.hip}
+        rows["device"] = device_info()
     if not args.no_cpu_baseline and not args.headline_only:
         log("cpu baseline (oracle)")
         res["cpu_baseline"] = cpu_baseline(d)
