@@ -59,7 +59,7 @@ __device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
 // Taken at x = |z|/sqrt(2) and written in base 2 (the coefficients are
 // P's times log2(e)).  With E = z erfc(x)/2 (the sign of z), GeLU = z - E
 // for z >= 0 and E for z < 0, i.e. max(z, 0) - |E|.  Branch-free: one
-// reciprocal, one exponential, twelve multiply(-add)s, a max and a
+// reciprocal, one exponential, fifteen multiply(-add)s, a max and a
 // subtract.  Evaluated in fp32 (hardware rcp/exp2): |error| <= 2.5e-7 |z|,
 // relative error <= 1e-5.
 __device__ __forceinline__ float gelu_erf(float z) {
@@ -84,6 +84,37 @@ __device__ __forceinline__ float gelu_erf(float z) {
   const float e = __builtin_amdgcn_exp2f(fmaf(z, z * (float)(-0.5 * L2E), p));
   const float E = (0.5f * z) * t * e;
   return fmaxf(z, 0.0f) - fabsf(E);
+}
+
+// GeLU(z) for a result rounded to bf16 (8-bit significand: an error well
+// below half a unit in the last place, 2^-9 relative, leaves at most one
+// unit after rounding).  Same form as gelu_erf with P replaced by Q of
+// degree 5, the minimax (Remez) fit of log2(erfc(x) exp(x^2) / t) - 1 over
+// t in [0.17, 1], i.e. |z| <= 13.8: erfc(x)/2 = t exp2(-x^2 log2(e) + Q(t)).
+// Q's maximum error is 1.1e-5 in base-2 units (7.6e-6 relative); with the
+// fp32 rounding of the exponent's argument (up to 104 in size at z = -12)
+// the GeLU's relative error stays below 1.2e-5 for |z| <= 12 and 1.4e-5
+// down to z = -13 (below about -13.06 the exponential leaves the normal fp32
+// range; the exact GeLU is 3.6e-38 there).  GeLU = max(z, 0) - (|z| t)
+// exp2(...) as one fused multiply-add: one reciprocal, one exponential and
+// eleven other vector operations (gelu_erf: seventeen).
+__device__ __forceinline__ float gelu_erf_bf16(float z) {
+  constexpr double L2E = 1.4426950408889634;
+  constexpr float Q0 = -2.827233510302323f, Q1 = 1.468683049078055f,
+                  Q2 = 0.3670840868812766f, Q3 = 0.6845487657077611f,
+                  Q4 = -1.0231460297394164f, Q5 = 0.33007462354023553f;
+  const float t = __builtin_amdgcn_rcpf(fmaf(fabsf(z), 0.35355339059327376f, 1.0f));
+  float q = fmaf(Q5, t, Q4);
+  q = fmaf(q, t, Q3);
+  q = fmaf(q, t, Q2);
+  q = fmaf(q, t, Q1);
+  q = fmaf(q, t, Q0);
+  const float e = __builtin_amdgcn_exp2f(fmaf(z, z * (float)(-0.5 * L2E), q));
+  // max(z, 0) as an integer max of the bits (a set sign bit is a negative
+  // integer): one instruction, where fmaxf first canonicalizes z
+  const int zb = __builtin_bit_cast(int, z);
+  const float zpos = __builtin_bit_cast(float, zb > 0 ? zb : 0);
+  return fmaf(-(fabsf(z) * t), e, zpos);
 }
 
 // ---------------------------------------------------------------------------
@@ -128,40 +159,51 @@ struct EpiStore {
   }
 };
 
-// GeLU(acc), row-major (row stride ldc) or, with kb_shift > 0 and bf16
-// output, K-blocked for the next product: column c of row r at
+// GeLU(acc) rounded to bf16, row-major (row stride ldc) or, with
+// kb_shift > 0, K-blocked for the next product: column c of row r at
 // ((c >> kb_shift) * rows + r) * kb + c % kb, kb = 1 << kb_shift, so that
 // each kb-column block of all rows is one contiguous [rows][kb] slab.
 struct EpiGelu {
-  void* C;
+  uint16_t* C;
   int64_t ldc;
-  int out;
   int rows;
   int kb_shift;
-  __device__ int64_t kblock_at(int row, int col0) const {
+  __device__ uint16_t* at(int row, int col0) const {
+    if (!kb_shift) return C + (int64_t)row * ldc + col0;
     const int kb = 1 << kb_shift;
-    return ((int64_t)(col0 >> kb_shift) * rows + row) * kb + (col0 & (kb - 1));
+    return C + ((int64_t)(col0 >> kb_shift) * rows + row) * kb + (col0 & (kb - 1));
   }
   __device__ void store4(int row, int col0, const float* v) const {
     float g[4];
 #pragma unroll
+    for (int r = 0; r < 4; ++r) g[r] = gelu_erf_bf16(v[r]);
+    *reinterpret_cast<uint2*>(at(row, col0)) = uint2{pack_bf16(g[0], g[1]), pack_bf16(g[2], g[3])};
+  }
+  __device__ void store8(int row, int col0, const float* v) const {
+    float g[8];
+#pragma unroll
+    for (int r = 0; r < 8; ++r) g[r] = gelu_erf_bf16(v[r]);
+    *reinterpret_cast<u32x4*>(at(row, col0)) =
+        u32x4{pack_bf16(g[0], g[1]), pack_bf16(g[2], g[3]), pack_bf16(g[4], g[5]),
+              pack_bf16(g[6], g[7])};
+  }
+};
+
+// GeLU(acc) kept in fp32 (the fp32 products), row stride ldc.
+struct EpiGeluF32 {
+  float* C;
+  int64_t ldc;
+  __device__ void store4(int row, int col0, const float* v) const {
+    float g[4];
+#pragma unroll
     for (int r = 0; r < 4; ++r) g[r] = gelu_erf(v[r]);
-    if (kb_shift)
-      *reinterpret_cast<uint2*>(static_cast<uint16_t*>(C) + kblock_at(row, col0)) =
-          uint2{pack_bf16(g[0], g[1]), pack_bf16(g[2], g[3])};
-    else
-      store_run4(C, ldc, out, row, col0, g);
+    store_run4(C, ldc, OUT_F32, row, col0, g);
   }
   __device__ void store8(int row, int col0, const float* v) const {
     float g[8];
 #pragma unroll
     for (int r = 0; r < 8; ++r) g[r] = gelu_erf(v[r]);
-    if (kb_shift)
-      *reinterpret_cast<u32x4*>(static_cast<uint16_t*>(C) + kblock_at(row, col0)) =
-          u32x4{pack_bf16(g[0], g[1]), pack_bf16(g[2], g[3]), pack_bf16(g[4], g[5]),
-                pack_bf16(g[6], g[7])};
-    else
-      store_run8(C, ldc, out, row, col0, g);
+    store_run8(C, ldc, OUT_F32, row, col0, g);
   }
 };
 
@@ -1083,7 +1125,7 @@ hipError_t gemm_bf16_gelu_akb(const uint16_t* Akb, int kb, const uint16_t* B, in
   if (kb_out != 32 && kb_out != 64) return hipErrorInvalidValue;
   if (M > 0 && N > 0 && kb != a_block(M, N)) return hipErrorInvalidValue;
   const int sh = kb_out == 32 ? 5 : 6;
-  return dispatch_bf16<true>(Akb, M, B, ldb, M, N, K, EpiGelu{C, 0, (int)OUT_BF16, M, sh}, s);
+  return dispatch_bf16<true>(Akb, M, B, ldb, M, N, K, EpiGelu{C, 0, M, sh}, s);
 }
 
 TileChoice choose_pair_tile(int M, int N) {
@@ -1112,7 +1154,7 @@ hipError_t gemm_bf16_gelu(const uint16_t* A, int64_t lda, const uint16_t* B,
                           int K, int kb, hipStream_t s) {
   if (kb != 0 && kb != 32 && kb != 64) return hipErrorInvalidValue;
   const int sh = kb == 32 ? 5 : (kb == 64 ? 6 : 0);
-  return dispatch_bf16<false>(A, lda, B, ldb, M, N, K, EpiGelu{C, ldc, (int)OUT_BF16, M, sh}, s);
+  return dispatch_bf16<false>(A, lda, B, ldb, M, N, K, EpiGelu{C, ldc, M, sh}, s);
 }
 
 hipError_t gemm_bf16_qkv(const uint16_t* A, int64_t lda, const uint16_t* B,
@@ -1137,7 +1179,10 @@ hipError_t gemm_f32_add(const float* A, int64_t lda, const float* B, int64_t ldb
 hipError_t gemm_f32(const float* A, int64_t lda, const float* B, int64_t ldb,
                     void* C, int64_t ldc, OutType out, bool gelu, int M, int N,
                     int K, hipStream_t s) {
-  if (gelu) return launch_f32(A, lda, B, ldb, M, N, K, EpiGelu{C, ldc, (int)out, 0, 0}, s);
+  if (gelu) {
+    if (out != OUT_F32) return hipErrorInvalidValue;  // GeLU(Z) stays fp32 on this path
+    return launch_f32(A, lda, B, ldb, M, N, K, EpiGeluF32{static_cast<float*>(C), ldc}, s);
+  }
   return launch_f32(A, lda, B, ldb, M, N, K, EpiStore{C, ldc, (int)out}, s);
 }
 

@@ -73,7 +73,8 @@ hipError_t gemm_bf16_qkv(const uint16_t* A, int64_t lda, const uint16_t* B,
                          int64_t ldb, const QkvOut& q, int M, int N, int K,
                          hipStream_t s);
 
-// fp32 inputs, fp32 MFMA.  Requirements: K % 4 == 0, N % 4 == 0.
+// fp32 inputs, fp32 MFMA.  Requirements: K % 4 == 0, N % 4 == 0; with gelu the
+// output is fp32 (GeLU(Z) is kept in fp32 between the fp32 products).
 hipError_t gemm_f32(const float* A, int64_t lda, const float* B, int64_t ldb,
                     void* C, int64_t ldc, OutType out, bool gelu, int M, int N,
                     int K, hipStream_t s);
