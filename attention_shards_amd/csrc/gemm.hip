@@ -861,10 +861,11 @@ double kind_cost(int k, int64_t tiles, int64_t ncu) {
 // 22528 in 256x256 tiles: 704 tiles = 2.75 waves); two rectangles avoid it:
 // whole waves of kind k1 over the first columns, then the remaining columns
 // in a kind whose tiles fill about one wave (there: 512 tiles of 256x256,
-// then 256 tiles of 256x192).  Both kinds share the stage depth, so one
-// K-blocked A serves both; a split plan is kept only when it is estimated
-// at least 3% cheaper than the best single kind.
-Plan plan_bf16(int M, int N) {
+// then 256 tiles of 256x192).  Over a K-blocked A both kinds share the
+// stage depth, so one blocking serves both (a row-major A serves any pair);
+// a split plan is kept only when it is estimated at least 3% cheaper than
+// the best single kind.
+Plan plan_bf16(int M, int N, bool a_kblocked) {
   const int64_t ncu = device_cu_count();
   Plan best{0, -1, N};
   double best_cost = 1e300;
@@ -889,7 +890,7 @@ Plan plan_bf16(int M, int N) {
     const double c1 = (double)(tm1 * cols1 / ncu) * t1.bm * t1.bn / t1.eff;
     for (int k2 = 0; k2 < NKIND; ++k2) {
       const TileKind& t2 = kKinds[k2];
-      if (t2.bk != t1.bk) continue;
+      if (a_kblocked && t2.bk != t1.bk) continue;
       const int64_t tiles2 = (int64_t)((M + t2.bm - 1) / t2.bm) * ((N - n1 + t2.bn - 1) / t2.bn);
       const double c = c1 + kind_cost(k2, tiles2, ncu);
       if (c < best_cost * 0.999 && c <= 0.97 * single) {
@@ -938,7 +939,7 @@ hipError_t launch_kind(int k, const uint16_t* A, int64_t lda, const uint16_t* B,
 
 // K block (stage depth) of the plan for an [M, N] output: 32 for 256x256
 // and 256x192 tiles (five stages fill the LDS), 64 for the others.
-int a_block(int M, int N) { return kKinds[plan_bf16(M, N).k1].bk; }
+int a_block(int M, int N) { return kKinds[plan_bf16(M, N, true).k1].bk; }
 
 // AKB: A is K-blocked by the plan's stage depth (see gemm_bf16_kernel), lda
 // its row count; the caller has checked the block.
@@ -949,7 +950,7 @@ hipError_t dispatch_bf16(const uint16_t* A, int64_t lda, const uint16_t* B,
   // tiles are addressed with 32-bit byte offsets: 256 rows of A, 64 of B
   // (K-blocked A tiles are at most 32 KiB)
   if ((!AKB && lda >= ((int64_t)1 << 22)) || ldb >= ((int64_t)1 << 24)) return hipErrorInvalidValue;
-  const Plan p = plan_bf16(M, N);
+  const Plan p = plan_bf16(M, N, AKB);
   hipError_t e = launch_kind<AKB>(p.k1, A, lda, B, ldb, M, 0, p.n1, K, epi, s);
   if (e == hipSuccess && p.k2 >= 0) e = launch_kind<AKB>(p.k2, A, lda, B, ldb, M, p.n1, N, K, epi, s);
   return e;
