@@ -20,12 +20,20 @@
 //     interleaved between the MFMAs of each wave.  256x256 tiles: each wave
 //     owns a 128x128 block (256 accumulator registers), K = 32 per stage
 //     through a 5-slot ring (160 KB) over a K-blocked A; the wide wave block
-//     halves the LDS fragment reads per MFMA of a 128x64 block.  256x128,
+//     halves the LDS fragment reads per MFMA of a 128x64 block.  256x192
+//     tiles: 128x96 per wave, K = 32 per stage, five 28 KB slots.  256x128,
 //     128x192 and 128x128 tiles: K = 64 per stage through a 3-slot ring.
 //     (128x192 fills all 256 CUs where 256x128 would leave a quarter idle,
 //     e.g. 2048 x 3072 outputs.)  The K = 32 kinds over a row-major A keep A
 //     in two slots of 128-byte rows, each the K columns of two stages,
 //     beside a 4-slot B ring, so that A's DMAs read whole lines of its rows.
+//   * A tile plan covers the output with whole waves of one kind and, where
+//     that leaves a wave partly idle, the remaining columns in a second kind
+//     (two launches).
+//   * Epilogues run on the fp32 accumulators staged through LDS: GeLU to
+//     bf16 (a fit accurate to well below bf16's rounding) or, for the fp32
+//     products, to fp32; plain stores; the Q/K/V^T scatter of the attention
+//     workspace; the add of a pre-summed fp32 matrix.
 //   * Workgroup ids are remapped so each XCD (dispatch is round-robin over
 //     the 8 XCDs) receives a contiguous run of tiles, ordered in groups of 8
 //     tile-rows so neighbouring tiles share A and B panels in that XCD's L2.
