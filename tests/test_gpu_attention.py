@@ -37,6 +37,28 @@ def test_attention_shard_t8_full(gpu):
     assert e <= TOL_BF16
 
 
+def test_attention_layer_shape_first_and_last_sequence(gpu):
+    """The whole-layer row's attention shard: 4 sequences of 2048 tokens,
+    hidden 12288, 96 heads of 128, t=4, shard i=1 (heads 24-47), causal,
+    fp32 partial [8192, 12288] (256-query blocks; the QKV product in four
+    waves of 256x256 tiles and one of 256x128).  The GPU runs the whole
+    call; sequences do not see one another, so the oracle runs the first and
+    the last sequence on their own (batch 1) and those row blocks are
+    compared in full."""
+    batch, seq, hidden, nh, d, t, i = 4, 2048, 12288, 96, 128, 4, 1
+    a = syn.make_attn_inputs(46, batch, seq, hidden, nh, d)
+    got = run(gpu, a, batch, seq, nh, d, i, t, True, syn.F32)
+    log("attention layer shape: GPU call done")
+    f = {k: syn.to_f64(a[k], syn.BF16) for k in ("WQ", "WK", "WV", "WO")}
+    for b in (0, batch - 1):
+        rows = slice(b * seq, (b + 1) * seq)
+        X = syn.to_f64(a["X"][rows], syn.BF16)
+        r = oracle.attn_shard(X, f["WQ"], f["WK"], f["WV"], f["WO"], 1, seq, nh, d, i, t, True)
+        e = rel_err(got[rows], r)
+        log(f"attention layer shape t=4 i=1, sequence {b}: err {e:.4f}")
+        assert e <= TOL_BF16
+
+
 @pytest.mark.parametrize("batch,seq,hidden,nh,t,i,causal,out", [
     (2, 100, 256, 4, 2, 1, True, syn.F32),     # ragged sequence, two sequences
     (2, 100, 256, 4, 2, 0, False, syn.F32),
