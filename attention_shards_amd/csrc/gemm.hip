@@ -37,8 +37,10 @@
 //   * Workgroup ids are remapped so each XCD (dispatch is round-robin over
 //     the 8 XCDs) receives a contiguous run of tiles, ordered in groups of 8
 //     tile-rows so neighbouring tiles share A and B panels in that XCD's L2.
+#include <algorithm>
 #include <atomic>
 #include <numeric>
+#include <type_traits>
 
 #include "internal.h"
 
@@ -267,8 +269,34 @@ struct EpiAdd {
   }
 };
 
+// fp32 partial product of one K part (a split K): part p's [M, ncols]
+// block of P at p * part_stride, columns counted from c_base.
+struct EpiPart {
+  float* P;
+  int64_t ldp;
+  int64_t part_stride;
+  int c_base;
+  int part;
+  __device__ void store4(int row, int col0, const float* v) const {
+    store_run4(P + part * part_stride, ldp, OUT_F32, row, col0 - c_base, v);
+  }
+  __device__ void store8(int row, int col0, const float* v) const {
+    store_run8(P + part * part_stride, ldp, OUT_F32, row, col0 - c_base, v);
+  }
+};
+
+// Epilogues that are told which K part they store.
+template <class Epi>
+struct PerPart {
+  static constexpr bool value = false;
+};
+template <>
+struct PerPart<EpiPart> {
+  static constexpr bool value = true;
+};
+
 // Rows per epilogue call in the GEMM's store loop (see the kernel).
-template <class E>
+template <class Epi>
 struct RowBatch {
   static constexpr int value = 1;
 };
@@ -360,12 +388,17 @@ struct ColumnRuns<EpiQkv> {
 };
 
 // Tile index with the XCD-contiguous remap and grouped (8 tile-rows) order.
+// With a K split the grid holds `parts` copies of the tile grid, part p
+// (the K columns [p*kpart, (p+1)*kpart)) at linear ids [p*tiles, (p+1)*tiles),
+// so each XCD's run covers whole groups of one part.
 __device__ __forceinline__ void tile_coords(int tiles_m, int tiles_n, int& tm,
-                                            int& tn) {
+                                            int& tn, int& part) {
   const int bid = blockIdx.x;
   const int nb = gridDim.x;
   const int xcd = bid & 7, j = bid >> 3, q = nb >> 3, r = nb & 7;
-  const int lin = xcd * q + (xcd < r ? xcd : r) + j;
+  int lin = xcd * q + (xcd < r ? xcd : r) + j;
+  part = lin / (tiles_m * tiles_n);
+  lin -= part * (tiles_m * tiles_n);
   constexpr int GROUP = 8;
   const int per_group = GROUP * tiles_n;
   const int g = lin / per_group;
@@ -374,6 +407,11 @@ __device__ __forceinline__ void tile_coords(int tiles_m, int tiles_n, int& tm,
   const int w = lin - g * per_group;
   tm = first_m + w % gsize;
   tn = w / gsize;
+}
+
+__device__ __forceinline__ void tile_coords(int tiles_m, int tiles_n, int& tm, int& tn) {
+  int part;
+  tile_coords(tiles_m, tiles_n, tm, tn, part);
 }
 
 // ---------------------------------------------------------------------------
@@ -548,11 +586,14 @@ template <int BM, int BN, int WM, int WN, int KS, int NSL, class Epi, bool AKB, 
 __global__ void __launch_bounds__(WM * WN * 64)
 gemm_bf16_kernel(const uint16_t* __restrict__ A, int64_t lda,
                  const uint16_t* __restrict__ B, int64_t ldb, int M, int N,
-                 int K, int tiles_m, int tiles_n, int n_base, Epi epi) {
+                 int K, int tiles_m, int tiles_n, int n_base, int kpart, Epi epi) {
   // With AKB, A is K-blocked by the stage depth BK: [ceil(K/BK)][lda][BK],
   // lda the padded row count, so a stage's A tile is one contiguous run of
   // rows.  The grid covers output columns [n_base, N) (tiles_n tiles wide);
-  // all coordinates are absolute.
+  // all coordinates are absolute.  A grid of several copies of the tile grid
+  // splits K: copy p multiplies K columns [p*kpart, min((p+1)*kpart, K))
+  // (kpart a multiple of BK, every part non-empty) and hands its partial
+  // product to an epilogue that stores per part.
   static_assert(KS == 2 || KS == 4, "k-steps per stage");
   static_assert(NSL >= 3 && NSL <= 6, "ring slots");
   static_assert(NA == 1 || (NA == 2 && AKB), "paired A operands are K-blocked");
@@ -589,8 +630,17 @@ gemm_bf16_kernel(const uint16_t* __restrict__ A, int64_t lda,
   const uint32_t lds_a_addr = (uint32_t)(uintptr_t)(lds_u8*)lds_a;
   const uint32_t lds_b_addr = (uint32_t)(uintptr_t)(lds_u8*)lds_b;
 
-  int tm, tn;
-  tile_coords(tiles_m, tiles_n, tm, tn);
+  int tm, tn, part;
+  tile_coords(tiles_m, tiles_n, tm, tn, part);
+  if constexpr (NA == 1) {  // (paired A operands are never split)
+    if (part > 0) {  // this part's K columns: shift A and B, shorten K
+      const int kbeg = part * kpart;
+      A += AKB ? (int64_t)(kbeg / BK) * lda * BK : (int64_t)kbeg;
+      B += (int64_t)kbeg * ldb;
+      K -= kbeg;
+    }
+  }
+  if (K > kpart) K = kpart;
   const int m0 = tm * BM, n0 = n_base + tn * BN;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wr0 = (wave / WN) * (BM / WM);
@@ -835,7 +885,9 @@ gemm_bf16_kernel(const uint16_t* __restrict__ A, int64_t lda,
   wait_vmcnt<0>();
   __syncthreads();
 
-  epilogue_lds<BN / WN>(smem, acc, epi, M, N, m0 + wr0, n0 + wc0, wave, lane);
+  Epi e = epi;
+  if constexpr (PerPart<Epi>::value) e.part = part;
+  epilogue_lds<BN / WN>(smem, acc, e, M, N, m0 + wr0, n0 + wc0, wave, lane);
 }
 
 // Tile kinds of the plain products: rows, columns, stage depth (the K
@@ -854,8 +906,11 @@ constexpr TileKind kKinds[NKIND] = {{256, 256, 32, 1.0},
 
 // How an [M, N] output is covered: columns [0, n1) by tiles of kind k1,
 // columns [n1, N) by tiles of kind k2 (k2 < 0: kind k1 covers all of N).
+// parts > 1: the k2 rectangle splits K into parts of kpart columns, each
+// part's product stored as an fp32 partial and the partials summed after.
 struct Plan {
   int k1, k2, n1;
+  int parts = 1, kpart = 0;
 };
 
 // Estimated time of `tiles` tiles of kind k: full waves over the compute
@@ -873,8 +928,7 @@ double kind_cost(int k, int64_t tiles, int64_t ncu) {
 // stage depth, so one blocking serves both (a row-major A serves any pair);
 // a split plan is kept only when it is estimated at least 3% cheaper than
 // the best single kind.
-Plan plan_bf16(int M, int N, bool a_kblocked) {
-  const int64_t ncu = device_cu_count();
+Plan plan_columns(int M, int N, bool a_kblocked, int64_t ncu) {
   Plan best{0, -1, N};
   double best_cost = 1e300;
   for (int k = 0; k < NKIND; ++k) {
@@ -910,58 +964,212 @@ Plan plan_bf16(int M, int N, bool a_kblocked) {
   return best;
 }
 
+// Seconds of one wave of kind-k tiles over K columns: the tile's FLOPs at
+// one CU's share of the 256x256 kind's steady rate (about 1340 TFLOP/s on
+// 256 CUs), plus a fixed cost per tile (first loads, epilogue).
+constexpr double kCuFlops = 1340e12 / 256;
+constexpr double kTileFixed = 8e-6;
+// The fp32 partials of a split K are written and read back once at about
+// this rate, by one more launch.
+constexpr double kPartialBytesPerSec = 5.0e12;
+constexpr double kSumLaunch = 4e-6;
+// Largest partial buffer a split may use.
+constexpr int64_t kMaxSplitBytes = (int64_t)1 << 30;
+
+double wave_seconds(int k, int64_t K) {
+  return kKinds[k].bm * (double)kKinds[k].bn * 2.0 * (double)K / kKinds[k].eff / kCuFlops +
+         kTileFixed;
+}
+
+double rect_seconds(int k, int M, int cols, int64_t K, int parts, int64_t ncu) {
+  if (cols <= 0) return 0.0;
+  const int64_t tiles = (int64_t)((M + kKinds[k].bm - 1) / kKinds[k].bm) *
+                        ((cols + kKinds[k].bn - 1) / kKinds[k].bn) * parts;
+  return (double)((tiles + ncu - 1) / ncu) * wave_seconds(k, K);
+}
+
+// With a long K (k_split > 0, the row-parallel product over a K-blocked
+// A), a plan may instead run whole waves of 256x256 tiles over the first
+// columns and the rest (often less than a wave of tiles) as 256x256 tiles
+// over 2-8 parts of K: a wave of short tiles instead of a partly idle wave
+// of full-length ones, for one round trip of fp32 partials.  At 2048 rows
+// and 10240 columns (320 tiles of 256x256): 256 full tiles, then 64 tiles
+// in 4 parts.  Taken when its estimate is at least 3% below the plan above.
+Plan plan_bf16(int M, int N, bool a_kblocked, int64_t k_split) {
+  const int64_t ncu = device_cu_count();
+  const Plan cols = plan_columns(M, N, a_kblocked, ncu);
+  if (k_split <= 0) return cols;
+  const double t_cols =
+      rect_seconds(cols.k1, M, cols.n1, k_split, 1, ncu) +
+      (cols.k2 >= 0 ? rect_seconds(cols.k2, M, N - cols.n1, k_split, 1, ncu) : 0.0);
+  const int64_t tm = (M + 255) / 256;
+  const int64_t step = ncu / std::gcd(ncu, tm);
+  int64_t whole = (N / 256) / step * step;
+  if (whole * 256 >= N) whole -= step;
+  Plan best = cols;
+  double best_t = 0.97 * t_cols;
+  for (const int64_t cols1 : {whole, (int64_t)0}) {
+    if (cols1 < 0) continue;
+    const int n1 = (int)(cols1 * 256), rest = N - n1;
+    if (rest <= 0) continue;
+    for (const int want : {2, 3, 4, 6, 8}) {
+      const int64_t kpart = (k_split + want * 32 - 1) / (want * 32) * 32;
+      const int parts = (int)((k_split + kpart - 1) / kpart);
+      if (parts < 2 || (int64_t)parts * M * rest * 4 > kMaxSplitBytes) continue;
+      const double t = rect_seconds(0, M, n1, k_split, 1, ncu) +
+                       rect_seconds(0, M, rest, kpart, parts, ncu) +
+                       8.0 * parts * M * rest / kPartialBytesPerSec + kSumLaunch;
+      if (t < best_t) {
+        best_t = t;
+        best = Plan{0, 0, n1, parts, (int)kpart};
+      }
+    }
+  }
+  return best;
+}
+
 template <int BM, int BN, int WM, int WN, int KS, int NSL, bool AKB, class Epi, int NA = 1,
           bool AP = false>
 hipError_t launch_bf16(const uint16_t* A, int64_t lda, const uint16_t* B, int64_t ldb, int M,
-                       int N, int K, const Epi& epi, hipStream_t s, int n_base = 0) {
+                       int N, int K, const Epi& epi, hipStream_t s, int n_base = 0,
+                       int parts = 1, int kpart = 0) {
   const int tm = (M + BM - 1) / BM, tn = (N - n_base + BN - 1) / BN;
-  hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, WM, WN, KS, NSL, Epi, AKB, NA, AP>), dim3(tm * tn),
-                     dim3(WM * WN * 64), 0, s, A, lda, B, ldb, M, N, K, tm, tn, n_base, epi);
+  if (tm <= 0 || tn <= 0) return hipSuccess;
+  hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, WM, WN, KS, NSL, Epi, AKB, NA, AP>),
+                     dim3(tm * tn * parts), dim3(WM * WN * 64), 0, s, A, lda, B, ldb, M, N, K, tm,
+                     tn, n_base, parts > 1 ? kpart : K, epi);
   return hipGetLastError();
 }
 
-// Output columns [n_base, n_end) in tiles of kind k.
+// Output columns [n_base, n_end) in tiles of kind k (over `parts` parts of
+// kpart K columns when parts > 1).
 template <bool AKB, class Epi>
 hipError_t launch_kind(int k, const uint16_t* A, int64_t lda, const uint16_t* B, int64_t ldb,
-                       int M, int n_base, int n_end, int K, const Epi& epi, hipStream_t s) {
+                       int M, int n_base, int n_end, int K, const Epi& epi, hipStream_t s,
+                       int parts = 1, int kpart = 0) {
   // K = 32 stages over a row-major A read it through A pairs (whole 128-byte
   // lines of its rows)
   switch (k) {
     case 0:
       if constexpr (AKB)
-        return launch_bf16<256, 256, 2, 2, 2, 5, AKB>(A, lda, B, ldb, M, n_end, K, epi, s, n_base);
+        return launch_bf16<256, 256, 2, 2, 2, 5, AKB>(A, lda, B, ldb, M, n_end, K, epi, s, n_base,
+                                                      parts, kpart);
       else
         return launch_bf16<256, 256, 2, 2, 2, 4, AKB, Epi, 1, true>(A, lda, B, ldb, M, n_end, K,
-                                                                   epi, s, n_base);
+                                                                   epi, s, n_base, parts, kpart);
     case 1:
       if constexpr (AKB)
-        return launch_bf16<256, 192, 2, 2, 2, 5, AKB>(A, lda, B, ldb, M, n_end, K, epi, s, n_base);
+        return launch_bf16<256, 192, 2, 2, 2, 5, AKB>(A, lda, B, ldb, M, n_end, K, epi, s, n_base,
+                                                      parts, kpart);
       else
         return launch_bf16<256, 192, 2, 2, 2, 4, AKB, Epi, 1, true>(A, lda, B, ldb, M, n_end, K,
-                                                                   epi, s, n_base);
-    case 2: return launch_bf16<256, 128, 2, 2, 4, 3, AKB>(A, lda, B, ldb, M, n_end, K, epi, s, n_base);
-    case 3: return launch_bf16<128, 192, 2, 2, 4, 3, AKB>(A, lda, B, ldb, M, n_end, K, epi, s, n_base);
-    default: return launch_bf16<128, 128, 2, 2, 4, 3, AKB>(A, lda, B, ldb, M, n_end, K, epi, s, n_base);
+                                                                   epi, s, n_base, parts, kpart);
+    case 2:
+      return launch_bf16<256, 128, 2, 2, 4, 3, AKB>(A, lda, B, ldb, M, n_end, K, epi, s, n_base,
+                                                    parts, kpart);
+    case 3:
+      return launch_bf16<128, 192, 2, 2, 4, 3, AKB>(A, lda, B, ldb, M, n_end, K, epi, s, n_base,
+                                                    parts, kpart);
+    default:
+      return launch_bf16<128, 128, 2, 2, 4, 3, AKB>(A, lda, B, ldb, M, n_end, K, epi, s, n_base,
+                                                    parts, kpart);
   }
 }
 
-// K block (stage depth) of the plan for an [M, N] output: 32 for 256x256
-// and 256x192 tiles (five stages fill the LDS), 64 for the others.
-int a_block(int M, int N) { return kKinds[plan_bf16(M, N, true).k1].bk; }
+// K block (stage depth) of the plan for an [M, N] output over K (k_split:
+// K when the product may split it, else 0): 32 for 256x256 and 256x192
+// tiles (five stages fill the LDS), 64 for the others.
+int a_block(int M, int N, int64_t k_split) {
+  return kKinds[plan_bf16(M, N, true, k_split).k1].bk;
+}
+
+// C[r, n1 + c] = S[r, n1 + c] (when S is given) + sum over the parts of
+// P[p][r][c], in part order, rounded once to the output type: the sum of a
+// split K.  8 columns per thread (ncols % 8 == 0), grid-stride over rows.
+__global__ void __launch_bounds__(256)
+splitk_sum_kernel(const float* __restrict__ P, int parts, int64_t part_stride, int ncols,
+                  const float* __restrict__ S, void* C, int64_t ldc, int out, int M, int n1) {
+  const int64_t groups = (int64_t)M * (ncols / 8);
+  for (int64_t g = (int64_t)blockIdx.x * 256 + threadIdx.x; g < groups;
+       g += (int64_t)gridDim.x * 256) {
+    const int r = (int)(g / (ncols / 8)), c = (int)(g - (int64_t)r * (ncols / 8)) * 8;
+    const f32x4* p = reinterpret_cast<const f32x4*>(P + (int64_t)r * ncols + c);
+    f32x4 a0 = __builtin_nontemporal_load(p), a1 = __builtin_nontemporal_load(p + 1);
+    for (int q = 1; q < parts; ++q) {
+      const f32x4* pq = reinterpret_cast<const f32x4*>(P + q * part_stride + (int64_t)r * ncols + c);
+      const f32x4 b0 = __builtin_nontemporal_load(pq), b1 = __builtin_nontemporal_load(pq + 1);
+      a0 += b0;
+      a1 += b1;
+    }
+    float v[8] = {a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]};
+    if (S) {
+      const f32x4* sp = reinterpret_cast<const f32x4*>(S + (int64_t)r * ldc + n1 + c);
+      const f32x4 s0 = __builtin_nontemporal_load(sp), s1 = __builtin_nontemporal_load(sp + 1);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        v[e] = s0[e] + v[e];
+        v[4 + e] = s1[e] + v[4 + e];
+      }
+    }
+    store_run8(C, ldc, out, r, n1 + c, v);
+  }
+}
+
+// Bytes of fp32 partials the plan of an [M, N] product over k_split K
+// columns needs (0 when it does not split K).
+int64_t split_bytes(int M, int N, int64_t k_split) {
+  if (M <= 0 || N <= 0 || k_split <= 0) return 0;
+  const Plan p = plan_bf16(M, N, true, k_split);
+  return p.parts > 1 ? (int64_t)p.parts * M * (N - p.n1) * 4 : 0;
+}
 
 // AKB: A is K-blocked by the plan's stage depth (see gemm_bf16_kernel), lda
-// its row count; the caller has checked the block.
+// its row count; the caller has checked the block.  With partials (fp32,
+// split_bytes(M, N, K) of them; EpiStore and EpiAdd only) the plan may split
+// K; without, it does not.
 template <bool AKB, class Epi>
 hipError_t dispatch_bf16(const uint16_t* A, int64_t lda, const uint16_t* B,
-                         int64_t ldb, int M, int N, int K, const Epi& epi, hipStream_t s) {
+                         int64_t ldb, int M, int N, int K, const Epi& epi, hipStream_t s,
+                         float* partials = nullptr) {
   if (M == 0 || N == 0) return hipSuccess;
   // tiles are addressed with 32-bit byte offsets: 256 rows of A, 64 of B
   // (K-blocked A tiles are at most 32 KiB)
   if ((!AKB && lda >= ((int64_t)1 << 22)) || ldb >= ((int64_t)1 << 24)) return hipErrorInvalidValue;
-  const Plan p = plan_bf16(M, N, AKB);
+  constexpr bool kSplittable = AKB && (std::is_same_v<Epi, EpiStore> || std::is_same_v<Epi, EpiAdd>);
+  const Plan p = plan_bf16(M, N, AKB, kSplittable && partials ? K : 0);
   hipError_t e = launch_kind<AKB>(p.k1, A, lda, B, ldb, M, 0, p.n1, K, epi, s);
-  if (e == hipSuccess && p.k2 >= 0) e = launch_kind<AKB>(p.k2, A, lda, B, ldb, M, p.n1, N, K, epi, s);
-  return e;
+  if (e != hipSuccess || p.k2 < 0) return e;
+  if constexpr (kSplittable) {
+    if (p.parts > 1) {
+      // the split rectangle is 256x256 tiles (plan_bf16)
+      const int ncols = N - p.n1;
+      const int64_t part_stride = (int64_t)M * ncols;
+      e = launch_bf16<256, 256, 2, 2, 2, 5, AKB>(A, lda, B, ldb, M, N, K,
+                                                 EpiPart{partials, ncols, part_stride, p.n1, 0},
+                                                 s, p.n1, p.parts, p.kpart);
+      if (e != hipSuccess) return e;
+      const float* S = nullptr;
+      void* C;
+      int64_t ldc;
+      int out;
+      if constexpr (std::is_same_v<Epi, EpiStore>) {
+        C = epi.C;
+        ldc = epi.ldc;
+        out = epi.out;
+      } else {
+        S = epi.S;
+        C = epi.out;
+        ldc = epi.ld;
+        out = epi.odt;
+      }
+      const int64_t groups = (int64_t)M * (ncols / 8);
+      const int64_t blocks = std::min<int64_t>((groups + 255) / 256, 8192);
+      hipLaunchKernelGGL(splitk_sum_kernel, dim3((unsigned)blocks), dim3(256), 0, s, partials,
+                         p.parts, part_stride, ncols, S, C, ldc, out, M, p.n1);
+      return hipGetLastError();
+    }
+  }
+  return launch_kind<AKB>(p.k2, A, lda, B, ldb, M, p.n1, N, K, epi, s);
 }
 
 // The paired product's tiles: 256x256 (three 48 KB slots) or 256x128 (four
@@ -1106,13 +1314,15 @@ int device_cu_count() {
   return n;
 }
 
-int gemm_bf16_a_block(int M, int N) { return a_block(M, N); }
+int gemm_bf16_a_block(int M, int N, int64_t k_split) { return a_block(M, N, k_split); }
+
+int64_t gemm_bf16_split_bytes(int M, int N, int64_t K) { return split_bytes(M, N, K); }
 
 hipError_t gemm_bf16_store_kb(const uint16_t* A, int kb, const uint16_t* B, int64_t ldb,
                               void* C, int64_t ldc, OutType out, int M, int N, int K,
-                              hipStream_t s) {
-  if (M > 0 && N > 0 && kb != a_block(M, N)) return hipErrorInvalidValue;
-  return dispatch_bf16<true>(A, M, B, ldb, M, N, K, EpiStore{C, ldc, (int)out}, s);
+                              float* partials, hipStream_t s) {
+  if (M > 0 && N > 0 && kb != a_block(M, N, partials ? K : 0)) return hipErrorInvalidValue;
+  return dispatch_bf16<true>(A, M, B, ldb, M, N, K, EpiStore{C, ldc, (int)out}, s, partials);
 }
 
 hipError_t kblock_bf16(const uint16_t* A, int64_t lda, uint16_t* out, int M, int K, int kb,
@@ -1132,7 +1342,7 @@ hipError_t kblock_bf16(const uint16_t* A, int64_t lda, uint16_t* out, int M, int
 hipError_t gemm_bf16_gelu_akb(const uint16_t* Akb, int kb, const uint16_t* B, int64_t ldb,
                               uint16_t* C, int M, int N, int K, int kb_out, hipStream_t s) {
   if (kb_out != 32 && kb_out != 64) return hipErrorInvalidValue;
-  if (M > 0 && N > 0 && kb != a_block(M, N)) return hipErrorInvalidValue;
+  if (M > 0 && N > 0 && kb != a_block(M, N, 0)) return hipErrorInvalidValue;
   const int sh = kb_out == 32 ? 5 : 6;
   return dispatch_bf16<true>(Akb, M, B, ldb, M, N, K, EpiGelu{C, 0, M, sh}, s);
 }
@@ -1174,9 +1384,9 @@ hipError_t gemm_bf16_qkv(const uint16_t* A, int64_t lda, const uint16_t* B,
 
 hipError_t gemm_bf16_add_kb(const uint16_t* A, int kb, const uint16_t* B, int64_t ldb,
                             const float* S, void* C, int64_t ldc, OutType out, int M, int N,
-                            int K, hipStream_t s) {
-  if (M > 0 && N > 0 && kb != a_block(M, N)) return hipErrorInvalidValue;
-  return dispatch_bf16<true>(A, M, B, ldb, M, N, K, EpiAdd{S, C, ldc, (int)out}, s);
+                            int K, float* partials, hipStream_t s) {
+  if (M > 0 && N > 0 && kb != a_block(M, N, partials ? K : 0)) return hipErrorInvalidValue;
+  return dispatch_bf16<true>(A, M, B, ldb, M, N, K, EpiAdd{S, C, ldc, (int)out}, s, partials);
 }
 
 hipError_t gemm_f32_add(const float* A, int64_t lda, const float* B, int64_t ldb,

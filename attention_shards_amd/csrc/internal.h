@@ -46,7 +46,7 @@ hipError_t gemm_bf16_gelu(const uint16_t* A, int64_t lda, const uint16_t* B,
                           int64_t ldb, uint16_t* C, int64_t ldc, int M, int N,
                           int K, int kb, hipStream_t s);
 // The same with A already K-blocked, [ceil(K/kb)][M][kb], kb =
-// gemm_bf16_a_block(M, N) (else hipErrorInvalidValue); C K-blocked by
+// gemm_bf16_a_block(M, N, 0) (else hipErrorInvalidValue); C K-blocked by
 // kb_out (32 or 64).
 hipError_t gemm_bf16_gelu_akb(const uint16_t* Akb, int kb, const uint16_t* B, int64_t ldb,
                               uint16_t* C, int M, int N, int K, int kb_out, hipStream_t s);
@@ -54,13 +54,20 @@ hipError_t gemm_bf16_gelu_akb(const uint16_t* Akb, int kb, const uint16_t* B, in
 // [ceil(K/kb)][M][kb] (kb = 32 or 64), zeros past K.  K, lda multiples of 8.
 hipError_t kblock_bf16(const uint16_t* A, int64_t lda, uint16_t* out, int M, int K, int kb,
                        hipStream_t s);
-// K block the kernel chosen for an [M, N] output reads a K-blocked A in.
-int gemm_bf16_a_block(int M, int N);
+// K block the kernel chosen for an [M, N] output reads a K-blocked A in;
+// k_split: K when the product is given fp32 partials for a split K (the
+// plan may then differ), else 0.
+int gemm_bf16_a_block(int M, int N, int64_t k_split);
+// Bytes of fp32 partials an [M, N] product over K may split K into (0: the
+// plan does not split it).
+int64_t gemm_bf16_split_bytes(int M, int N, int64_t K);
 // C = acc stored as `out` (row stride ldc), A K-blocked, [ceil(K/kb)][M][kb];
-// kb must be gemm_bf16_a_block(M, N) (else hipErrorInvalidValue).
+// kb must be gemm_bf16_a_block(M, N, partials ? K : 0) (else
+// hipErrorInvalidValue).  partials: nullptr, or gemm_bf16_split_bytes(M, N,
+// K) bytes (256-byte aligned) the call may use to split K.
 hipError_t gemm_bf16_store_kb(const uint16_t* A, int kb, const uint16_t* B, int64_t ldb,
                               void* C, int64_t ldc, OutType out, int M, int N, int K,
-                              hipStream_t s);
+                              float* partials, hipStream_t s);
 // C = (A_hi + A_lo) * B in one pass over K: every stage brings A_hi's and
 // A_lo's tiles and one B tile, both products use the same B fragments.  A2 is
 // K-blocked by 32, [2K/32][M][32] (A_hi's blocks, then A_lo's); K a multiple
@@ -123,11 +130,12 @@ hipError_t reduce_layernorm(const ReducePtrs& ptrs, int t, int pdt, const void* 
                             hipStream_t s);
 
 // C = S + A*B: the product added to an fp32 [M, N] matrix S (row stride
-// ldc, like C) and rounded once to the output type.  bf16 (A K-blocked as
-// for gemm_bf16_store_kb) and fp32 inputs (requirements of gemm_f32).
+// ldc, like C) and rounded once to the output type.  bf16 (A K-blocked and
+// partials as for gemm_bf16_store_kb) and fp32 inputs (requirements of
+// gemm_f32).
 hipError_t gemm_bf16_add_kb(const uint16_t* A, int kb, const uint16_t* B, int64_t ldb,
                             const float* S, void* C, int64_t ldc, OutType out, int M, int N,
-                            int K, hipStream_t s);
+                            int K, float* partials, hipStream_t s);
 hipError_t gemm_f32_add(const float* A, int64_t lda, const float* B, int64_t ldb,
                         const float* S, void* C, int64_t ldc, OutType out, int M, int N,
                         int K, hipStream_t s);

@@ -88,6 +88,14 @@ int64_t x_kblock_bytes(int64_t tokens, int64_t hidden, int64_t fs, int32_t in_dt
   if (in_dtype != TP_BF16 || fs < kXBlockMinCols) return 0;
   return (tokens * ((hidden + kZBlock - 1) / kZBlock * kZBlock) * 2 + 255) / 256 * 256;
 }
+
+// Bytes of the fp32 partials of GEMM2 when its plan splits K (bf16 inputs;
+// the dimensions have passed the ABI checks).
+int64_t split_partial_bytes(int64_t tokens, int64_t hidden, int64_t fs, int32_t in_dtype) {
+  if (in_dtype != TP_BF16 || tokens <= 0 || tokens > 2147483647 || hidden > 2147483647)
+    return 0;
+  return (tp::gemm_bf16_split_bytes((int)tokens, (int)hidden, fs) + 255) / 256 * 256;
+}
 constexpr int64_t kAttnHeadDim = 128;
 constexpr int64_t kAttnKeyTile = 64;
 
@@ -143,11 +151,13 @@ size_t tp_ffn_shard_workspace_bytes(int64_t tokens, int64_t hidden, int64_t ffn,
   if (tokens < 0 || hidden < 0 || ffn <= 0 || t < 1 || ffn % t != 0 || !valid_dtype(in_dtype))
     return 0;
   // bf16: GeLU(Z_i) K-blocked in blocks of up to 64 columns (kZBlock), then
-  // for wide shards the K-blocked copy of X
+  // for wide shards the K-blocked copy of X, then the fp32 partials of GEMM2
+  // when its plan splits K
   const int64_t fs = ffn / t;
   const int64_t cols = in_dtype == TP_BF16 ? (fs + kZBlock - 1) / kZBlock * kZBlock : fs;
   return (size_t)(align256(tokens * cols * esize(in_dtype)) +
-                  x_kblock_bytes(tokens, hidden, fs, in_dtype));
+                  x_kblock_bytes(tokens, hidden, fs, in_dtype) +
+                  split_partial_bytes(tokens, hidden, fs, in_dtype));
 }
 
 }  // extern "C"
@@ -270,27 +280,37 @@ hipError_t side_stream(int dev, SideStream** out) {
   return e;
 }
 
+// GEMM2's fp32 partials in the bf16 workspace, behind GeLU(Z_i) and the
+// K-blocked copy of X (nullptr when GEMM2's plan does not split K).
+float* split_partials(void* workspace, int64_t M, int64_t H, int64_t F, int32_t in_dtype) {
+  if (split_partial_bytes(M, H, F, in_dtype) == 0) return nullptr;
+  return reinterpret_cast<float*>(static_cast<char*>(workspace) +
+                                  align256(M * ((F + kZBlock - 1) / kZBlock * kZBlock) * 2) +
+                                  x_kblock_bytes(M, H, F, in_dtype));
+}
+
 // GEMM1 + GeLU into the workspace.  bf16: GeLU(Z_i) is stored K-blocked
 // in the block depth of the kernel GEMM2 will run (its A tiles are then
-// contiguous runs of memory); fp32: row-major.
+// contiguous runs of memory; GEMM2 is planned over its K = F, which may
+// split it); fp32: row-major.
 hipError_t ffn_gemm1(const void* X, const void* W1_i, int64_t ld_w1, void* workspace, int M,
                      int H, int F, int32_t in_dtype, hipStream_t s) {
   if (in_dtype == TP_BF16 && x_kblock_bytes(M, H, F, in_dtype) > 0) {
     // X copied K-blocked (in GEMM1's stage depth) behind GeLU(Z_i)
     uint16_t* xkb = reinterpret_cast<uint16_t*>(
         static_cast<char*>(workspace) + align256((int64_t)M * ((F + kZBlock - 1) / kZBlock * kZBlock) * 2));
-    const int kb1 = tp::gemm_bf16_a_block(M, F);
+    const int kb1 = tp::gemm_bf16_a_block(M, F, 0);
     hipError_t e = tp::kblock_bf16(static_cast<const uint16_t*>(X), H, xkb, M, H, kb1, s);
     if (e != hipSuccess) return e;
     return tp::gemm_bf16_gelu_akb(xkb, kb1, static_cast<const uint16_t*>(W1_i), ld_w1,
                                   static_cast<uint16_t*>(workspace), M, F, H,
-                                  tp::gemm_bf16_a_block(M, H), s);
+                                  tp::gemm_bf16_a_block(M, H, F), s);
   }
   if (in_dtype == TP_BF16)
     return tp::gemm_bf16_gelu(static_cast<const uint16_t*>(X), H,
                               static_cast<const uint16_t*>(W1_i), ld_w1,
                               static_cast<uint16_t*>(workspace), F, M, F, H,
-                              tp::gemm_bf16_a_block(M, H), s);
+                              tp::gemm_bf16_a_block(M, H, F), s);
   return tp::gemm_f32(static_cast<const float*>(X), H, static_cast<const float*>(W1_i), ld_w1,
                       workspace, F, tp::OUT_F32, true, M, F, H, s);
 }
@@ -320,8 +340,9 @@ tp_status_t tp_ffn_shard(const void* X, const void* W1_i, const void* W2_i,
     const tp::OutType ot = out_dtype == TP_F32 ? tp::OUT_F32 : tp::OUT_BF16;
     if (in_dtype == TP_BF16)
       e = tp::gemm_bf16_store_kb(static_cast<const uint16_t*>(workspace),
-                                 tp::gemm_bf16_a_block(M, H),
-                                 static_cast<const uint16_t*>(W2_i), H, Y_i, H, ot, M, H, F, s);
+                                 tp::gemm_bf16_a_block(M, H, F),
+                                 static_cast<const uint16_t*>(W2_i), H, Y_i, H, ot, M, H, F,
+                                 split_partials(workspace, M, H, F, in_dtype), s);
     else
       e = tp::gemm_f32(static_cast<const float*>(workspace), F,
                        static_cast<const float*>(W2_i), H, Y_i, H, ot, false, M, H, F, s);
@@ -407,9 +428,9 @@ tp_status_t tp_ffn_shard_reduce(const void* X, const void* W1_i, const void* W2_
     auto gemm2_store = [&]() {
       return in_dtype == TP_BF16
                  ? tp::gemm_bf16_store_kb(static_cast<const uint16_t*>(workspace),
-                                          tp::gemm_bf16_a_block(M, H),
+                                          tp::gemm_bf16_a_block(M, H, F),
                                           static_cast<const uint16_t*>(W2_i), H, out, H, ot, M,
-                                          H, F, s)
+                                          H, F, split_partials(workspace, M, H, F, in_dtype), s)
                  : tp::gemm_f32(static_cast<const float*>(workspace), F,
                                 static_cast<const float*>(W2_i), H, out, H, ot, false, M, H, F,
                                 s);
@@ -445,9 +466,9 @@ tp_status_t tp_ffn_shard_reduce(const void* X, const void* W1_i, const void* W2_
     if (e == hipSuccess)
       e = in_dtype == TP_BF16
               ? tp::gemm_bf16_add_kb(static_cast<const uint16_t*>(workspace),
-                                     tp::gemm_bf16_a_block(M, H),
+                                     tp::gemm_bf16_a_block(M, H, F),
                                      static_cast<const uint16_t*>(W2_i), H, S, out, H, ot, M, H,
-                                     F, s)
+                                     F, split_partials(workspace, M, H, F, in_dtype), s)
               : tp::gemm_f32_add(static_cast<const float*>(workspace), F,
                                  static_cast<const float*>(W2_i), H, S, out, H, ot, M, H, F, s);
     return hip_status(e, "tp_ffn_shard_reduce: launch");

@@ -101,8 +101,14 @@ typedef enum {
  *                                   fp32 row-major; with bf16 inputs and
  *                                   ffn/t >= 20480 also a K-blocked copy of X
  *                                   (tokens x hidden rounded up to 64 columns)
- *                                   that the first GEMM reads; contents are not
- *                                   part of the interface
+ *                                   that the first GEMM reads, and, when the
+ *                                   second GEMM's tile plan splits its K
+ *                                   (ffn/t) into parts, their fp32 partial
+ *                                   products (parts x tokens x the split
+ *                                   columns); contents are not part of the
+ *                                   interface.  The size depends on the
+ *                                   current device's compute-unit count (the
+ *                                   tile plans do)
  * Shape rules: tokens >= 0 (0 enqueues nothing); hidden and ffn/t multiples
  * of 8 (bf16) or 4 (fp32); ld_w1 >= ffn/t and a multiple of the same; every
  * dimension below 2^31; with bf16 inputs also hidden, ffn/t < 2^22 and
@@ -136,10 +142,11 @@ tp_status_t tp_ffn_shard(const void* X, const void* W1_i, const void* W2_i,
  *     device also looks up the array's device address (a failure there is
  *     TP_ERR_HIP).  A rejected call enqueues nothing.
  *   - Every call on one GPU shares that GPU's array, which keeps the last
- *     call's contents (nothing in it needs to start at zero: GeLU(Z_i) is
- *     written in full before it is read).  Calls that overlap in time on
- *     one GPU (different streams or host threads without ordering) race on
- *     it: order them on one stream.
+ *     call's contents (nothing in it needs to start at zero: GeLU(Z_i) and
+ *     any partial products of a split K are written in full before they
+ *     are read).  Calls that overlap in time on one GPU (different streams
+ *     or host threads without ordering) race on it: order them on one
+ *     stream.
  */
 #define TP_FFN_NOALLOC_MAX_WORKSPACE ((size_t)64 << 20)
 

@@ -74,10 +74,21 @@ def test_workspace_queries(lib):
     # rounded up to 64 columns): 2048 x 22528 x 2 after GeLU(Z) of 2048 x 90112
     assert lib.tp_ffn_shard_workspace_bytes(2048, 22528, 90112, 1, B.TP_BF16) == \
         2048 * 90112 * 2 + 2048 * 22528 * 2
+    # ... and, when GEMM2's plan splits K (here [100 x 1000] over 20480 or
+    # 20472 columns: 256x256 tiles over 8 parts of K), its fp32 partials
+    split = 8 * 100 * 1000 * 4
     assert lib.tp_ffn_shard_workspace_bytes(100, 1000, 20480, 1, B.TP_BF16) == \
-        (100 * 20480 * 2 + 255) // 256 * 256 + (100 * 1024 * 2 + 255) // 256 * 256
+        (100 * 20480 * 2 + 255) // 256 * 256 + (100 * 1024 * 2 + 255) // 256 * 256 + split
     assert lib.tp_ffn_shard_workspace_bytes(100, 1000, 20472 * 2, 2, B.TP_BF16) == \
-        (100 * 20480 * 2 + 255) // 256 * 256                     # 20472 < 20480 columns
+        (100 * 20480 * 2 + 255) // 256 * 256 + split             # 20472 < 20480 columns
+    # the hidden-10240 t=1 sweep shard: GEMM2 [2048 x 10240] over K = 40960
+    # runs one wave of 256x256 tiles over 8192 columns and the other 2048
+    # columns as 256x256 tiles over 4 parts of K
+    assert lib.tp_ffn_shard_workspace_bytes(2048, 10240, 40960, 1, B.TP_BF16) == \
+        2048 * 40960 * 2 + 2048 * 10240 * 2 + 4 * 2048 * 2048 * 4
+    # a wave of full tiles leaves nothing to split (the t=8 hidden-4096 shard,
+    # the headline hidden-22528 shard above)
+    assert lib.tp_ffn_shard_workspace_bytes(4096, 4096, 16384, 8, B.TP_BF16) == 4096 * 2048 * 2
     assert lib.tp_ffn_shard_workspace_bytes(10, 8, 20, 3, B.TP_BF16) == 0    # t does not divide f
     assert lib.tp_ffn_shard_workspace_bytes(10, 8, 16, 0, B.TP_BF16) == 0
     # attention: 4 x [heads, seq_pad, 128] (Q, K, V^T hi, V^T lo) + O hi/lo [tokens, 2*nl*128], 16-bit,
@@ -367,13 +378,17 @@ def test_ffn_noalloc_limit_matches_header(lib):
     m = re.search(r"#define TP_FFN_NOALLOC_MAX_WORKSPACE \(\(size_t\)(\d+) << (\d+)\)",
                   header_text())
     assert int(m.group(1)) << int(m.group(2)) == B.TP_FFN_NOALLOC_MAX_WORKSPACE
-    # 2048 tokens x 16384 bf16 columns of GeLU(Z) fill the 64 MiB exactly;
+    # 2048 tokens x 16384 bf16 columns of GeLU(Z) fill the 64 MiB exactly
+    # (hidden 8192: GEMM2 is one wave of 256x256 tiles, no split K);
     # 2048 x 16448 do not fit, nor do 1024 x 22528 (44 MiB of GeLU(Z) plus
-    # the K-blocked copy of 1024 x 16384 X, 32 MiB)
+    # the K-blocked copy of 1024 x 16384 X, 32 MiB), nor 2048 x 16384 with
+    # hidden 64 (GEMM2 then splits K: 4 MiB of partials on top)
+    assert lib.tp_ffn_shard_workspace_bytes(2048, 8192, 16384, 1, B.TP_BF16) == \
+        B.TP_FFN_NOALLOC_MAX_WORKSPACE
+    assert lib.tp_ffn_shard_workspace_bytes(2048, 8192, 16448, 1, B.TP_BF16) > \
+        B.TP_FFN_NOALLOC_MAX_WORKSPACE
     assert lib.tp_ffn_shard_workspace_bytes(2048, 64, 16384, 1, B.TP_BF16) == \
-        B.TP_FFN_NOALLOC_MAX_WORKSPACE
-    assert lib.tp_ffn_shard_workspace_bytes(2048, 64, 16448, 1, B.TP_BF16) > \
-        B.TP_FFN_NOALLOC_MAX_WORKSPACE
+        B.TP_FFN_NOALLOC_MAX_WORKSPACE + 8 * 2048 * 64 * 4
     assert lib.tp_ffn_shard_workspace_bytes(1024, 16384, 22528, 1, B.TP_BF16) == \
         1024 * 22528 * 2 + 1024 * 16384 * 2 > B.TP_FFN_NOALLOC_MAX_WORKSPACE
 

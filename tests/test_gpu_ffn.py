@@ -232,6 +232,39 @@ def test_layer_emulation_t4(gpu):
     assert e2 <= TOL_BF16
 
 
+def _split_bytes(gpu, M, h, f, t):
+    """Bytes of the second product's fp32 partials in the workspace (0 when
+    its plan does not split K): the workspace size less GeLU(Z_i) and the
+    K-blocked copy of X."""
+    fs = f // t
+    z = (M * ((fs + 63) // 64 * 64) * 2 + 255) // 256 * 256
+    x = (M * ((h + 63) // 64 * 64) * 2 + 255) // 256 * 256 if fs >= 20480 else 0
+    return gpu.tp_ffn_shard_workspace_bytes(M, h, f, t, gpu.TP_BF16) - z - x
+
+
+@pytest.mark.parametrize("M,h,f,t,i,nrows", [
+    (1000, 1000, 8200, 1, 0, None),    # all columns over 8 parts of K; ragged rows, columns, K
+    (300, 72, 2 * 6000, 2, 1, None),   # one ragged column of tiles, 72 of 256 columns, 8 parts
+    (2048, 8448, 8192, 1, 0, 64),      # a wave of full tiles over 8192 columns, then 8 parts
+])
+def test_split_k_second_product(gpu, M, h, f, t, i, nrows):
+    """Second products whose plan splits K: 256x256 tiles over parts of K,
+    each part's fp32 product in the workspace, summed in part order into Y.
+    Against the oracle (all rows, or nrows seeded rows), and bit for bit
+    over two calls."""
+    assert _split_bytes(gpu, M, h, f, t) > 0
+    d = syn.make_ffn_inputs(900 + M, M, h, f, syn.BF16)
+    got = run_shard(gpu, d, i, t, syn.F32, view=False)
+    again = run_shard(gpu, d, i, t, syn.F32, view=False)
+    assert np.array_equal(got, again)
+    rows = None if nrows is None else syn.sample_rows(900 + M, M, nrows)
+    ref = oracle_shard(d, i, t, rows)
+    e = rel_err(got if rows is None else got[rows], ref)
+    log(f"split K M={M} h={h} f={f} t={t} i={i}: err {e:.4f} "
+        f"({_split_bytes(gpu, M, h, f, t)} bytes of partials)")
+    assert e <= TOL_BF16
+
+
 def test_deterministic(gpu):
     d = syn.make_ffn_inputs(7, 1000, 1024, 4096, syn.BF16)
     a = run_shard(gpu, d, 1, 2, syn.BF16)
@@ -246,6 +279,7 @@ def test_deterministic(gpu):
     # over K = 1000), so the arithmetic is checked in fp32 (test_bf16_ragged)
     # and the bf16 store here, bit for bit
     (4000, 4000, 2 * 1000, 2, 1, 4100),
+    (1000, 1000, 8200, 1, 0, 4101),   # split K: the sum of the partials stores bf16
 ])
 def test_bf16_output_is_rne_of_fp32_output(gpu, M, h, f, t, i, seed):
     """The bf16-output epilogue rounds to nearest even: the same shard (the

@@ -51,6 +51,7 @@ def oracle_out(d, i, t, peers_np, pdt, R_np, rdt, rows=None):
     (257, 264, 4 * 136, 4, 0, syn.F32, syn.F32, syn.F32),
     (130, 512, 2 * 512, 2, 1, syn.BF16, None, syn.BF16),      # no residual, bf16 out
     (64, 128, 512, 1, 0, syn.BF16, syn.BF16, syn.F32),        # t=1: out = P_0 + R
+    (1000, 1000, 2 * 8200, 2, 1, syn.BF16, syn.BF16, syn.F32),  # GEMM2 splits K: S + partials
 ])
 def test_fused_matches_oracle(gpu, M, h, f, t, i, pdt, rdt, odt):
     d = syn.make_ffn_inputs(700 + M, M, h, f, syn.BF16, residual=rdt is not None)

@@ -1,8 +1,9 @@
 """tp_ffn_shard_noalloc (the FFN shard without a workspace, for callers that
 cannot allocate) against tp_ffn_shard, through the C ABI: the same kernels,
-so the outputs must agree bit for bit.  Two calls in a row, the second with
-a smaller input (the array keeps the first call's contents), then a shape
-whose GeLU(Z_i) does not fit the array, which must be rejected."""
+so the outputs must agree bit for bit.  Calls in a row, each with a smaller
+input than the one before (the array keeps the previous call's contents),
+then a shape whose GeLU(Z_i) does not fit the array, which must be
+rejected."""
 import numpy as np
 import pytest
 import torch
@@ -24,7 +25,10 @@ def _inputs(seed, M, h, f, i, t, dtype):
 
 @pytest.mark.parametrize("dtype,out", [(syn.BF16, syn.BF16), (syn.F32, syn.F32)])
 def test_noalloc_matches_workspace_entry_point(gpu, dtype, out):
-    shapes = [(4096, 1024, 8192, 3, 8, 11), (300, 200, 3 * 424, 1, 3, 12)]
+    # the first shape's second product splits K (its fp32 partials sit in the
+    # array behind GeLU(Z_i))
+    shapes = [(1000, 1000, 8200, 0, 1, 15), (4096, 1024, 8192, 3, 8, 11),
+              (300, 200, 3 * 424, 1, 3, 12)]
     if dtype == syn.F32:
         shapes = [(1000, 512, 4 * 512, 2, 4, 13), (77, 100, 2 * 52, 1, 2, 14)]
     for M, h, f, i, t, seed in shapes:
