@@ -784,6 +784,56 @@ def summarize_attn_profile(trace_csv, cmd):
     print(f"wrote attention profile ({len(calls)} calls, median {med:.1f} us)")
 
 
+def summarize_layer_profile(trace_csv, cmd):
+    """Write profiles/kernel_stats_layer_t4_h12288.md from a rocprofv3 kernel
+    trace of `bench.py --layer-only`: every kernel of the layer row (four
+    attention shards, their sum, the bf16 copy of X1, four FFN shards, their
+    sum), grouped by kernel and grid, per layer call (the trace's calls
+    counted by the FFN shards' GeLU products, four per layer)."""
+    import csv
+    import statistics
+    rows = list(csv.DictReader(open(trace_csv)))
+    wg = lambda r: int(r["Grid_Size_X"]) // int(r["Workgroup_Size_X"])
+    dur = lambda r: (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3
+    per = {}
+    for r in rows:
+        if "at::" in r["Kernel_Name"]:
+            continue      # the row's input generation (torch kernels)
+        per.setdefault((_short(r["Kernel_Name"]), wg(r)), []).append(dur(r))
+    n_layers = sum(len(v) for (n, g), v in per.items() if "EpiGelu" in n) // 4
+    total = sum(sum(v) for v in per.values()) / n_layers
+    roles = [("EpiQkv", "attention: QKV projection [8192 x 12288] x [12288 x 9216]"),
+             ("attn_fwd", "attention: causal attention, 24 local heads, 256-query blocks"),
+             ("attn_combine", "attention: merge of split query blocks"),
+             ("EpiStore, true, 2", "attention: output projection (O hi/lo) [8192 x 3072] x [3072 x 12288]"),
+             ("EpiGelu", "FFN: GEMM1 + GeLU [8192 x 12288] x [12288 x 12288]"),
+             ("EpiStore", "FFN: GEMM2 [8192 x 12288] x [12288 x 12288]"),
+             ("reduce_kernel<0, 1, 0", "sum: 4 fp32 attention partials + X (bf16) -> X1 (fp32)"),
+             ("reduce_kernel<1, 0, 0", "sum: 4 bf16 FFN partials + X1 -> X2 (fp32)"),
+             ("reduce_kernel<0, 2, 1", "copy: X1 -> bf16, the FFN input"),
+             ("vt_pad", "attention: zero the V^T padding")]
+    lines = ["# Kernel durations: one transformer layer on one GPU, t=4 "
+             "(hidden 12288, 96 heads of 128, ffn 49152, 4 x 2048 causal tokens)", "",
+             "Command (from the repository root, on one MI355X):", "", "```", cmd, "```", "",
+             f"Per-dispatch durations from the kernel trace, grouped by kernel and grid; "
+             f"{n_layers} layer calls (warm-up and timed) in the trace. Per layer: the "
+             "kernel's dispatches per layer call and their summed time.", "",
+             "| kernel | role | workgroups | per layer | avg us | us per layer | share |",
+             "|---|---|---:|---:|---:|---:|---:|"]
+    for (n, g), v in sorted(per.items(), key=lambda kv: -sum(kv[1])):
+        r = next((t for key, t in roles if key in n), "")
+        lines.append(f"| `{n}` | {r} | {g} | {len(v) / n_layers:.0f} | "
+                     f"{statistics.mean(v):.1f} | {sum(v) / n_layers:.0f} | "
+                     f"{sum(v) / n_layers / total:.1%} |")
+    fl = 4 * attn_flops(4, 2048, 12288, 96, 128, 4) + 4 * ffn_flops(8192, 12288, 49152, 4)
+    lines += ["", f"Kernel time per layer: {total / 1e3:.2f} ms for {fl / 1e12:.2f} TFLOP "
+              f"algorithmic, {fl / (total * 1e-6) / 1e12:.0f} TFLOP/s "
+              f"({fl / (total * 1e-6) / 1e12 / PEAK_BF16_TFLOPS:.1%} of the bf16 MFMA peak)."]
+    with open(os.path.join(ROOT, "profiles", "kernel_stats_layer_t4_h12288.md"), "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print(f"wrote layer profile ({n_layers} layers, {total / 1e3:.2f} ms of kernels per layer)")
+
+
 # First products of FFN shards (t = 1) whose tile plans are single kinds of
 # one tile per CU: [tokens, ffn] -> 128x192, 256x192, 256x256 and 256x128
 # tiles (X read as given: the K = 32 kinds through A pairs); K (the hidden
@@ -1017,6 +1067,9 @@ def main():
                     help="time the attention shard row only (profiling runs)")
     ap.add_argument("--step-only", action="store_true",
                     help="time the t=8 hidden-4096 FFN step row only (profiling runs)")
+    ap.add_argument("--layer-only", action="store_true",
+                    help="time the whole-layer row only (profiling runs)")
+    ap.add_argument("--summarize-layer-profile", metavar="KERNEL_TRACE_CSV", default=None)
     ap.add_argument("--summarize-clock-counters", nargs="+", metavar="CSV",
                     help="COUNTER_CSV TRACE_CSV pairs (one per run): write the per-kernel "
                          "MFMA-utilisation / clock table")
@@ -1043,6 +1096,9 @@ def main():
         return
     if args.summarize_attn_profile:
         summarize_attn_profile(args.summarize_attn_profile, args.profile_commands[0])
+        return
+    if args.summarize_layer_profile:
+        summarize_layer_profile(args.summarize_layer_profile, args.profile_commands[0])
         return
     if args.summarize_sweep:
         summarize_sweep(args.summarize_sweep, args.profile_commands[0])
@@ -1084,6 +1140,9 @@ def main():
         return
     if args.step_only:
         log(json.dumps(ffn_step_row(K, W, fused=False)[0]))
+        return
+    if args.layer_only:
+        log(json.dumps(layer_row(K, W)))
         return
     if args.tile_sweep:
         tile_sweep(args.tile_sweep_k)
