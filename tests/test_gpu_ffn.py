@@ -265,6 +265,27 @@ def test_split_k_second_product(gpu, M, h, f, t, i, nrows):
     assert e <= TOL_BF16
 
 
+# Shapes drawn at random (rows from a fixed menu, hidden below 3000 and ffn
+# between 1024 and 22000 in multiples of 8) among those whose second
+# product's plan splits K on a 256-CU device.
+SPLIT_RANDOM = [(1500, 752, 19968), (257, 824, 14456), (257, 2184, 9056),
+                (1500, 1456, 14648), (255, 1272, 18840), (255, 2824, 16376)]
+
+
+@pytest.mark.parametrize("M,h,f", SPLIT_RANDOM)
+def test_split_k_random_shapes(gpu, M, h, f):
+    """Odd shapes through the split-K plans (t=1): 16 seeded rows against
+    the oracle."""
+    if torch.cuda.get_device_properties(0).multi_processor_count == 256:
+        assert _split_bytes(gpu, M, h, f, 1) > 0
+    d = syn.make_ffn_inputs(950 + M + h, M, h, f, syn.BF16)
+    got = run_shard(gpu, d, 0, 1, syn.F32, view=False)
+    rows = syn.sample_rows(950 + M, M, 16)
+    e = rel_err(got[rows], oracle_shard(d, 0, 1, rows))
+    log(f"split K random M={M} h={h} f={f}: err {e:.4f}")
+    assert e <= TOL_BF16
+
+
 def test_deterministic(gpu):
     d = syn.make_ffn_inputs(7, 1000, 1024, 4096, syn.BF16)
     a = run_shard(gpu, d, 1, 2, syn.BF16)
