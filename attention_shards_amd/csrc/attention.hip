@@ -294,6 +294,9 @@ attn_fwd_kernel(QkvOut q, int causal, uint16_t* __restrict__ O, int o_kbs,
     for (int dc = 0; dc < 4; ++dc) {
       const int set = dc & 1;
       if (dc + 1 < 4) kread(set ^ 1, dc + 1);
+      // keep the next reads ahead of this step's MFMAs (the compiler would
+      // otherwise sink each read to just before its use and wait on it)
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int kc = 0; kc < 2; ++kc)
 #pragma unroll
@@ -391,6 +394,7 @@ attn_fwd_kernel(QkvOut q, int causal, uint16_t* __restrict__ O, int o_kbs,
     for (int grp = 0; grp < 4; ++grp) {
       const int set = grp & 1, kc = grp >> 1;
       if (grp + 1 < 4) vread(set ^ 1, grp + 1);
+      __builtin_amdgcn_sched_barrier(0);  // (as for the K fragments above)
 #pragma unroll
       for (int pass = 0; pass < 2; ++pass)
 #pragma unroll
