@@ -56,6 +56,20 @@ typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
+
+// Maximum of x over lanes l, l^16, l^32 and l^48 (the four 16-lane rows of
+// the wave), by two register swaps across the rows instead of LDS
+// permutes: permlane32_swap pairs lane l with l^32, permlane16_swap with
+// l^16; with the same register as both operands each returned half holds
+// one side of every pair.
+__device__ __forceinline__ float max_of_four_rows(float x) {
+  const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                  false);
+  x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                  false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int D = 128;    // head dim
@@ -352,8 +366,7 @@ attn_fwd_kernel(QkvOut q, int causal, uint16_t* __restrict__ O, int o_kbs,
 #pragma unroll
             for (int e = 0; e < 4; ++e) mt = fmaxf(mt, s[qg][kc][hb][e]);
       }
-      mt = fmaxf(mt, __shfl_xor(mt, 16));
-      mt = fmaxf(mt, __shfl_xor(mt, 32));
+      mt = max_of_four_rows(mt);
       const float m_new = fmaxf(m_run[qg], mt * scale_log2);
       const float m_use = (m_new == -__builtin_inff()) ? 0.0f : m_new;
       // probabilities rounded to fp16 in pairs; the denominator adds exactly
