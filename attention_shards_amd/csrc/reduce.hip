@@ -248,15 +248,39 @@ hipError_t partial_reduce(const ReducePtrs& ptrs, int t, int pdt, const void* R,
 // group costs a few memory round trips, not one per partial; the sum follows
 // the fixed order P_0 + ... + P_{t-1} + R in fp32 and the row stays in
 // registers.  Mean, then the biased variance of (x - mean), each a
-// fixed-order block sum (wave shuffles, then the waves' sums in order);
-// y = (x - mean) * rsqrt(var + eps) * gamma + beta.  HBM-bound: t partials
-// and the residual read, x and y written.
+// fixed-order block sum (lane swaps within each wave, then the waves' sums in
+// order); y = (x - mean) * rsqrt(var + eps) * gamma + beta.  HBM-bound: t
+// partials and the residual read, x and y written.
 // ---------------------------------------------------------------------------
 namespace {
 
+template <int Ctrl>
+__device__ __forceinline__ float dpp_mov(float x) {
+  return __builtin_bit_cast(
+      float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), Ctrl, 0xf, 0xf, false));
+}
+
+// Sum of v over the wave's 64 lanes, the same bits in every lane: within each
+// 16-lane row by DPP rotations (8, 4) and quad permutations (pairs 2 apart,
+// then 1 apart), then across rows by a permlane16 and a permlane32 swap.
+// Each step adds two lanes' values that the partner lane adds too, so all
+// lanes agree bit for bit; no LDS round trip (the xor shuffles this replaces
+// were six ds_bpermute waits per sum).
+__device__ __forceinline__ float wave_sum(float v) {
+  v += dpp_mov<0x128>(v);  // row_ror:8
+  v += dpp_mov<0x124>(v);  // row_ror:4
+  v += dpp_mov<0x4E>(v);   // quad_perm [2,3,0,1]
+  v += dpp_mov<0xB1>(v);   // quad_perm [1,0,3,2]
+  const auto a =
+      __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  const auto b =
+      __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+
 __device__ __forceinline__ float block_sum(float v, float* red, int nw) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o);
+  v = wave_sum(v);
   __syncthreads();  // red[] free (a previous sum's readers are done)
   if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
   __syncthreads();
