@@ -62,6 +62,11 @@ tp_status_t hip_status(hipError_t e, const char* what) {
 }
 
 constexpr int64_t kInt32Max = 2147483647;
+// Largest element count of one operand: its byte extent (at most 4 bytes an
+// element) then stays far inside int64, also for fp32 dimensions, which are
+// otherwise bounded only by 2^31 - 1 each.
+constexpr int64_t kMaxElems = int64_t(1) << 60;
+bool fits(int64_t a, int64_t b) { return a <= 0 || b <= kMaxElems / a; }
 // The bf16 GEMMs address a tile through a buffer descriptor with 32-bit byte
 // offsets: up to 256 rows of A (row stride lda) and 64 rows of B (ldb) per
 // tile, so lda < 2^22 and ldb < 2^24 elements.  The attention kernel reads
@@ -100,6 +105,19 @@ constexpr int64_t kAttnHeadDim = 128;
 constexpr int64_t kAttnKeyTile = 64;
 
 int64_t align256(int64_t b) { return (b + 255) / 256 * 256; }
+
+// The attention shapes the kernels address (checked by tp_attn_shard before
+// anything else uses them, and by its workspace query): tokens and the
+// (sequence, head, key tile) count within int32, V^T rows of seq_pad keys
+// and the [Q | K | V] and O row widths within the 32-bit buffer offsets.
+bool attn_shape_ok(int64_t batch, int64_t seq, int64_t nl) {
+  if (batch < 0 || seq < 0 || nl < 1 || batch > kInt32Max || nl > kInt32Max) return false;
+  if (seq > 0 && batch > kInt32Max / seq) return false;  // tokens
+  const int64_t seq_pad = (seq + kAttnKeyTile - 1) / kAttnKeyTile * kAttnKeyTile;
+  return 3 * nl * kAttnHeadDim <= kInt32Max && 2 * nl * kAttnHeadDim < kMaxLdA &&
+         seq_pad < kMaxSeqPad && batch * nl <= kInt32Max &&
+         batch * nl * (seq_pad / kAttnKeyTile) <= kInt32Max;
+}
 
 // Attention workspace: four [batch*nl, seq_pad, d] 16-bit arrays (Q, K in
 // fp16, V^T as an fp16 hi/lo pair) followed by O [batch*seq, 2*nl*d] bf16
@@ -155,6 +173,10 @@ size_t tp_ffn_shard_workspace_bytes(int64_t tokens, int64_t hidden, int64_t ffn,
   // when its plan splits K
   const int64_t fs = ffn / t;
   const int64_t cols = in_dtype == TP_BF16 ? (fs + kZBlock - 1) / kZBlock * kZBlock : fs;
+  // shapes tp_ffn_shard rejects for their size (0, not a wrapped product)
+  if (tokens > kInt32Max || hidden > kInt32Max || fs > kInt32Max || !fits(tokens, cols) ||
+      !fits(tokens, hidden))
+    return 0;
   return (size_t)(align256(tokens * cols * esize(in_dtype)) +
                   x_kblock_bytes(tokens, hidden, fs, in_dtype) +
                   split_partial_bytes(tokens, hidden, fs, in_dtype));
@@ -194,6 +216,8 @@ tp_status_t check_ffn(const char* fn, const void* X, const void* W1_i, const voi
                 fn, i, (long long)hidden, (long long)fs, (long long)*ld_w1, (long long)vec);
   if (tokens > kInt32Max || hidden > kInt32Max || fs > kInt32Max)
     return fail(TP_ERR_SHAPE, "%s(i=%d): a dimension exceeds 2^31-1", fn, i);
+  if (!fits(tokens, hidden) || !fits(hidden, *ld_w1) || !fits(tokens, fs))
+    return fail(TP_ERR_SHAPE, "%s(i=%d): an operand exceeds 2^60 elements", fn, i);
   if (in_dtype == TP_BF16 && (hidden >= kMaxLdA || fs >= kMaxLdA || *ld_w1 >= kMaxLdB))
     return fail(TP_ERR_SHAPE,
                 "%s(i=%d): bf16 needs hidden and ffn/t below 2^22 and ld_w1 below 2^24 "
@@ -482,7 +506,9 @@ tp_status_t tp_ffn_shard_reduce(const void* X, const void* W1_i, const void* W2_
 // ---------------------------------------------------------------------------
 size_t tp_attn_shard_workspace_bytes(int64_t batch, int64_t seq, int32_t n_heads,
                                      int32_t head_dim, int32_t t) {
-  if (batch < 0 || seq < 0 || n_heads < 1 || head_dim < 1 || t < 1 || n_heads % t) return 0;
+  if (batch < 0 || seq < 0 || n_heads < 1 || head_dim != kAttnHeadDim || t < 1 || n_heads % t ||
+      !attn_shape_ok(batch, seq, n_heads / t))
+    return 0;
   return (size_t)attn_layout(batch, seq, n_heads / t, head_dim).total;
 }
 
@@ -515,16 +541,13 @@ tp_status_t tp_attn_shard(const void* X, const void* Wqkv_i, const void* Wo_i,
       return fail(TP_ERR_SHAPE, "tp_attn_shard(i=%d): hidden=%lld must be a multiple of 8", i,
                   (long long)hidden);
     const int64_t nl = n_heads / t;
-    const int64_t tokens = batch * seq;
-    if (tokens > kInt32Max || hidden > kInt32Max || 3 * nl * head_dim > kInt32Max ||
-        batch * nl * ((seq + 63) / 64) > kInt32Max)
-      return fail(TP_ERR_SHAPE, "tp_attn_shard(i=%d): a dimension exceeds 2^31-1", i);
-    if (hidden >= kMaxLdA || 2 * nl * head_dim >= kMaxLdA ||
-        (seq + kAttnKeyTile - 1) / kAttnKeyTile * kAttnKeyTile >= kMaxSeqPad)
+    if (hidden >= kMaxLdA || !attn_shape_ok(batch, seq, nl))
       return fail(TP_ERR_SHAPE,
-                  "tp_attn_shard(i=%d): needs hidden and 2*(n_heads/t)*head_dim below 2^22 and "
-                  "seq below 2^23 (hidden=%lld n_heads/t=%lld seq=%lld)",
-                  i, (long long)hidden, (long long)nl, (long long)seq);
+                  "tp_attn_shard(i=%d): needs batch*seq and batch*(n_heads/t)*ceil(seq/64) "
+                  "within 2^31-1, hidden and 2*(n_heads/t)*head_dim below 2^22 and seq below "
+                  "2^23 (batch=%lld seq=%lld hidden=%lld n_heads/t=%lld)",
+                  i, (long long)batch, (long long)seq, (long long)hidden, (long long)nl);
+    const int64_t tokens = batch * seq;
     if (tokens == 0) return ok();
     if (!X || !Wqkv_i || !Wo_i || !Y_i)
       return fail(TP_ERR_NULL, "tp_attn_shard(i=%d): NULL tensor pointer", i);

@@ -111,8 +111,11 @@ typedef enum {
  *                                   tile plans do)
  * Shape rules: tokens >= 0 (0 enqueues nothing); hidden and ffn/t multiples
  * of 8 (bf16) or 4 (fp32); ld_w1 >= ffn/t and a multiple of the same; every
- * dimension below 2^31; with bf16 inputs also hidden, ffn/t < 2^22 and
- * ld_w1 < 2^24 (row strides the GEMM tiles address with 32-bit offsets).
+ * dimension below 2^31 and tokens*hidden, hidden*ld_w1, tokens*(ffn/t) at
+ * most 2^60; with bf16 inputs also hidden, ffn/t < 2^22 and ld_w1 < 2^24
+ * (row strides the GEMM tiles address with 32-bit offsets).  The size query
+ * returns 0 for an unknown dtype, t < 1 or not dividing ffn, a negative
+ * dimension, or one beyond these products and 2^31 limits.
  * Y_i must not overlap X, W1_i, W2_i or the workspace (TP_ERR_ALIAS).
  * The shard index i only selects which pointers the caller passes; it is
  * validated and reported in error messages.
@@ -184,8 +187,10 @@ tp_status_t tp_ffn_shard_noalloc(const void* X, const void* W1_i, const void* W2
  * range (|value| < 65504).  The workspace size depends on the current
  * device's compute-unit count (the attention work split does).
  * Shape rules: batch, seq >= 0; head_dim == 128; hidden multiple of 8;
- * batch*seq below 2^31; hidden and 2*(n_heads/t)*head_dim below 2^22; seq
- * below 2^23 (32-bit tile offsets in the GEMMs and the attention kernel).
+ * batch, batch*seq and batch*(n_heads/t)*ceil(seq/64) below 2^31; hidden and
+ * 2*(n_heads/t)*head_dim below 2^22; seq below 2^23 (32-bit tile offsets in
+ * the GEMMs and the attention kernel).  The size query returns 0 for any
+ * shape these rules (or n_heads % t, head_dim) reject.
  */
 size_t tp_attn_shard_workspace_bytes(int64_t batch, int64_t seq, int32_t n_heads,
                                      int32_t head_dim, int32_t t);

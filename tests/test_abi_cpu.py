@@ -106,6 +106,23 @@ def test_workspace_queries(lib):
     assert lib.tp_attn_shard_workspace_bytes(1, 8, 6, 128, 4) == 0
 
 
+def test_workspace_queries_reject_what_the_calls_reject(lib):
+    """Shapes the entry points refuse for their size give 0, never a
+    wrapped product (and the attention query never plans such a shape)."""
+    big = (1 << 31) - 4
+    assert lib.tp_ffn_shard_workspace_bytes(1 << 31, 64, 128, 1, B.TP_BF16) == 0
+    assert lib.tp_ffn_shard_workspace_bytes(big, big, 2 * big, 2, B.TP_F32) == 0
+    assert lib.tp_ffn_shard_workspace_bytes(1 << 40, 8, 1 << 40, 1 << 10, B.TP_F32) == 0
+    assert lib.tp_ffn_shard_reduce_workspace_bytes(big, big, 2 * big, 2, B.TP_F32) == 0
+    assert lib.tp_attn_shard_workspace_bytes(1 << 20, 1 << 12, 8, 128, 1) == 0
+    assert lib.tp_attn_shard_workspace_bytes(1 << 40, 0, 8, 128, 1) == 0
+    assert lib.tp_attn_shard_workspace_bytes(1, 1 << 23, 8, 128, 1) == 0
+    assert lib.tp_attn_shard_workspace_bytes(1, 1 << 22, 1 << 14, 128, 1) == 0
+    assert lib.tp_attn_shard_workspace_bytes(1, 2048, 8, 64, 1) == 0
+    # the largest accepted sequence still has a size
+    assert lib.tp_attn_shard_workspace_bytes(1, (1 << 23) - 64, 1, 128, 1) > 0
+
+
 # fake, 16-byte aligned, non-overlapping device addresses
 X, W1, W2, Y, WS = (0x10_0000_0000 * k for k in range(1, 6))
 
@@ -136,6 +153,11 @@ def ffn(lib, **kw):
     (dict(hidden=1 << 22, ffn=2 << 22), "TP_ERR_SHAPE"),  # bf16 row stride limits
     (dict(ffn=2 << 22), "TP_ERR_SHAPE"),
     (dict(ld=1 << 24), "TP_ERR_SHAPE"),
+    # fp32 dimensions are each below 2^31, but no operand may pass 2^60
+    # elements (its byte extent would wrap int64 in the alias checks)
+    (dict(din=B.TP_F32, dout=B.TP_F32, tokens=(1 << 31) - 1, hidden=(1 << 31) - 4,
+          ffn=2 * 64), "TP_ERR_SHAPE"),
+    (dict(din=B.TP_F32, dout=B.TP_F32, hidden=1 << 30, ld=1 << 40), "TP_ERR_SHAPE"),
     (dict(X=None), "TP_ERR_NULL"),
     (dict(Y=None), "TP_ERR_NULL"),
     (dict(ws=None), "TP_ERR_WORKSPACE"),
@@ -203,6 +225,9 @@ def attn(lib, **kw):
     (dict(seq=-3), "TP_ERR_SHAPE"),
     (dict(seq=1 << 23), "TP_ERR_SHAPE"),            # V^T rows addressed with 32-bit offsets
     (dict(hidden=1 << 22), "TP_ERR_SHAPE"),
+    (dict(batch=1 << 20, seq=1 << 12), "TP_ERR_SHAPE"),   # batch*seq = 2^32
+    (dict(batch=1 << 31, seq=0), "TP_ERR_SHAPE"),
+    (dict(batch=1 << 16, seq=1 << 14, nh=2048, t=1), "TP_ERR_SHAPE"),  # key tiles x heads
     (dict(Wo=None), "TP_ERR_NULL"),
     (dict(wsb=1000), "TP_ERR_WORKSPACE"),
     (dict(Y=X), "TP_ERR_ALIAS"),
