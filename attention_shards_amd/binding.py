@@ -119,6 +119,14 @@ def _dense(t, name: str):
     return t
 
 
+def _same_device(device, **tensors):
+    """Every tensor on `device`: the kernels run there and take the others'
+    addresses as its own."""
+    for name, t in tensors.items():
+        if t is not None and t.device != device:
+            raise ValueError(f"{name} is on {t.device}, the call runs on {device}")
+
+
 def _stream_of(stream, device):
     """The torch stream the call is enqueued on: the current stream of
     `device` for None, a torch stream as given, or a raw hipStream_t handle
@@ -156,7 +164,12 @@ def _workspace(ws, nbytes: int, device):
     if ws is None:
         return torch.empty(max(nbytes, 16), dtype=torch.uint8, device=device)
     _dense(ws, "workspace")
+    _same_device(device, workspace=ws)
     return ws
+
+
+def _nbytes(t) -> int:
+    return t.numel() * t.element_size()
 
 
 def tp_ffn_shard(X, W1_i, W2_i, Y_i, i: int, t: int, workspace=None,
@@ -182,6 +195,7 @@ def tp_ffn_shard(X, W1_i, W2_i, Y_i, i: int, t: int, workspace=None,
     in_dt = _dtype_code(X)
     if _dtype_code(W1_i) != in_dt or _dtype_code(W2_i) != in_dt:
         raise TypeError("X, W1_i and W2_i must share a dtype")
+    _same_device(X.device, W1_i=W1_i, W2_i=W2_i, Y_i=Y_i)
     ffn = fs * t
     need = tp_ffn_shard_workspace_bytes(tokens, hidden, ffn, t, in_dt)
     torch = _torch()
@@ -191,7 +205,7 @@ def tp_ffn_shard(X, W1_i, W2_i, Y_i, i: int, t: int, workspace=None,
         _check(lib.tp_ffn_shard(X.data_ptr(), W1_i.data_ptr(), W2_i.data_ptr(),
                                 Y_i.data_ptr(), tokens, hidden, ffn, i, t,
                                 W1_i.stride(0), in_dt, _dtype_code(Y_i),
-                                ws.data_ptr(), ws.numel(), s.cuda_stream))
+                                ws.data_ptr(), _nbytes(ws), s.cuda_stream))
     return Y_i
 
 
@@ -218,6 +232,7 @@ def tp_ffn_shard_noalloc(X, W1_i, W2_i, Y_i, i: int, t: int, stream=None):
     in_dt = _dtype_code(X)
     if _dtype_code(W1_i) != in_dt or _dtype_code(W2_i) != in_dt:
         raise TypeError("X, W1_i and W2_i must share a dtype")
+    _same_device(X.device, W1_i=W1_i, W2_i=W2_i, Y_i=Y_i)
     torch = _torch()
     s = _stream_of(stream, X.device)
     with torch.cuda.device(X.device):
@@ -270,6 +285,8 @@ def tp_ffn_shard_reduce(X, W1_i, W2_i, peer_partials, residual, out, i: int,
         if tuple(residual.shape) != (tokens, hidden):
             raise ValueError("residual shape mismatch")
         rdt, rptr = _dtype_code(residual), residual.data_ptr()
+    _same_device(X.device, W1_i=W1_i, W2_i=W2_i, out=out, residual=residual,
+                 **{f"peer_partials[{k}]": p for k, p in enumerate(peer_partials) if k != i})
     arr = (ctypes.c_void_p * t)(*[None if (k == i or p is None) else p.data_ptr()
                                   for k, p in enumerate(peer_partials)])
     ffn = fs * t
@@ -281,7 +298,7 @@ def tp_ffn_shard_reduce(X, W1_i, W2_i, peer_partials, residual, out, i: int,
         _check(lib.tp_ffn_shard_reduce(X.data_ptr(), W1_i.data_ptr(), W2_i.data_ptr(), arr,
                                        rptr, out.data_ptr(), tokens, hidden, ffn, i, t,
                                        W1_i.stride(0), in_dt, pdt, rdt, _dtype_code(out),
-                                       ws.data_ptr(), ws.numel(), s.cuda_stream))
+                                       ws.data_ptr(), _nbytes(ws), s.cuda_stream))
     return out
 
 
@@ -304,6 +321,9 @@ def tp_attn_shard(X, Wqkv_i, Wo_i, Y_i, batch: int, seq: int, n_heads: int,
             tuple(Y_i.shape) != (batch * seq, hidden):
         raise ValueError(f"shape mismatch: X{tuple(X.shape)} Wqkv_i{tuple(Wqkv_i.shape)} "
                          f"Wo_i{tuple(Wo_i.shape)} Y_i{tuple(Y_i.shape)}")
+    if _dtype_code(Wqkv_i) != _dtype_code(X) or _dtype_code(Wo_i) != _dtype_code(X):
+        raise TypeError("X, Wqkv_i and Wo_i must share a dtype")
+    _same_device(X.device, Wqkv_i=Wqkv_i, Wo_i=Wo_i, Y_i=Y_i)
     torch = _torch()
     s = _stream_of(stream, X.device)
     with torch.cuda.device(X.device), torch.cuda.stream(s):
@@ -313,7 +333,7 @@ def tp_attn_shard(X, Wqkv_i, Wo_i, Y_i, batch: int, seq: int, n_heads: int,
                                  Y_i.data_ptr(), batch, seq, hidden, n_heads,
                                  head_dim, i, t, 1 if causal else 0,
                                  _dtype_code(X), _dtype_code(Y_i), ws.data_ptr(),
-                                 ws.numel(), s.cuda_stream))
+                                 _nbytes(ws), s.cuda_stream))
     return Y_i
 
 
@@ -342,6 +362,8 @@ def tp_partial_reduce(partials, residual, out, stream=None, slice_of=None):
             raise ValueError("residual shape mismatch")
         rdt = _dtype_code(residual)
         rptr = residual.data_ptr()
+    _same_device(out.device, residual=residual,
+                 **{f"partials[{k}]": p for k, p in enumerate(partials)})
     arr = (ctypes.c_void_p * t)(*[p.data_ptr() for p in partials])
     torch = _torch()
     s = _stream_of(stream, out.device)
@@ -403,6 +425,8 @@ def tp_sp_reduce_layernorm(partials, residual, x_out, ln_out, gamma=None, beta=N
         if v.dtype != torch.float32 or tuple(v.shape) != (cols,):
             raise ValueError(f"{name} must be float32 [{cols}]")
         gb.append(v.data_ptr())
+    _same_device(ln_out.device, residual=residual, x_out=x_out, gamma=gamma, beta=beta,
+                 **{f"partials[{k}]": p for k, p in enumerate(partials)})
     arr = (ctypes.c_void_p * t)(*[p.data_ptr() for p in partials])
     s = _stream_of(stream, ln_out.device)
     slice_, nslices = slice_of

@@ -454,3 +454,15 @@ def test_sp_reduce_layernorm_rejects(lib):
 def test_sp_reduce_layernorm_empty_is_a_no_op(lib):
     assert sp_call(lib, [X], rows=0)[0] == "TP_SUCCESS"
     assert sp_call(lib, [X], rows=3, slice_=5, nslices=8)[0] == "TP_SUCCESS"   # empty block
+
+
+def test_binding_refuses_tensors_on_another_device():
+    """Every tensor of a call must sit on the device it runs on: the kernels
+    would otherwise take another device's addresses as their own."""
+    import torch
+    from attention_shards_amd import binding as Bd
+    a = torch.zeros(4)
+    Bd._same_device(a.device, x=a, y=None)
+    with pytest.raises(ValueError, match="W2_i is on cpu"):
+        Bd._same_device(torch.device("cuda", 0), W2_i=a)
+    assert Bd._nbytes(torch.zeros(5, dtype=torch.float32)) == 20

@@ -152,6 +152,39 @@ def test_bad_arguments_raise(gpu):
         gpu.tp_ffn_shard(X, W1, W2, torch.empty((8, 64), device="cuda"), 2, 2)
 
 
+def test_workspace_of_any_element_type_counts_in_bytes(gpu):
+    """A caller's workspace is sized by its bytes, whatever its dtype: a
+    float32 tensor of need/4 elements is enough, and the result equals the
+    one with the binding's own workspace."""
+    d = syn.make_ffn_inputs(41, 96, 64, 2 * 192, syn.BF16)
+    X = to_dev(d["X"], syn.BF16)
+    W1_i = to_dev(np.ascontiguousarray(d["W1"][:, 192:]), syn.BF16)
+    W2_i = to_dev(np.ascontiguousarray(d["W2"][192:, :]), syn.BF16)
+    need = gpu.tp_ffn_shard_workspace_bytes(96, 64, 2 * 192, 2, gpu.TP_BF16)
+    ws = torch.empty((need + 3) // 4, dtype=torch.float32, device="cuda")
+    Y1 = torch.empty((96, 64), dtype=torch.float32, device="cuda")
+    Y2 = torch.empty_like(Y1)
+    gpu.tp_ffn_shard(X, W1_i, W2_i, Y1, 1, 2, workspace=ws)
+    gpu.tp_ffn_shard(X, W1_i, W2_i, Y2, 1, 2)
+    torch.cuda.synchronize()
+    assert torch.equal(Y1, Y2)
+
+
+def test_mixed_devices_and_dtypes_are_refused(gpu):
+    X = torch.zeros((8, 64), dtype=torch.bfloat16, device="cuda")
+    W1 = torch.zeros((64, 128), dtype=torch.bfloat16, device="cuda")
+    W2 = torch.zeros((128, 64), dtype=torch.bfloat16, device="cuda")
+    Y = torch.empty((8, 64), dtype=torch.float32, device="cuda")
+    with pytest.raises(ValueError, match="must be a GPU tensor"):
+        gpu.tp_ffn_shard(X, W1, W2.cpu(), Y, 0, 1)
+    with pytest.raises(TypeError, match="share a dtype"):
+        gpu.tp_ffn_shard(X, W1.float(), W2, Y, 0, 1)
+    Wqkv = torch.zeros((64, 3 * 128), dtype=torch.float32, device="cuda")
+    Wo = torch.zeros((128, 64), dtype=torch.bfloat16, device="cuda")
+    with pytest.raises(TypeError, match="share a dtype"):
+        gpu.tp_attn_shard(X, Wqkv, Wo, Y, 1, 8, 2, 128, 0, 2)
+
+
 def test_sweep_small_point_full(gpu):
     """Sweep point hidden 2048, t=8: X[2048,2048], W1_0 = W1[:, :1024]."""
     h = 2048
