@@ -59,6 +59,22 @@ def test_attention_layer_shape_first_and_last_sequence(gpu):
         assert e <= TOL_BF16
 
 
+def test_attention_long_causal_sequence(gpu):
+    """8192 causal tokens with 8 local heads (hidden 1024, t=1): the work
+    split of the 8192-token timing shape (it depends only on the sequence
+    count, length, local heads and causality), key ranges of up to 128 tiles
+    of 64 keys, and the rows nearest the start of the sequence, whose outputs
+    are the largest against the RMS; whole tensor vs the oracle."""
+    batch, seq, hidden, nh, t, i = 1, 8192, 1024, 8, 1, 0
+    a = syn.make_attn_inputs(48, batch, seq, hidden, nh, 128)
+    got = run(gpu, a, batch, seq, nh, 128, i, t, True, syn.F32)
+    log("attention 8192 causal tokens: GPU call done")
+    r = ref(a, batch, seq, nh, 128, i, t, True)
+    e = rel_err(got, r)
+    log(f"attention 8192 causal tokens, 8 heads: err {e:.4f}")
+    assert e <= TOL_BF16
+
+
 @pytest.mark.parametrize("batch,seq,hidden,nh,t,i,causal,out", [
     (2, 100, 256, 4, 2, 1, True, syn.F32),     # ragged sequence, two sequences
     (2, 100, 256, 4, 2, 0, False, syn.F32),
