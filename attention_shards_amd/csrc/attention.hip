@@ -20,11 +20,12 @@
 // fp16 hi/lo pair.  Scores use one fp16 MFMA pass; the softmax runs in fp32
 // with exp2; probabilities are rounded to fp16 (values in [0, 1], 11
 // significant bits) and the running denominator sums exactly those rounded
-// values; P.V uses two fp16 MFMA passes (P.Vhi + P.Vlo).  O is written as a
-// bf16 hi/lo pair, so the output projection sees it with ~16 significant
-// bits.  Causal attention over short prefixes makes max|Y|/RMS(Y) large (row
-// 0 is v_0 itself), which is what rules out single roundings of V and O
-// here (an emulation of these rounding points on the CPU chose the split).
+// values; P.V uses two fp16 MFMA passes (P.Vhi + P.Vlo).  O is written as
+// fp16 plus its residual in bf8 (e5m2), so the output projection sees it
+// with ~14 significant bits (one fp16 pass and one bf8 pass of half the
+// cost).  Causal attention over short prefixes makes max|Y|/RMS(Y) large
+// (row 0 is v_0 itself), which is what rules out single roundings of V and
+// O here (an emulation of these rounding points on the CPU chose the split).
 // Q, K and V must lie within the fp16 range (|x| < 65504).
 //
 // Layout: a workgroup has 8 waves (two per SIMD, so one wave's LDS waits
@@ -128,13 +129,39 @@ __device__ __forceinline__ void wait_vmcnt() {
   asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
 
-// Element offset of O[row][col] in the O buffer ([rows][two_hd] bf16):
-// row-major for kbs == 0, else K-blocked by kb = 1 << kbs for the output
-// projection, [two_hd / kb][rows][kb].  col..col+3 (col % 4 == 0) stay
-// contiguous either way.
-__device__ __forceinline__ int64_t o_at(int64_t row, int col, int64_t rows, int two_hd, int kbs) {
-  return kbs ? ((int64_t)(col >> kbs) * rows + row) * (1 << kbs) + (col & ((1 << kbs) - 1))
-             : row * two_hd + col;
+// O for the output projection, [rows][hd] (hd = heads * D): O_hi, fp16,
+// K-blocked by 32 ([hd/32][rows][32]); after it O_lo, bf8, K-blocked by 64
+// ([hd/64][rows][64 bytes]) with each 64-byte row piece permuted so that
+// byte 32h + 8s + j holds column 16s + 8h + j (s = 0..3, h = 0..1,
+// j = 0..7), the order in which the projection's lo product consumes it.
+// Element (fp16) offset of O_hi[row][col]:
+__device__ __forceinline__ int64_t ohi_at(int64_t row, int col, int64_t rows) {
+  return ((int64_t)(col >> 5) * rows + row) * 32 + (col & 31);
+}
+// Byte offset of O_lo[row][col] from the start of O_lo; col..col+3
+// (col % 4 == 0) are contiguous, and so are col..col+7 for col % 8 == 0.
+__device__ __forceinline__ int64_t olo_at(int64_t row, int col, int64_t rows) {
+  const int k = col & 63;
+  return ((int64_t)(col >> 6) * rows + row) * 64 + (((k >> 3) & 1) << 5) + ((k >> 4) << 3) +
+         (k & 7);
+}
+// O_hi = fp16(x) (nearest even), O_lo = bf8(x - O_hi) with the residual
+// taken exactly by one fma (written out, so the rounding does not depend on
+// the compiler's contraction choices); x = o * inv.  Four values: two fp16
+// pairs and four bf8 bytes.
+__device__ __forceinline__ void o_split4(const float* o, float inv, uint32_t* hi, uint32_t* lo8) {
+  float r[4];
+#pragma unroll
+  for (int e = 0; e < 4; e += 2) {
+    const _Float16 h0 = (_Float16)(o[e] * inv), h1 = (_Float16)(o[e + 1] * inv);
+    r[e] = __builtin_fmaf(o[e], inv, -(float)h0);
+    r[e + 1] = __builtin_fmaf(o[e + 1], inv, -(float)h1);
+    hi[e / 2] = (uint32_t)__builtin_bit_cast(uint16_t, h0) |
+                ((uint32_t)__builtin_bit_cast(uint16_t, h1) << 16);
+  }
+  int v = __builtin_amdgcn_cvt_pk_bf8_f32(r[0], r[1], 0, false);
+  v = __builtin_amdgcn_cvt_pk_bf8_f32(r[2], r[3], v, true);
+  *lo8 = (uint32_t)v;
 }
 
 // Key tiles query block qb (of QB queries) needs.
@@ -145,7 +172,7 @@ __host__ __device__ inline int ntile_of(int qb, int seq, int causal, int QB) {
 
 template <int NQG>
 __global__ void __launch_bounds__(NT)
-attn_fwd_kernel(QkvOut q, int causal, uint16_t* __restrict__ O, int o_kbs,
+attn_fwd_kernel(QkvOut q, int causal, uint16_t* __restrict__ O,
                 float* __restrict__ part, AttnSplit sp, float scale_log2) {
   constexpr int QW = 16 * NQG;    // queries per wave
   constexpr int QB = NWAVE * QW;  // queries per workgroup
@@ -438,23 +465,15 @@ attn_fwd_kernel(QkvOut q, int causal, uint16_t* __restrict__ O, int o_kbs,
       if (myq[qg] < S) {
         const float inv = 1.0f / l_tot;
         const int64_t orow = (int64_t)b * S + myq[qg], rows = (int64_t)(sp.nbh / q.nl) * S;
+        uint8_t* const olo = reinterpret_cast<uint8_t*>(O) + rows * hd * 2;
 #pragma unroll
         for (int db = 0; db < 8; ++db) {
-          uint32_t hi[4], lo[4];
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            // hi = bf16(o * inv); lo = bf16 of the exact residual o * inv - hi
-            // (one fma, written out so the rounding does not depend on the
-            // compiler's contraction choices)
-            const float x = o[qg][db][e];
-            hi[e] = f2bf(x * inv);
-            lo[e] = f2bf(__builtin_fmaf(x, inv, -__uint_as_float(hi[e] << 16)));
-          }
+          uint32_t hi[2], lo8;
+          const float x[4] = {o[qg][db][0], o[qg][db][1], o[qg][db][2], o[qg][db][3]};
+          o_split4(x, inv, hi, &lo8);
           const int col = head * D + db * 16 + 4 * g;
-          *reinterpret_cast<uint2*>(O + o_at(orow, col, rows, 2 * hd, o_kbs)) =
-              uint2{hi[0] | (hi[1] << 16), hi[2] | (hi[3] << 16)};
-          *reinterpret_cast<uint2*>(O + o_at(orow, hd + col, rows, 2 * hd, o_kbs)) =
-              uint2{lo[0] | (lo[1] << 16), lo[2] | (lo[3] << 16)};
+          *reinterpret_cast<uint2*>(O + ohi_at(orow, col, rows)) = uint2{hi[0], hi[1]};
+          *reinterpret_cast<uint32_t*>(olo + olo_at(orow, col, rows)) = lo8;
         }
       }
     } else {
@@ -484,7 +503,7 @@ attn_fwd_kernel(QkvOut q, int causal, uint16_t* __restrict__ O, int o_kbs,
 // issues no more loads than it needs.
 template <int MAXC>
 __global__ void __launch_bounds__(256)
-attn_combine_kernel(QkvOut q, int causal, uint16_t* __restrict__ O, int o_kbs,
+attn_combine_kernel(QkvOut q, int causal, uint16_t* __restrict__ O,
                     const float* __restrict__ part, AttnSplit sp) {
   const int QB = sp.qb, wpg = QB / 16;
   const int grp = blockIdx.x / wpg;
@@ -565,20 +584,16 @@ attn_combine_kernel(QkvOut q, int causal, uint16_t* __restrict__ O, int o_kbs,
   const int b = bh / q.nl, head = bh - b * q.nl;
   const int hd = q.nl * D;
   const int64_t orow = (int64_t)b * S + myq, rows = (int64_t)(sp.nbh / q.nl) * S;
-  uint32_t hi[8], lo[8];
+  float x[8];
 #pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    const float x = e < 4 ? a0[e] : a1[e - 4];
-    hi[e] = f2bf(x * inv);  // hi/lo as in attn_fwd_kernel
-    lo[e] = f2bf(__builtin_fmaf(x, inv, -__uint_as_float(hi[e] << 16)));
-  }
+  for (int e = 0; e < 8; ++e) x[e] = e < 4 ? a0[e] : a1[e - 4];
+  uint32_t hi[4], lo8[2];  // split as in attn_fwd_kernel
+  o_split4(x, inv, hi, &lo8[0]);
+  o_split4(x + 4, inv, hi + 2, &lo8[1]);
   const int col = head * D + dg * 8;
-  *reinterpret_cast<u32x4*>(O + o_at(orow, col, rows, 2 * hd, o_kbs)) =
-      u32x4{hi[0] | (hi[1] << 16), hi[2] | (hi[3] << 16), hi[4] | (hi[5] << 16),
-            hi[6] | (hi[7] << 16)};
-  *reinterpret_cast<u32x4*>(O + o_at(orow, hd + col, rows, 2 * hd, o_kbs)) =
-      u32x4{lo[0] | (lo[1] << 16), lo[2] | (lo[3] << 16), lo[4] | (lo[5] << 16),
-            lo[6] | (lo[7] << 16)};
+  *reinterpret_cast<u32x4*>(O + ohi_at(orow, col, rows)) = u32x4{hi[0], hi[1], hi[2], hi[3]};
+  *reinterpret_cast<uint2*>(reinterpret_cast<uint8_t*>(O) + rows * hd * 2 +
+                            olo_at(orow, col, rows)) = uint2{lo8[0], lo8[1]};
 }
 
 // Zeroes V^T columns [seq, seq_pad) of every (sequence*head, dim) row, hi
@@ -741,10 +756,8 @@ int64_t attn_partial_bytes(int batch, int seq, int nl) {
   return bytes;
 }
 
-hipError_t attention_fwd(const QkvOut& q, int batch, bool causal, uint16_t* O, int o_kb,
-                         float* part, hipStream_t s) {
-  if (o_kb != 0 && o_kb != 32 && o_kb != 64) return hipErrorInvalidValue;
-  const int o_kbs = o_kb == 32 ? 5 : (o_kb == 64 ? 6 : 0);
+hipError_t attention_fwd(const QkvOut& q, int batch, bool causal, uint16_t* O, float* part,
+                         hipStream_t s) {
   if (batch == 0 || q.seq == 0 || q.nl == 0) return hipSuccess;
   const AttnSplit sp = attn_split(batch, q.seq, q.nl, causal);
   const float scale_log2 = 1.4426950408889634f / sqrtf((float)q.d);
@@ -758,23 +771,23 @@ hipError_t attention_fwd(const QkvOut& q, int batch, bool causal, uint16_t* O, i
   }
   if (sp.qb == 256)
     hipLaunchKernelGGL(attn_fwd_kernel<2>, dim3(sp.n_items), dim3(NT), 0, s, q, causal ? 1 : 0,
-                       O, o_kbs, part, sp, scale_log2);
+                       O, part, sp, scale_log2);
   else
     hipLaunchKernelGGL(attn_fwd_kernel<1>, dim3(sp.n_items), dim3(NT), 0, s, q, causal ? 1 : 0,
-                       O, o_kbs, part, sp, scale_log2);
+                       O, part, sp, scale_log2);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (sp.n_items == sp.nqb * sp.nbh) return hipSuccess;  // no query block was split
   const int max_nc = div_up(ntile_of(sp.nqb - 1, q.seq, causal ? 1 : 0, sp.qb), sp.ch);
   const dim3 grid(sp.nqb * sp.nbh * (sp.qb / 16));
   if (max_nc <= 4)
-    hipLaunchKernelGGL(attn_combine_kernel<4>, grid, dim3(256), 0, s, q, causal ? 1 : 0, O, o_kbs,
+    hipLaunchKernelGGL(attn_combine_kernel<4>, grid, dim3(256), 0, s, q, causal ? 1 : 0, O,
                        part, sp);
   else if (max_nc <= 8)
-    hipLaunchKernelGGL(attn_combine_kernel<8>, grid, dim3(256), 0, s, q, causal ? 1 : 0, O, o_kbs,
+    hipLaunchKernelGGL(attn_combine_kernel<8>, grid, dim3(256), 0, s, q, causal ? 1 : 0, O,
                        part, sp);
   else
-    hipLaunchKernelGGL(attn_combine_kernel<16>, grid, dim3(256), 0, s, q, causal ? 1 : 0, O, o_kbs,
+    hipLaunchKernelGGL(attn_combine_kernel<16>, grid, dim3(256), 0, s, q, causal ? 1 : 0, O,
                        part, sp);
   return hipGetLastError();
 }

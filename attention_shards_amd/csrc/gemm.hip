@@ -53,6 +53,8 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef int i32x8 __attribute__((ext_vector_type(8)));
 
 // Two fp32 values rounded to bf16 (nearest even) and packed, low half
 // first: one v_cvt_pk_bf16_f32.
@@ -571,10 +573,20 @@ __device__ __forceinline__ void epilogue_lds(uint8_t* smem, f32x16 (&acc)[FM][FN
 // KS MFMA k-steps of 16 per pipeline stage (stage K = BK = 16 KS) and an LDS
 // ring of NSL stages.  KS = 2 gives 64-byte A rows per stage; KS = 4 gives
 // 128-byte A rows (a whole cache line per row per DMA), at the price of
-// fewer, larger ring slots.  NA = 2: C = (A_1 + A_2) B with A = [A_1 | A_2]
-// K-blocked, [2 ceil(K/BK)][lda][BK], A_2's blocks after A_1's: every stage
-// brings the two A tiles and one B tile, and both products use the same B
-// fragments (half the B traffic of two passes over K).
+// fewer, larger ring slots.  NA = 2 (mixed precision, KS = 2, NSL = 4):
+// C = A_hi fp16(B) + A_lo bf8(B), A_hi fp16 K-blocked by 32,
+// [K/32][lda][32], then A_lo bf8 K-blocked by 64, [K/64][lda][64 bytes],
+// each 64-byte row piece permuted so that byte 32h + 8s + j holds column
+// 16s + 8h + j (K a multiple of 64).  B stays bf16 in LDS; each k-step's B
+// fragments are converted in registers to fp16 (exact for bf16 values of
+// magnitude 2^-14 .. 65504) for the hi product and to bf8 for the lo
+// product.  Every step brings A_hi's and B's stage; odd steps also bring
+// A_lo for two stages into one of two lo slots, and at the end of the
+// second stage of each pair the lo product runs as 32x32x64 bf8 MFMAs (half
+// the matrix-pipe time of the fp16 pass), its B fragments gathered from the
+// pair's four k-steps (lane l holds column l%32 with, for k-step s, columns
+// 16s + 8(l/32) + 0..7, which is why A_lo's row pieces are permuted to
+// match).
 // AP (A pairs; KS = 2, row-major A, NSL = 4): A goes into two slots of
 // 128-byte rows, each holding the K columns of two consecutive stages, so
 // every A DMA reads whole 128-byte lines of A's rows (a stage's 64-byte row
@@ -596,7 +608,9 @@ gemm_bf16_kernel(const uint16_t* __restrict__ A, int64_t lda,
   // product to an epilogue that stores per part.
   static_assert(KS == 2 || KS == 4, "k-steps per stage");
   static_assert(NSL >= 3 && NSL <= 6, "ring slots");
-  static_assert(NA == 1 || (NA == 2 && AKB), "paired A operands are K-blocked");
+  static_assert(NA == 1 || (NA == 2 && AKB && KS == 2 && NSL == 4), "mixed A: the layout below");
+  constexpr bool MIX = NA == 2;
+  constexpr int NAO = MIX ? 1 : NA;  // A operands in the stage ring
   static_assert(!AP || (KS == 2 && !AKB && NA == 1 && NSL == 4), "A pairs: the layout below");
   constexpr int BK = 16 * KS;
   constexpr int NW = WM * WN;
@@ -612,23 +626,28 @@ gemm_bf16_kernel(const uint16_t* __restrict__ A, int64_t lda,
   constexpr int B_STAGE = BK * B_ROWB;
   constexpr int A_DMA = A_STAGE / 1024 / NW;  // 1 KiB DMAs per wave per A slot
   constexpr int B_DMA = B_STAGE / 1024 / NW;
-  constexpr int NDMA = NA * A_DMA + B_DMA;     // AP: even steps; odd steps B_DMA
+  constexpr int NDMA = NAO * A_DMA + B_DMA;    // AP: even steps; odd steps B_DMA
   constexpr int A_SLOTS = AP ? 2 : NSL;
+  constexpr int LO_STAGE = MIX ? BM * 64 : 0;  // MIX: A_lo of two stages (bf8)
+  constexpr int LO_DMA = LO_STAGE / 1024 / NW;  // MIX: on odd steps
   static_assert(A_DMA * 1024 * NW == A_STAGE && B_DMA * 1024 * NW == B_STAGE, "DMA split");
   static_assert(B_CH % 16 == 0 || B_CH == 24, "B swizzle: 256-byte multiple or 384-byte rows");
   static_assert(FM >= 1 && FN >= 1, "wave tile");
 
-  // LDS ring: slot s holds A operand o at (s*NA + o)*A_STAGE (AP: pair slot
-  // s at s*A_STAGE) and B at A_SLOTS*NA*A_STAGE + s*B_STAGE.  The same memory
-  // later stages the epilogue (NW regions of 32 x (BN/WN+4)).
-  constexpr int PIPE_BYTES = A_SLOTS * NA * A_STAGE + NSL * B_STAGE;
+  // LDS ring: slot s holds A operand o at (s*NAO + o)*A_STAGE (AP: pair slot
+  // s at s*A_STAGE) and B at A_SLOTS*NAO*A_STAGE + s*B_STAGE; MIX: the two
+  // lo slots follow.  The same memory later stages the epilogue (NW regions
+  // of 32 x (BN/WN+4)).
+  constexpr int PIPE_BYTES = A_SLOTS * NAO * A_STAGE + NSL * B_STAGE + 2 * LO_STAGE;
   constexpr int EPI_BYTES = NW * 32 * (BN / WN + 4) * 4;
   __shared__ __attribute__((aligned(16))) uint8_t
       smem[PIPE_BYTES > EPI_BYTES ? PIPE_BYTES : EPI_BYTES];
   uint8_t* const lds_a = smem;
-  uint8_t* const lds_b = smem + A_SLOTS * NA * A_STAGE;
+  uint8_t* const lds_b = smem + A_SLOTS * NAO * A_STAGE;
+  uint8_t* const lds_lo = lds_b + NSL * B_STAGE;
   const uint32_t lds_a_addr = (uint32_t)(uintptr_t)(lds_u8*)lds_a;
   const uint32_t lds_b_addr = (uint32_t)(uintptr_t)(lds_u8*)lds_b;
+  const uint32_t lds_lo_addr = (uint32_t)(uintptr_t)(lds_u8*)lds_lo;
 
   int tm, tn, part;
   tile_coords(tiles_m, tiles_n, tm, tn, part);
@@ -694,21 +713,32 @@ gemm_bf16_kernel(const uint16_t* __restrict__ A, int64_t lda,
   auto dma = [&](int kt, auto SLOT, int j) {
     constexpr int slot = decltype(SLOT)::value;
     const int k0 = kt * BK;
-    if (j < NA * A_DMA) {
+    if (j < NAO * A_DMA) {
       const int op = j / A_DMA, ja = j - op * A_DMA;
       const int blk = kt + op * a_blocks;
       const __amdgpu_buffer_rsrc_t ra =
           AKB ? make_rsrc(A + ((int64_t)blk * lda + m0) * BK, (int64_t)rows_valid * A_ROWB)
               : make_rsrc(A + (int64_t)m0 * lda + k0, (int64_t)rows_valid * lda * 2 - (int64_t)k0 * 2);
       const int off = (k0 + a_col[ja] < K) ? a_off[ja] : OOB;
-      dma16(ra, off, lds_a_addr + (slot * NA + op) * A_STAGE + (ja * NW + wave) * 1024);
+      dma16(ra, off, lds_a_addr + (slot * NAO + op) * A_STAGE + (ja * NW + wave) * 1024);
     } else {
-      const int jb = j - NA * A_DMA;
+      const int jb = j - NAO * A_DMA;
       const __amdgpu_buffer_rsrc_t rb =
           make_rsrc(B + (int64_t)k0 * ldb + n0,
                     ((int64_t)(K - k0) - 1) * ldb * 2 + (int64_t)cols_valid * 2);
       dma16(rb, b_off[jb], lds_b_addr + slot * B_STAGE + (jb * NW + wave) * 1024);
     }
+  };
+  // MIX: DMA number ja (0 <= ja < LO_DMA) of A_lo pair p (K columns 64p ..
+  // 64p+63, 64-byte rows like A_hi's, same offsets and swizzle) into lo
+  // slot LS.
+  const uint8_t* const a_lo = reinterpret_cast<const uint8_t*>(A) + (int64_t)a_blocks * lda * 64;
+  auto dma_lo = [&](int p, auto LS, int ja) {
+    constexpr int ls = decltype(LS)::value;
+    const __amdgpu_buffer_rsrc_t ra =
+        make_rsrc(a_lo + ((int64_t)p * lda + m0) * 64, (int64_t)rows_valid * 64);
+    const int off = (p * 64 < K) ? a_off[ja] : OOB;
+    dma16(ra, off, lds_lo_addr + ls * LO_STAGE + (ja * NW + wave) * 1024);
   };
 
   // ---- fragment read addresses (byte offsets inside a slot).
@@ -747,7 +777,7 @@ gemm_bf16_kernel(const uint16_t* __restrict__ A, int64_t lda,
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[mi][ni][e] = 0.0f;
 
-  bf16x8 fa[2][NA][FM], fb[2][FN];
+  bf16x8 fa[2][NAO][FM], fb[2][FN];
   // Fragment read unit q of k-step ks from ring slot SLOT into set fset:
   // units 0..FN-1 are B fragments (two transposed reads each), units
   // FN..FN+NA*FM-1 are A fragments (operand by operand).
@@ -768,16 +798,65 @@ gemm_bf16_kernel(const uint16_t* __restrict__ A, int64_t lda,
     } else {
       const int op = (q - FN) / FM, mi = (q - FN) - op * FM;
       fa[fset][op][mi] = *reinterpret_cast<const bf16x8*>(
-          lds_a + (slot * NA + op) * A_STAGE + a_rd[0][ks] + mi * 32 * A_ROWB);
+          lds_a + (slot * NAO + op) * A_STAGE + a_rd[0][ks] + mi * 32 * A_ROWB);
     }
   };
-  // one MFMA of a k-step, idx in [0, NA*FM*FN): operand by operand, so an
-  // accumulator's two products of a k-step are FM*FN MFMAs apart
+  // one MFMA of a k-step, idx in [0, NAO*FM*FN): operand by operand (NA =
+  // 1 with AP or plain: one operand); MIX: the fp16 product of A_hi and the
+  // converted B fragments
   auto mfma1 = [&](int fset, int idx) {
     const int op = idx / (FM * FN), r = idx - op * (FM * FN);
     const int mi = r / FN, ni = r % FN;
-    acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[fset][op][mi], fb[fset][ni],
-                                                          acc[mi][ni], 0, 0, 0);
+    if constexpr (MIX)
+      acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_f16(
+          __builtin_bit_cast(f16x8, fa[fset][op][mi]), __builtin_bit_cast(f16x8, fb[fset][ni]),
+          acc[mi][ni], 0, 0, 0);
+    else
+      acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[fset][op][mi], fb[fset][ni],
+                                                            acc[mi][ni], 0, 0, 0);
+  };
+  // MIX: B fragment ni of set fset (bf16, k-step s = 0..3 of its stage pair)
+  // -> fp16 in place (round toward zero, exact for bf16 values in fp16's
+  // normal range) and bf8 (nearest even) into words 2s, 2s+1 of blo[ni].
+  i32x8 blo[MIX ? FN : 1];
+  auto convert_b = [&](int fset, int ni, int sk) {
+    const u32x4 d = __builtin_bit_cast(u32x4, fb[fset][ni]);
+    float lo[4], hi[4];
+    u32x4 h;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      lo[w] = __uint_as_float(d[w] << 16);
+      hi[w] = __uint_as_float(d[w] & 0xffff0000u);
+      h[w] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(lo[w], hi[w]));
+    }
+    fb[fset][ni] = __builtin_bit_cast(bf16x8, h);
+    blo[ni][2 * sk] = __builtin_amdgcn_cvt_pk_bf8_f32(
+        lo[1], hi[1], __builtin_amdgcn_cvt_pk_bf8_f32(lo[0], hi[0], 0, false), true);
+    blo[ni][2 * sk + 1] = __builtin_amdgcn_cvt_pk_bf8_f32(
+        lo[3], hi[3], __builtin_amdgcn_cvt_pk_bf8_f32(lo[2], hi[2], 0, false), true);
+  };
+  // MIX: A_lo fragment reads (row wr0 + mi*32 + lane%32, logical 16-byte
+  // chunks 2(lane/32) and 2(lane/32)+1 of the 64-byte row, A's swizzle) and
+  // the lo product, bf8 x bf8 with unit scales (E8M0 127).
+  int lo_rd[2];
+#pragma unroll
+  for (int c2 = 0; c2 < 2; ++c2) {
+    const int c = (2 * (lane >> 5) + c2) ^ (((lane & 31) >> ASH) & (CPR - 1));
+    lo_rd[c2] = (wr0 + (lane & 31)) * A_ROWB + c * 16;
+  }
+  i32x8 alo[MIX ? FM : 1];
+  auto read_lo = [&](auto LS, int mi) {
+    constexpr int ls = decltype(LS)::value;
+    const uint8_t* base = lds_lo + ls * LO_STAGE + mi * 32 * A_ROWB;
+    const u32x4 x0 = *reinterpret_cast<const u32x4*>(base + lo_rd[0]);
+    const u32x4 x1 = *reinterpret_cast<const u32x4*>(base + lo_rd[1]);
+    alo[mi] = i32x8{(int)x0[0], (int)x0[1], (int)x0[2], (int)x0[3],
+                    (int)x1[0], (int)x1[1], (int)x1[2], (int)x1[3]};
+  };
+  auto mfma_lo = [&](int idx) {
+    const int mi = idx / FN, ni = idx % FN;
+    acc[mi][ni] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(alo[mi], blo[ni], acc[mi][ni],
+                                                                  1, 1, 0, 127, 0, 127);
   };
 
   // Stages past the end of K load zeros (offsets outside the buffers), so
@@ -799,26 +878,39 @@ gemm_bf16_kernel(const uint16_t* __restrict__ A, int64_t lda,
   //   barrier;
   //   k-step KS-1: the fragment reads of k-step 0 of stage kt+1.
   // Fragment register sets alternate with the k-step's parity (KS even).
-  constexpr int NMF = NA * FM * FN;  // MFMAs per k-step
-  constexpr int NRU = NA * FM + FN;  // fragment read units per k-step
+  constexpr int NMF = NAO * FM * FN;  // MFMAs per k-step (MIX: the fp16 ones)
+  constexpr int NRU = NAO * FM + FN;  // fragment read units per k-step
   constexpr int DSLOTS = (KS - 1) * NMF;
-  static_assert(NDMA <= DSLOTS && NRU <= NMF, "traffic fits between the MFMAs");
+  static_assert(NDMA + LO_DMA <= DSLOTS && NRU <= NMF, "traffic fits between the MFMAs");
+  static_assert(!MIX || FM <= NMF, "MIX: A_lo reads fit between the MFMAs");
   // AP: step kt (kt % 4 == u) issues, on even u, the A pair kt/2 + 1 (the
   // stages two and three ahead) into pair slot (kt/2 + 1) % 2, then B of
   // stage kt+3; on odd u, B alone.  Stage kt+1 then needs the B issued three
   // steps back and the A pair issued at the last even step, so the loads
   // that may stay in flight are those of step kt-1 after its A pair (B) and
   // of step kt (odd u), or those after step kt-2's B (even u).
+  // MIX (NSL = 4, so u's parity is kt's): odd step kt issues, after its
+  // stage's DMAs, A_lo pair (kt+1)/2 into lo slot ((kt+1)/2) % 2 (that slot's
+  // previous pair was read in step kt-2, before step kt-1's barrier), and
+  // ends with the lo product of pair (kt-1)/2, issued at step kt-2 and so
+  // landed at this step's wait; the B fragments of the pair's four k-steps
+  // are converted as each k-step begins.  Steps kt-1 and kt hold one odd
+  // step between them, so the loads that may stay in flight at the wait are
+  // 2 NDMA + LO_DMA.
   auto step = [&](int kt, auto U) __attribute__((always_inline)) {
     constexpr int u = decltype(U)::value;
     constexpr int nxt = (u + NSL - 1) % NSL;
-    constexpr int nd = AP ? ((u & 1) ? B_DMA : A_DMA + B_DMA) : NDMA;  // DMAs this step
+    constexpr int nd = AP ? ((u & 1) ? B_DMA : A_DMA + B_DMA)
+                          : NDMA + ((MIX && (u & 1)) ? LO_DMA : 0);  // DMAs this step
     // MFMA slot after which DMA d of the step is issued
     auto dma_slot = [](int d) { return KS == 2 ? NMF - nd + d : d * DSLOTS / nd; };
 #pragma unroll
     for (int ksi = 0; ksi < KS - 1; ++ksi) {
 #pragma unroll
       for (int j = 0; j < NMF; ++j) {
+        if constexpr (MIX) {
+          if (j < FN) convert_b(ksi & 1, j, 2 * (u & 1) + ksi);
+        }
         mfma1(ksi & 1, j);
         __builtin_amdgcn_sched_barrier(0);
         if (j < NRU) read_unit(IC<u>{}, ksi + 1, (ksi + 1) & 1, j);
@@ -830,6 +922,8 @@ gemm_bf16_kernel(const uint16_t* __restrict__ A, int64_t lda,
                 dma_a_pair(kt / 2 + 1, IC<((u >> 1) + 1) & 1>{}, d);
               else
                 dma(kt + NSL - 1, IC<nxt>{}, NA * A_DMA + d - ((u & 1) ? 0 : A_DMA));
+            } else if (MIX && d >= NDMA) {
+              dma_lo((kt + 1) / 2, IC<((u + 1) / 2) & 1>{}, d - NDMA);
             } else {
               dma(kt + NSL - 1, IC<nxt>{}, d);
             }
@@ -840,19 +934,30 @@ gemm_bf16_kernel(const uint16_t* __restrict__ A, int64_t lda,
     if constexpr (AP)
       wait_vmcnt<(u & 1) ? 2 * B_DMA : A_DMA + 2 * B_DMA>();
     else
-      wait_vmcnt<(NSL - 2) * NDMA>();
+      wait_vmcnt<(NSL - 2) * NDMA + LO_DMA>();
     wait_lgkmcnt0();
     stage_barrier();
 #pragma unroll
     for (int j = 0; j < NMF; ++j) {
+      if constexpr (MIX) {
+        if (j < FN) convert_b((KS - 1) & 1, j, 2 * (u & 1) + KS - 1);
+      }
       mfma1((KS - 1) & 1, j);
       __builtin_amdgcn_sched_barrier(0);
       if (j < NRU) read_unit(IC<(u + 1) % NSL>{}, 0, 0, j);
+      if constexpr (MIX && (u & 1)) {
+        if (j < FM) read_lo(IC<((u - 1) / 2) & 1>{}, j);
+      }
       __builtin_amdgcn_sched_barrier(0);
+    }
+    if constexpr (MIX && (u & 1)) {
+#pragma unroll
+      for (int j = 0; j < FM * FN; ++j) mfma_lo(j);
     }
   };
 
-  // Prologue: stages 0..NSL-2 in flight, wait for stage 0.  AP: the loads
+  // Prologue: stages 0..NSL-2 in flight (MIX: then A_lo pair 0, as step -1
+  // would), wait for stage 0.  AP: the loads
   // steps -3, -2, -1 would have issued (B of stage 0; A pair 0 and B of
   // stage 1; B of stage 2), then wait for A pair 0 and B of stage 0.
   if constexpr (AP) {
@@ -870,7 +975,11 @@ gemm_bf16_kernel(const uint16_t* __restrict__ A, int64_t lda,
 #pragma unroll
       for (int j = 0; j < NDMA; ++j) dma(decltype(S)::value, S, j);
     });
-    wait_vmcnt<(NSL - 2) * NDMA>();
+    if constexpr (MIX) {  // step -1's lo pair
+#pragma unroll
+      for (int j = 0; j < LO_DMA; ++j) dma_lo(0, IC<0>{}, j);
+    }
+    wait_vmcnt<(NSL - 2) * NDMA + LO_DMA>();
   }
   stage_barrier();
 #pragma unroll
@@ -1172,13 +1281,6 @@ hipError_t dispatch_bf16(const uint16_t* A, int64_t lda, const uint16_t* B,
   return launch_kind<AKB>(p.k2, A, lda, B, ldb, M, p.n1, N, K, epi, s);
 }
 
-// The paired product's tiles: 256x256 (three 48 KB slots) or 256x128 (four
-// 40 KB slots), both K = 32 per stage; the same cost estimate as the plain
-// products (full waves of tiles times the tile's cost).
-struct TileChoice {
-  int bm, bn;
-};
-
 // X [M, K] row-major (row stride lda) -> K-blocked [ceil(K/kb)][M][kb]
 // (kb = 32 or 64; zeros in the columns past K of the last block), the A
 // layout whose stage tiles are contiguous runs.  A wave moves 8 rows x 64
@@ -1347,25 +1449,15 @@ hipError_t gemm_bf16_gelu_akb(const uint16_t* Akb, int kb, const uint16_t* B, in
   return dispatch_bf16<true>(Akb, M, B, ldb, M, N, K, EpiGelu{C, 0, M, sh}, s);
 }
 
-TileChoice choose_pair_tile(int M, int N) {
-  const int64_t ncu = device_cu_count();
-  const int64_t t256 = (int64_t)((M + 255) / 256) * ((N + 255) / 256);
-  const int64_t t128 = (int64_t)((M + 255) / 256) * ((N + 127) / 128);
-  const double c256 = (double)((t256 + ncu - 1) / ncu) * 256 * 256 / 1.0;
-  const double c128 = (double)((t128 + ncu - 1) / ncu) * 256 * 128 / 0.95;
-  return c256 <= c128 * 1.001 ? TileChoice{256, 256} : TileChoice{256, 128};
-}
-
-hipError_t gemm_bf16_store_pair_kb(const uint16_t* A2, const uint16_t* B, int64_t ldb, void* C,
-                                   int64_t ldc, OutType out, int M, int N, int K,
-                                   hipStream_t s) {
-  if (K % 32 || ldb >= ((int64_t)1 << 24)) return hipErrorInvalidValue;
+// The mixed-precision product: 256x256 tiles, K = 32 per stage through a
+// 4-slot ring of 32 KB stages (A_hi, B) plus two 16 KB A_lo slots, 160 KB.
+hipError_t gemm_f16_bf8_store_kb(const uint8_t* A, const uint16_t* B, int64_t ldb, void* C,
+                                 int64_t ldc, OutType out, int M, int N, int K, hipStream_t s) {
+  if (K % 64 || ldb >= ((int64_t)1 << 24)) return hipErrorInvalidValue;
   if (M == 0 || N == 0) return hipSuccess;
   const EpiStore epi{C, ldc, (int)out};
-  const TileChoice t = choose_pair_tile(M, N);
-  if (t.bn == 256)
-    return launch_bf16<256, 256, 2, 2, 2, 3, true, EpiStore, 2>(A2, M, B, ldb, M, N, K, epi, s);
-  return launch_bf16<256, 128, 2, 2, 2, 4, true, EpiStore, 2>(A2, M, B, ldb, M, N, K, epi, s);
+  return launch_bf16<256, 256, 2, 2, 2, 4, true, EpiStore, 2>(
+      reinterpret_cast<const uint16_t*>(A), M, B, ldb, M, N, K, epi, s);
 }
 
 hipError_t gemm_bf16_gelu(const uint16_t* A, int64_t lda, const uint16_t* B,

@@ -68,13 +68,14 @@ int64_t gemm_bf16_split_bytes(int M, int N, int64_t K);
 hipError_t gemm_bf16_store_kb(const uint16_t* A, int kb, const uint16_t* B, int64_t ldb,
                               void* C, int64_t ldc, OutType out, int M, int N, int K,
                               float* partials, hipStream_t s);
-// C = (A_hi + A_lo) * B in one pass over K: every stage brings A_hi's and
-// A_lo's tiles and one B tile, both products use the same B fragments.  A2 is
-// K-blocked by 32, [2K/32][M][32] (A_hi's blocks, then A_lo's); K a multiple
-// of 32.
-hipError_t gemm_bf16_store_pair_kb(const uint16_t* A2, const uint16_t* B, int64_t ldb, void* C,
-                                   int64_t ldc, OutType out, int M, int N, int K,
-                                   hipStream_t s);
+// C = A_hi * fp16(B) + A_lo * bf8(B) in one pass over K, B bf16 (converted
+// in registers), A as attention_fwd writes O: A_hi fp16 K-blocked by 32,
+// then A_lo bf8 K-blocked by 64 with permuted row pieces (3*K*M bytes); K a
+// multiple of 64.  Every stage brings A_hi's and B's tiles, every second
+// stage also A_lo's tile for two stages; the lo product runs 32x32x64 bf8
+// MFMAs (twice the fp16 rate).
+hipError_t gemm_f16_bf8_store_kb(const uint8_t* A, const uint16_t* B, int64_t ldb, void* C,
+                                 int64_t ldc, OutType out, int M, int N, int K, hipStream_t s);
 // Same product scattered into the attention workspace (N == 3*nl*d).
 hipError_t gemm_bf16_qkv(const uint16_t* A, int64_t lda, const uint16_t* B,
                          int64_t ldb, const QkvOut& q, int M, int N, int K,
@@ -101,14 +102,15 @@ AttnSplit attn_split(int batch, int seq, int nl, bool causal);
 // Bytes for the chunks' partial results (the larger of causal and full).
 int64_t attn_partial_bytes(int batch, int seq, int nl);
 
-// Causal / full attention over the QKV workspace; writes O as a bf16 hi/lo
-// pair [batch*seq, 2*nl*d]: O_hi in columns [0, nl*d), O_lo in
-// [nl*d, 2*nl*d), row-major for o_kb == 0 or K-blocked for the output
-// projection, [2*nl*d/o_kb][batch*seq][o_kb] (o_kb = 32 or 64).  d must be
-// 128.  `part` (attn_partial_bytes, 16-byte aligned) holds the partial
-// results of split query blocks.
-hipError_t attention_fwd(const QkvOut& q, int batch, bool causal, uint16_t* O, int o_kb,
-                         float* part, hipStream_t s);
+// Causal / full attention over the QKV workspace; writes O [batch*seq,
+// nl*d] for the output projection (gemm_f16_bf8_store_kb) as O_hi = fp16(O),
+// K-blocked by 32, [nl*d/32][batch*seq][32], followed by O_lo = bf8(O -
+// O_hi), K-blocked by 64, [nl*d/64][batch*seq][64 bytes], each 64-byte row
+// piece permuted (byte 32h + 8s + j holds column 16s + 8h + j): 3 bytes per
+// element in all.  d must be 128.  `part` (attn_partial_bytes, 16-byte
+// aligned) holds the partial results of split query blocks.
+hipError_t attention_fwd(const QkvOut& q, int batch, bool causal, uint16_t* O, float* part,
+                         hipStream_t s);
 
 // out = sum_i P_i + R, fp32 accumulate, any n (the last n % 8 elements take
 // a scalar path).

@@ -120,8 +120,9 @@ bool attn_shape_ok(int64_t batch, int64_t seq, int64_t nl) {
 }
 
 // Attention workspace: four [batch*nl, seq_pad, d] 16-bit arrays (Q, K in
-// fp16, V^T as an fp16 hi/lo pair) followed by O [batch*seq, 2*nl*d] bf16
-// (hi half, lo half), then the partial results of split query blocks (fp32).
+// fp16, V^T as an fp16 hi/lo pair) followed by O [batch*seq, nl*d] as fp16
+// plus a bf8 residual (3 bytes per element), then the partial results of
+// split query blocks (fp32).
 constexpr int64_t kAttnParts = 4;
 struct AttnLayout {
   int64_t seq_pad, part_bytes, o_bytes, split_bytes, total;
@@ -130,7 +131,7 @@ AttnLayout attn_layout(int64_t batch, int64_t seq, int64_t nl, int64_t d) {
   AttnLayout L;
   L.seq_pad = (seq + kAttnKeyTile - 1) / kAttnKeyTile * kAttnKeyTile;
   L.part_bytes = align256(batch * nl * L.seq_pad * d * 2);
-  L.o_bytes = align256(batch * seq * 2 * nl * d * 2);
+  L.o_bytes = align256(batch * seq * nl * d * 3);
   L.split_bytes = align256(tp::attn_partial_bytes((int)batch, (int)seq, (int)nl));
   L.total = kAttnParts * L.part_bytes + L.o_bytes + L.split_bytes;
   return L;
@@ -589,15 +590,15 @@ tp_status_t tp_attn_shard(const void* X, const void* Wqkv_i, const void* Wo_i,
                                      (int)tokens, (int)nqkv, (int)hidden, s);
     if (e != hipSuccess) return hip_status(e, "tp_attn_shard: QKV launch");
     float* part = reinterpret_cast<float*>(ws + kAttnParts * L.part_bytes + L.o_bytes);
-    // O is written K-blocked in the stage depth (32) of the output
-    // projection's paired kernel, so each of its A stages is one contiguous
-    // run; O_hi's blocks come first, then O_lo's.
-    const int o_kb = 32;
-    e = tp::attention_fwd(q, (int)batch, causal != 0, O, o_kb, part, s);
+    // O is written in the layout the output projection reads (fp16 O_hi
+    // K-blocked by its stage depth, then the bf8 residual O_lo K-blocked by
+    // the lo product's 64), so each of its A stages is one contiguous run.
+    e = tp::attention_fwd(q, (int)batch, causal != 0, O, part, s);
     if (e != hipSuccess) return hip_status(e, "tp_attn_shard: attention launch");
-    e = tp::gemm_bf16_store_pair_kb(O, static_cast<const uint16_t*>(Wo_i), hidden, Y_i, hidden,
-                                    out_dtype == TP_F32 ? tp::OUT_F32 : tp::OUT_BF16,
-                                    (int)tokens, (int)hidden, (int)(nl * head_dim), s);
+    e = tp::gemm_f16_bf8_store_kb(reinterpret_cast<const uint8_t*>(O),
+                                  static_cast<const uint16_t*>(Wo_i), hidden, Y_i, hidden,
+                                  out_dtype == TP_F32 ? tp::OUT_F32 : tp::OUT_BF16, (int)tokens,
+                                  (int)hidden, (int)(nl * head_dim), s);
     if (e != hipSuccess) return hip_status(e, "tp_attn_shard: output projection launch");
     return ok();
   } catch (...) {

@@ -759,8 +759,8 @@ def summarize_attn_profile(trace_csv, cmd):
                       "V^T as an fp16 hi/lo pair in 16-byte runs along the sequence",
             "attn_fwd": "causal attention (query blocks of 128 or 256 x up to a chunk of 64-key tiles each)",
             "attn_combine": "merge of the split query blocks",
-            "EpiStore": f"output projection [{S} x {nl * d}] x [{nl * d} x {h}] with O as a bf16 "
-                        "hi/lo pair (both halves against the same W_o tile per stage), fp32 partial"}
+            "EpiStore": f"output projection [{S} x {nl * d}] x [{nl * d} x {h}] with O as "
+                        "fp16 + bf8 residual (an fp16 pass and a 32x32x64 bf8 pass over W_o converted in registers), fp32 partial"}
     flop = 2 * S * h * 3 * nl * d + 4 * d * S * (S + 1) // 2 * nl + 2 * S * nl * d * h
     med = statistics.median(calls)
     lines = [f"# Kernel durations: attention shard t={a['t']} i={a['i']}, hidden {h}, "
@@ -805,7 +805,7 @@ def summarize_layer_profile(trace_csv, cmd):
     roles = [("EpiQkv", "attention: QKV projection [8192 x 12288] x [12288 x 9216]"),
              ("attn_fwd", "attention: causal attention, 24 local heads, 256-query blocks"),
              ("attn_combine", "attention: merge of split query blocks"),
-             ("EpiStore, true, 2", "attention: output projection (O hi/lo) [8192 x 3072] x [3072 x 12288]"),
+             ("EpiStore, true, 2", "attention: output projection (O fp16 + bf8) [8192 x 3072] x [3072 x 12288]"),
              ("EpiGelu", "FFN: GEMM1 + GeLU [8192 x 12288] x [12288 x 12288]"),
              ("EpiStore", "FFN: GEMM2 [8192 x 12288] x [12288 x 12288]"),
              ("reduce_kernel<0, 1, 0", "sum: 4 fp32 attention partials + X (bf16) -> X1 (fp32)"),

@@ -43,7 +43,7 @@
 extern "C" {
 #endif
 
-#define TP_ABI_VERSION 6
+#define TP_ABI_VERSION 7
 #define TP_MAX_PARTIALS 64
 
 /* Element types of tensors crossing the ABI. */
@@ -182,10 +182,14 @@ tp_status_t tp_ffn_shard_noalloc(const void* X, const void* W1_i, const void* W2
  * fp16 (11 significant bits) and V as an fp16 hi+lo pair (hi = fp16(v),
  * lo = fp16(v - hi)), so the value product carries about 22 significant
  * bits; softmax runs in fp32 with the probabilities rounded to fp16; the
- * head outputs O are kept as a bf16 hi+lo pair, which the output projection
- * multiplies by Wo_i in two passes.  Q, K and V must lie within the fp16
- * range (|value| < 65504).  The workspace size depends on the current
- * device's compute-unit count (the attention work split does).
+ * head outputs O are kept as fp16 plus their residual in bf8 (e5m2), about
+ * 14 significant bits, and the output projection multiplies the fp16 part
+ * by Wo_i converted to fp16 and the residual by Wo_i converted to bf8 in one
+ * pass over K.  Q, K and V must lie within the fp16 range (|value| <
+ * 65504), Wo_i within bf8's (|value| <= 57344); Wo_i entries below 2^-14 in
+ * magnitude keep fp16's absolute resolution of 2^-24.  The workspace size
+ * depends on the current device's compute-unit count (the attention work
+ * split does).
  * Shape rules: batch, seq >= 0; head_dim == 128; hidden multiple of 8;
  * batch, batch*seq and batch*(n_heads/t)*ceil(seq/64) below 2^31; hidden and
  * 2*(n_heads/t)*head_dim below 2^22; seq below 2^23 (32-bit tile offsets in

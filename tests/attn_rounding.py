@@ -4,18 +4,22 @@ The fp64 oracle never rounds an intermediate.  The GPU kernels round at
 fixed points: the QKV projection's fp32 accumulators are stored in 16-bit
 formats (single or as a hi/lo pair, hi = round(v), lo = round(v - hi)); the
 softmax probabilities are rounded before the P.V product (the running
-denominator sums the rounded values); O is stored in a 16-bit format (single
-or a hi/lo pair) for the output projection, which may read W_o converted to
-fp16.  This module replays one such choice in numpy: every product is exact
-(fp64), every rounding point is applied where the kernels apply it, and the
-softmax runs online over 64-key tiles like the kernel.  Its error against the
-oracle is what the choice costs, so a choice can be judged here, on the CPU,
-before a kernel implements it.
+denominator sums the rounded values); O is stored for the output projection
+in a 16-bit format (single or a hi/lo pair; the projection may read W_o
+converted to fp16) or as an fp16 value plus its residual in bf8 (e5m2:
+fp16's exponent range, 2 stored significand bits), the projection then
+multiplying the fp16 part by W_o in fp16 and the bf8 part by W_o in bf8.
+This module replays one such choice in numpy: every product is exact (fp64),
+every rounding point is applied where the kernels apply it, and the softmax
+runs online over 64-key tiles like the kernel.  Its error against the oracle
+is what the choice costs, so a choice can be judged here, on the CPU, before
+a kernel implements it.
 
 Formats: "bf16", "fp16" (one 16-bit value), "bf16x2", "fp16x2" (hi/lo
-pair), "f32" (no rounding beyond fp32).  The score product with a pair on
-both sides drops only lo.lo (three MFMA passes); a pair on one side and a
-single value on the other takes two passes; singles one.
+pair), "f32" (no rounding beyond fp32); for O also "fp16+bf8" (hi fp16, lo
+the fp32 residual rounded to bf8).  The score product with a pair on both
+sides drops only lo.lo (three MFMA passes); a pair on one side and a single
+value on the other takes two passes; singles one.
 """
 from __future__ import annotations
 
@@ -36,6 +40,7 @@ class Split:
     p: str = "fp16"
     o: str = "bf16x2"
     wo: str = "bf16"   # W_o as stored ("bf16") or converted to fp16 ("fp16")
+    # (O "fp16+bf8" fixes W_o: fp16 against O_hi, bf8 against O_lo)
 
     def name(self):
         return f"Q {self.q}, K {self.k}, V {self.v}, P {self.p}, O {self.o}, W_o {self.wo}"
@@ -45,7 +50,21 @@ def _f32(x):
     return np.asarray(x, np.float64).astype(np.float32)
 
 
+def bf8(x):
+    """Round to the nearest bf8 (OCP e5m2: 1 sign, 5 exponent bits of bias
+    15, 2 stored significand bits; subnormals below 2^-14 in steps of 2^-16),
+    ties to even.  Magnitudes are assumed below the largest finite value
+    (57344)."""
+    x = np.asarray(x, np.float64)
+    ax = np.abs(x)
+    e = np.floor(np.log2(np.where(ax > 0, ax, 1.0)))
+    step = 2.0 ** (np.maximum(e, -14.0) - 2.0)
+    return np.round(x / step) * step  # np.round: ties to even
+
+
 def _single(x32, fmt):
+    if fmt == "bf8":
+        return bf8(x32)
     if fmt == "bf16":
         return syn.bf16_bits_to_f32(syn.f32_to_bf16_bits(x32)).astype(np.float64)
     if fmt == "fp16":
@@ -58,6 +77,10 @@ def _single(x32, fmt):
 def split_value(x, fmt):
     """(hi, lo) of fp32(x) in `fmt`; lo is 0 for single formats."""
     x32 = _f32(x)
+    if fmt == "fp16+bf8":
+        hi = _single(x32, "fp16")
+        lo = bf8((x32.astype(np.float64) - hi).astype(np.float32))
+        return hi, lo
     if fmt.endswith("x2"):
         base = fmt[:-2]
         hi = _single(x32, base)
@@ -121,6 +144,8 @@ def attn_shard(X, WQ, WK, WV, WO, batch, seq, n_heads, d, i, t, causal, sp: Spli
     O = attention_heads(Q, K, V, batch, seq, hs, d, causal, sp)
     oh, ol = split_value(O, sp.o)
     Wo = WO[cols, :]
+    if sp.o == "fp16+bf8":
+        return oh @ _single(_f32(Wo), "fp16") + ol @ bf8(Wo)
     if sp.wo == "fp16":
         Wo = _single(_f32(Wo), "fp16")
     return (oh + ol) @ Wo

@@ -91,18 +91,18 @@ def test_workspace_queries(lib):
     assert lib.tp_ffn_shard_workspace_bytes(4096, 4096, 16384, 8, B.TP_BF16) == 4096 * 2048 * 2
     assert lib.tp_ffn_shard_workspace_bytes(10, 8, 20, 3, B.TP_BF16) == 0    # t does not divide f
     assert lib.tp_ffn_shard_workspace_bytes(10, 8, 16, 0, B.TP_BF16) == 0
-    # attention: 4 x [heads, seq_pad, 128] (Q, K, V^T hi, V^T lo) + O hi/lo [tokens, 2*nl*128], 16-bit,
-    # then fp32 partial results (qb x (128 + 2) floats) for every workgroup of
+    # attention: 4 x [heads, seq_pad, 128] 16-bit (Q, K, V^T hi, V^T lo) + O
+    # [tokens, nl*128] as fp16 + bf8 (3 bytes per element), then fp32 partial results (qb x (128 + 2) floats) for every workgroup of
     # the larger split: at seq 2048, 8 heads, both use 256-query blocks; the
     # causal one cuts the key ranges (4, 8, ..., 32 tiles) into chunks of 5
     # tiles: 32 chunks x 8 heads = 256 workgroups (the full one: 8 query
     # blocks x 4 chunks of 8 tiles x 8 heads = 256)
     split = 256 * 256 * 130 * 4
-    want = 4 * 8 * 2048 * 128 * 2 + 2048 * 2 * 1024 * 2 + split
+    want = 4 * 8 * 2048 * 128 * 2 + 2048 * 1024 * 3 + split
     assert lib.tp_attn_shard_workspace_bytes(1, 2048, 64, 128, 8) == want
     ragged = lib.tp_attn_shard_workspace_bytes(2, 100, 4, 128, 2)
     # one query block, one chunk, 2 sequences x 2 heads = 4 workgroups
-    assert ragged == 4 * 2 * 2 * 128 * 128 * 2 + 2 * 100 * 2 * 256 * 2 + 4 * 128 * 130 * 4
+    assert ragged == 4 * 2 * 2 * 128 * 128 * 2 + 2 * 100 * 256 * 3 + 4 * 128 * 130 * 4
     assert lib.tp_attn_shard_workspace_bytes(1, 8, 6, 128, 4) == 0
 
 
