@@ -732,9 +732,10 @@ gemm_bf16_kernel(const uint16_t* __restrict__ A, int64_t lda,
   // MIX: DMA number ja (0 <= ja < LO_DMA) of A_lo pair p (K columns 64p ..
   // 64p+63, 64-byte rows like A_hi's, same offsets and swizzle) into lo
   // slot LS.
-  const uint8_t* const a_lo = reinterpret_cast<const uint8_t*>(A) + (int64_t)a_blocks * lda * 64;
   auto dma_lo = [&](int p, auto LS, int ja) {
     constexpr int ls = decltype(LS)::value;
+    const uint8_t* const a_lo =
+        reinterpret_cast<const uint8_t*>(A) + (int64_t)a_blocks * lda * 64;
     const __amdgpu_buffer_rsrc_t ra =
         make_rsrc(a_lo + ((int64_t)p * lda + m0) * 64, (int64_t)rows_valid * 64);
     const int off = (p * 64 < K) ? a_off[ja] : OOB;
@@ -838,18 +839,14 @@ gemm_bf16_kernel(const uint16_t* __restrict__ A, int64_t lda,
   // MIX: A_lo fragment reads (row wr0 + mi*32 + lane%32, logical 16-byte
   // chunks 2(lane/32) and 2(lane/32)+1 of the 64-byte row, A's swizzle) and
   // the lo product, bf8 x bf8 with unit scales (E8M0 127).
-  int lo_rd[2];
-#pragma unroll
-  for (int c2 = 0; c2 < 2; ++c2) {
-    const int c = (2 * (lane >> 5) + c2) ^ (((lane & 31) >> ASH) & (CPR - 1));
-    lo_rd[c2] = (wr0 + (lane & 31)) * A_ROWB + c * 16;
-  }
   i32x8 alo[MIX ? FM : 1];
   auto read_lo = [&](auto LS, int mi) {
     constexpr int ls = decltype(LS)::value;
-    const uint8_t* base = lds_lo + ls * LO_STAGE + mi * 32 * A_ROWB;
-    const u32x4 x0 = *reinterpret_cast<const u32x4*>(base + lo_rd[0]);
-    const u32x4 x1 = *reinterpret_cast<const u32x4*>(base + lo_rd[1]);
+    const uint8_t* base =
+        lds_lo + ls * LO_STAGE + mi * 32 * A_ROWB + (wr0 + (lane & 31)) * A_ROWB;
+    const int sw = ((lane & 31) >> ASH) & (CPR - 1);
+    const u32x4 x0 = *reinterpret_cast<const u32x4*>(base + ((2 * (lane >> 5)) ^ sw) * 16);
+    const u32x4 x1 = *reinterpret_cast<const u32x4*>(base + ((2 * (lane >> 5) + 1) ^ sw) * 16);
     alo[mi] = i32x8{(int)x0[0], (int)x0[1], (int)x0[2], (int)x0[3],
                     (int)x1[0], (int)x1[1], (int)x1[2], (int)x1[3]};
   };
