@@ -46,6 +46,11 @@ class Split:
         return f"Q {self.q}, K {self.k}, V {self.v}, P {self.p}, O {self.o}, W_o {self.wo}"
 
 
+# The split the GPU kernels implement: Q and K single fp16 (one score pass),
+# V an fp16 hi/lo pair with fp16 P (two passes), O fp16 plus a bf8 residual.
+KERNEL = Split(q="fp16", k="fp16", v="fp16x2", p="fp16", o="fp16+bf8")
+
+
 def _f32(x):
     return np.asarray(x, np.float64).astype(np.float32)
 

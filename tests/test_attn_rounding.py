@@ -13,7 +13,7 @@ import pytest
 
 import oracle
 from attention_shards_amd import synthetic as syn
-from attn_rounding import Split, attn_shard, bf8
+from attn_rounding import KERNEL, Split, attn_shard, bf8
 
 HALF_BAR = 1e-2
 
@@ -28,8 +28,6 @@ SHAPES = [
     (3, 40, 384, 6, 3, 2, False),
     (1, 1200, 256, 2, 2, 0, False),
 ]
-
-KERNEL = Split(q="fp16", k="fp16", v="fp16x2", p="fp16", o="fp16+bf8")
 
 _cache = {}
 

@@ -104,6 +104,36 @@ def test_attention_small(gpu, batch, seq, hidden, nh, t, i, causal, out):
     assert e <= TOL_BF16
 
 
+@pytest.mark.parametrize("batch,seq,hidden,nh,t,i", [
+    (1, 4000, 512, 8, 2, 0),    # the emulation's worst shape: O's precision decides it
+    (2, 1500, 512, 16, 2, 1),   # ragged, two sequences, 256-query blocks
+])
+def test_attention_matches_its_rounding_emulation(gpu, batch, seq, hidden, nh, t, i):
+    """The kernels round where tests/attn_rounding.py replays them (Q and K
+    fp16, V an fp16 hi/lo pair, P fp16, O fp16 plus a bf8 residual against
+    W_o in fp16 and in bf8), with fp32 accumulation instead of exact
+    products: its error against the oracle equals the emulation's to within
+    1e-3, and element by element it lies closer to the emulation than the
+    emulation lies to the oracle (measured 0.0024 against 0.0050 and 0.0014
+    against 0.0036: fp32 accumulation flips some of the fp16 roundings of Q,
+    K and V).  A kernel that dropped or garbled one of those terms (the bf8
+    residual product, the V^T_lo pass) would sit about 0.009-0.012 from the
+    emulation here, where O or V as one fp16 value lands, even where its
+    error against the oracle stays within the bar."""
+    from attn_rounding import KERNEL, attn_shard as emulate
+    a = syn.make_attn_inputs(40 + seq, batch, seq, hidden, nh, 128)
+    got = run(gpu, a, batch, seq, nh, 128, i, t, True, syn.F32)
+    r = ref(a, batch, seq, nh, 128, i, t, True)
+    f = {k: syn.to_f64(a[k], syn.BF16) for k in ("X", "WQ", "WK", "WV", "WO")}
+    emu = emulate(f["X"], f["WQ"], f["WK"], f["WV"], f["WO"], batch, seq, nh, 128, i, t, True,
+                  KERNEL)
+    d, e, ee = rel_err(got, emu), rel_err(got, r), rel_err(emu, r)
+    log(f"attention batch={batch} seq={seq} nh={nh}: GPU vs emulation {d:.5f}, "
+        f"GPU vs oracle {e:.4f}, emulation vs oracle {ee:.4f}")
+    assert abs(e - ee) <= 1e-3
+    assert d <= 0.7 * ee
+
+
 def test_attention_bf16_output_at_its_floor(gpu):
     """A causal bf16 partial cannot meet 2e-2 on short sequences: rounding the
     exact result to bf16 already costs 0.024 here (row 0 equals v_0 W_o and
